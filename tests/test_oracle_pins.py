@@ -1,0 +1,389 @@
+"""Pins for the CPU oracle: each check ties an oracle function to something
+other than itself (library routines written independently of it, closed forms,
+brute force on tiny inputs, identities), chosen so that a dropped term, a
+wrong sign or index, or a transposed operand fails at least one of them.
+
+The pages print no worked numeric example of the layer (no input/output
+values), so no check here compares against printed values; see
+tests/golden/README.md.
+"""
+
+import itertools
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+# ---------------------------------------------------------------- decoders
+
+def test_bf16_decoder_matches_torch_for_every_code():
+    codes = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = oracle.decode_bf16(codes)
+    ref = torch.from_numpy(codes.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(ours))
+    assert np.array_equal(ours[~nan], ref[~nan])
+    # signed zeros survive
+    assert np.array_equal(np.signbit(ours[~nan]), np.signbit(ref[~nan]))
+
+
+def test_e4m3fn_decoder_matches_torch_for_every_code():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.decode_e4m3fn(codes)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert nan.sum() == 2                       # 0x7F and 0xFF only
+    assert np.array_equal(nan, np.isnan(ours))
+    assert np.array_equal(ours[~nan], ref[~nan])
+
+
+def test_e4m3fn_landmarks_from_the_ocp_definition():
+    d = oracle.decode_e4m3fn
+    assert d(0x7E) == 448.0                     # largest finite: 1.75 * 2^8
+    assert d(0xFE) == -448.0
+    assert d(0x01) == 2.0 ** -9                 # smallest subnormal
+    assert d(0x07) == 7 * 2.0 ** -9             # largest subnormal
+    assert d(0x08) == 2.0 ** -6                 # smallest normal
+    assert d(0x38) == 1.0                       # exponent field 7 = bias
+    assert d(0x39) == 1.125
+    assert np.isnan(d(0x7F)) and np.isnan(d(0xFF))
+    assert d(0x80) == 0.0 and np.signbit(d(0x80))
+
+
+def test_decode_weights_scales_rows_and_tensors():
+    codes = np.full((2, 3), 0x38, dtype=np.uint8)      # all 1.0
+    codes[1, 2] = 0xC0                                  # -2.0
+    w = oracle.decode_weights(codes, "e4m3fn", np.array([2.0, 3.0], np.float32))
+    assert np.array_equal(w, np.array([[2, 2, 2], [3, 3, -6]], np.float64))
+    w = oracle.decode_weights(codes, "e4m3fn", np.float32(0.5))
+    assert np.array_equal(w, np.array([[0.5, 0.5, 0.5], [0.5, 0.5, -1.0]]))
+    with pytest.raises(ValueError):
+        oracle.decode_weights(codes, "e4m3fn", np.ones(3, np.float32))   # wrong axis
+
+
+# ---------------------------------------------------------------- router
+
+def test_logits_one_hot_tokens_pick_router_columns():
+    rng = np.random.default_rng(1)
+    E, d = 5, 7                                      # non-square on purpose
+    wg = rng.standard_normal((E, d)).astype(np.float32)
+    cols = [3, 0, 6, 2]
+    x = np.zeros((len(cols), d))
+    for t, c in enumerate(cols):
+        x[t, c] = 1.0
+    lg = oracle.router_logits(x, wg)
+    assert lg.shape == (len(cols), E)
+    for t, c in enumerate(cols):
+        assert np.array_equal(lg[t], wg[:, c].astype(np.float64))
+
+
+def test_logits_match_exact_sums():
+    rng = np.random.default_rng(2)
+    T, E, d = 3, 4, 9
+    x = rng.standard_normal((T, d))
+    wg = rng.standard_normal((E, d)).astype(np.float32)
+    lg = oracle.router_logits(x, wg)
+    for t in range(T):
+        for e in range(E):
+            exact = math.fsum(float(x[t, i]) * float(wg[e, i]) for i in range(d))
+            assert abs(lg[t, e] - exact) <= 1e-14 * (1 + abs(exact))
+
+
+def _brute_topk(row, k):
+    return sorted(range(len(row)), key=lambda e: (-row[e], e))[:k]
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (5, 5), (7, 1), (32, 4), (256, 8)])
+def test_topk_brute_force(E, k):
+    rng = np.random.default_rng(E * 100 + k)
+    # coarse values make ties common
+    lg = rng.integers(-3, 4, size=(40, E)).astype(np.float64)
+    ids = oracle.select_topk(lg, k)
+    assert ids.dtype == np.int32 and ids.shape == (40, k)
+    for t in range(40):
+        assert list(ids[t]) == _brute_topk(list(lg[t]), k)
+
+
+def test_topk_ties_from_duplicate_router_rows_go_to_lower_index():
+    rng = np.random.default_rng(3)
+    d = 16
+    base = rng.standard_normal((3, d)).astype(np.float32)
+    wg = np.stack([base[0], base[1], base[0], base[2], base[1]])   # 0==2, 1==4
+    x = rng.standard_normal((50, d))
+    lg = oracle.router_logits(x, wg)
+    ids = oracle.select_topk(lg, 4)
+    for t in range(50):
+        row = list(ids[t])
+        assert row.index(0) < row.index(2) if 2 in row else True
+        assert row.index(1) < row.index(4) if 4 in row else True
+        assert list(row) == _brute_topk(list(lg[t]), 4)
+
+
+def test_topk_k_equals_E_is_a_full_ranking():
+    lg = np.array([[0.5, 2.0, -1.0, 2.0]])
+    assert list(oracle.select_topk(lg, 4)[0]) == [1, 3, 0, 2]
+    with pytest.raises(ValueError):
+        oracle.select_topk(lg, 5)
+    with pytest.raises(ValueError):
+        oracle.select_topk(lg, 0)
+
+
+def test_gates_closed_form():
+    lg = np.log(np.array([[1.0, 2.0, 3.0, 4.0]]))
+    ids = oracle.select_topk(lg, 2)
+    assert list(ids[0]) == [3, 2]
+    w = oracle.gate_weights(lg, ids)
+    assert np.allclose(w[0], [4 / 7, 3 / 7], rtol=0, atol=1e-15)
+    ids3 = oracle.select_topk(lg, 3)
+    assert np.allclose(oracle.gate_weights(lg, ids3)[0], [4 / 9, 3 / 9, 2 / 9], rtol=0, atol=1e-15)
+
+
+def test_gates_sum_to_one_and_k1_is_exactly_one():
+    rng = np.random.default_rng(4)
+    lg = rng.standard_normal((64, 32)) * 5
+    for k in (1, 3, 8, 32):
+        ids = oracle.select_topk(lg, k)
+        w = oracle.gate_weights(lg, ids)
+        assert np.all(np.abs(w.sum(axis=1) - 1) < 1e-12)
+        assert np.all(w > 0)
+        assert np.all(np.diff(w, axis=1) <= 0)      # rank order = descending gate
+        if k == 1:
+            assert np.all(w == 1.0)
+        sel = np.take_along_axis(lg, ids.astype(np.int64), 1)
+        assert np.allclose(w, scipy.special.softmax(sel, axis=1), rtol=1e-13, atol=0)
+        full = scipy.special.softmax(lg, axis=1)
+        renorm = np.take_along_axis(full, ids.astype(np.int64), 1)
+        renorm /= renorm.sum(axis=1, keepdims=True)
+        assert np.allclose(w, renorm, rtol=1e-12, atol=0)
+
+
+# ---------------------------------------------------------------- align
+
+def _brute_align(ids, E, B):
+    T, k = ids.shape
+    A = T * k
+    groups = {e: [] for e in range(E)}
+    for t in range(T):
+        for j in range(k):
+            groups[int(ids[t, j])].append(t * k + j)
+    rows, blocks = [], []
+    for e in range(E):
+        g = sorted(groups[e])
+        if not g:
+            continue
+        nb = -(-len(g) // B)
+        rows += g + [A] * (nb * B - len(g))
+        blocks += [e] * nb
+    cap = -(-(A + min(E, A) * (B - 1)) // B) * B
+    return ([len(groups[e]) for e in range(E)], rows + [A] * (cap - len(rows)),
+            blocks + [-1] * (cap // B - len(blocks)), len(rows))
+
+
+def test_align_hand_worked_case():
+    ids = np.array([[2, 0], [2, 1], [0, 2]])
+    al = oracle.align(ids, 4, 2)
+    assert list(al["counts"]) == [2, 1, 3, 0]
+    assert list(al["offsets"]) == [0, 2, 4, 8, 8]
+    assert al["num_padded"] == 8
+    assert al["capacity"] == 10
+    assert list(al["sorted_ids"]) == [1, 4, 3, 6, 0, 2, 5, 6, 6, 6]
+    assert list(al["block_expert"]) == [0, 1, 2, 2, -1]
+
+
+@pytest.mark.parametrize("T,E,k,B", [(16, 8, 2, 16), (5, 8, 2, 64), (33, 4, 4, 8),
+                                     (100, 32, 4, 16), (1, 8, 2, 64), (7, 3, 1, 4)])
+def test_align_brute_force_and_invariants(T, E, k, B):
+    rng = np.random.default_rng(T * 7 + E)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    al = oracle.align(ids, E, B)
+    counts, rows, blocks, npad = _brute_align(ids, E, B)
+    assert list(al["counts"]) == counts
+    assert list(al["sorted_ids"]) == rows
+    assert list(al["block_expert"]) == blocks
+    assert al["num_padded"] == npad
+    A = T * k
+    valid = al["sorted_ids"][al["sorted_ids"] < A]
+    assert sorted(valid.tolist()) == list(range(A))         # every slot exactly once
+    assert al["num_padded"] % B == 0 and sum(counts) == A
+    assert len(al["sorted_ids"]) == al["capacity"] >= al["num_padded"]
+    for b in range(al["num_padded"] // B):                  # each block's slots go to its expert
+        e = al["block_expert"][b]
+        blk = al["sorted_ids"][b * B:(b + 1) * B]
+        assert all(ids.reshape(-1)[f] == e for f in blk if f < A)
+
+
+def test_align_empty():
+    al = oracle.align(np.zeros((0, 2), np.int32), 8, 16)
+    assert al["num_padded"] == 0 and al["capacity"] == 0
+    assert list(al["counts"]) == [0] * 8
+
+
+# ---------------------------------------------------------------- expert network
+
+def test_silu_library_and_closed_form():
+    z = np.linspace(-30, 30, 601)
+    ref = torch.nn.functional.silu(torch.from_numpy(z)).numpy()
+    assert np.allclose(oracle.silu(z), ref, rtol=1e-15, atol=1e-300)
+    assert oracle.silu(np.array(1.0)) == pytest.approx(0.7310585786300049, rel=1e-15)  # 1 / (1 + 1/e)
+    assert oracle.silu(np.array(0.0)) == 0.0
+    assert oracle.silu(np.array(-800.0)) == 0.0
+
+
+def test_expert_ffn_scalar_closed_form():
+    # d = 1, I = 1: g = 0.5*2 = 1, u = 3*2 = 6, h = SiLU(1)*6, y = -1.5*h
+    y = oracle.expert_ffn(np.array([[2.0]]), np.array([[0.5], [3.0]]), np.array([[-1.5]]))
+    assert y[0, 0] == pytest.approx(-1.5 * 6 * 0.7310585786300049, rel=1e-15)
+
+
+def _torch_swiglu(x, w13, w2):
+    I = w13.shape[0] // 2
+    X = torch.from_numpy(x)
+    W1 = torch.from_numpy(w13[:I])
+    W3 = torch.from_numpy(w13[I:])
+    W2 = torch.from_numpy(w2)
+    h = torch.nn.functional.silu(torch.nn.functional.linear(X, W1)) * torch.nn.functional.linear(X, W3)
+    return torch.nn.functional.linear(h, W2).numpy()
+
+
+def test_single_expert_top1_is_a_dense_swiglu_mlp():
+    rng = np.random.default_rng(5)
+    T, d, I = 9, 24, 40                              # d != I != 2I catches transposes
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    w13 = (rng.standard_normal((1, 2 * I, d)) * 0.3).astype(np.float32)
+    w2 = (rng.standard_normal((1, d, I)) * 0.3).astype(np.float32)
+    wg = rng.standard_normal((1, d)).astype(np.float32)
+    r = oracle.moe_forward(x, wg, w13, w2, 1, act_fmt="f32", w_fmt="f32", block_m=4)
+    ref = _torch_swiglu(x.astype(np.float64), w13[0].astype(np.float64), w2[0].astype(np.float64))
+    assert np.allclose(r["out"], ref, rtol=1e-13, atol=1e-13)
+    assert np.all(r["gates"] == 1.0)
+
+
+# ---------------------------------------------------------------- whole layer
+
+def _dense_bruteforce(x, wg, W13, W2, k):
+    """Every expert on every token, masked by the selection.  Independent of
+    the oracle: selection by Python sorted, gates by scipy softmax, expert
+    networks by torch."""
+    T = x.shape[0]
+    E = wg.shape[0]
+    lg = x @ wg.astype(np.float64).T
+    out = np.zeros_like(x)
+    ys = [_torch_swiglu(x, W13[e], W2[e]) for e in range(E)]
+    for t in range(T):
+        sel = _brute_topk(list(lg[t]), k)
+        g = scipy.special.softmax(lg[t, sel])
+        for j, e in enumerate(sel):
+            out[t] += g[j] * ys[e][t]
+    return out
+
+
+def _rel(a, b):
+    return np.linalg.norm(a - b) / np.linalg.norm(b)
+
+
+@pytest.mark.parametrize("B", [4, 16, 64])
+def test_layer_fp32_matches_dense_bruteforce(B):
+    rng = np.random.default_rng(6)
+    T, d, E, k, I = 16, 256, 8, 2, 512              # the tiny fp32 workload's shapes
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    wg = (rng.standard_normal((E, d)) * 0.02).astype(np.float32)
+    w13 = (rng.standard_normal((E, 2 * I, d)) * 0.02).astype(np.float32)
+    w2 = (rng.standard_normal((E, d, I)) * 0.02).astype(np.float32)
+    r = oracle.moe_forward(x, wg, w13, w2, k, act_fmt="f32", w_fmt="f32", block_m=B)
+    ref = _dense_bruteforce(x.astype(np.float64), wg, w13.astype(np.float64), w2.astype(np.float64), k)
+    assert _rel(r["out"], ref) < 1e-13
+
+
+def test_layer_bf16_matches_dense_bruteforce():
+    rng = np.random.default_rng(7)
+    T, d, E, k, I = 12, 64, 6, 3, 96
+    xf = torch.from_numpy(rng.standard_normal((T, d)).astype(np.float32)).to(torch.bfloat16)
+    w13f = torch.from_numpy((rng.standard_normal((E, 2 * I, d)) * 0.1).astype(np.float32)).to(torch.bfloat16)
+    w2f = torch.from_numpy((rng.standard_normal((E, d, I)) * 0.1).astype(np.float32)).to(torch.bfloat16)
+    wg = (rng.standard_normal((E, d)) * 0.3).astype(np.float32)
+    raw = lambda t: t.view(torch.int16).numpy().view(np.uint16)
+    r = oracle.moe_forward(raw(xf), wg, raw(w13f), raw(w2f), k, act_fmt="bf16", w_fmt="bf16", block_m=8)
+    ref = _dense_bruteforce(xf.double().numpy(), wg, w13f.double().numpy(), w2f.double().numpy(), k)
+    assert _rel(r["out"], ref) < 1e-13
+
+
+@pytest.mark.parametrize("mode", ["channel", "tensor"])
+def test_layer_e4m3fn_matches_dense_bruteforce(mode):
+    from mixture_experts_moe_amd import synth
+    inp = synth.make_inputs("fp8", T=10, d=64, E=12, k=4, I=32, scale_mode=mode)
+    kw = synth.to_oracle(inp)
+    r = oracle.moe_forward(**kw, block_m=16)
+    # dequantise with torch's own e4m3fn cast, independently of the oracle's decoder
+    deq13 = inp.w13.view(torch.float8_e4m3fn).double()
+    deq2 = inp.w2.view(torch.float8_e4m3fn).double()
+    if mode == "channel":
+        deq13 = deq13 * inp.s13.double()[:, :, None]
+        deq2 = deq2 * inp.s2.double()[:, :, None]
+    else:
+        deq13 = deq13 * inp.s13.double()[:, None, None]
+        deq2 = deq2 * inp.s2.double()[:, None, None]
+    ref = _dense_bruteforce(inp.x.double().numpy(), inp.w_gate.numpy(), deq13.numpy(), deq2.numpy(), 4)
+    assert _rel(r["out"], ref) < 1e-13
+
+
+def test_uniform_gates_with_k_equal_E_give_the_expert_mean():
+    rng = np.random.default_rng(8)
+    T, d, E, I = 6, 32, 5, 48
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    wg = np.zeros((E, d), np.float32)               # all logits 0: uniform gates
+    w13 = (rng.standard_normal((E, 2 * I, d)) * 0.2).astype(np.float32)
+    w2 = (rng.standard_normal((E, d, I)) * 0.2).astype(np.float32)
+    r = oracle.moe_forward(x, wg, w13, w2, E, act_fmt="f32", w_fmt="f32", block_m=4)
+    assert np.all(r["ids"] == np.arange(E))        # ties: index order
+    assert np.allclose(r["gates"], 1.0 / E, rtol=1e-15, atol=0)
+    mean = np.mean([_torch_swiglu(x.astype(np.float64), w13[e].astype(np.float64),
+                                  w2[e].astype(np.float64)) for e in range(E)], axis=0)
+    assert np.allclose(r["out"], mean, rtol=1e-12, atol=1e-14)
+
+
+def test_idle_experts_and_block_size_do_not_change_outputs():
+    rng = np.random.default_rng(9)
+    T, d, E, k, I = 20, 32, 6, 2, 16
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    x[:, 0] = 1.0
+    wg = (rng.standard_normal((E, d)) * 0.1).astype(np.float32)
+    wg[:, 0] = [0, -50, 0, 0, -50, 0]               # experts 1 and 4 never chosen
+    w13 = (rng.standard_normal((E, 2 * I, d)) * 0.2).astype(np.float32)
+    w2 = (rng.standard_normal((E, d, I)) * 0.2).astype(np.float32)
+    outs = []
+    for B in (1, 4, 64):
+        r = oracle.moe_forward(x, wg, w13, w2, k, act_fmt="f32", w_fmt="f32", block_m=B)
+        assert r["counts"][1] == 0 and r["counts"][4] == 0
+        outs.append(r["out"])
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
+    ref = _dense_bruteforce(x.astype(np.float64), wg, w13.astype(np.float64), w2.astype(np.float64), k)
+    assert _rel(outs[0], ref) < 1e-13
+
+
+def test_zero_tokens():
+    x = np.zeros((0, 8), np.float32)
+    wg = np.zeros((3, 8), np.float32)
+    w13 = np.zeros((3, 4, 8), np.float32)
+    w2 = np.zeros((3, 8, 2), np.float32)
+    r = oracle.moe_forward(x, wg, w13, w2, 2, act_fmt="f32", w_fmt="f32", block_m=4)
+    assert r["out"].shape == (0, 8) and r["num_padded"] == 0
+
+
+def test_given_logits_override_routing():
+    rng = np.random.default_rng(10)
+    T, d, E, k, I = 4, 8, 4, 2, 4
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    wg = rng.standard_normal((E, d)).astype(np.float32)
+    w13 = rng.standard_normal((E, 2 * I, d)).astype(np.float32)
+    w2 = rng.standard_normal((E, d, I)).astype(np.float32)
+    lg = np.tile(np.array([[0.0, 1.0, 2.0, 3.0]]), (T, 1))
+    r = oracle.moe_forward(x, wg, w13, w2, k, act_fmt="f32", w_fmt="f32", block_m=4, logits=lg)
+    assert np.all(r["ids"] == [3, 2])
+    assert list(r["counts"]) == [0, 0, T, T]
