@@ -1,0 +1,216 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) fused Mixture-of-Experts layer.
+ *
+ * The layer (one batched GPU operation instead of a loop over experts):
+ *   1. route:   logits = x . W_gate^T (fp32), the top_k experts per token
+ *               (ties to the lower expert index), gates = softmax over the
+ *               selected logits;
+ *   2. align:   regroup the T*top_k routing slots by expert into blocks of
+ *               block_m rows (padded, slots ascending inside an expert);
+ *   3. W13:     per expert, h = SiLU(W1 x) * (W3 x) for the expert's tokens;
+ *   4. W2:      y = gate * (W2 h) per routing slot;
+ *   5. combine: out[t] = sum of the token's top_k slot outputs, in rank order.
+ * Sources: the Hungarian news page "Az AWS új MoE-optimalizációkkal gyorsítja
+ * a SageMaker AI-t", section "A fused MoE a számítási folyamat több lépését
+ * egyesíti" (routing, data rearrangement and expert computation fused into
+ * one batched GPU operation) and section "FP8 esetén a Triton backend
+ * bizonyult gyorsabbnak" (FP8 scaling, matrix product and aggregation of the
+ * experts' results in one pass); the French page "Ingénierie de kernels
+ * Mixture-of-Experts sur Amazon SageMaker AI", first paragraph.  The pages do
+ * not write out the router rule, the expert network or the FP8 format; the
+ * readings above (softmax/top-k, SwiGLU with W13 = [W1; W3], OCP e4m3fn)
+ * are the plain ones and are fixed by this ABI.
+ *
+ * Conventions for every entry point:
+ *   - Tensors are caller-owned DEVICE buffers, contiguous, row-major, 16-byte
+ *     aligned.  The library never allocates, frees or retains them; inputs
+ *     must stay alive and unmodified until the stream reaches the work.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and the call returns at once.  Outputs are valid once the stream has
+ *     executed it.  Outputs are fully overwritten, never accumulated into.
+ *   - Every argument is validated on the host before any HIP call; a bad
+ *     argument returns a negative status and enqueues nothing.  No C++
+ *     exception crosses the ABI.  MOE_ERR_HIP reports a failed launch.
+ *   - T = 0 is valid: after the descriptor is validated the call returns
+ *     MOE_OK, enqueues nothing and looks at no other argument.
+ *   - Inputs are assumed finite.  A NaN logit ranks below every number.
+ *   - Calls that share a workspace on one stream are ordered by the stream;
+ *     concurrent calls on different streams need different workspaces.
+ *
+ * Shapes (row-major):
+ *   x       [T, d]        act dtype (MOE_DTYPE_F32 or MOE_DTYPE_BF16)
+ *   W_gate  [E, d]        fp32
+ *   W13     [E, 2I, d]    weight dtype; rows 0..I-1 = W1 (gate projection),
+ *                         rows I..2I-1 = W3 (up projection)
+ *   W2      [E, d, I]     weight dtype
+ *   out     [T, d]        act dtype (fp32 -> bf16 rounding is to nearest even)
+ * Supported (act, weight) pairs: (F32, F32), (BF16, BF16), (BF16, E4M3FN).
+ * E4M3FN weights are OCP e4m3fn bytes; value = decoded byte * fp32 scale, the
+ * scale given per output channel (s13 [E, 2I], s2 [E, d]) or per expert
+ * matrix (s13 [E], s2 [E]).  Activations stay bf16 (weight-only FP8).
+ * Limits: d and I multiples of 64; 1 <= E <= 1024; 1 <= top_k <= min(E, 64);
+ * T * top_k < 2^30; block_m in {0 (library default), 16, 32, 64, 128}.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define MOE_API __attribute__((visibility("default")))
+#else
+#define MOE_API
+#endif
+
+/* ---- status codes ---- */
+#define MOE_OK 0
+#define MOE_ERR_NULL_PTR (-1)      /* a required pointer is NULL            */
+#define MOE_ERR_BAD_SHAPE (-2)     /* dimension out of range / not aligned  */
+#define MOE_ERR_BAD_TOPK (-3)      /* top_k < 1, > E or > 64                */
+#define MOE_ERR_BAD_DTYPE (-4)     /* unsupported dtype pair or scale mode  */
+#define MOE_ERR_MISALIGNED (-5)    /* a pointer is not 16-byte aligned      */
+#define MOE_ERR_WORKSPACE (-6)     /* workspace NULL or too small           */
+#define MOE_ERR_HIP (-7)           /* a HIP call or kernel launch failed    */
+#define MOE_ERR_BAD_BLOCK_M (-8)   /* block_m not in {0,16,32,64,128}       */
+#define MOE_ERR_BAD_ARG (-9)       /* any other invalid argument            */
+
+/* ---- dtypes and scale modes ---- */
+#define MOE_DTYPE_F32 0
+#define MOE_DTYPE_BF16 1
+#define MOE_DTYPE_E4M3FN 2
+
+#define MOE_SCALE_NONE 0         /* F32 / BF16 weights                       */
+#define MOE_SCALE_PER_TENSOR 1   /* one fp32 scale per expert matrix: [E]    */
+#define MOE_SCALE_PER_CHANNEL 2  /* one per output row: [E,2I] and [E,d]     */
+
+/* Problem description.  block_m is the row-block size of the regrouped
+ * layout (align); 0 lets the library choose from the shape. */
+typedef struct moe_desc {
+  int64_t num_tokens;    /* T >= 0                   */
+  int64_t hidden;        /* d                        */
+  int64_t num_experts;   /* E                        */
+  int64_t intermediate;  /* I                        */
+  int32_t act_dtype;     /* MOE_DTYPE_F32 / _BF16    */
+  int32_t weight_dtype;  /* MOE_DTYPE_F32/_BF16/_E4M3FN */
+  int32_t block_m;       /* 0 or 16/32/64/128        */
+  int32_t reserved;      /* must be 0                */
+} moe_desc;
+
+/* FP8 weight scales (device pointers, fp32).  Pass NULL (or mode
+ * MOE_SCALE_NONE) for F32 / BF16 weights. */
+typedef struct moe_scales {
+  int32_t mode;          /* MOE_SCALE_*              */
+  int32_t reserved;      /* must be 0                */
+  const float* w13;      /* [E, 2I] or [E]           */
+  const float* w2;       /* [E, d]  or [E]           */
+} moe_scales;
+
+/* ---- sizing ---- */
+
+/* The block size the library uses for `desc` (desc->block_m, or the default
+ * it picks when that is 0) and the capacity of the regrouped layout:
+ * capacity = roundup(A + min(E, A) * (block_m - 1), block_m) rows, A = T*top_k
+ * (each expert that receives a slot pads at most block_m - 1 rows).
+ * sorted_ids needs `capacity` int32 entries, block_expert capacity/block_m. */
+MOE_API int moe_align_capacity(const moe_desc* desc, int top_k, int32_t* block_m,
+                               int64_t* capacity);
+
+/* Bytes of device workspace moe_forward (with_routing = 1) or
+ * moe_expert_ffn (with_routing = 0) needs for `desc`. */
+MOE_API int moe_workspace_bytes(const moe_desc* desc, int top_k, int with_routing,
+                                size_t* bytes);
+
+/* ---- the fused layer ---- */
+
+/* out = MoE(x).  Runs route, align, W13+SiLU*mul, W2+gate scale and combine
+ * on `stream` with no host synchronisation.  `workspace` is a device buffer
+ * of at least moe_workspace_bytes(desc, top_k, 1) bytes, 256-byte aligned;
+ * its contents on entry do not matter.  `scales` may be NULL unless the
+ * weights are E4M3FN.  (Hungarian page, section "A fused MoE ...": routing,
+ * rearrangement and expert compute as one batched operation.) */
+MOE_API int moe_forward(const moe_desc* desc, const void* x, const float* w_gate,
+                        const void* w13, const void* w2, int top_k,
+                        const moe_scales* scales, void* out, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* ---- stage entry points (the same kernels moe_forward runs) ---- */
+
+/* Routing.  Writes logits_out [T, E] fp32 (x . W_gate^T, fp32 products and
+ * sums), topk_ids [T, top_k] int32 in rank order (descending logit, ties to
+ * the lower index) and topk_w [T, top_k] fp32 gates (softmax over the
+ * selected logits; they sum to 1 per token).  All three are required.
+ * (Hungarian page, section "A fused MoE ...": token routing.) */
+MOE_API int moe_route(const moe_desc* desc, const void* x, const float* w_gate, int top_k,
+                      float* logits_out, int32_t* topk_ids, float* topk_w, void* stream);
+
+/* Top-k selection and gates from given logits [T, E] fp32 (the second half
+ * of moe_route, same kernel).  Lets a caller check routing against any
+ * logits.  Same outputs and rules as moe_route. */
+MOE_API int moe_route_logits(const moe_desc* desc, const float* logits, int top_k,
+                             int32_t* topk_ids, float* topk_w, void* stream);
+
+/* Regrouping by expert (the pages' "data rearrangement"; Hungarian page,
+ * section "A fused MoE ..."; French page, first paragraph).  From topk_ids
+ * [T, top_k] writes:
+ *   counts      [E]          slots routed to each expert;
+ *   sorted_ids  [capacity]   expert e's group starts at
+ *                            sum_{e'<e} roundup(counts[e'], block_m) and
+ *                            lists its flat slot ids f = t*top_k + j in
+ *                            ascending order, padded with the sentinel
+ *                            A = T*top_k; entries past the padded total = A;
+ *   block_expert[capacity/block_m]  owner expert of each block, -1 past the
+ *                            padded total;
+ *   num_padded  [1]          the padded total (a multiple of block_m).
+ * Ids outside [0, E) are ignored (their slot is dropped).  Deterministic. */
+MOE_API int moe_align(const moe_desc* desc, const int32_t* topk_ids, int top_k,
+                      int32_t* counts, int32_t* sorted_ids, int32_t* block_expert,
+                      int32_t* num_padded, void* stream);
+
+/* Expert computation and combine for an existing routing: W13 grouped
+ * product with SiLU(gate)*up, W2 grouped product scaled by the slot's gate,
+ * sum of each token's slots into out [T, d].  topk_w [T, top_k] fp32 and
+ * sorted_ids / block_expert / num_padded as written by moe_align with the
+ * same desc (same block_m).  `workspace`: moe_workspace_bytes(desc, top_k, 0)
+ * bytes.  (Hungarian page, sections "A fused MoE ..." and "FP8 esetén ...":
+ * expert computation, FP8 scaling and aggregation of the experts' results.) */
+MOE_API int moe_expert_ffn(const moe_desc* desc, const void* x, const void* w13,
+                           const void* w2, int top_k, const moe_scales* scales,
+                           const float* topk_w, const int32_t* sorted_ids,
+                           const int32_t* block_expert, const int32_t* num_padded,
+                           void* out, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* ---- diagnostics ---- */
+
+/* Static text for a status code (never NULL). */
+MOE_API const char* moe_strerror(int status);
+
+/* Kernel timing.  While enabled, every kernel the library launches is
+ * bracketed by two HIP events on its stream (a small cost per launch);
+ * moe_timing_collect waits for the recorded events and adds their durations
+ * into per-kernel totals.  Kernel kinds index the arrays. */
+#define MOE_KERNEL_ROUTE_LOGITS 0
+#define MOE_KERNEL_ROUTE_TOPK 1
+#define MOE_KERNEL_ALIGN 2
+#define MOE_KERNEL_FFN13 3
+#define MOE_KERNEL_FFN2 4
+#define MOE_KERNEL_COMBINE 5
+#define MOE_KERNEL_COUNT 6
+
+MOE_API int moe_timing_enable(int enable);
+/* total_ms[MOE_KERNEL_COUNT], launches[MOE_KERNEL_COUNT]; reset != 0 clears
+ * the totals after reading.  Blocks until the recorded events complete. */
+MOE_API int moe_timing_collect(double* total_ms, int64_t* launches, int reset);
+/* Name of a kernel kind ("ffn13", ...), or "" if out of range. */
+MOE_API const char* moe_kernel_name(int kind);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

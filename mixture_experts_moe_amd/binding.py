@@ -1,0 +1,315 @@
+"""ctypes binding of the fused MoE C ABI (include/moe.h).
+
+Argument marshalling only: every function takes torch tensors, checks their
+shapes, dtypes and devices, and calls the C entry point of the same name with
+raw device pointers and the current HIP stream.  All computation happens in
+the HIP kernels of ``libmoe.so``; there is no fallback of any kind, and if
+the library is missing the first call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+
+MOE_DTYPE_F32 = 0
+MOE_DTYPE_BF16 = 1
+MOE_DTYPE_E4M3FN = 2
+MOE_SCALE_NONE = 0
+MOE_SCALE_PER_TENSOR = 1
+MOE_SCALE_PER_CHANNEL = 2
+MOE_KERNEL_COUNT = 6
+
+ENTRY_POINTS = (
+    "moe_align_capacity", "moe_workspace_bytes", "moe_forward", "moe_route",
+    "moe_route_logits", "moe_align", "moe_expert_ffn", "moe_strerror",
+    "moe_timing_enable", "moe_timing_collect", "moe_kernel_name",
+)
+
+
+class moe_desc(ctypes.Structure):
+    _fields_ = [("num_tokens", ctypes.c_int64), ("hidden", ctypes.c_int64),
+                ("num_experts", ctypes.c_int64), ("intermediate", ctypes.c_int64),
+                ("act_dtype", ctypes.c_int32), ("weight_dtype", ctypes.c_int32),
+                ("block_m", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class moe_scales(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("w13", ctypes.c_void_p), ("w2", ctypes.c_void_p)]
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {strerror(status)} (status {status})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is not built; run `python -m mixture_experts_moe_amd.build`")
+    L = ctypes.CDLL(_LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    D = ctypes.POINTER(moe_desc)
+    S = ctypes.POINTER(moe_scales)
+    sig = {
+        "moe_align_capacity": (I32, [D, I32, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(I64)]),
+        "moe_workspace_bytes": (I32, [D, I32, I32, ctypes.POINTER(SZ)]),
+        "moe_forward": (I32, [D, P, P, P, P, I32, S, P, P, SZ, P]),
+        "moe_route": (I32, [D, P, P, I32, P, P, P, P]),
+        "moe_route_logits": (I32, [D, P, I32, P, P, P]),
+        "moe_align": (I32, [D, P, I32, P, P, P, P, P]),
+        "moe_expert_ffn": (I32, [D, P, P, P, I32, S, P, P, P, P, P, P, SZ, P]),
+        "moe_strerror": (ctypes.c_char_p, [I32]),
+        "moe_timing_enable": (I32, [I32]),
+        "moe_timing_collect": (I32, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64), I32]),
+        "moe_kernel_name": (ctypes.c_char_p, [I32]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def strerror(status: int) -> str:
+    return lib().moe_strerror(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise MoEError(fn, status)
+
+
+# ------------------------------------------------------------ marshalling
+
+def _act_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MOE_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_DTYPE_BF16
+    raise TypeError(f"activations must be float32 or bfloat16, got {t.dtype}")
+
+
+def _w_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MOE_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_DTYPE_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return MOE_DTYPE_E4M3FN
+    raise TypeError(f"weights must be float32, bfloat16 or e4m3fn bytes, got {t.dtype}")
+
+
+def make_desc(T: int, d: int, E: int, I: int, act_dtype: int, weight_dtype: int,
+              block_m: int = 0) -> moe_desc:
+    return moe_desc(int(T), int(d), int(E), int(I), int(act_dtype), int(weight_dtype),
+                    int(block_m), 0)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(*ts: Optional[torch.Tensor]) -> torch.device:
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError("all tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors must be on one device")
+    return dev
+
+
+def _stream(dev: torch.device, stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _scales(w13: torch.Tensor, scales) -> Optional[moe_scales]:
+    if _w_code(w13) != MOE_DTYPE_E4M3FN:
+        if scales is not None:
+            raise ValueError("scales are only for e4m3fn weights")
+        return None
+    if scales is None:
+        raise ValueError("e4m3fn weights need (s13, s2) scales")
+    s13, s2 = scales
+    if s13.dtype != torch.float32 or s2.dtype != torch.float32:
+        raise TypeError("scales must be float32")
+    mode = MOE_SCALE_PER_CHANNEL if s13.dim() == 2 else MOE_SCALE_PER_TENSOR
+    return moe_scales(mode, 0, s13.data_ptr(), s2.data_ptr())
+
+
+def _shapes(x, w_gate, w13, w2):
+    T, d = x.shape
+    if w13.dim() != 3 or w2.dim() != 3:
+        raise ValueError("w13 must be [E, 2I, d] and w2 [E, d, I]")
+    E, twoI, d13 = w13.shape
+    I = twoI // 2
+    if d13 != d or twoI != 2 * I or tuple(w2.shape) != (E, d, I):
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)}, w13 {tuple(w13.shape)}, w2 {tuple(w2.shape)}")
+    if w_gate is not None:
+        if w_gate.dtype != torch.float32 or tuple(w_gate.shape) != (E, d):
+            raise ValueError(f"w_gate must be float32 [{E}, {d}]")
+    return T, d, E, I
+
+
+def _workspace(nbytes: int, dev, workspace: Optional[torch.Tensor]) -> torch.Tensor:
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError("workspace too small")
+        return workspace
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+
+
+# ------------------------------------------------------------ entry points
+
+def moe_align_capacity(desc: moe_desc, top_k: int) -> Tuple[int, int]:
+    """(block_m, capacity) of the regrouped layout for `desc`."""
+    bm = ctypes.c_int32()
+    cap = ctypes.c_int64()
+    _check("moe_align_capacity", lib().moe_align_capacity(ctypes.byref(desc), int(top_k),
+                                                         ctypes.byref(bm), ctypes.byref(cap)))
+    return bm.value, cap.value
+
+
+def moe_workspace_bytes(desc: moe_desc, top_k: int, with_routing: bool = True) -> int:
+    n = ctypes.c_size_t()
+    _check("moe_workspace_bytes", lib().moe_workspace_bytes(ctypes.byref(desc), int(top_k),
+                                                           int(bool(with_routing)), ctypes.byref(n)))
+    return n.value
+
+
+def moe_forward(x: torch.Tensor, w_gate: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor,
+                top_k: int, scales: Optional[Sequence[torch.Tensor]] = None,
+                out: Optional[torch.Tensor] = None, *, block_m: int = 0,
+                workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """out [T, d] = fused MoE layer of x (same dtype as x)."""
+    dev = _dev(x, w_gate, w13, w2, out)
+    T, d, E, I = _shapes(x, w_gate, w13, w2)
+    desc = make_desc(T, d, E, I, _act_code(x), _w_code(w13), block_m)
+    sc = _scales(w13, scales)
+    if out is None:
+        out = torch.empty((T, d), dtype=x.dtype, device=dev)
+    elif out.shape != x.shape or out.dtype != x.dtype:
+        raise ValueError("out must match x in shape and dtype")
+    nbytes = moe_workspace_bytes(desc, top_k, True)
+    ws = _workspace(nbytes, dev, workspace)
+    st = lib().moe_forward(ctypes.byref(desc), _ptr(x), _ptr(w_gate), _ptr(w13), _ptr(w2),
+                           int(top_k), ctypes.byref(sc) if sc is not None else None, _ptr(out),
+                           _ptr(ws), nbytes, _stream(dev, stream))
+    _check("moe_forward", st)
+    return out
+
+
+def moe_route(x: torch.Tensor, w_gate: torch.Tensor, top_k: int, *, stream=None):
+    """(logits [T,E] fp32, topk_ids [T,k] int32, topk_w [T,k] fp32)."""
+    dev = _dev(x, w_gate)
+    T, d = x.shape
+    E = w_gate.shape[0]
+    if w_gate.dtype != torch.float32 or w_gate.shape[1] != d:
+        raise ValueError("w_gate must be float32 [E, d]")
+    desc = make_desc(T, d, E, 64, _act_code(x), _act_code(x))
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    ids = torch.empty((T, top_k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, top_k), dtype=torch.float32, device=dev)
+    _check("moe_route", lib().moe_route(ctypes.byref(desc), _ptr(x), _ptr(w_gate), int(top_k),
+                                        _ptr(logits), _ptr(ids), _ptr(w), _stream(dev, stream)))
+    return logits, ids, w
+
+
+def moe_route_logits(logits: torch.Tensor, top_k: int, *, stream=None):
+    """(topk_ids [T,k] int32, topk_w [T,k] fp32) from given fp32 logits [T,E]."""
+    dev = _dev(logits)
+    if logits.dtype != torch.float32 or logits.dim() != 2:
+        raise ValueError("logits must be float32 [T, E]")
+    T, E = logits.shape
+    desc = make_desc(T, 64, E, 64, MOE_DTYPE_F32, MOE_DTYPE_F32)
+    ids = torch.empty((T, top_k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, top_k), dtype=torch.float32, device=dev)
+    _check("moe_route_logits", lib().moe_route_logits(ctypes.byref(desc), _ptr(logits), int(top_k),
+                                                      _ptr(ids), _ptr(w), _stream(dev, stream)))
+    return ids, w
+
+
+def moe_align(topk_ids: torch.Tensor, num_experts: int, *, block_m: int = 0, hidden: int = 64,
+              intermediate: int = 64, act_dtype: int = MOE_DTYPE_BF16,
+              weight_dtype: int = MOE_DTYPE_BF16, stream=None):
+    """Regroup slots by expert: (counts [E], sorted_ids [cap], block_expert [cap/B],
+    num_padded [1], block_m).  The default block_m depends on the whole
+    descriptor, so pass the layer's dims/dtypes to get the one moe_forward uses."""
+    dev = _dev(topk_ids)
+    if topk_ids.dtype != torch.int32 or topk_ids.dim() != 2:
+        raise ValueError("topk_ids must be int32 [T, k]")
+    T, k = topk_ids.shape
+    desc = make_desc(T, hidden, num_experts, intermediate, act_dtype, weight_dtype, block_m)
+    B, cap = moe_align_capacity(desc, k)
+    counts = torch.empty(num_experts, dtype=torch.int32, device=dev)
+    sorted_ids = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    block_expert = torch.empty(max(cap // B, 1), dtype=torch.int32, device=dev)
+    num_padded = torch.zeros(4, dtype=torch.int32, device=dev)
+    _check("moe_align", lib().moe_align(ctypes.byref(desc), _ptr(topk_ids), int(k), _ptr(counts),
+                                        _ptr(sorted_ids), _ptr(block_expert), _ptr(num_padded),
+                                        _stream(dev, stream)))
+    return counts, sorted_ids[:cap], block_expert[:cap // B], num_padded[:1], B
+
+
+def moe_expert_ffn(x: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, top_k: int,
+                   topk_w: torch.Tensor, sorted_ids: torch.Tensor, block_expert: torch.Tensor,
+                   num_padded: torch.Tensor, scales: Optional[Sequence[torch.Tensor]] = None,
+                   out: Optional[torch.Tensor] = None, *, block_m: int = 0,
+                   workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Expert networks + combine for a given routing (layout from moe_align
+    with the same block_m)."""
+    dev = _dev(x, w13, w2, topk_w, sorted_ids, block_expert, num_padded, out)
+    T, d, E, I = _shapes(x, None, w13, w2)
+    desc = make_desc(T, d, E, I, _act_code(x), _w_code(w13), block_m)
+    B, cap = moe_align_capacity(desc, top_k)
+    if sorted_ids.numel() < cap or block_expert.numel() < cap // B:
+        raise ValueError("sorted_ids / block_expert smaller than the layout capacity")
+    sc = _scales(w13, scales)
+    if out is None:
+        out = torch.empty((T, d), dtype=x.dtype, device=dev)
+    nbytes = moe_workspace_bytes(desc, top_k, False)
+    ws = _workspace(nbytes, dev, workspace)
+    st = lib().moe_expert_ffn(ctypes.byref(desc), _ptr(x), _ptr(w13), _ptr(w2), int(top_k),
+                              ctypes.byref(sc) if sc is not None else None, _ptr(topk_w),
+                              _ptr(sorted_ids), _ptr(block_expert), _ptr(num_padded), _ptr(out),
+                              _ptr(ws), nbytes, _stream(dev, stream))
+    _check("moe_expert_ffn", st)
+    return out
+
+
+def moe_timing_enable(enable: bool = True) -> None:
+    _check("moe_timing_enable", lib().moe_timing_enable(int(bool(enable))))
+
+
+def moe_timing_collect(reset: bool = True) -> dict:
+    """{kernel name: (total ms, launches)} for the kernels timed so far."""
+    ms = (ctypes.c_double * MOE_KERNEL_COUNT)()
+    n = (ctypes.c_int64 * MOE_KERNEL_COUNT)()
+    _check("moe_timing_collect", lib().moe_timing_collect(ms, n, int(bool(reset))))
+    return {moe_kernel_name(i): (ms[i], n[i]) for i in range(MOE_KERNEL_COUNT)}
+
+
+def moe_kernel_name(kind: int) -> str:
+    return lib().moe_kernel_name(int(kind)).decode()

@@ -1,0 +1,435 @@
+// C ABI of the fused MoE layer (declared in include/moe.h): argument
+// validation, workspace layout, launch policy and kernel timing.  Every
+// check runs on the host before the first HIP call.
+
+#include <algorithm>
+#include <mutex>
+#include <vector>
+
+#include "kernels.h"
+#include "moe.h"
+
+namespace {
+
+using moe::FfnArgs;
+
+constexpr int64_t kMaxDim = int64_t(1) << 20;
+constexpr int64_t kMaxSlots = int64_t(1) << 30;
+constexpr size_t kWsAlign = 256;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int act_bytes(int dt) { return dt == MOE_DTYPE_F32 ? 4 : 2; }
+
+// ------------------------------------------------------------ validation
+
+int check_desc(const moe_desc* d, int top_k) {
+  if (!d) return MOE_ERR_NULL_PTR;
+  if (d->reserved != 0) return MOE_ERR_BAD_ARG;
+  if (d->num_tokens < 0) return MOE_ERR_BAD_SHAPE;
+  if (d->hidden < 64 || d->hidden % 64 || d->hidden > kMaxDim) return MOE_ERR_BAD_SHAPE;
+  if (d->intermediate < 64 || d->intermediate % 64 || d->intermediate > kMaxDim)
+    return MOE_ERR_BAD_SHAPE;
+  if (d->num_experts < 1 || d->num_experts > moe::kMaxExperts) return MOE_ERR_BAD_SHAPE;
+  if (top_k < 1 || top_k > d->num_experts || top_k > moe::kMaxTopK) return MOE_ERR_BAD_TOPK;
+  if (d->num_tokens * top_k >= kMaxSlots) return MOE_ERR_BAD_SHAPE;
+  const bool pair_ok = (d->act_dtype == MOE_DTYPE_F32 && d->weight_dtype == MOE_DTYPE_F32) ||
+                       (d->act_dtype == MOE_DTYPE_BF16 && d->weight_dtype == MOE_DTYPE_BF16) ||
+                       (d->act_dtype == MOE_DTYPE_BF16 && d->weight_dtype == MOE_DTYPE_E4M3FN);
+  if (!pair_ok) return MOE_ERR_BAD_DTYPE;
+  const int bm = d->block_m;
+  if (bm != 0 && bm != 16 && bm != 32 && bm != 64 && bm != 128) return MOE_ERR_BAD_BLOCK_M;
+  return MOE_OK;
+}
+
+int check_scales(const moe_desc* d, const moe_scales* s) {
+  if (d->weight_dtype == MOE_DTYPE_E4M3FN) {
+    if (!s) return MOE_ERR_NULL_PTR;
+    if (s->reserved != 0) return MOE_ERR_BAD_ARG;
+    if (s->mode != MOE_SCALE_PER_TENSOR && s->mode != MOE_SCALE_PER_CHANNEL)
+      return MOE_ERR_BAD_DTYPE;
+    if (!s->w13 || !s->w2) return MOE_ERR_NULL_PTR;
+    if (!aligned16(s->w13) || !aligned16(s->w2)) return MOE_ERR_MISALIGNED;
+    return MOE_OK;
+  }
+  if (s && s->mode != MOE_SCALE_NONE) return MOE_ERR_BAD_DTYPE;
+  return MOE_OK;
+}
+
+int check_ptrs(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs)
+    if (!p) return MOE_ERR_NULL_PTR;
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOE_ERR_MISALIGNED;
+  return MOE_OK;
+}
+
+// ------------------------------------------------------------ launch plan
+
+struct Plan {
+  int T, d, E, I, k, A, B, cap;
+  int splits, ksplit;
+  int act, wdt;
+  // workspace offsets (bytes)
+  size_t logits, ids, gates, counts, num_padded, sorted, block_exp, h, y, total;
+};
+
+// Block size of the regrouped layout.  With B >= T every expert's tokens
+// fit one block (an expert holds at most one slot per token), so each
+// expert's weights are streamed exactly once; larger batches use 64-row
+// blocks.
+int default_block_m(const moe_desc* d) {
+  if (d->weight_dtype == MOE_DTYPE_F32) return 16;
+  const int64_t T = d->num_tokens;
+  if (T <= 16) return 16;
+  if (T <= 32) return 32;
+  return 64;
+}
+
+int64_t capacity(int64_t A, int64_t E, int64_t B) {
+  const int64_t n = A + (E < A ? E : A) * (B - 1);
+  return (n + B - 1) / B * B;
+}
+
+void make_plan(const moe_desc* d, int top_k, bool with_routing, Plan* p) {
+  p->T = static_cast<int>(d->num_tokens);
+  p->d = static_cast<int>(d->hidden);
+  p->E = static_cast<int>(d->num_experts);
+  p->I = static_cast<int>(d->intermediate);
+  p->k = top_k;
+  p->A = p->T * top_k;
+  p->B = d->block_m ? d->block_m : default_block_m(d);
+  p->cap = static_cast<int>(capacity(p->A, p->E, p->B));
+  p->act = d->act_dtype;
+  p->wdt = d->weight_dtype;
+
+  // Split W2's K range when there are too few workgroups to keep enough
+  // HBM requests in flight (small batches); the combine adds the splits in a
+  // fixed order.
+  p->splits = 1;
+  p->ksplit = p->I;
+  if (p->wdt != MOE_DTYPE_F32 && p->A > 0) {
+    const int kc = moe::ffn2_kchunk(p->I);
+    const int64_t blocks_est = std::min<int64_t>(p->cap / p->B, std::min(p->E, p->A) + p->A / p->B);
+    const int64_t wgs = blocks_est * (p->d / 128);
+    int s = 1;
+    while (s < 8 && wgs * s < 2048 && p->I / (2 * s) >= 4 * kc) s *= 2;
+    const int per = (p->I + s - 1) / s;
+    p->ksplit = (per + kc - 1) / kc * kc;
+    p->splits = (p->I + p->ksplit - 1) / p->ksplit;
+  }
+
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = round_up(off + bytes, kWsAlign);
+    return at;
+  };
+  const size_t T = p->T, E = p->E, A = p->A, cap = p->cap;
+  if (with_routing) {
+    p->logits = take(T * E * 4);
+    p->ids = take(A * 4);
+    p->gates = take(A * 4);
+    p->counts = take(E * 4);
+    p->num_padded = take(4);
+    p->sorted = take(cap * 4);
+    p->block_exp = take(cap / p->B * 4);
+  } else {
+    p->logits = p->ids = p->gates = p->counts = p->num_padded = p->sorted = p->block_exp = 0;
+  }
+  p->h = take(cap * static_cast<size_t>(p->I) * act_bytes(p->act));
+  p->y = take(static_cast<size_t>(p->splits) * A * p->d * 4);
+  p->total = p->T == 0 ? 0 : off;  // nothing runs for T = 0
+}
+
+// ------------------------------------------------------------ timing
+
+struct Pending {
+  int kind;
+  hipEvent_t start, stop;
+};
+
+std::mutex g_timing_mu;
+bool g_timing_on = false;
+std::vector<Pending> g_pending;
+std::vector<std::pair<hipEvent_t, hipEvent_t>> g_event_pool;
+double g_total_ms[MOE_KERNEL_COUNT] = {};
+int64_t g_launches[MOE_KERNEL_COUNT] = {};
+
+template <class F>
+hipError_t timed(int kind, hipStream_t s, F&& launch) {
+  bool on;
+  {
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    on = g_timing_on;
+  }
+  if (!on) return launch();
+  hipEvent_t a, b;
+  {
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    if (!g_event_pool.empty()) {
+      a = g_event_pool.back().first;
+      b = g_event_pool.back().second;
+      g_event_pool.pop_back();
+    } else {
+      if (hipEventCreate(&a) != hipSuccess) return hipErrorOutOfMemory;
+      if (hipEventCreate(&b) != hipSuccess) {
+        (void)hipEventDestroy(a);
+        return hipErrorOutOfMemory;
+      }
+    }
+  }
+  hipError_t err = hipEventRecord(a, s);
+  if (err == hipSuccess) err = launch();
+  if (err == hipSuccess) err = hipEventRecord(b, s);
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  if (err == hipSuccess)
+    g_pending.push_back({kind, a, b});
+  else
+    g_event_pool.push_back({a, b});
+  return err;
+}
+
+// ------------------------------------------------------------ launch sequences
+
+int to_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+FfnArgs ffn_args(const Plan& p, const void* x, const void* w13, const void* w2,
+                 const moe_scales* sc, const float* topk_w, const int32_t* sorted,
+                 const int32_t* block_exp, const int32_t* num_padded, void* out, char* ws) {
+  FfnArgs a{};
+  a.x = x;
+  a.w13 = w13;
+  a.w2 = w2;
+  const bool fp8 = p.wdt == MOE_DTYPE_E4M3FN;
+  a.s13 = fp8 ? sc->w13 : nullptr;
+  a.s2 = fp8 ? sc->w2 : nullptr;
+  a.scale_mode = fp8 ? sc->mode : moe::kScaleNone;
+  a.act_dtype = p.act;
+  a.w_dtype = p.wdt;
+  a.topk_w = topk_w;
+  a.sorted_ids = sorted;
+  a.block_expert = block_exp;
+  a.num_padded = num_padded;
+  a.h = ws + p.h;
+  a.y_part = reinterpret_cast<float*>(ws + p.y);
+  a.out = out;
+  a.T = p.T;
+  a.d = p.d;
+  a.E = p.E;
+  a.I = p.I;
+  a.k = p.k;
+  a.A = p.A;
+  a.B = p.B;
+  a.cap = p.cap;
+  a.splits = p.splits;
+  a.ksplit = p.ksplit;
+  return a;
+}
+
+hipError_t run_ffn(const FfnArgs& a, hipStream_t s) {
+  hipError_t e = timed(MOE_KERNEL_FFN13, s, [&] { return moe::launch_ffn13(a, s); });
+  if (e == hipSuccess) e = timed(MOE_KERNEL_FFN2, s, [&] { return moe::launch_ffn2(a, s); });
+  if (e == hipSuccess) e = timed(MOE_KERNEL_COMBINE, s, [&] { return moe::launch_combine(a, s); });
+  return e;
+}
+
+}  // namespace
+
+extern "C" {
+
+MOE_API const char* moe_strerror(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL_PTR: return "a required pointer is NULL";
+    case MOE_ERR_BAD_SHAPE: return "bad shape (d and I must be multiples of 64 in [64, 2^20], 1 <= E <= 1024, T >= 0, T*top_k < 2^30)";
+    case MOE_ERR_BAD_TOPK: return "top_k must be in [1, min(E, 64)]";
+    case MOE_ERR_BAD_DTYPE: return "unsupported dtype pair or scale mode (supported: f32/f32, bf16/bf16, bf16/e4m3fn with per-tensor or per-channel scales)";
+    case MOE_ERR_MISALIGNED: return "a pointer is not 16-byte aligned (workspace: 256-byte)";
+    case MOE_ERR_WORKSPACE: return "workspace is NULL or smaller than moe_workspace_bytes()";
+    case MOE_ERR_HIP: return "a HIP call or kernel launch failed";
+    case MOE_ERR_BAD_BLOCK_M: return "block_m must be 0, 16, 32, 64 or 128";
+    case MOE_ERR_BAD_ARG: return "invalid argument (reserved fields must be 0)";
+  }
+  return "unknown status";
+}
+
+MOE_API int moe_align_capacity(const moe_desc* desc, int top_k, int32_t* block_m,
+                               int64_t* cap) {
+  int st = check_desc(desc, top_k);
+  if (st) return st;
+  if (!block_m || !cap) return MOE_ERR_NULL_PTR;
+  Plan p;
+  make_plan(desc, top_k, true, &p);
+  *block_m = p.B;
+  *cap = p.cap;
+  return MOE_OK;
+}
+
+MOE_API int moe_workspace_bytes(const moe_desc* desc, int top_k, int with_routing,
+                                size_t* bytes) {
+  int st = check_desc(desc, top_k);
+  if (st) return st;
+  if (!bytes) return MOE_ERR_NULL_PTR;
+  Plan p;
+  make_plan(desc, top_k, with_routing != 0, &p);
+  *bytes = p.total;
+  return MOE_OK;
+}
+
+MOE_API int moe_route(const moe_desc* desc, const void* x, const float* w_gate, int top_k,
+                      float* logits, int32_t* topk_ids, float* topk_w, void* stream) {
+  int st = check_desc(desc, top_k);
+  if (st) return st;
+  const int T = static_cast<int>(desc->num_tokens);
+  if (T == 0) return MOE_OK;
+  if ((st = check_ptrs({x, w_gate, logits, topk_ids, topk_w}))) return st;
+  const int E = static_cast<int>(desc->num_experts), d = static_cast<int>(desc->hidden);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = timed(MOE_KERNEL_ROUTE_LOGITS, s, [&] {
+    return moe::launch_router_logits(x, desc->act_dtype, w_gate, logits, T, E, d, s);
+  });
+  if (e == hipSuccess)
+    e = timed(MOE_KERNEL_ROUTE_TOPK, s,
+              [&] { return moe::launch_router_topk(logits, topk_ids, topk_w, T, E, top_k, s); });
+  return to_status(e);
+}
+
+MOE_API int moe_route_logits(const moe_desc* desc, const float* logits, int top_k,
+                             int32_t* topk_ids, float* topk_w, void* stream) {
+  int st = check_desc(desc, top_k);
+  if (st) return st;
+  const int T = static_cast<int>(desc->num_tokens);
+  if (T == 0) return MOE_OK;
+  if ((st = check_ptrs({logits, topk_ids, topk_w}))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return to_status(timed(MOE_KERNEL_ROUTE_TOPK, s, [&] {
+    return moe::launch_router_topk(logits, topk_ids, topk_w, T,
+                                   static_cast<int>(desc->num_experts), top_k, s);
+  }));
+}
+
+MOE_API int moe_align(const moe_desc* desc, const int32_t* topk_ids, int top_k, int32_t* counts,
+                      int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded,
+                      void* stream) {
+  int st = check_desc(desc, top_k);
+  if (st) return st;
+  if (desc->num_tokens == 0) return MOE_OK;
+  if ((st = check_ptrs({topk_ids, counts, sorted_ids, block_expert, num_padded}))) return st;
+  Plan p;
+  make_plan(desc, top_k, true, &p);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return to_status(timed(MOE_KERNEL_ALIGN, s, [&] {
+    return moe::launch_align(topk_ids, p.A, p.E, p.B, p.cap, counts, sorted_ids, block_expert,
+                             num_padded, s);
+  }));
+}
+
+MOE_API int moe_expert_ffn(const moe_desc* desc, const void* x, const void* w13, const void* w2,
+                           int top_k, const moe_scales* scales, const float* topk_w,
+                           const int32_t* sorted_ids, const int32_t* block_expert,
+                           const int32_t* num_padded, void* out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  int st = check_desc(desc, top_k);
+  if (st) return st;
+  if (desc->num_tokens == 0) return MOE_OK;
+  if ((st = check_scales(desc, scales))) return st;
+  if ((st = check_ptrs({x, w13, w2, topk_w, sorted_ids, block_expert, num_padded, out})))
+    return st;
+  Plan p;
+  make_plan(desc, top_k, false, &p);
+  if (!workspace || workspace_bytes < p.total) return MOE_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % kWsAlign) return MOE_ERR_MISALIGNED;
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  FfnArgs a = ffn_args(p, x, w13, w2, scales, topk_w, sorted_ids, block_expert, num_padded, out,
+                       ws);
+  return to_status(run_ffn(a, s));
+}
+
+MOE_API int moe_forward(const moe_desc* desc, const void* x, const float* w_gate,
+                        const void* w13, const void* w2, int top_k, const moe_scales* scales,
+                        void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_desc(desc, top_k);
+  if (st) return st;
+  if (desc->num_tokens == 0) return MOE_OK;
+  if ((st = check_scales(desc, scales))) return st;
+  if ((st = check_ptrs({x, w_gate, w13, w2, out}))) return st;
+  Plan p;
+  make_plan(desc, top_k, true, &p);
+  if (!workspace || workspace_bytes < p.total) return MOE_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % kWsAlign) return MOE_ERR_MISALIGNED;
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* logits = reinterpret_cast<float*>(ws + p.logits);
+  int32_t* ids = reinterpret_cast<int32_t*>(ws + p.ids);
+  float* gates = reinterpret_cast<float*>(ws + p.gates);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + p.counts);
+  int32_t* num_padded = reinterpret_cast<int32_t*>(ws + p.num_padded);
+  int32_t* sorted = reinterpret_cast<int32_t*>(ws + p.sorted);
+  int32_t* block_exp = reinterpret_cast<int32_t*>(ws + p.block_exp);
+
+  hipError_t e = timed(MOE_KERNEL_ROUTE_LOGITS, s, [&] {
+    return moe::launch_router_logits(x, p.act, w_gate, logits, p.T, p.E, p.d, s);
+  });
+  if (e == hipSuccess)
+    e = timed(MOE_KERNEL_ROUTE_TOPK, s,
+              [&] { return moe::launch_router_topk(logits, ids, gates, p.T, p.E, p.k, s); });
+  if (e == hipSuccess)
+    e = timed(MOE_KERNEL_ALIGN, s, [&] {
+      return moe::launch_align(ids, p.A, p.E, p.B, p.cap, counts, sorted, block_exp, num_padded,
+                               s);
+    });
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  FfnArgs a = ffn_args(p, x, w13, w2, scales, gates, sorted, block_exp, num_padded, out, ws);
+  return to_status(run_ffn(a, s));
+}
+
+MOE_API int moe_timing_enable(int enable) {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  g_timing_on = enable != 0;
+  return MOE_OK;
+}
+
+MOE_API int moe_timing_collect(double* total_ms, int64_t* launches, int reset) {
+  std::vector<Pending> pend;
+  {
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    pend.swap(g_pending);
+  }
+  int status = MOE_OK;
+  std::vector<std::pair<int, float>> done;
+  for (const Pending& q : pend) {
+    float ms = 0.f;
+    if (hipEventSynchronize(q.stop) != hipSuccess ||
+        hipEventElapsedTime(&ms, q.start, q.stop) != hipSuccess)
+      status = MOE_ERR_HIP;
+    else
+      done.push_back({q.kind, ms});
+  }
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  for (const Pending& q : pend) g_event_pool.push_back({q.start, q.stop});
+  for (const auto& dk : done) {
+    g_total_ms[dk.first] += dk.second;
+    g_launches[dk.first] += 1;
+  }
+  for (int i = 0; i < MOE_KERNEL_COUNT; ++i) {
+    if (total_ms) total_ms[i] = g_total_ms[i];
+    if (launches) launches[i] = g_launches[i];
+    if (reset) {
+      g_total_ms[i] = 0.0;
+      g_launches[i] = 0;
+    }
+  }
+  return status;
+}
+
+MOE_API const char* moe_kernel_name(int kind) {
+  static const char* names[MOE_KERNEL_COUNT] = {"route_logits", "route_topk", "align",
+                                                "ffn13",        "ffn2",       "combine"};
+  return (kind >= 0 && kind < MOE_KERNEL_COUNT) ? names[kind] : "";
+}
+
+}  // extern "C"

@@ -1,0 +1,509 @@
+// Expert-side kernels of the fused MoE layer: the grouped W13 product with
+// SiLU(gate) * up fused in its epilogue, the grouped W2 product scaled by the
+// slot's gate, and the combine of each token's slots.
+//
+// Sources: the Hungarian news page "Az AWS új MoE-optimalizációkkal
+// gyorsítja a SageMaker AI-t", section "A fused MoE a számítási folyamat több
+// lépését egyesíti" (expert computation as one batched operation over all
+// experts) and section "FP8 esetén a Triton backend bizonyult gyorsabbnak"
+// (FP8 scaling, matrix product and aggregation of the experts' results done
+// in registers after one read from HBM, without intermediate round trips);
+// the French page "Ingénierie de kernels Mixture-of-Experts sur Amazon
+// SageMaker AI", second paragraph (decode: M = tokens is tiny, the expert
+// weight block is large) and the Hungarian page's section "A mátrixok
+// felcserélése jobban kihasználja a Hopper GPU-kat" (swap the operands so
+// the large expert dimension fills the matrix unit's fixed M side).
+//
+// CDNA4 design.  Every product is computed transposed, out^T = W . X^T: the
+// expert's weight rows (output channels) sit on the 16-row M side of
+// v_mfma_f32_16x16x32_bf16 and the block's tokens on its N side, 16 per
+// sub-tile.  Weights are read straight from HBM into registers -- each
+// weight element is used by exactly one wave, so LDS staging would only add
+// traffic -- and every wave reuses its weight fragments for all token
+// sub-tiles of its block, so an expert's weights are streamed once per
+// block.  e4m3fn weights are widened to bf16 in registers (exact) and their
+// fp32 scale is applied once per output channel in the epilogue.
+//
+// K-permutation: with a K chunk of KC elements, lane group g = lane/16 loads
+// KC/4 contiguous elements of its row (one or more 16-byte loads) and
+// fragment i of that run feeds MFMA i.  The B operand (tokens) is loaded
+// with the same mapping, so every MFMA pairs equal k on both sides while
+// each row is read in long contiguous runs.
+
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int kFfnThreads = 256;  // 4 waves
+
+// ------------------------------------------------------------ operand loads
+
+template <typename WT, int KC>
+struct RowChunk;  // one lane's KC/4 contiguous elements of one row
+
+template <int KC>
+struct RowChunk<bf16_t, KC> {
+  static constexpr int kLoads = KC / 32;  // 16-byte loads (8 bf16 each)
+  uint4 v[kLoads];
+  __device__ __forceinline__ void load(const bf16_t* p) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) v[i] = *reinterpret_cast<const uint4*>(p + 8 * i);
+  }
+  __device__ __forceinline__ bf16x8 frag(int i) const { return as_frag(v[i]); }
+};
+
+template <int KC>
+struct RowChunk<fp8_t, KC> {
+  static constexpr int kLoads = KC / 64;  // 16-byte loads (16 e4m3fn each)
+  uint4 v[kLoads];
+  __device__ __forceinline__ void load(const fp8_t* p) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) v[i] = *reinterpret_cast<const uint4*>(p + 16 * i);
+  }
+  // fragment i = elements 8i .. 8i+7 of the run
+  __device__ __forceinline__ bf16x8 frag(int i) const {
+    const uint4 q = v[i >> 1];
+    const uint32_t lo = (i & 1) ? q.z : q.x;
+    const uint32_t hi = (i & 1) ? q.w : q.y;
+    return as_frag(e4m3x8_to_frag_bits(lo, hi));
+  }
+};
+
+__device__ __forceinline__ float load_scale(const float* s, int mode, size_t matrix, size_t idx) {
+  if (mode == kScaleChannel) return s[idx];
+  if (mode == kScaleTensor) return s[matrix];
+  return 1.0f;
+}
+
+// Number of leading 16-row sub-tiles of block `blk` that hold at least one
+// real slot (valid slots form a prefix of every block).
+template <int NSUB>
+__device__ __forceinline__ int live_subtiles(const int32_t* blk, int A) {
+  int n = 0;
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s)
+    if (blk[16 * s] < A) n = s + 1;
+  return n;
+}
+
+// ------------------------------------------------------------ W13 + SiLU*mul
+//
+// Grid: x = row block b of the regrouped layout, y = group of 64 output
+// channels (4 waves x 16).  Each wave computes, for its 16 channels n, the
+// gate rows n and the up rows I + n against every token of the block and
+// writes h[row, n] = SiLU(s_g * gate) * (s_u * up) in bf16.
+
+template <typename WT, int NSUB, int KC>
+__global__ __launch_bounds__(kFfnThreads) void ffn13_kernel(
+    const bf16_t* __restrict__ x, const WT* __restrict__ w13, const float* __restrict__ s13,
+    int scale_mode, const int32_t* __restrict__ sorted_ids,
+    const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded,
+    bf16_t* __restrict__ h, int d, int I, int k, int A, int B) {
+  constexpr int NF = KC / 32;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  const int b = blockIdx.x;
+  if (b * B >= *num_padded) return;
+  const int e = block_expert[b];
+  const int n0 = (blockIdx.y * 4 + wave) * 16;
+  if (n0 >= I) return;
+  const int32_t* blk = sorted_ids + static_cast<size_t>(b) * B;
+  const int nsub = live_subtiles<NSUB>(blk, A);
+
+  const bf16_t* xrow[NSUB];
+  bool ok[NSUB];
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) {
+    const int f = s < nsub ? blk[16 * s + r16] : A;
+    ok[s] = f < A;
+    xrow[s] = x + static_cast<size_t>(ok[s] ? f / k : 0) * d;
+  }
+  const size_t two_i = 2 * static_cast<size_t>(I);
+  const WT* wg = w13 + (static_cast<size_t>(e) * two_i + n0 + r16) * d;
+  const WT* wu = w13 + (static_cast<size_t>(e) * two_i + I + n0 + r16) * d;
+
+  f32x4 accg[NSUB], accu[NSUB];
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) {
+    accg[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+    accu[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  RowChunk<WT, KC> ga, ua, gn, un;
+  const int koff = g * (KC / 4);
+  ga.load(wg + koff);
+  ua.load(wu + koff);
+  for (int kc = 0; kc < d; kc += KC) {
+    const bool more = kc + KC < d;
+    if (more) {  // prefetch the next chunk's weights while this one computes
+      gn.load(wg + kc + KC + koff);
+      un.load(wu + kc + KC + koff);
+    }
+    bf16x8 af[NF], bf[NF];
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+      af[i] = ga.frag(i);
+      bf[i] = ua.frag(i);
+    }
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      if (s < nsub) {
+        RowChunk<bf16_t, KC> xs;
+        if (ok[s]) {
+          xs.load(xrow[s] + kc + koff);
+        } else {
+#pragma unroll
+          for (int i = 0; i < RowChunk<bf16_t, KC>::kLoads; ++i) xs.v[i] = uint4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int i = 0; i < NF; ++i) {
+          const bf16x8 xf = xs.frag(i);
+          accg[s] = mfma16x16x32(af[i], xf, accg[s]);
+          accu[s] = mfma16x16x32(bf[i], xf, accu[s]);
+        }
+      }
+    }
+    if (more) {
+      ga = gn;
+      ua = un;
+    }
+  }
+
+  // Epilogue: lane holds token column r16, channels n0 + 4g .. n0 + 4g + 3.
+  const int nb = n0 + 4 * g;
+  float sg[4], su[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    sg[v] = load_scale(s13, scale_mode, e, static_cast<size_t>(e) * two_i + nb + v);
+    su[v] = load_scale(s13, scale_mode, e, static_cast<size_t>(e) * two_i + I + nb + v);
+  }
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) {
+    if (s < nsub) {
+      const size_t row = static_cast<size_t>(b) * B + 16 * s + r16;
+      uint32_t packed[2];
+#pragma unroll
+      for (int v = 0; v < 4; v += 2) {
+        const float h0 = silu(accg[s][v] * sg[v]) * (accu[s][v] * su[v]);
+        const float h1 = silu(accg[s][v + 1] * sg[v + 1]) * (accu[s][v + 1] * su[v + 1]);
+        packed[v / 2] = static_cast<uint32_t>(f32_to_bf16(h0)) |
+                        (static_cast<uint32_t>(f32_to_bf16(h1)) << 16);
+      }
+      *reinterpret_cast<uint2*>(h + row * I + nb) = uint2{packed[0], packed[1]};
+    }
+  }
+}
+
+// ------------------------------------------------------------ W2 + gate scale
+//
+// Grid: x = row block b, y = group of 4 * 16 * RN output channels of d,
+// z = split of the K = I range.  Each wave owns RN tiles of 16 channels and
+// writes y_part[z, f, n] = gate_f * s(n) * sum_{i in split} W2[e, n, i] h[r, i]
+// for every real slot f of the block; the combine sums the splits in a
+// fixed order, so the result is deterministic.
+
+template <typename WT, int NSUB, int KC, int RN>
+__global__ __launch_bounds__(kFfnThreads) void ffn2_kernel(
+    const bf16_t* __restrict__ h, const WT* __restrict__ w2, const float* __restrict__ s2,
+    int scale_mode, const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
+    const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded,
+    float* __restrict__ y_part, int d, int I, int A, int B, int ksplit) {
+  constexpr int NF = KC / 32;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  const int b = blockIdx.x;
+  if (b * B >= *num_padded) return;
+  const int e = block_expert[b];
+  const int n0 = (blockIdx.y * 4 + wave) * 16 * RN;
+  if (n0 >= d) return;
+  const int z = blockIdx.z;
+  const int k_begin = z * ksplit;
+  const int k_end = min(I, k_begin + ksplit);
+  const int32_t* blk = sorted_ids + static_cast<size_t>(b) * B;
+  const int nsub = live_subtiles<NSUB>(blk, A);
+
+  const bf16_t* hrow[NSUB];
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s)
+    hrow[s] = h + (static_cast<size_t>(b) * B + 16 * s + r16) * I;
+  const WT* wrow[RN];
+#pragma unroll
+  for (int rt = 0; rt < RN; ++rt)
+    wrow[rt] = w2 + (static_cast<size_t>(e) * d + n0 + rt * 16 + r16) * I;
+
+  f32x4 acc[NSUB][RN];
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+    for (int rt = 0; rt < RN; ++rt) acc[s][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int koff = g * (KC / 4);
+  RowChunk<WT, KC> wa[RN], wn[RN];
+  if (k_begin < k_end) {
+#pragma unroll
+    for (int rt = 0; rt < RN; ++rt) wa[rt].load(wrow[rt] + k_begin + koff);
+  }
+  for (int kc = k_begin; kc < k_end; kc += KC) {
+    const bool more = kc + KC < k_end;
+    if (more) {
+#pragma unroll
+      for (int rt = 0; rt < RN; ++rt) wn[rt].load(wrow[rt] + kc + KC + koff);
+    }
+    bf16x8 af[RN][NF];
+#pragma unroll
+    for (int rt = 0; rt < RN; ++rt)
+#pragma unroll
+      for (int i = 0; i < NF; ++i) af[rt][i] = wa[rt].frag(i);
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      if (s < nsub) {
+        RowChunk<bf16_t, KC> hs;
+        hs.load(hrow[s] + kc + koff);
+#pragma unroll
+        for (int i = 0; i < NF; ++i) {
+          const bf16x8 hf = hs.frag(i);
+#pragma unroll
+          for (int rt = 0; rt < RN; ++rt) acc[s][rt] = mfma16x16x32(af[rt][i], hf, acc[s][rt]);
+        }
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int rt = 0; rt < RN; ++rt) wa[rt] = wn[rt];
+    }
+  }
+
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) {
+    if (s < nsub) {
+      const int f = blk[16 * s + r16];
+      if (f < A) {
+        const float gate = topk_w[f];
+        float* yrow = y_part + (static_cast<size_t>(z) * A + f) * d;
+#pragma unroll
+        for (int rt = 0; rt < RN; ++rt) {
+          const int nb = n0 + rt * 16 + 4 * g;
+          float4 o;
+          o.x = acc[s][rt][0] * load_scale(s2, scale_mode, e, static_cast<size_t>(e) * d + nb) * gate;
+          o.y = acc[s][rt][1] * load_scale(s2, scale_mode, e, static_cast<size_t>(e) * d + nb + 1) * gate;
+          o.z = acc[s][rt][2] * load_scale(s2, scale_mode, e, static_cast<size_t>(e) * d + nb + 2) * gate;
+          o.w = acc[s][rt][3] * load_scale(s2, scale_mode, e, static_cast<size_t>(e) * d + nb + 3) * gate;
+          *reinterpret_cast<float4*>(yrow + nb) = o;
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------ fp32 path
+//
+// fp32 activations and weights: one thread per (regrouped row, channel),
+// fp32 fused multiply-adds.  Correctness path for fp32 models; the bf16 and
+// e4m3fn paths above are the tuned ones.
+
+__global__ __launch_bounds__(256) void ffn13_f32_kernel(
+    const float* __restrict__ x, const float* __restrict__ w13,
+    const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ block_expert,
+    const int32_t* __restrict__ num_padded, float* __restrict__ h, int d, int I, int k, int A,
+    int B) {
+  const int r = blockIdx.x;
+  const int n = blockIdx.y * 256 + threadIdx.x;
+  if (r >= *num_padded || n >= I) return;
+  const int f = sorted_ids[r];
+  float* hr = h + static_cast<size_t>(r) * I;
+  if (f >= A) {
+    hr[n] = 0.f;
+    return;
+  }
+  const int e = block_expert[r / B];
+  const float* xr = x + static_cast<size_t>(f / k) * d;
+  const float* wgr = w13 + (static_cast<size_t>(e) * 2 * I + n) * d;
+  const float* wur = w13 + (static_cast<size_t>(e) * 2 * I + I + n) * d;
+  float gsum = 0.f, usum = 0.f;
+  for (int i = 0; i < d; ++i) {
+    gsum = fmaf(wgr[i], xr[i], gsum);
+    usum = fmaf(wur[i], xr[i], usum);
+  }
+  hr[n] = silu(gsum) * usum;
+}
+
+__global__ __launch_bounds__(256) void ffn2_f32_kernel(
+    const float* __restrict__ h, const float* __restrict__ w2, const float* __restrict__ topk_w,
+    const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ block_expert,
+    const int32_t* __restrict__ num_padded, float* __restrict__ y, int d, int I, int A, int B) {
+  const int r = blockIdx.x;
+  const int n = blockIdx.y * 256 + threadIdx.x;
+  if (r >= *num_padded || n >= d) return;
+  const int f = sorted_ids[r];
+  if (f >= A) return;
+  const int e = block_expert[r / B];
+  const float* hr = h + static_cast<size_t>(r) * I;
+  const float* wr = w2 + (static_cast<size_t>(e) * d + n) * I;
+  float acc = 0.f;
+  for (int i = 0; i < I; ++i) acc = fmaf(wr[i], hr[i], acc);
+  y[static_cast<size_t>(f) * d + n] = acc * topk_w[f];
+}
+
+// ------------------------------------------------------------ combine
+//
+// out[t, n] = sum_j (sum_z y_part[z, t*k + j, n]) in rank order j, then
+// rounded to the activation dtype (bf16: round to nearest even).
+
+template <typename OT>
+__device__ __forceinline__ void store4(OT* p, float4 v);
+
+template <>
+__device__ __forceinline__ void store4<float>(float* p, float4 v) {
+  *reinterpret_cast<float4*>(p) = v;
+}
+
+template <>
+__device__ __forceinline__ void store4<bf16_t>(bf16_t* p, float4 v) {
+  const uint32_t lo = f32_to_bf16(v.x) | (static_cast<uint32_t>(f32_to_bf16(v.y)) << 16);
+  const uint32_t hi = f32_to_bf16(v.z) | (static_cast<uint32_t>(f32_to_bf16(v.w)) << 16);
+  *reinterpret_cast<uint2*>(p) = uint2{lo, hi};
+}
+
+template <typename OT>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_part,
+                                                      OT* __restrict__ out, int T, int d, int k,
+                                                      int splits, int A) {
+  const int groups = d / 4;
+  const size_t total = static_cast<size_t>(T) * groups;
+  for (size_t idx = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; idx < total;
+       idx += static_cast<size_t>(gridDim.x) * blockDim.x) {
+    const int t = static_cast<int>(idx / groups);
+    const int c = static_cast<int>(idx % groups) * 4;
+    float4 o = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+      const size_t f = static_cast<size_t>(t) * k + j;
+      float4 sj = {0.f, 0.f, 0.f, 0.f};
+      for (int z = 0; z < splits; ++z) {
+        const float4 p =
+            *reinterpret_cast<const float4*>(y_part + (static_cast<size_t>(z) * A + f) * d + c);
+        sj.x += p.x;
+        sj.y += p.y;
+        sj.z += p.z;
+        sj.w += p.w;
+      }
+      o.x += sj.x;
+      o.y += sj.y;
+      o.z += sj.z;
+      o.w += sj.w;
+    }
+    store4<OT>(out + static_cast<size_t>(t) * d + c, o);
+  }
+}
+
+// ------------------------------------------------------------ launchers
+
+int ffn2_kchunk(int I) { return (I % 128 == 0) ? 128 : 64; }
+
+namespace {
+
+template <typename WT, int NSUB>
+hipError_t ffn13_nsub(const FfnArgs& a, hipStream_t s) {
+  dim3 grid(a.cap / a.B, a.I / 64);
+  const auto* w = static_cast<const WT*>(a.w13);
+  const auto* x = static_cast<const bf16_t*>(a.x);
+  auto* h = static_cast<bf16_t*>(a.h);
+  if (a.d % 128 == 0)
+    ffn13_kernel<WT, NSUB, 128><<<grid, kFfnThreads, 0, s>>>(
+        x, w, a.s13, a.scale_mode, a.sorted_ids, a.block_expert, a.num_padded, h, a.d, a.I, a.k,
+        a.A, a.B);
+  else
+    ffn13_kernel<WT, NSUB, 64><<<grid, kFfnThreads, 0, s>>>(
+        x, w, a.s13, a.scale_mode, a.sorted_ids, a.block_expert, a.num_padded, h, a.d, a.I, a.k,
+        a.A, a.B);
+  return hipGetLastError();
+}
+
+template <typename WT>
+hipError_t ffn13_w(const FfnArgs& a, hipStream_t s) {
+  switch (a.B) {
+    case 16: return ffn13_nsub<WT, 1>(a, s);
+    case 32: return ffn13_nsub<WT, 2>(a, s);
+    case 64: return ffn13_nsub<WT, 4>(a, s);
+    case 128: return ffn13_nsub<WT, 8>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+constexpr int kFfn2RN = 2;
+
+template <typename WT, int NSUB>
+hipError_t ffn2_nsub(const FfnArgs& a, hipStream_t s) {
+  // 16 * kFfn2RN channels per wave; d is a multiple of 32, so a wave is either
+  // wholly inside [0, d) or wholly past it (and returns).
+  dim3 grid(a.cap / a.B, (a.d + 64 * kFfn2RN - 1) / (64 * kFfn2RN), a.splits);
+  const auto* w = static_cast<const WT*>(a.w2);
+  const auto* h = static_cast<const bf16_t*>(a.h);
+  if (ffn2_kchunk(a.I) == 128)
+    ffn2_kernel<WT, NSUB, 128, kFfn2RN><<<grid, kFfnThreads, 0, s>>>(
+        h, w, a.s2, a.scale_mode, a.topk_w, a.sorted_ids, a.block_expert, a.num_padded, a.y_part,
+        a.d, a.I, a.A, a.B, a.ksplit);
+  else
+    ffn2_kernel<WT, NSUB, 64, kFfn2RN><<<grid, kFfnThreads, 0, s>>>(
+        h, w, a.s2, a.scale_mode, a.topk_w, a.sorted_ids, a.block_expert, a.num_padded, a.y_part,
+        a.d, a.I, a.A, a.B, a.ksplit);
+  return hipGetLastError();
+}
+
+template <typename WT>
+hipError_t ffn2_w(const FfnArgs& a, hipStream_t s) {
+  switch (a.B) {
+    case 16: return ffn2_nsub<WT, 1>(a, s);
+    case 32: return ffn2_nsub<WT, 2>(a, s);
+    case 64: return ffn2_nsub<WT, 4>(a, s);
+    case 128: return ffn2_nsub<WT, 8>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_ffn13(const FfnArgs& a, hipStream_t s) {
+  if (a.w_dtype == kDtypeF32) {
+    dim3 grid(a.cap, (a.I + 255) / 256);
+    ffn13_f32_kernel<<<grid, 256, 0, s>>>(static_cast<const float*>(a.x),
+                                          static_cast<const float*>(a.w13), a.sorted_ids,
+                                          a.block_expert, a.num_padded,
+                                          static_cast<float*>(a.h), a.d, a.I, a.k, a.A, a.B);
+    return hipGetLastError();
+  }
+  if (a.w_dtype == kDtypeBF16) return ffn13_w<bf16_t>(a, s);
+  return ffn13_w<fp8_t>(a, s);
+}
+
+hipError_t launch_ffn2(const FfnArgs& a, hipStream_t s) {
+  if (a.w_dtype == kDtypeF32) {
+    dim3 grid(a.cap, (a.d + 255) / 256);
+    ffn2_f32_kernel<<<grid, 256, 0, s>>>(static_cast<const float*>(a.h),
+                                         static_cast<const float*>(a.w2), a.topk_w, a.sorted_ids,
+                                         a.block_expert, a.num_padded, a.y_part, a.d, a.I, a.A,
+                                         a.B);
+    return hipGetLastError();
+  }
+  if (a.w_dtype == kDtypeBF16) return ffn2_w<bf16_t>(a, s);
+  return ffn2_w<fp8_t>(a, s);
+}
+
+hipError_t launch_combine(const FfnArgs& a, hipStream_t s) {
+  const size_t total = static_cast<size_t>(a.T) * (a.d / 4);
+  const size_t want = (total + 255) / 256;
+  const int blocks = static_cast<int>(want < 65536 ? want : 65536);
+  if (a.act_dtype == kDtypeF32)
+    combine_kernel<float><<<blocks, 256, 0, s>>>(a.y_part, static_cast<float*>(a.out), a.T, a.d,
+                                                 a.k, a.splits, a.A);
+  else
+    combine_kernel<bf16_t><<<blocks, 256, 0, s>>>(a.y_part, static_cast<bf16_t*>(a.out), a.T,
+                                                  a.d, a.k, a.splits, a.A);
+  return hipGetLastError();
+}
+
+}  // namespace moe

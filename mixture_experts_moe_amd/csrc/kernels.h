@@ -1,0 +1,58 @@
+// Internal launchers of the fused MoE kernels (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Mirrors of the ABI dtype / scale codes (moe.h), for device code.
+constexpr int kDtypeF32 = 0;
+constexpr int kDtypeBF16 = 1;
+constexpr int kDtypeE4M3FN = 2;
+constexpr int kScaleNone = 0;
+constexpr int kScaleTensor = 1;
+constexpr int kScaleChannel = 2;
+
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 64;
+
+hipError_t launch_router_logits(const void* x, int act_dtype, const float* wg, float* logits,
+                                int T, int E, int d, hipStream_t s);
+hipError_t launch_router_topk(const float* logits, int32_t* ids, float* w, int T, int E, int k,
+                              hipStream_t s);
+hipError_t launch_align(const int32_t* ids, int A, int E, int B, int cap, int32_t* counts,
+                        int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded,
+                        hipStream_t s);
+
+// Everything the expert-side kernels need for one call.
+struct FfnArgs {
+  const void* x;            // [T, d] act dtype
+  const void* w13;          // [E, 2I, d]
+  const void* w2;           // [E, d, I]
+  const float* s13;         // scales or nullptr
+  const float* s2;
+  int scale_mode;
+  int act_dtype;
+  int w_dtype;
+  const float* topk_w;      // [T, k]
+  const int32_t* sorted_ids;    // [cap]
+  const int32_t* block_expert;  // [cap / B]
+  const int32_t* num_padded;    // [1]
+  void* h;                  // [cap, I] act dtype (workspace)
+  float* y_part;            // [splits, A, d] fp32 (workspace)
+  void* out;                // [T, d] act dtype
+  int T, d, E, I, k, A, B, cap;
+  int splits;               // split of W2's K (= I) range
+  int ksplit;               // K elements per split (multiple of the K chunk)
+};
+
+hipError_t launch_ffn13(const FfnArgs& a, hipStream_t s);
+hipError_t launch_ffn2(const FfnArgs& a, hipStream_t s);
+hipError_t launch_combine(const FfnArgs& a, hipStream_t s);
+
+// K-chunk the W2 kernel uses for a given I (the split length must be a
+// multiple of it).
+int ffn2_kchunk(int I);
+
+}  // namespace moe

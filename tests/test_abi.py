@@ -1,0 +1,172 @@
+"""C-ABI checks that need no GPU: the library loads, exports exactly the
+entry points include/moe.h declares, and rejects bad arguments on the host
+before any HIP call.  No compute call is made here."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from mixture_experts_moe_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B._LIB_PATH):
+        from mixture_experts_moe_amd import build
+        build.build()
+    return B.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"MOE_API\s+[\w\s\*]+?\b(moe_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_entry_points():
+    assert declared_functions() == sorted(B.ENTRY_POINTS)
+
+
+def test_library_exports_exactly_the_declared_symbols(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", B._LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = sorted({l.split()[-1] for l in out.splitlines() if " T " in l})
+    assert exported == declared_functions()
+
+
+def desc(T=4, d=128, E=8, I=128, act=B.MOE_DTYPE_BF16, w=B.MOE_DTYPE_BF16, bm=0):
+    return B.make_desc(T, d, E, I, act, w, bm)
+
+
+def ws_status(lib, dsc, k=2):
+    n = ctypes.c_size_t()
+    return lib.moe_workspace_bytes(ctypes.byref(dsc), k, 1, ctypes.byref(n))
+
+
+@pytest.mark.parametrize("kw,k,status", [
+    (dict(), 2, 0),
+    (dict(T=-1), 2, -2),
+    (dict(d=100), 2, -2),
+    (dict(d=0), 2, -2),
+    (dict(I=96), 2, -2),
+    (dict(E=0), 1, -2),
+    (dict(E=1025), 2, -2),
+    (dict(), 0, -3),
+    (dict(E=4), 5, -3),
+    (dict(E=128), 65, -3),
+    (dict(act=B.MOE_DTYPE_F32), 2, -4),
+    (dict(act=B.MOE_DTYPE_E4M3FN, w=B.MOE_DTYPE_E4M3FN), 2, -4),
+    (dict(act=B.MOE_DTYPE_F32, w=B.MOE_DTYPE_E4M3FN), 2, -4),
+    (dict(bm=48), 2, -8),
+    (dict(bm=256), 2, -8),
+    (dict(T=1 << 28), 8, -2),
+])
+def test_descriptor_validation(lib, kw, k, status):
+    assert ws_status(lib, desc(**kw), k) == status
+
+
+def test_reserved_field_and_null_descriptor(lib):
+    d = desc()
+    d.reserved = 1
+    assert ws_status(lib, d) == B.MOE_ERR_BAD_ARG if hasattr(B, "MOE_ERR_BAD_ARG") else -9
+    n = ctypes.c_size_t()
+    assert lib.moe_workspace_bytes(None, 2, 1, ctypes.byref(n)) == -1
+    assert lib.moe_workspace_bytes(ctypes.byref(desc()), 2, 1, None) == -1
+
+
+@pytest.mark.parametrize("T,E,k,bm", [(1, 8, 2, 16), (64, 8, 2, 64), (2048, 256, 8, 64),
+                                     (5, 3, 3, 32), (4096, 8, 2, 128)])
+def test_capacity_formula(lib, T, E, k, bm):
+    got_bm, cap = B.moe_align_capacity(desc(T=T, E=E, bm=bm), k)
+    A = T * k
+    assert got_bm == bm
+    assert cap == -(-(A + min(E, A) * (bm - 1)) // bm) * bm
+
+
+def test_default_block_covers_a_decode_batch(lib):
+    for T, want in [(1, 16), (8, 16), (16, 16), (17, 32), (32, 32), (64, 64)]:
+        assert B.moe_align_capacity(desc(T=T), 2)[0] == want
+    assert B.moe_align_capacity(desc(act=B.MOE_DTYPE_F32, w=B.MOE_DTYPE_F32), 2)[0] == 16
+
+
+def test_workspace_grows_with_tokens(lib):
+    sizes = [B.moe_workspace_bytes(desc(T=T), 2, True) for T in (1, 8, 64, 512)]
+    assert sizes == sorted(sizes) and sizes[0] > 0
+    assert B.moe_workspace_bytes(desc(T=0), 2, True) == 0
+    assert B.moe_workspace_bytes(desc(T=64), 2, False) < B.moe_workspace_bytes(desc(T=64), 2, True)
+
+
+FAKE = 1 << 20            # 16-byte aligned, never dereferenced: validation fails first
+
+
+def fwd(lib, dsc, k=2, x=FAKE, wg=FAKE, w13=FAKE, w2=FAKE, out=FAKE, ws=FAKE, nbytes=1 << 40,
+        scales=None):
+    return lib.moe_forward(ctypes.byref(dsc), x, wg, w13, w2, k,
+                           ctypes.byref(scales) if scales is not None else None, out, ws, nbytes,
+                           None)
+
+
+def test_forward_rejects_before_any_hip_call(lib):
+    d = desc()
+    assert fwd(lib, d, x=None) == -1
+    assert fwd(lib, d, wg=None) == -1
+    assert fwd(lib, d, out=None) == -1
+    assert fwd(lib, d, x=FAKE + 8) == -5
+    assert fwd(lib, d, w13=FAKE + 4) == -5
+    assert fwd(lib, d, ws=None) == -6
+    assert fwd(lib, d, nbytes=16) == -6
+    assert fwd(lib, d, ws=FAKE + 16) == -5        # workspace must be 256-byte aligned
+    assert fwd(lib, d, k=9) == -3
+    # T = 0 returns OK without looking at any pointer
+    assert fwd(lib, desc(T=0), x=None, wg=None, w13=None, w2=None, out=None, ws=None, nbytes=0) == 0
+
+
+def test_scale_validation(lib):
+    d8 = desc(w=B.MOE_DTYPE_E4M3FN)
+    assert fwd(lib, d8) == -1                                      # fp8 needs scales
+    sc = B.moe_scales(B.MOE_SCALE_NONE, 0, FAKE, FAKE)
+    assert fwd(lib, d8, scales=sc) == -4
+    sc = B.moe_scales(B.MOE_SCALE_PER_CHANNEL, 0, None, FAKE)
+    assert fwd(lib, d8, scales=sc) == -1
+    sc = B.moe_scales(B.MOE_SCALE_PER_TENSOR, 0, FAKE + 4, FAKE)
+    assert fwd(lib, d8, scales=sc) == -5
+    sc = B.moe_scales(B.MOE_SCALE_PER_CHANNEL, 1, FAKE, FAKE)
+    assert fwd(lib, d8, scales=sc) == -9
+    sc = B.moe_scales(B.MOE_SCALE_PER_CHANNEL, 0, FAKE, FAKE)
+    assert fwd(lib, desc(), scales=sc) == -4                       # bf16 weights take no scales
+
+
+def test_stage_entry_points_validate(lib):
+    d = desc()
+    P = ctypes.c_void_p
+    assert lib.moe_route(ctypes.byref(d), None, FAKE, 2, FAKE, FAKE, FAKE, None) == -1
+    assert lib.moe_route(ctypes.byref(d), FAKE, FAKE, 0, FAKE, FAKE, FAKE, None) == -3
+    assert lib.moe_route_logits(ctypes.byref(d), FAKE, 2, FAKE, None, None) == -1
+    assert lib.moe_align(ctypes.byref(d), FAKE, 2, FAKE, FAKE, FAKE + 2, FAKE, None) == -5
+    assert lib.moe_expert_ffn(ctypes.byref(d), FAKE, FAKE, FAKE, 2, None, FAKE, FAKE, FAKE, FAKE,
+                              FAKE, FAKE, 0, None) == -6
+    assert lib.moe_route(ctypes.byref(desc(T=0)), None, None, 2, None, None, None, None) == 0
+
+
+def test_strerror_and_names(lib):
+    for code in range(0, -10, -1):
+        s = B.strerror(code)
+        assert s and s != "unknown status"
+    assert B.strerror(-99) == "unknown status"
+    names = [B.moe_kernel_name(i) for i in range(B.MOE_KERNEL_COUNT)]
+    assert names == ["route_logits", "route_topk", "align", "ffn13", "ffn2", "combine"]
+    assert B.moe_kernel_name(99) == ""
+
+
+def test_timing_collect_without_work(lib):
+    B.moe_timing_enable(True)
+    t = B.moe_timing_collect(reset=True)
+    assert all(v == (0.0, 0) for v in t.values())
+    B.moe_timing_enable(False)

@@ -1,0 +1,270 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Routing and regrouping must match bit-exactly given identical logits; layer
+outputs must stay within the relative Frobenius error bound of their weight
+format (fp32 1e-5, bf16 2e-2, e4m3fn 6e-2) against the fp64 oracle, tokens
+whose k-th/(k+1)-th logit gap is below 1e-4 excluded.  Small cases run the
+oracle on every token; the full-size workloads run it on sampled tokens.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mixture_experts_moe_amd import binding as B
+from mixture_experts_moe_amd import synth
+from parity_utils import compare_layer, near_ties, subset, to_f64, with_x
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def note(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def loaded():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    B.lib()
+
+
+# ---------------------------------------------------------------- routing
+
+@pytest.mark.parametrize("T,E,k", [(1, 8, 2), (17, 8, 8), (300, 32, 4), (257, 256, 8),
+                                   (64, 1000, 64), (5, 1, 1), (130, 64, 1)])
+def test_topk_from_given_logits_is_exact(T, E, k):
+    note(f"topk T={T} E={E} k={k}")
+    g = torch.Generator().manual_seed(T * 1000 + E)
+    # coarse values: many exact ties, which must go to the lower index
+    lg = (torch.randint(-6, 7, (T, E), generator=g).float() / 4).contiguous()
+    ids, w = B.moe_route_logits(lg.to(DEV), k)
+    torch.cuda.synchronize()
+    ref_ids = oracle.select_topk(lg.double().numpy(), k)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    ref_w = oracle.gate_weights(lg.double().numpy(), ref_ids)
+    assert np.allclose(w.cpu().double().numpy(), ref_w, rtol=1e-6, atol=0)
+
+
+@pytest.mark.parametrize("wl,T", [("tiny_fp32", 16), ("decode_bf16", 64), ("fp8", 100), ("skew", 512)])
+def test_router_logits_and_selection(wl, T):
+    note(f"route {wl} T={T}")
+    cfg = synth.WORKLOADS[wl]
+    x = synth.make_x(T, cfg["d"], cfg["act"], cfg["x_std"], 0, DEV, skew=cfg["skew"])
+    wg = torch.randn((cfg["E"], cfg["d"]), generator=torch.Generator(DEV).manual_seed(5),
+                     device=DEV) * 0.02
+    if cfg["skew"]:
+        wg[:, 0] = synth.skew_biases(cfg["E"]).to(DEV)
+    logits, ids, w = B.moe_route(x, wg, cfg["k"])
+    torch.cuda.synchronize()
+    xv = to_f64(x)
+    wv = wg.cpu().numpy()
+    ref = oracle.router_logits(xv, wv)
+    bound = 1e-5 * (np.abs(xv) @ np.abs(wv.astype(np.float64)).T) + 1e-30
+    got = logits.cpu().double().numpy()
+    assert np.all(np.abs(got - ref) <= bound)
+    # selection and gates given the GPU's own logits: exact
+    ref_ids = oracle.select_topk(got, cfg["k"])
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    assert np.allclose(w.cpu().double().numpy(), oracle.gate_weights(got, ref_ids), rtol=1e-6, atol=0)
+
+
+# ---------------------------------------------------------------- align
+
+def _random_ids(T, E, k, seed, idle=()):
+    rng = np.random.default_rng(seed)
+    live = np.array([e for e in range(E) if e not in idle])
+    return np.stack([rng.permutation(live)[:k] for _ in range(T)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("T,E,k,bm", [(1, 8, 2, 16), (64, 8, 2, 64), (33, 8, 2, 16),
+                                      (300, 32, 4, 32), (2048, 256, 8, 64), (1000, 8, 2, 128),
+                                      (7, 300, 5, 16), (4096, 8, 2, 128)])
+def test_align_is_exact(T, E, k, bm):
+    note(f"align T={T} E={E} k={k} B={bm}")
+    idle = (3, 5) if E > 5 + k else ()
+    ids = _random_ids(T, E, k, T + E, idle)
+    counts, sorted_ids, block_expert, num_padded, got_bm = B.moe_align(
+        torch.from_numpy(ids).to(DEV), E, block_m=bm)
+    torch.cuda.synchronize()
+    assert got_bm == bm
+    ref = oracle.align(ids, E, bm)
+    assert np.array_equal(counts.cpu().numpy(), ref["counts"])
+    assert np.array_equal(sorted_ids.cpu().numpy(), ref["sorted_ids"])
+    assert np.array_equal(block_expert.cpu().numpy(), ref["block_expert"])
+    assert int(num_padded.item()) == ref["num_padded"]
+
+
+def test_align_is_deterministic():
+    ids = torch.from_numpy(_random_ids(2048, 256, 8, 7)).to(DEV)
+    a = B.moe_align(ids, 256, block_m=64)
+    b = B.moe_align(ids, 256, block_m=64)
+    torch.cuda.synchronize()
+    for u, v in zip(a[:4], b[:4]):
+        assert torch.equal(u, v)
+
+
+# ---------------------------------------------------------------- layer, small
+
+SMALL = [
+    # name, workload overrides, T, block_m
+    ("tiny_fp32", dict(), 16, 0),
+    ("tiny_fp32", dict(), 16, 64),
+    ("tiny_fp32", dict(), 37, 16),
+    ("bf16_ragged", dict(workload="decode_bf16", d=512, I=448, x_std=1.0), 1, 0),
+    ("bf16_ragged", dict(workload="decode_bf16", d=512, I=448, x_std=1.0), 5, 0),
+    ("bf16_ragged", dict(workload="decode_bf16", d=512, I=448, x_std=1.0), 33, 0),
+    ("bf16_ragged", dict(workload="decode_bf16", d=512, I=448, x_std=1.0), 64, 0),
+    ("bf16_ragged", dict(workload="decode_bf16", d=512, I=448, x_std=1.0), 257, 0),
+    ("bf16_ragged", dict(workload="decode_bf16", d=512, I=448, x_std=1.0), 257, 16),
+    ("bf16_ragged", dict(workload="decode_bf16", d=512, I=448, x_std=1.0), 257, 128),
+    ("bf16_d320", dict(workload="decode_bf16", d=320, I=192, x_std=1.0), 100, 32),
+    ("bf16_kE", dict(workload="decode_bf16", d=128, I=128, E=8, k=8, x_std=1.0), 40, 0),
+    ("bf16_E1", dict(workload="decode_bf16", d=256, I=128, E=1, k=1, x_std=1.0), 37, 0),
+    ("fp8_channel", dict(workload="fp8", d=256, I=192, E=16, k=4), 3, 0),
+    ("fp8_channel", dict(workload="fp8", d=256, I=192, E=16, k=4), 64, 0),
+    ("fp8_channel", dict(workload="fp8", d=256, I=192, E=16, k=4), 200, 128),
+    ("fp8_tensor", dict(workload="fp8", d=256, I=192, E=16, k=4, scale_mode="tensor"), 50, 0),
+    ("skew_small", dict(workload="skew", d=192, I=128), 300, 0),
+]
+
+
+@pytest.mark.parametrize("name,over,T,bm", SMALL, ids=[f"{c[0]}-T{c[2]}-B{c[3]}" for c in SMALL])
+def test_layer_small(name, over, T, bm):
+    note(f"layer {name} T={T} B={bm}")
+    over = dict(over)
+    wl = over.pop("workload", name)
+    inp = synth.make_inputs(wl, T=T, device=DEV, **over)
+    sc = (inp.s13, inp.s2) if inp.w == "e4m3fn" else None
+    out = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, sc, block_m=bm)
+    _, ids, _ = B.moe_route(inp.x, inp.w_gate, inp.top_k)
+    torch.cuda.synchronize()
+    r = compare_layer(inp, out, ids)
+    note(f"  rel_err={r['rel_err']:.3e} excluded={r['excluded']}")
+
+
+def test_zero_tokens_is_a_noop():
+    inp = synth.make_inputs("decode_bf16", T=0, device=DEV, d=128, I=128)
+    out = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 128)
+
+
+def test_forward_equals_stage_composition_and_is_deterministic():
+    inp = synth.make_inputs("fp8", T=77, device=DEV, d=256, I=192, E=16, k=4)
+    sc = (inp.s13, inp.s2)
+    out1 = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, sc)
+    out2 = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, sc)
+    _, ids, w = B.moe_route(inp.x, inp.w_gate, inp.top_k)
+    counts, sorted_ids, block_expert, num_padded, bm = B.moe_align(
+        ids, inp.E, hidden=inp.d, intermediate=inp.I, weight_dtype=B.MOE_DTYPE_E4M3FN)
+    out3 = B.moe_expert_ffn(inp.x, inp.w13, inp.w2, inp.top_k, w, sorted_ids, block_expert,
+                            num_padded, sc)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2)
+    assert torch.equal(out1, out3)
+
+
+def test_output_guard_bands_untouched():
+    inp = synth.make_inputs("decode_bf16", T=33, device=DEV, d=256, I=128, x_std=1.0)
+    pad = 64
+    buf = torch.full((pad + inp.T * inp.d + pad,), 12345, dtype=torch.int16, device=DEV)
+    out = buf[pad:pad + inp.T * inp.d].view(torch.bfloat16).view(inp.T, inp.d)
+    B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:pad] == 12345) and torch.all(buf[-pad:] == 12345)
+    assert torch.isfinite(out.float()).all()
+
+
+def test_kernel_timing_counts_launches():
+    inp = synth.make_inputs("decode_bf16", T=8, device=DEV, d=256, I=128, x_std=1.0)
+    B.moe_timing_collect(reset=True)
+    B.moe_timing_enable(True)
+    try:
+        for _ in range(3):
+            B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k)
+        t = B.moe_timing_collect(reset=True)
+    finally:
+        B.moe_timing_enable(False)
+    for name in ("route_logits", "route_topk", "align", "ffn13", "ffn2", "combine"):
+        ms, n = t[name]
+        assert n == 3 and ms > 0, (name, t[name])
+
+
+# ---------------------------------------------------------------- full-size workloads
+
+@pytest.fixture(scope="module")
+def decode_inputs():
+    return synth.make_inputs("decode_bf16", T=64, device=DEV)
+
+
+def _routing_exact(inp, ids, logits):
+    """Given the GPU's logits, its selection and regrouping are exact."""
+    got = logits.cpu().double().numpy()
+    ref_ids = oracle.select_topk(got, inp.top_k)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    desc = B.make_desc(inp.T, inp.d, inp.E, inp.I, B._act_code(inp.x), B._w_code(inp.w13))
+    counts, sorted_ids, block_expert, num_padded, bm = B.moe_align(
+        ids, inp.E, hidden=inp.d, intermediate=inp.I, act_dtype=desc.act_dtype,
+        weight_dtype=desc.weight_dtype)
+    ref = oracle.align(ref_ids, inp.E, bm)
+    assert np.array_equal(counts.cpu().numpy(), ref["counts"])
+    assert np.array_equal(sorted_ids.cpu().numpy(), ref["sorted_ids"])
+    assert np.array_equal(block_expert.cpu().numpy(), ref["block_expert"])
+    assert int(num_padded.item()) == ref["num_padded"]
+    return ref
+
+
+def _full_case(inp, tokens):
+    sc = (inp.s13, inp.s2) if inp.w == "e4m3fn" else None
+    out = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, sc)
+    logits, ids, _ = B.moe_route(inp.x, inp.w_gate, inp.top_k)
+    torch.cuda.synchronize()
+    _routing_exact(inp, ids, logits)
+    r = compare_layer(inp, out, ids, tokens=tokens)
+    note(f"  rel_err={r['rel_err']:.3e} compared={r['compared']} excluded={r['excluded']}")
+
+
+@pytest.mark.parametrize("T", [1, 8, 32, 64])
+def test_decode_bf16_full_size(decode_inputs, T):
+    note(f"decode_bf16 full size T={T}")
+    cfg = synth.WORKLOADS["decode_bf16"]
+    inp = with_x(decode_inputs, synth.make_x(T, cfg["d"], "bf16", cfg["x_std"], 0, DEV))
+    tokens = np.arange(T) if T <= 8 else np.linspace(0, T - 1, 8).astype(int)
+    _full_case(inp, tokens)
+
+
+def test_decode_shape_from_the_pages(decode_inputs):
+    """One token through a 4096 x 8192 expert block (2I = 8192): the decode
+    product printed on the French summary page (tests/golden/decode_shape.json)."""
+    import json, os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "decode_shape.json")))
+    inp = synth.make_inputs("decode_bf16", T=g["M_tokens"], device=DEV, d=g["K_hidden"],
+                            I=g["N_expert_out"] // 2, E=4, k=2)
+    _full_case(inp, np.arange(inp.T))
+
+
+def test_prefill_bf16_full_size():
+    note("prefill_bf16 full size T=4096")
+    inp = synth.make_inputs("prefill_bf16", device=DEV)
+    _full_case(inp, np.linspace(0, inp.T - 1, 12).astype(int))
+
+
+@pytest.mark.parametrize("T", [64, 2048])
+def test_fp8_full_size(T):
+    note(f"fp8 full size T={T}")
+    inp = synth.make_inputs("fp8", T=T, device=DEV)
+    _full_case(inp, np.linspace(0, T - 1, 4).astype(int))
+
+
+def test_skew_full_size():
+    note("skew full size T=512")
+    inp = synth.make_inputs("skew", device=DEV)
+    _full_case(inp, None)
+    _, ids, _ = B.moe_route(inp.x, inp.w_gate, inp.top_k)
+    counts = np.bincount(ids.cpu().numpy().ravel(), minlength=inp.E)
+    assert all(counts[e] == 0 for e in synth.SKEW_IDLE_EXPERTS)
+    note(f"  skew counts {counts.tolist()}")
