@@ -1,0 +1,339 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused MoE layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_bf16]
+
+A step is one pass of the whole layer (route, regroup, W13 + SiLU*mul,
+W2 + gate scale, combine: one moe_forward call) over every batch of the
+workload, back to back; for the default workload (decode bf16, Mixtral-like
+shapes d=4096, E=8, top-2, I=14336) that is T = 1, 8, 32 and 64 tokens.
+Inputs are seeded synthetic tensors already resident in HBM.  Two copies of
+the weights alternate between consecutive forwards, so no forward finds the
+previous one's weights in the 256 MB Infinity Cache.
+
+Prints one JSON line on stdout: tokens/s over the K timed steps, the
+dominant kernel's achieved HBM bandwidth against the 8 TB/s peak (its
+average duration measured with HIP events recorded on its own stream inside
+the timed region), and the CPU oracle timed on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fused-MoE tokens/s + achieved HBM GB/s (decode) / MFMA TFLOP/s (prefill)"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "e4m3fn": 2500.0, "f32": 157.3}  # W8A16 computes in bf16
+WORKLOAD_BATCHES = {
+    "decode_bf16": (1, 8, 32, 64),
+    "prefill_bf16": (4096,),
+    "fp8": (64, 2048),
+    "skew": (512,),
+    "tiny_fp32": (16,),
+}
+# Oracle sample per workload: (batch T, number of its tokens run on the CPU)
+CPU_SAMPLE = {"decode_bf16": (64, 64), "prefill_bf16": (4096, 16), "fp8": (2048, 4),
+              "skew": (512, 64), "tiny_fp32": (16, 16)}
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_bf16", choices=sorted(WORKLOAD_BATCHES))
+    ap.add_argument("--batches", default=None, help="comma-separated T values (default: the workload's)")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-breakdown", action="store_true", help="skip the per-kernel breakdown pass")
+    ap.add_argument("--block-m", type=int, default=0, help="regrouping block size (0 = library default)")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="instead of the layer, run a plain device copy of this many bytes "
+                         "(reference reading for HBM traffic counters)")
+    return ap.parse_args()
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mixture_experts_moe_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def copy_calibration(nbytes: int, reps: int = 5) -> None:
+    import torch
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
+
+
+def alg_work(inp, ids, k) -> dict:
+    """Algorithmic bytes and flops of one forward, from the realised routing.
+    Bytes: weights (and fp8 scales) of the touched experts, W_gate, x, out.
+    ffn13 bytes: touched experts' W13 (+ scales), x, h written for real slots."""
+    import torch
+    T, d, E, I = inp.T, inp.d, inp.E, inp.I
+    wb = {"f32": 4, "bf16": 2, "e4m3fn": 1}[inp.w]
+    ab = 4 if inp.act == "f32" else 2
+    touched = int(torch.unique(ids).numel()) if T else 0
+    A = T * k
+    sc13 = 2 * I * 4 if inp.w == "e4m3fn" else 0
+    sc2 = d * 4 if inp.w == "e4m3fn" else 0
+    w13 = touched * (2 * I * d * wb + sc13)
+    w2 = touched * (d * I * wb + sc2)
+    return {
+        "T": T, "touched_experts": touched,
+        "bytes": w13 + w2 + E * d * 4 + T * d * 2 * ab,
+        "flops": A * 6 * d * I + 2 * T * d * E,
+        "ffn13_bytes": w13 + T * d * ab + A * I * ab,
+        "ffn13_flops": A * 4 * d * I,
+    }
+
+
+def cpu_baseline(inp_T, k_sample: int, workload: str) -> dict:
+    """The oracle as it stands, on `k_sample` tokens of the batch, timed on
+    this host's cores."""
+    import numpy as np
+    import threadpoolctl
+
+    import oracle
+    from mixture_experts_moe_amd import synth
+    from dataclasses import replace
+    import torch
+
+    tokens = torch.linspace(0, inp_T.T - 1, k_sample).round().long().to(inp_T.x.device)
+    sub = replace(inp_T, x=inp_T.x.index_select(0, tokens).contiguous())
+    kw = synth.to_oracle(sub)
+    # fetch the experts the sample touches before timing (host copies are not oracle work)
+    lg = oracle.router_logits(oracle.decode_bf16(kw["x"]) if kw["act_fmt"] == "bf16"
+                              else kw["x"].astype(np.float64), kw["w_gate"])
+    for e in np.unique(oracle.select_topk(lg, sub.top_k)):
+        kw["w13"][e]
+        kw["w2"][e]
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    t0 = time.perf_counter()
+    oracle.moe_forward(**kw, block_m=16)
+    dt = time.perf_counter() - t0
+    return {"value": round(k_sample / dt, 3), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{workload}: {k_sample} of the T={inp_T.T} batch's tokens through the "
+                      f"fp64 NumPy per-expert-loop oracle, one forward, {dt:.2f} s "
+                      f"({len(os.sched_getaffinity(0))} host cores visible, BLAS threads {threads})"}
+
+
+def main() -> int:
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+              "(the layer is single-GPU; multi-GPU sharding is design only).", file=sys.stderr)
+        return 2
+    import torch
+
+    if args.copy_bytes:
+        copy_calibration(args.copy_bytes)
+        return 0
+
+    from mixture_experts_moe_amd import binding as B
+    from mixture_experts_moe_amd import synth
+    from dataclasses import replace
+
+    if not os.path.exists(B._LIB_PATH):
+        log("libmoe.so missing: building")
+        from mixture_experts_moe_amd import build
+        build.build()
+    B.lib()
+
+    wl = args.workload
+    batches = tuple(int(t) for t in args.batches.split(",")) if args.batches else WORKLOAD_BATCHES[wl]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"generating {wl} inputs, batches {batches}")
+    base = synth.make_inputs(wl, T=batches[0], device=dev)
+    cfg = synth.WORKLOADS[wl]
+    inputs = [replace(base, x=synth.make_x(T, base.d, base.act, cfg["x_std"], 0, dev, skew=cfg["skew"]))
+              for T in batches]
+    weight_bytes = base.w13.numel() * base.w13.element_size() + base.w2.numel() * base.w2.element_size()
+    copies = [(base.w13, base.w2)]
+    if weight_bytes > (64 << 20):
+        copies.append((base.w13.clone(), base.w2.clone()))
+    sc = (base.s13, base.s2) if base.w == "e4m3fn" else None
+    outs = [torch.empty_like(i.x) for i in inputs]
+    wss = []
+    for i in inputs:
+        desc = B.make_desc(i.T, i.d, i.E, i.I, B._act_code(i.x), B._w_code(i.w13))
+        desc.block_m = args.block_m
+        wss.append(torch.empty(max(B.moe_workspace_bytes(desc, i.top_k, True), 1), dtype=torch.uint8, device=dev))
+    torch.cuda.synchronize()
+    log(f"weights {weight_bytes / 1e9:.2f} GB x {len(copies)} copies")
+
+    counter = [0]
+
+    def step():
+        for bi, i in enumerate(inputs):
+            w13, w2 = copies[counter[0] % len(copies)]
+            counter[0] += 1
+            B.moe_forward(i.x, i.w_gate, w13, w2, i.top_k, sc, outs[bi], block_m=args.block_m,
+                          workspace=wss[bi])
+
+    # realised routing -> algorithmic work per forward
+    work = []
+    for i in inputs:
+        _, ids, _ = B.moe_route(i.x, i.w_gate, i.top_k)
+        work.append(alg_work(i, ids, i.top_k))
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done; timing {args.steps} steps")
+
+    # timed region: HIP events bracket only the dominant kernel (ffn13), on its stream
+    B.moe_timing_collect(reset=True)
+    B.moe_timing_enable(["ffn13"])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    B.moe_timing_enable(False)
+    tim = B.moe_timing_collect(reset=True)
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    tokens = sum(batches)
+    value = tokens / (ms_per_step / 1e3)
+    ffn13_ms, ffn13_n = tim["ffn13"]
+    log(f"{ms_per_step:.3f} ms/step, {value:,.0f} tokens/s; ffn13 {ffn13_ms / max(ffn13_n, 1) * 1e3:.1f} us avg")
+
+    bytes_step = sum(w["bytes"] for w in work)
+    flops_step = sum(w["flops"] for w in work)
+    f13_bytes_step = sum(w["ffn13_bytes"] for w in work)
+    f13_flops_step = sum(w["ffn13_flops"] for w in work)
+    f13_ms_step = ffn13_ms / args.steps
+    mfma_bound = wl == "prefill_bf16"
+    if mfma_bound:
+        peak = MFMA_PEAK_TFLOPS[base.w]
+        achieved = f13_flops_step / (f13_ms_step / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4)}
+    else:
+        achieved = f13_bytes_step / (f13_ms_step / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof["kernel"] = "ffn13 (grouped W13 + SiLU*mul)"
+    roof["avg_launch_us"] = round(ffn13_ms / max(ffn13_n, 1) * 1e3, 2)
+    roof["launches"] = ffn13_n
+    roof["traffic"] = load_traffic(wl)
+
+    breakdown = None
+    per_batch = []
+    if not args.no_breakdown:
+        # second pass, same number of forwards per batch: every kernel kind
+        # timed with HIP events, batch by batch, plus each whole forward
+        breakdown = {}
+        for bi, (i, w) in enumerate(zip(inputs, work)):
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            B.moe_timing_collect(reset=True)
+            B.moe_timing_enable(True)
+            fw = 0.0
+            for _ in range(args.steps):
+                w13, w2 = copies[counter[0] % len(copies)]
+                counter[0] += 1
+                ev0.record()
+                B.moe_forward(i.x, i.w_gate, w13, w2, i.top_k, sc, outs[bi], block_m=args.block_m,
+                              workspace=wss[bi])
+                ev1.record()
+                torch.cuda.synchronize()
+                fw += ev0.elapsed_time(ev1)
+            B.moe_timing_enable(False)
+            t2 = B.moe_timing_collect(reset=True)
+            kern = {k: round(v[0] / args.steps * 1e3, 2) for k, v in t2.items()}
+            for k, v in kern.items():
+                breakdown[k] = round(breakdown.get(k, 0.0) + v, 2)
+            ms = fw / args.steps
+            f13_us = kern["ffn13"]
+            per_batch.append({
+                "T": w["T"], "us": round(ms * 1e3, 1), "tokens_per_s": round(w["T"] / (ms / 1e3), 1),
+                "touched_experts": w["touched_experts"],
+                "layer_hbm_GBps": round(w["bytes"] / (ms / 1e3) / 1e9, 1),
+                "layer_hbm_frac": round(w["bytes"] / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                "layer_TFLOPs": round(w["flops"] / (ms / 1e3) / 1e12, 2),
+                "ffn13_hbm_frac": round(w["ffn13_bytes"] / (f13_us / 1e6) / 1e9 / HBM_PEAK_GBS, 4) if f13_us else None,
+                "ffn13_TFLOPs": round(w["ffn13_flops"] / (f13_us / 1e6) / 1e12, 2) if f13_us else None,
+                "kernel_us": kern,
+            })
+
+    cpu = None
+    if not args.no_cpu_baseline and wl in CPU_SAMPLE:
+        T_s, n_s = CPU_SAMPLE[wl]
+        src = next((i for i in inputs if i.T == T_s), inputs[-1])
+        log(f"timing the CPU oracle on {min(n_s, src.T)} tokens of T={src.T}")
+        cpu = cpu_baseline(src, min(n_s, src.T), wl)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if base.w == "f32" else "bf16",
+        "data": "synthetic (seeded Gaussian inputs and random-init weights; no trained model)",
+        "config": {
+            "workload": wl,
+            "batches_T": list(batches),
+            "hidden": base.d, "experts": base.E, "top_k": base.top_k, "intermediate": base.I,
+            "act": base.act, "weights": base.w,
+            "tokens_per_step": tokens,
+            "alg_bytes_per_step": bytes_step,
+            "alg_flops_per_step": flops_step,
+            "layer_hbm_frac": round(bytes_step / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "layer_TFLOPs": round(flops_step / (ms_per_step / 1e3) / 1e12, 2),
+            "weight_copies_rotated": len(copies),
+            "kernel_source_sha": kernel_source_sha(),
+        },
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "per_batch": per_batch,
+        "kernel_us_per_step": breakdown,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def load_traffic(workload: str):
+    """HBM bytes per ffn13 launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs,
+    if they were taken on the current kernel sources (else null)."""
+    path = os.path.join(ROOT, "profiles", f"ffn13_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+if __name__ == "__main__":
+    sys.exit(main())

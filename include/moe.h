@@ -48,7 +48,8 @@
  * E4M3FN weights are OCP e4m3fn bytes; value = decoded byte * fp32 scale, the
  * scale given per output channel (s13 [E, 2I], s2 [E, d]) or per expert
  * matrix (s13 [E], s2 [E]).  Activations stay bf16 (weight-only FP8).
- * Limits: d and I multiples of 64; 1 <= E <= 1024; 1 <= top_k <= min(E, 64);
+ * Limits: d and I multiples of 64 in [64, 2^19]; 1 <= E <= 1024;
+ * 1 <= top_k <= min(E, 64);
  * T * top_k < 2^30; block_m in {0 (library default), 16, 32, 64, 128}.
  */
 #ifndef MOE_H_
@@ -190,10 +191,12 @@ MOE_API int moe_expert_ffn(const moe_desc* desc, const void* x, const void* w13,
 /* Static text for a status code (never NULL). */
 MOE_API const char* moe_strerror(int status);
 
-/* Kernel timing.  While enabled, every kernel the library launches is
- * bracketed by two HIP events on its stream (a small cost per launch);
+/* Kernel timing.  Kernels of the kinds set in the mask given to
+ * moe_timing_enable (bit MOE_KERNEL_x) are each bracketed by two HIP events
+ * recorded on the stream they are launched on (a small cost per launch);
  * moe_timing_collect waits for the recorded events and adds their durations
- * into per-kernel totals.  Kernel kinds index the arrays. */
+ * into per-kind totals.  Mask 0 (the initial state) times nothing.  Kernel
+ * kinds index the arrays. */
 #define MOE_KERNEL_ROUTE_LOGITS 0
 #define MOE_KERNEL_ROUTE_TOPK 1
 #define MOE_KERNEL_ALIGN 2
@@ -202,7 +205,8 @@ MOE_API const char* moe_strerror(int status);
 #define MOE_KERNEL_COMBINE 5
 #define MOE_KERNEL_COUNT 6
 
-MOE_API int moe_timing_enable(int enable);
+MOE_API int moe_timing_enable(int kind_mask);  /* MOE_ERR_BAD_ARG if out of range */
+#define MOE_TIMING_ALL ((1 << MOE_KERNEL_COUNT) - 1)
 /* total_ms[MOE_KERNEL_COUNT], launches[MOE_KERNEL_COUNT]; reset != 0 clears
  * the totals after reading.  Blocks until the recorded events complete. */
 MOE_API int moe_timing_collect(double* total_ms, int64_t* launches, int reset);

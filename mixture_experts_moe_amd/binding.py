@@ -15,7 +15,9 @@ from typing import Optional, Sequence, Tuple
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+# MOE_LIBRARY may name another build of the same library (e.g. a tuning variant).
+_LIB_PATH = os.environ.get("MOE_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 MOE_DTYPE_F32 = 0
 MOE_DTYPE_BF16 = 1
@@ -299,8 +301,22 @@ def moe_expert_ffn(x: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, top_k: 
     return out
 
 
-def moe_timing_enable(enable: bool = True) -> None:
-    _check("moe_timing_enable", lib().moe_timing_enable(int(bool(enable))))
+MOE_TIMING_ALL = (1 << MOE_KERNEL_COUNT) - 1
+KERNEL_KINDS = {"route_logits": 0, "route_topk": 1, "align": 2, "ffn13": 3, "ffn2": 4, "combine": 5}
+
+
+def moe_timing_enable(kinds=True) -> None:
+    """Time the given kernel kinds: True = all, False/None = none, or an
+    iterable of kind names ("ffn13", ...)."""
+    if kinds is True:
+        mask = MOE_TIMING_ALL
+    elif not kinds:
+        mask = 0
+    else:
+        mask = 0
+        for k in kinds:
+            mask |= 1 << KERNEL_KINDS[k]
+    _check("moe_timing_enable", lib().moe_timing_enable(mask))
 
 
 def moe_timing_collect(reset: bool = True) -> dict:

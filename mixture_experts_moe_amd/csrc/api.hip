@@ -13,7 +13,7 @@ namespace {
 
 using moe::FfnArgs;
 
-constexpr int64_t kMaxDim = int64_t(1) << 20;
+constexpr int64_t kMaxDim = int64_t(1) << 19;
 constexpr int64_t kMaxSlots = int64_t(1) << 30;
 constexpr size_t kWsAlign = 256;
 
@@ -111,11 +111,11 @@ void make_plan(const moe_desc* d, int top_k, bool with_routing, Plan* p) {
   p->splits = 1;
   p->ksplit = p->I;
   if (p->wdt != MOE_DTYPE_F32 && p->A > 0) {
-    const int kc = moe::ffn2_kchunk(p->I);
+    const int kc = moe::ffn2_kchunk(p->I, p->wdt);
     const int64_t blocks_est = std::min<int64_t>(p->cap / p->B, std::min(p->E, p->A) + p->A / p->B);
-    const int64_t wgs = blocks_est * (p->d / 128);
+    const int64_t waves = blocks_est * (p->d / 32);  // one wave per 32 channels
     int s = 1;
-    while (s < 8 && wgs * s < 2048 && p->I / (2 * s) >= 4 * kc) s *= 2;
+    while (s < 8 && waves * s < 2048 && p->I / (2 * s) >= 4 * kc) s *= 2;
     const int per = (p->I + s - 1) / s;
     p->ksplit = (per + kc - 1) / kc * kc;
     p->splits = (p->I + p->ksplit - 1) / p->ksplit;
@@ -152,7 +152,7 @@ struct Pending {
 };
 
 std::mutex g_timing_mu;
-bool g_timing_on = false;
+uint32_t g_timing_mask = 0;  // bit k: time kernels of kind k
 std::vector<Pending> g_pending;
 std::vector<std::pair<hipEvent_t, hipEvent_t>> g_event_pool;
 double g_total_ms[MOE_KERNEL_COUNT] = {};
@@ -163,7 +163,7 @@ hipError_t timed(int kind, hipStream_t s, F&& launch) {
   bool on;
   {
     std::lock_guard<std::mutex> lk(g_timing_mu);
-    on = g_timing_on;
+    on = (g_timing_mask >> kind) & 1u;
   }
   if (!on) return launch();
   hipEvent_t a, b;
@@ -244,7 +244,7 @@ MOE_API const char* moe_strerror(int status) {
   switch (status) {
     case MOE_OK: return "ok";
     case MOE_ERR_NULL_PTR: return "a required pointer is NULL";
-    case MOE_ERR_BAD_SHAPE: return "bad shape (d and I must be multiples of 64 in [64, 2^20], 1 <= E <= 1024, T >= 0, T*top_k < 2^30)";
+    case MOE_ERR_BAD_SHAPE: return "bad shape (d and I must be multiples of 64 in [64, 2^19], 1 <= E <= 1024, T >= 0, T*top_k < 2^30)";
     case MOE_ERR_BAD_TOPK: return "top_k must be in [1, min(E, 64)]";
     case MOE_ERR_BAD_DTYPE: return "unsupported dtype pair or scale mode (supported: f32/f32, bf16/bf16, bf16/e4m3fn with per-tensor or per-channel scales)";
     case MOE_ERR_MISALIGNED: return "a pointer is not 16-byte aligned (workspace: 256-byte)";
@@ -387,9 +387,10 @@ MOE_API int moe_forward(const moe_desc* desc, const void* x, const float* w_gate
   return to_status(run_ffn(a, s));
 }
 
-MOE_API int moe_timing_enable(int enable) {
+MOE_API int moe_timing_enable(int kind_mask) {
+  if (kind_mask < 0 || kind_mask >= (1 << MOE_KERNEL_COUNT)) return MOE_ERR_BAD_ARG;
   std::lock_guard<std::mutex> lk(g_timing_mu);
-  g_timing_on = enable != 0;
+  g_timing_mask = static_cast<uint32_t>(kind_mask);
   return MOE_OK;
 }
 

@@ -24,31 +24,36 @@
 // block.  e4m3fn weights are widened to bf16 in registers (exact) and their
 // fp32 scale is applied once per output channel in the epilogue.
 //
-// K-permutation: with a K chunk of KC elements, lane group g = lane/16 loads
-// KC/4 contiguous elements of its row (one or more 16-byte loads) and
-// fragment i of that run feeds MFMA i.  The B operand (tokens) is loaded
-// with the same mapping, so every MFMA pairs equal k on both sides while
-// each row is read in long contiguous runs.
+// K layout: within a K chunk of KC elements, one 16-byte load instruction
+// covers, for each of the 16 rows of a tile, 64 contiguous bytes of that row
+// (lane group g = lane/16 takes bytes 16g .. 16g+15).  For bf16 weights that
+// is exactly one MFMA step (k = 32j + 8g .. +8, the operand's natural layout);
+// for e4m3fn weights it is two steps (lane group g holds k = 64j + 16g .. +16
+// and feeds the first eight to MFMA 2j, the last eight to MFMA 2j+1).  The
+// bf16 token operand is loaded with the same k for every (lane, MFMA).
+
+#include <algorithm>
 
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
-constexpr int kFfnThreads = 256;  // 4 waves
+constexpr int kFfnThreads = 64;  // one wave per workgroup: even spread over the CUs
 
 // ------------------------------------------------------------ operand loads
 
 template <typename WT, int KC>
-struct RowChunk;  // one lane's KC/4 contiguous elements of one row
+struct RowChunk;  // one lane's part of one weight row's K chunk
 
 template <int KC>
 struct RowChunk<bf16_t, KC> {
   static constexpr int kLoads = KC / 32;  // 16-byte loads (8 bf16 each)
   uint4 v[kLoads];
-  __device__ __forceinline__ void load(const bf16_t* p) {
+  // load j: k = 32j + 8g .. +8 of the chunk (fragment j)
+  __device__ __forceinline__ void load(const bf16_t* chunk, int g) {
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) v[i] = *reinterpret_cast<const uint4*>(p + 8 * i);
+    for (int j = 0; j < kLoads; ++j) v[j] = *reinterpret_cast<const uint4*>(chunk + 32 * j + 8 * g);
   }
   __device__ __forceinline__ bf16x8 frag(int i) const { return as_frag(v[i]); }
 };
@@ -57,17 +62,36 @@ template <int KC>
 struct RowChunk<fp8_t, KC> {
   static constexpr int kLoads = KC / 64;  // 16-byte loads (16 e4m3fn each)
   uint4 v[kLoads];
-  __device__ __forceinline__ void load(const fp8_t* p) {
+  // load j: k = 64j + 16g .. +16 of the chunk (fragments 2j and 2j+1)
+  __device__ __forceinline__ void load(const fp8_t* chunk, int g) {
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) v[i] = *reinterpret_cast<const uint4*>(p + 16 * i);
+    for (int j = 0; j < kLoads; ++j) v[j] = *reinterpret_cast<const uint4*>(chunk + 64 * j + 16 * g);
   }
-  // fragment i = elements 8i .. 8i+7 of the run
   __device__ __forceinline__ bf16x8 frag(int i) const {
     const uint4 q = v[i >> 1];
     const uint32_t lo = (i & 1) ? q.z : q.x;
     const uint32_t hi = (i & 1) ? q.w : q.y;
     return as_frag(e4m3x8_to_frag_bits(lo, hi));
   }
+};
+
+// The bf16 token operand of one K chunk, in the k layout of weight type WT.
+template <typename WT, int KC>
+struct ActChunk {
+  static constexpr int kFrags = KC / 32;
+  uint4 v[kFrags];
+  static __device__ __forceinline__ int off(int i, int g) {
+    return sizeof(WT) == 2 ? 32 * i + 8 * g : 64 * (i >> 1) + 16 * g + 8 * (i & 1);
+  }
+  __device__ __forceinline__ void load(const bf16_t* chunk, int g) {
+#pragma unroll
+    for (int i = 0; i < kFrags; ++i) v[i] = *reinterpret_cast<const uint4*>(chunk + off(i, g));
+  }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < kFrags; ++i) v[i] = uint4{0, 0, 0, 0};
+  }
+  __device__ __forceinline__ bf16x8 frag(int i) const { return as_frag(v[i]); }
 };
 
 __device__ __forceinline__ float load_scale(const float* s, int mode, size_t matrix, size_t idx) {
@@ -87,28 +111,71 @@ __device__ __forceinline__ int live_subtiles(const int32_t* blk, int A) {
   return n;
 }
 
+// Tuning knobs (compile-time): weight chunks kept in flight per wave, and
+// 16-channel tiles per wave.
+#ifndef MOE_FFN13_PIPE
+#define MOE_FFN13_PIPE 2
+#endif
+#ifndef MOE_FFN13_RN
+#define MOE_FFN13_RN 2
+#endif
+#ifndef MOE_FFN2_PIPE
+#define MOE_FFN2_PIPE 2
+#endif
+#ifndef MOE_FFN2_RN
+#define MOE_FFN2_RN 2
+#endif
+
+// Weight rows of one wave, streamed in K chunks through a ring of P register
+// buffers: chunk c is consumed from buffer c % P, which is then refilled with
+// chunk c + P, so P chunks of loads stay in flight while the MFMAs run.
+template <typename WT, int KC, int NROW, int P>
+struct WeightStream {
+  RowChunk<WT, KC> buf[P][NROW];
+  const WT* row[NROW];
+  int g, nch;
+
+  __device__ __forceinline__ void start(int k_begin) {
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+      if (p < nch)
+#pragma unroll
+        for (int r = 0; r < NROW; ++r) buf[p][r].load(row[r] + k_begin + p * KC, g);
+  }
+  // fragments of chunk c (held in buffer p = c % P), then refill buffer p
+  __device__ __forceinline__ void take(int p, int c, int k_begin, bf16x8 (&f)[NROW][KC / 32]) {
+#pragma unroll
+    for (int r = 0; r < NROW; ++r)
+#pragma unroll
+      for (int i = 0; i < KC / 32; ++i) f[r][i] = buf[p][r].frag(i);
+    if (c + P < nch)
+#pragma unroll
+      for (int r = 0; r < NROW; ++r) buf[p][r].load(row[r] + k_begin + (c + P) * KC, g);
+  }
+};
+
 // ------------------------------------------------------------ W13 + SiLU*mul
 //
-// Grid: x = row block b of the regrouped layout, y = group of 64 output
-// channels (4 waves x 16).  Each wave computes, for its 16 channels n, the
-// gate rows n and the up rows I + n against every token of the block and
-// writes h[row, n] = SiLU(s_g * gate) * (s_u * up) in bf16.
+// Grid: x = row block b of the regrouped layout, y = group of 16 * RN output
+// channels (one wave, RN 16-channel tiles).  Each wave computes, for
+// its channels n, the gate rows n and the up rows I + n against every token
+// of the block and writes h[row, n] = SiLU(s_g * gate) * (s_u * up) in bf16.
 
-template <typename WT, int NSUB, int KC>
+template <typename WT, int NSUB, int KC, int P, int RN>
 __global__ __launch_bounds__(kFfnThreads) void ffn13_kernel(
     const bf16_t* __restrict__ x, const WT* __restrict__ w13, const float* __restrict__ s13,
     int scale_mode, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded,
     bf16_t* __restrict__ h, int d, int I, int k, int A, int B) {
   constexpr int NF = KC / 32;
+  constexpr int NROW = 2 * RN;  // RN gate tiles then RN up tiles
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
   const int r16 = lane & 15;
   const int g = lane >> 4;
   const int b = blockIdx.x;
   if (b * B >= *num_padded) return;
   const int e = block_expert[b];
-  const int n0 = (blockIdx.y * 4 + wave) * 16;
+  const int n0 = blockIdx.y * 16 * RN;
   if (n0 >= I) return;
   const int32_t* blk = sorted_ids + static_cast<size_t>(b) * B;
   const int nsub = live_subtiles<NSUB>(blk, A);
@@ -122,90 +189,86 @@ __global__ __launch_bounds__(kFfnThreads) void ffn13_kernel(
     xrow[s] = x + static_cast<size_t>(ok[s] ? f / k : 0) * d;
   }
   const size_t two_i = 2 * static_cast<size_t>(I);
-  const WT* wg = w13 + (static_cast<size_t>(e) * two_i + n0 + r16) * d;
-  const WT* wu = w13 + (static_cast<size_t>(e) * two_i + I + n0 + r16) * d;
-
-  f32x4 accg[NSUB], accu[NSUB];
+  WeightStream<WT, KC, NROW, P> ws;
+  ws.g = g;
+  ws.nch = d / KC;
 #pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
-    accg[s] = f32x4{0.f, 0.f, 0.f, 0.f};
-    accu[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int rt = 0; rt < RN; ++rt) {
+    ws.row[rt] = w13 + (static_cast<size_t>(e) * two_i + n0 + rt * 16 + r16) * d;
+    ws.row[RN + rt] = w13 + (static_cast<size_t>(e) * two_i + I + n0 + rt * 16 + r16) * d;
   }
 
-  RowChunk<WT, KC> ga, ua, gn, un;
-  const int koff = g * (KC / 4);
-  ga.load(wg + koff);
-  ua.load(wu + koff);
-  for (int kc = 0; kc < d; kc += KC) {
-    const bool more = kc + KC < d;
-    if (more) {  // prefetch the next chunk's weights while this one computes
-      gn.load(wg + kc + KC + koff);
-      un.load(wu + kc + KC + koff);
-    }
-    bf16x8 af[NF], bf[NF];
+  f32x4 acc[NSUB][NROW];
 #pragma unroll
-    for (int i = 0; i < NF; ++i) {
-      af[i] = ga.frag(i);
-      bf[i] = ua.frag(i);
+  for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+    for (int r = 0; r < NROW; ++r) acc[s][r] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  ws.start(0);
+  for (int c0 = 0; c0 < ws.nch; c0 += P) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int c = c0 + p;
+      if (c < ws.nch) {
+        bf16x8 wf[NROW][NF];
+        ws.take(p, c, 0, wf);
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) {
+          if (s < nsub) {
+            ActChunk<WT, KC> xs;
+            if (ok[s])
+              xs.load(xrow[s] + c * KC, g);
+            else
+              xs.zero();
+#pragma unroll
+            for (int i = 0; i < NF; ++i) {
+              const bf16x8 xf = xs.frag(i);
+#pragma unroll
+              for (int r = 0; r < NROW; ++r) acc[s][r] = mfma16x16x32(wf[r][i], xf, acc[s][r]);
+            }
+          }
+        }
+      }
+    }
+  }
+
+  // Epilogue: lane holds token column r16, channels n0 + rt*16 + 4g .. +3.
+#pragma unroll
+  for (int rt = 0; rt < RN; ++rt) {
+    const int nb = n0 + rt * 16 + 4 * g;
+    float sg[4], su[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      sg[v] = load_scale(s13, scale_mode, e, static_cast<size_t>(e) * two_i + nb + v);
+      su[v] = load_scale(s13, scale_mode, e, static_cast<size_t>(e) * two_i + I + nb + v);
     }
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
       if (s < nsub) {
-        RowChunk<bf16_t, KC> xs;
-        if (ok[s]) {
-          xs.load(xrow[s] + kc + koff);
-        } else {
+        const size_t row = static_cast<size_t>(b) * B + 16 * s + r16;
+        uint32_t packed[2];
 #pragma unroll
-          for (int i = 0; i < RowChunk<bf16_t, KC>::kLoads; ++i) xs.v[i] = uint4{0, 0, 0, 0};
+        for (int v = 0; v < 4; v += 2) {
+          const float h0 = silu(acc[s][rt][v] * sg[v]) * (acc[s][RN + rt][v] * su[v]);
+          const float h1 = silu(acc[s][rt][v + 1] * sg[v + 1]) * (acc[s][RN + rt][v + 1] * su[v + 1]);
+          packed[v / 2] = static_cast<uint32_t>(f32_to_bf16(h0)) |
+                          (static_cast<uint32_t>(f32_to_bf16(h1)) << 16);
         }
-#pragma unroll
-        for (int i = 0; i < NF; ++i) {
-          const bf16x8 xf = xs.frag(i);
-          accg[s] = mfma16x16x32(af[i], xf, accg[s]);
-          accu[s] = mfma16x16x32(bf[i], xf, accu[s]);
-        }
+        *reinterpret_cast<uint2*>(h + row * I + nb) = uint2{packed[0], packed[1]};
       }
-    }
-    if (more) {
-      ga = gn;
-      ua = un;
-    }
-  }
-
-  // Epilogue: lane holds token column r16, channels n0 + 4g .. n0 + 4g + 3.
-  const int nb = n0 + 4 * g;
-  float sg[4], su[4];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    sg[v] = load_scale(s13, scale_mode, e, static_cast<size_t>(e) * two_i + nb + v);
-    su[v] = load_scale(s13, scale_mode, e, static_cast<size_t>(e) * two_i + I + nb + v);
-  }
-#pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
-    if (s < nsub) {
-      const size_t row = static_cast<size_t>(b) * B + 16 * s + r16;
-      uint32_t packed[2];
-#pragma unroll
-      for (int v = 0; v < 4; v += 2) {
-        const float h0 = silu(accg[s][v] * sg[v]) * (accu[s][v] * su[v]);
-        const float h1 = silu(accg[s][v + 1] * sg[v + 1]) * (accu[s][v + 1] * su[v + 1]);
-        packed[v / 2] = static_cast<uint32_t>(f32_to_bf16(h0)) |
-                        (static_cast<uint32_t>(f32_to_bf16(h1)) << 16);
-      }
-      *reinterpret_cast<uint2*>(h + row * I + nb) = uint2{packed[0], packed[1]};
     }
   }
 }
 
 // ------------------------------------------------------------ W2 + gate scale
 //
-// Grid: x = row block b, y = group of 4 * 16 * RN output channels of d,
-// z = split of the K = I range.  Each wave owns RN tiles of 16 channels and
+// Grid: x = row block b, y = group of 16 * RN output channels of d (one
+// wave), z = split of the K = I range.  Each wave owns RN tiles of 16 channels and
 // writes y_part[z, f, n] = gate_f * s(n) * sum_{i in split} W2[e, n, i] h[r, i]
 // for every real slot f of the block; the combine sums the splits in a
 // fixed order, so the result is deterministic.
 
-template <typename WT, int NSUB, int KC, int RN>
+template <typename WT, int NSUB, int KC, int P, int RN>
 __global__ __launch_bounds__(kFfnThreads) void ffn2_kernel(
     const bf16_t* __restrict__ h, const WT* __restrict__ w2, const float* __restrict__ s2,
     int scale_mode, const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
@@ -213,13 +276,12 @@ __global__ __launch_bounds__(kFfnThreads) void ffn2_kernel(
     float* __restrict__ y_part, int d, int I, int A, int B, int ksplit) {
   constexpr int NF = KC / 32;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
   const int r16 = lane & 15;
   const int g = lane >> 4;
   const int b = blockIdx.x;
   if (b * B >= *num_padded) return;
   const int e = block_expert[b];
-  const int n0 = (blockIdx.y * 4 + wave) * 16 * RN;
+  const int n0 = blockIdx.y * 16 * RN;
   if (n0 >= d) return;
   const int z = blockIdx.z;
   const int k_begin = z * ksplit;
@@ -228,13 +290,18 @@ __global__ __launch_bounds__(kFfnThreads) void ffn2_kernel(
   const int nsub = live_subtiles<NSUB>(blk, A);
 
   const bf16_t* hrow[NSUB];
+  bool ok[NSUB];  // pad rows hold zeros: skip their loads
 #pragma unroll
-  for (int s = 0; s < NSUB; ++s)
+  for (int s = 0; s < NSUB; ++s) {
+    ok[s] = s < nsub && blk[16 * s + r16] < A;
     hrow[s] = h + (static_cast<size_t>(b) * B + 16 * s + r16) * I;
-  const WT* wrow[RN];
+  }
+  WeightStream<WT, KC, RN, P> ws;
+  ws.g = g;
+  ws.nch = k_end > k_begin ? (k_end - k_begin) / KC : 0;
 #pragma unroll
   for (int rt = 0; rt < RN; ++rt)
-    wrow[rt] = w2 + (static_cast<size_t>(e) * d + n0 + rt * 16 + r16) * I;
+    ws.row[rt] = w2 + (static_cast<size_t>(e) * d + n0 + rt * 16 + r16) * I;
 
   f32x4 acc[NSUB][RN];
 #pragma unroll
@@ -242,39 +309,31 @@ __global__ __launch_bounds__(kFfnThreads) void ffn2_kernel(
 #pragma unroll
     for (int rt = 0; rt < RN; ++rt) acc[s][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int koff = g * (KC / 4);
-  RowChunk<WT, KC> wa[RN], wn[RN];
-  if (k_begin < k_end) {
+  ws.start(k_begin);
+  for (int c0 = 0; c0 < ws.nch; c0 += P) {
 #pragma unroll
-    for (int rt = 0; rt < RN; ++rt) wa[rt].load(wrow[rt] + k_begin + koff);
-  }
-  for (int kc = k_begin; kc < k_end; kc += KC) {
-    const bool more = kc + KC < k_end;
-    if (more) {
+    for (int p = 0; p < P; ++p) {
+      const int c = c0 + p;
+      if (c < ws.nch) {
+        bf16x8 wf[RN][NF];
+        ws.take(p, c, k_begin, wf);
 #pragma unroll
-      for (int rt = 0; rt < RN; ++rt) wn[rt].load(wrow[rt] + kc + KC + koff);
-    }
-    bf16x8 af[RN][NF];
+        for (int s = 0; s < NSUB; ++s) {
+          if (s < nsub) {
+            ActChunk<WT, KC> hs;
+            if (ok[s])
+              hs.load(hrow[s] + k_begin + c * KC, g);
+            else
+              hs.zero();
 #pragma unroll
-    for (int rt = 0; rt < RN; ++rt)
+            for (int i = 0; i < NF; ++i) {
+              const bf16x8 hf = hs.frag(i);
 #pragma unroll
-      for (int i = 0; i < NF; ++i) af[rt][i] = wa[rt].frag(i);
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-      if (s < nsub) {
-        RowChunk<bf16_t, KC> hs;
-        hs.load(hrow[s] + kc + koff);
-#pragma unroll
-        for (int i = 0; i < NF; ++i) {
-          const bf16x8 hf = hs.frag(i);
-#pragma unroll
-          for (int rt = 0; rt < RN; ++rt) acc[s][rt] = mfma16x16x32(af[rt][i], hf, acc[s][rt]);
+              for (int rt = 0; rt < RN; ++rt) acc[s][rt] = mfma16x16x32(wf[rt][i], hf, acc[s][rt]);
+            }
+          }
         }
       }
-    }
-    if (more) {
-#pragma unroll
-      for (int rt = 0; rt < RN; ++rt) wa[rt] = wn[rt];
     }
   }
 
@@ -402,24 +461,58 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 // ------------------------------------------------------------ launchers
 
-int ffn2_kchunk(int I) { return (I % 128 == 0) ? 128 : 64; }
+// K chunk: 128 elements (four MFMA steps), or 64 when 128 does not divide
+// the K dimension (K is a multiple of 64).  e4m3fn rows move half the bytes
+// per chunk, so they keep one more chunk in flight.
+template <typename WT>
+int kchunk_for(int K) {
+  return K % 128 == 0 ? 128 : 64;
+}
+
+int ffn2_kchunk(int I, int w_dtype) {
+  return w_dtype == kDtypeE4M3FN ? kchunk_for<fp8_t>(I) : kchunk_for<bf16_t>(I);
+}
 
 namespace {
 
+constexpr int kP13 = MOE_FFN13_PIPE, kRN13 = MOE_FFN13_RN;
+constexpr int kP2 = MOE_FFN2_PIPE, kRN2 = MOE_FFN2_RN;
+
+// Channel tiles per wave: two when that still leaves at least eight waves
+// per CU (x loads are shared by twice the weight rows), else one (twice the
+// waves, for small batches that touch few experts).
+inline int pick_rn(int blocks_est, int channels, int rn_max) {
+  return (rn_max >= 2 && int64_t(blocks_est) * (channels / 32) >= 8 * 256) ? 2 : 1;
+}
+
+inline int blocks_estimate(const FfnArgs& a) {
+  return std::min(a.cap / a.B, std::min(a.E, a.A) + a.A / a.B);
+}
+
+template <typename WT, int NSUB, int KC, int RN>
+void ffn13_launch(const FfnArgs& a, hipStream_t s) {
+  constexpr int P = sizeof(WT) == 1 ? kP13 + 1 : kP13;
+  dim3 grid(a.cap / a.B, a.I / (16 * RN));  // I is a multiple of 64: the tiles cover it
+  ffn13_kernel<WT, NSUB, KC, P, RN><<<grid, kFfnThreads, 0, s>>>(
+      static_cast<const bf16_t*>(a.x), static_cast<const WT*>(a.w13), a.s13, a.scale_mode,
+      a.sorted_ids, a.block_expert, a.num_padded, static_cast<bf16_t*>(a.h), a.d, a.I, a.k, a.A,
+      a.B);
+}
+
+template <typename WT, int NSUB, int KC>
+void ffn13_go(const FfnArgs& a, hipStream_t s) {
+  static_assert(kRN13 == 1 || kRN13 == 2, "channel tiles per wave: 1 or 2");
+  if (pick_rn(blocks_estimate(a), a.I, kRN13) == 2)
+    ffn13_launch<WT, NSUB, KC, kRN13>(a, s);
+  else
+    ffn13_launch<WT, NSUB, KC, 1>(a, s);
+}
+
 template <typename WT, int NSUB>
 hipError_t ffn13_nsub(const FfnArgs& a, hipStream_t s) {
-  dim3 grid(a.cap / a.B, a.I / 64);
-  const auto* w = static_cast<const WT*>(a.w13);
-  const auto* x = static_cast<const bf16_t*>(a.x);
-  auto* h = static_cast<bf16_t*>(a.h);
-  if (a.d % 128 == 0)
-    ffn13_kernel<WT, NSUB, 128><<<grid, kFfnThreads, 0, s>>>(
-        x, w, a.s13, a.scale_mode, a.sorted_ids, a.block_expert, a.num_padded, h, a.d, a.I, a.k,
-        a.A, a.B);
-  else
-    ffn13_kernel<WT, NSUB, 64><<<grid, kFfnThreads, 0, s>>>(
-        x, w, a.s13, a.scale_mode, a.sorted_ids, a.block_expert, a.num_padded, h, a.d, a.I, a.k,
-        a.A, a.B);
+  const int kc = kchunk_for<WT>(a.d);
+  if (kc == 128) ffn13_go<WT, NSUB, 128>(a, s);
+  else ffn13_go<WT, NSUB, 64>(a, s);
   return hipGetLastError();
 }
 
@@ -434,23 +527,30 @@ hipError_t ffn13_w(const FfnArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-constexpr int kFfn2RN = 2;
+template <typename WT, int NSUB, int KC, int RN>
+void ffn2_launch(const FfnArgs& a, hipStream_t s) {
+  constexpr int P = sizeof(WT) == 1 ? kP2 + 1 : kP2;
+  dim3 grid(a.cap / a.B, a.d / (16 * RN), a.splits);  // d is a multiple of 64
+  ffn2_kernel<WT, NSUB, KC, P, RN><<<grid, kFfnThreads, 0, s>>>(
+      static_cast<const bf16_t*>(a.h), static_cast<const WT*>(a.w2), a.s2, a.scale_mode,
+      a.topk_w, a.sorted_ids, a.block_expert, a.num_padded, a.y_part, a.d, a.I, a.A, a.B,
+      a.ksplit);
+}
+
+template <typename WT, int NSUB, int KC>
+void ffn2_go(const FfnArgs& a, hipStream_t s) {
+  static_assert(kRN2 == 1 || kRN2 == 2, "channel tiles per wave: 1 or 2");
+  if (pick_rn(blocks_estimate(a) * a.splits, a.d, kRN2) == 2)
+    ffn2_launch<WT, NSUB, KC, kRN2>(a, s);
+  else
+    ffn2_launch<WT, NSUB, KC, 1>(a, s);
+}
 
 template <typename WT, int NSUB>
 hipError_t ffn2_nsub(const FfnArgs& a, hipStream_t s) {
-  // 16 * kFfn2RN channels per wave; d is a multiple of 32, so a wave is either
-  // wholly inside [0, d) or wholly past it (and returns).
-  dim3 grid(a.cap / a.B, (a.d + 64 * kFfn2RN - 1) / (64 * kFfn2RN), a.splits);
-  const auto* w = static_cast<const WT*>(a.w2);
-  const auto* h = static_cast<const bf16_t*>(a.h);
-  if (ffn2_kchunk(a.I) == 128)
-    ffn2_kernel<WT, NSUB, 128, kFfn2RN><<<grid, kFfnThreads, 0, s>>>(
-        h, w, a.s2, a.scale_mode, a.topk_w, a.sorted_ids, a.block_expert, a.num_padded, a.y_part,
-        a.d, a.I, a.A, a.B, a.ksplit);
-  else
-    ffn2_kernel<WT, NSUB, 64, kFfn2RN><<<grid, kFfnThreads, 0, s>>>(
-        h, w, a.s2, a.scale_mode, a.topk_w, a.sorted_ids, a.block_expert, a.num_padded, a.y_part,
-        a.d, a.I, a.A, a.B, a.ksplit);
+  const int kc = kchunk_for<WT>(a.I);
+  if (kc == 128) ffn2_go<WT, NSUB, 128>(a, s);
+  else ffn2_go<WT, NSUB, 64>(a, s);
   return hipGetLastError();
 }
 

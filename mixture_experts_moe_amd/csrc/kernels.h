@@ -51,8 +51,8 @@ hipError_t launch_ffn13(const FfnArgs& a, hipStream_t s);
 hipError_t launch_ffn2(const FfnArgs& a, hipStream_t s);
 hipError_t launch_combine(const FfnArgs& a, hipStream_t s);
 
-// K-chunk the W2 kernel uses for a given I (the split length must be a
-// multiple of it).
-int ffn2_kchunk(int I);
+// K chunk the W2 kernel uses for a given I and weight dtype (the split
+// length must be a multiple of it).
+int ffn2_kchunk(int I, int w_dtype);
 
 }  // namespace moe

@@ -77,6 +77,111 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict
   }
 }
 
+// bf16 activations: the same product on bf16 matrix cores.  Each fp32
+// W_gate value is split exactly into three bf16 parts, w = hi + mid + lo
+// (hi = w rounded to bf16, mid = the remainder rounded to bf16, lo = the
+// rest, which has at most 8 significant bits).  A bf16 x bf16 product is
+// exact in fp32, so x.w = x.hi + x.mid + x.lo is an fp32 dot product of exact
+// products, at three 16x16x32 bf16 MFMAs per 32 k instead of eight 16x16x4
+// fp32 ones.  K is split over the four waves of a workgroup (each wave takes
+// a contiguous range of 32-wide steps) and the four partial tiles are added
+// in wave order through LDS, so the result is deterministic.  A workgroup
+// covers 16 experts x 16*NT tokens.
+
+__device__ __forceinline__ void split3_bf16(const float (&w)[8], uint4& hi, uint4& mid, uint4& lo) {
+  uint32_t h[4], m[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    bf16_t h0 = f32_to_bf16(w[i]), h1 = f32_to_bf16(w[i + 1]);
+    const float r0 = w[i] - bf16_to_f32(h0), r1 = w[i + 1] - bf16_to_f32(h1);
+    bf16_t m0 = f32_to_bf16(r0), m1 = f32_to_bf16(r1);
+    const float q0 = r0 - bf16_to_f32(m0), q1 = r1 - bf16_to_f32(m1);
+    h[i / 2] = h0 | (static_cast<uint32_t>(h1) << 16);
+    m[i / 2] = m0 | (static_cast<uint32_t>(m1) << 16);
+    l[i / 2] = f32_to_bf16(q0) | (static_cast<uint32_t>(f32_to_bf16(q1)) << 16);
+  }
+  hi = uint4{h[0], h[1], h[2], h[3]};
+  mid = uint4{m[0], m[1], m[2], m[3]};
+  lo = uint4{l[0], l[1], l[2], l[3]};
+}
+
+template <int NT, int NW>
+__global__ __launch_bounds__(64 * NW) void router_logits_bf16_kernel(const bf16_t* __restrict__ x,
+                                                                     const float* __restrict__ wg,
+                                                                     float* __restrict__ logits,
+                                                                     int T, int E, int d) {
+  constexpr int U = 4;  // 32-wide steps whose loads are issued together
+  __shared__ f32x4 red[NW][NT][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  const int t0 = blockIdx.x * 16 * NT;
+  const int e = blockIdx.y * 16 + r16;
+  const bool e_ok = e < E;
+  const float* wrow = wg + static_cast<size_t>(e_ok ? e : 0) * d + 8 * g;
+  const bf16_t* xrow[NT];
+  bool t_ok[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int t = t0 + nt * 16 + r16;
+    t_ok[nt] = t < T;
+    xrow[nt] = x + static_cast<size_t>(t_ok[nt] ? t : 0) * d + 8 * g;
+  }
+  const int steps = d / 32;
+  const int s_begin = wave * steps / NW;
+  const int s_end = (wave + 1) * steps / NW;
+  f32x4 acc_h[NT], acc_m[NT], acc_l[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc_h[nt] = acc_m[nt] = acc_l[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int s0 = s_begin; s0 < s_end; s0 += U) {
+    float4 wa[U], wb[U];
+    uint4 xb[U][NT];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {  // issue every load of U steps first
+      const int k = (s0 + u) * 32;
+      const bool live = s0 + u < s_end;
+      wa[u] = (live && e_ok) ? *reinterpret_cast<const float4*>(wrow + k) : float4{0.f, 0.f, 0.f, 0.f};
+      wb[u] = (live && e_ok) ? *reinterpret_cast<const float4*>(wrow + k + 4) : float4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        xb[u][nt] = (live && t_ok[nt]) ? *reinterpret_cast<const uint4*>(xrow[nt] + k) : uint4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float w[8] = {wa[u].x, wa[u].y, wa[u].z, wa[u].w, wb[u].x, wb[u].y, wb[u].z, wb[u].w};
+      uint4 hi, mid, lo;
+      split3_bf16(w, hi, mid, lo);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const bf16x8 xf = as_frag(xb[u][nt]);
+        acc_h[nt] = mfma16x16x32(as_frag(hi), xf, acc_h[nt]);
+        acc_m[nt] = mfma16x16x32(as_frag(mid), xf, acc_m[nt]);
+        acc_l[nt] = mfma16x16x32(as_frag(lo), xf, acc_l[nt]);
+      }
+    }
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) red[wave][nt][lane] = acc_h[nt] + (acc_m[nt] + acc_l[nt]);
+  __syncthreads();
+  // D layout: lane holds token column r16, expert rows 4g .. 4g+3.  The wave
+  // partials are added in wave order.
+  for (int nt = wave; nt < NT; nt += NW) {
+    f32x4 v = red[0][nt][lane];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) v += red[w][nt][lane];
+    const int t = t0 + nt * 16 + r16;
+    if (t < T) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int ee = blockIdx.y * 16 + 4 * g + q;
+        if (ee < E) logits[static_cast<size_t>(t) * E + ee] = v[q];
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- top-k + gates
 //
 // One wavefront per token.  Lane l holds the logits of experts l, l+64, ...
@@ -153,13 +258,19 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
 
 hipError_t launch_router_logits(const void* x, int act_dtype, const float* wg, float* logits,
                                 int T, int E, int d, hipStream_t s) {
-  dim3 grid((T + 15) / 16, (E + 63) / 64);
-  if (act_dtype == kDtypeF32)
+  if (act_dtype == kDtypeF32) {
+    dim3 grid((T + 15) / 16, (E + 63) / 64);
     router_logits_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(x), wg, logits,
                                                      T, E, d);
-  else
-    router_logits_kernel<bf16_t><<<grid, 256, 0, s>>>(static_cast<const bf16_t*>(x), wg,
-                                                      logits, T, E, d);
+  } else if (T <= 64) {  // few tokens: split K 16 ways for latency
+    dim3 grid((T + 15) / 16, (E + 15) / 16);
+    router_logits_bf16_kernel<1, 16><<<grid, 1024, 0, s>>>(static_cast<const bf16_t*>(x), wg,
+                                                           logits, T, E, d);
+  } else {
+    dim3 grid((T + 63) / 64, (E + 15) / 16);
+    router_logits_bf16_kernel<4, 4><<<grid, 256, 0, s>>>(static_cast<const bf16_t*>(x), wg,
+                                                         logits, T, E, d);
+  }
   return hipGetLastError();
 }
 
