@@ -50,7 +50,8 @@
  * matrix (s13 [E], s2 [E]).  Activations stay bf16 (weight-only FP8).
  * Limits: d and I multiples of 64 in [64, 2^19]; 1 <= E <= 1024;
  * 1 <= top_k <= min(E, 64);
- * T * top_k < 2^30; block_m in {0 (library default), 16, 32, 64, 128}.
+ * T * top_k < 2^30; block_m in {0 (library default), 16, 32, 64, 128, 256};
+ * 256 needs bf16 weights, d % 256 == 0 and I % 128 == 0.
  */
 #ifndef MOE_H_
 #define MOE_H_
@@ -77,7 +78,7 @@ extern "C" {
 #define MOE_ERR_MISALIGNED (-5)    /* a pointer is not 16-byte aligned      */
 #define MOE_ERR_WORKSPACE (-6)     /* workspace NULL or too small           */
 #define MOE_ERR_HIP (-7)           /* a HIP call or kernel launch failed    */
-#define MOE_ERR_BAD_BLOCK_M (-8)   /* block_m not in {0,16,32,64,128}       */
+#define MOE_ERR_BAD_BLOCK_M (-8)   /* block_m not allowed for the desc      */
 #define MOE_ERR_BAD_ARG (-9)       /* any other invalid argument            */
 
 /* ---- dtypes and scale modes ---- */
@@ -98,7 +99,7 @@ typedef struct moe_desc {
   int64_t intermediate;  /* I                        */
   int32_t act_dtype;     /* MOE_DTYPE_F32 / _BF16    */
   int32_t weight_dtype;  /* MOE_DTYPE_F32/_BF16/_E4M3FN */
-  int32_t block_m;       /* 0 or 16/32/64/128        */
+  int32_t block_m;       /* 0 or 16/32/64/128/256    */
   int32_t reserved;      /* must be 0                */
 } moe_desc;
 

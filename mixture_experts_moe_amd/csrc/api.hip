@@ -40,7 +40,11 @@ int check_desc(const moe_desc* d, int top_k) {
                        (d->act_dtype == MOE_DTYPE_BF16 && d->weight_dtype == MOE_DTYPE_E4M3FN);
   if (!pair_ok) return MOE_ERR_BAD_DTYPE;
   const int bm = d->block_m;
-  if (bm != 0 && bm != 16 && bm != 32 && bm != 64 && bm != 128) return MOE_ERR_BAD_BLOCK_M;
+  if (bm != 0 && bm != 16 && bm != 32 && bm != 64 && bm != 128 && bm != 256)
+    return MOE_ERR_BAD_BLOCK_M;
+  if (bm == 256 && !(d->weight_dtype == MOE_DTYPE_BF16 &&
+                     moe::big_gemm_fits(static_cast<int>(d->hidden), static_cast<int>(d->intermediate))))
+    return MOE_ERR_BAD_BLOCK_M;  // the 256-token GEMM is bf16 with d % 256 == 0, I % 128 == 0
   return MOE_OK;
 }
 
@@ -76,16 +80,23 @@ struct Plan {
   size_t logits, ids, gates, counts, num_padded, sorted, block_exp, h, y, total;
 };
 
-// Block size of the regrouped layout.  With B >= T every expert's tokens
-// fit one block (an expert holds at most one slot per token), so each
-// expert's weights are streamed exactly once; larger batches use 64-row
-// blocks.
-int default_block_m(const moe_desc* d) {
+// Block size of the regrouped layout.  Up to 64 tokens the weight-streaming
+// kernels run with B >= T: every expert's tokens fit one block (an expert
+// holds at most one slot per token), so each expert's weights are streamed
+// exactly once.  Larger batches use 128-token blocks and the token-tiled
+// grouped GEMM, and when experts average 256 tokens or more (bf16 weights,
+// fitting shapes) 256-token blocks and the large-tile GEMM.
+int default_block_m(const moe_desc* d, int top_k) {
   if (d->weight_dtype == MOE_DTYPE_F32) return 16;
   const int64_t T = d->num_tokens;
   if (T <= 16) return 16;
   if (T <= 32) return 32;
-  return 64;
+  if (T <= 64) return 64;
+  const int64_t per_expert = T * top_k / d->num_experts;
+  if (per_expert >= 256 && d->weight_dtype == MOE_DTYPE_BF16 &&
+      moe::big_gemm_fits(static_cast<int>(d->hidden), static_cast<int>(d->intermediate)))
+    return 256;
+  return 128;
 }
 
 int64_t capacity(int64_t A, int64_t E, int64_t B) {
@@ -100,7 +111,7 @@ void make_plan(const moe_desc* d, int top_k, bool with_routing, Plan* p) {
   p->I = static_cast<int>(d->intermediate);
   p->k = top_k;
   p->A = p->T * top_k;
-  p->B = d->block_m ? d->block_m : default_block_m(d);
+  p->B = d->block_m ? d->block_m : default_block_m(d, top_k);
   p->cap = static_cast<int>(capacity(p->A, p->E, p->B));
   p->act = d->act_dtype;
   p->wdt = d->weight_dtype;
@@ -110,7 +121,7 @@ void make_plan(const moe_desc* d, int top_k, bool with_routing, Plan* p) {
   // fixed order.
   p->splits = 1;
   p->ksplit = p->I;
-  if (p->wdt != MOE_DTYPE_F32 && p->A > 0) {
+  if (p->wdt != MOE_DTYPE_F32 && p->A > 0 && p->B <= 64) {  // the GEMM paths do not split
     const int kc = moe::ffn2_kchunk(p->I, p->wdt);
     const int64_t blocks_est = std::min<int64_t>(p->cap / p->B, std::min(p->E, p->A) + p->A / p->B);
     const int64_t waves = blocks_est * (p->d / 32);  // one wave per 32 channels
@@ -250,7 +261,7 @@ MOE_API const char* moe_strerror(int status) {
     case MOE_ERR_MISALIGNED: return "a pointer is not 16-byte aligned (workspace: 256-byte)";
     case MOE_ERR_WORKSPACE: return "workspace is NULL or smaller than moe_workspace_bytes()";
     case MOE_ERR_HIP: return "a HIP call or kernel launch failed";
-    case MOE_ERR_BAD_BLOCK_M: return "block_m must be 0, 16, 32, 64 or 128";
+    case MOE_ERR_BAD_BLOCK_M: return "block_m must be 0, 16, 32, 64, 128 or 256 (256: bf16 weights, d % 256 == 0, I % 128 == 0)";
     case MOE_ERR_BAD_ARG: return "invalid argument (reserved fields must be 0)";
   }
   return "unknown status";

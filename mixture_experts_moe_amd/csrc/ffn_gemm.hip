@@ -1,0 +1,377 @@
+// Token-tiled grouped GEMM for blocks of 128 tokens: the expert kernels of
+// the large-batch regime (prefill, and fine-grained experts at large T).
+//
+// Sources: the Hungarian news page "Az AWS új MoE-optimalizációkkal
+// gyorsítja a SageMaker AI-t", section "A fused MoE a számítási folyamat több
+// lépését egyesíti" (the experts' computation as one batched operation over
+// all experts), and section "FP8 esetén a Triton backend bizonyult
+// gyorsabbnak" (FP8 scaling and the matrix product in one pass over data read
+// once from HBM).
+//
+// With 128 tokens per block the product is a real dense contraction, so the
+// token operand is shared: a workgroup of four waves stages the block's
+// 128 x KC token tile in LDS (double buffered, rows padded by 16 bytes so the
+// 16-byte reads of 16 different rows hit different banks) and every wave
+// multiplies it with its own weight rows.  Weight rows still go HBM/L2 ->
+// registers through the per-wave ring of the streaming kernels (each weight
+// element is used by one wave only); the four waves of a workgroup cover
+// 4 * 16 * RN output channels.  Operands meet on v_mfma_f32_16x16x32_bf16
+// with weight rows on M and tokens on N; e4m3fn weights are widened exactly
+// in registers.  The W13 epilogue applies SiLU(gate) * up, the W2 epilogue
+// the per-channel scale and the slot's gate.
+
+#include "ffn_common.h"
+
+namespace moe {
+
+constexpr int kGemmWaves = 4;
+constexpr int kGemmThreads = 64 * kGemmWaves;
+constexpr int kGemmTokens = 128;  // block size B of this path
+constexpr int kGemmNSub = kGemmTokens / 16;
+
+#ifndef MOE_GEMM_PIPE
+#define MOE_GEMM_PIPE 2
+#endif
+#ifndef MOE_GEMM_RN
+#define MOE_GEMM_RN 1
+#endif
+
+// Rows of the token tile this thread stages: KC/8 16-byte pieces per row,
+// piece q = tid + 256*i, row = q / (KC/8).  Rows that hold no token (pad
+// slots, dead sub-tiles) read a valid address and are zeroed with a select,
+// so staging has no branches.
+template <int KC>
+struct Stager {
+  static constexpr int kPiecesPerRow = KC / 8;
+  static constexpr int kRowsPerPass = kGemmThreads / kPiecesPerRow;
+  static constexpr int kPieces = kGemmTokens / kRowsPerPass;  // per thread
+  static constexpr int kPitch = KC + 8;                       // elements per LDS row
+  const bf16_t* src[kPieces];  // row start + piece column (a valid row if dead)
+  uint32_t live;               // bit i: piece i carries a token
+  uint4 v[kPieces];
+
+  __device__ __forceinline__ int row(int i) const {
+    return static_cast<int>(threadIdx.x) / kPiecesPerRow + kRowsPerPass * i;
+  }
+  __device__ __forceinline__ int col() const {
+    return (static_cast<int>(threadIdx.x) % kPiecesPerRow) * 8;
+  }
+  __device__ __forceinline__ void load(int k0) {
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+      const uint4 q = *reinterpret_cast<const uint4*>(src[i] + k0);
+      const bool on = (live >> i) & 1u;
+      v[i] = uint4{on ? q.x : 0u, on ? q.y : 0u, on ? q.z : 0u, on ? q.w : 0u};
+    }
+  }
+  __device__ __forceinline__ void store(bf16_t* buf) const {
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i)
+      *reinterpret_cast<uint4*>(buf + row(i) * kPitch + col()) = v[i];
+  }
+};
+
+// Workgroup -> (row block, channel group).  The grid is 1-D.  Workgroup id p
+// runs on XCD p % 8 (the dispatcher deals workgroups round-robin over the 8
+// XCDs, each with its own L2), so logical tile l = (p % 8) * per_xcd + p / 8
+// gives every XCD a contiguous run of the logical order.  That order walks
+// super-rows of kGroupCols channel groups; inside one, the row block varies
+// slowest: the workgroups an XCD runs together cover kGroupCols channel
+// groups x consecutive row blocks (one expert's tokens), so their weight and
+// token tiles are shared through that XCD's L2.
+constexpr int kXcds = 8;
+constexpr int kGroupCols = 4;
+
+struct TileId {
+  int b, y;
+  bool live;
+};
+
+__device__ __forceinline__ TileId tile_of(int p, int gx, int gy) {
+  const int total = gx * gy;
+  const int per_xcd = (total + kXcds - 1) / kXcds;
+  const int l = (p % kXcds) * per_xcd + p / kXcds;
+  TileId t{0, 0, l < total};
+  if (!t.live) return t;
+  const int band = kGroupCols * gx;            // tiles per full super-row
+  const int sr = l / band;
+  const int rem = l - sr * band;
+  const int cols = min(kGroupCols, gy - sr * kGroupCols);  // channel groups in this super-row
+  t.b = rem / cols;
+  t.y = sr * kGroupCols + rem % cols;
+  return t;
+}
+
+inline int raster_grid(int gx, int gy) {
+  const int total = gx * gy;
+  return (total + kXcds - 1) / kXcds * kXcds;
+}
+
+// Shared main loop: acc[s][r] += W_rows[r] . tokens[s]^T over all K.  All
+// eight 16-token sub-tiles are computed (a partly filled block wastes MFMA
+// slots, not memory traffic); the only branches are the uniform loop ones.
+template <typename WT, int KC, int P, int NROW>
+__device__ __forceinline__ void gemm_mainloop(WeightStream<WT, KC, NROW, P>& ws,
+                                              Stager<KC>& st, bf16_t* lds,
+                                              f32x4 (&acc)[kGemmNSub][NROW]) {
+  constexpr int NF = KC / 32;
+  constexpr int kPitch = Stager<KC>::kPitch;
+  constexpr int kBuf = kGemmTokens * kPitch;
+  const int lane = threadIdx.x & 63;
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  const int last = ws.nch - 1;
+
+  st.load(0);
+  st.store(lds);
+  ws.start(0);
+  __syncthreads();
+  for (int c0 = 0; c0 < ws.nch; c0 += P) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int c = c0 + p;
+      if (c < ws.nch) {
+        st.load(min(c + 1, last) * KC);  // the last chunk reloads itself: harmless
+        bf16x8 wf[NROW][NF];
+        ws.take(p, c, 0, wf);
+        const bf16_t* tile = lds + (c & 1) * kBuf;
+#pragma unroll
+        for (int i = 0; i < NF; ++i) {
+          const int off = ActChunk<WT, KC>::off(i, g);
+#pragma unroll
+          for (int s = 0; s < kGemmNSub; ++s) {
+            const bf16x8 bf =
+                as_frag(*reinterpret_cast<const uint4*>(tile + (16 * s + r16) * kPitch + off));
+#pragma unroll
+            for (int r = 0; r < NROW; ++r) acc[s][r] = mfma16x16x32(wf[r][i], bf, acc[s][r]);
+          }
+        }
+        st.store(lds + ((c + 1) & 1) * kBuf);  // (after the last chunk: unread)
+        __syncthreads();
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------ W13 + SiLU*mul
+//
+// Grid: x = row block b (128 tokens of one expert), y = group of
+// 4 * 16 * RN output channels of I.
+
+template <typename WT, int KC, int P, int RN>
+__global__ __launch_bounds__(kGemmThreads) void ffn13_gemm_kernel(
+    const bf16_t* __restrict__ x, const WT* __restrict__ w13, const float* __restrict__ s13,
+    int scale_mode, const int32_t* __restrict__ sorted_ids,
+    const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded,
+    bf16_t* __restrict__ h, int d, int I, int k, int A, int gx, int gy) {
+  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * kGemmTokens * Stager<KC>::kPitch];
+  constexpr int NROW = 2 * RN;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  const TileId tid = tile_of(blockIdx.x, gx, gy);
+  const int b = tid.b;
+  if (!tid.live || b * kGemmTokens >= *num_padded) return;  // uniform over the workgroup
+  const int e = block_expert[b];
+  const int32_t* blk = sorted_ids + static_cast<size_t>(b) * kGemmTokens;
+  const int nsub = live_subtiles<kGemmNSub>(blk, A);
+  const int n0 = (tid.y * kGemmWaves + wave) * 16 * RN;  // the channel groups tile I exactly
+
+  Stager<KC> st;
+  st.live = 0;
+#pragma unroll
+  for (int i = 0; i < Stager<KC>::kPieces; ++i) {
+    const int f = blk[st.row(i)];
+    const bool on = f < A;
+    st.live |= static_cast<uint32_t>(on) << i;
+    st.src[i] = x + static_cast<size_t>(on ? f / k : 0) * d + st.col();
+  }
+  const size_t two_i = 2 * static_cast<size_t>(I);
+  WeightStream<WT, KC, NROW, P> ws;
+  ws.g = g;
+  ws.nch = d / KC;
+#pragma unroll
+  for (int rt = 0; rt < RN; ++rt) {
+    ws.row[rt] = w13 + (static_cast<size_t>(e) * two_i + n0 + rt * 16 + r16) * d;
+    ws.row[RN + rt] = w13 + (static_cast<size_t>(e) * two_i + I + n0 + rt * 16 + r16) * d;
+  }
+  f32x4 acc[kGemmNSub][NROW];
+#pragma unroll
+  for (int s = 0; s < kGemmNSub; ++s)
+#pragma unroll
+    for (int r = 0; r < NROW; ++r) acc[s][r] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  gemm_mainloop<WT, KC, P, NROW>(ws, st, lds, acc);
+
+#pragma unroll
+  for (int rt = 0; rt < RN; ++rt) {
+    const int nb = n0 + rt * 16 + 4 * g;
+    float sg[4], su[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      sg[v] = load_scale(s13, scale_mode, e, static_cast<size_t>(e) * two_i + nb + v);
+      su[v] = load_scale(s13, scale_mode, e, static_cast<size_t>(e) * two_i + I + nb + v);
+    }
+#pragma unroll
+    for (int s = 0; s < kGemmNSub; ++s) {
+      if (s < nsub) {
+        const size_t row = static_cast<size_t>(b) * kGemmTokens + 16 * s + r16;
+        uint32_t packed[2];
+#pragma unroll
+        for (int v = 0; v < 4; v += 2) {
+          const float h0 = silu(acc[s][rt][v] * sg[v]) * (acc[s][RN + rt][v] * su[v]);
+          const float h1 = silu(acc[s][rt][v + 1] * sg[v + 1]) * (acc[s][RN + rt][v + 1] * su[v + 1]);
+          packed[v / 2] = static_cast<uint32_t>(f32_to_bf16(h0)) |
+                          (static_cast<uint32_t>(f32_to_bf16(h1)) << 16);
+        }
+        *reinterpret_cast<uint2*>(h + row * I + nb) = uint2{packed[0], packed[1]};
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------ W2 + gate scale
+//
+// Grid: x = row block b, y = group of 4 * 16 * RN output channels of d.
+// Writes y[f, n] = gate_f * s(n) * (W2[e] h[row])[n] for the block's slots.
+
+template <typename WT, int KC, int P, int RN>
+__global__ __launch_bounds__(kGemmThreads) void ffn2_gemm_kernel(
+    const bf16_t* __restrict__ h, const WT* __restrict__ w2, const float* __restrict__ s2,
+    int scale_mode, const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
+    const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded,
+    float* __restrict__ y, int d, int I, int A, int gx, int gy) {
+  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * kGemmTokens * Stager<KC>::kPitch];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  const TileId tid = tile_of(blockIdx.x, gx, gy);
+  const int b = tid.b;
+  if (!tid.live || b * kGemmTokens >= *num_padded) return;
+  const int e = block_expert[b];
+  const int32_t* blk = sorted_ids + static_cast<size_t>(b) * kGemmTokens;
+  const int nsub = live_subtiles<kGemmNSub>(blk, A);
+  const int n0 = (tid.y * kGemmWaves + wave) * 16 * RN;  // the channel groups tile d exactly
+
+  Stager<KC> st;
+  st.live = 0;
+#pragma unroll
+  for (int i = 0; i < Stager<KC>::kPieces; ++i) {
+    const int r = st.row(i);
+    const bool on = r < 16 * nsub && blk[r] < A;  // h rows of pads and dead sub-tiles: zero
+    st.live |= static_cast<uint32_t>(on) << i;
+    st.src[i] = h + (static_cast<size_t>(b) * kGemmTokens + (on ? r : 0)) * I + st.col();
+  }
+  WeightStream<WT, KC, RN, P> ws;
+  ws.g = g;
+  ws.nch = I / KC;
+#pragma unroll
+  for (int rt = 0; rt < RN; ++rt)
+    ws.row[rt] = w2 + (static_cast<size_t>(e) * d + n0 + rt * 16 + r16) * I;
+  f32x4 acc[kGemmNSub][RN];
+#pragma unroll
+  for (int s = 0; s < kGemmNSub; ++s)
+#pragma unroll
+    for (int r = 0; r < RN; ++r) acc[s][r] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  gemm_mainloop<WT, KC, P, RN>(ws, st, lds, acc);
+
+#pragma unroll
+  for (int s = 0; s < kGemmNSub; ++s) {
+    if (s < nsub) {
+      const int f = blk[16 * s + r16];
+      if (f < A) {
+        const float gate = topk_w[f];
+        float* yrow = y + static_cast<size_t>(f) * d;
+#pragma unroll
+        for (int rt = 0; rt < RN; ++rt) {
+          const int nb = n0 + rt * 16 + 4 * g;
+          float4 o;
+          o.x = acc[s][rt][0] * load_scale(s2, scale_mode, e, static_cast<size_t>(e) * d + nb) * gate;
+          o.y = acc[s][rt][1] * load_scale(s2, scale_mode, e, static_cast<size_t>(e) * d + nb + 1) * gate;
+          o.z = acc[s][rt][2] * load_scale(s2, scale_mode, e, static_cast<size_t>(e) * d + nb + 2) * gate;
+          o.w = acc[s][rt][3] * load_scale(s2, scale_mode, e, static_cast<size_t>(e) * d + nb + 3) * gate;
+          *reinterpret_cast<float4*>(yrow + nb) = o;
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------ launchers
+
+namespace {
+
+constexpr int kPG = MOE_GEMM_PIPE, kRNG = MOE_GEMM_RN;
+static_assert(kRNG == 1 || kRNG == 2, "channel tiles per wave: 1 or 2");
+
+// A workgroup covers 64 * RN output channels; the channel count is a
+// multiple of 64, and RN = 2 is used when it also divides by 128.
+template <typename WT, int KC, int RN>
+void ffn13_gemm_launch(const FfnArgs& a, hipStream_t s) {
+  constexpr int P = sizeof(WT) == 1 ? kPG + 1 : kPG;
+  const int gx = a.cap / kGemmTokens, gy = a.I / (kGemmWaves * 16 * RN);
+  ffn13_gemm_kernel<WT, KC, P, RN><<<raster_grid(gx, gy), kGemmThreads, 0, s>>>(
+      static_cast<const bf16_t*>(a.x), static_cast<const WT*>(a.w13), a.s13, a.scale_mode,
+      a.sorted_ids, a.block_expert, a.num_padded, static_cast<bf16_t*>(a.h), a.d, a.I, a.k, a.A,
+      gx, gy);
+}
+
+template <typename WT, int KC>
+void ffn13_gemm_go(const FfnArgs& a, hipStream_t s) {
+  if (kRNG == 2 && a.I % 128 == 0)
+    ffn13_gemm_launch<WT, KC, kRNG>(a, s);
+  else
+    ffn13_gemm_launch<WT, KC, 1>(a, s);
+}
+
+template <typename WT, int KC, int RN>
+void ffn2_gemm_launch(const FfnArgs& a, hipStream_t s) {
+  constexpr int P = sizeof(WT) == 1 ? kPG + 1 : kPG;
+  const int gx = a.cap / kGemmTokens, gy = a.d / (kGemmWaves * 16 * RN);
+  ffn2_gemm_kernel<WT, KC, P, RN><<<raster_grid(gx, gy), kGemmThreads, 0, s>>>(
+      static_cast<const bf16_t*>(a.h), static_cast<const WT*>(a.w2), a.s2, a.scale_mode,
+      a.topk_w, a.sorted_ids, a.block_expert, a.num_padded, a.y_part, a.d, a.I, a.A, gx, gy);
+}
+
+template <typename WT, int KC>
+void ffn2_gemm_go(const FfnArgs& a, hipStream_t s) {
+  if (kRNG == 2 && a.d % 128 == 0)
+    ffn2_gemm_launch<WT, KC, kRNG>(a, s);
+  else
+    ffn2_gemm_launch<WT, KC, 1>(a, s);
+}
+
+template <typename WT>
+hipError_t ffn13_gemm_w(const FfnArgs& a, hipStream_t s) {
+  if (a.d % 128 == 0)
+    ffn13_gemm_go<WT, 128>(a, s);
+  else
+    ffn13_gemm_go<WT, 64>(a, s);
+  return hipGetLastError();
+}
+
+template <typename WT>
+hipError_t ffn2_gemm_w(const FfnArgs& a, hipStream_t s) {
+  if (a.I % 128 == 0)
+    ffn2_gemm_go<WT, 128>(a, s);
+  else
+    ffn2_gemm_go<WT, 64>(a, s);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_ffn13_gemm(const FfnArgs& a, hipStream_t s) {
+  if (a.B != kGemmTokens) return hipErrorInvalidValue;
+  return a.w_dtype == kDtypeE4M3FN ? ffn13_gemm_w<fp8_t>(a, s) : ffn13_gemm_w<bf16_t>(a, s);
+}
+
+hipError_t launch_ffn2_gemm(const FfnArgs& a, hipStream_t s) {
+  if (a.B != kGemmTokens || a.splits != 1) return hipErrorInvalidValue;
+  return a.w_dtype == kDtypeE4M3FN ? ffn2_gemm_w<fp8_t>(a, s) : ffn2_gemm_w<bf16_t>(a, s);
+}
+
+}  // namespace moe

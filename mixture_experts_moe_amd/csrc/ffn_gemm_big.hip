@@ -1,0 +1,344 @@
+// Large-tile grouped GEMM for blocks of 256 tokens (prefill-sized expert
+// groups, bf16 weights): the MFMA-bound end of the fused MoE layer.
+//
+// Sources: the Hungarian news page "Az AWS új MoE-optimalizációkkal
+// gyorsítja a SageMaker AI-t", section "A fused MoE a számítási folyamat több
+// lépését egyesíti" (all experts' computation as one batched operation); the
+// French summary "Ingénierie de kernels Mixture-of-Experts sur Amazon
+// SageMaker AI", second paragraph (the expert product A[M,K] x B[K,N], tokens
+// x hidden x expert output dim).
+//
+// When an expert holds hundreds of tokens the product is a dense contraction
+// and the limit is how many bytes each MFMA needs.  A workgroup computes a
+// 256 x 256 tile (256 weight rows x 256 tokens, so every operand byte staged
+// in LDS feeds 256 MACs), four waves of 128 x 128 each on
+// v_mfma_f32_16x16x32_bf16.  Both operands move HBM/L2 -> LDS with gfx950's
+// direct-to-LDS 16-byte loads (no VGPR staging), in K stages of 32 (or 64)
+// elements through a ring of several stages, so the loads of the next
+// stages stay queued while the MFMAs of the current one run; one barrier per
+// stage.  An LDS row holds one stage of one operand row in 16-byte slots,
+// XOR-swizzled by row so that the 16 rows read by one 16-lane group for the
+// same k fall in 16 different bank groups.
+//
+// W13: the tile's rows are 128 gate rows then the 128 matching up rows, so
+// each wave holds gate and up of the same 64 channels and the epilogue writes
+// h = SiLU(gate) * up.  W2: 256 output channels; the epilogue scales by the
+// slot's gate.  The grid is rasterised per XCD like the 128-token GEMM.
+
+#include "ffn_common.h"
+
+namespace moe {
+
+// Stage shape (compile-time): K elements per stage and stages in the LDS ring
+// (their product bounds the LDS: stages * 2 operands * 256 rows * 2 * K bytes).
+#ifndef MOE_BIG_K
+#define MOE_BIG_K 64
+#endif
+#ifndef MOE_BIG_STAGES
+#define MOE_BIG_STAGES 2
+#endif
+constexpr int kBigThreads = 256;
+constexpr int kBigTokens = 256;  // block size B of this path
+constexpr int kBigRows = 256;    // weight rows per tile
+constexpr int kBigK = MOE_BIG_K;  // K elements per stage (32 or 64)
+constexpr int kBigStages = MOE_BIG_STAGES;
+constexpr int kBigSlots = kBigK / 8;                 // 16-byte slots per LDS row
+constexpr int kBigRowBytes = kBigK * 2;
+constexpr int kBigRowsPerGroup = 1024 / kBigRowBytes;  // rows filled by one 1 KB load
+constexpr int kBigGroups = kBigRows / kBigRowsPerGroup / 4;  // per wave and operand
+constexpr int kBigOperandBytes = kBigRows * kBigRowBytes;
+constexpr int kBigStageBytes = 2 * kBigOperandBytes;
+static_assert(kBigK == 32 || kBigK == 64, "stage K");
+static_assert(kBigStages >= 2 && kBigStages * kBigStageBytes <= 160 * 1024, "LDS");
+#ifndef MOE_BIG_RASTER
+#define MOE_BIG_RASTER 1
+#endif
+#ifndef MOE_BIG_GROUP_COLS
+#define MOE_BIG_GROUP_COLS 4
+#endif
+constexpr int kBigXcds = MOE_BIG_RASTER ? 8 : 1;  // 1: plain order, no XCD remap
+constexpr int kBigGroupCols = MOE_BIG_GROUP_COLS;
+
+// Slot swizzle: with 8 slots per row (K = 64) rows pair up per bank line, with
+// 4 slots (K = 32) four rows share one; either way the 16 rows one 16-lane
+// group reads for the same k land in 16 different 16-byte bank groups.
+__device__ __forceinline__ int big_swz(int row) {
+  return kBigSlots == 8 ? (row >> 1) & 7 : (row >> 2) & 3;
+}
+
+struct BigTile {
+  int b, y;
+  bool live;
+};
+
+// Same rasterisation as the 128-token GEMM: contiguous runs of the logical
+// order per XCD, super-rows of kBigGroupCols channel groups, row block
+// slowest inside a super-row.
+__device__ __forceinline__ BigTile big_tile_of(int p, int gx, int gy) {
+  const int total = gx * gy;
+  const int per_xcd = (total + kBigXcds - 1) / kBigXcds;
+  const int l = (p % kBigXcds) * per_xcd + p / kBigXcds;
+  BigTile t{0, 0, l < total};
+  if (!t.live) return t;
+  const int band = kBigGroupCols * gx;
+  const int sr = l / band;
+  const int rem = l - sr * band;
+  const int cols = min(kBigGroupCols, gy - sr * kBigGroupCols);
+  t.b = rem / cols;
+  t.y = sr * kBigGroupCols + rem % cols;
+  return t;
+}
+
+// Each wave fills kBigGroups consecutive 1 KB groups (kBigRowsPerGroup rows
+// each) of an operand per stage: in group q, lane l writes tile row
+// 64*wave + kBigRowsPerGroup*q + l/kBigSlots, physical slot l%kBigSlots,
+// which holds logical slot (l%kBigSlots) ^ swz(row).  swz(row) depends on q
+// only through q's parity, so a lane's weight sources are two bases plus a
+// stride; token sources (gathered x rows, or h rows) are one pointer per
+// group.
+struct BigLoader {
+  const bf16_t* a_even;  // A source of group 0 (q even), at k = 0
+  const bf16_t* a_odd;   // A source of group 1 (q odd)
+  size_t a_step;         // elements between groups q and q + 2
+
+  __device__ __forceinline__ const bf16_t* a_src(int q, int k0) const {
+    return (q & 1 ? a_odd : a_even) + (q >> 1) * a_step + k0;
+  }
+};
+
+__device__ __forceinline__ void big_issue(const BigLoader& ld,
+                                          const bf16_t* const (&bsrc)[kBigGroups],
+                                          uint8_t* stage, int k0, int wave) {
+#pragma unroll
+  for (int q = 0; q < kBigGroups; ++q)
+    __builtin_amdgcn_global_load_lds(ld.a_src(q, k0), stage + (wave * kBigGroups + q) * 1024, 16,
+                                     0, 0);
+#pragma unroll
+  for (int q = 0; q < kBigGroups; ++q)
+    __builtin_amdgcn_global_load_lds(bsrc[q] + k0,
+                                     stage + kBigOperandBytes + (wave * kBigGroups + q) * 1024, 16,
+                                     0, 0);
+}
+
+// s_waitcnt immediate that waits until at most n vector-memory loads are
+// outstanding (lgkm and exp counters not waited on).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// 16-byte MFMA fragment of tile row `row`, logical slot `slot`.
+__device__ __forceinline__ bf16x8 big_frag(const uint8_t* op, int row, int slot) {
+  return as_frag(*reinterpret_cast<const uint4*>(op + row * kBigRowBytes +
+                                                 ((slot ^ big_swz(row)) << 4)));
+}
+
+struct BigFrags {
+  bf16x8 a[8], b[8];
+};
+
+// Fragments of k-step j (k = 32j .. 32j+31 of the stage) for this wave's
+// 8 row tiles (rows arow0 + 16t) and 8 token tiles (rows brow0 + 16u).
+__device__ __forceinline__ void big_load_frags(BigFrags& f, const uint8_t* opa, const uint8_t* opb,
+                                               int arow0, int arow_up, int brow0, int j) {
+  const int lane = threadIdx.x & 63;
+  const int r16 = lane & 15;
+  const int slot = 4 * j + (lane >> 4);  // lane group g: k = 32j + 8g .. +8
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+    f.a[t] = big_frag(opa, (t < 4 ? arow0 + 16 * t : arow_up + 16 * (t - 4)) + r16, slot);
+#pragma unroll
+  for (int u = 0; u < 8; ++u) f.b[u] = big_frag(opb, brow0 + 16 * u + r16, slot);
+}
+
+__device__ __forceinline__ void big_mma(const BigFrags& f, f32x4 (&acc)[8][8]) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[t][u] = mfma16x16x32(f.a[t], f.b[u], acc[t][u]);
+}
+
+// acc[t][u] += A_rows(t) . B_rows(u)^T over K.  A rows: arow0 + 16t (t < 4)
+// and arow_up + 16(t-4); B rows: brow0 + 16u.  Ring of kBigStages stages:
+// stages 0 .. S-2 are issued up front; at stage s a wave waits until its own
+// loads of stage s have landed (later stages may stay in flight), meets the
+// other waves at the barrier (after which the buffer read at stage s-1 is
+// free), issues stage s + S - 1 into that buffer and runs stage s's MFMAs.
+__device__ __forceinline__ void big_mainloop(const BigLoader& ld,
+                                             const bf16_t* const (&bsrc)[kBigGroups],
+                                             uint8_t* lds, int nst, int wave, int arow0,
+                                             int arow_up, int brow0, f32x4 (&acc)[8][8]) {
+  constexpr int kLoads = 2 * kBigGroups;  // per wave and stage
+#pragma unroll
+  for (int s = 0; s < kBigStages - 1; ++s)
+    if (s < nst) big_issue(ld, bsrc, lds + s * kBigStageBytes, s * kBigK, wave);
+  for (int s = 0; s < nst; ++s) {
+    if (s + kBigStages - 2 < nst)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoads * (kBigStages - 2)));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // tail: fewer stages behind this one
+    __syncthreads();
+    const int sn = s + kBigStages - 1;
+    if (sn < nst) big_issue(ld, bsrc, lds + (sn % kBigStages) * kBigStageBytes, sn * kBigK, wave);
+    const uint8_t* opa = lds + (s % kBigStages) * kBigStageBytes;
+    const uint8_t* opb = opa + kBigOperandBytes;
+    BigFrags f[kBigK / 32];
+#pragma unroll
+    for (int j = 0; j < kBigK / 32; ++j) big_load_frags(f[j], opa, opb, arow0, arow_up, brow0, j);
+#pragma unroll
+    for (int j = 0; j < kBigK / 32; ++j) big_mma(f[j], acc);
+  }
+}
+
+// ------------------------------------------------------------ W13 + SiLU*mul
+// Tile: channels n0 .. n0+127 (rows: 128 gate, then 128 up) x 256 tokens.
+
+__global__ __launch_bounds__(kBigThreads) void ffn13_big_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ w13,
+    const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ block_expert,
+    const int32_t* __restrict__ num_padded, bf16_t* __restrict__ h, int d, int I, int k, int A,
+    int gx, int gy) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kBigStages * kBigStageBytes];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  const BigTile tl = big_tile_of(blockIdx.x, gx, gy);
+  if (!tl.live || tl.b * kBigTokens >= *num_padded) return;  // uniform
+  const int b = tl.b;
+  const int e = block_expert[b];
+  const int n0 = tl.y * 128;
+  const int32_t* blk = sorted_ids + static_cast<size_t>(b) * kBigTokens;
+  const size_t two_i = 2 * static_cast<size_t>(I);
+
+  // tile rows: 0..127 gate rows n0.., 128..255 the matching up rows
+  BigLoader ld;
+  const int lrow = lane / kBigSlots;  // row within a 1 KB group
+  const int c_even = ((lane % kBigSlots) ^ big_swz(lrow)) * 8;
+  const int c_odd = ((lane % kBigSlots) ^ big_swz(kBigRowsPerGroup + lrow)) * 8;
+  const int row0 = 64 * wave + lrow;  // tile row of group 0
+  const size_t wrow0 = static_cast<size_t>(e) * two_i + (wave < 2 ? n0 + row0 : I + n0 + row0 - 128);
+  ld.a_even = w13 + wrow0 * d + c_even;
+  ld.a_odd = w13 + (wrow0 + kBigRowsPerGroup) * d + c_odd;
+  ld.a_step = static_cast<size_t>(2 * kBigRowsPerGroup) * d;
+  const bf16_t* bsrc[kBigGroups];
+#pragma unroll
+  for (int q = 0; q < kBigGroups; ++q) {
+    const int f = blk[row0 + kBigRowsPerGroup * q];  // pad slot: any valid row (never stored)
+    bsrc[q] = x + static_cast<size_t>(f < A ? f / k : 0) * d + (q & 1 ? c_odd : c_even);
+  }
+  const int wm = wave & 1, wn = wave >> 1;
+  f32x4 acc[8][8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  big_mainloop(ld, bsrc, lds, d / kBigK, wave, 64 * wm, 128 + 64 * wm, 128 * wn, acc);
+
+  // lane: token column r16 of tile u, channels n0 + 64wm + 16t + 4g .. +3
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const size_t row = static_cast<size_t>(b) * kBigTokens + 128 * wn + 16 * u + r16;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      uint32_t packed[2];
+#pragma unroll
+      for (int v = 0; v < 4; v += 2) {
+        const float h0 = silu(acc[t][u][v]) * acc[t + 4][u][v];
+        const float h1 = silu(acc[t][u][v + 1]) * acc[t + 4][u][v + 1];
+        packed[v / 2] = static_cast<uint32_t>(f32_to_bf16(h0)) |
+                        (static_cast<uint32_t>(f32_to_bf16(h1)) << 16);
+      }
+      *reinterpret_cast<uint2*>(h + row * I + n0 + 64 * wm + 16 * t + 4 * g) =
+          uint2{packed[0], packed[1]};
+    }
+  }
+}
+
+// ------------------------------------------------------------ W2 + gate scale
+// Tile: output channels n0 .. n0+255 x 256 tokens (h rows of the block).
+
+__global__ __launch_bounds__(kBigThreads) void ffn2_big_kernel(
+    const bf16_t* __restrict__ h, const bf16_t* __restrict__ w2,
+    const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
+    const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded,
+    float* __restrict__ y, int d, int I, int A, int gx, int gy) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kBigStages * kBigStageBytes];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  const BigTile tl = big_tile_of(blockIdx.x, gx, gy);
+  if (!tl.live || tl.b * kBigTokens >= *num_padded) return;
+  const int b = tl.b;
+  const int e = block_expert[b];
+  const int n0 = tl.y * kBigRows;
+  const int32_t* blk = sorted_ids + static_cast<size_t>(b) * kBigTokens;
+
+  BigLoader ld;
+  const int lrow = lane / kBigSlots;
+  const int c_even = ((lane % kBigSlots) ^ big_swz(lrow)) * 8;
+  const int c_odd = ((lane % kBigSlots) ^ big_swz(kBigRowsPerGroup + lrow)) * 8;
+  const int row0 = 64 * wave + lrow;
+  ld.a_even = w2 + (static_cast<size_t>(e) * d + n0 + row0) * I + c_even;
+  ld.a_odd = w2 + (static_cast<size_t>(e) * d + n0 + row0 + kBigRowsPerGroup) * I + c_odd;
+  ld.a_step = static_cast<size_t>(2 * kBigRowsPerGroup) * I;
+  // h rows of the block; pad slots hold no token and their columns are never stored
+  const bf16_t* bsrc[kBigGroups];
+  const bf16_t* hb = h + (static_cast<size_t>(b) * kBigTokens + row0) * I;
+#pragma unroll
+  for (int q = 0; q < kBigGroups; ++q)
+    bsrc[q] = hb + static_cast<size_t>(kBigRowsPerGroup * q) * I + (q & 1 ? c_odd : c_even);
+  const int wm = wave & 1, wn = wave >> 1;
+  f32x4 acc[8][8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // A rows 128*wm .. +127: eight consecutive 16-row tiles
+  big_mainloop(ld, bsrc, lds, I / kBigK, wave, 128 * wm, 128 * wm + 64, 128 * wn, acc);
+
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int f = blk[128 * wn + 16 * u + r16];
+    if (f < A) {
+      const float gate = topk_w[f];
+      float* yrow = y + static_cast<size_t>(f) * d + n0 + 128 * wm + 4 * g;
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        *reinterpret_cast<float4*>(yrow + 16 * t) =
+            float4{acc[t][u][0] * gate, acc[t][u][1] * gate, acc[t][u][2] * gate,
+                   acc[t][u][3] * gate};
+    }
+  }
+}
+
+// ------------------------------------------------------------ launchers
+
+bool big_gemm_fits(int d, int I) { return d % 256 == 0 && I % 128 == 0; }
+
+static int big_grid(int gx, int gy) {
+  const int total = gx * gy;
+  return (total + kBigXcds - 1) / kBigXcds * kBigXcds;
+}
+
+hipError_t launch_ffn13_big(const FfnArgs& a, hipStream_t s) {
+  if (a.B != kBigTokens || a.w_dtype != kDtypeBF16 || !big_gemm_fits(a.d, a.I))
+    return hipErrorInvalidValue;
+  const int gx = a.cap / kBigTokens, gy = a.I / 128;
+  ffn13_big_kernel<<<big_grid(gx, gy), kBigThreads, 0, s>>>(
+      static_cast<const bf16_t*>(a.x), static_cast<const bf16_t*>(a.w13), a.sorted_ids,
+      a.block_expert, a.num_padded, static_cast<bf16_t*>(a.h), a.d, a.I, a.k, a.A, gx, gy);
+  return hipGetLastError();
+}
+
+hipError_t launch_ffn2_big(const FfnArgs& a, hipStream_t s) {
+  if (a.B != kBigTokens || a.w_dtype != kDtypeBF16 || !big_gemm_fits(a.d, a.I) || a.splits != 1)
+    return hipErrorInvalidValue;
+  const int gx = a.cap / kBigTokens, gy = a.d / kBigRows;
+  ffn2_big_kernel<<<big_grid(gx, gy), kBigThreads, 0, s>>>(
+      static_cast<const bf16_t*>(a.h), static_cast<const bf16_t*>(a.w2), a.topk_w, a.sorted_ids,
+      a.block_expert, a.num_padded, a.y_part, a.d, a.I, a.A, gx, gy);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -50,6 +50,15 @@ struct FfnArgs {
 hipError_t launch_ffn13(const FfnArgs& a, hipStream_t s);
 hipError_t launch_ffn2(const FfnArgs& a, hipStream_t s);
 hipError_t launch_combine(const FfnArgs& a, hipStream_t s);
+// Token-tiled grouped GEMM (block size 128, no K split); used by the two
+// launchers above when a.B == 128.
+hipError_t launch_ffn13_gemm(const FfnArgs& a, hipStream_t s);
+hipError_t launch_ffn2_gemm(const FfnArgs& a, hipStream_t s);
+// Large-tile grouped GEMM (block size 256, bf16 weights, d % 256 == 0 and
+// I % 128 == 0); used when a.B == 256.
+bool big_gemm_fits(int d, int I);
+hipError_t launch_ffn13_big(const FfnArgs& a, hipStream_t s);
+hipError_t launch_ffn2_big(const FfnArgs& a, hipStream_t s);
 
 // K chunk the W2 kernel uses for a given I and weight dtype (the split
 // length must be a multiple of it).

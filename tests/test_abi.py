@@ -65,7 +65,11 @@ def ws_status(lib, dsc, k=2):
     (dict(act=B.MOE_DTYPE_E4M3FN, w=B.MOE_DTYPE_E4M3FN), 2, -4),
     (dict(act=B.MOE_DTYPE_F32, w=B.MOE_DTYPE_E4M3FN), 2, -4),
     (dict(bm=48), 2, -8),
-    (dict(bm=256), 2, -8),
+    (dict(bm=256), 2, -8),                               # d = 128: the 256 GEMM needs d % 256 == 0
+    (dict(d=256, bm=256), 2, 0),
+    (dict(d=256, I=64, bm=256), 2, -8),                  # I % 128 != 0
+    (dict(d=256, w=B.MOE_DTYPE_E4M3FN, bm=256), 2, -8),  # bf16 weights only
+    (dict(bm=512), 2, -8),
     (dict(T=1 << 28), 8, -2),
 ])
 def test_descriptor_validation(lib, kw, k, status):
@@ -91,8 +95,12 @@ def test_capacity_formula(lib, T, E, k, bm):
 
 
 def test_default_block_covers_a_decode_batch(lib):
-    for T, want in [(1, 16), (8, 16), (16, 16), (17, 32), (32, 32), (64, 64)]:
+    for T, want in [(1, 16), (8, 16), (16, 16), (17, 32), (32, 32), (64, 64), (65, 128)]:
         assert B.moe_align_capacity(desc(T=T), 2)[0] == want
+    # experts averaging >= 256 tokens with fitting bf16 shapes use the 256 GEMM
+    assert B.moe_align_capacity(desc(T=4096, d=4096, I=14336), 2)[0] == 256
+    assert B.moe_align_capacity(desc(T=4096, d=2880, I=2880), 2)[0] == 128
+    assert B.moe_align_capacity(desc(T=4096, d=4096, I=14336, w=B.MOE_DTYPE_E4M3FN), 2)[0] == 128
     assert B.moe_align_capacity(desc(act=B.MOE_DTYPE_F32, w=B.MOE_DTYPE_F32), 2)[0] == 16
 
 

@@ -122,6 +122,9 @@ SMALL = [
     ("bf16_ragged", dict(workload="decode_bf16", d=512, I=448, x_std=1.0), 257, 16),
     ("bf16_ragged", dict(workload="decode_bf16", d=512, I=448, x_std=1.0), 257, 128),
     ("bf16_d320", dict(workload="decode_bf16", d=320, I=192, x_std=1.0), 100, 32),
+    ("bf16_big", dict(workload="decode_bf16", d=512, I=384, E=4, x_std=1.0), 700, 256),
+    ("bf16_big", dict(workload="decode_bf16", d=256, I=128, E=8, k=2, x_std=1.0), 1500, 0),
+    ("bf16_big", dict(workload="decode_bf16", d=768, I=256, E=3, k=1, x_std=1.0), 300, 256),
     ("bf16_kE", dict(workload="decode_bf16", d=128, I=128, E=8, k=8, x_std=1.0), 40, 0),
     ("bf16_E1", dict(workload="decode_bf16", d=256, I=128, E=1, k=1, x_std=1.0), 37, 0),
     ("fp8_channel", dict(workload="fp8", d=256, I=192, E=16, k=4), 3, 0),
