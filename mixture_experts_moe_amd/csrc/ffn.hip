@@ -376,8 +376,12 @@ constexpr int kP2 = MOE_FFN2_PIPE, kRN2 = MOE_FFN2_RN;
 // Channel tiles per wave: two when that still leaves at least eight waves
 // per CU (x loads are shared by twice the weight rows), else one (twice the
 // waves, for small batches that touch few experts).
-inline int pick_rn(int blocks_est, int channels, int rn_max) {
-  return (rn_max >= 2 && int64_t(blocks_est) * (channels / 32) >= 8 * 256) ? 2 : 1;
+#ifndef MOE_RN2_MAX_NSUB
+#define MOE_RN2_MAX_NSUB 4
+#endif
+inline int pick_rn(int blocks_est, int channels, int rn_max, int nsub) {
+  return (rn_max >= 2 && nsub <= MOE_RN2_MAX_NSUB &&
+          int64_t(blocks_est) * (channels / 32) >= 8 * 256) ? 2 : 1;
 }
 
 inline int blocks_estimate(const FfnArgs& a) {
@@ -397,7 +401,7 @@ void ffn13_launch(const FfnArgs& a, hipStream_t s) {
 template <typename WT, int NSUB, int KC>
 void ffn13_go(const FfnArgs& a, hipStream_t s) {
   static_assert(kRN13 == 1 || kRN13 == 2, "channel tiles per wave: 1 or 2");
-  if (pick_rn(blocks_estimate(a), a.I, kRN13) == 2)
+  if (pick_rn(blocks_estimate(a), a.I, kRN13, NSUB) == 2)
     ffn13_launch<WT, NSUB, KC, kRN13>(a, s);
   else
     ffn13_launch<WT, NSUB, KC, 1>(a, s);
@@ -434,7 +438,7 @@ void ffn2_launch(const FfnArgs& a, hipStream_t s) {
 template <typename WT, int NSUB, int KC>
 void ffn2_go(const FfnArgs& a, hipStream_t s) {
   static_assert(kRN2 == 1 || kRN2 == 2, "channel tiles per wave: 1 or 2");
-  if (pick_rn(blocks_estimate(a) * a.splits, a.d, kRN2) == 2)
+  if (pick_rn(blocks_estimate(a) * a.splits, a.d, kRN2, NSUB) == 2)
     ffn2_launch<WT, NSUB, KC, kRN2>(a, s);
   else
     ffn2_launch<WT, NSUB, KC, 1>(a, s);

@@ -24,8 +24,10 @@
 
 namespace moe {
 
-constexpr int kGemmWaves = 4;
-constexpr int kGemmThreads = 64 * kGemmWaves;
+// Waves per workgroup (each wave owns 16 * RN output channels; the waves
+// share the token tile).  Measured: W13 runs best with 4, W2 with 8.
+constexpr int kWaves13 = 4;
+constexpr int kWaves2 = 8;
 constexpr int kGemmTokens = 128;  // block size B of this path
 constexpr int kGemmNSub = kGemmTokens / 16;
 
@@ -37,13 +39,13 @@ constexpr int kGemmNSub = kGemmTokens / 16;
 #endif
 
 // Rows of the token tile this thread stages: KC/8 16-byte pieces per row,
-// piece q = tid + 256*i, row = q / (KC/8).  Rows that hold no token (pad
-// slots, dead sub-tiles) read a valid address and are zeroed with a select,
-// so staging has no branches.
-template <int KC>
+// piece q = tid + 64*WAVES*i, row = q / (KC/8).  Rows that hold no token
+// (pad slots, dead sub-tiles) read a valid address and are zeroed with a
+// select, so staging has no branches (branching here measured slower).
+template <int KC, int WAVES>
 struct Stager {
   static constexpr int kPiecesPerRow = KC / 8;
-  static constexpr int kRowsPerPass = kGemmThreads / kPiecesPerRow;
+  static constexpr int kRowsPerPass = 64 * WAVES / kPiecesPerRow;
   static constexpr int kPieces = kGemmTokens / kRowsPerPass;  // per thread
   static constexpr int kPitch = KC + 8;                       // elements per LDS row
   const bf16_t* src[kPieces];  // row start + piece column (a valid row if dead)
@@ -107,16 +109,19 @@ inline int raster_grid(int gx, int gy) {
   return (total + kXcds - 1) / kXcds * kXcds;
 }
 
-// Shared main loop: acc[s][r] += W_rows[r] . tokens[s]^T over all K.  All
-// eight 16-token sub-tiles are computed (a partly filled block wastes MFMA
-// slots, not memory traffic); the only branches are the uniform loop ones.
-template <typename WT, int KC, int P, int NROW>
+// Shared main loop: acc[s][r] += W_rows[r] . tokens[s]^T over all K.  The
+// block's sub-tiles are processed in two halves of four; the second half is
+// skipped (one uniform branch) when it holds no token, which halves the MFMA
+// work of blocks that are at most half full.  Inside a half every sub-tile
+// is computed, branch-free.
+template <typename WT, int KC, int P, int NROW, int WAVES>
 __device__ __forceinline__ void gemm_mainloop(WeightStream<WT, KC, NROW, P>& ws,
-                                              Stager<KC>& st, bf16_t* lds,
+                                              Stager<KC, WAVES>& st, bf16_t* lds, bool upper_half,
                                               f32x4 (&acc)[kGemmNSub][NROW]) {
   constexpr int NF = KC / 32;
-  constexpr int kPitch = Stager<KC>::kPitch;
+  constexpr int kPitch = Stager<KC, WAVES>::kPitch;
   constexpr int kBuf = kGemmTokens * kPitch;
+  constexpr int kHalf = kGemmNSub / 2;
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15;
   const int g = lane >> 4;
@@ -139,11 +144,24 @@ __device__ __forceinline__ void gemm_mainloop(WeightStream<WT, KC, NROW, P>& ws,
         for (int i = 0; i < NF; ++i) {
           const int off = ActChunk<WT, KC>::off(i, g);
 #pragma unroll
-          for (int s = 0; s < kGemmNSub; ++s) {
+          for (int s = 0; s < kHalf; ++s) {
             const bf16x8 bf =
                 as_frag(*reinterpret_cast<const uint4*>(tile + (16 * s + r16) * kPitch + off));
 #pragma unroll
             for (int r = 0; r < NROW; ++r) acc[s][r] = mfma16x16x32(wf[r][i], bf, acc[s][r]);
+          }
+        }
+        if (upper_half) {
+#pragma unroll
+          for (int i = 0; i < NF; ++i) {
+            const int off = ActChunk<WT, KC>::off(i, g);
+#pragma unroll
+            for (int s = kHalf; s < kGemmNSub; ++s) {
+              const bf16x8 bf =
+                  as_frag(*reinterpret_cast<const uint4*>(tile + (16 * s + r16) * kPitch + off));
+#pragma unroll
+              for (int r = 0; r < NROW; ++r) acc[s][r] = mfma16x16x32(wf[r][i], bf, acc[s][r]);
+            }
           }
         }
         st.store(lds + ((c + 1) & 1) * kBuf);  // (after the last chunk: unread)
@@ -158,13 +176,13 @@ __device__ __forceinline__ void gemm_mainloop(WeightStream<WT, KC, NROW, P>& ws,
 // Grid: x = row block b (128 tokens of one expert), y = group of
 // 4 * 16 * RN output channels of I.
 
-template <typename WT, int KC, int P, int RN>
-__global__ __launch_bounds__(kGemmThreads) void ffn13_gemm_kernel(
+template <typename WT, int KC, int P, int RN, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void ffn13_gemm_kernel(
     const bf16_t* __restrict__ x, const WT* __restrict__ w13, const float* __restrict__ s13,
     int scale_mode, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded,
     bf16_t* __restrict__ h, int d, int I, int k, int A, int gx, int gy) {
-  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * kGemmTokens * Stager<KC>::kPitch];
+  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * kGemmTokens * Stager<KC, WAVES>::kPitch];
   constexpr int NROW = 2 * RN;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -176,12 +194,12 @@ __global__ __launch_bounds__(kGemmThreads) void ffn13_gemm_kernel(
   const int e = block_expert[b];
   const int32_t* blk = sorted_ids + static_cast<size_t>(b) * kGemmTokens;
   const int nsub = live_subtiles<kGemmNSub>(blk, A);
-  const int n0 = (tid.y * kGemmWaves + wave) * 16 * RN;  // the channel groups tile I exactly
+  const int n0 = (tid.y * WAVES + wave) * 16 * RN;  // the channel groups tile I exactly
 
-  Stager<KC> st;
+  Stager<KC, WAVES> st;
   st.live = 0;
 #pragma unroll
-  for (int i = 0; i < Stager<KC>::kPieces; ++i) {
+  for (int i = 0; i < Stager<KC, WAVES>::kPieces; ++i) {
     const int f = blk[st.row(i)];
     const bool on = f < A;
     st.live |= static_cast<uint32_t>(on) << i;
@@ -202,7 +220,7 @@ __global__ __launch_bounds__(kGemmThreads) void ffn13_gemm_kernel(
 #pragma unroll
     for (int r = 0; r < NROW; ++r) acc[s][r] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  gemm_mainloop<WT, KC, P, NROW>(ws, st, lds, acc);
+  gemm_mainloop<WT, KC, P, NROW, WAVES>(ws, st, lds, nsub > kGemmNSub / 2, acc);
 
 #pragma unroll
   for (int rt = 0; rt < RN; ++rt) {
@@ -236,13 +254,13 @@ __global__ __launch_bounds__(kGemmThreads) void ffn13_gemm_kernel(
 // Grid: x = row block b, y = group of 4 * 16 * RN output channels of d.
 // Writes y[f, n] = gate_f * s(n) * (W2[e] h[row])[n] for the block's slots.
 
-template <typename WT, int KC, int P, int RN>
-__global__ __launch_bounds__(kGemmThreads) void ffn2_gemm_kernel(
+template <typename WT, int KC, int P, int RN, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void ffn2_gemm_kernel(
     const bf16_t* __restrict__ h, const WT* __restrict__ w2, const float* __restrict__ s2,
     int scale_mode, const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded,
     float* __restrict__ y, int d, int I, int A, int gx, int gy) {
-  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * kGemmTokens * Stager<KC>::kPitch];
+  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * kGemmTokens * Stager<KC, WAVES>::kPitch];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r16 = lane & 15;
@@ -253,12 +271,12 @@ __global__ __launch_bounds__(kGemmThreads) void ffn2_gemm_kernel(
   const int e = block_expert[b];
   const int32_t* blk = sorted_ids + static_cast<size_t>(b) * kGemmTokens;
   const int nsub = live_subtiles<kGemmNSub>(blk, A);
-  const int n0 = (tid.y * kGemmWaves + wave) * 16 * RN;  // the channel groups tile d exactly
+  const int n0 = (tid.y * WAVES + wave) * 16 * RN;  // the channel groups tile d exactly
 
-  Stager<KC> st;
+  Stager<KC, WAVES> st;
   st.live = 0;
 #pragma unroll
-  for (int i = 0; i < Stager<KC>::kPieces; ++i) {
+  for (int i = 0; i < Stager<KC, WAVES>::kPieces; ++i) {
     const int r = st.row(i);
     const bool on = r < 16 * nsub && blk[r] < A;  // h rows of pads and dead sub-tiles: zero
     st.live |= static_cast<uint32_t>(on) << i;
@@ -276,7 +294,7 @@ __global__ __launch_bounds__(kGemmThreads) void ffn2_gemm_kernel(
 #pragma unroll
     for (int r = 0; r < RN; ++r) acc[s][r] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  gemm_mainloop<WT, KC, P, RN>(ws, st, lds, acc);
+  gemm_mainloop<WT, KC, P, RN, WAVES>(ws, st, lds, nsub > kGemmNSub / 2, acc);
 
 #pragma unroll
   for (int s = 0; s < kGemmNSub; ++s) {
@@ -307,13 +325,14 @@ namespace {
 constexpr int kPG = MOE_GEMM_PIPE, kRNG = MOE_GEMM_RN;
 static_assert(kRNG == 1 || kRNG == 2, "channel tiles per wave: 1 or 2");
 
-// A workgroup covers 64 * RN output channels; the channel count is a
-// multiple of 64, and RN = 2 is used when it also divides by 128.
-template <typename WT, int KC, int RN>
+// A workgroup covers 16 * RN * WAVES output channels; the launchers pick the
+// widest configuration whose channel group divides the channel count (a
+// multiple of 64, so 4 waves x 16 channels always fits).
+template <typename WT, int KC, int RN, int WAVES>
 void ffn13_gemm_launch(const FfnArgs& a, hipStream_t s) {
   constexpr int P = sizeof(WT) == 1 ? kPG + 1 : kPG;
-  const int gx = a.cap / kGemmTokens, gy = a.I / (kGemmWaves * 16 * RN);
-  ffn13_gemm_kernel<WT, KC, P, RN><<<raster_grid(gx, gy), kGemmThreads, 0, s>>>(
+  const int gx = a.cap / kGemmTokens, gy = a.I / (WAVES * 16 * RN);
+  ffn13_gemm_kernel<WT, KC, P, RN, WAVES><<<raster_grid(gx, gy), 64 * WAVES, 0, s>>>(
       static_cast<const bf16_t*>(a.x), static_cast<const WT*>(a.w13), a.s13, a.scale_mode,
       a.sorted_ids, a.block_expert, a.num_padded, static_cast<bf16_t*>(a.h), a.d, a.I, a.k, a.A,
       gx, gy);
@@ -321,27 +340,27 @@ void ffn13_gemm_launch(const FfnArgs& a, hipStream_t s) {
 
 template <typename WT, int KC>
 void ffn13_gemm_go(const FfnArgs& a, hipStream_t s) {
-  if (kRNG == 2 && a.I % 128 == 0)
-    ffn13_gemm_launch<WT, KC, kRNG>(a, s);
+  if (kRNG == 2 && a.I % (kWaves13 * 32) == 0)
+    ffn13_gemm_launch<WT, KC, kRNG, kWaves13>(a, s);
   else
-    ffn13_gemm_launch<WT, KC, 1>(a, s);
+    ffn13_gemm_launch<WT, KC, 1, kWaves13>(a, s);
 }
 
-template <typename WT, int KC, int RN>
+template <typename WT, int KC, int RN, int WAVES>
 void ffn2_gemm_launch(const FfnArgs& a, hipStream_t s) {
   constexpr int P = sizeof(WT) == 1 ? kPG + 1 : kPG;
-  const int gx = a.cap / kGemmTokens, gy = a.d / (kGemmWaves * 16 * RN);
-  ffn2_gemm_kernel<WT, KC, P, RN><<<raster_grid(gx, gy), kGemmThreads, 0, s>>>(
+  const int gx = a.cap / kGemmTokens, gy = a.d / (WAVES * 16 * RN);
+  ffn2_gemm_kernel<WT, KC, P, RN, WAVES><<<raster_grid(gx, gy), 64 * WAVES, 0, s>>>(
       static_cast<const bf16_t*>(a.h), static_cast<const WT*>(a.w2), a.s2, a.scale_mode,
       a.topk_w, a.sorted_ids, a.block_expert, a.num_padded, a.y_part, a.d, a.I, a.A, gx, gy);
 }
 
 template <typename WT, int KC>
 void ffn2_gemm_go(const FfnArgs& a, hipStream_t s) {
-  if (kRNG == 2 && a.d % 128 == 0)
-    ffn2_gemm_launch<WT, KC, kRNG>(a, s);
+  if (a.d % (kWaves2 * 16 * kRNG) == 0)
+    ffn2_gemm_launch<WT, KC, kRNG, kWaves2>(a, s);
   else
-    ffn2_gemm_launch<WT, KC, 1>(a, s);
+    ffn2_gemm_launch<WT, KC, 1, 4>(a, s);
 }
 
 template <typename WT>
