@@ -13,10 +13,9 @@
 // 256 x 256 tile (256 weight rows x 256 tokens, so every operand byte staged
 // in LDS feeds 256 MACs), four waves of 128 x 128 each on
 // v_mfma_f32_16x16x32_bf16.  Both operands move HBM/L2 -> LDS with gfx950's
-// direct-to-LDS 16-byte loads (no VGPR staging), in K stages of 32 (or 64)
-// elements through a ring of several stages, so the loads of the next
-// stages stay queued while the MFMAs of the current one run; one barrier per
-// stage.  An LDS row holds one stage of one operand row in 16-byte slots,
+// direct-to-LDS 16-byte loads (no VGPR staging), in K stages of 64 elements
+// through two LDS buffers, so the loads of the next stage are in flight while
+// the MFMAs of the current one run; one barrier per stage.  An LDS row holds one stage of one operand row in 16-byte slots,
 // XOR-swizzled by row so that the 16 rows read by one 16-lane group for the
 // same k fall in 16 different bank groups.
 //
@@ -29,27 +28,18 @@
 
 namespace moe {
 
-// Stage shape (compile-time): K elements per stage and stages in the LDS ring
-// (their product bounds the LDS: stages * 2 operands * 256 rows * 2 * K bytes).
-#ifndef MOE_BIG_K
-#define MOE_BIG_K 64
-#endif
-#ifndef MOE_BIG_STAGES
-#define MOE_BIG_STAGES 2
-#endif
+// Stage shape: 2 buffers x 2 operands x 256 rows x 64 K x 2 bytes = 128 KB LDS.
 constexpr int kBigThreads = 256;
 constexpr int kBigTokens = 256;  // block size B of this path
 constexpr int kBigRows = 256;    // weight rows per tile
-constexpr int kBigK = MOE_BIG_K;  // K elements per stage (32 or 64)
-constexpr int kBigStages = MOE_BIG_STAGES;
+constexpr int kBigK = 64;        // K elements per stage
 constexpr int kBigSlots = kBigK / 8;                 // 16-byte slots per LDS row
 constexpr int kBigRowBytes = kBigK * 2;
 constexpr int kBigRowsPerGroup = 1024 / kBigRowBytes;  // rows filled by one 1 KB load
 constexpr int kBigGroups = kBigRows / kBigRowsPerGroup / 4;  // per wave and operand
 constexpr int kBigOperandBytes = kBigRows * kBigRowBytes;
 constexpr int kBigStageBytes = 2 * kBigOperandBytes;
-static_assert(kBigK == 32 || kBigK == 64, "stage K");
-static_assert(kBigStages >= 2 && kBigStages * kBigStageBytes <= 160 * 1024, "LDS");
+static_assert(2 * kBigStageBytes <= 160 * 1024, "two stages fit in LDS");
 #ifndef MOE_BIG_RASTER
 #define MOE_BIG_RASTER 1
 #endif
@@ -59,12 +49,10 @@ static_assert(kBigStages >= 2 && kBigStages * kBigStageBytes <= 160 * 1024, "LDS
 constexpr int kBigXcds = MOE_BIG_RASTER ? 8 : 1;  // 1: plain order, no XCD remap
 constexpr int kBigGroupCols = MOE_BIG_GROUP_COLS;
 
-// Slot swizzle: with 8 slots per row (K = 64) rows pair up per bank line, with
-// 4 slots (K = 32) four rows share one; either way the 16 rows one 16-lane
-// group reads for the same k land in 16 different 16-byte bank groups.
-__device__ __forceinline__ int big_swz(int row) {
-  return kBigSlots == 8 ? (row >> 1) & 7 : (row >> 2) & 3;
-}
+// Slot swizzle: 8 slots per row, rows pair up per bank line, so the 16 rows
+// one 16-lane group reads for the same k land in 16 different 16-byte bank
+// groups.
+__device__ __forceinline__ int big_swz(int row) { return (row >> 1) & 7; }
 
 struct BigTile {
   int b, y;
@@ -155,36 +143,61 @@ __device__ __forceinline__ void big_mma(const BigFrags& f, f32x4 (&acc)[8][8]) {
     for (int u = 0; u < 8; ++u) acc[t][u] = mfma16x16x32(f.a[t], f.b[u], acc[t][u]);
 }
 
+// First part of one stage of the two-buffer ring: wait for this wave's
+// loads of `cur`, meet the other waves (after which nobody reads `nxt`, the
+// buffer of the previous stage, any more), read the first k-step's
+// fragments, issue the next stage into `nxt` (when kIssue) and read the
+// second k-step's fragments f1 under the first k-step's MFMAs.  The caller
+// runs f1's MFMAs; the compiler may spread them over the next stage's wait,
+// barrier and first reads since they only touch registers.
+template <bool kIssue>
+__device__ __forceinline__ void big_half(const BigLoader& ld,
+                                         const bf16_t* const (&bsrc)[kBigGroups],
+                                         const uint8_t* cur, uint8_t* nxt, int knext, int wave,
+                                         int arow0, int arow_up, int brow0, BigFrags& f1,
+                                         f32x4 (&acc)[8][8]) {
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();
+  const uint8_t* opb = cur + kBigOperandBytes;
+  BigFrags f0;
+  big_load_frags(f0, cur, opb, arow0, arow_up, brow0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  if (kIssue) big_issue(ld, bsrc, nxt, knext, wave);
+  __builtin_amdgcn_sched_barrier(0);
+  big_load_frags(f1, cur, opb, arow0, arow_up, brow0, 1);
+  big_mma(f0, acc);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // four MFMAs
+  }
+}
+
 // acc[t][u] += A_rows(t) . B_rows(u)^T over K.  A rows: arow0 + 16t (t < 4)
-// and arow_up + 16(t-4); B rows: brow0 + 16u.  Ring of kBigStages stages:
-// stages 0 .. S-2 are issued up front; at stage s a wave waits until its own
-// loads of stage s have landed (later stages may stay in flight), meets the
-// other waves at the barrier (after which the buffer read at stage s-1 is
-// free), issues stage s + S - 1 into that buffer and runs stage s's MFMAs.
+// and arow_up + 16(t-4); B rows: brow0 + 16u.  Stage s (K = 64s .. 64s+63)
+// lives in buffer s % 2.  The two buffers are two LDS arrays: with one array
+// the compiler cannot tell that reads of stage s do not depend on the loads
+// of stage s+1 in flight, and waits for those before every read.  The loop
+// is rotated by half a stage so that each stage's second k-step MFMAs can
+// overlap the next stage's start.  nst is even: the launchers require
+// d % 256 == 0 and I % 128 == 0.
 __device__ __forceinline__ void big_mainloop(const BigLoader& ld,
                                              const bf16_t* const (&bsrc)[kBigGroups],
-                                             uint8_t* lds, int nst, int wave, int arow0,
-                                             int arow_up, int brow0, f32x4 (&acc)[8][8]) {
-  constexpr int kLoads = 2 * kBigGroups;  // per wave and stage
-#pragma unroll
-  for (int s = 0; s < kBigStages - 1; ++s)
-    if (s < nst) big_issue(ld, bsrc, lds + s * kBigStageBytes, s * kBigK, wave);
-  for (int s = 0; s < nst; ++s) {
-    if (s + kBigStages - 2 < nst)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoads * (kBigStages - 2)));
-    else
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // tail: fewer stages behind this one
-    __syncthreads();
-    const int sn = s + kBigStages - 1;
-    if (sn < nst) big_issue(ld, bsrc, lds + (sn % kBigStages) * kBigStageBytes, sn * kBigK, wave);
-    const uint8_t* opa = lds + (s % kBigStages) * kBigStageBytes;
-    const uint8_t* opb = opa + kBigOperandBytes;
-    BigFrags f[kBigK / 32];
-#pragma unroll
-    for (int j = 0; j < kBigK / 32; ++j) big_load_frags(f[j], opa, opb, arow0, arow_up, brow0, j);
-#pragma unroll
-    for (int j = 0; j < kBigK / 32; ++j) big_mma(f[j], acc);
+                                             uint8_t* buf0, uint8_t* buf1, int nst, int wave,
+                                             int arow0, int arow_up, int brow0,
+                                             f32x4 (&acc)[8][8]) {
+  BigFrags f1;
+  big_issue(ld, bsrc, buf0, 0, wave);
+  big_half<true>(ld, bsrc, buf0, buf1, kBigK, wave, arow0, arow_up, brow0, f1, acc);
+  for (int s = 1; s + 1 < nst; s += 2) {
+    big_mma(f1, acc);
+    big_half<true>(ld, bsrc, buf1, buf0, (s + 1) * kBigK, wave, arow0, arow_up, brow0, f1, acc);
+    big_mma(f1, acc);
+    big_half<true>(ld, bsrc, buf0, buf1, (s + 2) * kBigK, wave, arow0, arow_up, brow0, f1, acc);
   }
+  big_mma(f1, acc);
+  big_half<false>(ld, bsrc, buf1, buf0, 0, wave, arow0, arow_up, brow0, f1, acc);
+  big_mma(f1, acc);
 }
 
 // ------------------------------------------------------------ W13 + SiLU*mul
@@ -195,7 +208,8 @@ __global__ __launch_bounds__(kBigThreads) void ffn13_big_kernel(
     const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ block_expert,
     const int32_t* __restrict__ num_padded, bf16_t* __restrict__ h, int d, int I, int k, int A,
     int gx, int gy) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kBigStages * kBigStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t buf0[kBigStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t buf1[kBigStageBytes];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15;
@@ -231,7 +245,7 @@ __global__ __launch_bounds__(kBigThreads) void ffn13_big_kernel(
 #pragma unroll
     for (int u = 0; u < 8; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  big_mainloop(ld, bsrc, lds, d / kBigK, wave, 64 * wm, 128 + 64 * wm, 128 * wn, acc);
+  big_mainloop(ld, bsrc, buf0, buf1, d / kBigK, wave, 64 * wm, 128 + 64 * wm, 128 * wn, acc);
 
   // lane: token column r16 of tile u, channels n0 + 64wm + 16t + 4g .. +3
 #pragma unroll
@@ -261,7 +275,8 @@ __global__ __launch_bounds__(kBigThreads) void ffn2_big_kernel(
     const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded,
     float* __restrict__ y, int d, int I, int A, int gx, int gy) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kBigStages * kBigStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t buf0[kBigStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t buf1[kBigStageBytes];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15;
@@ -295,7 +310,7 @@ __global__ __launch_bounds__(kBigThreads) void ffn2_big_kernel(
     for (int u = 0; u < 8; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // A rows 128*wm .. +127: eight consecutive 16-row tiles
-  big_mainloop(ld, bsrc, lds, I / kBigK, wave, 128 * wm, 128 * wm + 64, 128 * wn, acc);
+  big_mainloop(ld, bsrc, buf0, buf1, I / kBigK, wave, 128 * wm, 128 * wm + 64, 128 * wn, acc);
 
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
