@@ -91,7 +91,14 @@ int default_block_m(const moe_desc* d, int top_k) {
   const int64_t T = d->num_tokens;
   if (T <= 16) return 16;
   if (T <= 32) return 32;
-  if (T <= 64) return 64;
+  if (T <= 64) {
+    // blocks of 32 keep the LDS-streaming kernel (an expert holding more
+    // than 32 of the tokens takes a second block)
+    const bool lds = d->weight_dtype == MOE_DTYPE_BF16 && d->act_dtype == MOE_DTYPE_BF16 &&
+                     moe::dma_stream_fits(static_cast<int>(d->hidden),
+                                          static_cast<int>(d->intermediate));
+    return lds ? 32 : 64;
+  }
   const int64_t per_expert = T * top_k / d->num_experts;
   if (per_expert >= 256 && d->weight_dtype == MOE_DTYPE_BF16 &&
       moe::big_gemm_fits(static_cast<int>(d->hidden), static_cast<int>(d->intermediate)))
@@ -122,9 +129,12 @@ void make_plan(const moe_desc* d, int top_k, bool with_routing, Plan* p) {
   p->splits = 1;
   p->ksplit = p->I;
   if (p->wdt != MOE_DTYPE_F32 && p->A > 0 && p->B <= 64) {  // the GEMM paths do not split
-    const int kc = moe::ffn2_kchunk(p->I, p->wdt);
-    const int64_t blocks_est = std::min<int64_t>(p->cap / p->B, std::min(p->E, p->A) + p->A / p->B);
-    const int64_t waves = blocks_est * (p->d / 32);  // one wave per 32 channels
+    const int64_t blocks_est = moe::ffn_blocks_estimate(p->cap, p->B, p->E, p->A);
+    const bool lds = moe::dma_stream_use(p->wdt, p->act, p->B, p->d, p->I, blocks_est);
+    const int kc = moe::ffn2_kchunk(p->d, p->I, p->B, p->wdt, p->act, blocks_est);
+    // one wave per dma_w2_channels() (LDS streaming) or about 32 (register
+    // path) output channels
+    const int64_t waves = blocks_est * (p->d / (lds ? moe::dma_w2_channels() : 32));
     int s = 1;
     while (s < 8 && waves * s < 2048 && p->I / (2 * s) >= 4 * kc) s *= 2;
     const int per = (p->I + s - 1) / s;

@@ -364,7 +364,8 @@ int kchunk_for(int K) {
   return K % 128 == 0 ? 128 : 64;
 }
 
-int ffn2_kchunk(int I, int w_dtype) {
+int ffn2_kchunk(int d, int I, int B, int w_dtype, int act_dtype, int64_t blocks_est) {
+  if (dma_stream_use(w_dtype, act_dtype, B, d, I, blocks_est)) return 256;
   return w_dtype == kDtypeE4M3FN ? kchunk_for<fp8_t>(I) : kchunk_for<bf16_t>(I);
 }
 
@@ -385,7 +386,7 @@ inline int pick_rn(int blocks_est, int channels, int rn_max, int nsub) {
 }
 
 inline int blocks_estimate(const FfnArgs& a) {
-  return std::min(a.cap / a.B, std::min(a.E, a.A) + a.A / a.B);
+  return static_cast<int>(ffn_blocks_estimate(a.cap, a.B, a.E, a.A));
 }
 
 template <typename WT, int NSUB, int KC, int RN>
@@ -475,6 +476,7 @@ hipError_t launch_ffn13(const FfnArgs& a, hipStream_t s) {
   }
   if (a.B == 256) return launch_ffn13_big(a, s);   // large-tile grouped GEMM
   if (a.B == 128) return launch_ffn13_gemm(a, s);  // token-tiled grouped GEMM
+  if (dma_stream_use(a)) return launch_ffn13_dma(a, s);  // weights through LDS
   if (a.w_dtype == kDtypeBF16) return ffn13_w<bf16_t>(a, s);
   return ffn13_w<fp8_t>(a, s);
 }
@@ -490,6 +492,7 @@ hipError_t launch_ffn2(const FfnArgs& a, hipStream_t s) {
   }
   if (a.B == 256) return launch_ffn2_big(a, s);
   if (a.B == 128) return launch_ffn2_gemm(a, s);
+  if (dma_stream_use(a)) return launch_ffn2_dma(a, s);
   if (a.w_dtype == kDtypeBF16) return ffn2_w<bf16_t>(a, s);
   return ffn2_w<fp8_t>(a, s);
 }

@@ -1,0 +1,367 @@
+// Expert kernels for small token blocks (decode) with bf16 weights, weights
+// streamed through LDS: the HBM-bound end of the fused MoE layer.
+//
+// Sources: the Hungarian news page "Az AWS új MoE-optimalizációkkal
+// gyorsítja a SageMaker AI-t", section "A fused MoE a számítási folyamat több
+// lépését egyesíti" (the grouped expert computation and the gated SiLU
+// product); the French summary "Ingénierie de kernels Mixture-of-Experts sur
+// Amazon SageMaker AI", first paragraph (at decode the expert product has a
+// tiny token dimension, so its cost is reading the weights).
+//
+// With at most 32 tokens per expert block every weight byte feeds at most
+// 32 MACs, so the kernel's speed is the weight read rate.  Loading the
+// weights straight into MFMA registers makes every load instruction cover
+// 16 rows x 64 bytes, half of each row's 128-byte line; HBM serves that
+// pattern well below its streaming rate.  Here every load instruction is a
+// direct-to-LDS load of two rows x 512 contiguous bytes, with the
+// nontemporal hint (the weights are read once), and the MFMA fragments come
+// from LDS.  The token operand (x for W13, h for W2, a few L2-resident rows)
+// is loaded into a register ring of the same depth, in the same stream: loads
+// complete in issue order, so the wait for stage c leaves stages c+1 ..
+// c+P-2 in flight, and LDS holds weights only.
+//
+// LDS stage: one 16-row tile per gate / up / output tile, rows of 512 bytes
+// (256 bf16 of K).  Row r's 16-byte unit u sits in slot u ^ (r & 15), so the 16 rows one
+// 16-lane group reads for the same k hit 16 different bank groups; the
+// permutation is applied by choosing each lane's source address, which keeps
+// every 256-byte group of a row contiguous in HBM.  One wave per workgroup,
+// P stages each in an LDS array of its own (distinct arrays let the compiler
+// see that reads of one stage do not depend on loads into another).
+
+#include "ffn_common.h"
+
+namespace moe {
+
+constexpr int kDmaRowBytes = 512;            // bytes of one row per stage
+constexpr int kDmaKC = kDmaRowBytes / 2;     // K elements per stage
+constexpr int kDmaThreads = 64;
+constexpr int kDmaAux = 2;                   // cache policy of the loads: nontemporal
+
+bool dma_stream_fits(int d, int I) { return d % kDmaKC == 0 && I % kDmaKC == 0; }
+
+// Stage geometry for NROW weight tiles and NS live token subtiles.
+template <int NROW, int NS>
+struct DmaGeom {
+  static constexpr int kStageBytes = 16 * NROW * kDmaRowBytes;  // weight rows only
+  static constexpr int kLoadsW = 8 * NROW;  // direct-to-LDS loads (2 rows each)
+  static constexpr int kLoadsA = 8 * NS;    // token loads (one per MFMA k-step)
+  static constexpr int kLoads = kLoadsW + kLoadsA;
+};
+
+// s_waitcnt immediate: at most n vector-memory loads outstanding.
+constexpr int dma_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Per-lane operand sources.
+//   wlane[t]: weight tile t's row `hi` (= lane / 32) at k = 0; the stage row
+//             r of tile t is loaded by instruction 8t + (r & 15) / 2;
+//   arow[s]:  the token row of this lane's MFMA column in subtile s, k = 0
+//             (pad slots point at a valid row; their columns are dropped).
+template <int NROW, int NS>
+struct DmaOperands {
+  const bf16_t* wlane[NROW];
+  const bf16_t* arow[NS];
+  size_t wld;  // weight row length (elements)
+  int l31, hi, r16, g;
+
+  __device__ __forceinline__ void issue_w(uint8_t* stage, int k0) const {
+#pragma unroll
+    for (int i = 0; i < 8 * NROW; ++i) {
+      const int j = ((2 * i) & 15) + hi;  // row within the tile
+      const bf16_t* src = wlane[i / 8] + static_cast<size_t>((2 * i) & 15) * wld;
+      __builtin_amdgcn_global_load_lds(src + k0 + 8 * (l31 ^ j), stage + 1024 * i, 16, 0,
+                                       kDmaAux);
+    }
+  }
+  // Token fragments of one stage: k-step q takes k = k0 + 32q + 8g .. +8.
+  template <int NSL>
+  __device__ __forceinline__ void issue_a(uint4 (&a)[NS][8], int k0) const {
+#pragma unroll
+    for (int s = 0; s < NSL; ++s)
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        a[s][q] = *reinterpret_cast<const uint4*>(arow[s] + k0 + 32 * q + 8 * g);
+  }
+
+  // acc[s][t] += W_tile(t) . A_subtile(s) over the stage's 256 K.
+  template <int NSL>
+  __device__ __forceinline__ void mma(const uint8_t* stage, const uint4 (&a)[NS][8],
+                                      f32x4 (&acc)[NS][NROW]) const {
+#pragma unroll
+    for (int q = 0; q < kDmaKC / 32; ++q) {
+      const int slot = ((4 * q + g) ^ r16) << 4;
+      bf16x8 wf[NROW];
+#pragma unroll
+      for (int t = 0; t < NROW; ++t)
+        wf[t] = as_frag(*reinterpret_cast<const uint4*>(stage + (16 * t + r16) * kDmaRowBytes + slot));
+#pragma unroll
+      for (int s = 0; s < NSL; ++s)
+#pragma unroll
+        for (int t = 0; t < NROW; ++t) acc[s][t] = mfma16x16x32(wf[t], as_frag(a[s][q]), acc[s][t]);
+    }
+  }
+};
+
+// The ring: chunk c (K = k_begin + 256c ..) in buffer c % P (weights in LDS,
+// token fragments in registers).  At chunk c the wave waits until only the
+// P-2 later stages are outstanding (loads complete in issue order), issues
+// chunk c+P-1 into the buffers read at chunk c-1 (clamped to the last chunk:
+// the duplicate lands where nobody reads again, and keeps the wait counts
+// uniform), then runs chunk c's MFMAs.  NSL: live token subtiles.
+template <int NROW, int NS, int P, int NSL>
+struct DmaRing {
+  const DmaOperands<NROW, NS>& op;
+  uint8_t* const (&ring)[4];
+  int k_begin, nch;
+
+  template <int p>
+  __device__ __forceinline__ void step(int c, uint4 (&a)[P][NS][8], f32x4 (&acc)[NS][NROW]) const {
+    constexpr int pn = (p + P - 1) % P;
+    __builtin_amdgcn_s_waitcnt(dma_vmcnt(DmaGeom<NROW, NSL>::kLoads * (P - 2)));
+    const int kn = k_begin + min(c + P - 1, nch - 1) * kDmaKC;
+    op.issue_w(ring[pn], kn);
+    op.template issue_a<NSL>(a[pn], kn);
+    op.template mma<NSL>(ring[p], a[p], acc);
+  }
+
+  __device__ __forceinline__ void run(f32x4 (&acc)[NS][NROW]) const {
+    uint4 a[P][NS][8];
+#pragma unroll
+    for (int q = 0; q + 1 < P; ++q) {
+      const int kq = k_begin + min(q, nch - 1) * kDmaKC;
+      op.issue_w(ring[q], kq);
+      op.template issue_a<NSL>(a[q], kq);
+    }
+    int c0 = 0;
+    for (; c0 + P <= nch; c0 += P) {
+      step<0>(c0, a, acc);
+      if constexpr (P > 1) step<1>(c0 + 1, a, acc);
+      if constexpr (P > 2) step<2>(c0 + 2, a, acc);
+      if constexpr (P > 3) step<3>(c0 + 3, a, acc);
+    }
+    const int rem = nch - c0;  // 0 .. P-1 chunks left
+    if (rem >= 1) step<0>(c0, a, acc);
+    if constexpr (P > 2)
+      if (rem >= 2) step<1>(c0 + 1, a, acc);
+    if constexpr (P > 3)
+      if (rem >= 3) step<2>(c0 + 2, a, acc);
+    __builtin_amdgcn_s_waitcnt(dma_vmcnt(0));  // no load may land after the wave ends
+  }
+};
+
+template <int NROW, int NS, int P>
+__device__ __forceinline__ void dma_dot(int nsub, const DmaOperands<NROW, NS>& op,
+                                        uint8_t* const (&ring)[4], int k_begin, int nch,
+                                        f32x4 (&acc)[NS][NROW]) {
+  if (nsub == 1 || NS == 1) {
+    DmaRing<NROW, NS, P, 1>{op, ring, k_begin, nch}.run(acc);
+  } else {
+    DmaRing<NROW, NS, P, NS>{op, ring, k_begin, nch}.run(acc);
+  }
+}
+
+#define DMA_RING(name, bytes, P)                                                   \
+  __shared__ __attribute__((aligned(1024))) uint8_t name##0[bytes];                \
+  __shared__ __attribute__((aligned(1024))) uint8_t name##1[(P) > 1 ? (bytes) : 16]; \
+  __shared__ __attribute__((aligned(1024))) uint8_t name##2[(P) > 2 ? (bytes) : 16]; \
+  __shared__ __attribute__((aligned(1024))) uint8_t name##3[(P) > 3 ? (bytes) : 16]; \
+  uint8_t* const name[4] = {name##0, name##1, name##2, name##3}
+
+// ------------------------------------------------------------ W13 + SiLU*mul
+// Grid: x = row block b (B = 16 NS), y = 16-channel tile.  The wave computes
+// gate rows n0.. and up rows I+n0.. against the block's tokens and writes
+// h[row, n] = SiLU(gate) * up for the live subtiles (pad rows included:
+// their columns never reach an output).
+
+template <int NS, int P>
+__global__ __launch_bounds__(kDmaThreads) void ffn13_dma_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ w13,
+    const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ block_expert,
+    const int32_t* __restrict__ num_padded, bf16_t* __restrict__ h, int d, int I, int k, int A) {
+  constexpr int B = 16 * NS;
+  using G = DmaGeom<2, NS>;
+  DMA_RING(ring, G::kStageBytes, P);
+  const int lane = threadIdx.x;
+  const int b = blockIdx.x;
+  if (b * B >= *num_padded) return;
+  const int e = block_expert[b];
+  const int n0 = blockIdx.y * 16;
+  const int32_t* blk = sorted_ids + static_cast<size_t>(b) * B;
+  const int nsub = live_subtiles<NS>(blk, A);
+
+  DmaOperands<2, NS> op;
+  op.l31 = lane & 31;
+  op.hi = lane >> 5;
+  op.r16 = lane & 15;
+  op.g = lane >> 4;
+  op.wld = d;
+  const size_t erow = static_cast<size_t>(e) * 2 * I;
+  op.wlane[0] = w13 + (erow + n0 + op.hi) * d;      // gate tile
+  op.wlane[1] = w13 + (erow + I + n0 + op.hi) * d;  // up tile
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int f = blk[16 * s + op.r16];  // pad slots read token 0
+    op.arow[s] = x + static_cast<size_t>(f < A ? f / k : 0) * d;
+  }
+
+  f32x4 acc[NS][2];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) acc[s][0] = acc[s][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  dma_dot<2, NS, P>(nsub, op, ring, 0, d / kDmaKC, acc);
+
+  // lane: token column r16, channels n0 + 4g .. +3
+  const int nb = n0 + 4 * op.g;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    if (s < nsub) {
+      const size_t row = static_cast<size_t>(b) * B + 16 * s + op.r16;
+      uint32_t packed[2];
+#pragma unroll
+      for (int v = 0; v < 4; v += 2) {
+        const float h0 = silu(acc[s][0][v]) * acc[s][1][v];
+        const float h1 = silu(acc[s][0][v + 1]) * acc[s][1][v + 1];
+        packed[v / 2] = static_cast<uint32_t>(f32_to_bf16(h0)) |
+                        (static_cast<uint32_t>(f32_to_bf16(h1)) << 16);
+      }
+      *reinterpret_cast<uint2*>(h + row * I + nb) = uint2{packed[0], packed[1]};
+    }
+  }
+}
+
+// ------------------------------------------------------------ W2 + gate scale
+// Grid: x = row block b, y = group of 16 RN channels of d, z = split of
+// K = I.  Writes y_part[z, f, n] = gate_f * sum_{i in split} W2[e, n, i] h[row, i]
+// for the block's real slots f.  RN tiles per wave: every wave reads all h
+// rows of its block, so wider waves read less h per weight byte.
+
+template <int NS, int P, int RN>
+__global__ __launch_bounds__(kDmaThreads) void ffn2_dma_kernel(
+    const bf16_t* __restrict__ h, const bf16_t* __restrict__ w2, const float* __restrict__ topk_w,
+    const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ block_expert,
+    const int32_t* __restrict__ num_padded, float* __restrict__ y_part, int d, int I, int A,
+    int ksplit) {
+  constexpr int B = 16 * NS;
+  using G = DmaGeom<RN, NS>;
+  DMA_RING(ring, G::kStageBytes, P);
+  const int lane = threadIdx.x;
+  const int b = blockIdx.x;
+  if (b * B >= *num_padded) return;
+  const int e = block_expert[b];
+  const int n0 = blockIdx.y * 16 * RN;
+  const int z = blockIdx.z;
+  const int k_begin = z * ksplit;
+  const int nch = (min(I, k_begin + ksplit) - k_begin) / kDmaKC;
+  const int32_t* blk = sorted_ids + static_cast<size_t>(b) * B;
+  const int nsub = live_subtiles<NS>(blk, A);
+
+  DmaOperands<RN, NS> op;
+  op.l31 = lane & 31;
+  op.hi = lane >> 5;
+  op.r16 = lane & 15;
+  op.g = lane >> 4;
+  op.wld = I;
+#pragma unroll
+  for (int rt = 0; rt < RN; ++rt)
+    op.wlane[rt] = w2 + (static_cast<size_t>(e) * d + n0 + 16 * rt + op.hi) * I;
+  // h row of this lane's column; pad slots read the block's first row (a
+  // real slot's) so that their loads share one address
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int slot = 16 * s + op.r16;
+    const size_t row = static_cast<size_t>(b) * B + (blk[slot] < A ? slot : 0);
+    op.arow[s] = h + row * I;
+  }
+
+  f32x4 acc[NS][RN];
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+#pragma unroll
+    for (int rt = 0; rt < RN; ++rt) acc[s][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (nch > 0) dma_dot<RN, NS, P>(nsub, op, ring, k_begin, nch, acc);
+
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    if (s < nsub) {
+      const int f = blk[16 * s + op.r16];
+      if (f < A) {
+        const float gate = topk_w[f];
+        float* yrow = y_part + (static_cast<size_t>(z) * A + f) * d;
+#pragma unroll
+        for (int rt = 0; rt < RN; ++rt) {
+          float4 o;
+          o.x = acc[s][rt][0] * gate;
+          o.y = acc[s][rt][1] * gate;
+          o.z = acc[s][rt][2] * gate;
+          o.w = acc[s][rt][3] * gate;
+          *reinterpret_cast<float4*>(yrow + n0 + 16 * rt + 4 * op.g) = o;
+        }
+      }
+    }
+  }
+}
+
+#ifndef MOE_DMA13_P1
+#define MOE_DMA13_P1 4
+#endif
+#ifndef MOE_DMA13_P2
+#define MOE_DMA13_P2 3
+#endif
+#ifndef MOE_DMA2_P1
+#define MOE_DMA2_P1 3
+#endif
+#ifndef MOE_DMA2_P2
+#define MOE_DMA2_P2 3
+#endif
+#ifndef MOE_DMA2_RN
+#define MOE_DMA2_RN 2
+#endif
+constexpr int kDma2RN = MOE_DMA2_RN;
+
+int dma_w2_channels() { return 16 * kDma2RN; }
+
+hipError_t launch_ffn13_dma(const FfnArgs& a, hipStream_t s) {
+  if (a.w_dtype != kDtypeBF16 || a.act_dtype != kDtypeBF16 || !dma_stream_fits(a.d, a.I))
+    return hipErrorInvalidValue;
+  const dim3 grid(a.cap / a.B, a.I / 16);
+  const bf16_t* x = static_cast<const bf16_t*>(a.x);
+  const bf16_t* w = static_cast<const bf16_t*>(a.w13);
+  bf16_t* h = static_cast<bf16_t*>(a.h);
+  switch (a.B) {
+    case 16:
+      ffn13_dma_kernel<1, MOE_DMA13_P1><<<grid, kDmaThreads, 0, s>>>(
+          x, w, a.sorted_ids, a.block_expert, a.num_padded, h, a.d, a.I, a.k, a.A);
+      break;
+    case 32:
+      ffn13_dma_kernel<2, MOE_DMA13_P2><<<grid, kDmaThreads, 0, s>>>(
+          x, w, a.sorted_ids, a.block_expert, a.num_padded, h, a.d, a.I, a.k, a.A);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_ffn2_dma(const FfnArgs& a, hipStream_t s) {
+  if (a.w_dtype != kDtypeBF16 || a.act_dtype != kDtypeBF16 || !dma_stream_fits(a.d, a.I) ||
+      a.ksplit % kDmaKC != 0 || a.d % (16 * kDma2RN) != 0)
+    return hipErrorInvalidValue;
+  const dim3 grid(a.cap / a.B, a.d / (16 * kDma2RN), a.splits);
+  const bf16_t* h = static_cast<const bf16_t*>(a.h);
+  const bf16_t* w = static_cast<const bf16_t*>(a.w2);
+  switch (a.B) {
+    case 16:
+      ffn2_dma_kernel<1, MOE_DMA2_P1, kDma2RN><<<grid, kDmaThreads, 0, s>>>(
+          h, w, a.topk_w, a.sorted_ids, a.block_expert, a.num_padded, a.y_part, a.d, a.I, a.A,
+          a.ksplit);
+      break;
+    case 32:
+      ffn2_dma_kernel<2, MOE_DMA2_P2, kDma2RN><<<grid, kDmaThreads, 0, s>>>(
+          h, w, a.topk_w, a.sorted_ids, a.block_expert, a.num_padded, a.y_part, a.d, a.I, a.A,
+          a.ksplit);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -60,8 +60,38 @@ bool big_gemm_fits(int d, int I);
 hipError_t launch_ffn13_big(const FfnArgs& a, hipStream_t s);
 hipError_t launch_ffn2_big(const FfnArgs& a, hipStream_t s);
 
-// K chunk the W2 kernel uses for a given I and weight dtype (the split
-// length must be a multiple of it).
-int ffn2_kchunk(int I, int w_dtype);
+// Row blocks that hold at least one slot: the realised blocks are at most
+// the capacity's, and at most one partial block per used expert plus the
+// full ones.
+inline int64_t ffn_blocks_estimate(int64_t cap, int B, int E, int64_t A) {
+  const int64_t used = E < A ? E : A;
+  const int64_t est = used + A / B;
+  return cap / B < est ? cap / B : est;
+}
+
+// Weight streaming through LDS for bf16 blocks of 16 or 32 tokens (d and I
+// multiples of 256), when the W13 grid has enough workgroups for several
+// rounds of the LDS-limited occupancy; batches touching few experts keep the
+// register path, whose smaller workgroups all fit on the chip at once.
+bool dma_stream_fits(int d, int I);
+inline bool dma_stream_use(int w_dtype, int act_dtype, int B, int d, int I, int64_t blocks_est) {
+#ifdef MOE_NO_DMA_STREAM
+  return false;
+#else
+  return w_dtype == kDtypeBF16 && act_dtype == kDtypeBF16 && (B == 16 || B == 32) &&
+         dma_stream_fits(d, I) && blocks_est * (I / 16) >= 4096;
+#endif
+}
+inline bool dma_stream_use(const FfnArgs& a) {
+  return dma_stream_use(a.w_dtype, a.act_dtype, a.B, a.d, a.I,
+                        ffn_blocks_estimate(a.cap, a.B, a.E, a.A));
+}
+hipError_t launch_ffn13_dma(const FfnArgs& a, hipStream_t s);
+int dma_w2_channels();  // output channels per W2 workgroup of that path
+hipError_t launch_ffn2_dma(const FfnArgs& a, hipStream_t s);
+
+// K chunk the W2 kernel uses for a given shape, block size, dtypes and
+// block estimate (the split length must be a multiple of it).
+int ffn2_kchunk(int d, int I, int B, int w_dtype, int act_dtype, int64_t blocks_est);
 
 }  // namespace moe

@@ -97,6 +97,9 @@ def test_capacity_formula(lib, T, E, k, bm):
 def test_default_block_covers_a_decode_batch(lib):
     for T, want in [(1, 16), (8, 16), (16, 16), (17, 32), (32, 32), (64, 64), (65, 128)]:
         assert B.moe_align_capacity(desc(T=T), 2)[0] == want
+    # 33..64 tokens with LDS-streaming bf16 shapes take blocks of 32
+    assert B.moe_align_capacity(desc(T=64, d=4096, I=14336), 2)[0] == 32
+    assert B.moe_align_capacity(desc(T=64, d=4096, I=14336, w=B.MOE_DTYPE_E4M3FN), 2)[0] == 64
     # experts averaging >= 256 tokens with fitting bf16 shapes use the 256 GEMM
     assert B.moe_align_capacity(desc(T=4096, d=4096, I=14336), 2)[0] == 256
     assert B.moe_align_capacity(desc(T=4096, d=2880, I=2880), 2)[0] == 128

@@ -122,6 +122,12 @@ SMALL = [
     ("bf16_ragged", dict(workload="decode_bf16", d=512, I=448, x_std=1.0), 257, 16),
     ("bf16_ragged", dict(workload="decode_bf16", d=512, I=448, x_std=1.0), 257, 128),
     ("bf16_d320", dict(workload="decode_bf16", d=320, I=192, x_std=1.0), 100, 32),
+    # weights streamed through LDS (d and I multiples of 256, blocks of 16 / 32,
+    # enough blocks x channel tiles): ring remainders of 1..3 chunks, one and
+    # two live token subtiles, W2 split in two
+    ("bf16_lds", dict(workload="decode_bf16", d=768, I=2048, E=32, x_std=1.0), 16, 0),
+    ("bf16_lds", dict(workload="decode_bf16", d=256, I=2304, E=8, x_std=1.0), 384, 32),
+    ("bf16_lds", dict(workload="decode_bf16", d=1280, I=2048, E=32, x_std=1.0), 24, 0),
     ("bf16_big", dict(workload="decode_bf16", d=512, I=384, E=4, x_std=1.0), 700, 256),
     ("bf16_big", dict(workload="decode_bf16", d=256, I=128, E=8, k=2, x_std=1.0), 1500, 0),
     ("bf16_big", dict(workload="decode_bf16", d=768, I=256, E=3, k=1, x_std=1.0), 300, 256),
