@@ -300,6 +300,23 @@ MOE_API int moe_workspace_bytes(const moe_desc* desc, int top_k, int with_routin
   return MOE_OK;
 }
 
+// Router logits and top-k: one kernel when the router kernel can select
+// itself (timed as route_logits), else two launches.
+static hipError_t route(const void* x, int act, const float* w_gate, float* logits,
+                        int32_t* ids, float* gates, int T, int E, int d, int k, hipStream_t s) {
+  if (moe::router_fused(act, T, E))
+    return timed(MOE_KERNEL_ROUTE_LOGITS, s, [&] {
+      return moe::launch_router_fused(x, w_gate, logits, ids, gates, T, E, d, k, s);
+    });
+  hipError_t e = timed(MOE_KERNEL_ROUTE_LOGITS, s, [&] {
+    return moe::launch_router_logits(x, act, w_gate, logits, T, E, d, s);
+  });
+  if (e == hipSuccess)
+    e = timed(MOE_KERNEL_ROUTE_TOPK, s,
+              [&] { return moe::launch_router_topk(logits, ids, gates, T, E, k, s); });
+  return e;
+}
+
 MOE_API int moe_route(const moe_desc* desc, const void* x, const float* w_gate, int top_k,
                       float* logits, int32_t* topk_ids, float* topk_w, void* stream) {
   int st = check_desc(desc, top_k);
@@ -309,13 +326,7 @@ MOE_API int moe_route(const moe_desc* desc, const void* x, const float* w_gate, 
   if ((st = check_ptrs({x, w_gate, logits, topk_ids, topk_w}))) return st;
   const int E = static_cast<int>(desc->num_experts), d = static_cast<int>(desc->hidden);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = timed(MOE_KERNEL_ROUTE_LOGITS, s, [&] {
-    return moe::launch_router_logits(x, desc->act_dtype, w_gate, logits, T, E, d, s);
-  });
-  if (e == hipSuccess)
-    e = timed(MOE_KERNEL_ROUTE_TOPK, s,
-              [&] { return moe::launch_router_topk(logits, topk_ids, topk_w, T, E, top_k, s); });
-  return to_status(e);
+  return to_status(route(x, desc->act_dtype, w_gate, logits, topk_ids, topk_w, T, E, d, top_k, s));
 }
 
 MOE_API int moe_route_logits(const moe_desc* desc, const float* logits, int top_k,
@@ -392,12 +403,7 @@ MOE_API int moe_forward(const moe_desc* desc, const void* x, const float* w_gate
   int32_t* sorted = reinterpret_cast<int32_t*>(ws + p.sorted);
   int32_t* block_exp = reinterpret_cast<int32_t*>(ws + p.block_exp);
 
-  hipError_t e = timed(MOE_KERNEL_ROUTE_LOGITS, s, [&] {
-    return moe::launch_router_logits(x, p.act, w_gate, logits, p.T, p.E, p.d, s);
-  });
-  if (e == hipSuccess)
-    e = timed(MOE_KERNEL_ROUTE_TOPK, s,
-              [&] { return moe::launch_router_topk(logits, ids, gates, p.T, p.E, p.k, s); });
+  hipError_t e = route(x, p.act, w_gate, logits, ids, gates, p.T, p.E, p.d, p.k, s);
   if (e == hipSuccess)
     e = timed(MOE_KERNEL_ALIGN, s, [&] {
       return moe::launch_align(ids, p.A, p.E, p.B, p.cap, counts, sorted, block_exp, num_padded,

@@ -12,6 +12,85 @@
 
 namespace moe {
 
+// ---------------------------------------------------------------- top-k + gates
+//
+// One wavefront per token.  Lane l holds the logits of experts l, l+64, ...
+// Each of the k rounds takes the wave-wide best untaken expert, ordering by
+// (logit descending, index ascending); NaN counts as -inf.  Lane j keeps the
+// j-th pick, then the gates are exp(l_j - l_0) / sum, with l_0 the largest
+// selected logit.
+
+constexpr int kMaxExpertsPerLane = 16;  // E <= 1024
+
+__device__ __forceinline__ bool better(float av, int ae, float bv, int be) {
+  return av > bv || (av == bv && ae < be);
+}
+
+// The whole wave selects for one token: `row` holds its E logits (global or
+// LDS); writes k ids and gates.
+__device__ __forceinline__ void topk_wave(const float* row, int E, int k, int32_t* ids,
+                                          float* gates) {
+  const int lane = threadIdx.x & 63;
+  float v[kMaxExpertsPerLane];
+  const int per_lane = (E + 63) >> 6;
+#pragma unroll
+  for (int i = 0; i < kMaxExpertsPerLane; ++i) {
+    const int e = lane + 64 * i;
+    float val = -INFINITY;
+    if (i < per_lane && e < E) {
+      val = row[e];
+      if (val != val) val = -INFINITY;  // NaN ranks below every number
+    }
+    v[i] = val;
+  }
+  uint32_t taken = 0;  // bit i: expert lane + 64*i already selected
+  float my_v = -INFINITY;
+  int my_e = 0;
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < kMaxExpertsPerLane; ++i) {
+      const int e = lane + 64 * i;
+      if (i < per_lane && e < E && !((taken >> i) & 1u) && better(v[i], e, bv, be)) {
+        bv = v[i];
+        be = e;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const float ov = __shfl_xor(bv, off, kWave);
+      const int oe = __shfl_xor(be, off, kWave);
+      if (better(ov, oe, bv, be)) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    if (be < E && (be & 63) == lane) taken |= 1u << (be >> 6);
+    if (lane == j) {
+      my_v = bv;
+      my_e = be;
+    }
+  }
+  const float l0 = __shfl(my_v, 0, kWave);
+  const float p = lane < k ? expf(my_v - l0) : 0.f;
+  const float s = wave_sum(p);
+  if (lane < k) {
+    ids[lane] = my_e;
+    gates[lane] = p / s;
+  }
+}
+
+__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ logits,
+                                                          int32_t* __restrict__ topk_ids,
+                                                          float* __restrict__ topk_w, int T,
+                                                          int E, int k) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  topk_wave(logits + static_cast<size_t>(t) * E, E, k, topk_ids + static_cast<size_t>(t) * k,
+            topk_w + static_cast<size_t>(t) * k);
+}
+
 // ---------------------------------------------------------------- logits
 //
 // fp32 matrix-core product, experts on the MFMA M side and tokens on N
@@ -78,39 +157,55 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict
 }
 
 // bf16 activations: the same product on bf16 matrix cores.  Each fp32
-// W_gate value is split exactly into three bf16 parts, w = hi + mid + lo
-// (hi = w rounded to bf16, mid = the remainder rounded to bf16, lo = the
-// rest, which has at most 8 significant bits).  A bf16 x bf16 product is
-// exact in fp32, so x.w = x.hi + x.mid + x.lo is an fp32 dot product of exact
-// products, at three 16x16x32 bf16 MFMAs per 32 k instead of eight 16x16x4
-// fp32 ones.  K is split over the four waves of a workgroup (each wave takes
-// a contiguous range of 32-wide steps) and the four partial tiles are added
+// W_gate value is split exactly into three bf16 parts, w = hi + mid + lo, by
+// truncation: hi keeps the top 8 significand bits, mid the next 8 of the
+// remainder, lo the last 8 (an fp32 significand has 24), so each part is a
+// bf16 value and both subtractions are exact.  A bf16 x bf16 product is
+// exact in fp32, so x.w = x.hi + x.mid + x.lo is an fp32 dot product of
+// exact products, at three 16x16x32 bf16 MFMAs per 32 k instead of eight
+// 16x16x4 fp32 ones.  K is split over the waves of a workgroup (each wave
+// takes a contiguous range of 32-wide steps) and the partial tiles are added
 // in wave order through LDS, so the result is deterministic.  A workgroup
-// covers 16 experts x 16*NT tokens.
+// covers 16 experts x 16*NT tokens.  NaN weights stay NaN in hi.
+
+__device__ __forceinline__ uint32_t trunc_bf16_bits(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t t = u & 0xffff0000u;
+  return (u & 0x7fffffffu) > 0x7f800000u ? (t | 0x00400000u) : t;  // keep NaN a NaN
+}
 
 __device__ __forceinline__ void split3_bf16(const float (&w)[8], uint4& hi, uint4& mid, uint4& lo) {
   uint32_t h[4], m[4], l[4];
 #pragma unroll
   for (int i = 0; i < 8; i += 2) {
-    bf16_t h0 = f32_to_bf16(w[i]), h1 = f32_to_bf16(w[i + 1]);
-    const float r0 = w[i] - bf16_to_f32(h0), r1 = w[i + 1] - bf16_to_f32(h1);
-    bf16_t m0 = f32_to_bf16(r0), m1 = f32_to_bf16(r1);
-    const float q0 = r0 - bf16_to_f32(m0), q1 = r1 - bf16_to_f32(m1);
-    h[i / 2] = h0 | (static_cast<uint32_t>(h1) << 16);
-    m[i / 2] = m0 | (static_cast<uint32_t>(m1) << 16);
-    l[i / 2] = f32_to_bf16(q0) | (static_cast<uint32_t>(f32_to_bf16(q1)) << 16);
+    uint32_t hb[2], mb[2], lb[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float v = w[i + j];
+      hb[j] = trunc_bf16_bits(v);
+      const float r = v - __uint_as_float(hb[j]);
+      mb[j] = __float_as_uint(r) & 0xffff0000u;
+      lb[j] = __float_as_uint(r - __uint_as_float(mb[j])) & 0xffff0000u;
+    }
+    h[i / 2] = (hb[0] >> 16) | hb[1];
+    m[i / 2] = (mb[0] >> 16) | mb[1];
+    l[i / 2] = (lb[0] >> 16) | lb[1];
   }
   hi = uint4{h[0], h[1], h[2], h[3]};
   mid = uint4{m[0], m[1], m[2], m[3]};
   lo = uint4{l[0], l[1], l[2], l[3]};
 }
 
-template <int NT, int NW>
-__global__ __launch_bounds__(64 * NW) void router_logits_bf16_kernel(const bf16_t* __restrict__ x,
-                                                                     const float* __restrict__ wg,
-                                                                     float* __restrict__ logits,
-                                                                     int T, int E, int d) {
-  constexpr int U = 4;  // 32-wide steps whose loads are issued together
+// kTopk (NT = 1, NW = 16, E <= 16: one workgroup holds every expert of its
+// 16 tokens): the workgroup also selects, one wave per token.
+template <int NT, int NW, bool kTopk>
+__global__ __launch_bounds__(64 * NW) void router_logits_bf16_kernel(
+    const bf16_t* __restrict__ x, const float* __restrict__ wg, float* __restrict__ logits,
+    int32_t* __restrict__ topk_ids, float* __restrict__ topk_w, int T, int E, int d, int k) {
+  static_assert(!kTopk || (NT == 1 && NW == 16), "fused selection: 16 tokens, 16 waves");
+  // 32-wide steps whose loads are issued together: the few-token kernel is
+  // latency-bound, so it takes a whole wave's K range (d = 4096) in one round
+  constexpr int U = NT == 1 ? 8 : 4;
   __shared__ f32x4 red[NW][NT][64];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -167,90 +262,25 @@ __global__ __launch_bounds__(64 * NW) void router_logits_bf16_kernel(const bf16_
   __syncthreads();
   // D layout: lane holds token column r16, expert rows 4g .. 4g+3.  The wave
   // partials are added in wave order.
+  __shared__ float lg[kTopk ? 16 : 1][16];
   for (int nt = wave; nt < NT; nt += NW) {
     f32x4 v = red[0][nt][lane];
 #pragma unroll
     for (int w = 1; w < NW; ++w) v += red[w][nt][lane];
     const int t = t0 + nt * 16 + r16;
-    if (t < T) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int ee = blockIdx.y * 16 + 4 * g + q;
-        if (ee < E) logits[static_cast<size_t>(t) * E + ee] = v[q];
-      }
+    for (int q = 0; q < 4; ++q) {
+      const int ee = blockIdx.y * 16 + 4 * g + q;
+      if (t < T && ee < E) logits[static_cast<size_t>(t) * E + ee] = v[q];
+      if constexpr (kTopk) lg[r16][4 * g + q] = v[q];
     }
   }
-}
-
-// ---------------------------------------------------------------- top-k + gates
-//
-// One wavefront per token.  Lane l holds the logits of experts l, l+64, ...
-// Each of the k rounds takes the wave-wide best untaken expert, ordering by
-// (logit descending, index ascending); NaN counts as -inf.  Lane j keeps the
-// j-th pick, then the gates are exp(l_j - l_0) / sum, with l_0 the largest
-// selected logit.
-
-constexpr int kMaxExpertsPerLane = 16;  // E <= 1024
-
-__device__ __forceinline__ bool better(float av, int ae, float bv, int be) {
-  return av > bv || (av == bv && ae < be);
-}
-
-__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ logits,
-                                                          int32_t* __restrict__ topk_ids,
-                                                          float* __restrict__ topk_w, int T,
-                                                          int E, int k) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const float* row = logits + static_cast<size_t>(t) * E;
-  float v[kMaxExpertsPerLane];
-  const int per_lane = (E + 63) >> 6;
-#pragma unroll
-  for (int i = 0; i < kMaxExpertsPerLane; ++i) {
-    const int e = lane + 64 * i;
-    float val = -INFINITY;
-    if (i < per_lane && e < E) {
-      val = row[e];
-      if (val != val) val = -INFINITY;  // NaN ranks below every number
-    }
-    v[i] = val;
-  }
-  uint32_t taken = 0;  // bit i: expert lane + 64*i already selected
-  float my_v = -INFINITY;
-  int my_e = 0;
-  for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int be = 0x7fffffff;
-#pragma unroll
-    for (int i = 0; i < kMaxExpertsPerLane; ++i) {
-      const int e = lane + 64 * i;
-      if (i < per_lane && e < E && !((taken >> i) & 1u) && better(v[i], e, bv, be)) {
-        bv = v[i];
-        be = e;
-      }
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, kWave);
-      const int oe = __shfl_xor(be, off, kWave);
-      if (better(ov, oe, bv, be)) {
-        bv = ov;
-        be = oe;
-      }
-    }
-    if (be < E && (be & 63) == lane) taken |= 1u << (be >> 6);
-    if (lane == j) {
-      my_v = bv;
-      my_e = be;
-    }
-  }
-  const float l0 = __shfl(my_v, 0, kWave);
-  const float p = lane < k ? expf(my_v - l0) : 0.f;
-  const float s = wave_sum(p);
-  if (lane < k) {
-    topk_ids[static_cast<size_t>(t) * k + lane] = my_e;
-    topk_w[static_cast<size_t>(t) * k + lane] = p / s;
+  if constexpr (kTopk) {
+    __syncthreads();
+    const int t = t0 + wave;
+    if (t < T)
+      topk_wave(lg[wave], E, k, topk_ids + static_cast<size_t>(t) * k,
+                topk_w + static_cast<size_t>(t) * k);
   }
 }
 
@@ -264,13 +294,25 @@ hipError_t launch_router_logits(const void* x, int act_dtype, const float* wg, f
                                                      T, E, d);
   } else if (T <= 64) {  // few tokens: split K 16 ways for latency
     dim3 grid((T + 15) / 16, (E + 15) / 16);
-    router_logits_bf16_kernel<1, 16><<<grid, 1024, 0, s>>>(static_cast<const bf16_t*>(x), wg,
-                                                           logits, T, E, d);
+    router_logits_bf16_kernel<1, 16, false><<<grid, 1024, 0, s>>>(
+        static_cast<const bf16_t*>(x), wg, logits, nullptr, nullptr, T, E, d, 0);
   } else {
     dim3 grid((T + 63) / 64, (E + 15) / 16);
-    router_logits_bf16_kernel<4, 4><<<grid, 256, 0, s>>>(static_cast<const bf16_t*>(x), wg,
-                                                         logits, T, E, d);
+    router_logits_bf16_kernel<4, 4, false><<<grid, 256, 0, s>>>(
+        static_cast<const bf16_t*>(x), wg, logits, nullptr, nullptr, T, E, d, 0);
   }
+  return hipGetLastError();
+}
+
+bool router_fused(int act_dtype, int T, int E) {
+  return act_dtype == kDtypeBF16 && T <= 64 && E <= 16;
+}
+
+hipError_t launch_router_fused(const void* x, const float* wg, float* logits, int32_t* ids,
+                               float* w, int T, int E, int d, int k, hipStream_t s) {
+  if (E > 16) return hipErrorInvalidValue;
+  router_logits_bf16_kernel<1, 16, true><<<dim3((T + 15) / 16, 1), 1024, 0, s>>>(
+      static_cast<const bf16_t*>(x), wg, logits, ids, w, T, E, d, k);
   return hipGetLastError();
 }
 

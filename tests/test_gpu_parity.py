@@ -188,8 +188,10 @@ def test_output_guard_bands_untouched():
     assert torch.isfinite(out.float()).all()
 
 
-def test_kernel_timing_counts_launches():
-    inp = synth.make_inputs("decode_bf16", T=8, device=DEV, d=256, I=128, x_std=1.0)
+@pytest.mark.parametrize("E,topk_launches", [(8, 0), (32, 3)])
+def test_kernel_timing_counts_launches(E, topk_launches):
+    # with at most 16 experts and 64 tokens the router kernel selects itself
+    inp = synth.make_inputs("decode_bf16", T=8, device=DEV, d=256, I=128, E=E, x_std=1.0)
     B.moe_timing_collect(reset=True)
     B.moe_timing_enable(True)
     try:
@@ -198,9 +200,24 @@ def test_kernel_timing_counts_launches():
         t = B.moe_timing_collect(reset=True)
     finally:
         B.moe_timing_enable(False)
-    for name in ("route_logits", "route_topk", "align", "ffn13", "ffn2", "combine"):
+    for name in ("route_logits", "align", "ffn13", "ffn2", "combine"):
         ms, n = t[name]
         assert n == 3 and ms > 0, (name, t[name])
+    assert t["route_topk"][1] == topk_launches
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 8, 2), (16, 16, 4), (17, 8, 2), (64, 16, 16), (64, 12, 1)])
+def test_fused_router_selection_matches_topk_kernel(T, E, k):
+    # the router kernel's own selection (E <= 16, T <= 64) equals the separate
+    # top-k kernel's on the logits it wrote, ids and gates bit for bit
+    g = torch.Generator().manual_seed(T * 131 + E)
+    x = torch.randn(T, 512, generator=g).to(torch.bfloat16).to(DEV)
+    wg = (torch.randn(E, 512, generator=g) * 0.02).to(DEV)
+    logits, ids, w = B.moe_route(x, wg, k)
+    ids2, w2 = B.moe_route_logits(logits, k)
+    assert torch.equal(ids, ids2)
+    assert torch.equal(w, w2)
+    assert np.array_equal(ids.cpu().numpy(), oracle.select_topk(logits.cpu().double().numpy(), k))
 
 
 # ---------------------------------------------------------------- full-size workloads
