@@ -62,6 +62,14 @@ def parse():
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the layer, run a plain device copy of this many bytes "
                          "(reference reading for HBM traffic counters)")
+    ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="no GPU: write profiles/ffn13_<workload>_traffic.json from the output "
+                         "directories of four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE over "
+                         "this bench, then over --copy-bytes %d)" % (1 << 30))
+    ap.add_argument("--summarize-stats", nargs="+", metavar="DIR",
+                    help="no GPU: write profiles/<workload>_kernel_stats.md from a rocprofv3 "
+                         "--kernel-trace --stats output directory (and the run's stdout file)")
+    ap.add_argument("--command", default="", help="profiling command recorded in the summary")
     return ap.parse_args()
 
 
@@ -139,11 +147,135 @@ def cpu_baseline(inp_T, k_sample: int, workload: str) -> dict:
                       f"({len(os.sched_getaffinity(0))} host cores visible, BLAS threads {threads})"}
 
 
+COPY_CAL_BYTES = 1 << 30
+
+
+def _counter_rows(directory: str):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit(f"no counter_collection.csv under {directory}")
+    return rows
+
+
+def _short_kernel(name: str) -> str:
+    name = name.replace("void ", "", 1)
+    depth, out = 0, []
+    for ch in name:  # drop the parameter list, keep template arguments
+        if ch == "(" and depth == 0:
+            break
+        depth += ch == "<"
+        depth -= ch == ">"
+        out.append(ch)
+    return "".join(out).replace("moe::", "")
+
+
+def summarize_traffic(workload: str, dirs, command: str) -> str:
+    """HBM bytes per ffn13 launch: FETCH_SIZE and WRITE_SIZE (KiB per dispatch)
+    scaled by what the same counters read for a plain device copy of
+    COPY_CAL_BYTES bytes."""
+    fetch, write, cfetch, cwrite = (_counter_rows(d) for d in dirs)
+
+    def factor(rows, counter):
+        vals = sorted(float(r["Counter_Value"]) for r in rows
+                      if r["Counter_Name"] == counter and "copyBuffer" in r["Kernel_Name"])
+        if not vals:
+            raise SystemExit(f"no copy kernel with {counter} in the calibration run")
+        return COPY_CAL_BYTES / (vals[len(vals) // 2] * 1024.0)
+
+    ff, fw = factor(cfetch, "FETCH_SIZE"), factor(cwrite, "WRITE_SIZE")
+
+    def launches(rows, counter):
+        got = [(int(r["Dispatch_Id"]), r["Kernel_Name"], int(r["Grid_Size"]), float(r["Counter_Value"]))
+               for r in rows if r["Counter_Name"] == counter and "ffn13" in r["Kernel_Name"]]
+        return sorted(got)
+
+    lf, lw = launches(fetch, "FETCH_SIZE"), launches(write, "WRITE_SIZE")
+    if len(lf) != len(lw) or not lf:
+        raise SystemExit(f"ffn13 launches differ between the runs: {len(lf)} vs {len(lw)}")
+    rows = []
+    for (_, kf, gf, vf), (_, kw, gw, vw) in zip(lf, lw):
+        if kf != kw or gf != gw:
+            raise SystemExit("the two runs launched different ffn13 kernels in order")
+        rows.append({"kernel": _short_kernel(kf), "grid_threads": gf,
+                     "fetch_bytes": int(vf * 1024 * ff), "write_bytes": int(vw * 1024 * fw)})
+    per_launch = sum(r["fetch_bytes"] + r["write_bytes"] for r in rows) / len(rows)
+    out = {
+        "kernel": "ffn13 (grouped W13 + SiLU*mul)",
+        "workload": workload,
+        "kernel_source_sha": kernel_source_sha(),
+        "command": command,
+        "calibration": {
+            "copy_bytes": COPY_CAL_BYTES,
+            "FETCH_SIZE_bytes_per_counted_byte": round(ff, 4),
+            "WRITE_SIZE_bytes_per_counted_byte": round(fw, 4),
+            "note": "counter values are KiB per dispatch; each is scaled by the bytes a plain "
+                    "device copy of copy_bytes moves per counted byte",
+        },
+        "launches": rows,
+        "traffic_bytes_per_launch": int(per_launch),
+    }
+    path = os.path.join(ROOT, "profiles", f"ffn13_{workload}_traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    return path
+
+
+def summarize_stats(workload: str, paths, command: str) -> str:
+    """Markdown table of the layer's kernels from rocprofv3 --stats."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(paths[0], "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {paths[0]}")
+    with open(files[0]) as fh:
+        stats = [r for r in csv.DictReader(fh) if "moe::" in r["Name"]]
+    stats.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = [f"# Kernel stats: {workload} workload (batches {', '.join(map(str, WORKLOAD_BATCHES[workload]))})",
+             "", "Command (from the repository root, one MI355X):", "", f"    {command}", "",
+             f"Kernel sources sha (bench.py kernel_source_sha): `{kernel_source_sha()}`", "",
+             "| kernel | calls | avg us | min us | max us | total us |", "|---|---|---|---|---|---|"]
+    for r in stats:
+        lines.append(f"| `{_short_kernel(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                     f"{float(r['TotalDurationNs']) / 1e3:.0f} |")
+    f13 = [r for r in stats if "ffn13" in r["Name"]]
+    if f13:
+        calls = sum(int(r["Calls"]) for r in f13)
+        total = sum(float(r["TotalDurationNs"]) for r in f13)
+        lines += ["", f"ffn13 over all its instantiations: {calls} calls, average "
+                      f"{total / calls / 1e3:.1f} us per launch."]
+    if len(paths) > 1 and os.path.exists(paths[1]):
+        with open(paths[1]) as fh:
+            for line in fh:
+                if line.startswith("{") and '"roofline"' in line:
+                    j = json.loads(line)
+                    lines.append(f"bench.py in the same run measured {j['roofline']['avg_launch_us']} us "
+                                 f"per ffn13 launch with HIP events inside its timed region.")
+    lines += ["Other kernels in the trace (torch RNG, casts, copies) are input generation, "
+              "outside the timed region.", ""]
+    path = os.path.join(ROOT, "profiles", f"{workload}_kernel_stats.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines))
+    return path
+
+
 def main() -> int:
     args = parse()
+    if args.summarize_traffic:
+        print(summarize_traffic(args.workload, args.summarize_traffic, args.command))
+        return 0
+    if args.summarize_stats:
+        print(summarize_stats(args.workload, args.summarize_stats, args.command))
+        return 0
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
-              "(the layer is single-GPU; multi-GPU sharding is design only).", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the layer runs "
+              "on a single GPU (how it would shard is a design, not code).", file=sys.stderr)
         return 2
     import torch
 

@@ -102,48 +102,80 @@ struct DmaOperands {
 };
 
 // The ring: chunk c (K = k_begin + 256c ..) in buffer c % P (weights in LDS,
-// token fragments in registers).  At chunk c the wave waits until only the
-// P-2 later stages are outstanding (loads complete in issue order), issues
-// chunk c+P-1 into the buffers read at chunk c-1 (clamped to the last chunk:
-// the duplicate lands where nobody reads again, and keeps the wait counts
-// uniform), then runs chunk c's MFMAs.  NSL: live token subtiles.
+// token fragments in registers).  Stages 0 .. P-2 are issued up front; at
+// chunk c the wave waits until only the stages issued after chunk c are
+// outstanding (loads complete in issue order), issues chunk c+P-1 (while
+// there is one) into the buffers read at chunk c-1, then runs chunk c's
+// MFMAs.  Every wait count is a compile-time immediate: the steady loop goes
+// P chunks at a time, and the last P-1 chunks (which issue nothing) run from
+// a switch on the buffer they start in.  NSL: live token subtiles.
 template <int NROW, int NS, int P, int NSL>
 struct DmaRing {
+  static constexpr int kL = DmaGeom<NROW, NSL>::kLoads;
   const DmaOperands<NROW, NS>& op;
   uint8_t* const (&ring)[4];
   int k_begin, nch;
 
+  __device__ __forceinline__ void issue(int q, uint8_t* stage, uint4 (&a)[NS][8], int c) const {
+    const int k = k_begin + c * kDmaKC;
+    op.issue_w(stage, k);
+    op.template issue_a<NSL>(a, k);
+  }
+
+  // chunk c in buffer p, issuing chunk c+P-1
   template <int p>
   __device__ __forceinline__ void step(int c, uint4 (&a)[P][NS][8], f32x4 (&acc)[NS][NROW]) const {
     constexpr int pn = (p + P - 1) % P;
-    __builtin_amdgcn_s_waitcnt(dma_vmcnt(DmaGeom<NROW, NSL>::kLoads * (P - 2)));
-    const int kn = k_begin + min(c + P - 1, nch - 1) * kDmaKC;
-    op.issue_w(ring[pn], kn);
-    op.template issue_a<NSL>(a[pn], kn);
+    __builtin_amdgcn_s_waitcnt(dma_vmcnt(kL * (P - 2)));
+    issue(pn, ring[pn], a[pn], c + P - 1);
     op.template mma<NSL>(ring[p], a[p], acc);
+  }
+  // chunk in buffer p with W stages issued after it, issuing nothing
+  template <int p, int W>
+  __device__ __forceinline__ void last(uint4 (&a)[P][NS][8], f32x4 (&acc)[NS][NROW]) const {
+    __builtin_amdgcn_s_waitcnt(dma_vmcnt(kL * W));
+    op.template mma<NSL>(ring[p], a[p], acc);
+  }
+  // the final P-1 chunks, the first of them in buffer b
+  template <int b>
+  __device__ __forceinline__ void tail(uint4 (&a)[P][NS][8], f32x4 (&acc)[NS][NROW]) const {
+    last<b % P, P - 2>(a, acc);
+    if constexpr (P > 2) last<(b + 1) % P, P - 3>(a, acc);
+    if constexpr (P > 3) last<(b + 2) % P, P - 4>(a, acc);
   }
 
   __device__ __forceinline__ void run(f32x4 (&acc)[NS][NROW]) const {
+    static_assert(P >= 2 && P <= 4, "ring depth");
     uint4 a[P][NS][8];
+    // prologue; a chunk past the end (only when nch < P-1) repeats the last
 #pragma unroll
-    for (int q = 0; q + 1 < P; ++q) {
-      const int kq = k_begin + min(q, nch - 1) * kDmaKC;
-      op.issue_w(ring[q], kq);
-      op.template issue_a<NSL>(a[q], kq);
+    for (int q = 0; q + 1 < P; ++q) issue(q, ring[q], a[q], min(q, nch - 1));
+    if (nch >= P - 1) {
+      const int M = nch - P + 1;  // chunks that issue a later one
+      int c0 = 0;
+      for (; c0 + P <= M; c0 += P) {
+        step<0>(c0, a, acc);
+        step<1>(c0 + 1, a, acc);
+        if constexpr (P > 2) step<2>(c0 + 2, a, acc);
+        if constexpr (P > 3) step<3>(c0 + 3, a, acc);
+      }
+      const int r = M - c0;  // 0 .. P-1 issuing chunks left
+      if (r >= 1) step<0>(c0, a, acc);
+      if constexpr (P > 2)
+        if (r >= 2) step<1>(c0 + 1, a, acc);
+      if constexpr (P > 3)
+        if (r >= 3) step<2>(c0 + 2, a, acc);
+      switch (r) {
+        case 0: tail<0>(a, acc); break;
+        case 1: tail<1>(a, acc); break;
+        case 2: if constexpr (P > 2) tail<2>(a, acc); break;
+        case 3: if constexpr (P > 3) tail<3>(a, acc); break;
+      }
+    } else {  // nch < P-1: the prologue issued P-1 stages for nch chunks
+      last<0, P - 2>(a, acc);
+      if constexpr (P > 3)
+        if (nch >= 2) last<1, P - 3>(a, acc);
     }
-    int c0 = 0;
-    for (; c0 + P <= nch; c0 += P) {
-      step<0>(c0, a, acc);
-      if constexpr (P > 1) step<1>(c0 + 1, a, acc);
-      if constexpr (P > 2) step<2>(c0 + 2, a, acc);
-      if constexpr (P > 3) step<3>(c0 + 3, a, acc);
-    }
-    const int rem = nch - c0;  // 0 .. P-1 chunks left
-    if (rem >= 1) step<0>(c0, a, acc);
-    if constexpr (P > 2)
-      if (rem >= 2) step<1>(c0 + 1, a, acc);
-    if constexpr (P > 3)
-      if (rem >= 3) step<2>(c0 + 2, a, acc);
     __builtin_amdgcn_s_waitcnt(dma_vmcnt(0));  // no load may land after the wave ends
   }
 };
