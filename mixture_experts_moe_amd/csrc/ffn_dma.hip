@@ -335,7 +335,7 @@ __global__ __launch_bounds__(kDmaThreads) void ffn2_dma_kernel(
 #define MOE_DMA13_P1 4
 #endif
 #ifndef MOE_DMA13_P2
-#define MOE_DMA13_P2 3
+#define MOE_DMA13_P2 2
 #endif
 #ifndef MOE_DMA2_P1
 #define MOE_DMA2_P1 3

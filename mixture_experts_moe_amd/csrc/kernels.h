@@ -74,16 +74,19 @@ inline int64_t ffn_blocks_estimate(int64_t cap, int B, int E, int64_t A) {
 }
 
 // Weight streaming through LDS for bf16 blocks of 16 or 32 tokens (d and I
-// multiples of 256), when the W13 grid has enough workgroups for several
-// rounds of the LDS-limited occupancy; batches touching few experts keep the
-// register path, whose smaller workgroups all fit on the chip at once.
+// multiples of 256), when the W13 grid has at least MOE_DMA_MIN_WORKGROUPS
+// workgroups (about two rounds of the LDS-limited occupancy); smaller grids
+// keep the register path, whose workgroups all fit on the chip at once.
 bool dma_stream_fits(int d, int I);
+#ifndef MOE_DMA_MIN_WORKGROUPS
+#define MOE_DMA_MIN_WORKGROUPS 1024
+#endif
 inline bool dma_stream_use(int w_dtype, int act_dtype, int B, int d, int I, int64_t blocks_est) {
 #ifdef MOE_NO_DMA_STREAM
   return false;
 #else
   return w_dtype == kDtypeBF16 && act_dtype == kDtypeBF16 && (B == 16 || B == 32) &&
-         dma_stream_fits(d, I) && blocks_est * (I / 16) >= 4096;
+         dma_stream_fits(d, I) && blocks_est * (I / 16) >= MOE_DMA_MIN_WORKGROUPS;
 #endif
 }
 inline bool dma_stream_use(const FfnArgs& a) {
