@@ -89,14 +89,20 @@ struct Plan {
 int default_block_m(const moe_desc* d, int top_k) {
   if (d->weight_dtype == MOE_DTYPE_F32) return 16;
   const int64_t T = d->num_tokens;
+  const int hid = static_cast<int>(d->hidden), inter = static_cast<int>(d->intermediate);
+  const bool bf16_act = d->act_dtype == MOE_DTYPE_BF16;
   if (T <= 16) return 16;
+  // e4m3fn weights with experts averaging at most 4 slots: blocks of 16 keep
+  // the LDS-streaming kernel (an expert holding more takes further blocks)
+  if (T <= 64 && d->weight_dtype == MOE_DTYPE_E4M3FN && bf16_act &&
+      T * top_k <= 4 * d->num_experts && moe::dma_stream_fits(hid, inter, MOE_DTYPE_E4M3FN))
+    return 16;
   if (T <= 32) return 32;
   if (T <= 64) {
     // blocks of 32 keep the LDS-streaming kernel (an expert holding more
     // than 32 of the tokens takes a second block)
-    const bool lds = d->weight_dtype == MOE_DTYPE_BF16 && d->act_dtype == MOE_DTYPE_BF16 &&
-                     moe::dma_stream_fits(static_cast<int>(d->hidden),
-                                          static_cast<int>(d->intermediate));
+    const bool lds = d->weight_dtype == MOE_DTYPE_BF16 && bf16_act &&
+                     moe::dma_stream_fits(hid, inter, MOE_DTYPE_BF16);
     return lds ? 32 : 64;
   }
   const int64_t per_expert = T * top_k / d->num_experts;
@@ -134,7 +140,7 @@ void make_plan(const moe_desc* d, int top_k, bool with_routing, Plan* p) {
     const int kc = moe::ffn2_kchunk(p->d, p->I, p->B, p->wdt, p->act, blocks_est);
     // one wave per dma_w2_channels() (LDS streaming) or about 32 (register
     // path) output channels
-    const int64_t waves = blocks_est * (p->d / (lds ? moe::dma_w2_channels() : 32));
+    const int64_t waves = blocks_est * (p->d / (lds ? moe::dma_w2_channels(p->wdt) : 32));
     int s = 1;
     while (s < 8 && waves * s < 2048 && p->I / (2 * s) >= 4 * kc) s *= 2;
     const int per = (p->I + s - 1) / s;

@@ -365,7 +365,7 @@ int kchunk_for(int K) {
 }
 
 int ffn2_kchunk(int d, int I, int B, int w_dtype, int act_dtype, int64_t blocks_est) {
-  if (dma_stream_use(w_dtype, act_dtype, B, d, I, blocks_est)) return 256;
+  if (dma_stream_use(w_dtype, act_dtype, B, d, I, blocks_est)) return dma_stream_kc(w_dtype);
   return w_dtype == kDtypeE4M3FN ? kchunk_for<fp8_t>(I) : kchunk_for<bf16_t>(I);
 }
 

@@ -73,11 +73,14 @@ inline int64_t ffn_blocks_estimate(int64_t cap, int B, int E, int64_t A) {
   return cap / B < est ? cap / B : est;
 }
 
-// Weight streaming through LDS for bf16 blocks of 16 or 32 tokens (d and I
-// multiples of 256), when the W13 grid has at least MOE_DMA_MIN_WORKGROUPS
-// workgroups (about two rounds of the LDS-limited occupancy); smaller grids
-// keep the register path, whose workgroups all fit on the chip at once.
-bool dma_stream_fits(int d, int I);
+// Weight streaming through LDS: bf16 weights in blocks of 16 or 32 tokens,
+// e4m3fn weights in blocks of 16 (d and I multiples of the stage's K: 256
+// bf16 or 512 e4m3fn elements), bf16 activations, when the W13 grid has at
+// least MOE_DMA_MIN_WORKGROUPS workgroups (about two rounds of the
+// LDS-limited occupancy); smaller grids keep the register path, whose
+// workgroups all fit on the chip at once.
+bool dma_stream_fits(int d, int I, int w_dtype);
+int dma_stream_kc(int w_dtype);  // K elements per stage
 #ifndef MOE_DMA_MIN_WORKGROUPS
 #define MOE_DMA_MIN_WORKGROUPS 1024
 #endif
@@ -85,8 +88,10 @@ inline bool dma_stream_use(int w_dtype, int act_dtype, int B, int d, int I, int6
 #ifdef MOE_NO_DMA_STREAM
   return false;
 #else
-  return w_dtype == kDtypeBF16 && act_dtype == kDtypeBF16 && (B == 16 || B == 32) &&
-         dma_stream_fits(d, I) && blocks_est * (I / 16) >= MOE_DMA_MIN_WORKGROUPS;
+  const bool shape = (w_dtype == kDtypeBF16 && (B == 16 || B == 32)) ||
+                     (w_dtype == kDtypeE4M3FN && B == 16);
+  return act_dtype == kDtypeBF16 && shape && dma_stream_fits(d, I, w_dtype) &&
+         blocks_est * (I / 16) >= MOE_DMA_MIN_WORKGROUPS;
 #endif
 }
 inline bool dma_stream_use(const FfnArgs& a) {
@@ -94,7 +99,7 @@ inline bool dma_stream_use(const FfnArgs& a) {
                         ffn_blocks_estimate(a.cap, a.B, a.E, a.A));
 }
 hipError_t launch_ffn13_dma(const FfnArgs& a, hipStream_t s);
-int dma_w2_channels();  // output channels per W2 workgroup of that path
+int dma_w2_channels(int w_dtype);  // output channels per W2 workgroup of that path
 hipError_t launch_ffn2_dma(const FfnArgs& a, hipStream_t s);
 
 // K chunk the W2 kernel uses for a given shape, block size, dtypes and

@@ -137,6 +137,11 @@ SMALL = [
     ("fp8_channel", dict(workload="fp8", d=256, I=192, E=16, k=4), 64, 0),
     ("fp8_channel", dict(workload="fp8", d=256, I=192, E=16, k=4), 200, 128),
     ("fp8_tensor", dict(workload="fp8", d=256, I=192, E=16, k=4, scale_mode="tensor"), 50, 0),
+    # e4m3fn weights streamed through LDS (d and I multiples of 512, blocks of
+    # 16): ring tail only, one issuing chunk + tail, chunk count below the ring
+    ("fp8_lds", dict(workload="fp8", d=1024, I=1024, E=32, k=4), 8, 0),
+    ("fp8_lds", dict(workload="fp8", d=1536, I=1536, E=16, k=4), 12, 0),
+    ("fp8_lds", dict(workload="fp8", d=512, I=512, E=64, k=4, scale_mode="tensor"), 16, 0),
     ("skew_small", dict(workload="skew", d=192, I=128), 300, 0),
 ]
 
