@@ -134,7 +134,19 @@ void make_plan(const moe_desc* d, int top_k, bool with_routing, Plan* p) {
   // fixed order.
   p->splits = 1;
   p->ksplit = p->I;
-  if (p->wdt != MOE_DTYPE_F32 && p->A > 0 && p->B <= 64) {  // the GEMM paths do not split
+  if (p->A > 0 && p->B == 256) {
+    // the big-tile W2 has d/256 channel tiles per block: split K until the
+    // grid fills about four rounds of the CUs (splits of >= 16 stages)
+    const int64_t blocks_est = moe::ffn_blocks_estimate(p->cap, p->B, p->E, p->A);
+    const int64_t tiles = blocks_est * (p->d / 256);
+    const int kc = moe::big_w2_kchunk();
+    int s = 1;
+    while (s < 4 && tiles * s < 1024 && p->I / (2 * s) >= 8 * kc) s *= 2;
+    const int per = (p->I + s - 1) / s;
+    p->ksplit = (per + kc - 1) / kc * kc;
+    p->splits = (p->I + p->ksplit - 1) / p->ksplit;
+  }
+  if (p->wdt != MOE_DTYPE_F32 && p->A > 0 && p->B <= 64) {  // the 128-token GEMM does not split
     const int64_t blocks_est = moe::ffn_blocks_estimate(p->cap, p->B, p->E, p->A);
     const bool lds = moe::dma_stream_use(p->wdt, p->act, p->B, p->d, p->I, blocks_est);
     const int kc = moe::ffn2_kchunk(p->d, p->I, p->B, p->wdt, p->act, blocks_est);

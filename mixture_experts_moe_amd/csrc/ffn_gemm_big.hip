@@ -33,13 +33,28 @@ constexpr int kBigThreads = 256;
 constexpr int kBigTokens = 256;  // block size B of this path
 constexpr int kBigRows = 256;    // weight rows per tile
 constexpr int kBigK = 64;        // K elements per stage
+#ifndef MOE_BIG_N
+#define MOE_BIG_N 256
+#endif
+constexpr int kBigN = MOE_BIG_N;  // tokens per workgroup tile: all 256 of the block, or half
+constexpr int kBigHalves = kBigTokens / kBigN;
+constexpr int kBigNB = kBigN / 32;  // 16-token fragments per wave (two waves share N)
 constexpr int kBigSlots = kBigK / 8;                 // 16-byte slots per LDS row
 constexpr int kBigRowBytes = kBigK * 2;
 constexpr int kBigRowsPerGroup = 1024 / kBigRowBytes;  // rows filled by one 1 KB load
-constexpr int kBigGroups = kBigRows / kBigRowsPerGroup / 4;  // per wave and operand
+constexpr int kBigGroups = kBigRows / kBigRowsPerGroup / 4;  // A loads per wave and stage
+constexpr int kBigGroupsB = kBigN / kBigRowsPerGroup / 4;   // B loads per wave and stage
+constexpr int kBigLoads = kBigGroups + kBigGroupsB;
 constexpr int kBigOperandBytes = kBigRows * kBigRowBytes;
-constexpr int kBigStageBytes = 2 * kBigOperandBytes;
-static_assert(2 * kBigStageBytes <= 160 * 1024, "two stages fit in LDS");
+constexpr int kBigStageBytes = kBigOperandBytes + kBigN * kBigRowBytes;
+// 256 tokens: two stages (128 KB); 128 tokens: three stages (144 KB), which
+// lets the loads run two stages ahead
+constexpr int kBigStages = kBigN == 256 ? 2 : 3;
+static_assert(kBigN == 256 || kBigN == 128, "tile tokens");
+static_assert(kBigStages * kBigStageBytes <= 160 * 1024, "stages fit in LDS");
+#ifndef MOE_BIG_ISSUE_FIRST
+#define MOE_BIG_ISSUE_FIRST 1
+#endif
 #ifndef MOE_BIG_RASTER
 #define MOE_BIG_RASTER 1
 #endif
@@ -95,16 +110,16 @@ struct BigLoader {
 };
 
 __device__ __forceinline__ void big_issue(const BigLoader& ld,
-                                          const bf16_t* const (&bsrc)[kBigGroups],
+                                          const bf16_t* const (&bsrc)[kBigGroupsB],
                                           uint8_t* stage, int k0, int wave) {
 #pragma unroll
   for (int q = 0; q < kBigGroups; ++q)
     __builtin_amdgcn_global_load_lds(ld.a_src(q, k0), stage + (wave * kBigGroups + q) * 1024, 16,
                                      0, 0);
 #pragma unroll
-  for (int q = 0; q < kBigGroups; ++q)
+  for (int q = 0; q < kBigGroupsB; ++q)
     __builtin_amdgcn_global_load_lds(bsrc[q] + k0,
-                                     stage + kBigOperandBytes + (wave * kBigGroups + q) * 1024, 16,
+                                     stage + kBigOperandBytes + (wave * kBigGroupsB + q) * 1024, 16,
                                      0, 0);
 }
 
@@ -119,11 +134,11 @@ __device__ __forceinline__ bf16x8 big_frag(const uint8_t* op, int row, int slot)
 }
 
 struct BigFrags {
-  bf16x8 a[8], b[8];
+  bf16x8 a[8], b[kBigNB];
 };
 
 // Fragments of k-step j (k = 32j .. 32j+31 of the stage) for this wave's
-// 8 row tiles (rows arow0 + 16t) and 8 token tiles (rows brow0 + 16u).
+// 8 row tiles (rows arow0 + 16t) and kBigNB token tiles (rows brow0 + 16u).
 __device__ __forceinline__ void big_load_frags(BigFrags& f, const uint8_t* opa, const uint8_t* opb,
                                                int arow0, int arow_up, int brow0, int j) {
   const int lane = threadIdx.x & 63;
@@ -133,41 +148,58 @@ __device__ __forceinline__ void big_load_frags(BigFrags& f, const uint8_t* opa, 
   for (int t = 0; t < 8; ++t)
     f.a[t] = big_frag(opa, (t < 4 ? arow0 + 16 * t : arow_up + 16 * (t - 4)) + r16, slot);
 #pragma unroll
-  for (int u = 0; u < 8; ++u) f.b[u] = big_frag(opb, brow0 + 16 * u + r16, slot);
+  for (int u = 0; u < kBigNB; ++u) f.b[u] = big_frag(opb, brow0 + 16 * u + r16, slot);
 }
 
-__device__ __forceinline__ void big_mma(const BigFrags& f, f32x4 (&acc)[8][8]) {
+__device__ __forceinline__ void big_mma(const BigFrags& f, f32x4 (&acc)[8][kBigNB]) {
 #pragma unroll
   for (int t = 0; t < 8; ++t)
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc[t][u] = mfma16x16x32(f.a[t], f.b[u], acc[t][u]);
+    for (int u = 0; u < kBigNB; ++u) acc[t][u] = mfma16x16x32(f.a[t], f.b[u], acc[t][u]);
 }
 
-// First part of one stage of the two-buffer ring: wait for this wave's
-// loads of `cur`, meet the other waves (after which nobody reads `nxt`, the
-// buffer of the previous stage, any more), read the first k-step's
-// fragments, issue the next stage into `nxt` (when kIssue) and read the
-// second k-step's fragments f1 under the first k-step's MFMAs.  The caller
-// runs f1's MFMAs; the compiler may spread them over the next stage's wait,
-// barrier and first reads since they only touch registers.
-template <bool kIssue>
+// Wait for this wave's LDS reads, then meet the other waves.  No memory
+// fence: a workgroup-scope fence would also wait for every direct-to-LDS
+// load this wave has in flight, later stages' included.  Each wave waits
+// explicitly for its own loads of the stage about to be read before it
+// arrives; the memory clobber keeps the compiler from moving LDS accesses
+// across.
+__device__ __forceinline__ void big_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// First part of one stage: wait until this wave's loads of `cur` have
+// landed (kWait of its later loads may stay outstanding), meet the other
+// waves (after which nobody reads `nxt`, the buffer read one or two stages
+// ago, any more), issue the stage after the in-flight ones into `nxt` (when
+// kIssue), read the first k-step's fragments and then the second k-step's
+// (f1) under the first k-step's MFMAs.  The caller runs f1's MFMAs; the
+// compiler may spread them over the next stage's wait, barrier and first
+// reads since they only touch registers.
+template <bool kIssue, int kWait>
 __device__ __forceinline__ void big_half(const BigLoader& ld,
-                                         const bf16_t* const (&bsrc)[kBigGroups],
+                                         const bf16_t* const (&bsrc)[kBigGroupsB],
                                          const uint8_t* cur, uint8_t* nxt, int knext, int wave,
                                          int arow0, int arow_up, int brow0, BigFrags& f1,
-                                         f32x4 (&acc)[8][8]) {
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  __syncthreads();
+                                         f32x4 (&acc)[8][kBigNB]) {
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(kWait));
+  big_barrier();
   const uint8_t* opb = cur + kBigOperandBytes;
   BigFrags f0;
+#if MOE_BIG_ISSUE_FIRST
+  if (kIssue) big_issue(ld, bsrc, nxt, knext, wave);
+  __builtin_amdgcn_sched_barrier(0);
+  big_load_frags(f0, cur, opb, arow0, arow_up, brow0, 0);
+#else
   big_load_frags(f0, cur, opb, arow0, arow_up, brow0, 0);
   __builtin_amdgcn_sched_barrier(0);
   if (kIssue) big_issue(ld, bsrc, nxt, knext, wave);
+#endif
   __builtin_amdgcn_sched_barrier(0);
   big_load_frags(f1, cur, opb, arow0, arow_up, brow0, 1);
   big_mma(f0, acc);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < 8 + kBigNB; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // four MFMAs
   }
@@ -175,51 +207,128 @@ __device__ __forceinline__ void big_half(const BigLoader& ld,
 
 // acc[t][u] += A_rows(t) . B_rows(u)^T over K.  A rows: arow0 + 16t (t < 4)
 // and arow_up + 16(t-4); B rows: brow0 + 16u.  Stage s (K = 64s .. 64s+63)
-// lives in buffer s % 2.  The two buffers are two LDS arrays: with one array
-// the compiler cannot tell that reads of stage s do not depend on the loads
-// of stage s+1 in flight, and waits for those before every read.  The loop
-// is rotated by half a stage so that each stage's second k-step MFMAs can
-// overlap the next stage's start.  nst is even: the launchers require
-// d % 256 == 0 and I % 128 == 0.
-__device__ __forceinline__ void big_mainloop(const BigLoader& ld,
-                                             const bf16_t* const (&bsrc)[kBigGroups],
-                                             uint8_t* buf0, uint8_t* buf1, int nst, int wave,
-                                             int arow0, int arow_up, int brow0,
-                                             f32x4 (&acc)[8][8]) {
-  BigFrags f1;
-  big_issue(ld, bsrc, buf0, 0, wave);
-  big_half<true>(ld, bsrc, buf0, buf1, kBigK, wave, arow0, arow_up, brow0, f1, acc);
-  for (int s = 1; s + 1 < nst; s += 2) {
-    big_mma(f1, acc);
-    big_half<true>(ld, bsrc, buf1, buf0, (s + 1) * kBigK, wave, arow0, arow_up, brow0, f1, acc);
-    big_mma(f1, acc);
-    big_half<true>(ld, bsrc, buf0, buf1, (s + 2) * kBigK, wave, arow0, arow_up, brow0, f1, acc);
+// lives in buffer s % S.  The buffers are separate LDS arrays: with one
+// array the compiler cannot tell that reads of stage s do not depend on the
+// loads of later stages in flight, and waits for those before every read.
+// The loop is rotated by half a stage so that each stage's second k-step
+// MFMAs can overlap the next stage's start.
+struct BigRing {
+  const BigLoader& ld;
+  const bf16_t* const (&bsrc)[kBigGroupsB];
+  uint8_t* const (&buf)[3];
+  int wave, arow0, arow_up, brow0;
+
+  template <int b, bool kIssue, int kWait>
+  __device__ __forceinline__ void step(int s, BigFrags& f1, f32x4 (&acc)[8][kBigNB]) const {
+    constexpr int S = kBigStages;
+    big_half<kIssue, kWait>(ld, bsrc, buf[b], buf[(b + S - 1) % S], (s + S - 1) * kBigK, wave,
+                            arow0, arow_up, brow0, f1, acc);
   }
-  big_mma(f1, acc);
-  big_half<false>(ld, bsrc, buf1, buf0, 0, wave, arow0, arow_up, brow0, f1, acc);
-  big_mma(f1, acc);
-}
+
+  // two stages (nst even: the launchers require d % 256 == 0, I % 128 == 0)
+  __device__ __forceinline__ void run2(int nst, f32x4 (&acc)[8][kBigNB]) const {
+    BigFrags f1;
+    big_issue(ld, bsrc, buf[0], 0, wave);
+    step<0, true, 0>(0, f1, acc);
+    for (int s = 1; s + 1 < nst; s += 2) {
+      big_mma(f1, acc);
+      step<1, true, 0>(s, f1, acc);
+      big_mma(f1, acc);
+      step<0, true, 0>(s + 1, f1, acc);
+    }
+    big_mma(f1, acc);
+    step<1, false, 0>(nst - 1, f1, acc);
+    big_mma(f1, acc);
+  }
+
+  // three stages: loads run two stages ahead; a step waits until only the
+  // next stage's loads are outstanding (none at the last step).  The steady
+  // loop goes three stages at a time; the issuing steps left over and the
+  // last two stages (which issue nothing) start from a switch on their
+  // buffer.  nst >= 2.
+  template <int b>
+  __device__ __forceinline__ void tail3(BigFrags& f1, f32x4 (&acc)[8][kBigNB], int s) const {
+    big_mma(f1, acc);
+    step<b, false, kBigLoads>(s, f1, acc);
+    big_mma(f1, acc);
+    step<(b + 1) % 3, false, 0>(s + 1, f1, acc);
+  }
+  __device__ __forceinline__ void run3(int nst, f32x4 (&acc)[8][kBigNB]) const {
+    constexpr int L = kBigLoads;
+    BigFrags f1;
+    big_issue(ld, bsrc, buf[0], 0, wave);
+    big_issue(ld, bsrc, buf[1], kBigK, wave);
+    const int M = nst - 2;  // stages that issue a later one
+    if (M >= 1) {
+      step<0, true, L>(0, f1, acc);
+      int s = 1;
+      for (; s + 3 <= M; s += 3) {
+        big_mma(f1, acc);
+        step<1, true, L>(s, f1, acc);
+        big_mma(f1, acc);
+        step<2, true, L>(s + 1, f1, acc);
+        big_mma(f1, acc);
+        step<0, true, L>(s + 2, f1, acc);
+      }
+      const int r = M - s;  // 0, 1 or 2 issuing stages left; s == 1 (mod 3)
+      if (r >= 1) {
+        big_mma(f1, acc);
+        step<1, true, L>(s, f1, acc);
+      }
+      if (r >= 2) {
+        big_mma(f1, acc);
+        step<2, true, L>(s + 1, f1, acc);
+      }
+      switch (r) {
+        case 0: tail3<1>(f1, acc, s); break;
+        case 1: tail3<2>(f1, acc, s + 1); break;
+        default: tail3<0>(f1, acc, s + 2); break;
+      }
+    } else {
+      step<0, false, L>(0, f1, acc);
+      big_mma(f1, acc);
+      step<1, false, 0>(1, f1, acc);
+    }
+    big_mma(f1, acc);
+  }
+
+  __device__ __forceinline__ void run(int nst, f32x4 (&acc)[8][kBigNB]) const {
+    if constexpr (kBigStages == 2)
+      run2(nst, acc);
+    else
+      run3(nst, acc);
+  }
+};
+
+#define BIG_BUFFERS(name)                                                                 \
+  __shared__ __attribute__((aligned(1024))) uint8_t name##0[kBigStageBytes];              \
+  __shared__ __attribute__((aligned(1024))) uint8_t name##1[kBigStageBytes];              \
+  __shared__ __attribute__((aligned(1024))) uint8_t name##2[kBigStages > 2 ? kBigStageBytes : 16]; \
+  uint8_t* const name[3] = {name##0, name##1, name##2}
 
 // ------------------------------------------------------------ W13 + SiLU*mul
-// Tile: channels n0 .. n0+127 (rows: 128 gate, then 128 up) x 256 tokens.
+// Tile: channels n0 .. n0+127 (rows: 128 gate, then 128 up) x kBigN tokens
+// (tile b: row block b / kBigHalves, its half b % kBigHalves).
 
 __global__ __launch_bounds__(kBigThreads) void ffn13_big_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ w13,
     const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ block_expert,
     const int32_t* __restrict__ num_padded, bf16_t* __restrict__ h, int d, int I, int k, int A,
     int gx, int gy) {
-  __shared__ __attribute__((aligned(1024))) uint8_t buf0[kBigStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t buf1[kBigStageBytes];
+  BIG_BUFFERS(buf);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15;
   const int g = lane >> 4;
   const BigTile tl = big_tile_of(blockIdx.x, gx, gy);
-  if (!tl.live || tl.b * kBigTokens >= *num_padded) return;  // uniform
-  const int b = tl.b;
+  if (!tl.live) return;  // uniform
+  const int b = tl.b / kBigHalves;
+  const int n_off = (tl.b % kBigHalves) * kBigN;  // first slot of the tile in the block
+  if (b * kBigTokens >= *num_padded) return;
+  const int32_t* blk = sorted_ids + static_cast<size_t>(b) * kBigTokens;
+  if (blk[n_off] >= A) return;  // real slots come first: this half holds none
   const int e = block_expert[b];
   const int n0 = tl.y * 128;
-  const int32_t* blk = sorted_ids + static_cast<size_t>(b) * kBigTokens;
   const size_t two_i = 2 * static_cast<size_t>(I);
 
   // tile rows: 0..127 gate rows n0.., 128..255 the matching up rows
@@ -232,25 +341,26 @@ __global__ __launch_bounds__(kBigThreads) void ffn13_big_kernel(
   ld.a_even = w13 + wrow0 * d + c_even;
   ld.a_odd = w13 + (wrow0 + kBigRowsPerGroup) * d + c_odd;
   ld.a_step = static_cast<size_t>(2 * kBigRowsPerGroup) * d;
-  const bf16_t* bsrc[kBigGroups];
+  const int brow = (kBigN / 4) * wave + lrow;  // token row of B group 0
+  const bf16_t* bsrc[kBigGroupsB];
 #pragma unroll
-  for (int q = 0; q < kBigGroups; ++q) {
-    const int f = blk[row0 + kBigRowsPerGroup * q];  // pad slot: any valid row (never stored)
+  for (int q = 0; q < kBigGroupsB; ++q) {
+    const int f = blk[n_off + brow + kBigRowsPerGroup * q];  // pad slot: any valid row (never stored)
     bsrc[q] = x + static_cast<size_t>(f < A ? f / k : 0) * d + (q & 1 ? c_odd : c_even);
   }
   const int wm = wave & 1, wn = wave >> 1;
-  f32x4 acc[8][8];
+  f32x4 acc[8][kBigNB];
 #pragma unroll
   for (int t = 0; t < 8; ++t)
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < kBigNB; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  big_mainloop(ld, bsrc, buf0, buf1, d / kBigK, wave, 64 * wm, 128 + 64 * wm, 128 * wn, acc);
+  BigRing{ld, bsrc, buf, wave, 64 * wm, 128 + 64 * wm, (kBigN / 2) * wn}.run(d / kBigK, acc);
 
   // lane: token column r16 of tile u, channels n0 + 64wm + 16t + 4g .. +3
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const size_t row = static_cast<size_t>(b) * kBigTokens + 128 * wn + 16 * u + r16;
+  for (int u = 0; u < kBigNB; ++u) {
+    const size_t row = static_cast<size_t>(b) * kBigTokens + n_off + (kBigN / 2) * wn + 16 * u + r16;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       uint32_t packed[2];
@@ -268,53 +378,60 @@ __global__ __launch_bounds__(kBigThreads) void ffn13_big_kernel(
 }
 
 // ------------------------------------------------------------ W2 + gate scale
-// Tile: output channels n0 .. n0+255 x 256 tokens (h rows of the block).
+// Tile: output channels n0 .. n0+255 x kBigN tokens (h rows of the block).
 
 __global__ __launch_bounds__(kBigThreads) void ffn2_big_kernel(
     const bf16_t* __restrict__ h, const bf16_t* __restrict__ w2,
     const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded,
-    float* __restrict__ y, int d, int I, int A, int gx, int gy) {
-  __shared__ __attribute__((aligned(1024))) uint8_t buf0[kBigStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t buf1[kBigStageBytes];
+    float* __restrict__ y_part, int d, int I, int A, int ksplit, int gx, int gy) {
+  BIG_BUFFERS(buf);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15;
   const int g = lane >> 4;
   const BigTile tl = big_tile_of(blockIdx.x, gx, gy);
-  if (!tl.live || tl.b * kBigTokens >= *num_padded) return;
-  const int b = tl.b;
+  if (!tl.live) return;
+  const int b = tl.b / kBigHalves;
+  const int n_off = (tl.b % kBigHalves) * kBigN;
+  if (b * kBigTokens >= *num_padded) return;
+  const int32_t* blk = sorted_ids + static_cast<size_t>(b) * kBigTokens;
+  if (blk[n_off] >= A) return;
   const int e = block_expert[b];
   const int n0 = tl.y * kBigRows;
-  const int32_t* blk = sorted_ids + static_cast<size_t>(b) * kBigTokens;
+  // split z of K = I (grid z): the combine adds the splits in a fixed order
+  const int k_begin = blockIdx.z * ksplit;
+  const int nst = (min(I, k_begin + ksplit) - k_begin) / kBigK;
+  float* y = y_part + static_cast<size_t>(blockIdx.z) * A * d;
 
   BigLoader ld;
   const int lrow = lane / kBigSlots;
   const int c_even = ((lane % kBigSlots) ^ big_swz(lrow)) * 8;
   const int c_odd = ((lane % kBigSlots) ^ big_swz(kBigRowsPerGroup + lrow)) * 8;
   const int row0 = 64 * wave + lrow;
-  ld.a_even = w2 + (static_cast<size_t>(e) * d + n0 + row0) * I + c_even;
-  ld.a_odd = w2 + (static_cast<size_t>(e) * d + n0 + row0 + kBigRowsPerGroup) * I + c_odd;
+  ld.a_even = w2 + (static_cast<size_t>(e) * d + n0 + row0) * I + k_begin + c_even;
+  ld.a_odd = w2 + (static_cast<size_t>(e) * d + n0 + row0 + kBigRowsPerGroup) * I + k_begin + c_odd;
   ld.a_step = static_cast<size_t>(2 * kBigRowsPerGroup) * I;
-  // h rows of the block; pad slots hold no token and their columns are never stored
-  const bf16_t* bsrc[kBigGroups];
-  const bf16_t* hb = h + (static_cast<size_t>(b) * kBigTokens + row0) * I;
+  // h rows of the tile; pad slots hold no token and their columns are never stored
+  const int brow = (kBigN / 4) * wave + lrow;
+  const bf16_t* bsrc[kBigGroupsB];
+  const bf16_t* hb = h + (static_cast<size_t>(b) * kBigTokens + n_off + brow) * I + k_begin;
 #pragma unroll
-  for (int q = 0; q < kBigGroups; ++q)
+  for (int q = 0; q < kBigGroupsB; ++q)
     bsrc[q] = hb + static_cast<size_t>(kBigRowsPerGroup * q) * I + (q & 1 ? c_odd : c_even);
   const int wm = wave & 1, wn = wave >> 1;
-  f32x4 acc[8][8];
+  f32x4 acc[8][kBigNB];
 #pragma unroll
   for (int t = 0; t < 8; ++t)
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < kBigNB; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // A rows 128*wm .. +127: eight consecutive 16-row tiles
-  big_mainloop(ld, bsrc, buf0, buf1, I / kBigK, wave, 128 * wm, 128 * wm + 64, 128 * wn, acc);
+  BigRing{ld, bsrc, buf, wave, 128 * wm, 128 * wm + 64, (kBigN / 2) * wn}.run(nst, acc);
 
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int f = blk[128 * wn + 16 * u + r16];
+  for (int u = 0; u < kBigNB; ++u) {
+    const int f = blk[n_off + (kBigN / 2) * wn + 16 * u + r16];
     if (f < A) {
       const float gate = topk_w[f];
       float* yrow = y + static_cast<size_t>(f) * d + n0 + 128 * wm + 4 * g;
@@ -339,7 +456,7 @@ static int big_grid(int gx, int gy) {
 hipError_t launch_ffn13_big(const FfnArgs& a, hipStream_t s) {
   if (a.B != kBigTokens || a.w_dtype != kDtypeBF16 || !big_gemm_fits(a.d, a.I))
     return hipErrorInvalidValue;
-  const int gx = a.cap / kBigTokens, gy = a.I / 128;
+  const int gx = a.cap / kBigTokens * kBigHalves, gy = a.I / 128;
   ffn13_big_kernel<<<big_grid(gx, gy), kBigThreads, 0, s>>>(
       static_cast<const bf16_t*>(a.x), static_cast<const bf16_t*>(a.w13), a.sorted_ids,
       a.block_expert, a.num_padded, static_cast<bf16_t*>(a.h), a.d, a.I, a.k, a.A, gx, gy);
@@ -347,13 +464,18 @@ hipError_t launch_ffn13_big(const FfnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_ffn2_big(const FfnArgs& a, hipStream_t s) {
-  if (a.B != kBigTokens || a.w_dtype != kDtypeBF16 || !big_gemm_fits(a.d, a.I) || a.splits != 1)
+  // every split an even number (>= 2) of 64-wide K stages
+  if (a.B != kBigTokens || a.w_dtype != kDtypeBF16 || !big_gemm_fits(a.d, a.I) ||
+      a.ksplit % (2 * kBigK) != 0 || a.splits < 1 ||
+      static_cast<int64_t>(a.splits - 1) * a.ksplit >= a.I)
     return hipErrorInvalidValue;
-  const int gx = a.cap / kBigTokens, gy = a.d / kBigRows;
-  ffn2_big_kernel<<<big_grid(gx, gy), kBigThreads, 0, s>>>(
+  const int gx = a.cap / kBigTokens * kBigHalves, gy = a.d / kBigRows;
+  ffn2_big_kernel<<<dim3(big_grid(gx, gy), 1, a.splits), kBigThreads, 0, s>>>(
       static_cast<const bf16_t*>(a.h), static_cast<const bf16_t*>(a.w2), a.topk_w, a.sorted_ids,
-      a.block_expert, a.num_padded, a.y_part, a.d, a.I, a.A, gx, gy);
+      a.block_expert, a.num_padded, a.y_part, a.d, a.I, a.A, a.ksplit, gx, gy);
   return hipGetLastError();
 }
+
+int big_w2_kchunk() { return 2 * kBigK; }
 
 }  // namespace moe

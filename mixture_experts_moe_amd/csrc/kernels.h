@@ -63,6 +63,7 @@ hipError_t launch_ffn2_gemm(const FfnArgs& a, hipStream_t s);
 bool big_gemm_fits(int d, int I);
 hipError_t launch_ffn13_big(const FfnArgs& a, hipStream_t s);
 hipError_t launch_ffn2_big(const FfnArgs& a, hipStream_t s);
+int big_w2_kchunk();  // a split of the big W2's K range is a multiple of this
 
 // Row blocks that hold at least one slot: the realised blocks are at most
 // the capacity's, and at most one partial block per used expert plus the

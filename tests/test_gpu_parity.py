@@ -131,6 +131,8 @@ SMALL = [
     ("bf16_big", dict(workload="decode_bf16", d=512, I=384, E=4, x_std=1.0), 700, 256),
     ("bf16_big", dict(workload="decode_bf16", d=256, I=128, E=8, k=2, x_std=1.0), 1500, 0),
     ("bf16_big", dict(workload="decode_bf16", d=768, I=256, E=3, k=1, x_std=1.0), 300, 256),
+    # few channel tiles: the big-tile W2 splits K in two (1152 + 1152)
+    ("bf16_big", dict(workload="decode_bf16", d=256, I=2304, E=4, k=2, x_std=1.0), 600, 256),
     ("bf16_kE", dict(workload="decode_bf16", d=128, I=128, E=8, k=8, x_std=1.0), 40, 0),
     ("bf16_E1", dict(workload="decode_bf16", d=256, I=128, E=1, k=1, x_std=1.0), 37, 0),
     ("fp8_channel", dict(workload="fp8", d=256, I=192, E=16, k=4), 3, 0),
