@@ -112,6 +112,19 @@ int default_block_m(const moe_desc* d, int top_k) {
   return 128;
 }
 
+// W2 K split for blocks of <= 64 tokens: double the splits while the grid
+// has fewer waves than this, each split keeps at least this many K chunks,
+// and there are fewer splits than the maximum.
+#ifndef MOE_W2_SPLIT_WAVES
+#define MOE_W2_SPLIT_WAVES 2048
+#endif
+#ifndef MOE_W2_MIN_CHUNKS
+#define MOE_W2_MIN_CHUNKS 4
+#endif
+#ifndef MOE_W2_MAX_SPLITS
+#define MOE_W2_MAX_SPLITS 8
+#endif
+
 int64_t capacity(int64_t A, int64_t E, int64_t B) {
   const int64_t n = A + (E < A ? E : A) * (B - 1);
   return (n + B - 1) / B * B;
@@ -154,7 +167,9 @@ void make_plan(const moe_desc* d, int top_k, bool with_routing, Plan* p) {
     // path) output channels
     const int64_t waves = blocks_est * (p->d / (lds ? moe::dma_w2_channels(p->wdt) : 32));
     int s = 1;
-    while (s < 8 && waves * s < 2048 && p->I / (2 * s) >= 4 * kc) s *= 2;
+    while (s < MOE_W2_MAX_SPLITS && waves * s < MOE_W2_SPLIT_WAVES &&
+           p->I / (2 * s) >= MOE_W2_MIN_CHUNKS * kc)
+      s *= 2;
     const int per = (p->I + s - 1) / s;
     p->ksplit = (per + kc - 1) / kc * kc;
     p->splits = (p->I + p->ksplit - 1) / p->ksplit;

@@ -11,8 +11,11 @@
 // When an expert holds hundreds of tokens the product is a dense contraction
 // and the limit is how many bytes each MFMA needs.  A workgroup computes a
 // 256 x 256 tile (256 weight rows x 256 tokens, so every operand byte staged
-// in LDS feeds 256 MACs), four waves of 128 x 128 each on
-// v_mfma_f32_16x16x32_bf16.  Both operands move HBM/L2 -> LDS with gfx950's
+// in LDS feeds 256 MACs) on v_mfma_f32_16x16x32_bf16, eight waves of
+// 128 x 64 each: two waves per SIMD, so that one wave's MFMAs run while the
+// other waits on its LDS reads or the stage barrier (a single wave per SIMD
+// issuing this MFMA back to back keeps the matrix core only about half
+// busy).  Both operands move HBM/L2 -> LDS with gfx950's
 // direct-to-LDS 16-byte loads (no VGPR staging), in K stages of 64 elements
 // through two LDS buffers, so the loads of the next stage are in flight while
 // the MFMAs of the current one run; one barrier per stage.  An LDS row holds one stage of one operand row in 16-byte slots,
@@ -29,7 +32,13 @@
 namespace moe {
 
 // Stage shape: 2 buffers x 2 operands x 256 rows x 64 K x 2 bytes = 128 KB LDS.
-constexpr int kBigThreads = 256;
+#ifndef MOE_BIG_WAVES
+#define MOE_BIG_WAVES 8
+#endif
+constexpr int kBigWaves = MOE_BIG_WAVES;  // 4: 128 x 128 per wave; 8: 128 x 64, two per SIMD
+static_assert(kBigWaves == 4 || kBigWaves == 8, "waves per tile");
+constexpr int kBigWn = kBigWaves / 2;     // waves along the tokens (two along the rows)
+constexpr int kBigThreads = 64 * kBigWaves;
 constexpr int kBigTokens = 256;  // block size B of this path
 constexpr int kBigRows = 256;    // weight rows per tile
 constexpr int kBigK = 64;        // K elements per stage
@@ -38,12 +47,12 @@ constexpr int kBigK = 64;        // K elements per stage
 #endif
 constexpr int kBigN = MOE_BIG_N;  // tokens per workgroup tile: all 256 of the block, or half
 constexpr int kBigHalves = kBigTokens / kBigN;
-constexpr int kBigNB = kBigN / 32;  // 16-token fragments per wave (two waves share N)
+constexpr int kBigNB = kBigN / (16 * kBigWn);  // 16-token fragments per wave
 constexpr int kBigSlots = kBigK / 8;                 // 16-byte slots per LDS row
 constexpr int kBigRowBytes = kBigK * 2;
 constexpr int kBigRowsPerGroup = 1024 / kBigRowBytes;  // rows filled by one 1 KB load
-constexpr int kBigGroups = kBigRows / kBigRowsPerGroup / 4;  // A loads per wave and stage
-constexpr int kBigGroupsB = kBigN / kBigRowsPerGroup / 4;   // B loads per wave and stage
+constexpr int kBigGroups = kBigRows / kBigRowsPerGroup / kBigWaves;  // A loads per wave and stage
+constexpr int kBigGroupsB = kBigN / kBigRowsPerGroup / kBigWaves;   // B loads per wave and stage
 constexpr int kBigLoads = kBigGroups + kBigGroupsB;
 constexpr int kBigOperandBytes = kBigRows * kBigRowBytes;
 constexpr int kBigStageBytes = kBigOperandBytes + kBigN * kBigRowBytes;
@@ -195,13 +204,22 @@ __device__ __forceinline__ void big_half(const BigLoader& ld,
   __builtin_amdgcn_sched_barrier(0);
   if (kIssue) big_issue(ld, bsrc, nxt, knext, wave);
 #endif
+  if constexpr (kBigWaves == 8) {
+    // two waves per SIMD: the other wave covers the read latency, and one
+    // fragment set at a time keeps the wave within its 256 registers
+    big_mma(f0, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    big_load_frags(f1, cur, opb, arow0, arow_up, brow0, 1);
+    return;
+  }
   __builtin_amdgcn_sched_barrier(0);
   big_load_frags(f1, cur, opb, arow0, arow_up, brow0, 1);
   big_mma(f0, acc);
+  constexpr int kReads = 8 + kBigNB, kMfmas = 8 * kBigNB;
 #pragma unroll
-  for (int i = 0; i < 8 + kBigNB; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // four MFMAs
+  for (int i = 0; i < kReads; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                             // one LDS read
+    __builtin_amdgcn_sched_group_barrier(0x008, (kMfmas + kReads - 1) / kReads, 0);  // MFMAs
   }
 }
 
@@ -336,12 +354,12 @@ __global__ __launch_bounds__(kBigThreads) void ffn13_big_kernel(
   const int lrow = lane / kBigSlots;  // row within a 1 KB group
   const int c_even = ((lane % kBigSlots) ^ big_swz(lrow)) * 8;
   const int c_odd = ((lane % kBigSlots) ^ big_swz(kBigRowsPerGroup + lrow)) * 8;
-  const int row0 = 64 * wave + lrow;  // tile row of group 0
-  const size_t wrow0 = static_cast<size_t>(e) * two_i + (wave < 2 ? n0 + row0 : I + n0 + row0 - 128);
+  const int row0 = (kBigRows / kBigWaves) * wave + lrow;  // tile row of group 0
+  const size_t wrow0 = static_cast<size_t>(e) * two_i + (row0 < 128 ? n0 + row0 : I + n0 + row0 - 128);
   ld.a_even = w13 + wrow0 * d + c_even;
   ld.a_odd = w13 + (wrow0 + kBigRowsPerGroup) * d + c_odd;
   ld.a_step = static_cast<size_t>(2 * kBigRowsPerGroup) * d;
-  const int brow = (kBigN / 4) * wave + lrow;  // token row of B group 0
+  const int brow = (kBigN / kBigWaves) * wave + lrow;  // token row of B group 0
   const bf16_t* bsrc[kBigGroupsB];
 #pragma unroll
   for (int q = 0; q < kBigGroupsB; ++q) {
@@ -355,12 +373,12 @@ __global__ __launch_bounds__(kBigThreads) void ffn13_big_kernel(
 #pragma unroll
     for (int u = 0; u < kBigNB; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  BigRing{ld, bsrc, buf, wave, 64 * wm, 128 + 64 * wm, (kBigN / 2) * wn}.run(d / kBigK, acc);
+  BigRing{ld, bsrc, buf, wave, 64 * wm, 128 + 64 * wm, (kBigN / kBigWn) * wn}.run(d / kBigK, acc);
 
   // lane: token column r16 of tile u, channels n0 + 64wm + 16t + 4g .. +3
 #pragma unroll
   for (int u = 0; u < kBigNB; ++u) {
-    const size_t row = static_cast<size_t>(b) * kBigTokens + n_off + (kBigN / 2) * wn + 16 * u + r16;
+    const size_t row = static_cast<size_t>(b) * kBigTokens + n_off + (kBigN / kBigWn) * wn + 16 * u + r16;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       uint32_t packed[2];
@@ -408,12 +426,12 @@ __global__ __launch_bounds__(kBigThreads) void ffn2_big_kernel(
   const int lrow = lane / kBigSlots;
   const int c_even = ((lane % kBigSlots) ^ big_swz(lrow)) * 8;
   const int c_odd = ((lane % kBigSlots) ^ big_swz(kBigRowsPerGroup + lrow)) * 8;
-  const int row0 = 64 * wave + lrow;
+  const int row0 = (kBigRows / kBigWaves) * wave + lrow;
   ld.a_even = w2 + (static_cast<size_t>(e) * d + n0 + row0) * I + k_begin + c_even;
   ld.a_odd = w2 + (static_cast<size_t>(e) * d + n0 + row0 + kBigRowsPerGroup) * I + k_begin + c_odd;
   ld.a_step = static_cast<size_t>(2 * kBigRowsPerGroup) * I;
   // h rows of the tile; pad slots hold no token and their columns are never stored
-  const int brow = (kBigN / 4) * wave + lrow;
+  const int brow = (kBigN / kBigWaves) * wave + lrow;
   const bf16_t* bsrc[kBigGroupsB];
   const bf16_t* hb = h + (static_cast<size_t>(b) * kBigTokens + n_off + brow) * I + k_begin;
 #pragma unroll
@@ -427,11 +445,11 @@ __global__ __launch_bounds__(kBigThreads) void ffn2_big_kernel(
     for (int u = 0; u < kBigNB; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // A rows 128*wm .. +127: eight consecutive 16-row tiles
-  BigRing{ld, bsrc, buf, wave, 128 * wm, 128 * wm + 64, (kBigN / 2) * wn}.run(nst, acc);
+  BigRing{ld, bsrc, buf, wave, 128 * wm, 128 * wm + 64, (kBigN / kBigWn) * wn}.run(nst, acc);
 
 #pragma unroll
   for (int u = 0; u < kBigNB; ++u) {
-    const int f = blk[n_off + (kBigN / 2) * wn + 16 * u + r16];
+    const int f = blk[n_off + (kBigN / kBigWn) * wn + 16 * u + r16];
     if (f < A) {
       const float gate = topk_w[f];
       float* yrow = y + static_cast<size_t>(f) * d + n0 + 128 * wm + 4 * g;
