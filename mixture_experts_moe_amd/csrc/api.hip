@@ -43,7 +43,7 @@ int check_desc(const moe_desc* d, int top_k) {
   if (bm != 0 && bm != 16 && bm != 32 && bm != 64 && bm != 128 && bm != 256)
     return MOE_ERR_BAD_BLOCK_M;
   if (bm == 256 && !(d->weight_dtype == MOE_DTYPE_BF16 &&
-                     moe::big_gemm_fits(static_cast<int>(d->hidden), static_cast<int>(d->intermediate))))
+                     moe::big_gemm_fits(d->num_tokens, static_cast<int>(d->hidden), static_cast<int>(d->intermediate))))
     return MOE_ERR_BAD_BLOCK_M;  // the 256-token GEMM is bf16 with d % 256 == 0, I % 128 == 0
   return MOE_OK;
 }
@@ -107,7 +107,7 @@ int default_block_m(const moe_desc* d, int top_k) {
   }
   const int64_t per_expert = T * top_k / d->num_experts;
   if (per_expert >= 256 && d->weight_dtype == MOE_DTYPE_BF16 &&
-      moe::big_gemm_fits(static_cast<int>(d->hidden), static_cast<int>(d->intermediate)))
+      moe::big_gemm_fits(d->num_tokens, static_cast<int>(d->hidden), static_cast<int>(d->intermediate)))
     return 256;
   return 128;
 }
@@ -304,7 +304,7 @@ MOE_API const char* moe_strerror(int status) {
     case MOE_ERR_MISALIGNED: return "a pointer is not 16-byte aligned (workspace: 256-byte)";
     case MOE_ERR_WORKSPACE: return "workspace is NULL or smaller than moe_workspace_bytes()";
     case MOE_ERR_HIP: return "a HIP call or kernel launch failed";
-    case MOE_ERR_BAD_BLOCK_M: return "block_m must be 0, 16, 32, 64, 128 or 256 (256: bf16 weights, d % 256 == 0, I % 128 == 0)";
+    case MOE_ERR_BAD_BLOCK_M: return "block_m must be 0, 16, 32, 64, 128 or 256 (256: bf16 weights, d % 256 == 0, I % 128 == 0, 4*I*d and 2*T*d under 2^31)";
     case MOE_ERR_BAD_ARG: return "invalid argument (reserved fields must be 0)";
   }
   return "unknown status";

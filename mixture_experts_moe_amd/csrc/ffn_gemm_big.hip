@@ -15,12 +15,14 @@
 // 128 x 64 each: two waves per SIMD, so that one wave's MFMAs run while the
 // other waits on its LDS reads or the stage barrier (a single wave per SIMD
 // issuing this MFMA back to back keeps the matrix core only about half
-// busy).  Both operands move HBM/L2 -> LDS with gfx950's
-// direct-to-LDS 16-byte loads (no VGPR staging), in K stages of 64 elements
-// through two LDS buffers, so the loads of the next stage are in flight while
-// the MFMAs of the current one run; one barrier per stage.  An LDS row holds one stage of one operand row in 16-byte slots,
-// XOR-swizzled by row so that the 16 rows read by one 16-lane group for the
-// same k fall in 16 different bank groups.
+// busy).  Both operands move HBM/L2 -> LDS with gfx950's direct-to-LDS
+// 16-byte buffer loads (no VGPR staging), in K stages of 64 elements through
+// two LDS buffers, so the loads of the next stage are in flight while the
+// MFMAs of the current one run; one barrier per stage.  An LDS row holds one
+// stage of one operand row in 16-byte slots, XOR-swizzled by row so that the
+// 16 rows read by one 16-lane group for the same k fall in 16 different bank
+// groups.  The waves of a tile whose 64 token rows are all padding (the tail
+// block of an expert) only load and meet the barriers.
 //
 // W13: the tile's rows are 128 gate rows then the 128 matching up rows, so
 // each wave holds gate and up of the same 64 channels and the epilogue writes
@@ -32,11 +34,7 @@
 namespace moe {
 
 // Stage shape: 2 buffers x 2 operands x 256 rows x 64 K x 2 bytes = 128 KB LDS.
-#ifndef MOE_BIG_WAVES
-#define MOE_BIG_WAVES 8
-#endif
-constexpr int kBigWaves = MOE_BIG_WAVES;  // 4: 128 x 128 per wave; 8: 128 x 64, two per SIMD
-static_assert(kBigWaves == 4 || kBigWaves == 8, "waves per tile");
+constexpr int kBigWaves = 8;              // 128 x 64 per wave, two waves per SIMD
 constexpr int kBigWn = kBigWaves / 2;     // waves along the tokens (two along the rows)
 constexpr int kBigThreads = 64 * kBigWaves;
 constexpr int kBigTokens = 256;  // block size B of this path
@@ -47,7 +45,8 @@ constexpr int kBigK = 64;        // K elements per stage
 #endif
 constexpr int kBigN = MOE_BIG_N;  // tokens per workgroup tile: all 256 of the block, or half
 constexpr int kBigHalves = kBigTokens / kBigN;
-constexpr int kBigNB = kBigN / (16 * kBigWn);  // 16-token fragments per wave
+constexpr int kBigTA = 8;                      // 16-row weight tiles per wave (128 rows)
+constexpr int kBigNB = kBigN / (16 * kBigWn);  // 16-token tiles per wave
 constexpr int kBigSlots = kBigK / 8;                 // 16-byte slots per LDS row
 constexpr int kBigRowBytes = kBigK * 2;
 constexpr int kBigRowsPerGroup = 1024 / kBigRowBytes;  // rows filled by one 1 KB load
@@ -109,27 +108,43 @@ __device__ __forceinline__ BigTile big_tile_of(int p, int gx, int gy) {
 // stride; token sources (gathered x rows, or h rows) are one pointer per
 // group.
 struct BigLoader {
-  const bf16_t* a_even;  // A source of group 0 (q even), at k = 0
-  const bf16_t* a_odd;   // A source of group 1 (q odd)
-  size_t a_step;         // elements between groups q and q + 2
+  __amdgpu_buffer_rsrc_t ra;  // weight rows of the tile's expert
+  __amdgpu_buffer_rsrc_t rb;  // token rows (x, or the block's h rows)
+  uint32_t a_even;            // byte offset of this lane's group-0 source (q even), k = 0
+  uint32_t a_odd;             // group 1 (q odd)
+  uint32_t a_step;            // bytes between groups q and q + 2
+  uint32_t b[kBigGroupsB];    // byte offset of this lane's token source of group q, k = 0
 
-  __device__ __forceinline__ const bf16_t* a_src(int q, int k0) const {
-    return (q & 1 ? a_odd : a_even) + (q >> 1) * a_step + k0;
+  __device__ __forceinline__ uint32_t a_off(int q, int k0) const {
+    return (q & 1 ? a_odd : a_even) + (q >> 1) * a_step + 2 * k0;
   }
 };
 
-__device__ __forceinline__ void big_issue(const BigLoader& ld,
-                                          const bf16_t* const (&bsrc)[kBigGroupsB],
-                                          uint8_t* stage, int k0, int wave) {
+// Buffer resource over `bytes` bytes at `base` (raw: stride 0, byte
+// offsets; flags word as gfx9-family kernels use for plain dword data).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t big_rsrc(const void* base, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           0x00020000);
+}
+
+// The stage's direct-to-LDS loads go through buffer resources
+// (buffer_load ... lds) rather than global_load_lds: with the latter in
+// flight the compiler waits for every outstanding LDS read (lgkmcnt(0)) before
+// each MFMA group, which undoes the fragment pipelining; the buffer form
+// keeps those waits partial.
+__device__ __forceinline__ void big_issue(const BigLoader& ld, uint8_t* stage, int k0, int wave) {
 #pragma unroll
   for (int q = 0; q < kBigGroups; ++q)
-    __builtin_amdgcn_global_load_lds(ld.a_src(q, k0), stage + (wave * kBigGroups + q) * 1024, 16,
-                                     0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        ld.ra, (__attribute__((address_space(3))) void*)(stage + (wave * kBigGroups + q) * 1024), 16,
+        ld.a_off(q, k0), 0, 0, 0);
 #pragma unroll
   for (int q = 0; q < kBigGroupsB; ++q)
-    __builtin_amdgcn_global_load_lds(bsrc[q] + k0,
-                                     stage + kBigOperandBytes + (wave * kBigGroupsB + q) * 1024, 16,
-                                     0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        ld.rb,
+        (__attribute__((address_space(3))) void*)(stage + kBigOperandBytes +
+                                                   (wave * kBigGroupsB + q) * 1024),
+        16, ld.b[q] + 2 * k0, 0, 0, 0);
 }
 
 // s_waitcnt immediate that waits until at most n vector-memory loads are
@@ -142,27 +157,32 @@ __device__ __forceinline__ bf16x8 big_frag(const uint8_t* op, int row, int slot)
                                                  ((slot ^ big_swz(row)) << 4)));
 }
 
+typedef f32x4 BigAcc[kBigTA][kBigNB];
+
+// Fragments of 32 consecutive K of a stage (half h of it).
 struct BigFrags {
-  bf16x8 a[8], b[kBigNB];
+  bf16x8 a[kBigTA], b[kBigNB];
 };
 
-// Fragments of k-step j (k = 32j .. 32j+31 of the stage) for this wave's
-// 8 row tiles (rows arow0 + 16t) and kBigNB token tiles (rows brow0 + 16u).
+// Fragments of half stage h (k = 32h .. 32h+31) for this wave's row tiles
+// (rows arow0 + 16t for t < 4, arow_up + 16(t-4) after) and token tiles
+// (rows brow0 + 16u); lane group l/16 holds k = 32h + 8(l/16) .. +8, logical
+// slot 4h + l/16.
 __device__ __forceinline__ void big_load_frags(BigFrags& f, const uint8_t* opa, const uint8_t* opb,
-                                               int arow0, int arow_up, int brow0, int j) {
+                                               int arow0, int arow_up, int brow0, int h) {
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15;
-  const int slot = 4 * j + (lane >> 4);  // lane group g: k = 32j + 8g .. +8
+  const int slot = 4 * h + (lane >> 4);
 #pragma unroll
-  for (int t = 0; t < 8; ++t)
+  for (int t = 0; t < kBigTA; ++t)
     f.a[t] = big_frag(opa, (t < 4 ? arow0 + 16 * t : arow_up + 16 * (t - 4)) + r16, slot);
 #pragma unroll
   for (int u = 0; u < kBigNB; ++u) f.b[u] = big_frag(opb, brow0 + 16 * u + r16, slot);
 }
 
-__device__ __forceinline__ void big_mma(const BigFrags& f, f32x4 (&acc)[8][kBigNB]) {
+__device__ __forceinline__ void big_mma(const BigFrags& f, BigAcc& acc) {
 #pragma unroll
-  for (int t = 0; t < 8; ++t)
+  for (int t = 0; t < kBigTA; ++t)
 #pragma unroll
     for (int u = 0; u < kBigNB; ++u) acc[t][u] = mfma16x16x32(f.a[t], f.b[u], acc[t][u]);
 }
@@ -181,46 +201,36 @@ __device__ __forceinline__ void big_barrier() {
 // landed (kWait of its later loads may stay outstanding), meet the other
 // waves (after which nobody reads `nxt`, the buffer read one or two stages
 // ago, any more), issue the stage after the in-flight ones into `nxt` (when
-// kIssue), read the first k-step's fragments and then the second k-step's
-// (f1) under the first k-step's MFMAs.  The caller runs f1's MFMAs; the
-// compiler may spread them over the next stage's wait, barrier and first
-// reads since they only touch registers.
-template <bool kIssue, int kWait>
-__device__ __forceinline__ void big_half(const BigLoader& ld,
-                                         const bf16_t* const (&bsrc)[kBigGroupsB],
-                                         const uint8_t* cur, uint8_t* nxt, int knext, int wave,
-                                         int arow0, int arow_up, int brow0, BigFrags& f1,
-                                         f32x4 (&acc)[8][kBigNB]) {
+// kIssue), read the first half stage's fragments, run their MFMAs, and read
+// the second half's (f1), whose MFMAs the caller runs.  With two waves per
+// SIMD the other wave covers each wave's read latency, and one fragment set
+// at a time keeps a wave within its 256 registers.  A wave whose token rows
+// are all padding (kLive false) only loads and meets the barriers.
+template <bool kIssue, int kWait, bool kLive>
+__device__ __forceinline__ void big_half(const BigLoader& ld, const uint8_t* cur, uint8_t* nxt,
+                                         int knext, int wave, int arow0, int arow_up, int brow0,
+                                         BigFrags& f1, BigAcc& acc) {
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(kWait));
   big_barrier();
   const uint8_t* opb = cur + kBigOperandBytes;
   BigFrags f0;
 #if MOE_BIG_ISSUE_FIRST
-  if (kIssue) big_issue(ld, bsrc, nxt, knext, wave);
+  if (kIssue) big_issue(ld, nxt, knext, wave);
+  if (!kLive) return;
   __builtin_amdgcn_sched_barrier(0);
   big_load_frags(f0, cur, opb, arow0, arow_up, brow0, 0);
 #else
-  big_load_frags(f0, cur, opb, arow0, arow_up, brow0, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  if (kIssue) big_issue(ld, bsrc, nxt, knext, wave);
-#endif
-  if constexpr (kBigWaves == 8) {
-    // two waves per SIMD: the other wave covers the read latency, and one
-    // fragment set at a time keeps the wave within its 256 registers
-    big_mma(f0, acc);
-    __builtin_amdgcn_sched_barrier(0);
-    big_load_frags(f1, cur, opb, arow0, arow_up, brow0, 1);
+  if (!kLive) {
+    if (kIssue) big_issue(ld, nxt, knext, wave);
     return;
   }
+  big_load_frags(f0, cur, opb, arow0, arow_up, brow0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  if (kIssue) big_issue(ld, nxt, knext, wave);
+#endif
+  big_mma(f0, acc);
   __builtin_amdgcn_sched_barrier(0);
   big_load_frags(f1, cur, opb, arow0, arow_up, brow0, 1);
-  big_mma(f0, acc);
-  constexpr int kReads = 8 + kBigNB, kMfmas = 8 * kBigNB;
-#pragma unroll
-  for (int i = 0; i < kReads; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                             // one LDS read
-    __builtin_amdgcn_sched_group_barrier(0x008, (kMfmas + kReads - 1) / kReads, 0);  // MFMAs
-  }
 }
 
 // acc[t][u] += A_rows(t) . B_rows(u)^T over K.  A rows: arow0 + 16t (t < 4)
@@ -232,31 +242,40 @@ __device__ __forceinline__ void big_half(const BigLoader& ld,
 // MFMAs can overlap the next stage's start.
 struct BigRing {
   const BigLoader& ld;
-  const bf16_t* const (&bsrc)[kBigGroupsB];
   uint8_t* const (&buf)[3];
   int wave, arow0, arow_up, brow0;
+  bool live;  // the wave's token rows hold at least one real slot (wave-uniform)
 
-  template <int b, bool kIssue, int kWait>
-  __device__ __forceinline__ void step(int s, BigFrags& f1, f32x4 (&acc)[8][kBigNB]) const {
+  // a wave whose token rows are all padding (kLive false) only loads and
+  // meets the barriers; the choice is made once, outside the loops, so that
+  // each loop body is branch-free
+  template <bool kLive>
+  __device__ __forceinline__ void mma1(const BigFrags& f1, BigAcc& acc) const {
+    if constexpr (kLive) big_mma(f1, acc);
+  }
+
+  template <int b, bool kIssue, int kWait, bool kLive>
+  __device__ __forceinline__ void step(int s, BigFrags& f1, BigAcc& acc) const {
     constexpr int S = kBigStages;
-    big_half<kIssue, kWait>(ld, bsrc, buf[b], buf[(b + S - 1) % S], (s + S - 1) * kBigK, wave,
-                            arow0, arow_up, brow0, f1, acc);
+    big_half<kIssue, kWait, kLive>(ld, buf[b], buf[(b + S - 1) % S], (s + S - 1) * kBigK, wave,
+                                   arow0, arow_up, brow0, f1, acc);
   }
 
   // two stages (nst even: the launchers require d % 256 == 0, I % 128 == 0)
-  __device__ __forceinline__ void run2(int nst, f32x4 (&acc)[8][kBigNB]) const {
+  template <bool kLive>
+  __device__ __forceinline__ void run2(int nst, BigAcc& acc) const {
     BigFrags f1;
-    big_issue(ld, bsrc, buf[0], 0, wave);
-    step<0, true, 0>(0, f1, acc);
+    big_issue(ld, buf[0], 0, wave);
+    step<0, true, 0, kLive>(0, f1, acc);
     for (int s = 1; s + 1 < nst; s += 2) {
-      big_mma(f1, acc);
-      step<1, true, 0>(s, f1, acc);
-      big_mma(f1, acc);
-      step<0, true, 0>(s + 1, f1, acc);
+      mma1<kLive>(f1, acc);
+      step<1, true, 0, kLive>(s, f1, acc);
+      mma1<kLive>(f1, acc);
+      step<0, true, 0, kLive>(s + 1, f1, acc);
     }
-    big_mma(f1, acc);
-    step<1, false, 0>(nst - 1, f1, acc);
-    big_mma(f1, acc);
+    mma1<kLive>(f1, acc);
+    step<1, false, 0, kLive>(nst - 1, f1, acc);
+    mma1<kLive>(f1, acc);
   }
 
   // three stages: loads run two stages ahead; a step waits until only the
@@ -264,57 +283,65 @@ struct BigRing {
   // loop goes three stages at a time; the issuing steps left over and the
   // last two stages (which issue nothing) start from a switch on their
   // buffer.  nst >= 2.
-  template <int b>
-  __device__ __forceinline__ void tail3(BigFrags& f1, f32x4 (&acc)[8][kBigNB], int s) const {
-    big_mma(f1, acc);
-    step<b, false, kBigLoads>(s, f1, acc);
-    big_mma(f1, acc);
-    step<(b + 1) % 3, false, 0>(s + 1, f1, acc);
+  template <int b, bool kLive>
+  __device__ __forceinline__ void tail3(BigFrags& f1, BigAcc& acc, int s) const {
+    mma1<kLive>(f1, acc);
+    step<b, false, kBigLoads, kLive>(s, f1, acc);
+    mma1<kLive>(f1, acc);
+    step<(b + 1) % 3, false, 0, kLive>(s + 1, f1, acc);
   }
-  __device__ __forceinline__ void run3(int nst, f32x4 (&acc)[8][kBigNB]) const {
+  template <bool kLive>
+  __device__ __forceinline__ void run3(int nst, BigAcc& acc) const {
     constexpr int L = kBigLoads;
     BigFrags f1;
-    big_issue(ld, bsrc, buf[0], 0, wave);
-    big_issue(ld, bsrc, buf[1], kBigK, wave);
+    big_issue(ld, buf[0], 0, wave);
+    big_issue(ld, buf[1], kBigK, wave);
     const int M = nst - 2;  // stages that issue a later one
     if (M >= 1) {
-      step<0, true, L>(0, f1, acc);
+      step<0, true, L, kLive>(0, f1, acc);
       int s = 1;
       for (; s + 3 <= M; s += 3) {
-        big_mma(f1, acc);
-        step<1, true, L>(s, f1, acc);
-        big_mma(f1, acc);
-        step<2, true, L>(s + 1, f1, acc);
-        big_mma(f1, acc);
-        step<0, true, L>(s + 2, f1, acc);
+        mma1<kLive>(f1, acc);
+        step<1, true, L, kLive>(s, f1, acc);
+        mma1<kLive>(f1, acc);
+        step<2, true, L, kLive>(s + 1, f1, acc);
+        mma1<kLive>(f1, acc);
+        step<0, true, L, kLive>(s + 2, f1, acc);
       }
       const int r = M - s;  // 0, 1 or 2 issuing stages left; s == 1 (mod 3)
       if (r >= 1) {
-        big_mma(f1, acc);
-        step<1, true, L>(s, f1, acc);
+        mma1<kLive>(f1, acc);
+        step<1, true, L, kLive>(s, f1, acc);
       }
       if (r >= 2) {
-        big_mma(f1, acc);
-        step<2, true, L>(s + 1, f1, acc);
+        mma1<kLive>(f1, acc);
+        step<2, true, L, kLive>(s + 1, f1, acc);
       }
       switch (r) {
-        case 0: tail3<1>(f1, acc, s); break;
-        case 1: tail3<2>(f1, acc, s + 1); break;
-        default: tail3<0>(f1, acc, s + 2); break;
+        case 0: tail3<1, kLive>(f1, acc, s); break;
+        case 1: tail3<2, kLive>(f1, acc, s + 1); break;
+        default: tail3<0, kLive>(f1, acc, s + 2); break;
       }
     } else {
-      step<0, false, L>(0, f1, acc);
-      big_mma(f1, acc);
-      step<1, false, 0>(1, f1, acc);
+      step<0, false, L, kLive>(0, f1, acc);
+      mma1<kLive>(f1, acc);
+      step<1, false, 0, kLive>(1, f1, acc);
     }
-    big_mma(f1, acc);
+    mma1<kLive>(f1, acc);
   }
 
-  __device__ __forceinline__ void run(int nst, f32x4 (&acc)[8][kBigNB]) const {
+  template <bool kLive>
+  __device__ __forceinline__ void run_as(int nst, BigAcc& acc) const {
     if constexpr (kBigStages == 2)
-      run2(nst, acc);
+      run2<kLive>(nst, acc);
     else
-      run3(nst, acc);
+      run3<kLive>(nst, acc);
+  }
+  __device__ __forceinline__ void run(int nst, BigAcc& acc) const {
+    if (live)
+      run_as<true>(nst, acc);
+    else
+      run_as<false>(nst, acc);
   }
 };
 
@@ -336,8 +363,6 @@ __global__ __launch_bounds__(kBigThreads) void ffn13_big_kernel(
   BIG_BUFFERS(buf);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r16 = lane & 15;
-  const int g = lane >> 4;
   const BigTile tl = big_tile_of(blockIdx.x, gx, gy);
   if (!tl.live) return;  // uniform
   const int b = tl.b / kBigHalves;
@@ -355,30 +380,36 @@ __global__ __launch_bounds__(kBigThreads) void ffn13_big_kernel(
   const int c_even = ((lane % kBigSlots) ^ big_swz(lrow)) * 8;
   const int c_odd = ((lane % kBigSlots) ^ big_swz(kBigRowsPerGroup + lrow)) * 8;
   const int row0 = (kBigRows / kBigWaves) * wave + lrow;  // tile row of group 0
-  const size_t wrow0 = static_cast<size_t>(e) * two_i + (row0 < 128 ? n0 + row0 : I + n0 + row0 - 128);
-  ld.a_even = w13 + wrow0 * d + c_even;
-  ld.a_odd = w13 + (wrow0 + kBigRowsPerGroup) * d + c_odd;
-  ld.a_step = static_cast<size_t>(2 * kBigRowsPerGroup) * d;
+  const uint32_t wrow0 = row0 < 128 ? n0 + row0 : I + n0 + row0 - 128;  // row of expert e's W13
+  ld.ra = big_rsrc(w13 + static_cast<size_t>(e) * two_i * d, two_i * d * 2);
+  ld.rb = big_rsrc(x, static_cast<size_t>(A / k) * d * 2);
+  ld.a_even = 2 * (wrow0 * d + c_even);
+  ld.a_odd = 2 * ((wrow0 + kBigRowsPerGroup) * d + c_odd);
+  ld.a_step = 2 * (2 * kBigRowsPerGroup * d);
   const int brow = (kBigN / kBigWaves) * wave + lrow;  // token row of B group 0
-  const bf16_t* bsrc[kBigGroupsB];
 #pragma unroll
   for (int q = 0; q < kBigGroupsB; ++q) {
     const int f = blk[n_off + brow + kBigRowsPerGroup * q];  // pad slot: any valid row (never stored)
-    bsrc[q] = x + static_cast<size_t>(f < A ? f / k : 0) * d + (q & 1 ? c_odd : c_even);
+    ld.b[q] = 2 * (static_cast<uint32_t>(f < A ? f / k : 0) * d + (q & 1 ? c_odd : c_even));
   }
   const int wm = wave & 1, wn = wave >> 1;
-  f32x4 acc[8][kBigNB];
+  BigAcc acc;
 #pragma unroll
-  for (int t = 0; t < 8; ++t)
+  for (int t = 0; t < kBigTA; ++t)
 #pragma unroll
     for (int u = 0; u < kBigNB; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  BigRing{ld, bsrc, buf, wave, 64 * wm, 128 + 64 * wm, (kBigN / kBigWn) * wn}.run(d / kBigK, acc);
+  // real slots come first: the wave's token rows are all padding iff its first one is
+  const bool live = __builtin_amdgcn_readfirstlane(blk[n_off + (kBigN / kBigWn) * wn]) < A;
+  BigRing{ld, buf, wave, 64 * wm, 128 + 64 * wm, (kBigN / kBigWn) * wn, live}.run(d / kBigK, acc);
 
   // lane: token column r16 of tile u, channels n0 + 64wm + 16t + 4g .. +3
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
 #pragma unroll
   for (int u = 0; u < kBigNB; ++u) {
-    const size_t row = static_cast<size_t>(b) * kBigTokens + n_off + (kBigN / kBigWn) * wn + 16 * u + r16;
+    const size_t row =
+        static_cast<size_t>(b) * kBigTokens + n_off + (kBigN / kBigWn) * wn + 16 * u + r16;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       uint32_t packed[2];
@@ -406,8 +437,6 @@ __global__ __launch_bounds__(kBigThreads) void ffn2_big_kernel(
   BIG_BUFFERS(buf);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r16 = lane & 15;
-  const int g = lane >> 4;
   const BigTile tl = big_tile_of(blockIdx.x, gx, gy);
   if (!tl.live) return;
   const int b = tl.b / kBigHalves;
@@ -427,26 +456,31 @@ __global__ __launch_bounds__(kBigThreads) void ffn2_big_kernel(
   const int c_even = ((lane % kBigSlots) ^ big_swz(lrow)) * 8;
   const int c_odd = ((lane % kBigSlots) ^ big_swz(kBigRowsPerGroup + lrow)) * 8;
   const int row0 = (kBigRows / kBigWaves) * wave + lrow;
-  ld.a_even = w2 + (static_cast<size_t>(e) * d + n0 + row0) * I + k_begin + c_even;
-  ld.a_odd = w2 + (static_cast<size_t>(e) * d + n0 + row0 + kBigRowsPerGroup) * I + k_begin + c_odd;
-  ld.a_step = static_cast<size_t>(2 * kBigRowsPerGroup) * I;
+  ld.ra = big_rsrc(w2 + static_cast<size_t>(e) * d * I, static_cast<size_t>(d) * I * 2);
+  ld.a_even = 2 * (static_cast<uint32_t>(n0 + row0) * I + k_begin + c_even);
+  ld.a_odd = 2 * (static_cast<uint32_t>(n0 + row0 + kBigRowsPerGroup) * I + k_begin + c_odd);
+  ld.a_step = 2 * (2 * kBigRowsPerGroup * I);
   // h rows of the tile; pad slots hold no token and their columns are never stored
   const int brow = (kBigN / kBigWaves) * wave + lrow;
-  const bf16_t* bsrc[kBigGroupsB];
-  const bf16_t* hb = h + (static_cast<size_t>(b) * kBigTokens + n_off + brow) * I + k_begin;
+  ld.rb = big_rsrc(h + (static_cast<size_t>(b) * kBigTokens + n_off) * I, static_cast<size_t>(kBigN) * I * 2);
 #pragma unroll
   for (int q = 0; q < kBigGroupsB; ++q)
-    bsrc[q] = hb + static_cast<size_t>(kBigRowsPerGroup * q) * I + (q & 1 ? c_odd : c_even);
+    ld.b[q] = 2 * (static_cast<uint32_t>(brow + kBigRowsPerGroup * q) * I + k_begin +
+                   (q & 1 ? c_odd : c_even));
   const int wm = wave & 1, wn = wave >> 1;
-  f32x4 acc[8][kBigNB];
+  BigAcc acc;
 #pragma unroll
-  for (int t = 0; t < 8; ++t)
+  for (int t = 0; t < kBigTA; ++t)
 #pragma unroll
     for (int u = 0; u < kBigNB; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // A rows 128*wm .. +127: eight consecutive 16-row tiles
-  BigRing{ld, bsrc, buf, wave, 128 * wm, 128 * wm + 64, (kBigN / kBigWn) * wn}.run(nst, acc);
+  const bool live = __builtin_amdgcn_readfirstlane(blk[n_off + (kBigN / kBigWn) * wn]) < A;
+  BigRing{ld, buf, wave, 128 * wm, 128 * wm + 64, (kBigN / kBigWn) * wn, live}.run(nst, acc);
 
+  // lane: token column r16 of tile u, channels n0 + 128wm + 16t + 4g .. +3
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
 #pragma unroll
   for (int u = 0; u < kBigNB; ++u) {
     const int f = blk[n_off + (kBigN / kBigWn) * wn + 16 * u + r16];
@@ -454,7 +488,7 @@ __global__ __launch_bounds__(kBigThreads) void ffn2_big_kernel(
       const float gate = topk_w[f];
       float* yrow = y + static_cast<size_t>(f) * d + n0 + 128 * wm + 4 * g;
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
+      for (int t = 0; t < kBigTA; ++t)
         *reinterpret_cast<float4*>(yrow + 16 * t) =
             float4{acc[t][u][0] * gate, acc[t][u][1] * gate, acc[t][u][2] * gate,
                    acc[t][u][3] * gate};
@@ -464,7 +498,12 @@ __global__ __launch_bounds__(kBigThreads) void ffn2_big_kernel(
 
 // ------------------------------------------------------------ launchers
 
-bool big_gemm_fits(int d, int I) { return d % 256 == 0 && I % 128 == 0; }
+// The loads address an expert's W13 (2I x d) and x (T x d) with 32-bit
+// byte offsets: both must stay under 2 GiB.
+bool big_gemm_fits(int64_t T, int d, int I) {
+  const int64_t lim = int64_t(1) << 31;
+  return d % 256 == 0 && I % 128 == 0 && int64_t(4) * I * d < lim && T * d * 2 < lim;
+}
 
 static int big_grid(int gx, int gy) {
   const int total = gx * gy;
@@ -472,7 +511,7 @@ static int big_grid(int gx, int gy) {
 }
 
 hipError_t launch_ffn13_big(const FfnArgs& a, hipStream_t s) {
-  if (a.B != kBigTokens || a.w_dtype != kDtypeBF16 || !big_gemm_fits(a.d, a.I))
+  if (a.B != kBigTokens || a.w_dtype != kDtypeBF16 || !big_gemm_fits(a.T, a.d, a.I))
     return hipErrorInvalidValue;
   const int gx = a.cap / kBigTokens * kBigHalves, gy = a.I / 128;
   ffn13_big_kernel<<<big_grid(gx, gy), kBigThreads, 0, s>>>(
@@ -483,7 +522,7 @@ hipError_t launch_ffn13_big(const FfnArgs& a, hipStream_t s) {
 
 hipError_t launch_ffn2_big(const FfnArgs& a, hipStream_t s) {
   // every split an even number (>= 2) of 64-wide K stages
-  if (a.B != kBigTokens || a.w_dtype != kDtypeBF16 || !big_gemm_fits(a.d, a.I) ||
+  if (a.B != kBigTokens || a.w_dtype != kDtypeBF16 || !big_gemm_fits(a.T, a.d, a.I) ||
       a.ksplit % (2 * kBigK) != 0 || a.splits < 1 ||
       static_cast<int64_t>(a.splits - 1) * a.ksplit >= a.I)
     return hipErrorInvalidValue;

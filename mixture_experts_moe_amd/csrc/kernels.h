@@ -60,7 +60,7 @@ hipError_t launch_ffn13_gemm(const FfnArgs& a, hipStream_t s);
 hipError_t launch_ffn2_gemm(const FfnArgs& a, hipStream_t s);
 // Large-tile grouped GEMM (block size 256, bf16 weights, d % 256 == 0 and
 // I % 128 == 0); used when a.B == 256.
-bool big_gemm_fits(int d, int I);
+bool big_gemm_fits(int64_t T, int d, int I);
 hipError_t launch_ffn13_big(const FfnArgs& a, hipStream_t s);
 hipError_t launch_ffn2_big(const FfnArgs& a, hipStream_t s);
 int big_w2_kchunk();  // a split of the big W2's K range is a multiple of this
