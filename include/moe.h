@@ -23,8 +23,9 @@
  *
  * Conventions for every entry point:
  *   - Tensors are caller-owned DEVICE buffers, contiguous, row-major, 16-byte
- *     aligned.  The library never allocates, frees or retains them; inputs
- *     must stay alive and unmodified until the stream reaches the work.
+ *     aligned.  The library never allocates, frees or retains them (a
+ *     moe_graph keeps their addresses, see moe_graph_create); inputs must
+ *     stay alive and unmodified until the stream reaches the work.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  *     and the call returns at once.  Outputs are valid once the stream has
  *     executed it.  Outputs are fully overwritten, never accumulated into.
@@ -51,7 +52,8 @@
  * Limits: d and I multiples of 64 in [64, 2^19]; 1 <= E <= 1024;
  * 1 <= top_k <= min(E, 64);
  * T * top_k < 2^30; block_m in {0 (library default), 16, 32, 64, 128, 256};
- * 256 needs bf16 weights, d % 256 == 0 and I % 128 == 0.
+ * 256 needs bf16 weights, d % 256 == 0, I % 128 == 0, 4*I*d < 2^31 and
+ * 2*T*d < 2^31 (an expert's W13 and x addressed with 32-bit byte offsets).
  */
 #ifndef MOE_H_
 #define MOE_H_
@@ -173,6 +175,23 @@ MOE_API int moe_align(const moe_desc* desc, const int32_t* topk_ids, int top_k,
                       int32_t* counts, int32_t* sorted_ids, int32_t* block_expert,
                       int32_t* num_padded, void* stream);
 
+/* Routing and regrouping in one call: the outputs of moe_route (logits
+ * [T, E], topk_ids [T, top_k], topk_w [T, top_k]) followed by those of
+ * moe_align (counts, sorted_ids, block_expert, num_padded, laid out and
+ * sized as moe_align documents for the same desc), with the same rules,
+ * bit for bit.  The pages fuse the routing and the data rearrangement with
+ * the expert computation into one GPU operation (Hungarian page, section
+ * "A fused MoE ..."); here, for bf16 activations with T <= 16 and E <= 16,
+ * the workgroup that selects the experts also regroups the slots, so the
+ * two steps are a single kernel launch (otherwise the two steps' kernels run
+ * back to back).  moe_forward takes the same path.  All pointers are device
+ * buffers owned by the caller; outputs are overwritten; errors as moe_route.
+ * Asynchronous on `stream`. */
+MOE_API int moe_route_align(const moe_desc* desc, const void* x, const float* w_gate, int top_k,
+                            float* logits, int32_t* topk_ids, float* topk_w, int32_t* counts,
+                            int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded,
+                            void* stream);
+
 /* Expert computation and combine for an existing routing: W13 grouped
  * product with SiLU(gate)*up, W2 grouped product scaled by the slot's gate,
  * sum of each token's slots into out [T, d].  topk_w [T, top_k] fp32 and
@@ -190,6 +209,35 @@ MOE_API int moe_expert_ffn(const moe_desc* desc, const void* x, const void* w13,
 /* ---- diagnostics ---- */
 
 /* Static text for a status code (never NULL). */
+/* A captured forward: moe_forward's launch sequence for one desc and one
+ * set of buffers, recorded once into a HIP graph and replayed with a single
+ * launch per step.  The pages' fused operation replaces a sequence of
+ * separate operations by one batched GPU operation (Hungarian page, section
+ * "A fused MoE ..."); at decode sizes the gaps between the layer's kernels
+ * are a visible share of a step, and a graph replay submits the whole
+ * layer at once.  A decode loop writes the next tokens into the same x and
+ * replays.
+ *   moe_graph_create: same arguments and checks as moe_forward, plus the
+ *     handle out-parameter.  It records, it does not run: nothing is
+ *     enqueued on any caller stream.  The graph keeps the addresses given
+ *     here (x, w_gate, W13, W2, the scales, out, the workspace): they must
+ *     stay allocated, at the same addresses, until moe_graph_destroy.  Each
+ *     replay reads what those buffers hold when the stream reaches it.
+ *     *graph is NULL on error.  MOE_ERR_HIP if capture or instantiation
+ *     fails.  Kernel timing (moe_timing_enable) does not see replays.
+ *   moe_graph_launch: enqueue one replay on `stream`; asynchronous.
+ *     Replays of one graph share its workspace: replays on different
+ *     streams must be ordered by the caller.
+ *   moe_graph_destroy: release the graph (NULL is accepted); the stream
+ *     work already enqueued completes normally. */
+typedef struct moe_graph moe_graph;
+MOE_API int moe_graph_create(const moe_desc* desc, const void* x, const float* w_gate,
+                             const void* w13, const void* w2, int top_k,
+                             const moe_scales* scales, void* out, void* workspace,
+                             size_t workspace_bytes, moe_graph** graph);
+MOE_API int moe_graph_launch(moe_graph* graph, void* stream);
+MOE_API int moe_graph_destroy(moe_graph* graph);
+
 MOE_API const char* moe_strerror(int status);
 
 /* Kernel timing.  Kernels of the kinds set in the mask given to

@@ -29,7 +29,8 @@ MOE_KERNEL_COUNT = 6
 
 ENTRY_POINTS = (
     "moe_align_capacity", "moe_workspace_bytes", "moe_forward", "moe_route",
-    "moe_route_logits", "moe_align", "moe_expert_ffn", "moe_strerror",
+    "moe_route_logits", "moe_align", "moe_route_align", "moe_expert_ffn",
+    "moe_graph_create", "moe_graph_launch", "moe_graph_destroy", "moe_strerror",
     "moe_timing_enable", "moe_timing_collect", "moe_kernel_name",
 )
 
@@ -73,6 +74,10 @@ def lib() -> ctypes.CDLL:
         "moe_route": (I32, [D, P, P, I32, P, P, P, P]),
         "moe_route_logits": (I32, [D, P, I32, P, P, P]),
         "moe_align": (I32, [D, P, I32, P, P, P, P, P]),
+        "moe_route_align": (I32, [D, P, P, I32, P, P, P, P, P, P, P, P]),
+        "moe_graph_create": (I32, [D, P, P, P, P, I32, S, P, P, SZ, ctypes.POINTER(P)]),
+        "moe_graph_launch": (I32, [P, P]),
+        "moe_graph_destroy": (I32, [P]),
         "moe_expert_ffn": (I32, [D, P, P, P, I32, S, P, P, P, P, P, P, SZ, P]),
         "moe_strerror": (ctypes.c_char_p, [I32]),
         "moe_timing_enable": (I32, [I32]),
@@ -273,6 +278,81 @@ def moe_align(topk_ids: torch.Tensor, num_experts: int, *, block_m: int = 0, hid
                                         _ptr(sorted_ids), _ptr(block_expert), _ptr(num_padded),
                                         _stream(dev, stream)))
     return counts, sorted_ids[:cap], block_expert[:cap // B], num_padded[:1], B
+
+
+def moe_route_align(x: torch.Tensor, w_gate: torch.Tensor, top_k: int, *, intermediate: int = 64,
+                    weight_dtype: int = MOE_DTYPE_BF16, block_m: int = 0, stream=None):
+    """Routing then regrouping in one call: (logits, topk_ids, topk_w, counts,
+    sorted_ids, block_expert, num_padded, block_m), as moe_route followed by
+    moe_align with the same descriptor (pass the layer's intermediate size
+    and weight dtype to get the block size moe_forward uses)."""
+    dev = _dev(x, w_gate)
+    T, d = x.shape
+    E = w_gate.shape[0]
+    if w_gate.dtype != torch.float32 or w_gate.shape[1] != d:
+        raise ValueError("w_gate must be float32 [E, d]")
+    desc = make_desc(T, d, E, intermediate, _act_code(x), weight_dtype, block_m)
+    B, cap = moe_align_capacity(desc, top_k)
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    ids = torch.empty((T, top_k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, top_k), dtype=torch.float32, device=dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    sorted_ids = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    block_expert = torch.empty(max(cap // B, 1), dtype=torch.int32, device=dev)
+    num_padded = torch.zeros(4, dtype=torch.int32, device=dev)
+    _check("moe_route_align", lib().moe_route_align(
+        ctypes.byref(desc), _ptr(x), _ptr(w_gate), int(top_k), _ptr(logits), _ptr(ids), _ptr(w),
+        _ptr(counts), _ptr(sorted_ids), _ptr(block_expert), _ptr(num_padded),
+        _stream(dev, stream)))
+    return logits, ids, w, counts, sorted_ids[:cap], block_expert[:cap // B], num_padded[:1], B
+
+
+class MoeGraph:
+    """moe_forward recorded once into a HIP graph (moe_graph_create) and
+    replayed with one launch per call.  Holds references to every buffer it
+    was recorded with: write new tokens into `x` in place and call launch()."""
+
+    def __init__(self, x: torch.Tensor, w_gate: torch.Tensor, w13: torch.Tensor,
+                 w2: torch.Tensor, top_k: int, scales: Optional[Sequence[torch.Tensor]] = None,
+                 out: Optional[torch.Tensor] = None, *, block_m: int = 0,
+                 workspace: Optional[torch.Tensor] = None):
+        self._h = None
+        dev = _dev(x, w_gate, w13, w2, out)
+        T, d, E, I = _shapes(x, w_gate, w13, w2)
+        desc = make_desc(T, d, E, I, _act_code(x), _w_code(w13), block_m)
+        self._sc = _scales(w13, scales)
+        if out is None:
+            out = torch.empty((T, d), dtype=x.dtype, device=dev)
+        elif out.shape != x.shape or out.dtype != x.dtype:
+            raise ValueError("out must match x in shape and dtype")
+        nbytes = moe_workspace_bytes(desc, top_k, True)
+        ws = _workspace(nbytes, dev, workspace)
+        # the graph keeps these addresses: keep the tensors alive with it
+        self._keep = (x, w_gate, w13, w2, tuple(scales) if scales is not None else None, ws)
+        self.x, self.out, self.device = x, out, dev
+        h = ctypes.c_void_p()
+        _check("moe_graph_create", lib().moe_graph_create(
+            ctypes.byref(desc), _ptr(x), _ptr(w_gate), _ptr(w13), _ptr(w2), int(top_k),
+            ctypes.byref(self._sc) if self._sc is not None else None, _ptr(out), _ptr(ws), nbytes,
+            ctypes.byref(h)))
+        self._h = h
+
+    def launch(self, stream=None) -> torch.Tensor:
+        if self._h is None:
+            raise RuntimeError("graph already destroyed")
+        _check("moe_graph_launch", lib().moe_graph_launch(self._h, _stream(self.device, stream)))
+        return self.out
+
+    def close(self) -> None:
+        if self._h is not None:
+            h, self._h = self._h, None
+            _check("moe_graph_destroy", lib().moe_graph_destroy(h))
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def moe_expert_ffn(x: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, top_k: int,

@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <new>
 #include <vector>
 
 #include "kernels.h"
@@ -212,6 +213,9 @@ std::vector<std::pair<hipEvent_t, hipEvent_t>> g_event_pool;
 double g_total_ms[MOE_KERNEL_COUNT] = {};
 int64_t g_launches[MOE_KERNEL_COUNT] = {};
 
+// Set while this thread records a graph: captured launches are not timed.
+thread_local bool t_capturing = false;
+
 template <class F>
 hipError_t timed(int kind, hipStream_t s, F&& launch) {
   bool on;
@@ -219,7 +223,7 @@ hipError_t timed(int kind, hipStream_t s, F&& launch) {
     std::lock_guard<std::mutex> lk(g_timing_mu);
     on = (g_timing_mask >> kind) & 1u;
   }
-  if (!on) return launch();
+  if (!on || t_capturing) return launch();
   hipEvent_t a, b;
   {
     std::lock_guard<std::mutex> lk(g_timing_mu);
@@ -350,6 +354,25 @@ static hipError_t route(const void* x, int act, const float* w_gate, float* logi
   return e;
 }
 
+// Routing followed by the regrouping: one kernel when the router's single
+// workgroup can regroup too (timed as route_logits), else route() then the
+// regrouping kernel.
+static hipError_t route_align(const Plan& p, const void* x, const float* w_gate, float* logits,
+                              int32_t* ids, float* gates, int32_t* counts, int32_t* sorted,
+                              int32_t* block_exp, int32_t* num_padded, hipStream_t s) {
+  if (moe::route_align_fused(p.act, p.T, p.E))
+    return timed(MOE_KERNEL_ROUTE_LOGITS, s, [&] {
+      return moe::launch_route_align_fused(x, w_gate, logits, ids, gates, p.T, p.E, p.d, p.k, p.B,
+                                           p.cap, counts, sorted, block_exp, num_padded, s);
+    });
+  hipError_t e = route(x, p.act, w_gate, logits, ids, gates, p.T, p.E, p.d, p.k, s);
+  if (e == hipSuccess)
+    e = timed(MOE_KERNEL_ALIGN, s, [&] {
+      return moe::launch_align(ids, p.A, p.E, p.B, p.cap, counts, sorted, block_exp, num_padded, s);
+    });
+  return e;
+}
+
 MOE_API int moe_route(const moe_desc* desc, const void* x, const float* w_gate, int top_k,
                       float* logits, int32_t* topk_ids, float* topk_w, void* stream) {
   int st = check_desc(desc, top_k);
@@ -392,6 +415,23 @@ MOE_API int moe_align(const moe_desc* desc, const int32_t* topk_ids, int top_k, 
   }));
 }
 
+MOE_API int moe_route_align(const moe_desc* desc, const void* x, const float* w_gate, int top_k,
+                            float* logits, int32_t* topk_ids, float* topk_w, int32_t* counts,
+                            int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded,
+                            void* stream) {
+  int st = check_desc(desc, top_k);
+  if (st) return st;
+  if (desc->num_tokens == 0) return MOE_OK;
+  if ((st = check_ptrs({x, w_gate, logits, topk_ids, topk_w, counts, sorted_ids, block_expert,
+                        num_padded})))
+    return st;
+  Plan p;
+  make_plan(desc, top_k, true, &p);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return to_status(route_align(p, x, w_gate, logits, topk_ids, topk_w, counts, sorted_ids,
+                               block_expert, num_padded, s));
+}
+
 MOE_API int moe_expert_ffn(const moe_desc* desc, const void* x, const void* w13, const void* w2,
                            int top_k, const moe_scales* scales, const float* topk_w,
                            const int32_t* sorted_ids, const int32_t* block_expert,
@@ -414,20 +454,25 @@ MOE_API int moe_expert_ffn(const moe_desc* desc, const void* x, const void* w13,
   return to_status(run_ffn(a, s));
 }
 
-MOE_API int moe_forward(const moe_desc* desc, const void* x, const float* w_gate,
-                        const void* w13, const void* w2, int top_k, const moe_scales* scales,
-                        void* out, void* workspace, size_t workspace_bytes, void* stream) {
+// Checks shared by moe_forward and moe_graph_create; fills the plan.
+static int forward_checks(const moe_desc* desc, const void* x, const float* w_gate,
+                          const void* w13, const void* w2, int top_k, const moe_scales* scales,
+                          void* out, void* workspace, size_t workspace_bytes, Plan* p) {
   int st = check_desc(desc, top_k);
   if (st) return st;
   if (desc->num_tokens == 0) return MOE_OK;
   if ((st = check_scales(desc, scales))) return st;
   if ((st = check_ptrs({x, w_gate, w13, w2, out}))) return st;
-  Plan p;
-  make_plan(desc, top_k, true, &p);
-  if (!workspace || workspace_bytes < p.total) return MOE_ERR_WORKSPACE;
+  make_plan(desc, top_k, true, p);
+  if (!workspace || workspace_bytes < p->total) return MOE_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) % kWsAlign) return MOE_ERR_MISALIGNED;
-  char* ws = static_cast<char*>(workspace);
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  return MOE_OK;
+}
+
+// The whole layer on stream s (T > 0, arguments checked).
+static int enqueue_forward(const Plan& p, const void* x, const float* w_gate, const void* w13,
+                           const void* w2, const moe_scales* scales, void* out, char* ws,
+                           hipStream_t s) {
   float* logits = reinterpret_cast<float*>(ws + p.logits);
   int32_t* ids = reinterpret_cast<int32_t*>(ws + p.ids);
   float* gates = reinterpret_cast<float*>(ws + p.gates);
@@ -436,15 +481,87 @@ MOE_API int moe_forward(const moe_desc* desc, const void* x, const float* w_gate
   int32_t* sorted = reinterpret_cast<int32_t*>(ws + p.sorted);
   int32_t* block_exp = reinterpret_cast<int32_t*>(ws + p.block_exp);
 
-  hipError_t e = route(x, p.act, w_gate, logits, ids, gates, p.T, p.E, p.d, p.k, s);
-  if (e == hipSuccess)
-    e = timed(MOE_KERNEL_ALIGN, s, [&] {
-      return moe::launch_align(ids, p.A, p.E, p.B, p.cap, counts, sorted, block_exp, num_padded,
-                               s);
-    });
+  const hipError_t e =
+      route_align(p, x, w_gate, logits, ids, gates, counts, sorted, block_exp, num_padded, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   FfnArgs a = ffn_args(p, x, w13, w2, scales, gates, sorted, block_exp, num_padded, out, ws);
   return to_status(run_ffn(a, s));
+}
+
+MOE_API int moe_forward(const moe_desc* desc, const void* x, const float* w_gate,
+                        const void* w13, const void* w2, int top_k, const moe_scales* scales,
+                        void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  Plan p;
+  const int st = forward_checks(desc, x, w_gate, w13, w2, top_k, scales, out, workspace,
+                                workspace_bytes, &p);
+  if (st || desc->num_tokens == 0) return st;
+  return enqueue_forward(p, x, w_gate, w13, w2, scales, out, static_cast<char*>(workspace),
+                         static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+// Opaque graph handle: the instantiated graph (NULL for T = 0, whose
+// replay does nothing).
+struct moe_graph {
+  hipGraphExec_t exec;
+};
+
+extern "C" {
+
+MOE_API int moe_graph_create(const moe_desc* desc, const void* x, const float* w_gate,
+                             const void* w13, const void* w2, int top_k,
+                             const moe_scales* scales, void* out, void* workspace,
+                             size_t workspace_bytes, moe_graph** graph) {
+  if (!graph) return MOE_ERR_NULL_PTR;
+  *graph = nullptr;
+  Plan p;
+  int st = forward_checks(desc, x, w_gate, w13, w2, top_k, scales, out, workspace,
+                          workspace_bytes, &p);
+  if (st) return st;
+  if (desc->num_tokens == 0) {
+    *graph = new (std::nothrow) moe_graph{nullptr};
+    return *graph ? MOE_OK : MOE_ERR_HIP;
+  }
+  // record on a private stream; thread-local capture mode leaves other
+  // threads' HIP calls alone
+  hipStream_t cs;
+  if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess) return MOE_ERR_HIP;
+  hipGraph_t g = nullptr;
+  if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+    (void)hipStreamDestroy(cs);
+    return MOE_ERR_HIP;
+  }
+  t_capturing = true;
+  st = enqueue_forward(p, x, w_gate, w13, w2, scales, out, static_cast<char*>(workspace), cs);
+  t_capturing = false;
+  const hipError_t ce = hipStreamEndCapture(cs, &g);  // always ends the capture
+  (void)hipStreamDestroy(cs);
+  if (st == MOE_OK && (ce != hipSuccess || !g)) st = MOE_ERR_HIP;
+  hipGraphExec_t exec = nullptr;
+  if (st == MOE_OK && hipGraphInstantiate(&exec, g, nullptr, nullptr, 0) != hipSuccess)
+    st = MOE_ERR_HIP;
+  if (g) (void)hipGraphDestroy(g);
+  if (st != MOE_OK) return st;
+  *graph = new (std::nothrow) moe_graph{exec};
+  if (!*graph) {
+    (void)hipGraphExecDestroy(exec);
+    return MOE_ERR_HIP;
+  }
+  return MOE_OK;
+}
+
+MOE_API int moe_graph_launch(moe_graph* graph, void* stream) {
+  if (!graph) return MOE_ERR_NULL_PTR;
+  if (!graph->exec) return MOE_OK;  // T = 0
+  return to_status(hipGraphLaunch(graph->exec, static_cast<hipStream_t>(stream)));
+}
+
+MOE_API int moe_graph_destroy(moe_graph* graph) {
+  if (!graph) return MOE_OK;
+  const hipError_t e = graph->exec ? hipGraphExecDestroy(graph->exec) : hipSuccess;
+  delete graph;
+  return to_status(e);
 }
 
 MOE_API int moe_timing_enable(int kind_mask) {

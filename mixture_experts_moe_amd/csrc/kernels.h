@@ -25,6 +25,13 @@ hipError_t launch_router_topk(const float* logits, int32_t* ids, float* w, int T
 bool router_fused(int act_dtype, int T, int E);
 hipError_t launch_router_fused(const void* x, const float* wg, float* logits, int32_t* ids,
                                float* w, int T, int E, int d, int k, hipStream_t s);
+// bf16 activations, 1 <= T <= 16, E <= 16: logits, selection and the
+// regrouping (same outputs as launch_align) in one single-workgroup kernel.
+bool route_align_fused(int act_dtype, int T, int E);
+hipError_t launch_route_align_fused(const void* x, const float* wg, float* logits, int32_t* ids,
+                                    float* w, int T, int E, int d, int k, int B, int cap,
+                                    int32_t* counts, int32_t* sorted_ids, int32_t* block_expert,
+                                    int32_t* num_padded, hipStream_t s);
 hipError_t launch_align(const int32_t* ids, int A, int E, int B, int cap, int32_t* counts,
                         int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded,
                         hipStream_t s);

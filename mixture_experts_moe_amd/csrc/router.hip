@@ -29,7 +29,7 @@ __device__ __forceinline__ bool better(float av, int ae, float bv, int be) {
 // The whole wave selects for one token: `row` holds its E logits (global or
 // LDS); writes k ids and gates.
 __device__ __forceinline__ void topk_wave(const float* row, int E, int k, int32_t* ids,
-                                          float* gates) {
+                                          float* gates, int* lds_ids = nullptr) {
   const int lane = threadIdx.x & 63;
   float v[kMaxExpertsPerLane];
   const int per_lane = (E + 63) >> 6;
@@ -78,6 +78,7 @@ __device__ __forceinline__ void topk_wave(const float* row, int E, int k, int32_
   if (lane < k) {
     ids[lane] = my_e;
     gates[lane] = p / s;
+    if (lds_ids) lds_ids[lane] = my_e;
   }
 }
 
@@ -89,6 +90,75 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
   if (t >= T) return;
   topk_wave(logits + static_cast<size_t>(t) * E, E, k, topk_ids + static_cast<size_t>(t) * k,
             topk_w + static_cast<size_t>(t) * k);
+}
+
+// ---------------------------------------------------------------- regrouping in the router
+//
+// For a batch routed by a single workgroup (at most 16 tokens, so at most
+// 16 * 16 slots) the same workgroup also regroups the slots by expert, which
+// saves the separate regrouping launch on the small-batch (decode) path.  It
+// writes what the regrouping kernel writes, by the same definition: slot f
+// of expert e lands at off[e] + (number of slots f' < f routed to e), where
+// off[e] = sum over e' < e of counts rounded up to the block size; pads and
+// the tail hold the sentinel A, block owners -1 past the padded total.  Each
+// wave ranks its 64 slots per expert with a ballot; a wave's base is the sum
+// over lower waves.
+
+struct AlignOut {
+  int B, cap;
+  int32_t* counts;
+  int32_t* sorted_ids;
+  int32_t* block_expert;
+  int32_t* num_padded;
+};
+
+constexpr int kRaWaves = 16;  // the fused router's workgroup
+
+__device__ __forceinline__ void align_in_block(const int* s_ids, int A, int E, const AlignOut& o) {
+  __shared__ int s_wc[kRaWaves][16];  // [wave][expert]: this wave's slots routed to the expert
+  __shared__ int s_off[17], s_cnt[16];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int id = tid < A ? s_ids[tid] : -1;  // slot f = tid
+  int rank = 0;
+  for (int e = 0; e < E; ++e) {
+    const uint64_t m = __ballot(id == e);
+    if (id == e) rank = __popcll(m & ((1ull << lane) - 1ull));
+    if (lane == 0) s_wc[wave][e] = __popcll(m);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int off = 0;
+    for (int e = 0; e < E; ++e) {
+      int c = 0;
+      for (int w = 0; w < kRaWaves; ++w) c += s_wc[w][e];
+      s_cnt[e] = c;
+      s_off[e] = off;
+      off += (c + o.B - 1) / o.B * o.B;
+    }
+    s_off[E] = off;
+  }
+  __syncthreads();
+  if (static_cast<unsigned>(id) < static_cast<unsigned>(E)) {
+    int base = 0;
+    for (int w = 0; w < wave; ++w) base += s_wc[w][id];
+    o.sorted_ids[s_off[id] + base + rank] = tid;
+  }
+  const int total = s_off[E];
+  for (int r = tid; r < o.cap; r += 64 * kRaWaves) {  // pads and the tail
+    int e = 0;
+    while (e + 1 < E && s_off[e + 1] <= r) ++e;
+    if (r >= total || r - s_off[e] >= s_cnt[e]) o.sorted_ids[r] = A;
+  }
+  for (int b = tid; b < o.cap / o.B; b += 64 * kRaWaves) {
+    const int r = b * o.B;
+    int e = 0;
+    while (e + 1 < E && s_off[e + 1] <= r) ++e;
+    o.block_expert[b] = r < total ? e : -1;
+  }
+  if (tid < E) o.counts[tid] = s_cnt[tid];
+  if (tid == 0) *o.num_padded = total;
 }
 
 // ---------------------------------------------------------------- logits
@@ -198,11 +268,13 @@ __device__ __forceinline__ void split3_bf16(const float (&w)[8], uint4& hi, uint
 
 // kTopk (NT = 1, NW = 16, E <= 16: one workgroup holds every expert of its
 // 16 tokens): the workgroup also selects, one wave per token.
-template <int NT, int NW, bool kTopk>
+template <int NT, int NW, bool kTopk, bool kAlign = false>
 __global__ __launch_bounds__(64 * NW) void router_logits_bf16_kernel(
     const bf16_t* __restrict__ x, const float* __restrict__ wg, float* __restrict__ logits,
-    int32_t* __restrict__ topk_ids, float* __restrict__ topk_w, int T, int E, int d, int k) {
+    int32_t* __restrict__ topk_ids, float* __restrict__ topk_w, int T, int E, int d, int k,
+    AlignOut ao) {
   static_assert(!kTopk || (NT == 1 && NW == 16), "fused selection: 16 tokens, 16 waves");
+  static_assert(!kAlign || kTopk, "regrouping follows the selection");
   // 32-wide steps whose loads are issued together: the few-token kernel is
   // latency-bound, so it takes a whole wave's K range (d = 4096) in one round
   constexpr int U = NT == 1 ? 8 : 4;
@@ -276,11 +348,16 @@ __global__ __launch_bounds__(64 * NW) void router_logits_bf16_kernel(
     }
   }
   if constexpr (kTopk) {
+    __shared__ int s_ids[kAlign ? 16 * 16 : 1];  // [token][rank] expert ids (grid of one)
     __syncthreads();
     const int t = t0 + wave;
     if (t < T)
       topk_wave(lg[wave], E, k, topk_ids + static_cast<size_t>(t) * k,
-                topk_w + static_cast<size_t>(t) * k);
+                topk_w + static_cast<size_t>(t) * k, kAlign ? s_ids + wave * k : nullptr);
+    if constexpr (kAlign) {
+      __syncthreads();
+      align_in_block(s_ids, T * k, E, ao);
+    }
   }
 }
 
@@ -295,11 +372,11 @@ hipError_t launch_router_logits(const void* x, int act_dtype, const float* wg, f
   } else if (T <= 64) {  // few tokens: split K 16 ways for latency
     dim3 grid((T + 15) / 16, (E + 15) / 16);
     router_logits_bf16_kernel<1, 16, false><<<grid, 1024, 0, s>>>(
-        static_cast<const bf16_t*>(x), wg, logits, nullptr, nullptr, T, E, d, 0);
+        static_cast<const bf16_t*>(x), wg, logits, nullptr, nullptr, T, E, d, 0, AlignOut{});
   } else {
     dim3 grid((T + 63) / 64, (E + 15) / 16);
     router_logits_bf16_kernel<4, 4, false><<<grid, 256, 0, s>>>(
-        static_cast<const bf16_t*>(x), wg, logits, nullptr, nullptr, T, E, d, 0);
+        static_cast<const bf16_t*>(x), wg, logits, nullptr, nullptr, T, E, d, 0, AlignOut{});
   }
   return hipGetLastError();
 }
@@ -312,7 +389,23 @@ hipError_t launch_router_fused(const void* x, const float* wg, float* logits, in
                                float* w, int T, int E, int d, int k, hipStream_t s) {
   if (E > 16) return hipErrorInvalidValue;
   router_logits_bf16_kernel<1, 16, true><<<dim3((T + 15) / 16, 1), 1024, 0, s>>>(
-      static_cast<const bf16_t*>(x), wg, logits, ids, w, T, E, d, k);
+      static_cast<const bf16_t*>(x), wg, logits, ids, w, T, E, d, k, AlignOut{});
+  return hipGetLastError();
+}
+
+bool route_align_fused(int act_dtype, int T, int E) {
+  return act_dtype == kDtypeBF16 && T >= 1 && T <= 16 && E <= 16;
+}
+
+hipError_t launch_route_align_fused(const void* x, const float* wg, float* logits, int32_t* ids,
+                                    float* w, int T, int E, int d, int k, int B, int cap,
+                                    int32_t* counts, int32_t* sorted_ids, int32_t* block_expert,
+                                    int32_t* num_padded, hipStream_t s) {
+  if (!route_align_fused(kDtypeBF16, T, E) || k > E || B < 1 || cap % B != 0)
+    return hipErrorInvalidValue;
+  const AlignOut ao{B, cap, counts, sorted_ids, block_expert, num_padded};
+  router_logits_bf16_kernel<1, 16, true, true><<<dim3(1, 1), 1024, 0, s>>>(
+      static_cast<const bf16_t*>(x), wg, logits, ids, w, T, E, d, k, ao);
   return hipGetLastError();
 }
 

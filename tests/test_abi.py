@@ -71,6 +71,10 @@ def ws_status(lib, dsc, k=2):
     (dict(d=256, w=B.MOE_DTYPE_E4M3FN, bm=256), 2, -8),  # bf16 weights only
     (dict(bm=512), 2, -8),
     (dict(T=1 << 28), 8, -2),
+    # the 256-token GEMM addresses an expert's W13 and x with 32-bit offsets
+    (dict(T=1 << 18, d=4096, bm=256), 2, -8),          # 2*T*d = 2^31
+    (dict(T=(1 << 18) - 64, d=4096, bm=256), 2, 0),
+    (dict(d=1 << 15, I=1 << 15, bm=256), 2, -8),      # 4*I*d = 2^32
 ])
 def test_descriptor_validation(lib, kw, k, status):
     assert ws_status(lib, desc(**kw), k) == status
@@ -164,6 +168,35 @@ def test_stage_entry_points_validate(lib):
     assert lib.moe_expert_ffn(ctypes.byref(d), FAKE, FAKE, FAKE, 2, None, FAKE, FAKE, FAKE, FAKE,
                               FAKE, FAKE, 0, None) == -6
     assert lib.moe_route(ctypes.byref(desc(T=0)), None, None, 2, None, None, None, None) == 0
+
+
+def test_route_align_and_graph_validate(lib):
+    d = desc()
+    ra = lib.moe_route_align
+    assert ra(ctypes.byref(d), None, FAKE, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -1
+    assert ra(ctypes.byref(d), FAKE, FAKE, 9, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -3
+    assert ra(ctypes.byref(d), FAKE, FAKE, 2, FAKE, FAKE, FAKE, FAKE + 4, FAKE, FAKE, FAKE,
+              None) == -5
+    assert ra(ctypes.byref(desc(T=0)), None, None, 2, None, None, None, None, None, None, None,
+              None) == 0
+    h = ctypes.c_void_p(12345)
+    gc = lib.moe_graph_create
+    assert gc(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 2, None, FAKE, FAKE, 1 << 40, None) == -1
+    assert gc(ctypes.byref(d), None, FAKE, FAKE, FAKE, 2, None, FAKE, FAKE, 1 << 40,
+              ctypes.byref(h)) == -1
+    assert h.value is None                       # NULL on error
+    assert gc(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 2, None, FAKE, FAKE, 16,
+              ctypes.byref(h)) == -6
+    assert gc(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 2, None, FAKE, FAKE + 16, 1 << 40,
+              ctypes.byref(h)) == -5
+    # T = 0: a handle whose replay does nothing (no HIP call anywhere)
+    assert gc(ctypes.byref(desc(T=0)), None, None, None, None, 2, None, None, None, 0,
+              ctypes.byref(h)) == 0
+    assert h.value
+    assert lib.moe_graph_launch(h, None) == 0
+    assert lib.moe_graph_destroy(h) == 0
+    assert lib.moe_graph_launch(None, None) == -1
+    assert lib.moe_graph_destroy(None) == 0
 
 
 def test_strerror_and_names(lib):

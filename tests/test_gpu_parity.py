@@ -195,10 +195,12 @@ def test_output_guard_bands_untouched():
     assert torch.isfinite(out.float()).all()
 
 
-@pytest.mark.parametrize("E,topk_launches", [(8, 0), (32, 3)])
-def test_kernel_timing_counts_launches(E, topk_launches):
-    # with at most 16 experts and 64 tokens the router kernel selects itself
-    inp = synth.make_inputs("decode_bf16", T=8, device=DEV, d=256, I=128, E=E, x_std=1.0)
+@pytest.mark.parametrize("E,T,topk_launches,align_launches", [(8, 8, 0, 0), (8, 20, 0, 3),
+                                                               (32, 8, 3, 3)])
+def test_kernel_timing_counts_launches(E, T, topk_launches, align_launches):
+    # with at most 16 experts and 64 tokens the router kernel selects itself;
+    # with at most 16 tokens it also regroups (one routing launch)
+    inp = synth.make_inputs("decode_bf16", T=T, device=DEV, d=256, I=128, E=E, x_std=1.0)
     B.moe_timing_collect(reset=True)
     B.moe_timing_enable(True)
     try:
@@ -207,10 +209,11 @@ def test_kernel_timing_counts_launches(E, topk_launches):
         t = B.moe_timing_collect(reset=True)
     finally:
         B.moe_timing_enable(False)
-    for name in ("route_logits", "align", "ffn13", "ffn2", "combine"):
+    for name in ("route_logits", "ffn13", "ffn2", "combine"):
         ms, n = t[name]
         assert n == 3 and ms > 0, (name, t[name])
     assert t["route_topk"][1] == topk_launches
+    assert t["align"][1] == align_launches
 
 
 @pytest.mark.parametrize("T,E,k", [(1, 8, 2), (16, 16, 4), (17, 8, 2), (64, 16, 16), (64, 12, 1)])
@@ -301,3 +304,68 @@ def test_skew_full_size():
     counts = np.bincount(ids.cpu().numpy().ravel(), minlength=inp.E)
     assert all(counts[e] == 0 for e in synth.SKEW_IDLE_EXPERTS)
     note(f"  skew counts {counts.tolist()}")
+
+
+# ---------------------------------------------------------------- single-launch decode
+
+@pytest.mark.parametrize("T,E,k,bm,d,I", [
+    (1, 8, 2, 0, 4096, 14336), (8, 8, 2, 0, 4096, 14336),    # the decode shape: fused
+    (16, 16, 4, 0, 512, 512), (5, 16, 16, 32, 512, 512), (16, 8, 1, 64, 512, 512),
+    (3, 2, 2, 16, 256, 256),
+    (17, 8, 2, 0, 512, 512), (40, 16, 4, 0, 512, 512),       # two launches: T > 16
+    (16, 32, 2, 0, 512, 512)])                                # two launches: E > 16
+def test_route_align_equals_route_then_align(T, E, k, bm, d, I):
+    note(f"route_align T={T} E={E} k={k} B={bm}")
+    g = torch.Generator(device="cpu").manual_seed(T * 131 + E)
+    x = (torch.randn(T, d, generator=g) * 0.5).to(torch.bfloat16).to(DEV)
+    wg = (torch.randn(E, d, generator=g) * 0.02).to(DEV)
+    got = B.moe_route_align(x, wg, k, intermediate=I, block_m=bm)
+    logits, ids, w = B.moe_route(x, wg, k)
+    ref = B.moe_align(ids, E, block_m=bm, hidden=d, intermediate=I)
+    torch.cuda.synchronize()
+    assert got[7] == ref[4]
+    for a, b in zip(got[:3], (logits, ids, w)):
+        assert torch.equal(a, b)
+    for a, b in zip(got[3:7], ref[:4]):
+        assert torch.equal(a, b)
+    # and the regrouping is the oracle's for these ids
+    o = oracle.align(ids.cpu().numpy(), E, got[7])
+    assert np.array_equal(got[3].cpu().numpy(), o["counts"])
+    assert np.array_equal(got[4].cpu().numpy(), o["sorted_ids"])
+    assert np.array_equal(got[5].cpu().numpy(), o["block_expert"])
+    assert int(got[6].item()) == o["num_padded"]
+
+
+@pytest.mark.parametrize("wl,T,over", [
+    ("decode_bf16", 1, dict(d=512, I=512)),
+    ("decode_bf16", 8, dict(d=512, I=512)),
+    ("decode_bf16", 40, dict(d=512, I=512)),
+    ("decode_bf16", 16, dict(d=768, I=2048, E=32)),          # weights streamed through LDS
+    ("fp8", 16, dict(d=512, I=512, E=16, k=4)),
+    ("decode_bf16", 300, dict(d=512, I=256)),               # 128-token GEMM
+])
+def test_graph_replay_matches_eager(wl, T, over):
+    note(f"graph {wl} T={T} {over}")
+    inp = synth.make_inputs(wl, T=T, device=DEV, x_std=1.0, **over)
+    sc = (inp.s13, inp.s2) if inp.w == "e4m3fn" else None
+    ref = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, sc)
+    out = torch.empty_like(ref)
+    graph = B.MoeGraph(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, sc, out=out)
+    try:
+        for rep in range(3):
+            out.fill_(float("nan"))                  # eager work between replays
+            graph.launch()
+            other = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, sc)
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref), f"replay {rep}"
+            assert torch.equal(other, ref)
+        # the next step's tokens, written into the recorded x
+        x2 = synth.make_x(inp.T, inp.d, inp.act, 1.0, 1, DEV)
+        inp.x.copy_(x2)
+        ref2 = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, sc)
+        graph.launch()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref2)
+        assert not torch.equal(ref2, ref)
+    finally:
+        graph.close()
