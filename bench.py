@@ -374,6 +374,28 @@ def main() -> int:
     roof["launches"] = ffn13_n
     roof["traffic"] = load_traffic(wl)
 
+    # the same step as one recorded graph per forward (moe_graph_*): one
+    # launch per forward, weights rotated through the same copies
+    graphs = [[B.MoeGraph(i.x, i.w_gate, w13, w2, i.top_k, sc, out=outs[bi], block_m=args.block_m,
+                          workspace=wss[bi]) for (w13, w2) in copies]
+              for bi, i in enumerate(inputs)]
+    gcount = [0]
+
+    def gstep():
+        for bi in range(len(inputs)):
+            graphs[bi][gcount[0] % len(copies)].launch()
+            gcount[0] += 1
+
+    for _ in range(args.warmup):
+        gstep()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        gstep()
+    torch.cuda.synchronize()
+    graph_ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    log(f"graph replay: {graph_ms_per_step:.3f} ms/step")
+
     breakdown = None
     per_batch = []
     if not args.no_breakdown:
@@ -396,6 +418,16 @@ def main() -> int:
                 fw += ev0.elapsed_time(ev1)
             B.moe_timing_enable(False)
             t2 = B.moe_timing_collect(reset=True)
+            # one forward at a time, as a single graph launch
+            gfw = 0.0
+            for _ in range(args.steps):
+                g = graphs[bi][counter[0] % len(copies)]
+                counter[0] += 1
+                ev0.record()
+                g.launch()
+                ev1.record()
+                torch.cuda.synchronize()
+                gfw += ev0.elapsed_time(ev1)
             kern = {k: round(v[0] / args.steps * 1e3, 2) for k, v in t2.items()}
             for k, v in kern.items():
                 breakdown[k] = round(breakdown.get(k, 0.0) + v, 2)
@@ -403,6 +435,7 @@ def main() -> int:
             f13_us = kern["ffn13"]
             per_batch.append({
                 "T": w["T"], "us": round(ms * 1e3, 1), "tokens_per_s": round(w["T"] / (ms / 1e3), 1),
+                "graph_us": round(gfw / args.steps * 1e3, 1),
                 "touched_experts": w["touched_experts"],
                 "layer_hbm_GBps": round(w["bytes"] / (ms / 1e3) / 1e9, 1),
                 "layer_hbm_frac": round(w["bytes"] / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -446,6 +479,8 @@ def main() -> int:
             "kernel_source_sha": kernel_source_sha(),
         },
         "roofline": roof,
+        "graph_replay": {"ms_per_step": round(graph_ms_per_step, 4),
+                         "tokens_per_s": round(tokens / (graph_ms_per_step / 1e3), 1)},
         "cpu_baseline": cpu,
         "per_batch": per_batch,
         "kernel_us_per_step": breakdown,
