@@ -73,10 +73,17 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_sha() -> str:
+# sources that routing and regrouping alone use: they do not change the
+# expert kernels, so their edits leave recorded ffn13 traffic valid
+ROUTING_ONLY_SOURCES = ("router.hip", "align.hip")
+
+
+def kernel_source_sha(exclude=()) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mixture_experts_moe_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
+        if name in exclude:
+            continue
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -207,7 +214,8 @@ def summarize_traffic(workload: str, dirs, command: str) -> str:
     out = {
         "kernel": "ffn13 (grouped W13 + SiLU*mul)",
         "workload": workload,
-        "kernel_source_sha": kernel_source_sha(),
+        # expert-kernel sources (all but the routing-only files)
+        "kernel_source_sha": kernel_source_sha(exclude=ROUTING_ONLY_SOURCES),
         "command": command,
         "calibration": {
             "copy_bytes": COPY_CAL_BYTES,
@@ -491,13 +499,13 @@ def main() -> int:
 
 def load_traffic(workload: str):
     """HBM bytes per ffn13 launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs,
-    if they were taken on the current kernel sources (else null)."""
+    if they were taken on the current expert-kernel sources (else null)."""
     path = os.path.join(ROOT, "profiles", f"ffn13_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_sha") != kernel_source_sha():
+    if t.get("kernel_source_sha") != kernel_source_sha(exclude=ROUTING_ONLY_SOURCES):
         return None
     return t.get("traffic_bytes_per_launch")
 
