@@ -377,6 +377,22 @@ def main() -> int:
         achieved = f13_bytes_step / (f13_ms_step / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    # the chip's attainable rate for the same bound, measured here
+    # (include/moe_bench.h): a streaming read in the weight-streaming pattern
+    # over 1 GiB (past the 256 MB last-level cache), or the big tile's LDS-fed
+    # MFMA loop on random bf16
+    try:
+        if mfma_bound:
+            att = B.bench_mfma_bf16(iters=4096, reps=4, device=dev)
+        else:
+            probe = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+            att = B.bench_hbm_read(probe, reps=5)
+            del probe
+        roof["attainable"] = round(att, 1)
+        roof["frac_attainable"] = round(achieved / att, 4)
+    except (RuntimeError, OSError) as e:
+        log(f"attainable-rate probe unavailable: {e}")
+        roof["attainable"] = roof["frac_attainable"] = None
     roof["kernel"] = "ffn13 (grouped W13 + SiLU*mul)"
     roof["avg_launch_us"] = round(ffn13_ms / max(ffn13_n, 1) * 1e3, 2)
     roof["launches"] = ffn13_n

@@ -92,6 +92,49 @@ def lib() -> ctypes.CDLL:
     return L
 
 
+# ------------------------------------------------------------ attainable-rate probes
+
+BENCH_ENTRY_POINTS = ("moe_bench_hbm_read", "moe_bench_mfma_bf16")
+_BENCH_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_bench.so")
+_bench_lib = None
+
+
+def bench_lib() -> ctypes.CDLL:
+    """Load libmoe_bench.so (once).  Raises if it has not been built."""
+    global _bench_lib
+    if _bench_lib is not None:
+        return _bench_lib
+    if not os.path.exists(_BENCH_LIB_PATH):
+        raise RuntimeError(f"{_BENCH_LIB_PATH} is not built; run `python -m mixture_experts_moe_amd.build`")
+    L = ctypes.CDLL(_BENCH_LIB_PATH)
+    P, I32, SZ, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.POINTER(ctypes.c_double)
+    L.moe_bench_hbm_read.restype = I32
+    L.moe_bench_hbm_read.argtypes = [P, SZ, I32, D, P]
+    L.moe_bench_mfma_bf16.restype = I32
+    L.moe_bench_mfma_bf16.argtypes = [I32, I32, D, P]
+    _bench_lib = L
+    return L
+
+
+def bench_hbm_read(buf: torch.Tensor, reps: int = 5, stream=None) -> float:
+    """Attainable streaming-read rate (GB/s) over the device buffer `buf`."""
+    dev = _dev(buf)
+    r = ctypes.c_double()
+    _check("moe_bench_hbm_read", bench_lib().moe_bench_hbm_read(
+        _ptr(buf), buf.numel() * buf.element_size(), int(reps), ctypes.byref(r),
+        _stream(dev, stream)))
+    return r.value
+
+
+def bench_mfma_bf16(iters: int = 4096, reps: int = 4, device="cuda", stream=None) -> float:
+    """Attainable bf16 MFMA rate (TFLOP/s) of an LDS-fed loop on random data."""
+    dev = torch.device(device)
+    r = ctypes.c_double()
+    _check("moe_bench_mfma_bf16", bench_lib().moe_bench_mfma_bf16(
+        int(iters), int(reps), ctypes.byref(r), _stream(dev, stream)))
+    return r.value
+
+
 def strerror(status: int) -> str:
     return lib().moe_strerror(int(status)).decode()
 

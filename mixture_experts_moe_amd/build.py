@@ -1,4 +1,6 @@
-"""Build the gfx950 shared library ``libmoe.so`` from ``csrc/`` with hipcc.
+"""Build the gfx950 shared libraries with hipcc: ``libmoe.so`` (the layer,
+from ``csrc/``) and ``libmoe_bench.so`` (attainable-rate probes for the
+roofline, from ``csrc_bench/``).
 
 Run as ``python -m mixture_experts_moe_amd.build`` or through
 ``__graft_entry__.build()``.  It always recompiles.
@@ -14,6 +16,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libmoe.so")
+BENCH_LIB = os.path.join(PKG, "libmoe_bench.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -31,16 +34,16 @@ FLAGS = [
 ]
 
 
-def sources():
-    return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
+def sources(folder: str = "csrc"):
+    return sorted(glob.glob(os.path.join(PKG, folder, "*.hip")))
 
 
-def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
-    """Compile every csrc/*.hip into one shared library at `out`.
+def build(verbose: bool = False, extra_flags=(), out: str = LIB, folder: str = "csrc") -> str:
+    """Compile every <folder>/*.hip into one shared library at `out`.
     `extra_flags` (e.g. -D tuning macros) are appended to the hipcc line."""
     tmp = out + ".tmp"
     cmd = [HIPCC, *FLAGS, *extra_flags, "-I", os.path.join(ROOT, "include"),
-           "-I", os.path.join(PKG, "csrc"), *sources(), "-o", tmp]
+           "-I", os.path.join(PKG, folder), *sources(folder), "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -55,5 +58,11 @@ def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
     return out
 
 
+def build_bench(verbose: bool = False) -> str:
+    """The attainable-rate probe library (include/moe_bench.h)."""
+    return build(verbose=verbose, out=BENCH_LIB, folder="csrc_bench")
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_bench(verbose=True))

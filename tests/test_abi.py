@@ -199,6 +199,31 @@ def test_route_align_and_graph_validate(lib):
     assert lib.moe_graph_destroy(None) == 0
 
 
+BENCH_HEADER = os.path.join(ROOT, "include", "moe_bench.h")
+
+
+def test_bench_library_exports_and_validates():
+    from mixture_experts_moe_amd import build
+    if not os.path.exists(B._BENCH_LIB_PATH):
+        build.build_bench()
+    declared = sorted(set(re.findall(r"MOE_BENCH_API\s+[\w\s\*]+?\b(moe_bench_\w+)\s*\(",
+                                     open(BENCH_HEADER).read())))
+    assert declared == sorted(B.BENCH_ENTRY_POINTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", B._BENCH_LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    assert sorted({l.split()[-1] for l in out.splitlines() if " T " in l}) == declared
+    L = B.bench_lib()
+    r = ctypes.c_double()
+    assert L.moe_bench_hbm_read(None, 1 << 20, 3, ctypes.byref(r), None) == -1
+    assert L.moe_bench_hbm_read(FAKE, 1 << 20, 3, None, None) == -1
+    assert L.moe_bench_hbm_read(FAKE, (1 << 20) + 1024, 3, ctypes.byref(r), None) == -9
+    assert L.moe_bench_hbm_read(FAKE, 1 << 20, 1, ctypes.byref(r), None) == -9
+    assert L.moe_bench_hbm_read(FAKE + 8, 1 << 20, 3, ctypes.byref(r), None) == -9
+    assert L.moe_bench_mfma_bf16(100, 3, None, None) == -1
+    assert L.moe_bench_mfma_bf16(1, 3, ctypes.byref(r), None) == -9
+    assert L.moe_bench_mfma_bf16(100, 1, ctypes.byref(r), None) == -9
+
+
 def test_strerror_and_names(lib):
     for code in range(0, -10, -1):
         s = B.strerror(code)
