@@ -431,6 +431,7 @@ def main() -> int:
             B.moe_timing_collect(reset=True)
             B.moe_timing_enable(True)
             fw = 0.0
+            fws = []
             for _ in range(args.steps):
                 w13, w2 = copies[counter[0] % len(copies)]
                 counter[0] += 1
@@ -439,11 +440,13 @@ def main() -> int:
                               workspace=wss[bi])
                 ev1.record()
                 torch.cuda.synchronize()
-                fw += ev0.elapsed_time(ev1)
+                fws.append(ev0.elapsed_time(ev1))
+                fw += fws[-1]
             B.moe_timing_enable(False)
             t2 = B.moe_timing_collect(reset=True)
             # one forward at a time, as a single graph launch
             gfw = 0.0
+            gfws = []
             for _ in range(args.steps):
                 g = graphs[bi][counter[0] % len(copies)]
                 counter[0] += 1
@@ -451,7 +454,8 @@ def main() -> int:
                 g.launch()
                 ev1.record()
                 torch.cuda.synchronize()
-                gfw += ev0.elapsed_time(ev1)
+                gfws.append(ev0.elapsed_time(ev1))
+                gfw += gfws[-1]
             kern = {k: round(v[0] / args.steps * 1e3, 2) for k, v in t2.items()}
             for k, v in kern.items():
                 breakdown[k] = round(breakdown.get(k, 0.0) + v, 2)
@@ -459,7 +463,9 @@ def main() -> int:
             f13_us = kern["ffn13"]
             per_batch.append({
                 "T": w["T"], "us": round(ms * 1e3, 1), "tokens_per_s": round(w["T"] / (ms / 1e3), 1),
+                "us_p10_p50_p90": _percentiles_us(fws),
                 "graph_us": round(gfw / args.steps * 1e3, 1),
+                "graph_us_p10_p50_p90": _percentiles_us(gfws),
                 "touched_experts": w["touched_experts"],
                 "layer_hbm_GBps": round(w["bytes"] / (ms / 1e3) / 1e9, 1),
                 "layer_hbm_frac": round(w["bytes"] / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -511,6 +517,19 @@ def main() -> int:
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+def _percentiles_us(ms_list):
+    """p10, median, p90 of per-forward times (ms in, us out)."""
+    a = sorted(ms_list)
+    if not a:
+        return None
+    def q(f):
+        x = f * (len(a) - 1)
+        i = int(x)
+        j = min(i + 1, len(a) - 1)
+        return (a[i] + (a[j] - a[i]) * (x - i)) * 1e3
+    return [round(q(0.1), 1), round(q(0.5), 1), round(q(0.9), 1)]
 
 
 def load_traffic(workload: str):
