@@ -40,11 +40,7 @@ constexpr int kBigThreads = 64 * kBigWaves;
 constexpr int kBigTokens = 256;  // block size B of this path
 constexpr int kBigRows = 256;    // weight rows per tile
 constexpr int kBigK = 64;        // K elements per stage
-#ifndef MOE_BIG_N
-#define MOE_BIG_N 256
-#endif
-constexpr int kBigN = MOE_BIG_N;  // tokens per workgroup tile: all 256 of the block, or half
-constexpr int kBigHalves = kBigTokens / kBigN;
+constexpr int kBigN = kBigTokens;  // tokens per workgroup tile: the whole block
 constexpr int kBigTA = 8;                      // 16-row weight tiles per wave (128 rows)
 constexpr int kBigNB = kBigN / (16 * kBigWn);  // 16-token tiles per wave
 constexpr int kBigSlots = kBigK / 8;                 // 16-byte slots per LDS row
@@ -55,10 +51,7 @@ constexpr int kBigGroupsB = kBigN / kBigRowsPerGroup / kBigWaves;   // B loads p
 constexpr int kBigLoads = kBigGroups + kBigGroupsB;
 constexpr int kBigOperandBytes = kBigRows * kBigRowBytes;
 constexpr int kBigStageBytes = kBigOperandBytes + kBigN * kBigRowBytes;
-// 256 tokens: two stages (128 KB); 128 tokens: three stages (144 KB), which
-// lets the loads run two stages ahead
-constexpr int kBigStages = kBigN == 256 ? 2 : 3;
-static_assert(kBigN == 256 || kBigN == 128, "tile tokens");
+constexpr int kBigStages = 2;  // 2 x 64 KB of the 160 KB LDS
 static_assert(kBigStages * kBigStageBytes <= 160 * 1024, "stages fit in LDS");
 #ifndef MOE_BIG_ISSUE_FIRST
 #define MOE_BIG_ISSUE_FIRST 1
@@ -242,7 +235,7 @@ __device__ __forceinline__ void big_half(const BigLoader& ld, const uint8_t* cur
 // MFMAs can overlap the next stage's start.
 struct BigRing {
   const BigLoader& ld;
-  uint8_t* const (&buf)[3];
+  uint8_t* const (&buf)[2];
   int wave, arow0, arow_up, brow0;
   bool live;  // the wave's token rows hold at least one real slot (wave-uniform)
 
@@ -278,82 +271,22 @@ struct BigRing {
     mma1<kLive>(f1, acc);
   }
 
-  // three stages: loads run two stages ahead; a step waits until only the
-  // next stage's loads are outstanding (none at the last step).  The steady
-  // loop goes three stages at a time; the issuing steps left over and the
-  // last two stages (which issue nothing) start from a switch on their
-  // buffer.  nst >= 2.
-  template <int b, bool kLive>
-  __device__ __forceinline__ void tail3(BigFrags& f1, BigAcc& acc, int s) const {
-    mma1<kLive>(f1, acc);
-    step<b, false, kBigLoads, kLive>(s, f1, acc);
-    mma1<kLive>(f1, acc);
-    step<(b + 1) % 3, false, 0, kLive>(s + 1, f1, acc);
-  }
-  template <bool kLive>
-  __device__ __forceinline__ void run3(int nst, BigAcc& acc) const {
-    constexpr int L = kBigLoads;
-    BigFrags f1;
-    big_issue(ld, buf[0], 0, wave);
-    big_issue(ld, buf[1], kBigK, wave);
-    const int M = nst - 2;  // stages that issue a later one
-    if (M >= 1) {
-      step<0, true, L, kLive>(0, f1, acc);
-      int s = 1;
-      for (; s + 3 <= M; s += 3) {
-        mma1<kLive>(f1, acc);
-        step<1, true, L, kLive>(s, f1, acc);
-        mma1<kLive>(f1, acc);
-        step<2, true, L, kLive>(s + 1, f1, acc);
-        mma1<kLive>(f1, acc);
-        step<0, true, L, kLive>(s + 2, f1, acc);
-      }
-      const int r = M - s;  // 0, 1 or 2 issuing stages left; s == 1 (mod 3)
-      if (r >= 1) {
-        mma1<kLive>(f1, acc);
-        step<1, true, L, kLive>(s, f1, acc);
-      }
-      if (r >= 2) {
-        mma1<kLive>(f1, acc);
-        step<2, true, L, kLive>(s + 1, f1, acc);
-      }
-      switch (r) {
-        case 0: tail3<1, kLive>(f1, acc, s); break;
-        case 1: tail3<2, kLive>(f1, acc, s + 1); break;
-        default: tail3<0, kLive>(f1, acc, s + 2); break;
-      }
-    } else {
-      step<0, false, L, kLive>(0, f1, acc);
-      mma1<kLive>(f1, acc);
-      step<1, false, 0, kLive>(1, f1, acc);
-    }
-    mma1<kLive>(f1, acc);
-  }
-
-  template <bool kLive>
-  __device__ __forceinline__ void run_as(int nst, BigAcc& acc) const {
-    if constexpr (kBigStages == 2)
-      run2<kLive>(nst, acc);
-    else
-      run3<kLive>(nst, acc);
-  }
   __device__ __forceinline__ void run(int nst, BigAcc& acc) const {
     if (live)
-      run_as<true>(nst, acc);
+      run2<true>(nst, acc);
     else
-      run_as<false>(nst, acc);
+      run2<false>(nst, acc);
   }
 };
 
 #define BIG_BUFFERS(name)                                                                 \
   __shared__ __attribute__((aligned(1024))) uint8_t name##0[kBigStageBytes];              \
   __shared__ __attribute__((aligned(1024))) uint8_t name##1[kBigStageBytes];              \
-  __shared__ __attribute__((aligned(1024))) uint8_t name##2[kBigStages > 2 ? kBigStageBytes : 16]; \
-  uint8_t* const name[3] = {name##0, name##1, name##2}
+  uint8_t* const name[2] = {name##0, name##1}
 
 // ------------------------------------------------------------ W13 + SiLU*mul
-// Tile: channels n0 .. n0+127 (rows: 128 gate, then 128 up) x kBigN tokens
-// (tile b: row block b / kBigHalves, its half b % kBigHalves).
+// Tile: channels n0 .. n0+127 (rows: 128 gate, then 128 up) x the 256
+// tokens of row block b.
 
 __global__ __launch_bounds__(kBigThreads) void ffn13_big_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ w13,
@@ -365,11 +298,10 @@ __global__ __launch_bounds__(kBigThreads) void ffn13_big_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const BigTile tl = big_tile_of(blockIdx.x, gx, gy);
   if (!tl.live) return;  // uniform
-  const int b = tl.b / kBigHalves;
-  const int n_off = (tl.b % kBigHalves) * kBigN;  // first slot of the tile in the block
+  const int b = tl.b;
   if (b * kBigTokens >= *num_padded) return;
   const int32_t* blk = sorted_ids + static_cast<size_t>(b) * kBigTokens;
-  if (blk[n_off] >= A) return;  // real slots come first: this half holds none
+  if (blk[0] >= A) return;  // real slots come first: this block holds none
   const int e = block_expert[b];
   const int n0 = tl.y * 128;
   const size_t two_i = 2 * static_cast<size_t>(I);
@@ -389,7 +321,7 @@ __global__ __launch_bounds__(kBigThreads) void ffn13_big_kernel(
   const int brow = (kBigN / kBigWaves) * wave + lrow;  // token row of B group 0
 #pragma unroll
   for (int q = 0; q < kBigGroupsB; ++q) {
-    const int f = blk[n_off + brow + kBigRowsPerGroup * q];  // pad slot: any valid row (never stored)
+    const int f = blk[brow + kBigRowsPerGroup * q];  // pad slot: any valid row (never stored)
     ld.b[q] = 2 * (static_cast<uint32_t>(f < A ? f / k : 0) * d + (q & 1 ? c_odd : c_even));
   }
   const int wm = wave & 1, wn = wave >> 1;
@@ -400,7 +332,7 @@ __global__ __launch_bounds__(kBigThreads) void ffn13_big_kernel(
     for (int u = 0; u < kBigNB; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // real slots come first: the wave's token rows are all padding iff its first one is
-  const bool live = __builtin_amdgcn_readfirstlane(blk[n_off + (kBigN / kBigWn) * wn]) < A;
+  const bool live = __builtin_amdgcn_readfirstlane(blk[(kBigN / kBigWn) * wn]) < A;
   BigRing{ld, buf, wave, 64 * wm, 128 + 64 * wm, (kBigN / kBigWn) * wn, live}.run(d / kBigK, acc);
 
   // lane: token column r16 of tile u, channels n0 + 64wm + 16t + 4g .. +3
@@ -409,7 +341,7 @@ __global__ __launch_bounds__(kBigThreads) void ffn13_big_kernel(
 #pragma unroll
   for (int u = 0; u < kBigNB; ++u) {
     const size_t row =
-        static_cast<size_t>(b) * kBigTokens + n_off + (kBigN / kBigWn) * wn + 16 * u + r16;
+        static_cast<size_t>(b) * kBigTokens + (kBigN / kBigWn) * wn + 16 * u + r16;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       uint32_t packed[2];
@@ -439,11 +371,10 @@ __global__ __launch_bounds__(kBigThreads) void ffn2_big_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const BigTile tl = big_tile_of(blockIdx.x, gx, gy);
   if (!tl.live) return;
-  const int b = tl.b / kBigHalves;
-  const int n_off = (tl.b % kBigHalves) * kBigN;
+  const int b = tl.b;
   if (b * kBigTokens >= *num_padded) return;
   const int32_t* blk = sorted_ids + static_cast<size_t>(b) * kBigTokens;
-  if (blk[n_off] >= A) return;
+  if (blk[0] >= A) return;
   const int e = block_expert[b];
   const int n0 = tl.y * kBigRows;
   // split z of K = I (grid z): the combine adds the splits in a fixed order
@@ -462,7 +393,7 @@ __global__ __launch_bounds__(kBigThreads) void ffn2_big_kernel(
   ld.a_step = 2 * (2 * kBigRowsPerGroup * I);
   // h rows of the tile; pad slots hold no token and their columns are never stored
   const int brow = (kBigN / kBigWaves) * wave + lrow;
-  ld.rb = big_rsrc(h + (static_cast<size_t>(b) * kBigTokens + n_off) * I, static_cast<size_t>(kBigN) * I * 2);
+  ld.rb = big_rsrc(h + (static_cast<size_t>(b) * kBigTokens) * I, static_cast<size_t>(kBigN) * I * 2);
 #pragma unroll
   for (int q = 0; q < kBigGroupsB; ++q)
     ld.b[q] = 2 * (static_cast<uint32_t>(brow + kBigRowsPerGroup * q) * I + k_begin +
@@ -475,7 +406,7 @@ __global__ __launch_bounds__(kBigThreads) void ffn2_big_kernel(
     for (int u = 0; u < kBigNB; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // A rows 128*wm .. +127: eight consecutive 16-row tiles
-  const bool live = __builtin_amdgcn_readfirstlane(blk[n_off + (kBigN / kBigWn) * wn]) < A;
+  const bool live = __builtin_amdgcn_readfirstlane(blk[(kBigN / kBigWn) * wn]) < A;
   BigRing{ld, buf, wave, 128 * wm, 128 * wm + 64, (kBigN / kBigWn) * wn, live}.run(nst, acc);
 
   // lane: token column r16 of tile u, channels n0 + 128wm + 16t + 4g .. +3
@@ -483,7 +414,7 @@ __global__ __launch_bounds__(kBigThreads) void ffn2_big_kernel(
   const int g = lane >> 4;
 #pragma unroll
   for (int u = 0; u < kBigNB; ++u) {
-    const int f = blk[n_off + (kBigN / kBigWn) * wn + 16 * u + r16];
+    const int f = blk[(kBigN / kBigWn) * wn + 16 * u + r16];
     if (f < A) {
       const float gate = topk_w[f];
       float* yrow = y + static_cast<size_t>(f) * d + n0 + 128 * wm + 4 * g;
@@ -513,7 +444,7 @@ static int big_grid(int gx, int gy) {
 hipError_t launch_ffn13_big(const FfnArgs& a, hipStream_t s) {
   if (a.B != kBigTokens || a.w_dtype != kDtypeBF16 || !big_gemm_fits(a.T, a.d, a.I))
     return hipErrorInvalidValue;
-  const int gx = a.cap / kBigTokens * kBigHalves, gy = a.I / 128;
+  const int gx = a.cap / kBigTokens, gy = a.I / 128;
   ffn13_big_kernel<<<big_grid(gx, gy), kBigThreads, 0, s>>>(
       static_cast<const bf16_t*>(a.x), static_cast<const bf16_t*>(a.w13), a.sorted_ids,
       a.block_expert, a.num_padded, static_cast<bf16_t*>(a.h), a.d, a.I, a.k, a.A, gx, gy);
@@ -526,7 +457,7 @@ hipError_t launch_ffn2_big(const FfnArgs& a, hipStream_t s) {
       a.ksplit % (2 * kBigK) != 0 || a.splits < 1 ||
       static_cast<int64_t>(a.splits - 1) * a.ksplit >= a.I)
     return hipErrorInvalidValue;
-  const int gx = a.cap / kBigTokens * kBigHalves, gy = a.d / kBigRows;
+  const int gx = a.cap / kBigTokens, gy = a.d / kBigRows;
   ffn2_big_kernel<<<dim3(big_grid(gx, gy), 1, a.splits), kBigThreads, 0, s>>>(
       static_cast<const bf16_t*>(a.h), static_cast<const bf16_t*>(a.w2), a.topk_w, a.sorted_ids,
       a.block_expert, a.num_padded, a.y_part, a.d, a.I, a.A, a.ksplit, gx, gy);
