@@ -13,6 +13,8 @@ from .moe_oracle import (  # noqa: F401
     expert_ffn,
     gate_weights,
     moe_forward,
+    mx_dequantize,
+    mx_quantize,
     router_logits,
     select_topk,
     silu,

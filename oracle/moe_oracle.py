@@ -34,7 +34,11 @@ router, the expert network or the FP8 format; the readings taken here are:
   * the gate weight scales the expert output; a token's output is the sum over
     its k slots in rank order;
   * FP8 weights are OCP e4m3fn bytes times an fp32 scale per output channel
-    (or one per expert matrix); activations stay bf16;
+    (or one per expert matrix); activations stay bf16, or, in the optional
+    W8A8 mode ([P2] §fp8: FP8 scaling fused with the matrix product), are
+    quantised to e4m3fn in blocks of 32 consecutive values of a row with one
+    power-of-two scale per block (the OCP microscaling layout): x per token
+    before W13, the SwiGLU output h per routing slot before W2;
   * regrouping: per-expert counts, each expert's group padded to a multiple of
     a block size B, groups laid out in expert order, inside a group the flat
     slot ids f = t*k + j ascending, pad slots hold the sentinel A = T*k.
@@ -58,7 +62,12 @@ under ``-m "not gpu"``):
       evaluated with torch.nn.functional.silu in fp64; scalar closed form;
   moe_forward .................. dense brute force (every expert on every
       token, masked by the selection); k = E with W_gate = 0 gives the mean
-      of all experts; zero tokens; idle experts.
+      of all experts; zero tokens; idle experts; the W8A8 mode against a
+      dense brute force that quantises with torch's e4m3fn cast;
+  mx_quantize .................. brute force over all 256 codes (nearest,
+      ties to even); torch's float8_e4m3fn cast of the scaled, clamped
+      values; representable values round-trip; the block maximum lands in
+      [256, 512) before clamping; zero blocks; saturation.
 No function here is "parity unpinned".
 """
 
@@ -79,6 +88,8 @@ __all__ = [
     "align",
     "silu",
     "expert_ffn",
+    "mx_quantize",
+    "mx_dequantize",
     "moe_forward",
 ]
 
@@ -260,6 +271,73 @@ def align(ids: np.ndarray, num_experts: int, block_m: int) -> dict:
 
 
 # --------------------------------------------------------------------------
+# Block-scaled FP8 activations (the W8A8 mode; [P2] §fp8)
+# --------------------------------------------------------------------------
+
+MX_BLOCK = 32          # values sharing one scale
+E4M3_MAX = 448.0       # largest finite e4m3fn value
+E4M3_EMAX = 8          # its exponent: 448 = 1.75 * 2^8
+
+# the 127 non-negative finite e4m3fn values, ascending with their codes
+# (code 0x7F is NaN); codes 0x00..0x7E are already in ascending value order
+_E4M3_POS = np.array([_e4m3fn_value(c) for c in range(0x7F)], dtype=np.float64)
+
+
+def _e4m3fn_nearest(y: np.ndarray) -> np.ndarray:
+    """e4m3fn code nearest to each y with |y| <= 448; ties to the even code."""
+    pos = _E4M3_POS
+    a = np.abs(y)
+    hi = np.clip(np.searchsorted(pos, a, side="left"), 0, pos.size - 1)
+    lo = np.clip(hi - 1, 0, pos.size - 1)
+    dlo = np.abs(a - pos[lo])
+    dhi = np.abs(pos[hi] - a)
+    pick = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+    codes = pick.astype(np.uint8)
+    neg = np.signbit(y)                    # the sign is kept, also on zero
+    return np.where(neg, codes | np.uint8(0x80), codes).astype(np.uint8)
+
+
+def mx_quantize(v, block: int = MX_BLOCK):
+    """Quantise each row of v [rows, K] (K a multiple of `block`) to e4m3fn
+    codes with one power-of-two scale per block of consecutive values.
+
+    For each block: amax = max |v|; the scale is X = 2^(floor(log2 amax) - 8)
+    (8 is the exponent of e4m3fn's largest value), or X = 1 when amax = 0;
+    each value becomes the e4m3fn code nearest to clamp(v / X, -448, 448),
+    ties to the even code.  Returns (codes uint8 [rows, K], exps int32
+    [rows, K / block]) with X = 2^exps.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    rows, K = v.shape
+    if K % block:
+        raise ValueError("K must be a multiple of the block")
+    vb = v.reshape(rows, K // block, block)
+    amax = np.abs(vb).max(axis=2)
+    exps = np.zeros(amax.shape, dtype=np.int32)
+    nz = amax > 0
+    if nz.any():
+        # floor(log2 amax) from the float's own exponent (exact at powers of two)
+        _, e = np.frexp(amax[nz])          # amax = m * 2^e, m in [0.5, 1)
+        exps[nz] = (e - 1).astype(np.int32) - E4M3_EMAX
+    y = vb / np.ldexp(1.0, exps)[:, :, None]
+    y = np.clip(y, -E4M3_MAX, E4M3_MAX)
+    codes = _e4m3fn_nearest(y.reshape(rows, K))
+    return codes, exps
+
+
+def mx_dequantize(codes, exps, block: int = MX_BLOCK) -> np.ndarray:
+    """codes [rows, K], exps [rows, K / block] -> values, exactly."""
+    vals = decode_e4m3fn(codes)
+    rows, K = vals.shape
+    sc = np.ldexp(1.0, np.asarray(exps, dtype=np.int64))
+    return (vals.reshape(rows, K // block, block) * sc[:, :, None]).reshape(rows, K)
+
+
+def _mx_roundtrip(v):
+    return mx_dequantize(*mx_quantize(v))
+
+
+# --------------------------------------------------------------------------
 # Expert computation ([P2] §fused: "a szakértői hálózatok számításai")
 # --------------------------------------------------------------------------
 
@@ -270,17 +348,21 @@ def silu(z: np.ndarray) -> np.ndarray:
         return z / (1.0 + np.exp(-z))
 
 
-def expert_ffn(xrows: np.ndarray, w13: np.ndarray, w2: np.ndarray) -> np.ndarray:
+def expert_ffn(xrows: np.ndarray, w13: np.ndarray, w2: np.ndarray, h_quant=None) -> np.ndarray:
     """One expert's SwiGLU network on a batch of rows.
 
     xrows [n, d]; w13 [2I, d] with rows 0..I-1 the gate projection W1 and rows
     I..2I-1 the up projection W3; w2 [d, I].  Returns [n, d]:
-    W2 . (SiLU(W1 x) * (W3 x)) for every row x.
+    W2 . (SiLU(W1 x) * (W3 x)) for every row x.  `h_quant`, when given, maps
+    the rows of SiLU(W1 x) * (W3 x) to the values W2 sees (the W8A8 mode's
+    quantise-dequantise step).
     """
     I = w13.shape[0] // 2
     g = xrows @ w13[:I].T
     u = xrows @ w13[I:].T
     h = silu(g) * u
+    if h_quant is not None:
+        h = h_quant(h)
     return h @ w2.T
 
 
@@ -290,7 +372,7 @@ def expert_ffn(xrows: np.ndarray, w13: np.ndarray, w2: np.ndarray) -> np.ndarray
 
 def moe_forward(x, w_gate, w13, w2, top_k: int, *, act_fmt: str = "bf16",
                 w_fmt: str = "bf16", s13=None, s2=None, scale_mode: str | None = None,
-                block_m: int = 64, logits=None) -> dict:
+                block_m: int = 64, logits=None, act_quant: str | None = None) -> dict:
     """The MoE layer computed as a plain loop over experts.
 
     x: [T, d] raw activations (uint16 bf16 patterns or float32);
@@ -300,7 +382,10 @@ def moe_forward(x, w_gate, w13, w2, top_k: int, *, act_fmt: str = "bf16",
       fetch experts lazily -- only experts that receive tokens are read);
     s13, s2: e4m3fn scales, [E, 2I] and [E, d] per channel or [E] per tensor;
     logits: optional [T, E] router logits to use instead of computing them
-      (used to compare routing given identical logits).
+      (used to compare routing given identical logits);
+    act_quant: None (activations as given) or "mx_e4m3" (the W8A8 mode: the
+      router still sees x as given; the experts see x quantised per token
+      and h quantised per routing slot by mx_quantize, then dequantised).
 
     Steps: (1) logits, (2) top-k selection and gates, (3) regrouping by expert,
     (4) for each expert, gather its tokens, run its SwiGLU network and scale
@@ -335,6 +420,10 @@ def moe_forward(x, w_gate, w13, w2, top_k: int, *, act_fmt: str = "bf16",
     if w_fmt == "e4m3fn":
         if scale_mode not in ("channel", "tensor"):
             raise ValueError("e4m3fn weights need scale_mode 'channel' or 'tensor'")
+    if act_quant not in (None, "mx_e4m3"):
+        raise ValueError(f"unknown act_quant {act_quant!r}")
+    xe = _mx_roundtrip(xv) if (act_quant and T) else xv   # what the experts see
+    hq = _mx_roundtrip if act_quant else None
     for e in range(E):
         n = int(al["counts"][e])
         if n == 0:
@@ -351,7 +440,7 @@ def moe_forward(x, w_gate, w13, w2, top_k: int, *, act_fmt: str = "bf16",
         W2e = decode_weights(w2[e], w_fmt, sc2)
         if W13e.shape[1] != d or W2e.shape[0] != d or W13e.shape[0] != 2 * W2e.shape[1]:
             raise ValueError("weight shapes do not match x / each other")
-        Y = expert_ffn(xv[ts], W13e, W2e)
+        Y = expert_ffn(xe[ts], W13e, W2e, hq)
         y_slot[fs] = flat_gates[fs][:, None] * Y
 
     out = np.zeros((T, d), dtype=np.float64)

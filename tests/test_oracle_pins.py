@@ -387,3 +387,123 @@ def test_given_logits_override_routing():
     r = oracle.moe_forward(x, wg, w13, w2, k, act_fmt="f32", w_fmt="f32", block_m=4, logits=lg)
     assert np.all(r["ids"] == [3, 2])
     assert list(r["counts"]) == [0, 0, T, T]
+
+
+# ---------------------------------------------------------------- W8A8 mode: block-scaled e4m3fn
+
+def _e4m3_brute(y):
+    """Nearest e4m3fn code to y (|y| <= 448) over all 256 codes; ties to the
+    even code; the sign of y is kept (also on zero)."""
+    best, bd = None, None
+    for c in range(256):
+        if c & 0x7F == 0x7F:
+            continue
+        v = oracle.decode_e4m3fn(np.array([c], np.uint8))[0]
+        if (c & 0x80) != (0x80 if math.copysign(1.0, y) < 0 else 0):
+            continue
+        dd = abs(v - y)
+        if bd is None or dd < bd or (dd == bd and c % 2 == 0):
+            best, bd = c, dd
+    return best
+
+
+def _block_exp(block):
+    amax = max(abs(float(v)) for v in block)
+    return 0 if amax == 0 else math.frexp(amax)[1] - 1 - 8
+
+
+def _mx_rows():
+    rng = np.random.default_rng(11)
+    rows = [rng.standard_normal(64) * s for s in (1.0, 1e-3, 300.0)]
+    rows.append(np.concatenate([np.zeros(32), rng.standard_normal(32)]))   # a zero block
+    r = rng.standard_normal(64)
+    r[5], r[40] = 2.0, -1.99                                             # amax at / below 2^1
+    rows.append(r)
+    return np.stack(rows)
+
+
+def test_mx_quantize_brute_force():
+    v = _mx_rows()
+    codes, exps = oracle.mx_quantize(v)
+    assert codes.shape == v.shape and exps.shape == (v.shape[0], 2)
+    for i in range(v.shape[0]):
+        for b in range(2):
+            blk = v[i, 32 * b:32 * b + 32]
+            assert exps[i, b] == _block_exp(blk)
+            X = math.ldexp(1.0, int(exps[i, b]))
+            for j in range(32):
+                y = min(max(blk[j] / X, -448.0), 448.0)
+                assert codes[i, 32 * b + j] == _e4m3_brute(y), (i, b, j)
+
+
+def test_mx_quantize_matches_torch_cast():
+    v = np.random.default_rng(12).standard_normal((16, 256)) * np.logspace(-4, 4, 16)[:, None]
+    codes, exps = oracle.mx_quantize(v)
+    X = np.ldexp(1.0, np.repeat(exps, 32, axis=1))
+    y = np.clip(v / X, -448.0, 448.0)
+    ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codes, ref)
+
+
+def test_mx_block_maximum_range_zero_block_and_saturation():
+    v = _mx_rows()
+    codes, exps = oracle.mx_quantize(v)
+    amax = np.abs(v.reshape(v.shape[0], 2, 32)).max(axis=2)
+    nz = amax > 0
+    ratio = amax[nz] / np.ldexp(1.0, exps[nz])
+    assert np.all((ratio >= 256) & (ratio < 512))
+    assert exps[3, 0] == 0 and np.all(codes[3, :32] == 0)                 # zero block
+    assert exps[4, 0] == 1 - 8 and exps[4, 1] == 0 - 8
+    # -1.99 / 2^-8 = -509.4 saturates to -448 (code 0xFE)
+    assert codes[4, 40] == 0xFE and oracle.decode_e4m3fn(codes[4:5, 40:41])[0, 0] == -448.0
+
+
+def test_mx_representable_values_round_trip():
+    rng = np.random.default_rng(13)
+    c = rng.integers(0, 0x7F, size=(4, 64), dtype=np.uint8) | (rng.integers(0, 2, size=(4, 64), dtype=np.uint8) << 7)
+    c[:, 0], c[:, 32] = 0x7E, 0xFE                      # each block holds +-448: X = 2^s exactly
+    for s in (-6, 0, 5):
+        v = oracle.decode_e4m3fn(c) * math.ldexp(1.0, s)
+        codes, exps = oracle.mx_quantize(v)
+        assert np.all(exps == s)
+        assert np.array_equal(oracle.decode_e4m3fn(codes), oracle.decode_e4m3fn(c))
+        assert np.array_equal(oracle.mx_dequantize(codes, exps), v)
+
+
+def _torch_mx(rows):
+    """Block quantise-dequantise written with torch's e4m3fn cast and
+    math.frexp, independently of the oracle's quantiser."""
+    out = np.empty_like(rows)
+    for i in range(rows.shape[0]):
+        for b in range(rows.shape[1] // 32):
+            blk = rows[i, 32 * b:32 * b + 32]
+            X = math.ldexp(1.0, _block_exp(blk))
+            y = torch.from_numpy(np.clip(blk / X, -448.0, 448.0)).to(torch.float8_e4m3fn).double()
+            out[i, 32 * b:32 * b + 32] = y.numpy() * X
+    return out
+
+
+def test_layer_w8a8_matches_dense_bruteforce():
+    from mixture_experts_moe_amd import synth
+    inp = synth.make_inputs("fp8", T=7, d=64, E=6, k=2, I=64)
+    kw = synth.to_oracle(inp)
+    r = oracle.moe_forward(**kw, block_m=16, act_quant="mx_e4m3")
+    deq13 = (inp.w13.view(torch.float8_e4m3fn).double() * inp.s13.double()[:, :, None]).numpy()
+    deq2 = (inp.w2.view(torch.float8_e4m3fn).double() * inp.s2.double()[:, :, None]).numpy()
+    x = inp.x.double().numpy()
+    xq = _torch_mx(x)
+    lg = x @ inp.w_gate.double().numpy().T
+    I = deq2.shape[2]
+    out = np.zeros_like(x)
+    for t in range(x.shape[0]):
+        sel = _brute_topk(list(lg[t]), 2)
+        g = scipy.special.softmax(lg[t, sel])
+        for j, e in enumerate(sel):
+            xt = torch.from_numpy(xq[t:t + 1])
+            gate = xt @ torch.from_numpy(deq13[e, :I]).T
+            up = xt @ torch.from_numpy(deq13[e, I:]).T
+            h = _torch_mx((torch.nn.functional.silu(gate) * up).numpy())
+            out[t] += g[j] * (h @ deq2[e].T)[0]
+    assert _rel(r["out"], out) < 1e-12
+    # and it is a different layer from the weight-only one (the quantisation shows)
+    assert _rel(oracle.moe_forward(**kw, block_m=16)["out"], out) > 1e-4
