@@ -67,7 +67,8 @@ under ``-m "not gpu"``):
   mx_quantize .................. brute force over all 256 codes (nearest,
       ties to even); torch's float8_e4m3fn cast of the scaled, clamped
       values; representable values round-trip; the block maximum lands in
-      [256, 512) before clamping; zero blocks; saturation.
+      [256, 512) before clamping; zero blocks; saturation; a block too small
+      for the scale it asks for (the E8M0 range stops at 2^-127).
 No function here is "parity unpinned".
 """
 
@@ -277,6 +278,7 @@ def align(ids: np.ndarray, num_experts: int, block_m: int) -> dict:
 MX_BLOCK = 32          # values sharing one scale
 E4M3_MAX = 448.0       # largest finite e4m3fn value
 E4M3_EMAX = 8          # its exponent: 448 = 1.75 * 2^8
+E8M0_EMIN, E8M0_EMAX = -127, 127   # exponents an 8-bit E8M0 scale holds (code 255 is NaN)
 
 # the 127 non-negative finite e4m3fn values, ascending with their codes
 # (code 0x7F is NaN); codes 0x00..0x7E are already in ascending value order
@@ -302,10 +304,11 @@ def mx_quantize(v, block: int = MX_BLOCK):
     codes with one power-of-two scale per block of consecutive values.
 
     For each block: amax = max |v|; the scale is X = 2^(floor(log2 amax) - 8)
-    (8 is the exponent of e4m3fn's largest value), or X = 1 when amax = 0;
-    each value becomes the e4m3fn code nearest to clamp(v / X, -448, 448),
-    ties to the even code.  Returns (codes uint8 [rows, K], exps int32
-    [rows, K / block]) with X = 2^exps.
+    (8 is the exponent of e4m3fn's largest value), or X = 1 when amax = 0,
+    with the exponent kept inside E8M0's range [-127, 127] (the scale is an
+    8-bit exponent); each value becomes the e4m3fn code nearest to
+    clamp(v / X, -448, 448), ties to the even code.  Returns (codes uint8
+    [rows, K], exps int32 [rows, K / block]) with X = 2^exps.
     """
     v = np.asarray(v, dtype=np.float64)
     rows, K = v.shape
@@ -318,7 +321,7 @@ def mx_quantize(v, block: int = MX_BLOCK):
     if nz.any():
         # floor(log2 amax) from the float's own exponent (exact at powers of two)
         _, e = np.frexp(amax[nz])          # amax = m * 2^e, m in [0.5, 1)
-        exps[nz] = (e - 1).astype(np.int32) - E4M3_EMAX
+        exps[nz] = np.clip((e - 1).astype(np.int32) - E4M3_EMAX, E8M0_EMIN, E8M0_EMAX)
     y = vb / np.ldexp(1.0, exps)[:, :, None]
     y = np.clip(y, -E4M3_MAX, E4M3_MAX)
     codes = _e4m3fn_nearest(y.reshape(rows, K))

@@ -458,6 +458,24 @@ def test_mx_block_maximum_range_zero_block_and_saturation():
     assert codes[4, 40] == 0xFE and oracle.decode_e4m3fn(codes[4:5, 40:41])[0, 0] == -448.0
 
 
+def test_mx_scale_exponent_stays_in_e8m0_range():
+    # amax = 2^-130 would ask for X = 2^-138; E8M0 stops at 2^-127, so the
+    # block's values are quantised at that scale: 2^-130 / 2^-127 = 0.125
+    # (exact in e4m3fn), 2^-137 / 2^-127 = 2^-10 rounds to the subnormal
+    # 2^-9 (code 1) or 0 -- the tie 2^-10 goes to the even code, 0.
+    v = np.zeros((2, 32))
+    v[0, :] = math.ldexp(1.0, -130)
+    v[1, 0], v[1, 1] = math.ldexp(1.0, -130), -math.ldexp(1.0, -137)
+    codes, exps = oracle.mx_quantize(v)
+    assert np.all(exps == -127)
+    vals = oracle.decode_e4m3fn(codes)
+    assert np.all(vals[0] == 0.125)
+    assert vals[1, 0] == 0.125 and vals[1, 1] == 0.0 and codes[1, 1] == 0x80
+    # at the top, 2^120 (exponent 112) is still inside the range
+    _, e = oracle.mx_quantize(np.full((1, 32), math.ldexp(1.0, 120)))
+    assert e[0, 0] == 112
+
+
 def test_mx_representable_values_round_trip():
     rng = np.random.default_rng(13)
     c = rng.integers(0, 0x7F, size=(4, 64), dtype=np.uint8) | (rng.integers(0, 2, size=(4, 64), dtype=np.uint8) << 7)
