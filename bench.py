@@ -32,16 +32,20 @@ if ROOT not in sys.path:
 
 METRIC = "fused-MoE tokens/s + achieved HBM GB/s (decode) / MFMA TFLOP/s (prefill)"
 HBM_PEAK_GBS = 8000.0
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "e4m3fn": 2500.0, "f32": 157.3}  # W8A16 computes in bf16
+# dense MFMA peaks by what the expert products compute in: W8A16 widens its
+# e4m3fn weights to bf16; the W8A8 mode multiplies e4m3fn by e4m3fn
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "e4m3fn": 2500.0, "f32": 157.3, "mx_e4m3": 5000.0}
 WORKLOAD_BATCHES = {
     "decode_bf16": (1, 8, 32, 64),
     "prefill_bf16": (4096,),
+    "prefill_w8a8": (4096,),
     "fp8": (64, 2048),
     "skew": (512,),
     "tiny_fp32": (16,),
 }
 # Oracle sample per workload: (batch T, number of its tokens run on the CPU)
-CPU_SAMPLE = {"decode_bf16": (64, 64), "prefill_bf16": (4096, 16), "fp8": (2048, 4),
+CPU_SAMPLE = {"decode_bf16": (64, 64), "prefill_bf16": (4096, 16), "prefill_w8a8": (4096, 16),
+              "fp8": (2048, 4),
               "skew": (512, 64), "tiny_fp32": (16, 16)}
 
 
@@ -102,7 +106,8 @@ def copy_calibration(nbytes: int, reps: int = 5) -> None:
 def alg_work(inp, ids, k) -> dict:
     """Algorithmic bytes and flops of one forward, from the realised routing.
     Bytes: weights (and fp8 scales) of the touched experts, W_gate, x, out.
-    ffn13 bytes: touched experts' W13 (+ scales), x, h written for real slots."""
+    ffn13 bytes: touched experts' W13 (+ scales), x, h written for real slots
+    (in the W8A8 mode x and h are e4m3fn codes plus one exponent byte per 32)."""
     import torch
     T, d, E, I = inp.T, inp.d, inp.E, inp.I
     wb = {"f32": 4, "bf16": 2, "e4m3fn": 1}[inp.w]
@@ -117,7 +122,8 @@ def alg_work(inp, ids, k) -> dict:
         "T": T, "touched_experts": touched,
         "bytes": w13 + w2 + E * d * 4 + T * d * 2 * ab,
         "flops": A * 6 * d * I + 2 * T * d * E,
-        "ffn13_bytes": w13 + T * d * ab + A * I * ab,
+        "ffn13_bytes": w13 + (T * d * 33 // 32 + A * I * 33 // 32 if inp.act_quant
+                              else T * d * ab + A * I * ab),
         "ffn13_flops": A * 4 * d * I,
     }
 
@@ -318,7 +324,8 @@ def main() -> int:
     outs = [torch.empty_like(i.x) for i in inputs]
     wss = []
     for i in inputs:
-        desc = B.make_desc(i.T, i.d, i.E, i.I, B._act_code(i.x), B._w_code(i.w13))
+        desc = B.make_desc(i.T, i.d, i.E, i.I, B._act_code(i.x), B._w_code(i.w13),
+                           act_quant=i.act_quant)
         desc.block_m = args.block_m
         wss.append(torch.empty(max(B.moe_workspace_bytes(desc, i.top_k, True), 1), dtype=torch.uint8, device=dev))
     torch.cuda.synchronize()
@@ -331,7 +338,7 @@ def main() -> int:
             w13, w2 = copies[counter[0] % len(copies)]
             counter[0] += 1
             B.moe_forward(i.x, i.w_gate, w13, w2, i.top_k, sc, outs[bi], block_m=args.block_m,
-                          workspace=wss[bi])
+                          workspace=wss[bi], act_quant=i.act_quant)
 
     # realised routing -> algorithmic work per forward
     work = []
@@ -367,9 +374,10 @@ def main() -> int:
     f13_bytes_step = sum(w["ffn13_bytes"] for w in work)
     f13_flops_step = sum(w["ffn13_flops"] for w in work)
     f13_ms_step = ffn13_ms / args.steps
-    mfma_bound = wl == "prefill_bf16"
+    mfma_bound = wl in ("prefill_bf16", "prefill_w8a8")
+    compute = base.act_quant or base.w
     if mfma_bound:
-        peak = MFMA_PEAK_TFLOPS[base.w]
+        peak = MFMA_PEAK_TFLOPS[compute]
         achieved = f13_flops_step / (f13_ms_step / 1e3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4)}
@@ -382,7 +390,9 @@ def main() -> int:
     # over 1 GiB (past the 256 MB last-level cache), or the big tile's LDS-fed
     # MFMA loop on random bf16
     try:
-        if mfma_bound:
+        if mfma_bound and compute == "mx_e4m3":
+            att = B.bench_mfma_fp8(iters=4096, reps=4, device=dev)
+        elif mfma_bound:
             att = B.bench_mfma_bf16(iters=4096, reps=4, device=dev)
         else:
             probe = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -401,7 +411,7 @@ def main() -> int:
     # the same step as one recorded graph per forward (moe_graph_*): one
     # launch per forward, weights rotated through the same copies
     graphs = [[B.MoeGraph(i.x, i.w_gate, w13, w2, i.top_k, sc, out=outs[bi], block_m=args.block_m,
-                          workspace=wss[bi]) for (w13, w2) in copies]
+                          workspace=wss[bi], act_quant=i.act_quant) for (w13, w2) in copies]
               for bi, i in enumerate(inputs)]
     gcount = [0]
 
@@ -437,7 +447,7 @@ def main() -> int:
                 counter[0] += 1
                 ev0.record()
                 B.moe_forward(i.x, i.w_gate, w13, w2, i.top_k, sc, outs[bi], block_m=args.block_m,
-                              workspace=wss[bi])
+                              workspace=wss[bi], act_quant=i.act_quant)
                 ev1.record()
                 torch.cuda.synchronize()
                 fws.append(ev0.elapsed_time(ev1))
@@ -493,13 +503,13 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if base.w == "f32" else "bf16",
+        "dtype": {"f32": "f32", "mx_e4m3": "e4m3fn"}.get(compute, "bf16"),
         "data": "synthetic (seeded Gaussian inputs and random-init weights; no trained model)",
         "config": {
             "workload": wl,
             "batches_T": list(batches),
             "hidden": base.d, "experts": base.E, "top_k": base.top_k, "intermediate": base.I,
-            "act": base.act, "weights": base.w,
+            "act": base.act, "weights": base.w, "act_quant": base.act_quant,
             "tokens_per_step": tokens,
             "alg_bytes_per_step": bytes_step,
             "alg_flops_per_step": flops_step,

@@ -48,7 +48,8 @@
  * Supported (act, weight) pairs: (F32, F32), (BF16, BF16), (BF16, E4M3FN).
  * E4M3FN weights are OCP e4m3fn bytes; value = decoded byte * fp32 scale, the
  * scale given per output channel (s13 [E, 2I], s2 [E, d]) or per expert
- * matrix (s13 [E], s2 [E]).  Activations stay bf16 (weight-only FP8).
+ * matrix (s13 [E], s2 [E]).  Activations stay bf16 (weight-only FP8) unless
+ * desc->act_quant selects the W8A8 mode (MOE_ACT_MX_E4M3 below).
  * Limits: d and I multiples of 64 in [64, 2^19]; 1 <= E <= 1024;
  * 1 <= top_k <= min(E, 64);
  * T * top_k < 2^30; block_m in {0 (library default), 16, 32, 64, 128, 256};
@@ -88,6 +89,18 @@ extern "C" {
 #define MOE_DTYPE_BF16 1
 #define MOE_DTYPE_E4M3FN 2
 
+/* Activations seen by the expert products.  MOE_ACT_MX_E4M3 (the W8A8 mode;
+ * Hungarian page, section "FP8 esetén ...": FP8 scaling fused with the
+ * matrix product) quantises x per token before W13 and h per routing slot
+ * before W2 to e4m3fn in blocks of 32 consecutive values of a row, each block
+ * with one power-of-two scale 2^(floor(log2 amax) - 8) (at least 2^-127; 1
+ * for an all-zero block), values rounded to nearest even after clamping to
+ * +-448.  Requires bf16 activations, e4m3fn weights, block_m 0 or 256 (0
+ * means 256 here), d and I multiples of 256, 2*I*d and T*d under 2^31.  The
+ * router still sees x as given. */
+#define MOE_ACT_AS_IS 0
+#define MOE_ACT_MX_E4M3 1
+
 #define MOE_SCALE_NONE 0         /* F32 / BF16 weights                       */
 #define MOE_SCALE_PER_TENSOR 1   /* one fp32 scale per expert matrix: [E]    */
 #define MOE_SCALE_PER_CHANNEL 2  /* one per output row: [E,2I] and [E,d]     */
@@ -102,7 +115,7 @@ typedef struct moe_desc {
   int32_t act_dtype;     /* MOE_DTYPE_F32 / _BF16    */
   int32_t weight_dtype;  /* MOE_DTYPE_F32/_BF16/_E4M3FN */
   int32_t block_m;       /* 0 or 16/32/64/128/256    */
-  int32_t reserved;      /* must be 0                */
+  int32_t act_quant;     /* MOE_ACT_AS_IS or MOE_ACT_MX_E4M3 */
 } moe_desc;
 
 /* FP8 weight scales (device pointers, fp32).  Pass NULL (or mode
@@ -206,9 +219,19 @@ MOE_API int moe_expert_ffn(const moe_desc* desc, const void* x, const void* w13,
                            void* out, void* workspace, size_t workspace_bytes,
                            void* stream);
 
-/* ---- diagnostics ---- */
+/* Activation quantisation of the W8A8 mode: the step moe_forward and
+ * moe_expert_ffn run on x before W13 when desc->act_quant is
+ * MOE_ACT_MX_E4M3 (Hungarian page, section "FP8 esetén ...": the FP8
+ * scaling of the activations).  From x [T, d] bf16 writes codes [T, d]
+ * (e4m3fn bytes) and exps [T, d/32] (E8M0 bytes: block j of row t is scaled
+ * by 2^(exps[t, j] - 127)) by the rule stated at MOE_ACT_MX_E4M3; a value
+ * is codes * 2^(exps - 127).  desc must be a valid descriptor with
+ * act_quant = MOE_ACT_MX_E4M3 (else MOE_ERR_BAD_ARG); its E, I and weight
+ * dtype are only validated.  Caller-owned device buffers, asynchronous on
+ * `stream`. */
+MOE_API int moe_quantize_act(const moe_desc* desc, const void* x, uint8_t* codes,
+                             uint8_t* exps, void* stream);
 
-/* Static text for a status code (never NULL). */
 /* A captured forward: moe_forward's launch sequence for one desc and one
  * set of buffers, recorded once into a HIP graph and replayed with a single
  * launch per step.  The pages' fused operation replaces a sequence of
@@ -238,6 +261,10 @@ MOE_API int moe_graph_create(const moe_desc* desc, const void* x, const float* w
 MOE_API int moe_graph_launch(moe_graph* graph, void* stream);
 MOE_API int moe_graph_destroy(moe_graph* graph);
 
+/* ---- diagnostics ---- */
+
+/* Static text for a status code (never NULL). */
+
 MOE_API const char* moe_strerror(int status);
 
 /* Kernel timing.  Kernels of the kinds set in the mask given to
@@ -252,7 +279,8 @@ MOE_API const char* moe_strerror(int status);
 #define MOE_KERNEL_FFN13 3
 #define MOE_KERNEL_FFN2 4
 #define MOE_KERNEL_COMBINE 5
-#define MOE_KERNEL_COUNT 6
+#define MOE_KERNEL_QUANT_X 6  /* W8A8 mode: x to block-scaled e4m3fn */
+#define MOE_KERNEL_COUNT 7
 
 MOE_API int moe_timing_enable(int kind_mask);  /* MOE_ERR_BAD_ARG if out of range */
 #define MOE_TIMING_ALL ((1 << MOE_KERNEL_COUNT) - 1)

@@ -1,5 +1,5 @@
 /*
- * moe_bench.h -- attainable rates of the GPU for the two bounds the fused
+ * moe_bench.h -- attainable rates of the GPU for the bounds the fused
  * MoE layer's kernels meet, measured on the device itself, so that a
  * kernel's roofline fraction can be read against what the chip delivers as
  * well as against its published peaks.  Measurement support, not part of the
@@ -42,6 +42,12 @@ MOE_BENCH_API int moe_bench_hbm_read(const void* buf, size_t bytes, int reps, do
  * workgroup, one workgroup per CU; best of `reps` >= 2 runs after the first,
  * in TFLOP/s (1e12), to *tflops.  Allocates nothing. */
 MOE_BENCH_API int moe_bench_mfma_bf16(int iters, int reps, double* tflops, void* stream);
+
+/* The same for the W8A8 large tile's loop: e4m3fn operands (random codes,
+ * no NaN) on v_mfma_scale_f32_16x16x128_f8f6f4 with unit block scales, one
+ * k-step of 128 and one barrier per iteration; `iters` >= 2 iterations per
+ * workgroup.  TFLOP/s to *tflops.  Allocates nothing. */
+MOE_BENCH_API int moe_bench_mfma_fp8(int iters, int reps, double* tflops, void* stream);
 
 #ifdef __cplusplus
 }

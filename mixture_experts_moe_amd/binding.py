@@ -25,12 +25,14 @@ MOE_DTYPE_E4M3FN = 2
 MOE_SCALE_NONE = 0
 MOE_SCALE_PER_TENSOR = 1
 MOE_SCALE_PER_CHANNEL = 2
-MOE_KERNEL_COUNT = 6
+MOE_ACT_AS_IS = 0
+MOE_ACT_MX_E4M3 = 1
+MOE_KERNEL_COUNT = 7
 
 ENTRY_POINTS = (
     "moe_align_capacity", "moe_workspace_bytes", "moe_forward", "moe_route",
     "moe_route_logits", "moe_align", "moe_route_align", "moe_expert_ffn",
-    "moe_graph_create", "moe_graph_launch", "moe_graph_destroy", "moe_strerror",
+    "moe_quantize_act", "moe_graph_create", "moe_graph_launch", "moe_graph_destroy", "moe_strerror",
     "moe_timing_enable", "moe_timing_collect", "moe_kernel_name",
 )
 
@@ -39,7 +41,7 @@ class moe_desc(ctypes.Structure):
     _fields_ = [("num_tokens", ctypes.c_int64), ("hidden", ctypes.c_int64),
                 ("num_experts", ctypes.c_int64), ("intermediate", ctypes.c_int64),
                 ("act_dtype", ctypes.c_int32), ("weight_dtype", ctypes.c_int32),
-                ("block_m", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("block_m", ctypes.c_int32), ("act_quant", ctypes.c_int32)]
 
 
 class moe_scales(ctypes.Structure):
@@ -79,6 +81,7 @@ def lib() -> ctypes.CDLL:
         "moe_graph_launch": (I32, [P, P]),
         "moe_graph_destroy": (I32, [P]),
         "moe_expert_ffn": (I32, [D, P, P, P, I32, S, P, P, P, P, P, P, SZ, P]),
+        "moe_quantize_act": (I32, [D, P, P, P, P]),
         "moe_strerror": (ctypes.c_char_p, [I32]),
         "moe_timing_enable": (I32, [I32]),
         "moe_timing_collect": (I32, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64), I32]),
@@ -94,7 +97,7 @@ def lib() -> ctypes.CDLL:
 
 # ------------------------------------------------------------ attainable-rate probes
 
-BENCH_ENTRY_POINTS = ("moe_bench_hbm_read", "moe_bench_mfma_bf16")
+BENCH_ENTRY_POINTS = ("moe_bench_hbm_read", "moe_bench_mfma_bf16", "moe_bench_mfma_fp8")
 _BENCH_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_bench.so")
 _bench_lib = None
 
@@ -112,6 +115,8 @@ def bench_lib() -> ctypes.CDLL:
     L.moe_bench_hbm_read.argtypes = [P, SZ, I32, D, P]
     L.moe_bench_mfma_bf16.restype = I32
     L.moe_bench_mfma_bf16.argtypes = [I32, I32, D, P]
+    L.moe_bench_mfma_fp8.restype = I32
+    L.moe_bench_mfma_fp8.argtypes = [I32, I32, D, P]
     _bench_lib = L
     return L
 
@@ -131,6 +136,16 @@ def bench_mfma_bf16(iters: int = 4096, reps: int = 4, device="cuda", stream=None
     dev = torch.device(device)
     r = ctypes.c_double()
     _check("moe_bench_mfma_bf16", bench_lib().moe_bench_mfma_bf16(
+        int(iters), int(reps), ctypes.byref(r), _stream(dev, stream)))
+    return r.value
+
+
+def bench_mfma_fp8(iters: int = 4096, reps: int = 4, device="cuda", stream=None) -> float:
+    """Attainable e4m3fn (block-scaled) MFMA rate (TFLOP/s) of the W8A8 tile's
+    LDS-fed loop on random codes."""
+    dev = torch.device(device)
+    r = ctypes.c_double()
+    _check("moe_bench_mfma_fp8", bench_lib().moe_bench_mfma_fp8(
         int(iters), int(reps), ctypes.byref(r), _stream(dev, stream)))
     return r.value
 
@@ -164,10 +179,18 @@ def _w_code(t: torch.Tensor) -> int:
     raise TypeError(f"weights must be float32, bfloat16 or e4m3fn bytes, got {t.dtype}")
 
 
+def _act_quant_code(act_quant: Optional[str]) -> int:
+    if act_quant is None:
+        return MOE_ACT_AS_IS
+    if act_quant == "mx_e4m3":
+        return MOE_ACT_MX_E4M3
+    raise ValueError(f"act_quant must be None or 'mx_e4m3', got {act_quant!r}")
+
+
 def make_desc(T: int, d: int, E: int, I: int, act_dtype: int, weight_dtype: int,
-              block_m: int = 0) -> moe_desc:
+              block_m: int = 0, act_quant: Optional[str] = None) -> moe_desc:
     return moe_desc(int(T), int(d), int(E), int(I), int(act_dtype), int(weight_dtype),
-                    int(block_m), 0)
+                    int(block_m), _act_quant_code(act_quant))
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -252,11 +275,13 @@ def moe_workspace_bytes(desc: moe_desc, top_k: int, with_routing: bool = True) -
 def moe_forward(x: torch.Tensor, w_gate: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor,
                 top_k: int, scales: Optional[Sequence[torch.Tensor]] = None,
                 out: Optional[torch.Tensor] = None, *, block_m: int = 0,
-                workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """out [T, d] = fused MoE layer of x (same dtype as x)."""
+                workspace: Optional[torch.Tensor] = None, stream=None,
+                act_quant: Optional[str] = None) -> torch.Tensor:
+    """out [T, d] = fused MoE layer of x (same dtype as x).  act_quant="mx_e4m3"
+    selects the W8A8 mode (e4m3fn weights; x and h block-scaled e4m3fn)."""
     dev = _dev(x, w_gate, w13, w2, out)
     T, d, E, I = _shapes(x, w_gate, w13, w2)
-    desc = make_desc(T, d, E, I, _act_code(x), _w_code(w13), block_m)
+    desc = make_desc(T, d, E, I, _act_code(x), _w_code(w13), block_m, act_quant)
     sc = _scales(w13, scales)
     if out is None:
         out = torch.empty((T, d), dtype=x.dtype, device=dev)
@@ -301,17 +326,35 @@ def moe_route_logits(logits: torch.Tensor, top_k: int, *, stream=None):
     return ids, w
 
 
+def moe_quantize_act(x: torch.Tensor, *, stream=None):
+    """W8A8 activation quantisation of bf16 x [T, d]: (codes [T, d] uint8
+    e4m3fn bytes, exps [T, d/32] uint8 E8M0 bytes, scale 2^(byte - 127))."""
+    dev = _dev(x)
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise ValueError("x must be bfloat16 [T, d]")
+    T, d = x.shape
+    inter = 256
+    desc = make_desc(T, d, 1, inter, MOE_DTYPE_BF16, MOE_DTYPE_E4M3FN, 0, "mx_e4m3")
+    codes = torch.empty((T, d), dtype=torch.uint8, device=dev)
+    exps = torch.empty((T, d // 32), dtype=torch.uint8, device=dev)
+    _check("moe_quantize_act", lib().moe_quantize_act(ctypes.byref(desc), _ptr(x), _ptr(codes),
+                                                      _ptr(exps), _stream(dev, stream)))
+    return codes, exps
+
+
 def moe_align(topk_ids: torch.Tensor, num_experts: int, *, block_m: int = 0, hidden: int = 64,
               intermediate: int = 64, act_dtype: int = MOE_DTYPE_BF16,
-              weight_dtype: int = MOE_DTYPE_BF16, stream=None):
+              weight_dtype: int = MOE_DTYPE_BF16, stream=None, act_quant: Optional[str] = None):
     """Regroup slots by expert: (counts [E], sorted_ids [cap], block_expert [cap/B],
     num_padded [1], block_m).  The default block_m depends on the whole
-    descriptor, so pass the layer's dims/dtypes to get the one moe_forward uses."""
+    descriptor, so pass the layer's dims/dtypes/act_quant to get the one
+    moe_forward uses."""
     dev = _dev(topk_ids)
     if topk_ids.dtype != torch.int32 or topk_ids.dim() != 2:
         raise ValueError("topk_ids must be int32 [T, k]")
     T, k = topk_ids.shape
-    desc = make_desc(T, hidden, num_experts, intermediate, act_dtype, weight_dtype, block_m)
+    desc = make_desc(T, hidden, num_experts, intermediate, act_dtype, weight_dtype, block_m,
+                     act_quant)
     B, cap = moe_align_capacity(desc, k)
     counts = torch.empty(num_experts, dtype=torch.int32, device=dev)
     sorted_ids = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
@@ -358,11 +401,11 @@ class MoeGraph:
     def __init__(self, x: torch.Tensor, w_gate: torch.Tensor, w13: torch.Tensor,
                  w2: torch.Tensor, top_k: int, scales: Optional[Sequence[torch.Tensor]] = None,
                  out: Optional[torch.Tensor] = None, *, block_m: int = 0,
-                 workspace: Optional[torch.Tensor] = None):
+                 workspace: Optional[torch.Tensor] = None, act_quant: Optional[str] = None):
         self._h = None
         dev = _dev(x, w_gate, w13, w2, out)
         T, d, E, I = _shapes(x, w_gate, w13, w2)
-        desc = make_desc(T, d, E, I, _act_code(x), _w_code(w13), block_m)
+        desc = make_desc(T, d, E, I, _act_code(x), _w_code(w13), block_m, act_quant)
         self._sc = _scales(w13, scales)
         if out is None:
             out = torch.empty((T, d), dtype=x.dtype, device=dev)
@@ -402,12 +445,13 @@ def moe_expert_ffn(x: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, top_k: 
                    topk_w: torch.Tensor, sorted_ids: torch.Tensor, block_expert: torch.Tensor,
                    num_padded: torch.Tensor, scales: Optional[Sequence[torch.Tensor]] = None,
                    out: Optional[torch.Tensor] = None, *, block_m: int = 0,
-                   workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                   workspace: Optional[torch.Tensor] = None, stream=None,
+                   act_quant: Optional[str] = None) -> torch.Tensor:
     """Expert networks + combine for a given routing (layout from moe_align
-    with the same block_m)."""
+    with the same block_m and act_quant)."""
     dev = _dev(x, w13, w2, topk_w, sorted_ids, block_expert, num_padded, out)
     T, d, E, I = _shapes(x, None, w13, w2)
-    desc = make_desc(T, d, E, I, _act_code(x), _w_code(w13), block_m)
+    desc = make_desc(T, d, E, I, _act_code(x), _w_code(w13), block_m, act_quant)
     B, cap = moe_align_capacity(desc, top_k)
     if sorted_ids.numel() < cap or block_expert.numel() < cap // B:
         raise ValueError("sorted_ids / block_expert smaller than the layout capacity")

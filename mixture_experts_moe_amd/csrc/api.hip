@@ -28,7 +28,7 @@ int act_bytes(int dt) { return dt == MOE_DTYPE_F32 ? 4 : 2; }
 
 int check_desc(const moe_desc* d, int top_k) {
   if (!d) return MOE_ERR_NULL_PTR;
-  if (d->reserved != 0) return MOE_ERR_BAD_ARG;
+  if (d->act_quant != MOE_ACT_AS_IS && d->act_quant != MOE_ACT_MX_E4M3) return MOE_ERR_BAD_ARG;
   if (d->num_tokens < 0) return MOE_ERR_BAD_SHAPE;
   if (d->hidden < 64 || d->hidden % 64 || d->hidden > kMaxDim) return MOE_ERR_BAD_SHAPE;
   if (d->intermediate < 64 || d->intermediate % 64 || d->intermediate > kMaxDim)
@@ -43,8 +43,17 @@ int check_desc(const moe_desc* d, int top_k) {
   const int bm = d->block_m;
   if (bm != 0 && bm != 16 && bm != 32 && bm != 64 && bm != 128 && bm != 256)
     return MOE_ERR_BAD_BLOCK_M;
+  const int hid = static_cast<int>(d->hidden), inter = static_cast<int>(d->intermediate);
+  if (d->act_quant == MOE_ACT_MX_E4M3) {
+    // W8A8: bf16 x quantised in the library, e4m3fn weights, the 256-token tile
+    if (d->act_dtype != MOE_DTYPE_BF16 || d->weight_dtype != MOE_DTYPE_E4M3FN)
+      return MOE_ERR_BAD_DTYPE;
+    if (bm != 0 && bm != 256) return MOE_ERR_BAD_BLOCK_M;
+    if (!moe::big8_fits(d->num_tokens, hid, inter)) return MOE_ERR_BAD_SHAPE;
+    return MOE_OK;
+  }
   if (bm == 256 && !(d->weight_dtype == MOE_DTYPE_BF16 &&
-                     moe::big_gemm_fits(d->num_tokens, static_cast<int>(d->hidden), static_cast<int>(d->intermediate))))
+                     moe::big_gemm_fits(d->num_tokens, hid, inter)))
     return MOE_ERR_BAD_BLOCK_M;  // the 256-token GEMM is bf16 with d % 256 == 0, I % 128 == 0
   return MOE_OK;
 }
@@ -77,8 +86,9 @@ struct Plan {
   int T, d, E, I, k, A, B, cap;
   int splits, ksplit;
   int act, wdt;
-  // workspace offsets (bytes)
-  size_t logits, ids, gates, counts, num_padded, sorted, block_exp, h, y, total;
+  bool act_mx;  // W8A8 mode
+  // workspace offsets (bytes); xq, sx, sh only in the W8A8 mode
+  size_t logits, ids, gates, counts, num_padded, sorted, block_exp, h, y, xq, sx, sh, total;
 };
 
 // Block size of the regrouped layout.  Up to 64 tokens the weight-streaming
@@ -88,6 +98,7 @@ struct Plan {
 // grouped GEMM, and when experts average 256 tokens or more (bf16 weights,
 // fitting shapes) 256-token blocks and the large-tile GEMM.
 int default_block_m(const moe_desc* d, int top_k) {
+  if (d->act_quant == MOE_ACT_MX_E4M3) return 256;  // the W8A8 tile
   if (d->weight_dtype == MOE_DTYPE_F32) return 16;
   const int64_t T = d->num_tokens;
   const int hid = static_cast<int>(d->hidden), inter = static_cast<int>(d->intermediate);
@@ -142,6 +153,7 @@ void make_plan(const moe_desc* d, int top_k, bool with_routing, Plan* p) {
   p->cap = static_cast<int>(capacity(p->A, p->E, p->B));
   p->act = d->act_dtype;
   p->wdt = d->weight_dtype;
+  p->act_mx = d->act_quant == MOE_ACT_MX_E4M3;
 
   // Split W2's K range when there are too few workgroups to keep enough
   // HBM requests in flight (small batches); the combine adds the splits in a
@@ -153,7 +165,7 @@ void make_plan(const moe_desc* d, int top_k, bool with_routing, Plan* p) {
     // grid fills about four rounds of the CUs (splits of >= 16 stages)
     const int64_t blocks_est = moe::ffn_blocks_estimate(p->cap, p->B, p->E, p->A);
     const int64_t tiles = blocks_est * (p->d / 256);
-    const int kc = moe::big_w2_kchunk();
+    const int kc = p->act_mx ? moe::big8_w2_kchunk() : moe::big_w2_kchunk();
     int s = 1;
     while (s < 4 && tiles * s < 1024 && p->I / (2 * s) >= 8 * kc) s *= 2;
     const int per = (p->I + s - 1) / s;
@@ -194,8 +206,16 @@ void make_plan(const moe_desc* d, int top_k, bool with_routing, Plan* p) {
   } else {
     p->logits = p->ids = p->gates = p->counts = p->num_padded = p->sorted = p->block_exp = 0;
   }
-  p->h = take(cap * static_cast<size_t>(p->I) * act_bytes(p->act));
+  // h: bf16 (fp32 for fp32 layers), or e4m3fn codes in the W8A8 mode
+  p->h = take(cap * static_cast<size_t>(p->I) * (p->act_mx ? 1 : act_bytes(p->act)));
   p->y = take(static_cast<size_t>(p->splits) * A * p->d * 4);
+  if (p->act_mx) {
+    p->xq = take(T * static_cast<size_t>(p->d));
+    p->sx = take(T * static_cast<size_t>(p->d) / 32);
+    p->sh = take(cap * static_cast<size_t>(p->I) / 32);
+  } else {
+    p->xq = p->sx = p->sh = 0;
+  }
   p->total = p->T == 0 ? 0 : off;  // nothing runs for T = 0
 }
 
@@ -284,11 +304,17 @@ FfnArgs ffn_args(const Plan& p, const void* x, const void* w13, const void* w2,
   a.cap = p.cap;
   a.splits = p.splits;
   a.ksplit = p.ksplit;
+  a.act_mx = p.act_mx;
+  a.xq = p.act_mx ? reinterpret_cast<uint8_t*>(ws + p.xq) : nullptr;
+  a.sx = p.act_mx ? reinterpret_cast<uint8_t*>(ws + p.sx) : nullptr;
+  a.sh = p.act_mx ? reinterpret_cast<uint8_t*>(ws + p.sh) : nullptr;
   return a;
 }
 
 hipError_t run_ffn(const FfnArgs& a, hipStream_t s) {
-  hipError_t e = timed(MOE_KERNEL_FFN13, s, [&] { return moe::launch_ffn13(a, s); });
+  hipError_t e = hipSuccess;
+  if (a.act_mx) e = timed(MOE_KERNEL_QUANT_X, s, [&] { return moe::launch_quantize_x(a, s); });
+  if (e == hipSuccess) e = timed(MOE_KERNEL_FFN13, s, [&] { return moe::launch_ffn13(a, s); });
   if (e == hipSuccess) e = timed(MOE_KERNEL_FFN2, s, [&] { return moe::launch_ffn2(a, s); });
   if (e == hipSuccess) e = timed(MOE_KERNEL_COMBINE, s, [&] { return moe::launch_combine(a, s); });
   return e;
@@ -454,6 +480,24 @@ MOE_API int moe_expert_ffn(const moe_desc* desc, const void* x, const void* w13,
   return to_status(run_ffn(a, s));
 }
 
+MOE_API int moe_quantize_act(const moe_desc* desc, const void* x, uint8_t* codes, uint8_t* exps,
+                             void* stream) {
+  int st = check_desc(desc, 1);
+  if (st) return st;
+  if (desc->act_quant != MOE_ACT_MX_E4M3) return MOE_ERR_BAD_ARG;
+  if (desc->num_tokens == 0) return MOE_OK;
+  if ((st = check_ptrs({x, codes, exps}))) return st;
+  FfnArgs a{};
+  a.x = x;
+  a.T = static_cast<int>(desc->num_tokens);
+  a.d = static_cast<int>(desc->hidden);
+  a.act_mx = true;
+  a.xq = codes;
+  a.sx = exps;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return to_status(timed(MOE_KERNEL_QUANT_X, s, [&] { return moe::launch_quantize_x(a, s); }));
+}
+
 // Checks shared by moe_forward and moe_graph_create; fills the plan.
 static int forward_checks(const moe_desc* desc, const void* x, const float* w_gate,
                           const void* w13, const void* w2, int top_k, const moe_scales* scales,
@@ -606,7 +650,8 @@ MOE_API int moe_timing_collect(double* total_ms, int64_t* launches, int reset) {
 
 MOE_API const char* moe_kernel_name(int kind) {
   static const char* names[MOE_KERNEL_COUNT] = {"route_logits", "route_topk", "align",
-                                                "ffn13",        "ffn2",       "combine"};
+                                                "ffn13",        "ffn2",       "combine",
+                                                "quant_x"};
   return (kind >= 0 && kind < MOE_KERNEL_COUNT) ? names[kind] : "";
 }
 

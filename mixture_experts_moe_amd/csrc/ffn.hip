@@ -474,6 +474,7 @@ hipError_t launch_ffn13(const FfnArgs& a, hipStream_t s) {
                                           static_cast<float*>(a.h), a.d, a.I, a.k, a.A, a.B);
     return hipGetLastError();
   }
+  if (a.act_mx) return launch_ffn13_big8(a, s);    // W8A8: block-scaled e4m3fn activations
   if (a.B == 256) return launch_ffn13_big(a, s);   // large-tile grouped GEMM
   if (a.B == 128) return launch_ffn13_gemm(a, s);  // token-tiled grouped GEMM
   if (dma_stream_use(a)) return launch_ffn13_dma(a, s);  // weights through LDS
@@ -490,6 +491,7 @@ hipError_t launch_ffn2(const FfnArgs& a, hipStream_t s) {
                                          a.B);
     return hipGetLastError();
   }
+  if (a.act_mx) return launch_ffn2_big8(a, s);
   if (a.B == 256) return launch_ffn2_big(a, s);
   if (a.B == 128) return launch_ffn2_gemm(a, s);
   if (dma_stream_use(a)) return launch_ffn2_dma(a, s);

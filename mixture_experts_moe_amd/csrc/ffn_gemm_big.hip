@@ -29,120 +29,11 @@
 // h = SiLU(gate) * up.  W2: 256 output channels; the epilogue scales by the
 // slot's gate.  The grid is rasterised per XCD like the 128-token GEMM.
 
-#include "ffn_common.h"
+#include "ffn_big_common.h"
 
 namespace moe {
 
-// Stage shape: 2 buffers x 2 operands x 256 rows x 64 K x 2 bytes = 128 KB LDS.
-constexpr int kBigWaves = 8;              // 128 x 64 per wave, two waves per SIMD
-constexpr int kBigWn = kBigWaves / 2;     // waves along the tokens (two along the rows)
-constexpr int kBigThreads = 64 * kBigWaves;
-constexpr int kBigTokens = 256;  // block size B of this path
-constexpr int kBigRows = 256;    // weight rows per tile
-constexpr int kBigK = 64;        // K elements per stage
-constexpr int kBigN = kBigTokens;  // tokens per workgroup tile: the whole block
-constexpr int kBigTA = 8;                      // 16-row weight tiles per wave (128 rows)
-constexpr int kBigNB = kBigN / (16 * kBigWn);  // 16-token tiles per wave
-constexpr int kBigSlots = kBigK / 8;                 // 16-byte slots per LDS row
-constexpr int kBigRowBytes = kBigK * 2;
-constexpr int kBigRowsPerGroup = 1024 / kBigRowBytes;  // rows filled by one 1 KB load
-constexpr int kBigGroups = kBigRows / kBigRowsPerGroup / kBigWaves;  // A loads per wave and stage
-constexpr int kBigGroupsB = kBigN / kBigRowsPerGroup / kBigWaves;   // B loads per wave and stage
-constexpr int kBigLoads = kBigGroups + kBigGroupsB;
-constexpr int kBigOperandBytes = kBigRows * kBigRowBytes;
-constexpr int kBigStageBytes = kBigOperandBytes + kBigN * kBigRowBytes;
-constexpr int kBigStages = 2;  // 2 x 64 KB of the 160 KB LDS
-static_assert(kBigStages * kBigStageBytes <= 160 * 1024, "stages fit in LDS");
-#ifndef MOE_BIG_ISSUE_FIRST
-#define MOE_BIG_ISSUE_FIRST 1
-#endif
-#ifndef MOE_BIG_RASTER
-#define MOE_BIG_RASTER 1
-#endif
-#ifndef MOE_BIG_GROUP_COLS
-#define MOE_BIG_GROUP_COLS 4
-#endif
-constexpr int kBigXcds = MOE_BIG_RASTER ? 8 : 1;  // 1: plain order, no XCD remap
-constexpr int kBigGroupCols = MOE_BIG_GROUP_COLS;
-
-// Slot swizzle: 8 slots per row, rows pair up per bank line, so the 16 rows
-// one 16-lane group reads for the same k land in 16 different 16-byte bank
-// groups.
-__device__ __forceinline__ int big_swz(int row) { return (row >> 1) & 7; }
-
-struct BigTile {
-  int b, y;
-  bool live;
-};
-
-// Same rasterisation as the 128-token GEMM: contiguous runs of the logical
-// order per XCD, super-rows of kBigGroupCols channel groups, row block
-// slowest inside a super-row.
-__device__ __forceinline__ BigTile big_tile_of(int p, int gx, int gy) {
-  const int total = gx * gy;
-  const int per_xcd = (total + kBigXcds - 1) / kBigXcds;
-  const int l = (p % kBigXcds) * per_xcd + p / kBigXcds;
-  BigTile t{0, 0, l < total};
-  if (!t.live) return t;
-  const int band = kBigGroupCols * gx;
-  const int sr = l / band;
-  const int rem = l - sr * band;
-  const int cols = min(kBigGroupCols, gy - sr * kBigGroupCols);
-  t.b = rem / cols;
-  t.y = sr * kBigGroupCols + rem % cols;
-  return t;
-}
-
-// Each wave fills kBigGroups consecutive 1 KB groups (kBigRowsPerGroup rows
-// each) of an operand per stage: in group q, lane l writes tile row
-// 64*wave + kBigRowsPerGroup*q + l/kBigSlots, physical slot l%kBigSlots,
-// which holds logical slot (l%kBigSlots) ^ swz(row).  swz(row) depends on q
-// only through q's parity, so a lane's weight sources are two bases plus a
-// stride; token sources (gathered x rows, or h rows) are one pointer per
-// group.
-struct BigLoader {
-  __amdgpu_buffer_rsrc_t ra;  // weight rows of the tile's expert
-  __amdgpu_buffer_rsrc_t rb;  // token rows (x, or the block's h rows)
-  uint32_t a_even;            // byte offset of this lane's group-0 source (q even), k = 0
-  uint32_t a_odd;             // group 1 (q odd)
-  uint32_t a_step;            // bytes between groups q and q + 2
-  uint32_t b[kBigGroupsB];    // byte offset of this lane's token source of group q, k = 0
-
-  __device__ __forceinline__ uint32_t a_off(int q, int k0) const {
-    return (q & 1 ? a_odd : a_even) + (q >> 1) * a_step + 2 * k0;
-  }
-};
-
-// Buffer resource over `bytes` bytes at `base` (raw: stride 0, byte
-// offsets; flags word as gfx9-family kernels use for plain dword data).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t big_rsrc(const void* base, size_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
-                                           0x00020000);
-}
-
-// The stage's direct-to-LDS loads go through buffer resources
-// (buffer_load ... lds) rather than global_load_lds: with the latter in
-// flight the compiler waits for every outstanding LDS read (lgkmcnt(0)) before
-// each MFMA group, which undoes the fragment pipelining; the buffer form
-// keeps those waits partial.
-__device__ __forceinline__ void big_issue(const BigLoader& ld, uint8_t* stage, int k0, int wave) {
-#pragma unroll
-  for (int q = 0; q < kBigGroups; ++q)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        ld.ra, (__attribute__((address_space(3))) void*)(stage + (wave * kBigGroups + q) * 1024), 16,
-        ld.a_off(q, k0), 0, 0, 0);
-#pragma unroll
-  for (int q = 0; q < kBigGroupsB; ++q)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        ld.rb,
-        (__attribute__((address_space(3))) void*)(stage + kBigOperandBytes +
-                                                   (wave * kBigGroupsB + q) * 1024),
-        16, ld.b[q] + 2 * k0, 0, 0, 0);
-}
-
-// s_waitcnt immediate that waits until at most n vector-memory loads are
-// outstanding (lgkm and exp counters not waited on).
-constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kBigK = 64;  // bf16 K elements per stage (128-byte rows)
 
 // 16-byte MFMA fragment of tile row `row`, logical slot `slot`.
 __device__ __forceinline__ bf16x8 big_frag(const uint8_t* op, int row, int slot) {
@@ -180,16 +71,6 @@ __device__ __forceinline__ void big_mma(const BigFrags& f, BigAcc& acc) {
     for (int u = 0; u < kBigNB; ++u) acc[t][u] = mfma16x16x32(f.a[t], f.b[u], acc[t][u]);
 }
 
-// Wait for this wave's LDS reads, then meet the other waves.  No memory
-// fence: a workgroup-scope fence would also wait for every direct-to-LDS
-// load this wave has in flight, later stages' included.  Each wave waits
-// explicitly for its own loads of the stage about to be read before it
-// arrives; the memory clobber keeps the compiler from moving LDS accesses
-// across.
-__device__ __forceinline__ void big_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
 // First part of one stage: wait until this wave's loads of `cur` have
 // landed (kWait of its later loads may stay outstanding), meet the other
 // waves (after which nobody reads `nxt`, the buffer read one or two stages
@@ -208,18 +89,18 @@ __device__ __forceinline__ void big_half(const BigLoader& ld, const uint8_t* cur
   const uint8_t* opb = cur + kBigOperandBytes;
   BigFrags f0;
 #if MOE_BIG_ISSUE_FIRST
-  if (kIssue) big_issue(ld, nxt, knext, wave);
+  if (kIssue) big_issue(ld, nxt, 2 * knext, wave);
   if (!kLive) return;
   __builtin_amdgcn_sched_barrier(0);
   big_load_frags(f0, cur, opb, arow0, arow_up, brow0, 0);
 #else
   if (!kLive) {
-    if (kIssue) big_issue(ld, nxt, knext, wave);
+    if (kIssue) big_issue(ld, nxt, 2 * knext, wave);
     return;
   }
   big_load_frags(f0, cur, opb, arow0, arow_up, brow0, 0);
   __builtin_amdgcn_sched_barrier(0);
-  if (kIssue) big_issue(ld, nxt, knext, wave);
+  if (kIssue) big_issue(ld, nxt, 2 * knext, wave);
 #endif
   big_mma(f0, acc);
   __builtin_amdgcn_sched_barrier(0);
@@ -278,11 +159,6 @@ struct BigRing {
       run2<false>(nst, acc);
   }
 };
-
-#define BIG_BUFFERS(name)                                                                 \
-  __shared__ __attribute__((aligned(1024))) uint8_t name##0[kBigStageBytes];              \
-  __shared__ __attribute__((aligned(1024))) uint8_t name##1[kBigStageBytes];              \
-  uint8_t* const name[2] = {name##0, name##1}
 
 // ------------------------------------------------------------ W13 + SiLU*mul
 // Tile: channels n0 .. n0+127 (rows: 128 gate, then 128 up) x the 256

@@ -50,12 +50,18 @@ struct FfnArgs {
   const int32_t* sorted_ids;    // [cap]
   const int32_t* block_expert;  // [cap / B]
   const int32_t* num_padded;    // [1]
-  void* h;                  // [cap, I] act dtype (workspace)
+  void* h;                  // [cap, I] act dtype (workspace); e4m3fn codes in the W8A8 mode
   float* y_part;            // [splits, A, d] fp32 (workspace)
   void* out;                // [T, d] act dtype
   int T, d, E, I, k, A, B, cap;
   int splits;               // split of W2's K (= I) range
   int ksplit;               // K elements per split (multiple of the K chunk)
+  // W8A8 mode (block-scaled e4m3fn activations, workspace): x codes [T, d]
+  // and exponents [T, d/32]; h's exponents [cap, I/32] (h holds its codes)
+  bool act_mx;
+  uint8_t* xq;
+  uint8_t* sx;
+  uint8_t* sh;
 };
 
 hipError_t launch_ffn13(const FfnArgs& a, hipStream_t s);
@@ -68,6 +74,14 @@ hipError_t launch_ffn2_gemm(const FfnArgs& a, hipStream_t s);
 // Large-tile grouped GEMM (block size 256, bf16 weights, d % 256 == 0 and
 // I % 128 == 0); used when a.B == 256.
 bool big_gemm_fits(int64_t T, int d, int I);
+// W8A8 large tile (e4m3fn weights, block-scaled e4m3fn activations, blocks
+// of 256): d and I multiples of 256, an expert's W13 (2I x d bytes) and xq
+// (T x d bytes) under 2 GiB.
+bool big8_fits(int64_t T, int d, int I);
+hipError_t launch_quantize_x(const FfnArgs& a, hipStream_t s);
+hipError_t launch_ffn13_big8(const FfnArgs& a, hipStream_t s);
+hipError_t launch_ffn2_big8(const FfnArgs& a, hipStream_t s);
+int big8_w2_kchunk();  // a split of the W8A8 W2's K range is a multiple of this
 hipError_t launch_ffn13_big(const FfnArgs& a, hipStream_t s);
 hipError_t launch_ffn2_big(const FfnArgs& a, hipStream_t s);
 int big_w2_kchunk();  // a split of the big W2's K range is a multiple of this

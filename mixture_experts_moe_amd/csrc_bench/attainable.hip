@@ -1,6 +1,7 @@
 // Attainable-rate kernels behind include/moe_bench.h: a streaming HBM read in
-// the layer's best weight-streaming pattern, and the large-tile GEMM's
-// LDS-fed MFMA loop on random data.  Measurement support only.
+// the layer's best weight-streaming pattern, and the large-tile GEMMs'
+// LDS-fed MFMA loops (bf16, and e4m3fn with block scales) on random data.
+// Measurement support only.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -18,6 +19,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // ------------------------------------------------------------ HBM read
 // One wave per workgroup reads one 32 KB chunk: 32 direct-to-LDS loads of
@@ -95,6 +97,68 @@ __global__ __launch_bounds__(64 * kMmaWaves) void mfma_loop_kernel(int iters) {
   if (s == 1234.5f) moe_bench_sink_float[lane] = s;
 }
 
+// ------------------------------------------------------------ fp8 MFMA loop
+// The W8A8 large tile's inner loop: LDS as above (rows of 128 e4m3fn bytes
+// of K), per iteration one k-step of 128: each wave reads its four token
+// fragments, then its eight weight fragments in two halves of four, each
+// half followed by 16 v_mfma_scale_f32_16x16x128_f8f6f4 (unit E8M0 scales);
+// one barrier per iteration.  Random e4m3fn codes of magnitude 0.5 .. 1.875,
+// both signs (no NaN code).
+
+__device__ __forceinline__ i32x8 frag8(const uint8_t* buf, int row, int g) {
+  row &= 511;
+  const uint8_t* r = buf + row * 128;
+  const int sw = (row >> 1) & 7;
+  const uint4 lo = *reinterpret_cast<const uint4*>(r + ((g ^ sw) << 4));
+  const uint4 hi = *reinterpret_cast<const uint4*>(r + (((4 + g) ^ sw) << 4));
+  return i32x8{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z),
+               static_cast<int>(lo.w), static_cast<int>(hi.x), static_cast<int>(hi.y),
+               static_cast<int>(hi.z), static_cast<int>(hi.w)};
+}
+
+__global__ __launch_bounds__(64 * kMmaWaves) void mfma_fp8_loop_kernel(int iters) {
+  __shared__ __attribute__((aligned(1024))) uint8_t buf[64 * 1024];
+  const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, g = lane >> 4, wave = tid >> 6;
+  for (int i = tid; i < 4096; i += 64 * kMmaWaves) {
+    uint32_t h = static_cast<uint32_t>(i) * 2654435761u + 777u;
+    uint32_t w[4];
+    for (int q = 0; q < 4; ++q) {
+      // per byte: sign, mantissa and the exponent field's low bit random (field 6 or 7)
+      w[q] = ((h ^ (h >> 11)) & 0x8f8f8f8fu) | 0x30303030u;
+      h = h * 1664525u + 1013904223u;
+    }
+    reinterpret_cast<uint4*>(buf)[i] = uint4{w[0], w[1], w[2], w[3]};
+  }
+  __syncthreads();
+  const int abase = 128 * (wave & 1), bbase = 256 + 64 * (wave >> 1);
+  f32x4 acc[8][4];
+  for (int t = 0; t < 8; ++t)
+    for (int u = 0; u < 4; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int it = 0; it < iters; ++it) {
+    const int rot = (it * 16) & 127;  // walk the rows so reads are not loop-invariant
+    i32x8 a[4], b[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) b[u] = frag8(buf, bbase + ((16 * u + rot) & 63) + r16, g);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        a[t] = frag8(buf, abase + ((64 * half + 16 * t + rot) & 127) + r16, g);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          acc[4 * half + t][u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              a[t], b[u], acc[4 * half + t][u], 0, 0, 0, 127, 0, 127);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+  float s = 0.f;
+  for (int t = 0; t < 8; ++t)
+    for (int u = 0; u < 4; ++u) s += acc[t][u][0] + acc[t][u][3];
+  if (s == 1234.5f) moe_bench_sink_float[lane] = s;
+}
+
 template <class F>
 int best_ms(hipStream_t s, int reps, F&& launch, float* best) {
   hipEvent_t a, b;
@@ -156,6 +220,25 @@ MOE_BENCH_API int moe_bench_mfma_bf16(int iters, int reps, double* tflops, void*
   if (st) return st;
   // per workgroup and iteration: 8 waves x 2 k-steps x 32 MFMAs of 16 x 16 x 32
   const double flop = 2.0 * 16 * 16 * 32 * 32 * 2 * kMmaWaves * static_cast<double>(iters) * cus;
+  *tflops = flop / (ms * 1e-3) / 1e12;
+  return MOE_OK;
+}
+
+MOE_BENCH_API int moe_bench_mfma_fp8(int iters, int reps, double* tflops, void* stream) {
+  if (!tflops) return MOE_ERR_NULL_PTR;
+  if (iters < 2 || reps < 2) return MOE_ERR_BAD_ARG;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return MOE_ERR_HIP;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float ms;
+  const int st = best_ms(s, reps, [&] {
+    mfma_fp8_loop_kernel<<<cus, 64 * kMmaWaves, 0, s>>>(iters);
+  }, &ms);
+  if (st) return st;
+  // per workgroup and iteration: 8 waves x 32 MFMAs of 16 x 16 x 128
+  const double flop = 2.0 * 16 * 16 * 128 * 32 * kMmaWaves * static_cast<double>(iters) * cus;
   *tflops = flop / (ms * 1e-3) / 1e12;
   return MOE_OK;
 }

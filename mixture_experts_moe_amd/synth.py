@@ -18,6 +18,9 @@ Workloads (hidden d, experts E, top-k, intermediate I):
   fp8          T in {64,2048}, d=7168, E=256, k=8, I=2048; bf16 x ~ N(0,1);
                weights ~ N(0,0.02) quantised to e4m3fn with one fp32 scale per
                output channel (scale = row amax / 448, 1 for an all-zero row)
+  prefill_w8a8 the prefill_bf16 shapes with e4m3fn weights (per-channel
+               scales, as fp8) and the W8A8 mode: x and h block-scaled
+               e4m3fn (act_quant "mx_e4m3")
   skew         T=512, d=2880, E=32, k=4, I=2880; bf16 x ~ N(0,1) with
                x[:,0] = 1 (a constant feature) and W_gate[e,0] = b_e so that
                expert popularity follows a Zipf(1.2)-like tail; experts 3, 11,
@@ -44,6 +47,8 @@ WORKLOADS = {
                          x_std=1.0, w_std=0.02, skew=False),
     "fp8": dict(T=(64, 2048), d=7168, E=256, k=8, I=2048, act="bf16", w="e4m3fn",
                 x_std=1.0, w_std=0.02, skew=False),
+    "prefill_w8a8": dict(T=(4096,), d=4096, E=8, k=2, I=14336, act="bf16", w="e4m3fn",
+                         x_std=1.0, w_std=0.02, skew=False, act_quant="mx_e4m3"),
     "skew": dict(T=(512,), d=2880, E=32, k=4, I=2880, act="bf16", w="bf16",
                  x_std=1.0, w_std=0.02, skew=True),
 }
@@ -66,6 +71,7 @@ class MoEInputs:
     w2     [E, d, I]  same dtype as w13
     s13    [E, 2I] float32 per-channel scales (e4m3fn only, else None)
     s2     [E, d]  float32 (e4m3fn only, else None)
+    act_quant  None, or "mx_e4m3" for the W8A8 mode
     """
     x: torch.Tensor
     w_gate: torch.Tensor
@@ -77,6 +83,7 @@ class MoEInputs:
     act: str
     w: str
     name: str
+    act_quant: Optional[str] = None
 
     @property
     def T(self) -> int:
@@ -145,7 +152,7 @@ def make_inputs(workload: Union[str, dict] = "tiny_fp32", T: Optional[int] = Non
                 k: Optional[int] = None, I: Optional[int] = None, act: Optional[str] = None,
                 w: Optional[str] = None, x_std: Optional[float] = None,
                 w_std: Optional[float] = None, skew: Optional[bool] = None,
-                scale_mode: str = "channel") -> MoEInputs:
+                scale_mode: str = "channel", act_quant: Optional[str] = None) -> MoEInputs:
     """Draw one layer's inputs.  Keyword overrides change single dimensions
     (tests use them for edge shapes); ``scale_mode`` is "channel" or "tensor"
     for e4m3fn weights."""
@@ -155,7 +162,8 @@ def make_inputs(workload: Union[str, dict] = "tiny_fp32", T: Optional[int] = Non
     else:
         cfg = dict(workload)
         name = cfg.pop("name", "custom")
-    over = dict(d=d, E=E, k=k, I=I, act=act, w=w, x_std=x_std, w_std=w_std, skew=skew)
+    over = dict(d=d, E=E, k=k, I=I, act=act, w=w, x_std=x_std, w_std=w_std, skew=skew,
+                act_quant=act_quant)
     for key, val in over.items():
         if val is not None:
             cfg[key] = val
@@ -196,7 +204,7 @@ def make_inputs(workload: Union[str, dict] = "tiny_fp32", T: Optional[int] = Non
         s13 = s13[:, 0].contiguous()
         s2 = s2[:, 0].contiguous()
     return MoEInputs(x=x, w_gate=w_gate, w13=w13, w2=w2, s13=s13, s2=s2, top_k=k_,
-                     act=cfg["act"], w=cfg["w"], name=name)
+                     act=cfg["act"], w=cfg["w"], name=name, act_quant=cfg.get("act_quant"))
 
 
 def _quantize_tensor(w: torch.Tensor):
@@ -233,4 +241,6 @@ def to_oracle(inp: MoEInputs, experts: Optional[Sequence[int]] = None) -> dict:
     if inp.w == "e4m3fn":
         kw.update(s13=raw(inp.s13), s2=raw(inp.s2),
                   scale_mode="tensor" if inp.s13.dim() == 1 else "channel")
+    if inp.act_quant is not None:
+        kw["act_quant"] = inp.act_quant
     return kw

@@ -41,8 +41,11 @@ def test_library_exports_exactly_the_declared_symbols(lib):
     assert exported == declared_functions()
 
 
-def desc(T=4, d=128, E=8, I=128, act=B.MOE_DTYPE_BF16, w=B.MOE_DTYPE_BF16, bm=0):
-    return B.make_desc(T, d, E, I, act, w, bm)
+def desc(T=4, d=128, E=8, I=128, act=B.MOE_DTYPE_BF16, w=B.MOE_DTYPE_BF16, bm=0, q=None):
+    return B.make_desc(T, d, E, I, act, w, bm, q)
+
+
+E4 = B.MOE_DTYPE_E4M3FN
 
 
 def ws_status(lib, dsc, k=2):
@@ -75,15 +78,28 @@ def ws_status(lib, dsc, k=2):
     (dict(T=1 << 18, d=4096, bm=256), 2, -8),          # 2*T*d = 2^31
     (dict(T=(1 << 18) - 64, d=4096, bm=256), 2, 0),
     (dict(d=1 << 15, I=1 << 15, bm=256), 2, -8),      # 4*I*d = 2^32
+    # W8A8: bf16 x, e4m3fn weights, blocks of 256, d and I multiples of 256
+    (dict(d=256, I=256, w=E4, q="mx_e4m3"), 2, 0),
+    (dict(d=256, I=256, w=E4, bm=256, q="mx_e4m3"), 2, 0),
+    (dict(d=256, I=256, q="mx_e4m3"), 2, -4),             # bf16 weights
+    (dict(d=256, I=256, act=B.MOE_DTYPE_F32, w=B.MOE_DTYPE_F32, q="mx_e4m3"), 2, -4),
+    (dict(d=256, I=256, w=E4, bm=128, q="mx_e4m3"), 2, -8),
+    (dict(d=128, I=256, w=E4, q="mx_e4m3"), 2, -2),
+    (dict(d=256, I=384, w=E4, q="mx_e4m3"), 2, -2),
+    (dict(d=1 << 15, I=1 << 15, w=E4, q="mx_e4m3"), 2, -2),  # 2*I*d = 2^31
+    (dict(T=1 << 19, d=4096, I=256, w=E4, q="mx_e4m3"), 2, -2),  # T*d = 2^31
+    (dict(T=(1 << 19) - 64, d=4096, I=256, w=E4, q="mx_e4m3"), 2, 0),
 ])
 def test_descriptor_validation(lib, kw, k, status):
     assert ws_status(lib, desc(**kw), k) == status
 
 
-def test_reserved_field_and_null_descriptor(lib):
+def test_unknown_act_quant_and_null_descriptor(lib):
     d = desc()
-    d.reserved = 1
-    assert ws_status(lib, d) == B.MOE_ERR_BAD_ARG if hasattr(B, "MOE_ERR_BAD_ARG") else -9
+    d.act_quant = 2
+    assert ws_status(lib, d) == -9
+    with pytest.raises(ValueError):
+        desc(q="mx_e5m2")
     n = ctypes.c_size_t()
     assert lib.moe_workspace_bytes(None, 2, 1, ctypes.byref(n)) == -1
     assert lib.moe_workspace_bytes(ctypes.byref(desc()), 2, 1, None) == -1
@@ -109,6 +125,8 @@ def test_default_block_covers_a_decode_batch(lib):
     assert B.moe_align_capacity(desc(T=4096, d=2880, I=2880), 2)[0] == 128
     assert B.moe_align_capacity(desc(T=4096, d=4096, I=14336, w=B.MOE_DTYPE_E4M3FN), 2)[0] == 128
     assert B.moe_align_capacity(desc(act=B.MOE_DTYPE_F32, w=B.MOE_DTYPE_F32), 2)[0] == 16
+    # the W8A8 mode has one tile: blocks of 256 at any batch
+    assert B.moe_align_capacity(desc(T=1, d=256, I=256, w=E4, q="mx_e4m3"), 2)[0] == 256
 
 
 def test_workspace_grows_with_tokens(lib):
@@ -170,6 +188,17 @@ def test_stage_entry_points_validate(lib):
     assert lib.moe_route(ctypes.byref(desc(T=0)), None, None, 2, None, None, None, None) == 0
 
 
+def test_quantize_act_validates(lib):
+    q = lib.moe_quantize_act
+    d8 = desc(d=256, I=256, w=E4, q="mx_e4m3")
+    assert q(ctypes.byref(d8), None, FAKE, FAKE, None) == -1
+    assert q(ctypes.byref(d8), FAKE, FAKE, FAKE + 8, None) == -5
+    assert q(ctypes.byref(desc(d=256, I=256, w=E4)), FAKE, FAKE, FAKE, None) == -9  # not W8A8
+    assert q(ctypes.byref(desc(d=128, I=256, w=E4, q="mx_e4m3")), FAKE, FAKE, FAKE, None) == -2
+    assert q(None, FAKE, FAKE, FAKE, None) == -1
+    assert q(ctypes.byref(desc(T=0, d=256, I=256, w=E4, q="mx_e4m3")), None, None, None, None) == 0
+
+
 def test_route_align_and_graph_validate(lib):
     d = desc()
     ra = lib.moe_route_align
@@ -222,6 +251,9 @@ def test_bench_library_exports_and_validates():
     assert L.moe_bench_mfma_bf16(100, 3, None, None) == -1
     assert L.moe_bench_mfma_bf16(1, 3, ctypes.byref(r), None) == -9
     assert L.moe_bench_mfma_bf16(100, 1, ctypes.byref(r), None) == -9
+    assert L.moe_bench_mfma_fp8(100, 3, None, None) == -1
+    assert L.moe_bench_mfma_fp8(1, 3, ctypes.byref(r), None) == -9
+    assert L.moe_bench_mfma_fp8(100, 1, ctypes.byref(r), None) == -9
 
 
 def test_strerror_and_names(lib):
@@ -230,7 +262,8 @@ def test_strerror_and_names(lib):
         assert s and s != "unknown status"
     assert B.strerror(-99) == "unknown status"
     names = [B.moe_kernel_name(i) for i in range(B.MOE_KERNEL_COUNT)]
-    assert names == ["route_logits", "route_topk", "align", "ffn13", "ffn2", "combine"]
+    assert names == ["route_logits", "route_topk", "align", "ffn13", "ffn2", "combine",
+                     "quant_x"]
     assert B.moe_kernel_name(99) == ""
 
 

@@ -145,6 +145,17 @@ SMALL = [
     ("fp8_lds", dict(workload="fp8", d=1536, I=1536, E=16, k=4), 12, 0),
     ("fp8_lds", dict(workload="fp8", d=512, I=512, E=64, k=4, scale_mode="tensor"), 16, 0),
     ("skew_small", dict(workload="skew", d=192, I=128), 300, 0),
+    # W8A8 (block-scaled e4m3fn x and h, blocks of 256): one token, a ragged
+    # block, several blocks per expert, E = 1, per-tensor scales, more
+    # channel tiles than one, and W2's K split in two (I = 4096, few tiles)
+    ("w8a8", dict(workload="fp8", d=256, I=256, E=4, k=2, act_quant="mx_e4m3"), 1, 0),
+    ("w8a8", dict(workload="fp8", d=256, I=256, E=4, k=2, act_quant="mx_e4m3"), 37, 256),
+    ("w8a8", dict(workload="fp8", d=256, I=256, E=4, k=2, act_quant="mx_e4m3"), 700, 0),
+    ("w8a8", dict(workload="fp8", d=512, I=768, E=8, k=2, act_quant="mx_e4m3"), 1000, 0),
+    ("w8a8", dict(workload="fp8", d=768, I=512, E=1, k=1, act_quant="mx_e4m3"), 300, 0),
+    ("w8a8", dict(workload="fp8", d=256, I=512, E=16, k=4, act_quant="mx_e4m3",
+                  scale_mode="tensor"), 200, 0),
+    ("w8a8", dict(workload="fp8", d=256, I=4096, E=2, k=1, act_quant="mx_e4m3"), 300, 0),
 ]
 
 
@@ -155,7 +166,8 @@ def test_layer_small(name, over, T, bm):
     wl = over.pop("workload", name)
     inp = synth.make_inputs(wl, T=T, device=DEV, **over)
     sc = (inp.s13, inp.s2) if inp.w == "e4m3fn" else None
-    out = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, sc, block_m=bm)
+    out = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, sc, block_m=bm,
+                        act_quant=inp.act_quant)
     _, ids, _ = B.moe_route(inp.x, inp.w_gate, inp.top_k)
     torch.cuda.synchronize()
     r = compare_layer(inp, out, ids)
@@ -182,6 +194,60 @@ def test_forward_equals_stage_composition_and_is_deterministic():
     torch.cuda.synchronize()
     assert torch.equal(out1, out2)
     assert torch.equal(out1, out3)
+
+
+def _mx_probe_rows(T, d, seed):
+    """bf16 rows spanning magnitudes 2^-120 .. 2^120, with an all-zero
+    block, signed zeros, a block of subnormals, bf16's largest values and
+    values at e4m3fn rounding ties after scaling, and a saturating block."""
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(T, d, generator=g, dtype=torch.float64)
+    x *= torch.exp2(torch.linspace(-120, 120, T, dtype=torch.float64))[:, None]
+    x = x.to(torch.bfloat16)
+    if T >= 4 and d >= 128:
+        x[0, :32] = 0.0
+        x[0, 32:64] = -0.0
+        x[1, :32] = torch.tensor(2.0 ** -130, dtype=torch.bfloat16) * torch.arange(32)
+        x[2, :32] = torch.finfo(torch.bfloat16).max
+        x[2, 5] = -torch.finfo(torch.bfloat16).max
+        # block max 2^8 * 1.0 -> scale 2^0; 1.0625 (between e4m3fn 1 and
+        # 1.125) and 9.5 are ties and go to the even code; 500 saturates to 448
+        x[3, :32] = 1.0
+        x[3, 0], x[3, 1], x[3, 2], x[3, 3] = 256.0, 1.0625, 9.5, -9.5
+        x[3, 64:96] = 500.0
+    return x
+
+
+@pytest.mark.parametrize("T,d", [(1, 256), (37, 256), (300, 768), (2048, 7168)])
+def test_quantize_act_is_exact(T, d):
+    note(f"quantize_act T={T} d={d}")
+    x = _mx_probe_rows(T, d, T + d)
+    codes, exps = B.moe_quantize_act(x.to(DEV))
+    torch.cuda.synchronize()
+    ref_codes, ref_exps = oracle.mx_quantize(oracle.decode_bf16(x.view(torch.int16).numpy().view("uint16")))
+    assert np.array_equal(exps.cpu().numpy().astype(np.int32) - 127, ref_exps)
+    assert np.array_equal(codes.cpu().numpy(), ref_codes)
+
+
+def test_w8a8_forward_equals_stage_composition_and_is_deterministic():
+    inp = synth.make_inputs("fp8", T=300, device=DEV, d=512, I=512, E=8, k=2,
+                            act_quant="mx_e4m3")
+    sc = (inp.s13, inp.s2)
+    out1 = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, sc, act_quant="mx_e4m3")
+    out2 = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, sc, act_quant="mx_e4m3")
+    _, ids, w = B.moe_route(inp.x, inp.w_gate, inp.top_k)
+    counts, sorted_ids, block_expert, num_padded, bm = B.moe_align(
+        ids, inp.E, hidden=inp.d, intermediate=inp.I, weight_dtype=B.MOE_DTYPE_E4M3FN,
+        act_quant="mx_e4m3")
+    assert bm == 256
+    out3 = B.moe_expert_ffn(inp.x, inp.w13, inp.w2, inp.top_k, w, sorted_ids, block_expert,
+                            num_padded, sc, act_quant="mx_e4m3")
+    zero = B.moe_forward(inp.x[:0], inp.w_gate, inp.w13, inp.w2, inp.top_k, sc,
+                         act_quant="mx_e4m3")
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2)
+    assert torch.equal(out1, out3)
+    assert zero.shape == (0, inp.d)
 
 
 def test_output_guard_bands_untouched():
@@ -245,7 +311,7 @@ def _routing_exact(inp, ids, logits):
     desc = B.make_desc(inp.T, inp.d, inp.E, inp.I, B._act_code(inp.x), B._w_code(inp.w13))
     counts, sorted_ids, block_expert, num_padded, bm = B.moe_align(
         ids, inp.E, hidden=inp.d, intermediate=inp.I, act_dtype=desc.act_dtype,
-        weight_dtype=desc.weight_dtype)
+        weight_dtype=desc.weight_dtype, act_quant=inp.act_quant)
     ref = oracle.align(ref_ids, inp.E, bm)
     assert np.array_equal(counts.cpu().numpy(), ref["counts"])
     assert np.array_equal(sorted_ids.cpu().numpy(), ref["sorted_ids"])
@@ -256,7 +322,8 @@ def _routing_exact(inp, ids, logits):
 
 def _full_case(inp, tokens):
     sc = (inp.s13, inp.s2) if inp.w == "e4m3fn" else None
-    out = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, sc)
+    out = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, sc,
+                        act_quant=inp.act_quant)
     logits, ids, _ = B.moe_route(inp.x, inp.w_gate, inp.top_k)
     torch.cuda.synchronize()
     _routing_exact(inp, ids, logits)
@@ -294,6 +361,19 @@ def test_fp8_full_size(T):
     note(f"fp8 full size T={T}")
     inp = synth.make_inputs("fp8", T=T, device=DEV)
     _full_case(inp, np.linspace(0, T - 1, 4).astype(int))
+
+
+def test_prefill_w8a8_full_size():
+    note("prefill_w8a8 full size T=4096")
+    inp = synth.make_inputs("prefill_w8a8", device=DEV)
+    _full_case(inp, np.linspace(0, inp.T - 1, 8).astype(int))
+
+
+def test_fp8_shapes_w8a8_full_size():
+    # the fine-grained FP8 shapes (d = 7168, E = 256, top-8) in the W8A8 mode
+    note("fp8 shapes W8A8 T=2048")
+    inp = synth.make_inputs("fp8", T=2048, device=DEV, act_quant="mx_e4m3")
+    _full_case(inp, np.linspace(0, inp.T - 1, 4).astype(int))
 
 
 def test_skew_full_size():
