@@ -35,15 +35,35 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 typedef f32x4 Big8Acc[kBigTA][kBigNB];
 
-// 32 bytes of tile row `row` for lane group g: logical slots g and 4 + g.
-__device__ __forceinline__ i32x8 big8_frag(const uint8_t* op, int row, int g) {
-  const uint8_t* r = op + row * kBigRowBytes;
-  const int sw = big_swz(row);
-  const uint4 lo = *reinterpret_cast<const uint4*>(r + ((g ^ sw) << 4));
-  const uint4 hi = *reinterpret_cast<const uint4*>(r + (((4 + g) ^ sw) << 4));
-  return i32x8{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z),
-               static_cast<int>(lo.w), static_cast<int>(hi.x), static_cast<int>(hi.y),
-               static_cast<int>(hi.z), static_cast<int>(hi.w)};
+// A lane's LDS byte offsets inside a stage buffer.  Lane (r16, g) reads row
+// r16 of a 16-row tile, logical slots g and 4 + g.  Tiles start at multiples
+// of 16 rows, so a row's swizzle big_swz(row) = (r16 >> 1) & 7 is the same
+// for every tile and a tile's fragment is at these offsets plus the tile's
+// first row x 128 (a constant): four registers address every read.
+struct Big8Lane {
+  uint32_t a_lo, a_hi;  // weight rows from the wave's first weight row
+  uint32_t b_lo, b_hi;  // token rows from the wave's first token row
+};
+
+__device__ __forceinline__ Big8Lane big8_lane(int arow0, int brow0) {
+  const int lane = threadIdx.x & 63;
+  const int r16 = lane & 15, g = lane >> 4;
+  const uint32_t lo = r16 * kBigRowBytes + ((g ^ ((r16 >> 1) & 7)) << 4);
+  const uint32_t hi = lo ^ 64;  // slot 4 + g: (4 + g) ^ sw = (g ^ sw) ^ 4
+  return Big8Lane{arow0 * kBigRowBytes + lo, arow0 * kBigRowBytes + hi,
+                  kBigOperandBytes + brow0 * kBigRowBytes + lo,
+                  kBigOperandBytes + brow0 * kBigRowBytes + hi};
+}
+
+// 32 bytes of K for the lane, `row_bytes` = the tile's first row x 128
+// (relative to the wave's first row of that operand).
+__device__ __forceinline__ i32x8 big8_frag(const uint8_t* buf, uint32_t lo, uint32_t hi,
+                                           int row_bytes) {
+  const uint4 l = *reinterpret_cast<const uint4*>(buf + lo + row_bytes);
+  const uint4 h = *reinterpret_cast<const uint4*>(buf + hi + row_bytes);
+  return i32x8{static_cast<int>(l.x), static_cast<int>(l.y), static_cast<int>(l.z),
+               static_cast<int>(l.w), static_cast<int>(h.x), static_cast<int>(h.y),
+               static_cast<int>(h.z), static_cast<int>(h.w)};
 }
 
 // acc += A . B over one stage's 128 K; B's K block l/16 scaled by 2^(sb - 127).
@@ -51,78 +71,124 @@ __device__ __forceinline__ f32x4 big8_mfma(i32x8 a, i32x8 b, f32x4 c, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, kE8M0One, 0, sb);
 }
 
-// Per-lane sources of the activation exponents: each token row has K/32
-// exponent bytes; one dword holds a stage's four blocks.
+// The activation exponents of a stage travel with it: the block's 256 token
+// rows x 4 bytes (K blocks 4s .. 4s + 3 of each row) go to a 1 KB LDS array
+// per buffer, loaded by waves 0..3 (64 rows each, one 4-byte direct-to-LDS
+// load per lane).  Kept out of registers: the loop runs at the 256-register
+// limit.
+constexpr int kBig8ExpBytes = kBigN * 4;
+
+#ifndef MOE_BIG8_PREFETCH
+#define MOE_BIG8_PREFETCH 1
+#endif
+
 struct Big8Scales {
   __amdgpu_buffer_rsrc_t r;
-  uint32_t row[kBigNB];  // byte offset of this lane's token row u (token column l%16 of tile u)
-  int shift;             // 8 * (l / 16): this lane's block inside the dword
+  uint32_t off;  // waves 0..3: byte offset of token row 64 * wave + lane's exponents, k = 0
 
-  __device__ __forceinline__ void load(int (&sc)[kBigNB], int s) const {
-#pragma unroll
-    for (int u = 0; u < kBigNB; ++u)
-      sc[u] = __builtin_amdgcn_raw_buffer_load_b32(r, row[u] + 4 * s, 0, 0);
+  __device__ __forceinline__ void load(uint8_t* lds, int s, int wave) const {
+    if (wave < kBigN / 64)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)(lds + 256 * wave), 4, off + 4 * s, 0, 0, 0);
   }
-  __device__ __forceinline__ int pick(int word) const { return (word >> shift) & 0xff; }
 };
 
 // One stage: wait for this wave's loads of `cur` (and its exponents), meet
-// the other waves, issue the next stage into `nxt` with its exponents
-// (when kIssue), then the stage's MFMAs in two halves of the weight tiles
-// (the token fragments are read once).  A wave whose token rows are all
-// padding (kLive false) only loads and meets the barriers.
-template <bool kIssue, bool kLive>
+// the other waves, issue the next stage into `nxt` with its exponents (when
+// kIssue), then the stage's 32 MFMAs in four groups of two weight tiles x
+// the four token tiles.  The token fragments are read once; with
+// MOE_BIG8_PREFETCH the weight fragments of group q + 1 are read while group
+// q's MFMAs run (two register sets).  The scheduling barrier after the issue
+// keeps the compiler from sinking the next stage's loads to the end of the
+// stage, which would leave nothing in flight during the MFMAs.  A wave whose
+// token rows are all padding (kLive false) only loads and meets the barriers.
+// kUp: first tile row of the wave's second group of four weight tiles,
+// relative to its first (128 for W13's up rows, 64 for W2).  ex_off: this
+// lane's exponent byte in the stage's exponent array (token row
+// 64 wn + r16, block g; tile u adds 64 bytes).
+template <bool kIssue, bool kLive, int kUp>
 __device__ __forceinline__ void big8_stage(const BigLoader& ld, const Big8Scales& sx,
-                                           const uint8_t* cur, uint8_t* nxt, int s, int wave,
-                                           int arow0, int arow_up, int brow0,
-                                           const int (&sc)[kBigNB], int (&scn)[kBigNB],
-                                           Big8Acc& acc) {
+                                           const uint8_t* cur, uint8_t* nxt, const uint8_t* ex,
+                                           uint8_t* exn, int s, int wave, const Big8Lane& ln,
+                                           uint32_t ex_off, Big8Acc& acc) {
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   big_barrier();
   if (kIssue) {
     big_issue(ld, nxt, static_cast<uint32_t>(s + 1) * kBig8K, wave);
-    sx.load(scn, s + 1);
+    sx.load(exn, s + 1, wave);
   }
+  __builtin_amdgcn_sched_barrier(0);
   if (!kLive) return;
-  const int lane = threadIdx.x & 63;
-  const int r16 = lane & 15, g = lane >> 4;
-  const uint8_t* opb = cur + kBigOperandBytes;
-  i32x8 b[kBigNB], a[4];
+  // Opaque copies of the lane offsets: otherwise the compiler hoists the
+  // fragment addresses of both buffers out of the loop as separate
+  // registers, runs out and spills them; this way each stage forms its bases
+  // and every tile offset is a read's immediate.
+  uint32_t alo = ln.a_lo, ahi = ln.a_hi, blo = ln.b_lo, bhi = ln.b_hi, eo = ex_off;
+  asm volatile("" : "+v"(alo), "+v"(ahi), "+v"(blo), "+v"(bhi), "+v"(eo));
+  i32x8 b[kBigNB];
   int sb[kBigNB];
 #pragma unroll
   for (int u = 0; u < kBigNB; ++u) {
-    b[u] = big8_frag(opb, brow0 + 16 * u + r16, g);
-    sb[u] = sx.pick(sc[u]);
+    b[u] = big8_frag(cur, blo, bhi, 16 * u * kBigRowBytes);
+    sb[u] = ex[eo + 64 * u];
   }
+  // weight tile t: rows 16t (t < 4) and kUp + 16(t - 4) past the wave's first
+  constexpr auto arow = [](int t) { return (t < 4 ? 16 * t : kUp + 16 * (t - 4)) * kBigRowBytes; };
+#if MOE_BIG8_PREFETCH
+  i32x8 a[2][2];
+  a[0][0] = big8_frag(cur, alo, ahi, arow(0));
+  a[0][1] = big8_frag(cur, alo, ahi, arow(1));
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int rbase = half ? arow_up : arow0;
+  for (int q = 0; q < kBigTA / 2; ++q) {
+    if (q + 1 < kBigTA / 2) {
+      a[(q + 1) & 1][0] = big8_frag(cur, alo, ahi, arow(2 * q + 2));
+      a[(q + 1) & 1][1] = big8_frag(cur, alo, ahi, arow(2 * q + 3));
+    }
 #pragma unroll
-    for (int t = 0; t < 4; ++t) a[t] = big8_frag(cur, rbase + 16 * t + r16, g);
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int u = 0; u < kBigNB; ++u)
-        acc[4 * half + t][u] = big8_mfma(a[t], b[u], acc[4 * half + t][u], sb[u]);
+        acc[2 * q + j][u] = big8_mfma(a[q & 1][j], b[u], acc[2 * q + j][u], sb[u]);
+    __builtin_amdgcn_sched_barrier(0);
   }
+#else
+#pragma unroll
+  for (int q = 0; q < kBigTA / 2; ++q) {
+    const i32x8 a0 = big8_frag(cur, alo, ahi, arow(2 * q));
+    const i32x8 a1 = big8_frag(cur, alo, ahi, arow(2 * q + 1));
+#pragma unroll
+    for (int u = 0; u < kBigNB; ++u) {
+      acc[2 * q][u] = big8_mfma(a0, b[u], acc[2 * q][u], sb[u]);
+      acc[2 * q + 1][u] = big8_mfma(a1, b[u], acc[2 * q + 1][u], sb[u]);
+    }
+  }
+#endif
 }
 
-template <bool kLive>
+template <bool kLive, int kUp>
 __device__ __forceinline__ void big8_run(const BigLoader& ld, const Big8Scales& sx,
-                                         uint8_t* const (&buf)[2], int nst, int wave, int arow0,
-                                         int arow_up, int brow0, Big8Acc& acc) {
-  int sc0[kBigNB], sc1[kBigNB];
+                                         uint8_t* const (&buf)[2], uint8_t* const (&ex)[2],
+                                         int nst, int wave, const Big8Lane& ln, uint32_t ex_off,
+                                         Big8Acc& acc) {
   big_issue(ld, buf[0], 0, wave);
-  sx.load(sc0, 0);
+  sx.load(ex[0], 0, wave);
   // nst is even (d % 256 == 0 for W13, splits of I in multiples of 256 for W2)
   for (int s = 0; s + 2 < nst; s += 2) {
-    big8_stage<true, kLive>(ld, sx, buf[0], buf[1], s, wave, arow0, arow_up, brow0, sc0, sc1, acc);
-    big8_stage<true, kLive>(ld, sx, buf[1], buf[0], s + 1, wave, arow0, arow_up, brow0, sc1, sc0, acc);
+    big8_stage<true, kLive, kUp>(ld, sx, buf[0], buf[1], ex[0], ex[1], s, wave, ln, ex_off, acc);
+    big8_stage<true, kLive, kUp>(ld, sx, buf[1], buf[0], ex[1], ex[0], s + 1, wave, ln, ex_off,
+                                 acc);
   }
-  big8_stage<true, kLive>(ld, sx, buf[0], buf[1], nst - 2, wave, arow0, arow_up, brow0, sc0, sc1, acc);
-  big8_stage<false, kLive>(ld, sx, buf[1], buf[0], nst - 1, wave, arow0, arow_up, brow0, sc1, sc0, acc);
+  big8_stage<true, kLive, kUp>(ld, sx, buf[0], buf[1], ex[0], ex[1], nst - 2, wave, ln, ex_off,
+                               acc);
+  big8_stage<false, kLive, kUp>(ld, sx, buf[1], buf[0], ex[1], ex[0], nst - 1, wave, ln, ex_off,
+                                acc);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
+
+#define BIG8_EXPS(name)                                                          \
+  __shared__ __attribute__((aligned(1024))) uint8_t name##0[kBig8ExpBytes];      \
+  __shared__ __attribute__((aligned(1024))) uint8_t name##1[kBig8ExpBytes];      \
+  uint8_t* const name[2] = {name##0, name##1}
 
 // E8M0 exponent of a block whose largest magnitude is amax: floor(log2 amax)
 // - 8 (8 = exponent of 448, e4m3fn's largest value), 0 for amax = 0, at
@@ -201,6 +267,7 @@ __global__ __launch_bounds__(kBigThreads) void ffn13_big8_kernel(
     const int32_t* __restrict__ num_padded, uint8_t* __restrict__ hq, uint8_t* __restrict__ sh,
     int d, int I, int k, int A, int gx, int gy) {
   BIG_BUFFERS(buf);
+  BIG8_EXPS(exb);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const BigTile tl = big_tile_of(blockIdx.x, gx, gy);
@@ -236,11 +303,9 @@ __global__ __launch_bounds__(kBigThreads) void ffn13_big8_kernel(
   const int kb = d / kMx;  // exponent bytes per token row
   Big8Scales sc;
   sc.r = big_rsrc(sx, static_cast<size_t>(T) * kb);
-  sc.shift = 8 * g;
-#pragma unroll
-  for (int u = 0; u < kBigNB; ++u) {
-    const int f = blk[(kBigN / kBigWn) * wn + 16 * u + r16];
-    sc.row[u] = static_cast<uint32_t>(f < A ? f / k : 0) * kb;
+  {
+    const int f = blk[64 * (wave & 3) + lane];  // waves 0..3 load rows 64 wave + lane
+    sc.off = static_cast<uint32_t>(f < A ? f / k : 0) * kb;
   }
   Big8Acc acc;
 #pragma unroll
@@ -250,10 +315,13 @@ __global__ __launch_bounds__(kBigThreads) void ffn13_big8_kernel(
 
   const bool live = __builtin_amdgcn_readfirstlane(blk[(kBigN / kBigWn) * wn]) < A;
   const int nst = d / kBig8K;
+  // weight rows: gate 64wm .. +63 and up 128 + 64wm .. +63 of the tile
+  const Big8Lane ln = big8_lane(64 * wm, (kBigN / kBigWn) * wn);
+  const uint32_t ex_off = ((kBigN / kBigWn) * wn + r16) * 4 + g;
   if (live)
-    big8_run<true>(ld, sc, buf, nst, wave, 64 * wm, 128 + 64 * wm, (kBigN / kBigWn) * wn, acc);
+    big8_run<true, 128>(ld, sc, buf, exb, nst, wave, ln, ex_off, acc);
   else
-    big8_run<false>(ld, sc, buf, nst, wave, 64 * wm, 128 + 64 * wm, (kBigN / kBigWn) * wn, acc);
+    big8_run<false, 128>(ld, sc, buf, exb, nst, wave, ln, ex_off, acc);
 
   // weight scales of this lane's channels n0 + 64wm + 16t + 4g + v
   float sg[4][4], su[4][4];
@@ -306,6 +374,7 @@ __global__ __launch_bounds__(kBigThreads) void ffn2_big8_kernel(
     const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded,
     float* __restrict__ y_part, int d, int I, int A, int ksplit, int gx, int gy) {
   BIG_BUFFERS(buf);
+  BIG8_EXPS(exb);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const BigTile tl = big_tile_of(blockIdx.x, gx, gy);
@@ -341,10 +410,7 @@ __global__ __launch_bounds__(kBigThreads) void ffn2_big8_kernel(
   const int ib = I / kMx;
   Big8Scales sc;
   sc.r = big_rsrc(sh + hrow0 * ib, static_cast<size_t>(kBigN) * ib);
-  sc.shift = 8 * g;
-#pragma unroll
-  for (int u = 0; u < kBigNB; ++u)
-    sc.row[u] = static_cast<uint32_t>((kBigN / kBigWn) * wn + 16 * u + r16) * ib + k_begin / kMx;
+  sc.off = static_cast<uint32_t>(64 * (wave & 3) + lane) * ib + k_begin / kMx;
   Big8Acc acc;
 #pragma unroll
   for (int t = 0; t < kBigTA; ++t)
@@ -352,10 +418,13 @@ __global__ __launch_bounds__(kBigThreads) void ffn2_big8_kernel(
     for (int u = 0; u < kBigNB; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const bool live = __builtin_amdgcn_readfirstlane(blk[(kBigN / kBigWn) * wn]) < A;
+  // weight rows 128wm .. +127 of the tile
+  const Big8Lane ln = big8_lane(128 * wm, (kBigN / kBigWn) * wn);
+  const uint32_t ex_off = ((kBigN / kBigWn) * wn + r16) * 4 + g;
   if (live)
-    big8_run<true>(ld, sc, buf, nst, wave, 128 * wm, 128 * wm + 64, (kBigN / kBigWn) * wn, acc);
+    big8_run<true, 64>(ld, sc, buf, exb, nst, wave, ln, ex_off, acc);
   else
-    big8_run<false>(ld, sc, buf, nst, wave, 128 * wm, 128 * wm + 64, (kBigN / kBigWn) * wn, acc);
+    big8_run<false, 64>(ld, sc, buf, exb, nst, wave, ln, ex_off, acc);
 
   // lane: token column r16 of tile u, channels n0 + 128wm + 16t + 4g .. +3
 #pragma unroll
