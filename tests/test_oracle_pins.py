@@ -525,3 +525,16 @@ def test_layer_w8a8_matches_dense_bruteforce():
     assert _rel(r["out"], out) < 1e-12
     # and it is a different layer from the weight-only one (the quantisation shows)
     assert _rel(oracle.moe_forward(**kw, block_m=16)["out"], out) > 1e-4
+
+
+def test_w8a8_quantisation_error_is_of_e4m3_size():
+    # Rounding to 3 mantissa bits costs about 2^-4 / sqrt(3) ~ 3.6% RMS per
+    # value; x and h are both quantised, so the layer moves by a few
+    # percent: far from zero (the quantisation is applied) and inside the
+    # fp8 budget of 6e-2 (no scale off by a power of two, no lost block).
+    from mixture_experts_moe_amd import synth
+    inp = synth.make_inputs("fp8", T=32, d=256, E=4, k=2, I=256)
+    kw = synth.to_oracle(inp)
+    a = oracle.moe_forward(**kw, block_m=16)["out"]
+    b = oracle.moe_forward(**kw, block_m=16, act_quant="mx_e4m3")["out"]
+    assert 0.02 < _rel(b, a) < 0.06
