@@ -423,26 +423,29 @@ def test_route_align_equals_route_then_align(T, E, k, bm, d, I):
     ("decode_bf16", 16, dict(d=768, I=2048, E=32)),          # weights streamed through LDS
     ("fp8", 16, dict(d=512, I=512, E=16, k=4)),
     ("decode_bf16", 300, dict(d=512, I=256)),               # 128-token GEMM
+    ("decode_bf16", 600, dict(d=512, I=256, E=4)),          # 256-token big tile
+    ("fp8", 300, dict(d=512, I=512, E=8, k=2, act_quant="mx_e4m3")),  # W8A8
 ])
 def test_graph_replay_matches_eager(wl, T, over):
     note(f"graph {wl} T={T} {over}")
     inp = synth.make_inputs(wl, T=T, device=DEV, x_std=1.0, **over)
     sc = (inp.s13, inp.s2) if inp.w == "e4m3fn" else None
-    ref = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, sc)
+    q = inp.act_quant
+    ref = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, sc, act_quant=q)
     out = torch.empty_like(ref)
-    graph = B.MoeGraph(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, sc, out=out)
+    graph = B.MoeGraph(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, sc, out=out, act_quant=q)
     try:
         for rep in range(3):
             out.fill_(float("nan"))                  # eager work between replays
             graph.launch()
-            other = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, sc)
+            other = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, sc, act_quant=q)
             torch.cuda.synchronize()
             assert torch.equal(out, ref), f"replay {rep}"
             assert torch.equal(other, ref)
         # the next step's tokens, written into the recorded x
         x2 = synth.make_x(inp.T, inp.d, inp.act, 1.0, 1, DEV)
         inp.x.copy_(x2)
-        ref2 = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, sc)
+        ref2 = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, sc, act_quant=q)
         graph.launch()
         torch.cuda.synchronize()
         assert torch.equal(out, ref2)
