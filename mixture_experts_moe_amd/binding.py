@@ -228,7 +228,17 @@ def _scales(w13: torch.Tensor, scales) -> Optional[moe_scales]:
     s13, s2 = scales
     if s13.dtype != torch.float32 or s2.dtype != torch.float32:
         raise TypeError("scales must be float32")
-    mode = MOE_SCALE_PER_CHANNEL if s13.dim() == 2 else MOE_SCALE_PER_TENSOR
+    if _dev(w13, s13, s2) != w13.device:
+        raise ValueError("scales must be on the weights' device")
+    E, two_i, d = w13.shape
+    if s13.dim() == 2:
+        mode = MOE_SCALE_PER_CHANNEL
+        if tuple(s13.shape) != (E, two_i) or tuple(s2.shape) != (E, d):
+            raise ValueError(f"per-channel scales must be [{E}, {two_i}] and [{E}, {d}]")
+    else:
+        mode = MOE_SCALE_PER_TENSOR
+        if tuple(s13.shape) != (E,) or tuple(s2.shape) != (E,):
+            raise ValueError(f"per-tensor scales must be [{E}] and [{E}]")
     return moe_scales(mode, 0, s13.data_ptr(), s2.data_ptr())
 
 

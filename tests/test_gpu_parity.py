@@ -250,6 +250,21 @@ def test_w8a8_forward_equals_stage_composition_and_is_deterministic():
     assert zero.shape == (0, inp.d)
 
 
+def test_binding_rejects_bad_scales_before_any_launch():
+    inp = synth.make_inputs("fp8", T=4, device=DEV, d=256, I=128, E=4, k=2)
+    bad = [
+        (inp.s13.cpu(), inp.s2),                          # host memory
+        (inp.s13[:, :-1].contiguous(), inp.s2),           # wrong per-channel shape
+        (inp.s13[:, 0].contiguous(), inp.s2),             # per-tensor s13 with per-channel s2
+        (inp.s13.t(), inp.s2),                            # not contiguous
+    ]
+    for sc in bad:
+        with pytest.raises((ValueError, TypeError)):
+            B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, sc)
+    with pytest.raises(ValueError):
+        B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k)   # e4m3fn needs scales
+
+
 def test_output_guard_bands_untouched():
     inp = synth.make_inputs("decode_bf16", T=33, device=DEV, d=256, I=128, x_std=1.0)
     pad = 64
