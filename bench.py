@@ -63,6 +63,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-kernel breakdown pass")
     ap.add_argument("--block-m", type=int, default=0, help="regrouping block size (0 = library default)")
+    ap.add_argument("--act-quant", default=None, choices=["mx_e4m3", "none"],
+                    help="override the workload's activation mode: mx_e4m3 (W8A8, e4m3fn weights "
+                         "only) or none (activations as given)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the layer, run a plain device copy of this many bytes "
                          "(reference reading for HBM traffic counters)")
@@ -313,6 +316,8 @@ def main() -> int:
     torch.cuda.set_device(dev)
     log(f"generating {wl} inputs, batches {batches}")
     base = synth.make_inputs(wl, T=batches[0], device=dev)
+    if args.act_quant:
+        base = replace(base, act_quant=None if args.act_quant == "none" else args.act_quant)
     cfg = synth.WORKLOADS[wl]
     inputs = [replace(base, x=synth.make_x(T, base.d, base.act, cfg["x_std"], 0, dev, skew=cfg["skew"]))
               for T in batches]
@@ -406,7 +411,8 @@ def main() -> int:
     roof["kernel"] = "ffn13 (grouped W13 + SiLU*mul)"
     roof["avg_launch_us"] = round(ffn13_ms / max(ffn13_n, 1) * 1e3, 2)
     roof["launches"] = ffn13_n
-    roof["traffic"] = load_traffic(wl)
+    # the stored counters belong to the workload's own mode
+    roof["traffic"] = None if args.act_quant else load_traffic(wl)
 
     # the same step as one recorded graph per forward (moe_graph_*): one
     # launch per forward, weights rotated through the same copies
