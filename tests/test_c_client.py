@@ -1,0 +1,61 @@
+"""The C ABI from plain C: a C99 client compiled against include/moe.h and
+linked with libmoe.so calls the host-only entry points (sizing, validation,
+status text) and checks their results.  No GPU is touched."""
+
+import os
+import shutil
+import subprocess
+import textwrap
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PKG = os.path.join(ROOT, "mixture_experts_moe_amd")
+
+C_SOURCE = textwrap.dedent(r"""
+    #include <stdio.h>
+    #include <string.h>
+    #include "moe.h"
+
+    int main(void) {
+      moe_desc d = {64, 4096, 8, 14336, MOE_DTYPE_BF16, MOE_DTYPE_BF16, 0, MOE_ACT_AS_IS};
+      int32_t bm = 0;
+      int64_t cap = 0;
+      size_t ws = 0;
+      if (moe_align_capacity(&d, 2, &bm, &cap) != MOE_OK) return 1;
+      /* capacity = roundup(A + min(E, A) * (B - 1), B) */
+      int64_t A = 64 * 2, n = A + 8 * (bm - 1);
+      if (cap != (n + bm - 1) / bm * bm) return 2;
+      if (moe_workspace_bytes(&d, 2, 1, &ws) != MOE_OK || ws == 0) return 3;
+      d.hidden = 100;                                   /* not a multiple of 64 */
+      if (moe_workspace_bytes(&d, 2, 1, &ws) != MOE_ERR_BAD_SHAPE) return 4;
+      d.hidden = 4096;
+      d.act_quant = MOE_ACT_MX_E4M3;                    /* W8A8 needs e4m3fn weights */
+      if (moe_workspace_bytes(&d, 2, 1, &ws) != MOE_ERR_BAD_DTYPE) return 5;
+      d.weight_dtype = MOE_DTYPE_E4M3FN;
+      if (moe_align_capacity(&d, 2, &bm, &cap) != MOE_OK || bm != 256) return 6;
+      if (moe_forward(NULL, NULL, NULL, NULL, NULL, 2, NULL, NULL, NULL, 0, NULL) != MOE_ERR_NULL_PTR)
+        return 7;
+      if (strlen(moe_strerror(MOE_ERR_WORKSPACE)) == 0) return 8;
+      printf("ok %d %lld\n", (int)bm, (long long)cap);
+      return 0;
+    }
+""")
+
+
+def test_c99_client_uses_the_abi(tmp_path):
+    lib = os.path.join(PKG, "libmoe.so")
+    if not os.path.exists(lib):
+        pytest.skip("libmoe.so is not built")
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "client.c"
+    src.write_text(C_SOURCE)
+    exe = tmp_path / "client"
+    subprocess.run([cc, "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    str(src), "-o", str(exe), "-L", PKG, "-lmoe", f"-Wl,-rpath,{PKG}"],
+                   check=True, capture_output=True, text=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
+    assert r.stdout.startswith("ok 256 ")
