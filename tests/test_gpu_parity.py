@@ -156,6 +156,11 @@ SMALL = [
     ("w8a8", dict(workload="fp8", d=256, I=512, E=16, k=4, act_quant="mx_e4m3",
                   scale_mode="tensor"), 200, 0),
     ("w8a8", dict(workload="fp8", d=256, I=4096, E=2, k=1, act_quant="mx_e4m3"), 300, 0),
+    # extreme aspect ratios: a very wide hidden size, a very long intermediate
+    ("bf16_wide", dict(workload="decode_bf16", d=65536, I=64, E=2, k=1, x_std=1.0), 5, 0),
+    ("bf16_tall", dict(workload="decode_bf16", d=64, I=65536, E=2, k=2, x_std=1.0), 5, 0),
+    ("fp8_wide", dict(workload="fp8", d=65536, I=64, E=3, k=2), 4, 0),
+    ("w8a8_wide", dict(workload="fp8", d=32768, I=256, E=2, k=1, act_quant="mx_e4m3"), 9, 0),
 ]
 
 
