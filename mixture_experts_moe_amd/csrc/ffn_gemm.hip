@@ -37,6 +37,14 @@ constexpr int kGemmNSub = kGemmTokens / 16;
 #ifndef MOE_GEMM_RN
 #define MOE_GEMM_RN 1
 #endif
+// W2 takes two channel tiles per wave: each workgroup then covers 256
+// output channels, so the block's h rows (streamed through LDS once per
+// workgroup) are read half as often.  Measured side by side at the fp8
+// workload's T = 2048: W2 1433 against 1444 us (W13 is much slower that way,
+// 2.0 -> 2.9 ms, and keeps one).
+#ifndef MOE_GEMM_RN2
+#define MOE_GEMM_RN2 2
+#endif
 
 // Rows of the token tile this thread stages: KC/8 16-byte pieces per row,
 // piece q = tid + 64*WAVES*i, row = q / (KC/8).  Rows that hold no token
@@ -322,8 +330,9 @@ __global__ __launch_bounds__(64 * WAVES) void ffn2_gemm_kernel(
 
 namespace {
 
-constexpr int kPG = MOE_GEMM_PIPE, kRNG = MOE_GEMM_RN;
+constexpr int kPG = MOE_GEMM_PIPE, kRNG = MOE_GEMM_RN, kRNG2 = MOE_GEMM_RN2;
 static_assert(kRNG == 1 || kRNG == 2, "channel tiles per wave: 1 or 2");
+static_assert(kRNG2 == 1 || kRNG2 == 2, "channel tiles per wave: 1 or 2");
 
 // A workgroup covers 16 * RN * WAVES output channels; the launchers pick the
 // widest configuration whose channel group divides the channel count (a
@@ -357,8 +366,8 @@ void ffn2_gemm_launch(const FfnArgs& a, hipStream_t s) {
 
 template <typename WT, int KC>
 void ffn2_gemm_go(const FfnArgs& a, hipStream_t s) {
-  if (a.d % (kWaves2 * 16 * kRNG) == 0)
-    ffn2_gemm_launch<WT, KC, kRNG, kWaves2>(a, s);
+  if (a.d % (kWaves2 * 16 * kRNG2) == 0)
+    ffn2_gemm_launch<WT, KC, kRNG2, kWaves2>(a, s);
   else
     ffn2_gemm_launch<WT, KC, 1, 4>(a, s);
 }
