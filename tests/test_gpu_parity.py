@@ -472,3 +472,53 @@ def test_graph_replay_matches_eager(wl, T, over):
         assert not torch.equal(ref2, ref)
     finally:
         graph.close()
+
+
+# ---------------------------------------------------------------- seeded shape sweep
+
+def _sweep_cases(n=48, seed=2024):
+    """Seeded random layer configurations over the ABI's limits (small
+    enough for the oracle): every weight format, block size and mode."""
+    import random
+    rng = random.Random(seed)
+    cases = []
+    while len(cases) < n:
+        fmt = rng.choice(["f32", "bf16", "bf16", "e4m3fn", "e4m3fn", "w8a8"])
+        if fmt == "w8a8":
+            d = 256 * rng.randint(1, 3)
+            I = 256 * rng.randint(1, 3)
+        else:
+            d = 64 * rng.randint(1, 12)
+            I = 64 * rng.randint(1, 12)
+        E = rng.choice([1, 2, 3, 5, 8, 13, 16, 33, 64])
+        k = rng.randint(1, min(E, 8))
+        T = rng.choice([1, 2, 7, 16, 17, 40, 64, 65, 130, 300])
+        bm = rng.choice([0, 0, 16, 32, 64, 128])
+        if fmt == "f32":
+            bm = rng.choice([0, 16])
+        if fmt == "w8a8":
+            bm = rng.choice([0, 256])
+        if bm == 128 and fmt != "bf16" and fmt != "e4m3fn":
+            bm = 0
+        cases.append((fmt, T, d, I, E, k, bm, rng.choice(["channel", "tensor"])))
+    return cases
+
+
+@pytest.mark.parametrize("fmt,T,d,I,E,k,bm,smode", _sweep_cases(),
+                         ids=lambda v: str(v))
+def test_layer_seeded_sweep(fmt, T, d, I, E, k, bm, smode):
+    note(f"sweep {fmt} T={T} d={d} I={I} E={E} k={k} B={bm} {smode}")
+    if fmt == "f32":
+        inp = synth.make_inputs("tiny_fp32", T=T, device=DEV, d=d, I=I, E=E, k=k)
+    elif fmt == "bf16":
+        inp = synth.make_inputs("decode_bf16", T=T, device=DEV, d=d, I=I, E=E, k=k, x_std=1.0)
+    else:
+        inp = synth.make_inputs("fp8", T=T, device=DEV, d=d, I=I, E=E, k=k, scale_mode=smode,
+                                act_quant="mx_e4m3" if fmt == "w8a8" else None)
+    sc = (inp.s13, inp.s2) if inp.w == "e4m3fn" else None
+    out = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, sc, block_m=bm,
+                        act_quant=inp.act_quant)
+    _, ids, _ = B.moe_route(inp.x, inp.w_gate, inp.top_k)
+    torch.cuda.synchronize()
+    r = compare_layer(inp, out, ids)
+    note(f"  rel_err={r['rel_err']:.3e} excluded={r['excluded']}")
