@@ -17,6 +17,15 @@ TOL = {"f32": 1e-5, "bf16": 2e-2, "e4m3fn": 6e-2}
 # e4m3fn weights alike.  5e-3 catches systematic errors (a wrong dequantised
 # code, a dropped scale) that the looser bound above could hide.
 DERIVED_TOL = {"f32": 1e-5, "bf16": 5e-3, "e4m3fn": 5e-3}
+# The W8A8 mode adds one more rounding point: h is quantised to e4m3fn from
+# fp32 on the GPU and from fp64 in the oracle, so a value within fp32 error of
+# a rounding midpoint takes the neighbouring code (one step, 6-12% of that
+# value).  Over many slots those flips are rare and average out (measured
+# 1.7-2.3e-3 at 37+ tokens), but with a handful of slots one flip moves the
+# relative error by a few 1e-3 (4.3e-3 at T = 2): the mode's derived bound is
+# 1e-2, still far below anything a wrong block exponent (a factor of 2) or a
+# lost block would give.
+DERIVED_TOL_W8A8 = 1e-2
 
 
 def rel_fro(got: np.ndarray, ref: np.ndarray) -> float:
@@ -71,7 +80,8 @@ def compare_layer(inp: synth.MoEInputs, out_gpu: torch.Tensor, gpu_ids: torch.Te
     assert routed_same, "GPU routing differs from the oracle on a token that is not a near tie"
     assert np.all(np.isfinite(got)), "non-finite outputs"
     assert err <= tol, f"relative Frobenius error {err:.3e} > {tol:.1e}"
-    assert err <= DERIVED_TOL[inp.w], (
+    derived = DERIVED_TOL_W8A8 if inp.act_quant else DERIVED_TOL[inp.w]
+    assert err <= derived, (
         f"relative Frobenius error {err:.3e} above the bound derived from the kernels' rounding "
-        f"({DERIVED_TOL[inp.w]:.1e})")
+        f"({derived:.1e})")
     return {"rel_err": err, "excluded": int(excl.sum()), "compared": int(keep.sum())}
