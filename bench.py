@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-kernel breakdown pass")
     ap.add_argument("--block-m", type=int, default=0, help="regrouping block size (0 = library default)")
+    ap.add_argument("--schedule", default="auto", choices=["auto", "static", "queue"],
+                    help="tile schedule of the 128-token-block expert kernels")
     ap.add_argument("--act-quant", default=None, choices=["mx_e4m3", "none"],
                     help="override the workload's activation mode: mx_e4m3 (W8A8, e4m3fn weights "
                          "only) or none (activations as given)")
@@ -330,7 +332,7 @@ def main() -> int:
     wss = []
     for i in inputs:
         desc = B.make_desc(i.T, i.d, i.E, i.I, B._act_code(i.x), B._w_code(i.w13),
-                           act_quant=i.act_quant)
+                           act_quant=i.act_quant, schedule=args.schedule)
         desc.block_m = args.block_m
         wss.append(torch.empty(max(B.moe_workspace_bytes(desc, i.top_k, True), 1), dtype=torch.uint8, device=dev))
     torch.cuda.synchronize()
@@ -343,7 +345,8 @@ def main() -> int:
             w13, w2 = copies[counter[0] % len(copies)]
             counter[0] += 1
             B.moe_forward(i.x, i.w_gate, w13, w2, i.top_k, sc, outs[bi], block_m=args.block_m,
-                          workspace=wss[bi], act_quant=i.act_quant)
+                          workspace=wss[bi], act_quant=i.act_quant,
+                          schedule=args.schedule)
 
     # realised routing -> algorithmic work per forward
     work = []
@@ -411,13 +414,14 @@ def main() -> int:
     roof["kernel"] = "ffn13 (grouped W13 + SiLU*mul)"
     roof["avg_launch_us"] = round(ffn13_ms / max(ffn13_n, 1) * 1e3, 2)
     roof["launches"] = ffn13_n
-    # the stored counters belong to the workload's own mode
-    roof["traffic"] = None if args.act_quant else load_traffic(wl)
+    # the stored counters belong to the workload's own mode and schedule
+    roof["traffic"] = None if args.act_quant or args.schedule != "auto" else load_traffic(wl)
 
     # the same step as one recorded graph per forward (moe_graph_*): one
     # launch per forward, weights rotated through the same copies
     graphs = [[B.MoeGraph(i.x, i.w_gate, w13, w2, i.top_k, sc, out=outs[bi], block_m=args.block_m,
-                          workspace=wss[bi], act_quant=i.act_quant) for (w13, w2) in copies]
+                          workspace=wss[bi], act_quant=i.act_quant,
+                          schedule=args.schedule) for (w13, w2) in copies]
               for bi, i in enumerate(inputs)]
     gcount = [0]
 
@@ -453,7 +457,8 @@ def main() -> int:
                 counter[0] += 1
                 ev0.record()
                 B.moe_forward(i.x, i.w_gate, w13, w2, i.top_k, sc, outs[bi], block_m=args.block_m,
-                              workspace=wss[bi], act_quant=i.act_quant)
+                              workspace=wss[bi], act_quant=i.act_quant,
+                              schedule=args.schedule)
                 ev1.record()
                 torch.cuda.synchronize()
                 fws.append(ev0.elapsed_time(ev1))
@@ -516,6 +521,7 @@ def main() -> int:
             "batches_T": list(batches),
             "hidden": base.d, "experts": base.E, "top_k": base.top_k, "intermediate": base.I,
             "act": base.act, "weights": base.w, "act_quant": base.act_quant,
+            "schedule": args.schedule,
             "tokens_per_step": tokens,
             "alg_bytes_per_step": bytes_step,
             "alg_flops_per_step": flops_step,

@@ -101,6 +101,20 @@ extern "C" {
 #define MOE_ACT_AS_IS 0
 #define MOE_ACT_MX_E4M3 1
 
+/* How the expert products with 128-token blocks (block_m 128) hand their
+ * (row block, output-channel group) tiles to workgroups (Hungarian page,
+ * section "FP8 esetén ...": dynamic scheduling layouts for token groups of
+ * varying size).  MOE_SCHED_STATIC: one workgroup per possible tile, in an
+ * XCD-aware raster; those of row blocks past the realised ones exit at once.
+ * MOE_SCHED_QUEUE: as many workgroups as the GPU holds at once take only the
+ * realised tiles, from one work queue per XCD, and help drain the other
+ * queues when their own is empty.  MOE_SCHED_AUTO (0) is the queue.  Both
+ * give bit-identical outputs; other block sizes have a single schedule and
+ * ignore the field. */
+#define MOE_SCHED_AUTO 0
+#define MOE_SCHED_STATIC 1
+#define MOE_SCHED_QUEUE 2
+
 #define MOE_SCALE_NONE 0         /* F32 / BF16 weights                       */
 #define MOE_SCALE_PER_TENSOR 1   /* one fp32 scale per expert matrix: [E]    */
 #define MOE_SCALE_PER_CHANNEL 2  /* one per output row: [E,2I] and [E,d]     */
@@ -116,6 +130,8 @@ typedef struct moe_desc {
   int32_t weight_dtype;  /* MOE_DTYPE_F32/_BF16/_E4M3FN */
   int32_t block_m;       /* 0 or 16/32/64/128/256    */
   int32_t act_quant;     /* MOE_ACT_AS_IS or MOE_ACT_MX_E4M3 */
+  int32_t schedule;      /* MOE_SCHED_*              */
+  int32_t reserved;      /* must be 0                */
 } moe_desc;
 
 /* FP8 weight scales (device pointers, fp32).  Pass NULL (or mode

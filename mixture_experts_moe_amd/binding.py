@@ -27,6 +27,9 @@ MOE_SCALE_PER_TENSOR = 1
 MOE_SCALE_PER_CHANNEL = 2
 MOE_ACT_AS_IS = 0
 MOE_ACT_MX_E4M3 = 1
+MOE_SCHED_AUTO = 0
+MOE_SCHED_STATIC = 1
+MOE_SCHED_QUEUE = 2
 MOE_KERNEL_COUNT = 7
 
 ENTRY_POINTS = (
@@ -41,7 +44,8 @@ class moe_desc(ctypes.Structure):
     _fields_ = [("num_tokens", ctypes.c_int64), ("hidden", ctypes.c_int64),
                 ("num_experts", ctypes.c_int64), ("intermediate", ctypes.c_int64),
                 ("act_dtype", ctypes.c_int32), ("weight_dtype", ctypes.c_int32),
-                ("block_m", ctypes.c_int32), ("act_quant", ctypes.c_int32)]
+                ("block_m", ctypes.c_int32), ("act_quant", ctypes.c_int32),
+                ("schedule", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class moe_scales(ctypes.Structure):
@@ -187,10 +191,20 @@ def _act_quant_code(act_quant: Optional[str]) -> int:
     raise ValueError(f"act_quant must be None or 'mx_e4m3', got {act_quant!r}")
 
 
+_SCHEDULES = {"auto": MOE_SCHED_AUTO, "static": MOE_SCHED_STATIC, "queue": MOE_SCHED_QUEUE}
+
+
+def _schedule_code(schedule: str) -> int:
+    if schedule not in _SCHEDULES:
+        raise ValueError(f"schedule must be one of {sorted(_SCHEDULES)}, got {schedule!r}")
+    return _SCHEDULES[schedule]
+
+
 def make_desc(T: int, d: int, E: int, I: int, act_dtype: int, weight_dtype: int,
-              block_m: int = 0, act_quant: Optional[str] = None) -> moe_desc:
+              block_m: int = 0, act_quant: Optional[str] = None,
+              schedule: str = "auto") -> moe_desc:
     return moe_desc(int(T), int(d), int(E), int(I), int(act_dtype), int(weight_dtype),
-                    int(block_m), _act_quant_code(act_quant))
+                    int(block_m), _act_quant_code(act_quant), _schedule_code(schedule), 0)
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -286,12 +300,14 @@ def moe_forward(x: torch.Tensor, w_gate: torch.Tensor, w13: torch.Tensor, w2: to
                 top_k: int, scales: Optional[Sequence[torch.Tensor]] = None,
                 out: Optional[torch.Tensor] = None, *, block_m: int = 0,
                 workspace: Optional[torch.Tensor] = None, stream=None,
-                act_quant: Optional[str] = None) -> torch.Tensor:
+                act_quant: Optional[str] = None, schedule: str = "auto") -> torch.Tensor:
     """out [T, d] = fused MoE layer of x (same dtype as x).  act_quant="mx_e4m3"
-    selects the W8A8 mode (e4m3fn weights; x and h block-scaled e4m3fn)."""
+    selects the W8A8 mode (e4m3fn weights; x and h block-scaled e4m3fn);
+    schedule ("auto", "static", "queue") how the 128-token-block expert
+    kernels hand out their tiles."""
     dev = _dev(x, w_gate, w13, w2, out)
     T, d, E, I = _shapes(x, w_gate, w13, w2)
-    desc = make_desc(T, d, E, I, _act_code(x), _w_code(w13), block_m, act_quant)
+    desc = make_desc(T, d, E, I, _act_code(x), _w_code(w13), block_m, act_quant, schedule)
     sc = _scales(w13, scales)
     if out is None:
         out = torch.empty((T, d), dtype=x.dtype, device=dev)
@@ -411,11 +427,12 @@ class MoeGraph:
     def __init__(self, x: torch.Tensor, w_gate: torch.Tensor, w13: torch.Tensor,
                  w2: torch.Tensor, top_k: int, scales: Optional[Sequence[torch.Tensor]] = None,
                  out: Optional[torch.Tensor] = None, *, block_m: int = 0,
-                 workspace: Optional[torch.Tensor] = None, act_quant: Optional[str] = None):
+                 workspace: Optional[torch.Tensor] = None, act_quant: Optional[str] = None,
+                 schedule: str = "auto"):
         self._h = None
         dev = _dev(x, w_gate, w13, w2, out)
         T, d, E, I = _shapes(x, w_gate, w13, w2)
-        desc = make_desc(T, d, E, I, _act_code(x), _w_code(w13), block_m, act_quant)
+        desc = make_desc(T, d, E, I, _act_code(x), _w_code(w13), block_m, act_quant, schedule)
         self._sc = _scales(w13, scales)
         if out is None:
             out = torch.empty((T, d), dtype=x.dtype, device=dev)
@@ -456,12 +473,12 @@ def moe_expert_ffn(x: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, top_k: 
                    num_padded: torch.Tensor, scales: Optional[Sequence[torch.Tensor]] = None,
                    out: Optional[torch.Tensor] = None, *, block_m: int = 0,
                    workspace: Optional[torch.Tensor] = None, stream=None,
-                   act_quant: Optional[str] = None) -> torch.Tensor:
+                   act_quant: Optional[str] = None, schedule: str = "auto") -> torch.Tensor:
     """Expert networks + combine for a given routing (layout from moe_align
     with the same block_m and act_quant)."""
     dev = _dev(x, w13, w2, topk_w, sorted_ids, block_expert, num_padded, out)
     T, d, E, I = _shapes(x, None, w13, w2)
-    desc = make_desc(T, d, E, I, _act_code(x), _w_code(w13), block_m, act_quant)
+    desc = make_desc(T, d, E, I, _act_code(x), _w_code(w13), block_m, act_quant, schedule)
     B, cap = moe_align_capacity(desc, top_k)
     if sorted_ids.numel() < cap or block_expert.numel() < cap // B:
         raise ValueError("sorted_ids / block_expert smaller than the layout capacity")

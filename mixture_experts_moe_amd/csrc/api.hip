@@ -29,6 +29,10 @@ int act_bytes(int dt) { return dt == MOE_DTYPE_F32 ? 4 : 2; }
 int check_desc(const moe_desc* d, int top_k) {
   if (!d) return MOE_ERR_NULL_PTR;
   if (d->act_quant != MOE_ACT_AS_IS && d->act_quant != MOE_ACT_MX_E4M3) return MOE_ERR_BAD_ARG;
+  if (d->schedule != MOE_SCHED_AUTO && d->schedule != MOE_SCHED_STATIC &&
+      d->schedule != MOE_SCHED_QUEUE)
+    return MOE_ERR_BAD_ARG;
+  if (d->reserved != 0) return MOE_ERR_BAD_ARG;
   if (d->num_tokens < 0) return MOE_ERR_BAD_SHAPE;
   if (d->hidden < 64 || d->hidden % 64 || d->hidden > kMaxDim) return MOE_ERR_BAD_SHAPE;
   if (d->intermediate < 64 || d->intermediate % 64 || d->intermediate > kMaxDim)
@@ -87,8 +91,10 @@ struct Plan {
   int splits, ksplit;
   int act, wdt;
   bool act_mx;  // W8A8 mode
-  // workspace offsets (bytes); xq, sx, sh only in the W8A8 mode
-  size_t logits, ids, gates, counts, num_padded, sorted, block_exp, h, y, xq, sx, sh, total;
+  bool queue;   // tile-queue schedule of the 128-token GEMM
+  // workspace offsets (bytes); xq, sx, sh only in the W8A8 mode, qcnt only
+  // with the queue schedule
+  size_t logits, ids, gates, counts, num_padded, sorted, block_exp, h, y, xq, sx, sh, qcnt, total;
 };
 
 // Block size of the regrouped layout.  Up to 64 tokens the weight-streaming
@@ -154,6 +160,8 @@ void make_plan(const moe_desc* d, int top_k, bool with_routing, Plan* p) {
   p->act = d->act_dtype;
   p->wdt = d->weight_dtype;
   p->act_mx = d->act_quant == MOE_ACT_MX_E4M3;
+  p->queue = d->schedule != MOE_SCHED_STATIC && p->B == 128 && p->wdt != MOE_DTYPE_F32 &&
+             !p->act_mx;
 
   // Split W2's K range when there are too few workgroups to keep enough
   // HBM requests in flight (small batches); the combine adds the splits in a
@@ -216,6 +224,7 @@ void make_plan(const moe_desc* d, int top_k, bool with_routing, Plan* p) {
   } else {
     p->xq = p->sx = p->sh = 0;
   }
+  p->qcnt = p->queue ? take(moe::gemm_queue_ints() * 4) : 0;
   p->total = p->T == 0 ? 0 : off;  // nothing runs for T = 0
 }
 
@@ -308,12 +317,15 @@ FfnArgs ffn_args(const Plan& p, const void* x, const void* w13, const void* w2,
   a.xq = p.act_mx ? reinterpret_cast<uint8_t*>(ws + p.xq) : nullptr;
   a.sx = p.act_mx ? reinterpret_cast<uint8_t*>(ws + p.sx) : nullptr;
   a.sh = p.act_mx ? reinterpret_cast<uint8_t*>(ws + p.sh) : nullptr;
+  a.queue_sched = p.queue;
+  a.queue = p.queue ? reinterpret_cast<int32_t*>(ws + p.qcnt) : nullptr;
   return a;
 }
 
 hipError_t run_ffn(const FfnArgs& a, hipStream_t s) {
   hipError_t e = hipSuccess;
   if (a.act_mx) e = timed(MOE_KERNEL_QUANT_X, s, [&] { return moe::launch_quantize_x(a, s); });
+  if (e == hipSuccess && a.queue_sched) e = moe::launch_gemm_queue_reset(a, s);
   if (e == hipSuccess) e = timed(MOE_KERNEL_FFN13, s, [&] { return moe::launch_ffn13(a, s); });
   if (e == hipSuccess) e = timed(MOE_KERNEL_FFN2, s, [&] { return moe::launch_ffn2(a, s); });
   if (e == hipSuccess) e = timed(MOE_KERNEL_COMBINE, s, [&] { return moe::launch_combine(a, s); });

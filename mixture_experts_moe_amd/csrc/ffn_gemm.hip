@@ -19,6 +19,12 @@
 // with weight rows on M and tokens on N; e4m3fn weights are widened exactly
 // in registers.  The W13 epilogue applies SiLU(gate) * up, the W2 epilogue
 // the per-channel scale and the slot's gate.
+//
+// Tiles reach workgroups by one of two schedules (same page, same section:
+// dynamic scheduling of token groups of varying size): a static XCD-aware
+// raster over every possible tile, or persistent workgroups that take the
+// realised tiles from per-XCD work queues.  A tile's arithmetic does not
+// depend on the workgroup that runs it, so both give the same bits.
 
 #include "ffn_common.h"
 
@@ -58,14 +64,13 @@ struct Stager {
   static constexpr int kPitch = KC + 8;                       // elements per LDS row
   const bf16_t* src[kPieces];  // row start + piece column (a valid row if dead)
   uint32_t live;               // bit i: piece i carries a token
+  int tid;                     // thread index in the workgroup
   uint4 v[kPieces];
 
   __device__ __forceinline__ int row(int i) const {
-    return static_cast<int>(threadIdx.x) / kPiecesPerRow + kRowsPerPass * i;
+    return tid / kPiecesPerRow + kRowsPerPass * i;
   }
-  __device__ __forceinline__ int col() const {
-    return (static_cast<int>(threadIdx.x) % kPiecesPerRow) * 8;
-  }
+  __device__ __forceinline__ int col() const { return (tid % kPiecesPerRow) * 8; }
   __device__ __forceinline__ void load(int k0) {
 #pragma unroll
     for (int i = 0; i < kPieces; ++i) {
@@ -97,12 +102,9 @@ struct TileId {
   bool live;
 };
 
-__device__ __forceinline__ TileId tile_of(int p, int gx, int gy) {
-  const int total = gx * gy;
-  const int per_xcd = (total + kXcds - 1) / kXcds;
-  const int l = (p % kXcds) * per_xcd + p / kXcds;
-  TileId t{0, 0, l < total};
-  if (!t.live) return t;
+// Logical tile l (< gx * gy) -> (row block, channel group).
+__device__ __forceinline__ TileId logical_tile(int l, int gx, int gy) {
+  TileId t{0, 0, true};
   const int band = kGroupCols * gx;            // tiles per full super-row
   const int sr = l / band;
   const int rem = l - sr * band;
@@ -112,9 +114,99 @@ __device__ __forceinline__ TileId tile_of(int p, int gx, int gy) {
   return t;
 }
 
+__device__ __forceinline__ TileId tile_of(int p, int gx, int gy) {
+  const int total = gx * gy;
+  const int per_xcd = (total + kXcds - 1) / kXcds;
+  const int l = (p % kXcds) * per_xcd + p / kXcds;
+  if (l >= total) return TileId{0, 0, false};
+  return logical_tile(l, gx, gy);
+}
+
 inline int raster_grid(int gx, int gy) {
   const int total = gx * gy;
   return (total + kXcds - 1) / kXcds * kXcds;
+}
+
+// Queue schedule (persistent workgroups).  The live tiles -- row blocks below
+// num_padded, read on the device -- in the same logical order, cut into
+// kXcds contiguous segments with one counter each.  Workgroup p belongs to
+// segment p % kXcds, the XCD it runs on, so each XCD still walks its own
+// stretch of the order and shares weight and token tiles through its L2.
+// Its first tile is fixed (tile p / kXcds of the segment: no counter traffic
+// while every workgroup starts at once); after that it takes tickets from
+// the segment's counter, and once the segment is drained from the next
+// segments in turn, so an XCD whose tiles ran faster (blocks at most half
+// full skip half of the MFMA work) helps the others finish.  A workgroup
+// gives up a segment after one ticket past its end and never returns to
+// it, so it exits after at most kXcds empty tickets.  Device-scope atomics
+// leave the XCD, so each counter sits in a 128-byte line of its own and a
+// segment is read before it is added to.  The counters must be zero at
+// launch.
+constexpr int kQueueStride = 32;                          // int32 per counter line
+constexpr int kQueueInts = 2 * kXcds * kQueueStride;      // W13's lines, then W2's
+
+struct TileQueue {
+  int32_t* cnt;  // kXcds counters, kQueueStride apart
+  int total;     // live tiles
+  int home;      // this workgroup's segment
+  int per;       // workgroups per segment (first tiles handed out without a counter)
+  int tried;     // segments given up (thread 0's copy is the one used)
+  bool started;
+
+  __device__ __forceinline__ int seg_begin(int s) const {
+    return static_cast<int>(static_cast<int64_t>(total) * s / kXcds);
+  }
+  // Next logical tile, or -1 once every segment is drained (thread 0 only).
+  __device__ __forceinline__ int take() {
+    if (!started) {
+      started = true;
+      const int first = static_cast<int>(blockIdx.x / kXcds);
+      if (first < seg_begin(home + 1) - seg_begin(home)) return seg_begin(home) + first;
+    }
+    while (tried < kXcds) {
+      const int s = (home + tried) % kXcds;
+      const int b0 = seg_begin(s), n = seg_begin(s + 1) - b0;
+      int32_t* c = cnt + s * kQueueStride;
+      if (per + __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n) {
+        const int t = per + atomicAdd(c, 1);
+        if (t < n) return b0 + t;
+      }
+      ++tried;
+    }
+    return -1;
+  }
+};
+
+// Runs body(b, y) for every tile this workgroup takes; all threads of the
+// workgroup see the same tile, and the loop ends for all of them together.
+// The grid is a multiple of kXcds.
+template <class Body>
+__device__ __forceinline__ void queue_loop(int32_t* cnt, int live_blocks, int gy, Body&& body) {
+  __shared__ int s_tile;
+  TileQueue q{cnt, live_blocks * gy, static_cast<int>(blockIdx.x % kXcds),
+              static_cast<int>(gridDim.x / kXcds), 0, false};
+  for (;;) {
+    if (threadIdx.x == 0) s_tile = q.take();
+    __syncthreads();
+    const int l = s_tile;
+    __syncthreads();  // every thread has read s_tile before thread 0 writes it again
+    if (l < 0) break;
+    const TileId t = logical_tile(l, live_blocks, gy);
+    body(t.b, t.y);
+  }
+}
+
+// threadIdx.x through an empty asm statement: what a tile derives from it is
+// then computed per tile rather than hoisted out of the persistent loop,
+// where it would stay live (in registers) through every main loop.
+__device__ __forceinline__ int tile_tid() {
+  int t = static_cast<int>(threadIdx.x);
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
+__global__ void queue_reset_kernel(int32_t* cnt) {
+  for (int i = threadIdx.x; i < kQueueInts; i += blockDim.x) cnt[i] = 0;
 }
 
 // Shared main loop: acc[s][r] += W_rows[r] . tokens[s]^T over all K.  The
@@ -130,7 +222,7 @@ __device__ __forceinline__ void gemm_mainloop(WeightStream<WT, KC, NROW, P>& ws,
   constexpr int kPitch = Stager<KC, WAVES>::kPitch;
   constexpr int kBuf = kGemmTokens * kPitch;
   constexpr int kHalf = kGemmNSub / 2;
-  const int lane = threadIdx.x & 63;
+  const int lane = st.tid & 63;
   const int r16 = lane & 15;
   const int g = lane >> 4;
   const int last = ws.nch - 1;
@@ -181,31 +273,29 @@ __device__ __forceinline__ void gemm_mainloop(WeightStream<WT, KC, NROW, P>& ws,
 
 // ------------------------------------------------------------ W13 + SiLU*mul
 //
-// Grid: x = row block b (128 tokens of one expert), y = group of
+// Tile (b, y): row block b (128 tokens of one expert) x group y of
 // 4 * 16 * RN output channels of I.
 
 template <typename WT, int KC, int P, int RN, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void ffn13_gemm_kernel(
+__device__ __forceinline__ void ffn13_gemm_tile(
     const bf16_t* __restrict__ x, const WT* __restrict__ w13, const float* __restrict__ s13,
     int scale_mode, const int32_t* __restrict__ sorted_ids,
-    const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded,
-    bf16_t* __restrict__ h, int d, int I, int k, int A, int gx, int gy) {
-  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * kGemmTokens * Stager<KC, WAVES>::kPitch];
+    const int32_t* __restrict__ block_expert, bf16_t* __restrict__ h, int d, int I, int k, int A,
+    int b, int cg, bf16_t* lds) {
   constexpr int NROW = 2 * RN;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int tid = tile_tid();
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int r16 = lane & 15;
   const int g = lane >> 4;
-  const TileId tid = tile_of(blockIdx.x, gx, gy);
-  const int b = tid.b;
-  if (!tid.live || b * kGemmTokens >= *num_padded) return;  // uniform over the workgroup
   const int e = block_expert[b];
   const int32_t* blk = sorted_ids + static_cast<size_t>(b) * kGemmTokens;
   const int nsub = live_subtiles<kGemmNSub>(blk, A);
-  const int n0 = (tid.y * WAVES + wave) * 16 * RN;  // the channel groups tile I exactly
+  const int n0 = (cg * WAVES + wave) * 16 * RN;  // the channel groups tile I exactly
 
   Stager<KC, WAVES> st;
   st.live = 0;
+  st.tid = tid;
 #pragma unroll
   for (int i = 0; i < Stager<KC, WAVES>::kPieces; ++i) {
     const int f = blk[st.row(i)];
@@ -257,32 +347,53 @@ __global__ __launch_bounds__(64 * WAVES) void ffn13_gemm_kernel(
   }
 }
 
+// Static schedule: one workgroup per tile of the XCD-aware raster (dead row
+// blocks exit at once).  Queue schedule: a grid of resident workgroups
+// takes the live tiles from the queue.
+template <typename WT, int KC, int P, int RN, int WAVES, bool kQueue>
+__global__ __launch_bounds__(64 * WAVES) void ffn13_gemm_kernel(
+    const bf16_t* __restrict__ x, const WT* __restrict__ w13, const float* __restrict__ s13,
+    int scale_mode, const int32_t* __restrict__ sorted_ids,
+    const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded,
+    bf16_t* __restrict__ h, int d, int I, int k, int A, int gx, int gy, int32_t* queue) {
+  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * kGemmTokens * Stager<KC, WAVES>::kPitch];
+  if constexpr (kQueue) {
+    queue_loop(queue, *num_padded / kGemmTokens, gy, [&](int b, int cg) {
+      ffn13_gemm_tile<WT, KC, P, RN, WAVES>(x, w13, s13, scale_mode, sorted_ids, block_expert, h,
+                                            d, I, k, A, b, cg, lds);
+    });
+  } else {
+    const TileId t = tile_of(blockIdx.x, gx, gy);
+    if (!t.live || t.b * kGemmTokens >= *num_padded) return;  // uniform over the workgroup
+    ffn13_gemm_tile<WT, KC, P, RN, WAVES>(x, w13, s13, scale_mode, sorted_ids, block_expert, h, d,
+                                          I, k, A, t.b, t.y, lds);
+  }
+}
+
 // ------------------------------------------------------------ W2 + gate scale
 //
-// Grid: x = row block b, y = group of 4 * 16 * RN output channels of d.
+// Tile (b, cg): row block b x group cg of 4 * 16 * RN output channels of d.
 // Writes y[f, n] = gate_f * s(n) * (W2[e] h[row])[n] for the block's slots.
 
 template <typename WT, int KC, int P, int RN, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void ffn2_gemm_kernel(
+__device__ __forceinline__ void ffn2_gemm_tile(
     const bf16_t* __restrict__ h, const WT* __restrict__ w2, const float* __restrict__ s2,
     int scale_mode, const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
-    const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded,
-    float* __restrict__ y, int d, int I, int A, int gx, int gy) {
-  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * kGemmTokens * Stager<KC, WAVES>::kPitch];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+    const int32_t* __restrict__ block_expert, float* __restrict__ y, int d, int I, int A, int b,
+    int cg, bf16_t* lds) {
+  const int tid = tile_tid();
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int r16 = lane & 15;
   const int g = lane >> 4;
-  const TileId tid = tile_of(blockIdx.x, gx, gy);
-  const int b = tid.b;
-  if (!tid.live || b * kGemmTokens >= *num_padded) return;
   const int e = block_expert[b];
   const int32_t* blk = sorted_ids + static_cast<size_t>(b) * kGemmTokens;
   const int nsub = live_subtiles<kGemmNSub>(blk, A);
-  const int n0 = (tid.y * WAVES + wave) * 16 * RN;  // the channel groups tile d exactly
+  const int n0 = (cg * WAVES + wave) * 16 * RN;  // the channel groups tile d exactly
 
   Stager<KC, WAVES> st;
   st.live = 0;
+  st.tid = tid;
 #pragma unroll
   for (int i = 0; i < Stager<KC, WAVES>::kPieces; ++i) {
     const int r = st.row(i);
@@ -326,6 +437,26 @@ __global__ __launch_bounds__(64 * WAVES) void ffn2_gemm_kernel(
   }
 }
 
+template <typename WT, int KC, int P, int RN, int WAVES, bool kQueue>
+__global__ __launch_bounds__(64 * WAVES) void ffn2_gemm_kernel(
+    const bf16_t* __restrict__ h, const WT* __restrict__ w2, const float* __restrict__ s2,
+    int scale_mode, const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
+    const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded,
+    float* __restrict__ y, int d, int I, int A, int gx, int gy, int32_t* queue) {
+  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * kGemmTokens * Stager<KC, WAVES>::kPitch];
+  if constexpr (kQueue) {
+    queue_loop(queue, *num_padded / kGemmTokens, gy, [&](int b, int cg) {
+      ffn2_gemm_tile<WT, KC, P, RN, WAVES>(h, w2, s2, scale_mode, topk_w, sorted_ids,
+                                           block_expert, y, d, I, A, b, cg, lds);
+    });
+  } else {
+    const TileId t = tile_of(blockIdx.x, gx, gy);
+    if (!t.live || t.b * kGemmTokens >= *num_padded) return;
+    ffn2_gemm_tile<WT, KC, P, RN, WAVES>(h, w2, s2, scale_mode, topk_w, sorted_ids, block_expert,
+                                         y, d, I, A, t.b, t.y, lds);
+  }
+}
+
 // ------------------------------------------------------------ launchers
 
 namespace {
@@ -337,14 +468,50 @@ static_assert(kRNG2 == 1 || kRNG2 == 2, "channel tiles per wave: 1 or 2");
 // A workgroup covers 16 * RN * WAVES output channels; the launchers pick the
 // widest configuration whose channel group divides the channel count (a
 // multiple of 64, so 4 waves x 16 channels always fits).
-template <typename WT, int KC, int RN, int WAVES>
+// Workgroups of kernel K the chip holds at once (occupancy x compute units),
+// asked of the runtime once per kernel (for the first device it runs on; a
+// process is taken to drive one kind of GPU); 0 when it cannot say.
+template <auto K>
+int resident_workgroups(int threads) {
+  static const int n = [threads] {
+    int per_cu = 0, dev = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, K, threads, 0) != hipSuccess ||
+        hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    return per_cu * cus;
+  }();
+  return n;
+}
+
+// Grid of a launch: the raster for the static schedule; for the queue, the
+// resident workgroups (a multiple of kXcds so every XCD's segment has its
+// own takers), at most one per possible tile.
+template <auto K>
+int sched_grid(bool queue, int gx, int gy, int threads) {
+  const int full = raster_grid(gx, gy);
+  if (!queue) return full;
+  const int res = resident_workgroups<K>(threads) / kXcds * kXcds;
+  return res > 0 && res < full ? res : full;
+}
+
+template <typename WT, int KC, int RN, int WAVES, bool kQueue>
 void ffn13_gemm_launch(const FfnArgs& a, hipStream_t s) {
   constexpr int P = sizeof(WT) == 1 ? kPG + 1 : kPG;
+  constexpr auto kern = ffn13_gemm_kernel<WT, KC, P, RN, WAVES, kQueue>;
   const int gx = a.cap / kGemmTokens, gy = a.I / (WAVES * 16 * RN);
-  ffn13_gemm_kernel<WT, KC, P, RN, WAVES><<<raster_grid(gx, gy), 64 * WAVES, 0, s>>>(
+  kern<<<sched_grid<kern>(kQueue, gx, gy, 64 * WAVES), 64 * WAVES, 0, s>>>(
       static_cast<const bf16_t*>(a.x), static_cast<const WT*>(a.w13), a.s13, a.scale_mode,
       a.sorted_ids, a.block_expert, a.num_padded, static_cast<bf16_t*>(a.h), a.d, a.I, a.k, a.A,
-      gx, gy);
+      gx, gy, a.queue);
+}
+
+template <typename WT, int KC, int RN, int WAVES>
+void ffn13_gemm_launch(const FfnArgs& a, hipStream_t s) {
+  if (a.queue_sched)
+    ffn13_gemm_launch<WT, KC, RN, WAVES, true>(a, s);
+  else
+    ffn13_gemm_launch<WT, KC, RN, WAVES, false>(a, s);
 }
 
 template <typename WT, int KC>
@@ -355,13 +522,23 @@ void ffn13_gemm_go(const FfnArgs& a, hipStream_t s) {
     ffn13_gemm_launch<WT, KC, 1, kWaves13>(a, s);
 }
 
-template <typename WT, int KC, int RN, int WAVES>
+template <typename WT, int KC, int RN, int WAVES, bool kQueue>
 void ffn2_gemm_launch(const FfnArgs& a, hipStream_t s) {
   constexpr int P = sizeof(WT) == 1 ? kPG + 1 : kPG;
+  constexpr auto kern = ffn2_gemm_kernel<WT, KC, P, RN, WAVES, kQueue>;
   const int gx = a.cap / kGemmTokens, gy = a.d / (WAVES * 16 * RN);
-  ffn2_gemm_kernel<WT, KC, P, RN, WAVES><<<raster_grid(gx, gy), 64 * WAVES, 0, s>>>(
+  kern<<<sched_grid<kern>(kQueue, gx, gy, 64 * WAVES), 64 * WAVES, 0, s>>>(
       static_cast<const bf16_t*>(a.h), static_cast<const WT*>(a.w2), a.s2, a.scale_mode,
-      a.topk_w, a.sorted_ids, a.block_expert, a.num_padded, a.y_part, a.d, a.I, a.A, gx, gy);
+      a.topk_w, a.sorted_ids, a.block_expert, a.num_padded, a.y_part, a.d, a.I, a.A, gx, gy,
+      a.queue + kXcds * kQueueStride);
+}
+
+template <typename WT, int KC, int RN, int WAVES>
+void ffn2_gemm_launch(const FfnArgs& a, hipStream_t s) {
+  if (a.queue_sched)
+    ffn2_gemm_launch<WT, KC, RN, WAVES, true>(a, s);
+  else
+    ffn2_gemm_launch<WT, KC, RN, WAVES, false>(a, s);
 }
 
 template <typename WT, int KC>
@@ -392,13 +569,22 @@ hipError_t ffn2_gemm_w(const FfnArgs& a, hipStream_t s) {
 
 }  // namespace
 
+int gemm_queue_ints() { return kQueueInts; }
+
+hipError_t launch_gemm_queue_reset(const FfnArgs& a, hipStream_t s) {
+  if (!a.queue) return hipErrorInvalidValue;
+  queue_reset_kernel<<<1, 256, 0, s>>>(a.queue);
+  return hipGetLastError();
+}
+
 hipError_t launch_ffn13_gemm(const FfnArgs& a, hipStream_t s) {
-  if (a.B != kGemmTokens) return hipErrorInvalidValue;
+  if (a.B != kGemmTokens || (a.queue_sched && !a.queue)) return hipErrorInvalidValue;
   return a.w_dtype == kDtypeE4M3FN ? ffn13_gemm_w<fp8_t>(a, s) : ffn13_gemm_w<bf16_t>(a, s);
 }
 
 hipError_t launch_ffn2_gemm(const FfnArgs& a, hipStream_t s) {
-  if (a.B != kGemmTokens || a.splits != 1) return hipErrorInvalidValue;
+  if (a.B != kGemmTokens || a.splits != 1 || (a.queue_sched && !a.queue))
+    return hipErrorInvalidValue;
   return a.w_dtype == kDtypeE4M3FN ? ffn2_gemm_w<fp8_t>(a, s) : ffn2_gemm_w<bf16_t>(a, s);
 }
 

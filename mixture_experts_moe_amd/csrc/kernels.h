@@ -62,6 +62,10 @@ struct FfnArgs {
   uint8_t* xq;
   uint8_t* sx;
   uint8_t* sh;
+  // Tile-queue schedule of the 128-token GEMM: counters in the workspace
+  // (gemm_queue_ints() int32), zeroed by launch_gemm_queue_reset.
+  bool queue_sched;
+  int32_t* queue;
 };
 
 hipError_t launch_ffn13(const FfnArgs& a, hipStream_t s);
@@ -71,6 +75,8 @@ hipError_t launch_combine(const FfnArgs& a, hipStream_t s);
 // launchers above when a.B == 128.
 hipError_t launch_ffn13_gemm(const FfnArgs& a, hipStream_t s);
 hipError_t launch_ffn2_gemm(const FfnArgs& a, hipStream_t s);
+int gemm_queue_ints();
+hipError_t launch_gemm_queue_reset(const FfnArgs& a, hipStream_t s);
 // Large-tile grouped GEMM (block size 256, bf16 weights, d % 256 == 0 and
 // I % 128 == 0); used when a.B == 256.
 bool big_gemm_fits(int64_t T, int d, int I);

@@ -94,6 +94,33 @@ def test_descriptor_validation(lib, kw, k, status):
     assert ws_status(lib, desc(**kw), k) == status
 
 
+def test_schedule_field_validation(lib):
+    d = desc()
+    d.schedule = 3
+    assert ws_status(lib, d) == -9
+    d = desc()
+    d.reserved = 1
+    assert ws_status(lib, d) == -9
+    with pytest.raises(ValueError):
+        B.make_desc(4, 128, 8, 128, B.MOE_DTYPE_BF16, B.MOE_DTYPE_BF16, schedule="dynamic")
+    for name in ("auto", "static", "queue"):
+        assert ws_status(lib, B.make_desc(4, 128, 8, 128, B.MOE_DTYPE_BF16, B.MOE_DTYPE_BF16,
+                                          schedule=name)) == 0
+
+
+def test_queue_schedule_workspace(lib):
+    """The queue's counters take workspace only where the 128-token GEMM runs
+    with that schedule."""
+    def nbytes(bm, schedule, w=B.MOE_DTYPE_BF16):
+        return B.moe_workspace_bytes(
+            B.make_desc(512, 256, 8, 256, B.MOE_DTYPE_BF16, w, bm, None, schedule), 2, True)
+    for w in (B.MOE_DTYPE_BF16, E4):
+        assert nbytes(128, "auto", w) == nbytes(128, "queue", w) > nbytes(128, "static", w)
+        assert nbytes(128, "queue", w) - nbytes(128, "static", w) <= 4096
+    assert nbytes(64, "queue") == nbytes(64, "static")
+    assert nbytes(256, "queue") == nbytes(256, "static")
+
+
 def test_unknown_act_quant_and_null_descriptor(lib):
     d = desc()
     d.act_quant = 2

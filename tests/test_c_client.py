@@ -37,6 +37,10 @@ C_SOURCE = textwrap.dedent(r"""
       if (moe_forward(NULL, NULL, NULL, NULL, NULL, 2, NULL, NULL, NULL, 0, NULL) != MOE_ERR_NULL_PTR)
         return 7;
       if (strlen(moe_strerror(MOE_ERR_WORKSPACE)) == 0) return 8;
+      d.schedule = MOE_SCHED_QUEUE + 1;                 /* no such schedule */
+      if (moe_workspace_bytes(&d, 2, 1, &ws) != MOE_ERR_BAD_ARG) return 9;
+      d.schedule = MOE_SCHED_STATIC;
+      if (moe_workspace_bytes(&d, 2, 1, &ws) != MOE_OK) return 10;
       printf("ok %d %lld\n", (int)bm, (long long)cap);
       return 0;
     }

@@ -474,6 +474,62 @@ def test_graph_replay_matches_eager(wl, T, over):
         graph.close()
 
 
+# ---------------------------------------------------------------- tile schedules
+
+SCHED_CASES = [
+    # name, workload overrides, T (block_m 128: the GEMM with two schedules)
+    ("bf16_ragged", dict(workload="decode_bf16", d=512, I=448, x_std=1.0), 257),
+    ("bf16_multi", dict(workload="decode_bf16", d=512, I=512, E=8, x_std=1.0), 1500),
+    ("fp8_channel", dict(workload="fp8", d=256, I=192, E=16, k=4), 200),
+    ("skew_small", dict(workload="skew", d=192, I=128), 300),
+    # one tile in all: seven of the eight queues are empty
+    ("one_tile", dict(workload="decode_bf16", d=256, I=64, E=1, k=1, x_std=1.0), 3),
+]
+
+
+@pytest.mark.parametrize("name,over,T", SCHED_CASES, ids=[f"{c[0]}-T{c[2]}" for c in SCHED_CASES])
+def test_schedules_give_identical_bits(name, over, T):
+    """The queue and the static raster run the same tile arithmetic, so the
+    layer's output is bit-identical; the queue's is also the oracle's."""
+    note(f"schedules {name} T={T}")
+    over = dict(over)
+    wl = over.pop("workload")
+    inp = synth.make_inputs(wl, T=T, device=DEV, **over)
+    sc = (inp.s13, inp.s2) if inp.w == "e4m3fn" else None
+    outs = {s: B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, sc, block_m=128,
+                             schedule=s) for s in ("static", "queue", "auto")}
+    _, ids, _ = B.moe_route(inp.x, inp.w_gate, inp.top_k)
+    torch.cuda.synchronize()
+    assert torch.equal(outs["static"], outs["queue"])
+    assert torch.equal(outs["auto"], outs["queue"])
+    compare_layer(inp, outs["queue"], ids)
+
+
+def test_queue_counters_restart_every_call():
+    """Calls of different sizes in a row, through the layer and through the
+    expert stage with one workspace: each starts its queues from zero."""
+    big = synth.make_inputs("decode_bf16", T=1500, device=DEV, d=512, I=512, E=8, x_std=1.0)
+    small = synth.make_inputs("decode_bf16", T=200, device=DEV, d=512, I=512, E=8, x_std=1.0,
+                              seed=5)
+    ws_bytes = B.moe_workspace_bytes(
+        B.make_desc(1500, 512, 8, 512, B.MOE_DTYPE_BF16, B.MOE_DTYPE_BF16, 128), 2, True)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+    for inp in (big, small, big, small):
+        ref = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, block_m=128,
+                            schedule="static")
+        got = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, block_m=128,
+                            workspace=ws, schedule="queue")
+        _, ids, w = B.moe_route(inp.x, inp.w_gate, inp.top_k)
+        counts, sorted_ids, block_expert, num_padded, bm = B.moe_align(
+            ids, inp.E, block_m=128, hidden=inp.d, intermediate=inp.I)
+        stage = B.moe_expert_ffn(inp.x, inp.w13, inp.w2, inp.top_k, w, sorted_ids, block_expert,
+                                 num_padded, block_m=128, workspace=ws, schedule="queue")
+        torch.cuda.synchronize()
+        assert bm == 128
+        assert torch.equal(got, ref)
+        assert torch.equal(stage, ref)
+
+
 # ---------------------------------------------------------------- seeded shape sweep
 
 def _sweep_cases(n=48, seed=2024):
