@@ -60,7 +60,7 @@ template <int kAlignThreads>
 __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     const int32_t* __restrict__ ids, int A, int E, int B, int cap, int32_t* __restrict__ counts,
     int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
-    int32_t* __restrict__ num_padded) {
+    int32_t* __restrict__ num_padded, int32_t* __restrict__ zero, int nzero) {
   constexpr int kAlignWaves = kAlignThreads / kWave;
   __shared__ int cnt[kMaxExperts];
   __shared__ int red[kAlignWaves];
@@ -70,6 +70,8 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
   const int wave = tid >> 6;
   const int e = blockIdx.x;
 
+  if (e == 0)  // the next kernels' work-queue counters (none: nzero = 0)
+    for (int i = tid; i < nzero; i += kAlignThreads) zero[i] = 0;
   for (int i = tid; i < E; i += kAlignThreads) cnt[i] = 0;
   __syncthreads();
   for (int f = tid; f < A; f += kAlignThreads) {
@@ -138,13 +140,14 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
 
 hipError_t launch_align(const int32_t* ids, int A, int E, int B, int cap, int32_t* counts,
                         int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded,
-                        hipStream_t s) {
+                        hipStream_t s, int32_t* zero, int nzero) {
+  if (nzero > 0 && !zero) return hipErrorInvalidValue;
   if (A > 2048)
     align_kernel<1024><<<E, 1024, 0, s>>>(ids, A, E, B, cap, counts, sorted_ids, block_expert,
-                                          num_padded);
+                                          num_padded, zero, nzero);
   else
     align_kernel<256><<<E, 256, 0, s>>>(ids, A, E, B, cap, counts, sorted_ids, block_expert,
-                                        num_padded);
+                                        num_padded, zero, nzero);
   return hipGetLastError();
 }
 

@@ -325,7 +325,7 @@ FfnArgs ffn_args(const Plan& p, const void* x, const void* w13, const void* w2,
 hipError_t run_ffn(const FfnArgs& a, hipStream_t s) {
   hipError_t e = hipSuccess;
   if (a.act_mx) e = timed(MOE_KERNEL_QUANT_X, s, [&] { return moe::launch_quantize_x(a, s); });
-  if (e == hipSuccess && a.queue_sched) e = moe::launch_gemm_queue_reset(a, s);
+  if (e == hipSuccess && a.queue_sched && !a.queue_zeroed) e = moe::launch_gemm_queue_reset(a, s);
   if (e == hipSuccess) e = timed(MOE_KERNEL_FFN13, s, [&] { return moe::launch_ffn13(a, s); });
   if (e == hipSuccess) e = timed(MOE_KERNEL_FFN2, s, [&] { return moe::launch_ffn2(a, s); });
   if (e == hipSuccess) e = timed(MOE_KERNEL_COMBINE, s, [&] { return moe::launch_combine(a, s); });
@@ -395,19 +395,27 @@ static hipError_t route(const void* x, int act, const float* w_gate, float* logi
 // Routing followed by the regrouping: one kernel when the router's single
 // workgroup can regroup too (timed as route_logits), else route() then the
 // regrouping kernel.
+// Routing and regrouping of the layer.  `queue` (or nullptr): the expert
+// kernels' work-queue counters; *queue_zeroed tells whether the align launch
+// has cleared them.
 static hipError_t route_align(const Plan& p, const void* x, const float* w_gate, float* logits,
                               int32_t* ids, float* gates, int32_t* counts, int32_t* sorted,
-                              int32_t* block_exp, int32_t* num_padded, hipStream_t s) {
+                              int32_t* block_exp, int32_t* num_padded, int32_t* queue,
+                              bool* queue_zeroed, hipStream_t s) {
+  *queue_zeroed = false;
   if (moe::route_align_fused(p.act, p.T, p.E))
     return timed(MOE_KERNEL_ROUTE_LOGITS, s, [&] {
       return moe::launch_route_align_fused(x, w_gate, logits, ids, gates, p.T, p.E, p.d, p.k, p.B,
                                            p.cap, counts, sorted, block_exp, num_padded, s);
     });
   hipError_t e = route(x, p.act, w_gate, logits, ids, gates, p.T, p.E, p.d, p.k, s);
+  const int nzero = queue ? moe::gemm_queue_ints() : 0;
   if (e == hipSuccess)
     e = timed(MOE_KERNEL_ALIGN, s, [&] {
-      return moe::launch_align(ids, p.A, p.E, p.B, p.cap, counts, sorted, block_exp, num_padded, s);
+      return moe::launch_align(ids, p.A, p.E, p.B, p.cap, counts, sorted, block_exp, num_padded, s,
+                               queue, nzero);
     });
+  *queue_zeroed = e == hipSuccess && nzero > 0;
   return e;
 }
 
@@ -466,8 +474,9 @@ MOE_API int moe_route_align(const moe_desc* desc, const void* x, const float* w_
   Plan p;
   make_plan(desc, top_k, true, &p);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  bool zeroed = false;
   return to_status(route_align(p, x, w_gate, logits, topk_ids, topk_w, counts, sorted_ids,
-                               block_expert, num_padded, s));
+                               block_expert, num_padded, nullptr, &zeroed, s));
 }
 
 MOE_API int moe_expert_ffn(const moe_desc* desc, const void* x, const void* w13, const void* w2,
@@ -537,10 +546,13 @@ static int enqueue_forward(const Plan& p, const void* x, const float* w_gate, co
   int32_t* sorted = reinterpret_cast<int32_t*>(ws + p.sorted);
   int32_t* block_exp = reinterpret_cast<int32_t*>(ws + p.block_exp);
 
-  const hipError_t e =
-      route_align(p, x, w_gate, logits, ids, gates, counts, sorted, block_exp, num_padded, s);
+  int32_t* queue = p.queue ? reinterpret_cast<int32_t*>(ws + p.qcnt) : nullptr;
+  bool zeroed = false;
+  const hipError_t e = route_align(p, x, w_gate, logits, ids, gates, counts, sorted, block_exp,
+                                   num_padded, queue, &zeroed, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   FfnArgs a = ffn_args(p, x, w13, w2, scales, gates, sorted, block_exp, num_padded, out, ws);
+  a.queue_zeroed = zeroed;
   return to_status(run_ffn(a, s));
 }
 

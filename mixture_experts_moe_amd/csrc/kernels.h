@@ -32,9 +32,11 @@ hipError_t launch_route_align_fused(const void* x, const float* wg, float* logit
                                     float* w, int T, int E, int d, int k, int B, int cap,
                                     int32_t* counts, int32_t* sorted_ids, int32_t* block_expert,
                                     int32_t* num_padded, hipStream_t s);
+// `zero`: nzero int32 that the launch also sets to 0 (the expert kernels'
+// work-queue counters when the layer runs align right before them).
 hipError_t launch_align(const int32_t* ids, int A, int E, int B, int cap, int32_t* counts,
                         int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded,
-                        hipStream_t s);
+                        hipStream_t s, int32_t* zero = nullptr, int nzero = 0);
 
 // Everything the expert-side kernels need for one call.
 struct FfnArgs {
@@ -63,8 +65,10 @@ struct FfnArgs {
   uint8_t* sx;
   uint8_t* sh;
   // Tile-queue schedule of the 128-token GEMM: counters in the workspace
-  // (gemm_queue_ints() int32), zeroed by launch_gemm_queue_reset.
+  // (gemm_queue_ints() int32), zeroed by launch_gemm_queue_reset unless
+  // queue_zeroed says an earlier launch on the stream has done it.
   bool queue_sched;
+  bool queue_zeroed;
   int32_t* queue;
 };
 
