@@ -7,6 +7,7 @@ whose k-th/(k+1)-th logit gap is below 1e-4 excluded.  Small cases run the
 oracle on every token; the full-size workloads run it on sampled tokens.
 """
 
+import os
 import sys
 
 import numpy as np
@@ -528,6 +529,35 @@ def test_queue_counters_restart_every_call():
         assert bm == 128
         assert torch.equal(got, ref)
         assert torch.equal(stage, ref)
+
+
+_GRAPH_FIRST = r"""
+import sys, torch
+sys.path.insert(0, sys.argv[1])
+from mixture_experts_moe_amd import binding as B, synth
+inp = synth.make_inputs("decode_bf16", T=300, device="cuda:0", d=512, I=256, x_std=1.0)
+out = torch.empty_like(inp.x)
+g = B.MoeGraph(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, out=out, block_m=128)
+g.launch()
+ref = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, block_m=128,
+                    schedule="static")
+torch.cuda.synchronize()
+assert torch.equal(out, ref), "graph replay differs from the eager static schedule"
+g.close()
+print("graph-first ok", flush=True)
+"""
+
+
+def test_queue_layer_recorded_before_any_eager_call():
+    """A fresh process whose first library call records a 128-token-block
+    layer into a graph: the queue's one-time grid sizing happens during the
+    capture, and the replay still equals the eager static schedule."""
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", _GRAPH_FIRST, root], capture_output=True,
+                       text=True, timeout=100)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
+    assert "graph-first ok" in r.stdout
 
 
 # ---------------------------------------------------------------- seeded shape sweep
