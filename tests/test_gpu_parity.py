@@ -36,7 +36,7 @@ def loaded():
 # ---------------------------------------------------------------- routing
 
 @pytest.mark.parametrize("T,E,k", [(1, 8, 2), (17, 8, 8), (300, 32, 4), (257, 256, 8),
-                                   (64, 1000, 64), (5, 1, 1), (130, 64, 1)])
+                                   (64, 1000, 64), (5, 1, 1), (130, 64, 1), (33, 1024, 64)])
 def test_topk_from_given_logits_is_exact(T, E, k):
     note(f"topk T={T} E={E} k={k}")
     g = torch.Generator().manual_seed(T * 1000 + E)
@@ -157,6 +157,12 @@ SMALL = [
     ("w8a8", dict(workload="fp8", d=256, I=512, E=16, k=4, act_quant="mx_e4m3",
                   scale_mode="tensor"), 200, 0),
     ("w8a8", dict(workload="fp8", d=256, I=4096, E=2, k=1, act_quant="mx_e4m3"), 300, 0),
+    # the ABI's limits: 1024 experts (also through the 128-token GEMM's
+    # queues, with most of its 1035 possible blocks live), top-64, and both
+    ("bf16_maxE", dict(workload="decode_bf16", d=128, I=128, E=1024, k=2, x_std=1.0), 40, 0),
+    ("bf16_maxE", dict(workload="decode_bf16", d=128, I=128, E=1024, k=8, x_std=1.0), 300, 128),
+    ("bf16_maxk", dict(workload="decode_bf16", d=128, I=128, E=64, k=64, x_std=1.0), 20, 0),
+    ("fp8_maxEk", dict(workload="fp8", d=256, I=128, E=1024, k=64), 17, 0),
     # extreme aspect ratios: a very wide hidden size, a very long intermediate
     ("bf16_wide", dict(workload="decode_bf16", d=65536, I=64, E=2, k=1, x_std=1.0), 5, 0),
     ("bf16_tall", dict(workload="decode_bf16", d=64, I=65536, E=2, k=2, x_std=1.0), 5, 0),
