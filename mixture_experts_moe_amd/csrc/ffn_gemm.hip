@@ -181,9 +181,9 @@ struct TileQueue {
 // workgroup see the same tile, and the loop ends for all of them together.
 // The grid is a multiple of kXcds.
 template <class Body>
-__device__ __forceinline__ void queue_loop(int32_t* cnt, int live_blocks, int gy, Body&& body) {
+__device__ __forceinline__ void queue_loop(int32_t* cnt, int nblocks, int gy, Body&& body) {
   __shared__ int s_tile;
-  TileQueue q{cnt, live_blocks * gy, static_cast<int>(blockIdx.x % kXcds),
+  TileQueue q{cnt, nblocks * gy, static_cast<int>(blockIdx.x % kXcds),
               static_cast<int>(gridDim.x / kXcds), 0, false};
   for (;;) {
     if (threadIdx.x == 0) s_tile = q.take();
@@ -191,7 +191,7 @@ __device__ __forceinline__ void queue_loop(int32_t* cnt, int live_blocks, int gy
     const int l = s_tile;
     __syncthreads();  // every thread has read s_tile before thread 0 writes it again
     if (l < 0) break;
-    const TileId t = logical_tile(l, live_blocks, gy);
+    const TileId t = logical_tile(l, nblocks, gy);
     body(t.b, t.y);
   }
 }
@@ -203,6 +203,12 @@ __device__ __forceinline__ int tile_tid() {
   int t = static_cast<int>(threadIdx.x);
   asm volatile("" : "+v"(t));
   return t;
+}
+
+// Row blocks the queue hands out: the realised ones, never more than the
+// capacity holds (as the static grid, whatever num_padded says).
+__device__ __forceinline__ int live_blocks(const int32_t* num_padded, int gx) {
+  return max(0, min(*num_padded / kGemmTokens, gx));
 }
 
 __global__ void queue_reset_kernel(int32_t* cnt) {
@@ -358,7 +364,7 @@ __global__ __launch_bounds__(64 * WAVES) void ffn13_gemm_kernel(
     bf16_t* __restrict__ h, int d, int I, int k, int A, int gx, int gy, int32_t* queue) {
   __shared__ __attribute__((aligned(16))) bf16_t lds[2 * kGemmTokens * Stager<KC, WAVES>::kPitch];
   if constexpr (kQueue) {
-    queue_loop(queue, *num_padded / kGemmTokens, gy, [&](int b, int cg) {
+    queue_loop(queue, live_blocks(num_padded, gx), gy, [&](int b, int cg) {
       ffn13_gemm_tile<WT, KC, P, RN, WAVES>(x, w13, s13, scale_mode, sorted_ids, block_expert, h,
                                             d, I, k, A, b, cg, lds);
     });
@@ -445,7 +451,7 @@ __global__ __launch_bounds__(64 * WAVES) void ffn2_gemm_kernel(
     float* __restrict__ y, int d, int I, int A, int gx, int gy, int32_t* queue) {
   __shared__ __attribute__((aligned(16))) bf16_t lds[2 * kGemmTokens * Stager<KC, WAVES>::kPitch];
   if constexpr (kQueue) {
-    queue_loop(queue, *num_padded / kGemmTokens, gy, [&](int b, int cg) {
+    queue_loop(queue, live_blocks(num_padded, gx), gy, [&](int b, int cg) {
       ffn2_gemm_tile<WT, KC, P, RN, WAVES>(h, w2, s2, scale_mode, topk_w, sorted_ids,
                                            block_expert, y, d, I, A, b, cg, lds);
     });
