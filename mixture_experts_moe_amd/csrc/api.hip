@@ -95,6 +95,8 @@ struct Plan {
   // workspace offsets (bytes); xq, sx, sh only in the W8A8 mode, qcnt only
   // with the queue schedule
   size_t logits, ids, gates, counts, num_padded, sorted, block_exp, h, y, xq, sx, sh, qcnt, total;
+  size_t rpart;  // the split router's partial tiles (layer path, few tokens), or 0
+  bool rsplit;
 };
 
 // Block size of the regrouped layout.  Up to 64 tokens the weight-streaming
@@ -212,6 +214,8 @@ void make_plan(const moe_desc* d, int top_k, bool with_routing, Plan* p) {
     p->sorted = take(cap * 4);
     p->block_exp = take(cap / p->B * 4);
   } else {
+    p->rsplit = false;
+    p->rpart = 0;
     p->logits = p->ids = p->gates = p->counts = p->num_padded = p->sorted = p->block_exp = 0;
   }
   // h: bf16 (fp32 for fp32 layers), or e4m3fn codes in the W8A8 mode
@@ -225,6 +229,10 @@ void make_plan(const moe_desc* d, int top_k, bool with_routing, Plan* p) {
     p->xq = p->sx = p->sh = 0;
   }
   p->qcnt = p->queue ? take(moe::gemm_queue_ints() * 4) : 0;
+  if (with_routing) {
+    p->rsplit = moe::router_fused(p->act, p->T, p->E);
+    p->rpart = p->rsplit ? take(moe::router_split_bytes(p->T, p->E)) : 0;
+  }
   p->total = p->T == 0 ? 0 : off;  // nothing runs for T = 0
 }
 
@@ -377,11 +385,15 @@ MOE_API int moe_workspace_bytes(const moe_desc* desc, int top_k, int with_routin
 
 // Router logits and top-k: one kernel when the router kernel can select
 // itself (timed as route_logits), else two launches.
+// `part` (or nullptr): scratch for the split router when it applies.
 static hipError_t route(const void* x, int act, const float* w_gate, float* logits,
-                        int32_t* ids, float* gates, int T, int E, int d, int k, hipStream_t s) {
+                        int32_t* ids, float* gates, int T, int E, int d, int k, void* part,
+                        hipStream_t s) {
   if (moe::router_fused(act, T, E))
     return timed(MOE_KERNEL_ROUTE_LOGITS, s, [&] {
-      return moe::launch_router_fused(x, w_gate, logits, ids, gates, T, E, d, k, s);
+      return part ? moe::launch_router_fused_split(x, w_gate, logits, ids, gates, T, E, d, k,
+                                                   part, s)
+                  : moe::launch_router_fused(x, w_gate, logits, ids, gates, T, E, d, k, s);
     });
   hipError_t e = timed(MOE_KERNEL_ROUTE_LOGITS, s, [&] {
     return moe::launch_router_logits(x, act, w_gate, logits, T, E, d, s);
@@ -392,23 +404,26 @@ static hipError_t route(const void* x, int act, const float* w_gate, float* logi
   return e;
 }
 
-// Routing followed by the regrouping: one kernel when the router's single
-// workgroup can regroup too (timed as route_logits), else route() then the
-// regrouping kernel.
-// Routing and regrouping of the layer.  `queue` (or nullptr): the expert
-// kernels' work-queue counters; *queue_zeroed tells whether the align launch
-// has cleared them.
+// Routing followed by the regrouping: the router's single workgroup also
+// regroups when it can (timed as route_logits), else route() then the
+// regrouping kernel.  `part` (or nullptr): scratch for the split router.
+// `queue` (or nullptr): the expert kernels' work-queue counters;
+// *queue_zeroed tells whether the align launch has cleared them.
 static hipError_t route_align(const Plan& p, const void* x, const float* w_gate, float* logits,
                               int32_t* ids, float* gates, int32_t* counts, int32_t* sorted,
-                              int32_t* block_exp, int32_t* num_padded, int32_t* queue,
-                              bool* queue_zeroed, hipStream_t s) {
+                              int32_t* block_exp, int32_t* num_padded, void* part,
+                              int32_t* queue, bool* queue_zeroed, hipStream_t s) {
   *queue_zeroed = false;
   if (moe::route_align_fused(p.act, p.T, p.E))
     return timed(MOE_KERNEL_ROUTE_LOGITS, s, [&] {
-      return moe::launch_route_align_fused(x, w_gate, logits, ids, gates, p.T, p.E, p.d, p.k, p.B,
-                                           p.cap, counts, sorted, block_exp, num_padded, s);
+      return part ? moe::launch_route_align_fused_split(x, w_gate, logits, ids, gates, p.T, p.E,
+                                                        p.d, p.k, p.B, p.cap, counts, sorted,
+                                                        block_exp, num_padded, part, s)
+                  : moe::launch_route_align_fused(x, w_gate, logits, ids, gates, p.T, p.E, p.d,
+                                                  p.k, p.B, p.cap, counts, sorted, block_exp,
+                                                  num_padded, s);
     });
-  hipError_t e = route(x, p.act, w_gate, logits, ids, gates, p.T, p.E, p.d, p.k, s);
+  hipError_t e = route(x, p.act, w_gate, logits, ids, gates, p.T, p.E, p.d, p.k, part, s);
   const int nzero = queue ? moe::gemm_queue_ints() : 0;
   if (e == hipSuccess)
     e = timed(MOE_KERNEL_ALIGN, s, [&] {
@@ -428,7 +443,8 @@ MOE_API int moe_route(const moe_desc* desc, const void* x, const float* w_gate, 
   if ((st = check_ptrs({x, w_gate, logits, topk_ids, topk_w}))) return st;
   const int E = static_cast<int>(desc->num_experts), d = static_cast<int>(desc->hidden);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return to_status(route(x, desc->act_dtype, w_gate, logits, topk_ids, topk_w, T, E, d, top_k, s));
+  return to_status(
+      route(x, desc->act_dtype, w_gate, logits, topk_ids, topk_w, T, E, d, top_k, nullptr, s));
 }
 
 MOE_API int moe_route_logits(const moe_desc* desc, const float* logits, int top_k,
@@ -476,7 +492,7 @@ MOE_API int moe_route_align(const moe_desc* desc, const void* x, const float* w_
   hipStream_t s = static_cast<hipStream_t>(stream);
   bool zeroed = false;
   return to_status(route_align(p, x, w_gate, logits, topk_ids, topk_w, counts, sorted_ids,
-                               block_expert, num_padded, nullptr, &zeroed, s));
+                               block_expert, num_padded, nullptr, nullptr, &zeroed, s));
 }
 
 MOE_API int moe_expert_ffn(const moe_desc* desc, const void* x, const void* w13, const void* w2,
@@ -548,8 +564,9 @@ static int enqueue_forward(const Plan& p, const void* x, const float* w_gate, co
 
   int32_t* queue = p.queue ? reinterpret_cast<int32_t*>(ws + p.qcnt) : nullptr;
   bool zeroed = false;
+  void* part = p.rsplit ? ws + p.rpart : nullptr;
   const hipError_t e = route_align(p, x, w_gate, logits, ids, gates, counts, sorted, block_exp,
-                                   num_padded, queue, &zeroed, s);
+                                   num_padded, part, queue, &zeroed, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   FfnArgs a = ffn_args(p, x, w13, w2, scales, gates, sorted, block_exp, num_padded, out, ws);
   a.queue_zeroed = zeroed;

@@ -32,6 +32,18 @@ hipError_t launch_route_align_fused(const void* x, const float* wg, float* logit
                                     float* w, int T, int E, int d, int k, int B, int cap,
                                     int32_t* counts, int32_t* sorted_ids, int32_t* block_expert,
                                     int32_t* num_padded, hipStream_t s);
+// The same two operations with K split over 16 one-wave workgroups and a
+// second launch that adds their partials in the fused kernel's order (same
+// results, bit for bit); `part` is router_split_bytes(T, E) of scratch.
+size_t router_split_bytes(int T, int E);
+hipError_t launch_router_fused_split(const void* x, const float* wg, float* logits, int32_t* ids,
+                                     float* w, int T, int E, int d, int k, void* part,
+                                     hipStream_t s);
+hipError_t launch_route_align_fused_split(const void* x, const float* wg, float* logits,
+                                          int32_t* ids, float* w, int T, int E, int d, int k,
+                                          int B, int cap, int32_t* counts, int32_t* sorted_ids,
+                                          int32_t* block_expert, int32_t* num_padded, void* part,
+                                          hipStream_t s);
 // `zero`: nzero int32 that the launch also sets to 0 (the expert kernels'
 // work-queue counters when the layer runs align right before them).
 hipError_t launch_align(const int32_t* ids, int A, int E, int B, int cap, int32_t* counts,

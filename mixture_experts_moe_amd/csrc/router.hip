@@ -268,13 +268,25 @@ __device__ __forceinline__ void split3_bf16(const float (&w)[8], uint4& hi, uint
 
 // kTopk (NT = 1, NW = 16, E <= 16: one workgroup holds every expert of its
 // 16 tokens): the workgroup also selects, one wave per token.
-template <int NT, int NW, bool kTopk, bool kAlign = false>
+// K split over several workgroups (kPart): the 16-wave workgroup's work cut
+// in two launches with the same arithmetic.  kPart = 1: a one-wave workgroup
+// per (token tile, expert tile, slice z) computes what wave z of the 16-wave
+// workgroup computes and stores that partial tile; kPart = 2: the 16-wave
+// workgroup takes wave w's partial tile from that store instead of computing
+// it, then adds, selects and regroups exactly as kPart = 0 does.  A few
+// tokens' W_gate (128 KB at d = 4096, E = 8) then streams through 16 CUs'
+// miss queues instead of one.
+constexpr int kRouterSlices = 16;
+
+template <int NT, int NW, bool kTopk, bool kAlign = false, int kPart = 0>
 __global__ __launch_bounds__(64 * NW) void router_logits_bf16_kernel(
     const bf16_t* __restrict__ x, const float* __restrict__ wg, float* __restrict__ logits,
     int32_t* __restrict__ topk_ids, float* __restrict__ topk_w, int T, int E, int d, int k,
-    AlignOut ao) {
+    AlignOut ao, f32x4* __restrict__ part) {
   static_assert(!kTopk || (NT == 1 && NW == 16), "fused selection: 16 tokens, 16 waves");
   static_assert(!kAlign || kTopk, "regrouping follows the selection");
+  static_assert(kPart == 0 || (NT == 1 && NW == (kPart == 1 ? 1 : kRouterSlices)),
+                "split K: one-wave slices, then the 16-wave workgroup");
   // 32-wide steps whose loads are issued together: the few-token kernel is
   // latency-bound, so it takes a whole wave's K range (d = 4096) in one round
   constexpr int U = NT == 1 ? 8 : 4;
@@ -296,8 +308,10 @@ __global__ __launch_bounds__(64 * NW) void router_logits_bf16_kernel(
     xrow[nt] = x + static_cast<size_t>(t_ok[nt] ? t : 0) * d + 8 * g;
   }
   const int steps = d / 32;
-  const int s_begin = wave * steps / NW;
-  const int s_end = (wave + 1) * steps / NW;
+  constexpr int kSlices = kPart == 0 ? NW : kRouterSlices;
+  const int slice = kPart == 1 ? static_cast<int>(blockIdx.z) : wave;
+  const int s_begin = slice * steps / kSlices;
+  const int s_end = kPart == 2 ? s_begin : (slice + 1) * steps / kSlices;  // 2: nothing to compute
   f32x4 acc_h[NT], acc_m[NT], acc_l[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc_h[nt] = acc_m[nt] = acc_l[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -329,8 +343,17 @@ __global__ __launch_bounds__(64 * NW) void router_logits_bf16_kernel(
       }
     }
   }
+  // partial tile of slice z for this (token tile, expert tile)
+  const size_t part_at =
+      ((static_cast<size_t>(slice) * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x) * 64 + lane;
+  if constexpr (kPart == 1) {
+    part[part_at] = acc_h[0] + (acc_m[0] + acc_l[0]);
+    return;
+  } else {
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) red[wave][nt][lane] = acc_h[nt] + (acc_m[nt] + acc_l[nt]);
+    for (int nt = 0; nt < NT; ++nt)
+      red[wave][nt][lane] = kPart == 2 ? part[part_at] : acc_h[nt] + (acc_m[nt] + acc_l[nt]);
+  }
   __syncthreads();
   // D layout: lane holds token column r16, expert rows 4g .. 4g+3.  The wave
   // partials are added in wave order.
@@ -382,11 +405,11 @@ hipError_t launch_router_logits(const void* x, int act_dtype, const float* wg, f
     // with K split 16 ways
     dim3 grid((T + 15) / 16, (E + 15) / 16);
     router_logits_bf16_kernel<1, 16, false><<<grid, 1024, 0, s>>>(
-        static_cast<const bf16_t*>(x), wg, logits, nullptr, nullptr, T, E, d, 0, AlignOut{});
+        static_cast<const bf16_t*>(x), wg, logits, nullptr, nullptr, T, E, d, 0, AlignOut{}, nullptr);
   } else {
     dim3 grid((T + 63) / 64, (E + 15) / 16);
     router_logits_bf16_kernel<4, 4, false><<<grid, 256, 0, s>>>(
-        static_cast<const bf16_t*>(x), wg, logits, nullptr, nullptr, T, E, d, 0, AlignOut{});
+        static_cast<const bf16_t*>(x), wg, logits, nullptr, nullptr, T, E, d, 0, AlignOut{}, nullptr);
   }
   return hipGetLastError();
 }
@@ -399,7 +422,7 @@ hipError_t launch_router_fused(const void* x, const float* wg, float* logits, in
                                float* w, int T, int E, int d, int k, hipStream_t s) {
   if (E > 16) return hipErrorInvalidValue;
   router_logits_bf16_kernel<1, 16, true><<<dim3((T + 15) / 16, 1), 1024, 0, s>>>(
-      static_cast<const bf16_t*>(x), wg, logits, ids, w, T, E, d, k, AlignOut{});
+      static_cast<const bf16_t*>(x), wg, logits, ids, w, T, E, d, k, AlignOut{}, nullptr);
   return hipGetLastError();
 }
 
@@ -415,7 +438,42 @@ hipError_t launch_route_align_fused(const void* x, const float* wg, float* logit
     return hipErrorInvalidValue;
   const AlignOut ao{B, cap, counts, sorted_ids, block_expert, num_padded};
   router_logits_bf16_kernel<1, 16, true, true><<<dim3(1, 1), 1024, 0, s>>>(
-      static_cast<const bf16_t*>(x), wg, logits, ids, w, T, E, d, k, ao);
+      static_cast<const bf16_t*>(x), wg, logits, ids, w, T, E, d, k, ao, nullptr);
+  return hipGetLastError();
+}
+
+size_t router_split_bytes(int T, int E) {
+  return static_cast<size_t>(kRouterSlices) * ((T + 15) / 16) * ((E + 15) / 16) * 64 *
+         sizeof(f32x4);
+}
+
+hipError_t launch_router_fused_split(const void* x, const float* wg, float* logits, int32_t* ids,
+                                     float* w, int T, int E, int d, int k, void* part,
+                                     hipStream_t s) {
+  if (!router_fused(kDtypeBF16, T, E) || !part) return hipErrorInvalidValue;
+  const bf16_t* xb = static_cast<const bf16_t*>(x);
+  f32x4* pt = static_cast<f32x4*>(part);
+  router_logits_bf16_kernel<1, 1, false, false, 1><<<dim3((T + 15) / 16, 1, kRouterSlices), 64, 0, s>>>(
+      xb, wg, nullptr, nullptr, nullptr, T, E, d, 0, AlignOut{}, pt);
+  router_logits_bf16_kernel<1, 16, true, false, 2><<<dim3((T + 15) / 16, 1), 1024, 0, s>>>(
+      xb, wg, logits, ids, w, T, E, d, k, AlignOut{}, pt);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_align_fused_split(const void* x, const float* wg, float* logits,
+                                          int32_t* ids, float* w, int T, int E, int d, int k,
+                                          int B, int cap, int32_t* counts, int32_t* sorted_ids,
+                                          int32_t* block_expert, int32_t* num_padded, void* part,
+                                          hipStream_t s) {
+  if (!route_align_fused(kDtypeBF16, T, E) || k > E || B < 1 || cap % B != 0 || !part)
+    return hipErrorInvalidValue;
+  const AlignOut ao{B, cap, counts, sorted_ids, block_expert, num_padded};
+  const bf16_t* xb = static_cast<const bf16_t*>(x);
+  f32x4* pt = static_cast<f32x4*>(part);
+  router_logits_bf16_kernel<1, 1, false, false, 1><<<dim3(1, 1, kRouterSlices), 64, 0, s>>>(
+      xb, wg, nullptr, nullptr, nullptr, T, E, d, 0, AlignOut{}, pt);
+  router_logits_bf16_kernel<1, 16, true, true, 2><<<dim3(1, 1), 1024, 0, s>>>(
+      xb, wg, logits, ids, w, T, E, d, k, ao, pt);
   return hipGetLastError();
 }
 

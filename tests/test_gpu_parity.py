@@ -481,6 +481,24 @@ def test_graph_replay_matches_eager(wl, T, over):
         graph.close()
 
 
+@pytest.mark.parametrize("T,E,k,d", [(1, 8, 2, 4096), (8, 8, 2, 4096), (16, 16, 4, 512),
+                                     (17, 8, 2, 4096), (32, 8, 2, 4096), (64, 8, 2, 4096),
+                                     (64, 12, 1, 512), (5, 16, 16, 320)])
+def test_layer_split_router_equals_single_workgroup_router(T, E, k, d):
+    """The layer splits the few-token router over 16 workgroups; the stage
+    entry points run it in one.  Gates enter the output, so bit-equal layer
+    outputs mean bit-equal logits, ids and gates."""
+    note(f"split router T={T} E={E} k={k} d={d}")
+    inp = synth.make_inputs("decode_bf16", T=T, device=DEV, d=d, I=256, E=E, k=k, x_std=1.0)
+    out = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k)
+    got = B.moe_route_align(inp.x, inp.w_gate, inp.top_k, intermediate=inp.I)
+    logits, ids, w, counts, sorted_ids, block_expert, num_padded, bm = got
+    ref = B.moe_expert_ffn(inp.x, inp.w13, inp.w2, inp.top_k, w, sorted_ids, block_expert,
+                           num_padded)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+
+
 # ---------------------------------------------------------------- tile schedules
 
 SCHED_CASES = [
