@@ -230,7 +230,8 @@ void make_plan(const moe_desc* d, int top_k, bool with_routing, Plan* p) {
   }
   p->qcnt = p->queue ? take(moe::gemm_queue_ints() * 4) : 0;
   if (with_routing) {
-    p->rsplit = moe::router_fused(p->act, p->T, p->E);
+    p->rsplit = moe::router_fused(p->act, p->T, p->E) ||
+                moe::router_split_logits(p->act, p->T, p->E);
     p->rpart = p->rsplit ? take(moe::router_split_bytes(p->T, p->E)) : 0;
   }
   p->total = p->T == 0 ? 0 : off;  // nothing runs for T = 0
@@ -396,7 +397,9 @@ static hipError_t route(const void* x, int act, const float* w_gate, float* logi
                   : moe::launch_router_fused(x, w_gate, logits, ids, gates, T, E, d, k, s);
     });
   hipError_t e = timed(MOE_KERNEL_ROUTE_LOGITS, s, [&] {
-    return moe::launch_router_logits(x, act, w_gate, logits, T, E, d, s);
+    return part && moe::router_split_logits(act, T, E)
+               ? moe::launch_router_split_logits(x, w_gate, logits, T, E, d, part, s)
+               : moe::launch_router_logits(x, act, w_gate, logits, T, E, d, s);
   });
   if (e == hipSuccess)
     e = timed(MOE_KERNEL_ROUTE_TOPK, s,

@@ -44,6 +44,12 @@ hipError_t launch_route_align_fused_split(const void* x, const float* wg, float*
                                           int B, int cap, int32_t* counts, int32_t* sorted_ids,
                                           int32_t* block_expert, int32_t* num_padded, void* part,
                                           hipStream_t s);
+// bf16 activations, 1 <= T <= 64, any E: the logits alone, K split the same
+// way (16 one-wave workgroups per tile, then a sum in slice order: the same
+// bits as launch_router_logits); `part` is router_split_bytes(T, E).
+bool router_split_logits(int act_dtype, int T, int E);
+hipError_t launch_router_split_logits(const void* x, const float* wg, float* logits, int T, int E,
+                                      int d, void* part, hipStream_t s);
 // `zero`: nzero int32 that the launch also sets to 0 (the expert kernels'
 // work-queue counters when the layer runs align right before them).
 hipError_t launch_align(const int32_t* ids, int A, int E, int B, int cap, int32_t* counts,

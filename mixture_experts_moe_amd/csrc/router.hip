@@ -460,6 +460,40 @@ hipError_t launch_router_fused_split(const void* x, const float* wg, float* logi
   return hipGetLastError();
 }
 
+// Split logits for any E: slice z's partial tiles summed in slice order
+// into the logits (what the 16-wave router's workgroup writes).  Grid: the
+// partial launch's token and expert tiles, one wave each.
+__global__ __launch_bounds__(64) void router_split_sum_kernel(const f32x4* __restrict__ part,
+                                                             float* __restrict__ logits, int T,
+                                                             int E) {
+  const int lane = threadIdx.x;
+  const size_t tile = static_cast<size_t>(blockIdx.y) * gridDim.x + blockIdx.x;
+  const size_t tiles = static_cast<size_t>(gridDim.x) * gridDim.y;
+  f32x4 v = part[tile * 64 + lane];
+  for (int z = 1; z < kRouterSlices; ++z) v += part[(z * tiles + tile) * 64 + lane];
+  const int t = blockIdx.x * 16 + (lane & 15);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int ee = blockIdx.y * 16 + 4 * (lane >> 4) + q;
+    if (t < T && ee < E) logits[static_cast<size_t>(t) * E + ee] = v[q];
+  }
+}
+
+bool router_split_logits(int act_dtype, int T, int E) {
+  return act_dtype == kDtypeBF16 && T >= 1 && T <= 64 && E <= kMaxExperts;
+}
+
+hipError_t launch_router_split_logits(const void* x, const float* wg, float* logits, int T, int E,
+                                      int d, void* part, hipStream_t s) {
+  if (!router_split_logits(kDtypeBF16, T, E) || !part) return hipErrorInvalidValue;
+  f32x4* pt = static_cast<f32x4*>(part);
+  const int gx = (T + 15) / 16, gy = (E + 15) / 16;
+  router_logits_bf16_kernel<1, 1, false, false, 1><<<dim3(gx, gy, kRouterSlices), 64, 0, s>>>(
+      static_cast<const bf16_t*>(x), wg, nullptr, nullptr, nullptr, T, E, d, 0, AlignOut{}, pt);
+  router_split_sum_kernel<<<dim3(gx, gy), 64, 0, s>>>(pt, logits, T, E);
+  return hipGetLastError();
+}
+
 hipError_t launch_route_align_fused_split(const void* x, const float* wg, float* logits,
                                           int32_t* ids, float* w, int T, int E, int d, int k,
                                           int B, int cap, int32_t* counts, int32_t* sorted_ids,

@@ -483,7 +483,9 @@ def test_graph_replay_matches_eager(wl, T, over):
 
 @pytest.mark.parametrize("T,E,k,d", [(1, 8, 2, 4096), (8, 8, 2, 4096), (16, 16, 4, 512),
                                      (17, 8, 2, 4096), (32, 8, 2, 4096), (64, 8, 2, 4096),
-                                     (64, 12, 1, 512), (5, 16, 16, 320)])
+                                     (64, 12, 1, 512), (5, 16, 16, 320),
+                                     # more than 16 experts: split logits, then top-k
+                                     (1, 32, 4, 512), (64, 256, 8, 1024), (40, 1024, 2, 256)])
 def test_layer_split_router_equals_single_workgroup_router(T, E, k, d):
     """The layer splits the few-token router over 16 workgroups; the stage
     entry points run it in one.  Gates enter the output, so bit-equal layer
