@@ -188,7 +188,8 @@ void make_plan(const moe_desc* d, int top_k, bool with_routing, Plan* p) {
     const int kc = moe::ffn2_kchunk(p->d, p->I, p->B, p->wdt, p->act, blocks_est);
     // one wave per dma_w2_channels() (LDS streaming) or about 32 (register
     // path) output channels
-    const int64_t waves = blocks_est * (p->d / (lds ? moe::dma_w2_channels(p->wdt) : 32));
+    const int64_t waves =
+        blocks_est * (p->d / (lds ? moe::dma_w2_channels(p->wdt, p->B, blocks_est) : 32));
     int s = 1;
     while (s < MOE_W2_MAX_SPLITS && waves * s < MOE_W2_SPLIT_WAVES &&
            p->I / (2 * s) >= MOE_W2_MIN_CHUNKS * kc)

@@ -405,7 +405,23 @@ __global__ __launch_bounds__(kDmaThreads) void ffn2_dma_kernel(
 constexpr int kDma2RN = MOE_DMA2_RN;
 constexpr int kDma2RNFp8 = MOE_DMA_FP8_RN2;
 
-int dma_w2_channels(int w_dtype) { return 16 * (w_dtype == kDtypeE4M3FN ? kDma2RNFp8 : kDma2RN); }
+// Four channel tiles per bf16 W2 wave when blocks of 16 give at most two row
+// blocks (a single token of a top-2 layer): the grid is small there, and
+// wider waves read the block's h rows half as often (measured at d = 4096,
+// I = 14336: 50 -> 44 us with a two-stage ring); with more blocks two tiles
+// per wave are faster (T = 8: 160 against 172 us).
+constexpr int kDma2WideRN = 4;
+constexpr int kDma2WideP = 2;
+constexpr int64_t kDma2WideBlocks = 2;
+
+static int dma_w2_rn(int w_dtype, int B, int64_t blocks_est) {
+  if (w_dtype == kDtypeE4M3FN) return kDma2RNFp8;
+  return B == 16 && blocks_est <= kDma2WideBlocks ? kDma2WideRN : kDma2RN;
+}
+
+int dma_w2_channels(int w_dtype, int B, int64_t blocks_est) {
+  return 16 * dma_w2_rn(w_dtype, B, blocks_est);
+}
 
 namespace {
 
@@ -418,9 +434,8 @@ hipError_t ffn13_dma_go(const FfnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename WT, int NS, int P>
+template <typename WT, int NS, int P, int RN = sizeof(WT) == 1 ? kDma2RNFp8 : kDma2RN>
 hipError_t ffn2_dma_go(const FfnArgs& a, hipStream_t s) {
-  constexpr int RN = sizeof(WT) == 1 ? kDma2RNFp8 : kDma2RN;
   const dim3 grid(a.cap / a.B, a.d / (16 * RN), a.splits);
   ffn2_dma_kernel<WT, NS, P, RN><<<grid, kDmaThreads, 0, s>>>(
       static_cast<const bf16_t*>(a.h), static_cast<const WT*>(a.w2), a.s2, a.scale_mode,
@@ -448,12 +463,15 @@ hipError_t launch_ffn13_dma(const FfnArgs& a, hipStream_t s) {
 
 hipError_t launch_ffn2_dma(const FfnArgs& a, hipStream_t s) {
   if (!dma_args_ok(a) || a.ksplit % dma_stream_kc(a.w_dtype) != 0 ||
-      a.d % dma_w2_channels(a.w_dtype) != 0)
+      a.d % dma_w2_channels(a.w_dtype, a.B, ffn_blocks_estimate(a.cap, a.B, a.E, a.A)) != 0)
     return hipErrorInvalidValue;
   if (a.w_dtype == kDtypeE4M3FN)
     return a.B == 16 ? ffn2_dma_go<fp8_t, 1, MOE_DMA_FP8_P2>(a, s) : hipErrorInvalidValue;
   switch (a.B) {
-    case 16: return ffn2_dma_go<bf16_t, 1, MOE_DMA2_P1>(a, s);
+    case 16:
+      if (dma_w2_rn(a.w_dtype, a.B, ffn_blocks_estimate(a.cap, a.B, a.E, a.A)) == kDma2WideRN)
+        return ffn2_dma_go<bf16_t, 1, kDma2WideP, kDma2WideRN>(a, s);
+      return ffn2_dma_go<bf16_t, 1, MOE_DMA2_P1>(a, s);
     case 32: return ffn2_dma_go<bf16_t, 2, MOE_DMA2_P2>(a, s);
   }
   return hipErrorInvalidValue;

@@ -149,7 +149,8 @@ inline bool dma_stream_use(const FfnArgs& a) {
                         ffn_blocks_estimate(a.cap, a.B, a.E, a.A));
 }
 hipError_t launch_ffn13_dma(const FfnArgs& a, hipStream_t s);
-int dma_w2_channels(int w_dtype);  // output channels per W2 workgroup of that path
+// output channels per W2 workgroup of that path for a block size and block estimate
+int dma_w2_channels(int w_dtype, int B, int64_t blocks_est);
 hipError_t launch_ffn2_dma(const FfnArgs& a, hipStream_t s);
 
 // K chunk the W2 kernel uses for a given shape, block size, dtypes and

@@ -129,6 +129,8 @@ SMALL = [
     ("bf16_lds", dict(workload="decode_bf16", d=768, I=2048, E=32, x_std=1.0), 16, 0),
     ("bf16_lds", dict(workload="decode_bf16", d=256, I=2304, E=8, x_std=1.0), 384, 32),
     ("bf16_lds", dict(workload="decode_bf16", d=1280, I=2048, E=32, x_std=1.0), 24, 0),
+    # one token, two row blocks: W2 with four channel tiles per wave
+    ("bf16_lds", dict(workload="decode_bf16", d=512, I=8192, E=8, x_std=1.0), 1, 0),
     ("bf16_big", dict(workload="decode_bf16", d=512, I=384, E=4, x_std=1.0), 700, 256),
     ("bf16_big", dict(workload="decode_bf16", d=256, I=128, E=8, k=2, x_std=1.0), 1500, 0),
     ("bf16_big", dict(workload="decode_bf16", d=768, I=256, E=3, k=1, x_std=1.0), 300, 256),
