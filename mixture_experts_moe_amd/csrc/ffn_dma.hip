@@ -455,7 +455,13 @@ hipError_t launch_ffn13_dma(const FfnArgs& a, hipStream_t s) {
   if (a.w_dtype == kDtypeE4M3FN)
     return a.B == 16 ? ffn13_dma_go<fp8_t, 1, MOE_DMA_FP8_P13>(a, s) : hipErrorInvalidValue;
   switch (a.B) {
-    case 16: return ffn13_dma_go<bf16_t, 1, MOE_DMA13_P1>(a, s);
+    case 16:
+      // at most two row blocks (one token of a top-2 layer): a two-stage
+      // ring keeps more workgroups resident for the few rounds there are
+      // (d = 4096, I = 14336: 83 -> 77 us; with eight blocks it is level)
+      if (ffn_blocks_estimate(a.cap, a.B, a.E, a.A) <= kDma2WideBlocks)
+        return ffn13_dma_go<bf16_t, 1, 2>(a, s);
+      return ffn13_dma_go<bf16_t, 1, MOE_DMA13_P1>(a, s);
     case 32: return ffn13_dma_go<bf16_t, 2, MOE_DMA13_P2>(a, s);
   }
   return hipErrorInvalidValue;
