@@ -182,8 +182,13 @@ MOE_API int moe_route(const moe_desc* desc, const void* x, const float* w_gate, 
                       float* logits_out, int32_t* topk_ids, float* topk_w, void* stream);
 
 /* Top-k selection and gates from given logits [T, E] fp32 (the second half
- * of moe_route, same kernel).  Lets a caller check routing against any
- * logits.  Same outputs and rules as moe_route. */
+ * of moe_route, same kernel): the token routing of the Hungarian page,
+ * section "A fused MoE ..." (which names the step, not its rule; the rule is
+ * the reading at the top of this header: the top_k largest logits, ties to
+ * the lower expert index, gates = softmax over the selected logits).  Lets a
+ * caller check routing against any logits.  logits, topk_ids [T, top_k]
+ * int32 and topk_w [T, top_k] fp32 are caller-owned device buffers; same
+ * outputs, rules and errors as moe_route; asynchronous on `stream`. */
 MOE_API int moe_route_logits(const moe_desc* desc, const float* logits, int top_k,
                              int32_t* topk_ids, float* topk_w, void* stream);
 

@@ -2,7 +2,10 @@
 
 Argument marshalling only: every function takes torch tensors, checks their
 shapes, dtypes and devices, and calls the C entry point of the same name with
-raw device pointers and the current HIP stream.  All computation happens in
+raw device pointers and a HIP stream (the one given, else torch's current
+stream of the tensors' device).  Tensors the binding allocates (outputs,
+workspace) are allocated on that stream, so torch's caching allocator only
+reuses their memory for work ordered after these kernels.  All computation happens in
 the HIP kernels of ``libmoe.so``; there is no fallback of any kind, and if
 the library is missing the first call raises.
 """
@@ -257,9 +260,15 @@ def _scales(w13: torch.Tensor, scales) -> Optional[moe_scales]:
 
 
 def _shapes(x, w_gate, w13, w2):
+    """(T, d, E, I) from the tensors' shapes; raises before any launch when
+    shapes or dtypes do not fit together (metadata only: no device access)."""
+    if x.dim() != 2:
+        raise ValueError(f"x must be [T, d], got shape {tuple(x.shape)}")
     T, d = x.shape
     if w13.dim() != 3 or w2.dim() != 3:
         raise ValueError("w13 must be [E, 2I, d] and w2 [E, d, I]")
+    if _w_code(w2) != _w_code(w13) or w2.element_size() != w13.element_size():
+        raise TypeError(f"w13 and w2 must have one weight format, got {w13.dtype} and {w2.dtype}")
     E, twoI, d13 = w13.shape
     I = twoI // 2
     if d13 != d or twoI != 2 * I or tuple(w2.shape) != (E, d, I):
@@ -270,12 +279,49 @@ def _shapes(x, w_gate, w13, w2):
     return T, d, E, I
 
 
-def _workspace(nbytes: int, dev, workspace: Optional[torch.Tensor]) -> torch.Tensor:
+def _launch_stream(dev: torch.device, stream=None):
+    """The torch stream the kernels are enqueued on."""
+    return stream if stream is not None else torch.cuda.current_stream(dev)
+
+
+def _alloc(shape, dtype, dev, stream) -> torch.Tensor:
+    """A new device tensor owned by `stream` in torch's caching allocator, so
+    that once it is dropped its memory is only handed to later work on that
+    same stream, i.e. after the kernels enqueued here have used it."""
+    with torch.cuda.stream(stream):
+        return torch.empty(shape, dtype=dtype, device=dev)
+
+
+def _workspace(nbytes: int, dev, workspace: Optional[torch.Tensor], stream) -> torch.Tensor:
     if workspace is not None:
         if workspace.numel() * workspace.element_size() < nbytes:
             raise ValueError("workspace too small")
         return workspace
-    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    return _alloc((max(nbytes, 1),), torch.uint8, dev, stream)
+
+
+def _check_out(out: torch.Tensor, x: torch.Tensor) -> None:
+    if tuple(out.shape) != tuple(x.shape) or out.dtype != x.dtype:
+        raise ValueError(f"out must match x in shape and dtype: out {tuple(out.shape)} "
+                         f"{out.dtype}, x {tuple(x.shape)} {x.dtype}")
+
+
+def _check_routing(T: int, top_k: int, topk_w: torch.Tensor, sorted_ids: torch.Tensor,
+                   block_expert: torch.Tensor, num_padded: torch.Tensor, cap: int,
+                   bm: int) -> None:
+    """The routing tensors moe_expert_ffn reads: gates fp32 [T, k], the
+    regrouped layout int32 and at least as long as the capacity."""
+    if topk_w.dtype != torch.float32 or tuple(topk_w.shape) != (T, top_k):
+        raise ValueError(f"topk_w must be float32 [{T}, {top_k}], got {topk_w.dtype} "
+                         f"{tuple(topk_w.shape)}")
+    for name, t in (("sorted_ids", sorted_ids), ("block_expert", block_expert),
+                    ("num_padded", num_padded)):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32, got {t.dtype}")
+    if sorted_ids.numel() < cap or block_expert.numel() < cap // bm:
+        raise ValueError("sorted_ids / block_expert smaller than the layout capacity")
+    if num_padded.numel() < 1:
+        raise ValueError("num_padded must hold one int32")
 
 
 # ------------------------------------------------------------ entry points
@@ -305,19 +351,20 @@ def moe_forward(x: torch.Tensor, w_gate: torch.Tensor, w13: torch.Tensor, w2: to
     selects the W8A8 mode (e4m3fn weights; x and h block-scaled e4m3fn);
     schedule ("auto", "static", "queue") how the 128-token-block expert
     kernels hand out their tiles."""
-    dev = _dev(x, w_gate, w13, w2, out)
     T, d, E, I = _shapes(x, w_gate, w13, w2)
+    if out is not None:
+        _check_out(out, x)
+    dev = _dev(x, w_gate, w13, w2, out)
     desc = make_desc(T, d, E, I, _act_code(x), _w_code(w13), block_m, act_quant, schedule)
     sc = _scales(w13, scales)
+    s = _launch_stream(dev, stream)
     if out is None:
-        out = torch.empty((T, d), dtype=x.dtype, device=dev)
-    elif out.shape != x.shape or out.dtype != x.dtype:
-        raise ValueError("out must match x in shape and dtype")
+        out = _alloc((T, d), x.dtype, dev, s)
     nbytes = moe_workspace_bytes(desc, top_k, True)
-    ws = _workspace(nbytes, dev, workspace)
+    ws = _workspace(nbytes, dev, workspace, s)
     st = lib().moe_forward(ctypes.byref(desc), _ptr(x), _ptr(w_gate), _ptr(w13), _ptr(w2),
                            int(top_k), ctypes.byref(sc) if sc is not None else None, _ptr(out),
-                           _ptr(ws), nbytes, _stream(dev, stream))
+                           _ptr(ws), nbytes, ctypes.c_void_p(s.cuda_stream))
     _check("moe_forward", st)
     return out
 
@@ -325,30 +372,32 @@ def moe_forward(x: torch.Tensor, w_gate: torch.Tensor, w13: torch.Tensor, w2: to
 def moe_route(x: torch.Tensor, w_gate: torch.Tensor, top_k: int, *, stream=None):
     """(logits [T,E] fp32, topk_ids [T,k] int32, topk_w [T,k] fp32)."""
     dev = _dev(x, w_gate)
+    s = _launch_stream(dev, stream)
     T, d = x.shape
     E = w_gate.shape[0]
     if w_gate.dtype != torch.float32 or w_gate.shape[1] != d:
         raise ValueError("w_gate must be float32 [E, d]")
     desc = make_desc(T, d, E, 64, _act_code(x), _act_code(x))
-    logits = torch.empty((T, E), dtype=torch.float32, device=dev)
-    ids = torch.empty((T, top_k), dtype=torch.int32, device=dev)
-    w = torch.empty((T, top_k), dtype=torch.float32, device=dev)
+    logits = _alloc((T, E), torch.float32, dev, s)
+    ids = _alloc((T, top_k), torch.int32, dev, s)
+    w = _alloc((T, top_k), torch.float32, dev, s)
     _check("moe_route", lib().moe_route(ctypes.byref(desc), _ptr(x), _ptr(w_gate), int(top_k),
-                                        _ptr(logits), _ptr(ids), _ptr(w), _stream(dev, stream)))
+                                        _ptr(logits), _ptr(ids), _ptr(w), ctypes.c_void_p(s.cuda_stream)))
     return logits, ids, w
 
 
 def moe_route_logits(logits: torch.Tensor, top_k: int, *, stream=None):
     """(topk_ids [T,k] int32, topk_w [T,k] fp32) from given fp32 logits [T,E]."""
     dev = _dev(logits)
+    s = _launch_stream(dev, stream)
     if logits.dtype != torch.float32 or logits.dim() != 2:
         raise ValueError("logits must be float32 [T, E]")
     T, E = logits.shape
     desc = make_desc(T, 64, E, 64, MOE_DTYPE_F32, MOE_DTYPE_F32)
-    ids = torch.empty((T, top_k), dtype=torch.int32, device=dev)
-    w = torch.empty((T, top_k), dtype=torch.float32, device=dev)
+    ids = _alloc((T, top_k), torch.int32, dev, s)
+    w = _alloc((T, top_k), torch.float32, dev, s)
     _check("moe_route_logits", lib().moe_route_logits(ctypes.byref(desc), _ptr(logits), int(top_k),
-                                                      _ptr(ids), _ptr(w), _stream(dev, stream)))
+                                                      _ptr(ids), _ptr(w), ctypes.c_void_p(s.cuda_stream)))
     return ids, w
 
 
@@ -356,15 +405,16 @@ def moe_quantize_act(x: torch.Tensor, *, stream=None):
     """W8A8 activation quantisation of bf16 x [T, d]: (codes [T, d] uint8
     e4m3fn bytes, exps [T, d/32] uint8 E8M0 bytes, scale 2^(byte - 127))."""
     dev = _dev(x)
+    s = _launch_stream(dev, stream)
     if x.dtype != torch.bfloat16 or x.dim() != 2:
         raise ValueError("x must be bfloat16 [T, d]")
     T, d = x.shape
     inter = 256
     desc = make_desc(T, d, 1, inter, MOE_DTYPE_BF16, MOE_DTYPE_E4M3FN, 0, "mx_e4m3")
-    codes = torch.empty((T, d), dtype=torch.uint8, device=dev)
-    exps = torch.empty((T, d // 32), dtype=torch.uint8, device=dev)
+    codes = _alloc((T, d), torch.uint8, dev, s)
+    exps = _alloc((T, d // 32), torch.uint8, dev, s)
     _check("moe_quantize_act", lib().moe_quantize_act(ctypes.byref(desc), _ptr(x), _ptr(codes),
-                                                      _ptr(exps), _stream(dev, stream)))
+                                                      _ptr(exps), ctypes.c_void_p(s.cuda_stream)))
     return codes, exps
 
 
@@ -376,19 +426,20 @@ def moe_align(topk_ids: torch.Tensor, num_experts: int, *, block_m: int = 0, hid
     descriptor, so pass the layer's dims/dtypes/act_quant to get the one
     moe_forward uses."""
     dev = _dev(topk_ids)
+    s = _launch_stream(dev, stream)
     if topk_ids.dtype != torch.int32 or topk_ids.dim() != 2:
         raise ValueError("topk_ids must be int32 [T, k]")
     T, k = topk_ids.shape
     desc = make_desc(T, hidden, num_experts, intermediate, act_dtype, weight_dtype, block_m,
                      act_quant)
     B, cap = moe_align_capacity(desc, k)
-    counts = torch.empty(num_experts, dtype=torch.int32, device=dev)
-    sorted_ids = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
-    block_expert = torch.empty(max(cap // B, 1), dtype=torch.int32, device=dev)
-    num_padded = torch.zeros(4, dtype=torch.int32, device=dev)
+    counts = _alloc(num_experts, torch.int32, dev, s)
+    sorted_ids = _alloc(max(cap, 1), torch.int32, dev, s)
+    block_expert = _alloc(max(cap // B, 1), torch.int32, dev, s)
+    num_padded = _alloc((4,), torch.int32, dev, s)
     _check("moe_align", lib().moe_align(ctypes.byref(desc), _ptr(topk_ids), int(k), _ptr(counts),
                                         _ptr(sorted_ids), _ptr(block_expert), _ptr(num_padded),
-                                        _stream(dev, stream)))
+                                        ctypes.c_void_p(s.cuda_stream)))
     return counts, sorted_ids[:cap], block_expert[:cap // B], num_padded[:1], B
 
 
@@ -399,23 +450,24 @@ def moe_route_align(x: torch.Tensor, w_gate: torch.Tensor, top_k: int, *, interm
     moe_align with the same descriptor (pass the layer's intermediate size
     and weight dtype to get the block size moe_forward uses)."""
     dev = _dev(x, w_gate)
+    s = _launch_stream(dev, stream)
     T, d = x.shape
     E = w_gate.shape[0]
     if w_gate.dtype != torch.float32 or w_gate.shape[1] != d:
         raise ValueError("w_gate must be float32 [E, d]")
     desc = make_desc(T, d, E, intermediate, _act_code(x), weight_dtype, block_m)
     B, cap = moe_align_capacity(desc, top_k)
-    logits = torch.empty((T, E), dtype=torch.float32, device=dev)
-    ids = torch.empty((T, top_k), dtype=torch.int32, device=dev)
-    w = torch.empty((T, top_k), dtype=torch.float32, device=dev)
-    counts = torch.empty(E, dtype=torch.int32, device=dev)
-    sorted_ids = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
-    block_expert = torch.empty(max(cap // B, 1), dtype=torch.int32, device=dev)
-    num_padded = torch.zeros(4, dtype=torch.int32, device=dev)
+    logits = _alloc((T, E), torch.float32, dev, s)
+    ids = _alloc((T, top_k), torch.int32, dev, s)
+    w = _alloc((T, top_k), torch.float32, dev, s)
+    counts = _alloc(E, torch.int32, dev, s)
+    sorted_ids = _alloc(max(cap, 1), torch.int32, dev, s)
+    block_expert = _alloc(max(cap // B, 1), torch.int32, dev, s)
+    num_padded = _alloc((4,), torch.int32, dev, s)
     _check("moe_route_align", lib().moe_route_align(
         ctypes.byref(desc), _ptr(x), _ptr(w_gate), int(top_k), _ptr(logits), _ptr(ids), _ptr(w),
         _ptr(counts), _ptr(sorted_ids), _ptr(block_expert), _ptr(num_padded),
-        _stream(dev, stream)))
+        ctypes.c_void_p(s.cuda_stream)))
     return logits, ids, w, counts, sorted_ids[:cap], block_expert[:cap // B], num_padded[:1], B
 
 
@@ -430,18 +482,23 @@ class MoeGraph:
                  workspace: Optional[torch.Tensor] = None, act_quant: Optional[str] = None,
                  schedule: str = "auto"):
         self._h = None
-        dev = _dev(x, w_gate, w13, w2, out)
         T, d, E, I = _shapes(x, w_gate, w13, w2)
+        if out is not None:
+            _check_out(out, x)
+        dev = _dev(x, w_gate, w13, w2, out)
         desc = make_desc(T, d, E, I, _act_code(x), _w_code(w13), block_m, act_quant, schedule)
         self._sc = _scales(w13, scales)
-        if out is None:
-            out = torch.empty((T, d), dtype=x.dtype, device=dev)
-        elif out.shape != x.shape or out.dtype != x.dtype:
-            raise ValueError("out must match x in shape and dtype")
+        s = torch.cuda.current_stream(dev)
+        own_out = out is None
+        if own_out:
+            out = _alloc((T, d), x.dtype, dev, s)
         nbytes = moe_workspace_bytes(desc, top_k, True)
-        ws = _workspace(nbytes, dev, workspace)
+        ws = _workspace(nbytes, dev, workspace, s)
         # the graph keeps these addresses: keep the tensors alive with it
         self._keep = (x, w_gate, w13, w2, tuple(scales) if scales is not None else None, ws)
+        # tensors allocated here, which a replay on another stream must keep
+        # from being reused before it has run
+        self._owned = ([ws] if workspace is None else []) + ([out] if own_out else [])
         self.x, self.out, self.device = x, out, dev
         h = ctypes.c_void_p()
         _check("moe_graph_create", lib().moe_graph_create(
@@ -453,7 +510,11 @@ class MoeGraph:
     def launch(self, stream=None) -> torch.Tensor:
         if self._h is None:
             raise RuntimeError("graph already destroyed")
-        _check("moe_graph_launch", lib().moe_graph_launch(self._h, _stream(self.device, stream)))
+        s = _launch_stream(self.device, stream)
+        _check("moe_graph_launch", lib().moe_graph_launch(self._h, ctypes.c_void_p(s.cuda_stream)))
+        if s != torch.cuda.current_stream(self.device):
+            for t in self._owned:
+                t.record_stream(s)
         return self.out
 
     def close(self) -> None:
@@ -476,21 +537,23 @@ def moe_expert_ffn(x: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, top_k: 
                    act_quant: Optional[str] = None, schedule: str = "auto") -> torch.Tensor:
     """Expert networks + combine for a given routing (layout from moe_align
     with the same block_m and act_quant)."""
-    dev = _dev(x, w13, w2, topk_w, sorted_ids, block_expert, num_padded, out)
     T, d, E, I = _shapes(x, None, w13, w2)
+    if out is not None:
+        _check_out(out, x)
     desc = make_desc(T, d, E, I, _act_code(x), _w_code(w13), block_m, act_quant, schedule)
     B, cap = moe_align_capacity(desc, top_k)
-    if sorted_ids.numel() < cap or block_expert.numel() < cap // B:
-        raise ValueError("sorted_ids / block_expert smaller than the layout capacity")
+    _check_routing(T, int(top_k), topk_w, sorted_ids, block_expert, num_padded, cap, B)
+    dev = _dev(x, w13, w2, topk_w, sorted_ids, block_expert, num_padded, out)
     sc = _scales(w13, scales)
+    s = _launch_stream(dev, stream)
     if out is None:
-        out = torch.empty((T, d), dtype=x.dtype, device=dev)
+        out = _alloc((T, d), x.dtype, dev, s)
     nbytes = moe_workspace_bytes(desc, top_k, False)
-    ws = _workspace(nbytes, dev, workspace)
+    ws = _workspace(nbytes, dev, workspace, s)
     st = lib().moe_expert_ffn(ctypes.byref(desc), _ptr(x), _ptr(w13), _ptr(w2), int(top_k),
                               ctypes.byref(sc) if sc is not None else None, _ptr(topk_w),
                               _ptr(sorted_ids), _ptr(block_expert), _ptr(num_padded), _ptr(out),
-                              _ptr(ws), nbytes, _stream(dev, stream))
+                              _ptr(ws), nbytes, ctypes.c_void_p(s.cuda_stream))
     _check("moe_expert_ffn", st)
     return out
 

@@ -58,7 +58,10 @@ struct DmaGeom {
   static constexpr int kLoads = kLoadsW + kLoadsA;
 };
 
-// s_waitcnt immediate: at most n vector-memory loads outstanding.
+// s_waitcnt immediate: at most n vector-memory loads outstanding.  The
+// vmcnt field is 6 bits (0..63); callers static_assert that n fits, since a
+// larger count would silently encode a smaller wait.
+constexpr int kDmaMaxVmcnt = 63;
 constexpr int dma_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 // Per-lane operand sources.
@@ -160,6 +163,9 @@ struct DmaRing {
   }
 
   // chunk c in buffer p, issuing chunk c+P-1
+  static_assert(kL * (P - 2) <= kDmaMaxVmcnt,
+                "loads per stage x (ring depth - 2) exceed the 6-bit vmcnt field");
+
   template <int p>
   __device__ __forceinline__ void step(int c, uint4 (&a)[P][NS][kF], f32x4 (&acc)[NS][NROW]) const {
     constexpr int pn = (p + P - 1) % P;
@@ -170,6 +176,7 @@ struct DmaRing {
   // chunk in buffer p with W stages issued after it, issuing nothing
   template <int p, int W>
   __device__ __forceinline__ void last(uint4 (&a)[P][NS][kF], f32x4 (&acc)[NS][NROW]) const {
+    static_assert(kL * W <= kDmaMaxVmcnt, "wait count exceeds the 6-bit vmcnt field");
     __builtin_amdgcn_s_waitcnt(dma_vmcnt(kL * W));
     op.template mma<NSL>(ring[p], a[p], acc);
   }

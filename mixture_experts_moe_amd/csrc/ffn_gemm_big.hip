@@ -84,6 +84,7 @@ template <bool kIssue, int kWait, bool kLive>
 __device__ __forceinline__ void big_half(const BigLoader& ld, const uint8_t* cur, uint8_t* nxt,
                                          int knext, int wave, int arow0, int arow_up, int brow0,
                                          BigFrags& f1, BigAcc& acc) {
+  static_assert(kWait >= 0 && kWait <= 63, "wait count exceeds the 6-bit vmcnt field");
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(kWait));
   big_barrier();
   const uint8_t* opb = cur + kBigOperandBytes;

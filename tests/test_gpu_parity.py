@@ -369,6 +369,31 @@ def test_decode_bf16_full_size(decode_inputs, T):
     _full_case(inp, tokens)
 
 
+def test_forward_on_a_side_stream_keeps_its_workspace(decode_inputs):
+    """moe_forward on a non-current stream: the workspace (and out) the
+    binding allocates belong to that stream, so allocations on the current
+    stream made right after the call, while the side stream's kernels still
+    run, cannot be handed the same memory.  Bit-equal to the current-stream
+    result."""
+    inp = with_x(decode_inputs, synth.make_x(8, decode_inputs.d, "bf16", 0.02, 0, DEV))
+    ref = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k)
+    torch.cuda.synchronize()
+    desc = B.make_desc(inp.T, inp.d, inp.E, inp.I, B.MOE_DTYPE_BF16, B.MOE_DTYPE_BF16)
+    nbytes = B.moe_workspace_bytes(desc, inp.top_k, True)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs, junk = [], []
+    for _ in range(4):
+        outs.append(B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, stream=side))
+        # same-size allocations and writes on the current stream at once
+        junk.append(torch.full((nbytes,), 0x7F, dtype=torch.uint8, device=DEV))
+        junk.append(torch.full((inp.T, inp.d), 3.0, dtype=torch.bfloat16, device=DEV))
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o, ref)
+
+
 def test_decode_shape_from_the_pages(decode_inputs):
     """One token through a 4096 x 8192 expert block (2I = 8192): the decode
     product printed on the French summary page (tests/golden/decode_shape.json)."""
