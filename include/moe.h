@@ -83,6 +83,8 @@ extern "C" {
 #define MOE_ERR_HIP (-7)           /* a HIP call or kernel launch failed    */
 #define MOE_ERR_BAD_BLOCK_M (-8)   /* block_m not allowed for the desc      */
 #define MOE_ERR_BAD_ARG (-9)       /* any other invalid argument            */
+#define MOE_ERR_NOALLOC_SIZE (-10) /* moe_forward_noalloc: workspace needed  */
+                                   /* exceeds MOE_NOALLOC_WORKSPACE_BYTES    */
 
 /* ---- dtypes and scale modes ---- */
 #define MOE_DTYPE_F32 0
@@ -170,6 +172,33 @@ MOE_API int moe_forward(const moe_desc* desc, const void* x, const float* w_gate
                         const void* w13, const void* w2, int top_k,
                         const moe_scales* scales, void* out, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/* moe_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same layer, checks and results, bit for bit, with no workspace
+ * argument.  Its workspace is a static device array of
+ * MOE_NOALLOC_WORKSPACE_BYTES bytes inside the library, one per GPU, which
+ * exists from the library's load until the process ends; the call allocates
+ * and frees nothing (no hipMalloc, no allocating library routine).
+ *   - Size limit: returns MOE_ERR_NOALLOC_SIZE, enqueuing nothing, when
+ *     moe_workspace_bytes(desc, top_k, 1) exceeds the array (it holds every
+ *     decode batch up to 64 tokens at d = 4096, I = 14336, E = 8, top-2, and
+ *     64 tokens at d = 7168, I = 2048, E = 256, top-8; larger batches need
+ *     moe_forward and a caller workspace).
+ *   - Sharing: every call on one GPU uses that GPU's one array, which keeps
+ *     whatever the last call left in it (nothing reads it before writing).
+ *     Calls ordered on one stream are safe; calls that may overlap on one
+ *     GPU (different streams, or threads without ordering) race on the
+ *     array and give wrong results.
+ *   - The device is the stream's (the current device for the null stream);
+ *     the first call on a device looks up the array's address there (a HIP
+ *     call, MOE_ERR_HIP if it fails).
+ * Other arguments, ownership and errors as moe_forward; asynchronous on
+ * `stream`. */
+#define MOE_NOALLOC_WORKSPACE_BYTES (64u << 20)
+MOE_API int moe_forward_noalloc(const moe_desc* desc, const void* x, const float* w_gate,
+                                const void* w13, const void* w2, int top_k,
+                                const moe_scales* scales, void* out, void* stream);
 
 /* ---- stage entry points (the same kernels moe_forward runs) ---- */
 

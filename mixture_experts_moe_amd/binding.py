@@ -39,8 +39,10 @@ ENTRY_POINTS = (
     "moe_align_capacity", "moe_workspace_bytes", "moe_forward", "moe_route",
     "moe_route_logits", "moe_align", "moe_route_align", "moe_expert_ffn",
     "moe_quantize_act", "moe_graph_create", "moe_graph_launch", "moe_graph_destroy", "moe_strerror",
-    "moe_timing_enable", "moe_timing_collect", "moe_kernel_name",
+    "moe_timing_enable", "moe_timing_collect", "moe_kernel_name", "moe_forward_noalloc",
 )
+MOE_ERR_NOALLOC_SIZE = -10
+MOE_NOALLOC_WORKSPACE_BYTES = 64 << 20
 
 
 class moe_desc(ctypes.Structure):
@@ -80,6 +82,7 @@ def lib() -> ctypes.CDLL:
         "moe_align_capacity": (I32, [D, I32, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(I64)]),
         "moe_workspace_bytes": (I32, [D, I32, I32, ctypes.POINTER(SZ)]),
         "moe_forward": (I32, [D, P, P, P, P, I32, S, P, P, SZ, P]),
+        "moe_forward_noalloc": (I32, [D, P, P, P, P, I32, S, P, P]),
         "moe_route": (I32, [D, P, P, I32, P, P, P, P]),
         "moe_route_logits": (I32, [D, P, I32, P, P, P]),
         "moe_align": (I32, [D, P, I32, P, P, P, P, P]),
@@ -366,6 +369,30 @@ def moe_forward(x: torch.Tensor, w_gate: torch.Tensor, w13: torch.Tensor, w2: to
                            int(top_k), ctypes.byref(sc) if sc is not None else None, _ptr(out),
                            _ptr(ws), nbytes, ctypes.c_void_p(s.cuda_stream))
     _check("moe_forward", st)
+    return out
+
+
+def moe_forward_noalloc(x: torch.Tensor, w_gate: torch.Tensor, w13: torch.Tensor,
+                        w2: torch.Tensor, top_k: int, out: torch.Tensor,
+                        scales: Optional[Sequence[torch.Tensor]] = None, *, block_m: int = 0,
+                        stream=None, act_quant: Optional[str] = None,
+                        schedule: str = "auto") -> torch.Tensor:
+    """moe_forward into the caller's `out` with the library's static
+    workspace (the C entry point allocates nothing; nor does this wrapper).
+    Raises MoEError (status MOE_ERR_NOALLOC_SIZE) when the layer needs more
+    than MOE_NOALLOC_WORKSPACE_BYTES of workspace.  Calls that may overlap on
+    one GPU share that workspace and race."""
+    T, d, E, I = _shapes(x, w_gate, w13, w2)
+    _check_out(out, x)
+    dev = _dev(x, w_gate, w13, w2, out)
+    desc = make_desc(T, d, E, I, _act_code(x), _w_code(w13), block_m, act_quant, schedule)
+    sc = _scales(w13, scales)
+    s = _launch_stream(dev, stream)
+    st = lib().moe_forward_noalloc(ctypes.byref(desc), _ptr(x), _ptr(w_gate), _ptr(w13),
+                                   _ptr(w2), int(top_k),
+                                   ctypes.byref(sc) if sc is not None else None, _ptr(out),
+                                   ctypes.c_void_p(s.cuda_stream))
+    _check("moe_forward_noalloc", st)
     return out
 
 

@@ -10,6 +10,15 @@
 #include "kernels.h"
 #include "moe.h"
 
+// Workspace of moe_forward_noalloc: one array per GPU, in the code object's
+// zero-initialised device data, held from module load until the process
+// ends.  In host code `scratch` only names the symbol: its device address
+// comes from hipGetSymbolAddress, once per device (scratch_address below).
+// No `used` attribute: it would keep the device symbol's binding local,
+// where the runtime's lookup by name does not find it; referenced from host
+// code, the compiler gives it global binding by itself.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_WORKSPACE_BYTES];
+
 namespace {
 
 using moe::FfnArgs;
@@ -358,6 +367,7 @@ MOE_API const char* moe_strerror(int status) {
     case MOE_ERR_HIP: return "a HIP call or kernel launch failed";
     case MOE_ERR_BAD_BLOCK_M: return "block_m must be 0, 16, 32, 64, 128 or 256 (256: bf16 weights, d % 256 == 0, I % 128 == 0, 4*I*d and 2*T*d under 2^31)";
     case MOE_ERR_BAD_ARG: return "invalid argument (reserved fields must be 0)";
+    case MOE_ERR_NOALLOC_SIZE: return "the layer needs more workspace than moe_forward_noalloc's static array (MOE_NOALLOC_WORKSPACE_BYTES, 64 MiB); call moe_forward with a caller workspace";
   }
   return "unknown status";
 }
@@ -577,6 +587,36 @@ static int enqueue_forward(const Plan& p, const void* x, const float* w_gate, co
   return to_status(run_ffn(a, s));
 }
 
+// Device address of `scratch` on the device that runs `stream` (the current
+// device for the null stream), fetched with that device current on the first
+// call for it and kept per device.
+constexpr int kMaxScratchDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_addr[kMaxScratchDevices] = {};
+
+static int scratch_address(hipStream_t stream, void** addr) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return MOE_ERR_HIP;
+  int dev = cur;
+  if (stream) {
+    hipDevice_t sd;
+    if (hipStreamGetDevice(stream, &sd) != hipSuccess) return MOE_ERR_HIP;
+    dev = static_cast<int>(sd);
+  }
+  if (dev < 0 || dev >= kMaxScratchDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return MOE_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return MOE_ERR_HIP;
+    if (e != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch_addr[dev] = p;
+  }
+  *addr = g_scratch_addr[dev];
+  return MOE_OK;
+}
+
 MOE_API int moe_forward(const moe_desc* desc, const void* x, const float* w_gate,
                         const void* w13, const void* w2, int top_k, const moe_scales* scales,
                         void* out, void* workspace, size_t workspace_bytes, void* stream) {
@@ -586,6 +626,25 @@ MOE_API int moe_forward(const moe_desc* desc, const void* x, const float* w_gate
   if (st || desc->num_tokens == 0) return st;
   return enqueue_forward(p, x, w_gate, w13, w2, scales, out, static_cast<char*>(workspace),
                          static_cast<hipStream_t>(stream));
+}
+
+MOE_API int moe_forward_noalloc(const moe_desc* desc, const void* x, const float* w_gate,
+                                const void* w13, const void* w2, int top_k,
+                                const moe_scales* scales, void* out, void* stream) {
+  int st = check_desc(desc, top_k);
+  if (st) return st;
+  if (desc->num_tokens == 0) return MOE_OK;
+  if ((st = check_scales(desc, scales))) return st;
+  if ((st = check_ptrs({x, w_gate, w13, w2, out}))) return st;
+  Plan p;
+  make_plan(desc, top_k, true, &p);
+  if (p.total > static_cast<size_t>(MOE_NOALLOC_WORKSPACE_BYTES)) return MOE_ERR_NOALLOC_SIZE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if ((st = scratch_address(s, &ws))) return st;
+  // every region the layer reads is written earlier in the same call (the
+  // align launch clears the queue counters), as with a caller workspace
+  return enqueue_forward(p, x, w_gate, w13, w2, scales, out, static_cast<char*>(ws), s);
 }
 
 }  // extern "C"

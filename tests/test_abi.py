@@ -299,3 +299,27 @@ def test_timing_collect_without_work(lib):
     t = B.moe_timing_collect(reset=True)
     assert all(v == (0.0, 0) for v in t.values())
     B.moe_timing_enable(False)
+
+
+def test_noalloc_forward_rejects_before_any_hip_call(lib):
+    """moe_forward_noalloc checks its arguments and the size of its static
+    workspace on the host before its first HIP call (the device lookup of
+    that array), so these return without a GPU."""
+    def call(dsc, k=2, x=FAKE, wg=FAKE, w13=FAKE, w2=FAKE, out=FAKE, scales=None):
+        return lib.moe_forward_noalloc(ctypes.byref(dsc), x, wg, w13, w2, k,
+                                       ctypes.byref(scales) if scales is not None else None,
+                                       out, None)
+    d = desc()
+    assert call(d, x=None) == -1
+    assert call(d, out=None) == -1
+    assert call(d, w2=FAKE + 8) == -5
+    assert call(d, k=9) == -3
+    assert call(desc(w=B.MOE_DTYPE_E4M3FN)) == -1                  # fp8 needs scales
+    assert call(desc(T=0), x=None, wg=None, w13=None, w2=None, out=None) == 0
+    # a layer whose workspace exceeds the array: the size error, before any HIP call
+    big = desc(T=20000, d=512, I=512)
+    n = ctypes.c_size_t()
+    assert lib.moe_workspace_bytes(ctypes.byref(big), 2, 1, ctypes.byref(n)) == 0
+    assert n.value > B.MOE_NOALLOC_WORKSPACE_BYTES
+    assert call(big) == B.MOE_ERR_NOALLOC_SIZE == -10
+    assert "static" in B.strerror(-10)
