@@ -49,6 +49,17 @@ MOE_BENCH_API int moe_bench_mfma_bf16(int iters, int reps, double* tflops, void*
  * workgroup.  TFLOP/s to *tflops.  Allocates nothing. */
 MOE_BENCH_API int moe_bench_mfma_fp8(int iters, int reps, double* tflops, void* stream);
 
+/* Numerics probe of the scaled fp8 matrix-core instruction the W8A8 tile
+ * uses (v_mfma_scale_f32_16x16x128_f8f6f4, unit block scales): for each of
+ * `n` trials, c[t] + sum_k A[t,k] * B[t,k] as the instruction computes
+ * it, A and B [n, 128] e4m3fn codes (device buffers, 16-byte aligned), c
+ * [n] fp32; out [n, 256] fp32 (16-byte aligned) receives all 256 outputs of
+ * the trial's 16 x 16 tile, which all hold that one dot product.  Lets a test pin how the
+ * instruction accumulates (the parity bounds of the W8A8 mode rest on it).
+ * Synchronises `stream` before returning.  Allocates nothing. */
+MOE_BENCH_API int moe_bench_fp8_dot(const void* a, const void* b, const float* c, float* out,
+                                    int n, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

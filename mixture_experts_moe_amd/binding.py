@@ -107,7 +107,8 @@ def lib() -> ctypes.CDLL:
 
 # ------------------------------------------------------------ attainable-rate probes
 
-BENCH_ENTRY_POINTS = ("moe_bench_hbm_read", "moe_bench_mfma_bf16", "moe_bench_mfma_fp8")
+BENCH_ENTRY_POINTS = ("moe_bench_hbm_read", "moe_bench_mfma_bf16", "moe_bench_mfma_fp8",
+                      "moe_bench_fp8_dot")
 _BENCH_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_bench.so")
 _bench_lib = None
 
@@ -127,6 +128,8 @@ def bench_lib() -> ctypes.CDLL:
     L.moe_bench_mfma_bf16.argtypes = [I32, I32, D, P]
     L.moe_bench_mfma_fp8.restype = I32
     L.moe_bench_mfma_fp8.argtypes = [I32, I32, D, P]
+    L.moe_bench_fp8_dot.restype = I32
+    L.moe_bench_fp8_dot.argtypes = [P, P, P, P, I32, P]
     _bench_lib = L
     return L
 
@@ -158,6 +161,23 @@ def bench_mfma_fp8(iters: int = 4096, reps: int = 4, device="cuda", stream=None)
     _check("moe_bench_mfma_fp8", bench_lib().moe_bench_mfma_fp8(
         int(iters), int(reps), ctypes.byref(r), _stream(dev, stream)))
     return r.value
+
+
+def bench_fp8_dot(a: torch.Tensor, b: torch.Tensor, c: torch.Tensor, stream=None) -> torch.Tensor:
+    """c[t] + A[t] . B[t] for e4m3fn code rows a, b [n, 128] (uint8) and
+    fp32 c [n], as the scaled fp8 MFMA computes it (unit block scales)."""
+    dev = _dev(a, b, c)
+    if a.dtype != torch.uint8 or b.dtype != torch.uint8 or c.dtype != torch.float32:
+        raise TypeError("a, b must be uint8 codes and c float32")
+    n = a.shape[0]
+    if tuple(a.shape) != (n, 128) or tuple(b.shape) != (n, 128) or tuple(c.shape) != (n,):
+        raise ValueError("a, b must be [n, 128] and c [n]")
+    out = torch.empty((n, 256), dtype=torch.float32, device=dev)
+    _check("moe_bench_fp8_dot", bench_lib().moe_bench_fp8_dot(
+        _ptr(a), _ptr(b), _ptr(c), _ptr(out), int(n), _stream(dev, stream)))
+    if not bool((out == out[:, :1]).all()):
+        raise RuntimeError("moe_bench_fp8_dot: the tile's 256 outputs differ")
+    return out[:, 0].contiguous()
 
 
 def strerror(status: int) -> str:

@@ -184,9 +184,54 @@ int best_ms(hipStream_t s, int reps, F&& launch, float* best) {
   return st;
 }
 
+// ------------------------------------------------------------ fp8 dot probe
+// One wave per trial: the trial's 128-byte A row and B column (e4m3fn codes,
+// K in byte order) are given to every row and column of one
+// v_mfma_scale_f32_16x16x128_f8f6f4 with unit block scales and accumulator
+// input c[t], so all 256 outputs are the same dot product.  Lane l supplies
+// K bytes 16(l/16)..+15 and 64 + 16(l/16)..+15 of both operands; every load
+// lies inside the trial's 128 bytes.  Every lane stores its four outputs
+// (out[t, 4l .. 4l + 3]): with a store by lane 0 alone the compiler moved the
+// MFMA under that lane's branch, where it ran with one lane enabled.
+__global__ __launch_bounds__(64) void fp8_dot_kernel(const uint8_t* __restrict__ a,
+                                                     const uint8_t* __restrict__ b,
+                                                     const float* __restrict__ c,
+                                                     float* __restrict__ out, int n) {
+  const int t = blockIdx.x;
+  if (t >= n) return;
+  const int kg = threadIdx.x / 16;
+  const uint8_t* ar = a + static_cast<size_t>(t) * 128;
+  const uint8_t* br = b + static_cast<size_t>(t) * 128;
+  i32x8 av, bv;
+  for (int i = 0; i < 4; ++i) {
+    av[i] = *reinterpret_cast<const int*>(ar + 16 * kg + 4 * i);
+    av[4 + i] = *reinterpret_cast<const int*>(ar + 64 + 16 * kg + 4 * i);
+    bv[i] = *reinterpret_cast<const int*>(br + 16 * kg + 4 * i);
+    bv[4 + i] = *reinterpret_cast<const int*>(br + 64 + 16 * kg + 4 * i);
+  }
+  const float c0 = c[t];
+  f32x4 acc = {c0, c0, c0, c0};
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 0, 0, 0, 127, 0, 127);
+  float4* o = reinterpret_cast<float4*>(out + static_cast<size_t>(t) * 256) + threadIdx.x;
+  *o = float4{acc[0], acc[1], acc[2], acc[3]};
+}
+
 }  // namespace
 
 extern "C" {
+
+MOE_BENCH_API int moe_bench_fp8_dot(const void* a, const void* b, const float* c, float* out,
+                                    int n, void* stream) {
+  if (!a || !b || !c || !out) return MOE_ERR_NULL_PTR;
+  if (n < 1 || reinterpret_cast<uintptr_t>(a) % 16 || reinterpret_cast<uintptr_t>(b) % 16 ||
+      reinterpret_cast<uintptr_t>(out) % 16)
+    return MOE_ERR_BAD_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  fp8_dot_kernel<<<n, 64, 0, s>>>(static_cast<const uint8_t*>(a), static_cast<const uint8_t*>(b),
+                                  c, out, n);
+  if (hipGetLastError() != hipSuccess || hipStreamSynchronize(s) != hipSuccess) return MOE_ERR_HIP;
+  return MOE_OK;
+}
 
 MOE_BENCH_API int moe_bench_hbm_read(const void* buf, size_t bytes, int reps, double* gbps,
                                      void* stream) {

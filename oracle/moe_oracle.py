@@ -351,22 +351,26 @@ def silu(z: np.ndarray) -> np.ndarray:
         return z / (1.0 + np.exp(-z))
 
 
-def expert_ffn(xrows: np.ndarray, w13: np.ndarray, w2: np.ndarray, h_quant=None) -> np.ndarray:
+def expert_ffn(xrows: np.ndarray, w13: np.ndarray, w2: np.ndarray, h_quant=None,
+               parts: dict | None = None) -> np.ndarray:
     """One expert's SwiGLU network on a batch of rows.
 
     xrows [n, d]; w13 [2I, d] with rows 0..I-1 the gate projection W1 and rows
     I..2I-1 the up projection W3; w2 [d, I].  Returns [n, d]:
     W2 . (SiLU(W1 x) * (W3 x)) for every row x.  `h_quant`, when given, maps
     the rows of SiLU(W1 x) * (W3 x) to the values W2 sees (the W8A8 mode's
-    quantise-dequantise step).
+    quantise-dequantise step).  `parts`, when given, receives the
+    intermediates: "g" = W1 x, "u" = W3 x, "h" = SiLU(g) * u and "h_used"
+    (what W2 multiplies: h, or its quantised values), each [n, I].
     """
     I = w13.shape[0] // 2
     g = xrows @ w13[:I].T
     u = xrows @ w13[I:].T
     h = silu(g) * u
-    if h_quant is not None:
-        h = h_quant(h)
-    return h @ w2.T
+    hq = h_quant(h) if h_quant is not None else h
+    if parts is not None:
+        parts.update(g=g, u=u, h=h, h_used=hq)
+    return hq @ w2.T
 
 
 # --------------------------------------------------------------------------
@@ -375,7 +379,8 @@ def expert_ffn(xrows: np.ndarray, w13: np.ndarray, w2: np.ndarray, h_quant=None)
 
 def moe_forward(x, w_gate, w13, w2, top_k: int, *, act_fmt: str = "bf16",
                 w_fmt: str = "bf16", s13=None, s2=None, scale_mode: str | None = None,
-                block_m: int = 64, logits=None, act_quant: str | None = None) -> dict:
+                block_m: int = 64, logits=None, act_quant: str | None = None,
+                expert_hook=None, workers: int = 1) -> dict:
     """The MoE layer computed as a plain loop over experts.
 
     x: [T, d] raw activations (uint16 bf16 patterns or float32);
@@ -388,7 +393,17 @@ def moe_forward(x, w_gate, w13, w2, top_k: int, *, act_fmt: str = "bf16",
       (used to compare routing given identical logits);
     act_quant: None (activations as given) or "mx_e4m3" (the W8A8 mode: the
       router still sees x as given; the experts see x quantised per token
-      and h quantised per routing slot by mx_quantize, then dequantised).
+      and h quantised per routing slot by mx_quantize, then dequantised);
+    expert_hook: optional callable, called once per expert that receives
+      slots, after its network has run, with a dict of what the loop has at
+      hand: "e", "slots" (flat slot ids f, ascending), "x" (the rows the
+      expert saw [n, d]), "w13" [2I, d] and "w2" [d, I] (decoded fp64
+      values), "gates" [n], and the intermediates of expert_ffn ("g", "u",
+      "h", "h_used", [n, I]).  It observes only: nothing it returns is used.
+    workers: experts are independent, so with workers > 1 their networks
+      run in a pool of that many threads (each writes only its own slots'
+      rows; the hook may then be called from several threads at once).  The
+      arithmetic of each expert is the same either way.
 
     Steps: (1) logits, (2) top-k selection and gates, (3) regrouping by expert,
     (4) for each expert, gather its tokens, run its SwiGLU network and scale
@@ -427,10 +442,9 @@ def moe_forward(x, w_gate, w13, w2, top_k: int, *, act_fmt: str = "bf16",
         raise ValueError(f"unknown act_quant {act_quant!r}")
     xe = _mx_roundtrip(xv) if (act_quant and T) else xv   # what the experts see
     hq = _mx_roundtrip if act_quant else None
-    for e in range(E):
+
+    def run_expert(e: int) -> None:
         n = int(al["counts"][e])
-        if n == 0:
-            continue
         start = int(al["offsets"][e])
         fs = al["sorted_ids"][start:start + n].astype(np.int64)
         ts = fs // k
@@ -443,8 +457,22 @@ def moe_forward(x, w_gate, w13, w2, top_k: int, *, act_fmt: str = "bf16",
         W2e = decode_weights(w2[e], w_fmt, sc2)
         if W13e.shape[1] != d or W2e.shape[0] != d or W13e.shape[0] != 2 * W2e.shape[1]:
             raise ValueError("weight shapes do not match x / each other")
-        Y = expert_ffn(xe[ts], W13e, W2e, hq)
+        parts = {} if expert_hook is not None else None
+        Y = expert_ffn(xe[ts], W13e, W2e, hq, parts)
         y_slot[fs] = flat_gates[fs][:, None] * Y
+        if expert_hook is not None:
+            expert_hook(dict(e=e, slots=fs, x=xe[ts], w13=W13e, w2=W2e,
+                             gates=flat_gates[fs], **parts))
+
+    live = [e for e in range(E) if int(al["counts"][e]) > 0]
+    if workers > 1 and len(live) > 1:
+        import concurrent.futures
+        with concurrent.futures.ThreadPoolExecutor(max_workers=int(workers)) as pool:
+            for _ in pool.map(run_expert, live):
+                pass
+    else:
+        for e in live:
+            run_expert(e)
 
     out = np.zeros((T, d), dtype=np.float64)
     ys = y_slot.reshape(T, k, d)

@@ -281,10 +281,14 @@ def test_bench_library_exports_and_validates():
     assert L.moe_bench_mfma_fp8(100, 3, None, None) == -1
     assert L.moe_bench_mfma_fp8(1, 3, ctypes.byref(r), None) == -9
     assert L.moe_bench_mfma_fp8(100, 1, ctypes.byref(r), None) == -9
+    assert L.moe_bench_fp8_dot(None, FAKE, FAKE, FAKE, 4, None) == -1
+    assert L.moe_bench_fp8_dot(FAKE, FAKE, FAKE, None, 4, None) == -1
+    assert L.moe_bench_fp8_dot(FAKE, FAKE, FAKE, FAKE, 0, None) == -9
+    assert L.moe_bench_fp8_dot(FAKE + 8, FAKE, FAKE, FAKE, 4, None) == -9
 
 
 def test_strerror_and_names(lib):
-    for code in range(0, -10, -1):
+    for code in range(0, -11, -1):
         s = B.strerror(code)
         assert s and s != "unknown status"
     assert B.strerror(-99) == "unknown status"

@@ -17,7 +17,7 @@ import torch
 import oracle
 from mixture_experts_moe_amd import binding as B
 from mixture_experts_moe_amd import synth
-from parity_utils import compare_layer, near_ties, subset, to_f64, with_x
+from parity_utils import compare_layer, covering_tokens, near_ties, subset, to_f64, with_x
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -185,7 +185,7 @@ def test_layer_small(name, over, T, bm):
     _, ids, _ = B.moe_route(inp.x, inp.w_gate, inp.top_k)
     torch.cuda.synchronize()
     r = compare_layer(inp, out, ids)
-    note(f"  rel_err={r['rel_err']:.3e} excluded={r['excluded']}")
+    _report(r)
 
 
 def test_zero_tokens_is_a_noop():
@@ -346,18 +346,46 @@ def _routing_exact(inp, ids, logits):
     assert np.array_equal(sorted_ids.cpu().numpy(), ref["sorted_ids"])
     assert np.array_equal(block_expert.cpu().numpy(), ref["block_expert"])
     assert int(num_padded.item()) == ref["num_padded"]
-    return ref
+    return ref, bm
 
 
-def _full_case(inp, tokens):
+def _report(r):
+    note(f"  rel_err={r['rel_err']:.3e} (derived global bound {r['derived_rel']:.2e}) "
+         f"worst element/bound {r['elem_ratio']:.2f} worst token/bound {r['token_ratio']:.2f} "
+         f"compared={r['compared']} excluded={r['excluded']}"
+         + (f" flippable h values {r['flips']} of {r['h_values']}" if r["h_values"] else ""))
+
+
+def _full_case(inp, tokens=None, out=None):
+    """Routing and regrouping over all tokens bit-exact given the GPU's
+    logits; the layer against the oracle on `tokens`, by default tokens that
+    hold the first and the last real slot of every row block of the layout
+    (every touched expert, every expert's ragged tail block)."""
     sc = (inp.s13, inp.s2) if inp.w == "e4m3fn" else None
-    out = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, sc,
-                        act_quant=inp.act_quant)
+    if out is None:
+        out = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, sc,
+                            act_quant=inp.act_quant)
     logits, ids, _ = B.moe_route(inp.x, inp.w_gate, inp.top_k)
     torch.cuda.synchronize()
-    _routing_exact(inp, ids, logits)
+    al, bm = _routing_exact(inp, ids, logits)
+    ids_np = ids.cpu().numpy()
+    if tokens is None:
+        tokens = covering_tokens(ids_np, inp.E, bm)
     r = compare_layer(inp, out, ids, tokens=tokens)
-    note(f"  rel_err={r['rel_err']:.3e} compared={r['compared']} excluded={r['excluded']}")
+    _report(r)
+    # every row block of the realised layout holds a slot of a compared token
+    A = inp.T * inp.top_k
+    kept = np.asarray(tokens)[~near_ties(logits.cpu().double().numpy()[np.asarray(tokens)],
+                                         inp.top_k)]
+    slots = set((int(t) * inp.top_k + j) for t in kept for j in range(inp.top_k))
+    srt = al["sorted_ids"]
+    nblocks = al["num_padded"] // bm
+    covered = sum(1 for b in range(nblocks)
+                  if any(int(f) in slots for f in srt[b * bm:(b + 1) * bm] if f < A))
+    note(f"  row blocks covered {covered} of {nblocks} (B={bm}), tokens {len(tokens)}")
+    if len(kept) == len(tokens):
+        assert covered == nblocks
+    return r
 
 
 @pytest.mark.parametrize("T", [1, 8, 32, 64])
@@ -365,8 +393,7 @@ def test_decode_bf16_full_size(decode_inputs, T):
     note(f"decode_bf16 full size T={T}")
     cfg = synth.WORKLOADS["decode_bf16"]
     inp = with_x(decode_inputs, synth.make_x(T, cfg["d"], "bf16", cfg["x_std"], 0, DEV))
-    tokens = np.arange(T) if T <= 8 else np.linspace(0, T - 1, 8).astype(int)
-    _full_case(inp, tokens)
+    _full_case(inp, np.arange(T) if T <= 16 else None)
 
 
 def test_forward_on_a_side_stream_keeps_its_workspace(decode_inputs):
@@ -407,33 +434,33 @@ def test_decode_shape_from_the_pages(decode_inputs):
 def test_prefill_bf16_full_size():
     note("prefill_bf16 full size T=4096")
     inp = synth.make_inputs("prefill_bf16", device=DEV)
-    _full_case(inp, np.linspace(0, inp.T - 1, 12).astype(int))
+    _full_case(inp)
 
 
 @pytest.mark.parametrize("T", [64, 2048])
 def test_fp8_full_size(T):
     note(f"fp8 full size T={T}")
     inp = synth.make_inputs("fp8", T=T, device=DEV)
-    _full_case(inp, np.linspace(0, T - 1, 4).astype(int))
+    _full_case(inp)
 
 
 def test_prefill_w8a8_full_size():
     note("prefill_w8a8 full size T=4096")
     inp = synth.make_inputs("prefill_w8a8", device=DEV)
-    _full_case(inp, np.linspace(0, inp.T - 1, 8).astype(int))
+    _full_case(inp)
 
 
 def test_fp8_shapes_w8a8_full_size():
     # the fine-grained FP8 shapes (d = 7168, E = 256, top-8) in the W8A8 mode
     note("fp8 shapes W8A8 T=2048")
     inp = synth.make_inputs("fp8", T=2048, device=DEV, act_quant="mx_e4m3")
-    _full_case(inp, np.linspace(0, inp.T - 1, 4).astype(int))
+    _full_case(inp)
 
 
 def test_skew_full_size():
     note("skew full size T=512")
     inp = synth.make_inputs("skew", device=DEV)
-    _full_case(inp, None)
+    _full_case(inp, np.arange(inp.T))
     _, ids, _ = B.moe_route(inp.x, inp.w_gate, inp.top_k)
     counts = np.bincount(ids.cpu().numpy().ravel(), minlength=inp.E)
     assert all(counts[e] == 0 for e in synth.SKEW_IDLE_EXPERTS)
@@ -504,6 +531,35 @@ def test_graph_replay_matches_eager(wl, T, over):
         torch.cuda.synchronize()
         assert torch.equal(out, ref2)
         assert not torch.equal(ref2, ref)
+    finally:
+        graph.close()
+
+
+@pytest.mark.parametrize("T", [1, 8, 64])
+def test_graph_replay_matches_oracle_at_decode_size(decode_inputs, T):
+    """The recorded forward (one graph launch) at the decode shape, replayed
+    three times with eager work in between and once more after new tokens
+    are written into the recorded x, each replay against the oracle."""
+    note(f"graph vs oracle decode_bf16 T={T}")
+    cfg = synth.WORKLOADS["decode_bf16"]
+    inp = with_x(decode_inputs, synth.make_x(T, cfg["d"], "bf16", cfg["x_std"], 0, DEV).clone())
+    out = torch.empty_like(inp.x)
+    graph = B.MoeGraph(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, out=out)
+    try:
+        for rep in range(3):
+            out.fill_(float("nan"))
+            graph.launch()
+            B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k)   # eager work between
+            torch.cuda.synchronize()
+            if rep == 0:
+                _full_case(inp, np.arange(T) if T <= 16 else None, out=out.clone())
+            else:
+                assert torch.equal(out, first)
+            first = out.clone() if rep == 0 else first
+        inp.x.copy_(synth.make_x(T, cfg["d"], "bf16", cfg["x_std"], 7, DEV))
+        graph.launch()
+        torch.cuda.synchronize()
+        _full_case(inp, np.arange(T) if T <= 16 else None, out=out.clone())
     finally:
         graph.close()
 
@@ -660,4 +716,4 @@ def test_layer_seeded_sweep(fmt, T, d, I, E, k, bm, smode):
     _, ids, _ = B.moe_route(inp.x, inp.w_gate, inp.top_k)
     torch.cuda.synchronize()
     r = compare_layer(inp, out, ids)
-    note(f"  rel_err={r['rel_err']:.3e} excluded={r['excluded']}")
+    _report(r)
