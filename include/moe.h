@@ -103,16 +103,25 @@ extern "C" {
 #define MOE_ACT_AS_IS 0
 #define MOE_ACT_MX_E4M3 1
 
-/* How the expert products with 128-token blocks (block_m 128) hand their
- * (row block, output-channel group) tiles to workgroups (Hungarian page,
+/* How the expert products hand their tiles to workgroups (Hungarian page,
  * section "FP8 esetén ...": dynamic scheduling layouts for token groups of
- * varying size).  MOE_SCHED_STATIC: one workgroup per possible tile, in an
- * XCD-aware raster; those of row blocks past the realised ones exit at once.
- * MOE_SCHED_QUEUE: as many workgroups as the GPU holds at once take only the
- * realised tiles, from one work queue per XCD, and help drain the other
- * queues when their own is empty.  MOE_SCHED_AUTO (0) is the queue.  Both
- * give bit-identical outputs; other block sizes have a single schedule and
- * ignore the field. */
+ * varying size; section "A fused MoE ...": one batched GPU operation).
+ * With 128-token blocks (block_m 128): MOE_SCHED_STATIC is one workgroup per
+ * possible (row block, output-channel group) tile, in an XCD-aware raster,
+ * those of row blocks past the realised ones exiting at once;
+ * MOE_SCHED_QUEUE is as many workgroups as the GPU holds at once taking only
+ * the realised tiles, from one work queue per XCD, helping drain the other
+ * queues when their own is empty.  In moe_forward with bf16 weights and
+ * activations on the decode path (blocks of 16 or 32 tokens, d and I
+ * multiples of 256, T <= 64): MOE_SCHED_STATIC runs W13, W2 and the combine
+ * as three launches; MOE_SCHED_QUEUE runs them as one persistent launch
+ * whose workgroups take W13 tiles, then W2 tiles (each once the W13 tiles it
+ * reads are done), from one ticket counter, and add up each token's slots as
+ * soon as its last partial lands.  MOE_SCHED_AUTO (0) is the queue for 128-token
+ * blocks and the three launches on the decode path, where the persistent
+ * kernel is slower (every W13 tile has to publish its rows at device scope
+ * before a W2 tile on another XCD may read them).  The two give
+ * bit-identical outputs; other paths ignore the field. */
 #define MOE_SCHED_AUTO 0
 #define MOE_SCHED_STATIC 1
 #define MOE_SCHED_QUEUE 2
@@ -330,7 +339,8 @@ MOE_API const char* moe_strerror(int status);
 #define MOE_KERNEL_FFN2 4
 #define MOE_KERNEL_COMBINE 5
 #define MOE_KERNEL_QUANT_X 6  /* W8A8 mode: x to block-scaled e4m3fn */
-#define MOE_KERNEL_COUNT 7
+#define MOE_KERNEL_FFN_FUSED 7  /* decode: W13, W2 and combine in one launch */
+#define MOE_KERNEL_COUNT 8
 
 MOE_API int moe_timing_enable(int kind_mask);  /* MOE_ERR_BAD_ARG if out of range */
 #define MOE_TIMING_ALL ((1 << MOE_KERNEL_COUNT) - 1)

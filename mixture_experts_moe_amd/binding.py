@@ -33,7 +33,7 @@ MOE_ACT_MX_E4M3 = 1
 MOE_SCHED_AUTO = 0
 MOE_SCHED_STATIC = 1
 MOE_SCHED_QUEUE = 2
-MOE_KERNEL_COUNT = 7
+MOE_KERNEL_COUNT = 8
 
 ENTRY_POINTS = (
     "moe_align_capacity", "moe_workspace_bytes", "moe_forward", "moe_route",
@@ -606,7 +606,8 @@ def moe_expert_ffn(x: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, top_k: 
 
 
 MOE_TIMING_ALL = (1 << MOE_KERNEL_COUNT) - 1
-KERNEL_KINDS = {"route_logits": 0, "route_topk": 1, "align": 2, "ffn13": 3, "ffn2": 4, "combine": 5}
+KERNEL_KINDS = {"route_logits": 0, "route_topk": 1, "align": 2, "ffn13": 3, "ffn2": 4, "combine": 5,
+                "quant_x": 6, "ffn_fused": 7}
 
 
 def moe_timing_enable(kinds=True) -> None:

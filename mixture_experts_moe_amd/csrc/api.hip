@@ -106,6 +106,9 @@ struct Plan {
   size_t logits, ids, gates, counts, num_padded, sorted, block_exp, h, y, xq, sx, sh, qcnt, total;
   size_t rpart;  // the split router's partial tiles (layer path, few tokens), or 0
   bool rsplit;
+  bool fused;    // W13, W2 and combine as one persistent launch (layer path, decode)
+  size_t fcnt;   // its counters
+  int nfcnt;
 };
 
 // Block size of the regrouped layout.  Up to 64 tokens the weight-streaming
@@ -239,10 +242,32 @@ void make_plan(const moe_desc* d, int top_k, bool with_routing, Plan* p) {
     p->xq = p->sx = p->sh = 0;
   }
   p->qcnt = p->queue ? take(moe::gemm_queue_ints() * 4) : 0;
+  p->fused = false;
+  p->fcnt = 0;
+  p->nfcnt = 0;
   if (with_routing) {
     p->rsplit = moe::router_fused(p->act, p->T, p->E) ||
                 moe::router_split_logits(p->act, p->T, p->E);
     p->rpart = p->rsplit ? take(moe::router_split_bytes(p->T, p->E)) : 0;
+    // the fused decode kernel: its counters are cleared by the split
+    // router's first launch, so it runs where that launch does
+    const int64_t blocks_est = moe::ffn_blocks_estimate(p->cap, p->B, p->E, p->A);
+    if (p->rsplit && p->A > 0 && d->schedule == MOE_SCHED_QUEUE && !p->act_mx &&
+        moe::fused_decode_fits(p->wdt, p->act, p->B, p->d, p->I, blocks_est)) {
+      FfnArgs a{};
+      a.T = p->T;
+      a.d = p->d;
+      a.E = p->E;
+      a.I = p->I;
+      a.A = p->A;
+      a.B = p->B;
+      a.cap = p->cap;
+      a.splits = p->splits;
+      a.w_dtype = p->wdt;
+      p->nfcnt = moe::fused_counter_ints(a);
+      p->fcnt = take(static_cast<size_t>(p->nfcnt) * 4);
+      p->fused = true;
+    }
   }
   p->total = p->T == 0 ? 0 : off;  // nothing runs for T = 0
 }
@@ -342,6 +367,8 @@ FfnArgs ffn_args(const Plan& p, const void* x, const void* w13, const void* w2,
 }
 
 hipError_t run_ffn(const FfnArgs& a, hipStream_t s) {
+  if (a.fused_cnt)  // W13, W2 and the combine in one persistent launch
+    return timed(MOE_KERNEL_FFN_FUSED, s, [&] { return moe::launch_ffn_fused(a, s); });
   hipError_t e = hipSuccess;
   if (a.act_mx) e = timed(MOE_KERNEL_QUANT_X, s, [&] { return moe::launch_quantize_x(a, s); });
   if (e == hipSuccess && a.queue_sched && !a.queue_zeroed) e = moe::launch_gemm_queue_reset(a, s);
@@ -398,18 +425,21 @@ MOE_API int moe_workspace_bytes(const moe_desc* desc, int top_k, int with_routin
 // Router logits and top-k: one kernel when the router kernel can select
 // itself (timed as route_logits), else two launches.
 // `part` (or nullptr): scratch for the split router when it applies.
+// `zero`, `nzero`: counters the split router's first launch clears (only
+// with `part`).
 static hipError_t route(const void* x, int act, const float* w_gate, float* logits,
                         int32_t* ids, float* gates, int T, int E, int d, int k, void* part,
-                        hipStream_t s) {
+                        hipStream_t s, int32_t* zero = nullptr, int nzero = 0) {
   if (moe::router_fused(act, T, E))
     return timed(MOE_KERNEL_ROUTE_LOGITS, s, [&] {
       return part ? moe::launch_router_fused_split(x, w_gate, logits, ids, gates, T, E, d, k,
-                                                   part, s)
+                                                   part, s, zero, nzero)
                   : moe::launch_router_fused(x, w_gate, logits, ids, gates, T, E, d, k, s);
     });
   hipError_t e = timed(MOE_KERNEL_ROUTE_LOGITS, s, [&] {
     return part && moe::router_split_logits(act, T, E)
-               ? moe::launch_router_split_logits(x, w_gate, logits, T, E, d, part, s)
+               ? moe::launch_router_split_logits(x, w_gate, logits, T, E, d, part, s, zero,
+                                                 nzero)
                : moe::launch_router_logits(x, act, w_gate, logits, T, E, d, s);
   });
   if (e == hipSuccess)
@@ -426,18 +456,22 @@ static hipError_t route(const void* x, int act, const float* w_gate, float* logi
 static hipError_t route_align(const Plan& p, const void* x, const float* w_gate, float* logits,
                               int32_t* ids, float* gates, int32_t* counts, int32_t* sorted,
                               int32_t* block_exp, int32_t* num_padded, void* part,
-                              int32_t* queue, bool* queue_zeroed, hipStream_t s) {
+                              int32_t* queue, bool* queue_zeroed, hipStream_t s,
+                              int32_t* fcnt = nullptr) {
   *queue_zeroed = false;
+  const int nf = fcnt ? p.nfcnt : 0;
   if (moe::route_align_fused(p.act, p.T, p.E))
     return timed(MOE_KERNEL_ROUTE_LOGITS, s, [&] {
       return part ? moe::launch_route_align_fused_split(x, w_gate, logits, ids, gates, p.T, p.E,
                                                         p.d, p.k, p.B, p.cap, counts, sorted,
-                                                        block_exp, num_padded, part, s)
+                                                        block_exp, num_padded, part, s, fcnt,
+                                                        nf)
                   : moe::launch_route_align_fused(x, w_gate, logits, ids, gates, p.T, p.E, p.d,
                                                   p.k, p.B, p.cap, counts, sorted, block_exp,
                                                   num_padded, s);
     });
-  hipError_t e = route(x, p.act, w_gate, logits, ids, gates, p.T, p.E, p.d, p.k, part, s);
+  hipError_t e =
+      route(x, p.act, w_gate, logits, ids, gates, p.T, p.E, p.d, p.k, part, s, fcnt, nf);
   const int nzero = queue ? moe::gemm_queue_ints() : 0;
   if (e == hipSuccess)
     e = timed(MOE_KERNEL_ALIGN, s, [&] {
@@ -577,13 +611,15 @@ static int enqueue_forward(const Plan& p, const void* x, const float* w_gate, co
   int32_t* block_exp = reinterpret_cast<int32_t*>(ws + p.block_exp);
 
   int32_t* queue = p.queue ? reinterpret_cast<int32_t*>(ws + p.qcnt) : nullptr;
+  int32_t* fcnt = p.fused ? reinterpret_cast<int32_t*>(ws + p.fcnt) : nullptr;
   bool zeroed = false;
   void* part = p.rsplit ? ws + p.rpart : nullptr;
   const hipError_t e = route_align(p, x, w_gate, logits, ids, gates, counts, sorted, block_exp,
-                                   num_padded, part, queue, &zeroed, s);
+                                   num_padded, part, queue, &zeroed, s, fcnt);
   if (e != hipSuccess) return MOE_ERR_HIP;
   FfnArgs a = ffn_args(p, x, w13, w2, scales, gates, sorted, block_exp, num_padded, out, ws);
   a.queue_zeroed = zeroed;
+  a.fused_cnt = fcnt;
   return to_status(run_ffn(a, s));
 }
 
@@ -755,7 +791,7 @@ MOE_API int moe_timing_collect(double* total_ms, int64_t* launches, int reset) {
 MOE_API const char* moe_kernel_name(int kind) {
   static const char* names[MOE_KERNEL_COUNT] = {"route_logits", "route_topk", "align",
                                                 "ffn13",        "ffn2",       "combine",
-                                                "quant_x"};
+                                                "quant_x",      "ffn_fused"};
   return (kind >= 0 && kind < MOE_KERNEL_COUNT) ? names[kind] : "";
 }
 

@@ -81,11 +81,18 @@ struct DmaOperands {
   int l31, hi, r16, g;
 
   __device__ __forceinline__ void issue_w(uint8_t* stage, size_t kbyte) const {
+    // the stage as an LDS address: the low 32 bits of a generic pointer into
+    // LDS are its LDS offset (taken this way rather than by an address-space
+    // cast, which the backend lowered to an unencodable compare in the fused
+    // kernel's tile loop)
+    typedef __attribute__((address_space(3))) uint8_t lds_u8;
+    lds_u8* const lds = reinterpret_cast<lds_u8*>(
+        static_cast<uintptr_t>(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(stage))));
 #pragma unroll
     for (int i = 0; i < 8 * NROW; ++i) {
       const int j = ((2 * i) & 15) + hi;  // row within the tile
       const uint8_t* src = wlane[i / 8] + static_cast<size_t>((2 * i) & 15) * wld + kbyte;
-      __builtin_amdgcn_global_load_lds(src + 16 * (l31 ^ j), stage + 1024 * i, 16, 0, kDmaAux);
+      __builtin_amdgcn_global_load_lds(src + 16 * (l31 ^ j), lds + 1024 * i, 16, 0, kDmaAux);
     }
   }
   template <int NSL>
@@ -253,24 +260,19 @@ __device__ __forceinline__ void dma_lanes(DmaOperands<WT, NROW, NS>& op, size_t 
 }
 
 // ------------------------------------------------------------ W13 + SiLU*mul
-// Grid: x = row block b (B = 16 NS), y = 16-channel tile.  The wave computes
+// One tile: row block b (B = 16 NS), 16 channels from n0.  The wave computes
 // gate rows n0.. and up rows I+n0.. against the block's tokens and writes
 // h[row, n] = SiLU(s_g gate) * (s_u up) for the live subtiles (pad rows
 // included: their columns never reach an output).
 
 template <typename WT, int NS, int P>
-__global__ __launch_bounds__(kDmaThreads) void ffn13_dma_kernel(
+__device__ __forceinline__ void dma13_tile(
     const bf16_t* __restrict__ x, const WT* __restrict__ w13, const float* __restrict__ s13,
     int scale_mode, const int32_t* __restrict__ sorted_ids,
-    const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded,
-    bf16_t* __restrict__ h, int d, int I, int k, int A) {
+    const int32_t* __restrict__ block_expert, bf16_t* __restrict__ h, int d, int I, int k, int A,
+    int b, int n0, uint8_t* const (&ring)[4]) {
   constexpr int B = 16 * NS;
-  using G = DmaGeom<WT, 2, NS>;
-  DMA_RING(ring, G::kStageBytes, P);
-  const int b = blockIdx.x;
-  if (b * B >= *num_padded) return;
   const int e = block_expert[b];
-  const int n0 = blockIdx.y * 16;
   const int32_t* blk = sorted_ids + static_cast<size_t>(b) * B;
   const int nsub = live_subtiles<NS>(blk, A);
 
@@ -316,26 +318,35 @@ __global__ __launch_bounds__(kDmaThreads) void ffn13_dma_kernel(
   }
 }
 
+// Grid: x = row block b, y = 16-channel tile.
+template <typename WT, int NS, int P>
+__global__ __launch_bounds__(kDmaThreads) void ffn13_dma_kernel(
+    const bf16_t* __restrict__ x, const WT* __restrict__ w13, const float* __restrict__ s13,
+    int scale_mode, const int32_t* __restrict__ sorted_ids,
+    const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded,
+    bf16_t* __restrict__ h, int d, int I, int k, int A) {
+  using G = DmaGeom<WT, 2, NS>;
+  DMA_RING(ring, G::kStageBytes, P);
+  const int b = blockIdx.x;
+  if (b * 16 * NS >= *num_padded) return;
+  dma13_tile<WT, NS, P>(x, w13, s13, scale_mode, sorted_ids, block_expert, h, d, I, k, A, b,
+                        blockIdx.y * 16, ring);
+}
+
 // ------------------------------------------------------------ W2 + gate scale
-// Grid: x = row block b, y = group of 16 RN channels of d, z = split of
-// K = I.  Writes y_part[z, f, n] = gate_f * s(n) * sum_{i in split} W2[e, n, i] h[row, i]
+// One tile: row block b, 16 RN channels of d from n0, split z of K = I.
+// Writes y_part[z, f, n] = gate_f * s(n) * sum_{i in split} W2[e, n, i] h[row, i]
 // for the block's real slots f.  RN tiles per wave: every wave reads all h
 // rows of its block, so wider waves read less h per weight byte.
 
 template <typename WT, int NS, int P, int RN>
-__global__ __launch_bounds__(kDmaThreads) void ffn2_dma_kernel(
+__device__ __forceinline__ void dma2_tile(
     const bf16_t* __restrict__ h, const WT* __restrict__ w2, const float* __restrict__ s2,
     int scale_mode, const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
-    const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded,
-    float* __restrict__ y_part, int d, int I, int A, int ksplit) {
+    const int32_t* __restrict__ block_expert, float* __restrict__ y_part, int d, int I, int A,
+    int ksplit, int b, int n0, int z, uint8_t* const (&ring)[4]) {
   constexpr int B = 16 * NS;
-  using G = DmaGeom<WT, RN, NS>;
-  DMA_RING(ring, G::kStageBytes, P);
-  const int b = blockIdx.x;
-  if (b * B >= *num_padded) return;
   const int e = block_expert[b];
-  const int n0 = blockIdx.y * 16 * RN;
-  const int z = blockIdx.z;
   const int k_begin = z * ksplit;
   const int nch = (min(I, k_begin + ksplit) - k_begin) / dma_kc<WT>();
   const int32_t* blk = sorted_ids + static_cast<size_t>(b) * B;
@@ -379,6 +390,191 @@ __global__ __launch_bounds__(kDmaThreads) void ffn2_dma_kernel(
           o.z = acc[s][rt][2] * load_scale(s2, scale_mode, e, static_cast<size_t>(e) * d + nb + 2) * gate;
           o.w = acc[s][rt][3] * load_scale(s2, scale_mode, e, static_cast<size_t>(e) * d + nb + 3) * gate;
           *reinterpret_cast<float4*>(yrow + nb) = o;
+        }
+      }
+    }
+  }
+}
+
+// Grid: x = row block b, y = group of 16 RN channels of d, z = split of K = I.
+template <typename WT, int NS, int P, int RN>
+__global__ __launch_bounds__(kDmaThreads) void ffn2_dma_kernel(
+    const bf16_t* __restrict__ h, const WT* __restrict__ w2, const float* __restrict__ s2,
+    int scale_mode, const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
+    const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded,
+    float* __restrict__ y_part, int d, int I, int A, int ksplit) {
+  using G = DmaGeom<WT, RN, NS>;
+  DMA_RING(ring, G::kStageBytes, P);
+  const int b = blockIdx.x;
+  if (b * 16 * NS >= *num_padded) return;
+  dma2_tile<WT, NS, P, RN>(h, w2, s2, scale_mode, topk_w, sorted_ids, block_expert, y_part, d,
+                           I, A, ksplit, b, blockIdx.y * 16 * RN, blockIdx.z, ring);
+}
+
+// ------------------------------------------------------------ fused W13 -> W2 -> combine
+// The decode path's expert computation as one persistent launch (the pages'
+// "one batched GPU operation": routing, regrouping and the experts' work
+// fused; Hungarian page, section "A fused MoE ...").  Workgroups take tiles
+// from one monotone ticket counter: first every W13 tile (ordered channel
+// tile by channel tile, so the h columns fill up in K order), then every W2
+// tile (split by split).  A W2 tile waits until the W13 tiles of its block
+// and K range have counted themselves done; every W13 ticket precedes every
+// W2 ticket and W13 tiles wait for nothing, so a waiting workgroup only ever
+// waits on work a running workgroup already holds (no deadlock, whatever
+// the grid size).  The wait is bounded (a flag records a timeout instead of
+// hanging).  The combine is fused: after a W2 tile writes its partials it
+// counts one arrival per real slot on the slot's (token, channel group); the
+// tile that brings a counter to k * splits adds that token's partials, slots
+// then splits in the same fixed order as the combine kernel, and writes the
+// output, so the result is bit-identical to the three separate launches.
+// Cross-workgroup data (h, the partials) is published with an agent-scope
+// release fence before the counter update and read after an acquire fence
+// (the GPU's L2s are per XCD).  Counters are zeroed by the routing launch.
+
+// Counter words: ticket, timeout flag, done13[blocks][splits], arrive[T][d / (16 RN)].
+constexpr int kFusedTicket = 0;
+constexpr int kFusedTimeout = 32;
+constexpr int kFusedDone = 64;
+#ifndef MOE_FUSED_SPIN_LIMIT
+#define MOE_FUSED_SPIN_LIMIT (1 << 20)
+#endif
+
+static int fused_counter_words(int T, int cap, int B, int splits, int d, int rn) {
+  return kFusedDone + (cap / B) * splits + T * (d / (16 * rn));
+}
+
+template <typename OT>
+__device__ __forceinline__ void fused_store4(OT* p, float4 v);
+template <>
+__device__ __forceinline__ void fused_store4<bf16_t>(bf16_t* p, float4 v) {
+  const uint32_t lo = f32_to_bf16(v.x) | (static_cast<uint32_t>(f32_to_bf16(v.y)) << 16);
+  const uint32_t hi = f32_to_bf16(v.z) | (static_cast<uint32_t>(f32_to_bf16(v.w)) << 16);
+  *reinterpret_cast<uint2*>(p) = uint2{lo, hi};
+}
+
+struct FusedParams {
+  const bf16_t* x;
+  const void* w13;
+  const void* w2;
+  const float* s13;
+  const float* s2;
+  int scale_mode;
+  const float* topk_w;
+  const int32_t* sorted_ids;
+  const int32_t* block_expert;
+  const int32_t* num_padded;
+  bf16_t* h;
+  float* y_part;
+  bf16_t* out;
+  int32_t* cnt;
+  int T, d, I, k, A, cap, splits, ksplit;
+};
+
+template <typename WT, int NS, int P13, int P2, int RN>
+__global__ __launch_bounds__(kDmaThreads) void ffn_fused_dma_kernel(FusedParams p) {
+  constexpr int B = 16 * NS;
+  constexpr int kS13 = DmaGeom<WT, 2, NS>::kStageBytes;
+  constexpr int kS2 = DmaGeom<WT, RN, NS>::kStageBytes;
+  constexpr int kStage = kS13 > kS2 ? kS13 : kS2;
+  constexpr int P = P13 > P2 ? P13 : P2;
+  DMA_RING(ring, kStage, P);
+  const int lane = threadIdx.x;
+  const int nblk = *p.num_padded / B;
+  const int n13 = nblk * (p.I / 16);
+  const int nd = p.d / (16 * RN);
+  const int n2 = nblk * nd * p.splits;
+  int32_t* const done13 = p.cnt + kFusedDone;
+  int32_t* const arrive = done13 + (p.cap / B) * p.splits;
+  const WT* w13 = static_cast<const WT*>(p.w13);
+  const WT* w2 = static_cast<const WT*>(p.w2);
+
+  // Every branch of this loop is wave-uniform (tickets and counters go
+  // through readfirstlane; the one-lane atomics are issued by every lane
+  // with 0 added by all but lane 0): lane-divergent branches that skip to
+  // the next iteration let the compiler restructure the loop so that some
+  // lanes re-entered it without lane 0 and never took a new ticket.
+  for (;;) {
+    const int t = __builtin_amdgcn_readfirstlane(__hip_atomic_fetch_add(
+        p.cnt + kFusedTicket, lane == 0 ? 1 : 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    if (t >= n13 + n2) break;
+    if (t < n13) {
+      const int y = t / nblk;
+      const int b = t - y * nblk;
+      dma13_tile<WT, NS, P13>(p.x, w13, p.s13, p.scale_mode, p.sorted_ids, p.block_expert, p.h,
+                              p.d, p.I, p.k, p.A, b, 16 * y, ring);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // h of this tile, device-wide
+      __hip_atomic_fetch_add(done13 + b * p.splits + (16 * y) / p.ksplit, lane == 0 ? 1 : 0,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      const int t2 = t - n13;
+      const int z = t2 / (nblk * nd);
+      const int r = t2 - z * (nblk * nd);
+      const int dt = r / nblk;
+      const int b = r - dt * nblk;
+      const int kb = z * p.ksplit;
+      const int need = (min(p.I, kb + p.ksplit) - kb) / 16;
+      // bounded wait for the W13 tiles of this block's K range
+      for (int spin = 0;; ++spin) {
+        const int got = __builtin_amdgcn_readfirstlane(__hip_atomic_load(
+            done13 + b * p.splits + z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        if (got >= need) break;
+        if (spin >= MOE_FUSED_SPIN_LIMIT) {
+          __hip_atomic_store(p.cnt + kFusedTimeout, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the W13 tiles' h
+      dma2_tile<WT, NS, P2, RN>(p.h, w2, p.s2, p.scale_mode, p.topk_w, p.sorted_ids,
+                                p.block_expert, p.y_part, p.d, p.I, p.A, p.ksplit, b,
+                                dt * 16 * RN, z, ring);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // this tile's partials, device-wide
+      // one arrival per real slot; the last one for a token's channel group
+      // adds up that token's partials
+      const int32_t* blk = p.sorted_ids + static_cast<size_t>(b) * B;
+      const int total = p.k * p.splits;
+      uint64_t last = 0;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        int mine = 0;
+        if (lane < 16) {
+          const int f = blk[16 * s + lane];
+          if (f < p.A) {
+            const int prev = __hip_atomic_fetch_add(arrive + (f / p.k) * nd + dt, 1,
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            mine = prev == total - 1;
+          }
+        }
+        last |= static_cast<uint64_t>(__ballot(mine)) << (16 * s);
+      }
+      if (last != 0) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the other tiles' partials
+        constexpr int kGroups = 4 * RN;  // float4 groups of the 16 RN channels
+        while (last) {
+          const int bit = __builtin_ctzll(last);
+          last &= last - 1;
+          const int tok = blk[16 * (bit / 16) + bit % 16] / p.k;
+          if (lane < kGroups) {
+            const int c = dt * 16 * RN + 4 * lane;
+            float4 o = {0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < p.k; ++j) {
+              const size_t f = static_cast<size_t>(tok) * p.k + j;
+              float4 sj = {0.f, 0.f, 0.f, 0.f};
+              for (int zz = 0; zz < p.splits; ++zz) {
+                const float4 q = *reinterpret_cast<const float4*>(
+                    p.y_part + (static_cast<size_t>(zz) * p.A + f) * p.d + c);
+                sj.x += q.x;
+                sj.y += q.y;
+                sj.z += q.z;
+                sj.w += q.w;
+              }
+              o.x += sj.x;
+              o.y += sj.y;
+              o.z += sj.z;
+              o.w += sj.w;
+            }
+            fused_store4<bf16_t>(p.out + static_cast<size_t>(tok) * p.d + c, o);
+          }
         }
       }
     }
@@ -486,6 +682,92 @@ hipError_t launch_ffn2_dma(const FfnArgs& a, hipStream_t s) {
         return ffn2_dma_go<bf16_t, 1, kDma2WideP, kDma2WideRN>(a, s);
       return ffn2_dma_go<bf16_t, 1, MOE_DMA2_P1>(a, s);
     case 32: return ffn2_dma_go<bf16_t, 2, MOE_DMA2_P2>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+// ------------------------------------------------------------ fused launcher
+
+bool fused_decode_fits(int w_dtype, int act_dtype, int B, int d, int I, int64_t blocks_est) {
+#ifdef MOE_NO_FUSED_DECODE
+  return false;
+#else
+  return w_dtype == kDtypeBF16 && act_dtype == kDtypeBF16 &&
+         dma_stream_use(w_dtype, act_dtype, B, d, I, blocks_est) &&
+         d % (16 * dma_w2_rn(w_dtype, B, blocks_est)) == 0;
+#endif
+}
+
+int fused_counter_ints(const FfnArgs& a) {
+  const int64_t blocks = ffn_blocks_estimate(a.cap, a.B, a.E, a.A);
+  return fused_counter_words(a.T, a.cap, a.B, a.splits, a.d, dma_w2_rn(a.w_dtype, a.B, blocks));
+}
+
+namespace {
+
+// Workgroups of kernel K the chip holds at once (occupancy x compute units),
+// asked of the runtime once per kernel; 0 when it cannot say.
+template <auto K>
+int fused_resident(int threads) {
+  static const int n = [threads] {
+    int per_cu = 0, dev = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, K, threads, 0) != hipSuccess ||
+        hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    return per_cu * cus;
+  }();
+  return n;
+}
+
+template <int NS, int P13, int P2, int RN>
+hipError_t ffn_fused_go(const FfnArgs& a, hipStream_t s) {
+  FusedParams p{};
+  p.x = static_cast<const bf16_t*>(a.x);
+  p.w13 = a.w13;
+  p.w2 = a.w2;
+  p.s13 = a.s13;
+  p.s2 = a.s2;
+  p.scale_mode = a.scale_mode;
+  p.topk_w = a.topk_w;
+  p.sorted_ids = a.sorted_ids;
+  p.block_expert = a.block_expert;
+  p.num_padded = a.num_padded;
+  p.h = static_cast<bf16_t*>(a.h);
+  p.y_part = a.y_part;
+  p.out = static_cast<bf16_t*>(a.out);
+  p.cnt = a.fused_cnt;
+  p.T = a.T;
+  p.d = a.d;
+  p.I = a.I;
+  p.k = a.k;
+  p.A = a.A;
+  p.cap = a.cap;
+  p.splits = a.splits;
+  p.ksplit = a.ksplit;
+  constexpr auto kern = ffn_fused_dma_kernel<bf16_t, NS, P13, P2, RN>;
+  // at most one workgroup per possible tile of the capacity's blocks
+  const int64_t blocks = a.cap / a.B;
+  const int64_t tiles = blocks * (a.I / 16 + (a.d / (16 * RN)) * a.splits);
+  const int res = fused_resident<kern>(kDmaThreads);
+  const int grid = static_cast<int>(res > 0 && res < tiles ? res : tiles);
+  kern<<<grid, kDmaThreads, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_ffn_fused(const FfnArgs& a, hipStream_t s) {
+  const int64_t blocks = ffn_blocks_estimate(a.cap, a.B, a.E, a.A);
+  if (!a.fused_cnt || !fused_decode_fits(a.w_dtype, a.act_dtype, a.B, a.d, a.I, blocks) ||
+      a.ksplit % 16 != 0 || a.ksplit % dma_stream_kc(a.w_dtype) != 0)
+    return hipErrorInvalidValue;
+  switch (a.B) {
+    case 16:
+      if (dma_w2_rn(a.w_dtype, a.B, blocks) == kDma2WideRN)
+        return ffn_fused_go<1, 2, kDma2WideP, kDma2WideRN>(a, s);
+      return ffn_fused_go<1, MOE_DMA13_P1, MOE_DMA2_P1, kDma2RN>(a, s);
+    case 32: return ffn_fused_go<2, MOE_DMA13_P2, MOE_DMA2_P2, kDma2RN>(a, s);
   }
   return hipErrorInvalidValue;
 }

@@ -36,20 +36,23 @@ hipError_t launch_route_align_fused(const void* x, const float* wg, float* logit
 // second launch that adds their partials in the fused kernel's order (same
 // results, bit for bit); `part` is router_split_bytes(T, E) of scratch.
 size_t router_split_bytes(int T, int E);
+// `zero`: nzero int32 words the partial launch sets to 0 (counters of the
+// fused expert kernel that follows in the layer path), or none.
 hipError_t launch_router_fused_split(const void* x, const float* wg, float* logits, int32_t* ids,
                                      float* w, int T, int E, int d, int k, void* part,
-                                     hipStream_t s);
+                                     hipStream_t s, int32_t* zero = nullptr, int nzero = 0);
 hipError_t launch_route_align_fused_split(const void* x, const float* wg, float* logits,
                                           int32_t* ids, float* w, int T, int E, int d, int k,
                                           int B, int cap, int32_t* counts, int32_t* sorted_ids,
                                           int32_t* block_expert, int32_t* num_padded, void* part,
-                                          hipStream_t s);
+                                          hipStream_t s, int32_t* zero = nullptr, int nzero = 0);
 // bf16 activations, 1 <= T <= 64, any E: the logits alone, K split the same
 // way (16 one-wave workgroups per tile, then a sum in slice order: the same
 // bits as launch_router_logits); `part` is router_split_bytes(T, E).
 bool router_split_logits(int act_dtype, int T, int E);
 hipError_t launch_router_split_logits(const void* x, const float* wg, float* logits, int T, int E,
-                                      int d, void* part, hipStream_t s);
+                                      int d, void* part, hipStream_t s, int32_t* zero = nullptr,
+                                      int nzero = 0);
 // `zero`: nzero int32 that the launch also sets to 0 (the expert kernels'
 // work-queue counters when the layer runs align right before them).
 hipError_t launch_align(const int32_t* ids, int A, int E, int B, int cap, int32_t* counts,
@@ -88,6 +91,10 @@ struct FfnArgs {
   bool queue_sched;
   bool queue_zeroed;
   int32_t* queue;
+  // The fused decode kernel (W13, W2 and combine in one persistent launch):
+  // its counters (fused_counter_ints()), zeroed by the routing launch; null
+  // when the expert kernels run as separate launches.
+  int32_t* fused_cnt;
 };
 
 hipError_t launch_ffn13(const FfnArgs& a, hipStream_t s);
@@ -152,6 +159,13 @@ hipError_t launch_ffn13_dma(const FfnArgs& a, hipStream_t s);
 // output channels per W2 workgroup of that path for a block size and block estimate
 int dma_w2_channels(int w_dtype, int B, int64_t blocks_est);
 hipError_t launch_ffn2_dma(const FfnArgs& a, hipStream_t s);
+
+// The fused decode kernel: bf16 activations and weights on the
+// LDS-streaming path (blocks of 16 or 32).  fused_counter_ints() is the
+// counter workspace it needs; launch_ffn_fused runs W13, W2 and the combine.
+bool fused_decode_fits(int w_dtype, int act_dtype, int B, int d, int I, int64_t blocks_est);
+int fused_counter_ints(const FfnArgs& a);
+hipError_t launch_ffn_fused(const FfnArgs& a, hipStream_t s);
 
 // K chunk the W2 kernel uses for a given shape, block size, dtypes and
 // block estimate (the split length must be a multiple of it).

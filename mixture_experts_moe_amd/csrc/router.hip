@@ -110,6 +110,10 @@ struct AlignOut {
   int32_t* sorted_ids;
   int32_t* block_expert;
   int32_t* num_padded;
+  // int32 words the split router's partial launch sets to 0 (the next
+  // kernels' counters), or none
+  int32_t* zero = nullptr;
+  int nzero = 0;
 };
 
 constexpr int kRaWaves = 16;  // the fused router's workgroup
@@ -348,6 +352,11 @@ __global__ __launch_bounds__(64 * NW) void router_logits_bf16_kernel(
       ((static_cast<size_t>(slice) * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x) * 64 + lane;
   if constexpr (kPart == 1) {
     part[part_at] = acc_h[0] + (acc_m[0] + acc_l[0]);
+    if (ao.nzero > 0) {  // every workgroup clears its share of the counters
+      const int nwg = gridDim.x * gridDim.y * gridDim.z;
+      const int wg = (blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
+      for (int i = wg * 64 + lane; i < ao.nzero; i += nwg * 64) ao.zero[i] = 0;
+    }
     return;
   } else {
 #pragma unroll
@@ -449,12 +458,15 @@ size_t router_split_bytes(int T, int E) {
 
 hipError_t launch_router_fused_split(const void* x, const float* wg, float* logits, int32_t* ids,
                                      float* w, int T, int E, int d, int k, void* part,
-                                     hipStream_t s) {
-  if (!router_fused(kDtypeBF16, T, E) || !part) return hipErrorInvalidValue;
+                                     hipStream_t s, int32_t* zero, int nzero) {
+  if (!router_fused(kDtypeBF16, T, E) || !part || (nzero > 0 && !zero)) return hipErrorInvalidValue;
   const bf16_t* xb = static_cast<const bf16_t*>(x);
   f32x4* pt = static_cast<f32x4*>(part);
+  AlignOut zo{};
+  zo.zero = zero;
+  zo.nzero = nzero;
   router_logits_bf16_kernel<1, 1, false, false, 1><<<dim3((T + 15) / 16, 1, kRouterSlices), 64, 0, s>>>(
-      xb, wg, nullptr, nullptr, nullptr, T, E, d, 0, AlignOut{}, pt);
+      xb, wg, nullptr, nullptr, nullptr, T, E, d, 0, zo, pt);
   router_logits_bf16_kernel<1, 16, true, false, 2><<<dim3((T + 15) / 16, 1), 1024, 0, s>>>(
       xb, wg, logits, ids, w, T, E, d, k, AlignOut{}, pt);
   return hipGetLastError();
@@ -484,12 +496,16 @@ bool router_split_logits(int act_dtype, int T, int E) {
 }
 
 hipError_t launch_router_split_logits(const void* x, const float* wg, float* logits, int T, int E,
-                                      int d, void* part, hipStream_t s) {
-  if (!router_split_logits(kDtypeBF16, T, E) || !part) return hipErrorInvalidValue;
+                                      int d, void* part, hipStream_t s, int32_t* zero, int nzero) {
+  if (!router_split_logits(kDtypeBF16, T, E) || !part || (nzero > 0 && !zero))
+    return hipErrorInvalidValue;
   f32x4* pt = static_cast<f32x4*>(part);
   const int gx = (T + 15) / 16, gy = (E + 15) / 16;
+  AlignOut zo{};
+  zo.zero = zero;
+  zo.nzero = nzero;
   router_logits_bf16_kernel<1, 1, false, false, 1><<<dim3(gx, gy, kRouterSlices), 64, 0, s>>>(
-      static_cast<const bf16_t*>(x), wg, nullptr, nullptr, nullptr, T, E, d, 0, AlignOut{}, pt);
+      static_cast<const bf16_t*>(x), wg, nullptr, nullptr, nullptr, T, E, d, 0, zo, pt);
   router_split_sum_kernel<<<dim3(gx, gy), 64, 0, s>>>(pt, logits, T, E);
   return hipGetLastError();
 }
@@ -498,14 +514,18 @@ hipError_t launch_route_align_fused_split(const void* x, const float* wg, float*
                                           int32_t* ids, float* w, int T, int E, int d, int k,
                                           int B, int cap, int32_t* counts, int32_t* sorted_ids,
                                           int32_t* block_expert, int32_t* num_padded, void* part,
-                                          hipStream_t s) {
-  if (!route_align_fused(kDtypeBF16, T, E) || k > E || B < 1 || cap % B != 0 || !part)
+                                          hipStream_t s, int32_t* zero, int nzero) {
+  if (!route_align_fused(kDtypeBF16, T, E) || k > E || B < 1 || cap % B != 0 || !part ||
+      (nzero > 0 && !zero))
     return hipErrorInvalidValue;
   const AlignOut ao{B, cap, counts, sorted_ids, block_expert, num_padded};
   const bf16_t* xb = static_cast<const bf16_t*>(x);
   f32x4* pt = static_cast<f32x4*>(part);
+  AlignOut zo{};
+  zo.zero = zero;
+  zo.nzero = nzero;
   router_logits_bf16_kernel<1, 1, false, false, 1><<<dim3(1, 1, kRouterSlices), 64, 0, s>>>(
-      xb, wg, nullptr, nullptr, nullptr, T, E, d, 0, AlignOut{}, pt);
+      xb, wg, nullptr, nullptr, nullptr, T, E, d, 0, zo, pt);
   router_logits_bf16_kernel<1, 16, true, true, 2><<<dim3(1, 1), 1024, 0, s>>>(
       xb, wg, logits, ids, w, T, E, d, k, ao, pt);
   return hipGetLastError();

@@ -294,7 +294,7 @@ def test_strerror_and_names(lib):
     assert B.strerror(-99) == "unknown status"
     names = [B.moe_kernel_name(i) for i in range(B.MOE_KERNEL_COUNT)]
     assert names == ["route_logits", "route_topk", "align", "ffn13", "ffn2", "combine",
-                     "quant_x"]
+                     "quant_x", "ffn_fused"]
     assert B.moe_kernel_name(99) == ""
 
 

@@ -584,6 +584,85 @@ def test_layer_split_router_equals_single_workgroup_router(T, E, k, d):
     assert torch.equal(out, ref)
 
 
+# ---------------------------------------------------------------- fused decode kernel
+
+def _launches(fn):
+    B.moe_timing_collect(reset=True)
+    B.moe_timing_enable(True)
+    try:
+        out = fn()
+        t = B.moe_timing_collect(reset=True)
+    finally:
+        B.moe_timing_enable(False)
+    return out, {k: v[1] for k, v in t.items()}
+
+
+FUSED_CASES = [
+    # T, overrides of the decode workload (None: the full decode shape)
+    (1, None), (5, None), (8, None), (16, None), (17, None), (32, None), (64, None),
+    (3, dict(d=512, I=4096, E=8, k=2)),
+    (13, dict(d=768, I=2048, E=16, k=4)),
+    (40, dict(d=256, I=4096, E=4, k=1)),       # an expert with two 32-token blocks
+    (64, dict(d=512, I=3840, E=8, k=2)),       # a shorter last K split
+]
+
+
+@pytest.mark.parametrize("T,over", FUSED_CASES, ids=[f"T{c[0]}-{'full' if c[1] is None else 'small'}"
+                                                     for c in FUSED_CASES])
+def test_fused_decode_equals_separate_launches(decode_inputs, T, over):
+    """The persistent W13 -> W2 -> combine launch (schedule queue) against
+    the three separate launches (schedules static and auto): bit-identical
+    outputs, one fused launch instead of three; and the oracle on the fused
+    output."""
+    note(f"fused decode T={T} {over}")
+    if over is None:
+        cfg = synth.WORKLOADS["decode_bf16"]
+        inp = with_x(decode_inputs, synth.make_x(T, cfg["d"], "bf16", cfg["x_std"], 3, DEV))
+    else:
+        inp = synth.make_inputs("decode_bf16", T=T, device=DEV, x_std=1.0, **over)
+    run = lambda sched: B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k,
+                                      schedule=sched)
+    fused, n_f = _launches(lambda: run("queue"))
+    sep, n_s = _launches(lambda: run("static"))
+    dflt, n_a = _launches(lambda: run("auto"))
+    torch.cuda.synchronize()
+    assert n_f["ffn_fused"] == 1 and n_f["ffn13"] == n_f["ffn2"] == n_f["combine"] == 0, n_f
+    for n in (n_s, n_a):
+        assert n["ffn_fused"] == 0 and n["ffn13"] == n["ffn2"] == n["combine"] == 1, n
+    assert torch.equal(fused, sep) and torch.equal(dflt, sep)
+    _full_case(inp, np.arange(T) if T <= 16 else None, out=fused)
+
+
+def test_fused_decode_back_to_back_and_in_a_graph(decode_inputs):
+    """Forwards of different sizes in a row sharing one workspace, then a
+    recorded graph replayed several times: every call starts its counters
+    from zero (the routing launch clears them)."""
+    cfg = synth.WORKLOADS["decode_bf16"]
+    desc = B.make_desc(64, cfg["d"], cfg["E"], cfg["I"], B.MOE_DTYPE_BF16, B.MOE_DTYPE_BF16,
+                       schedule="queue")
+    ws = torch.empty(B.moe_workspace_bytes(desc, cfg["k"], True), dtype=torch.uint8, device=DEV)
+    refs = {}
+    for T in (64, 1, 32, 8, 64, 1):
+        inp = with_x(decode_inputs, synth.make_x(T, cfg["d"], "bf16", cfg["x_std"], T, DEV))
+        got = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, workspace=ws,
+                            schedule="queue")
+        ref = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, schedule="static")
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), f"T={T}"
+        refs[T] = ref
+    inp = with_x(decode_inputs, synth.make_x(8, cfg["d"], "bf16", cfg["x_std"], 8, DEV).clone())
+    out = torch.empty_like(inp.x)
+    g = B.MoeGraph(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, out=out, schedule="queue")
+    try:
+        for _ in range(4):
+            out.fill_(float("nan"))
+            g.launch()
+            torch.cuda.synchronize()
+            assert torch.equal(out, refs[8])
+    finally:
+        g.close()
+
+
 # ---------------------------------------------------------------- tile schedules
 
 SCHED_CASES = [
