@@ -78,6 +78,13 @@ def parse():
     ap.add_argument("--summarize-stats", nargs="+", metavar="DIR",
                     help="no GPU: write profiles/<workload>_kernel_stats.md from a rocprofv3 "
                          "--kernel-trace --stats output directory (and the run's stdout file)")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
+                    help="no GPU: write profiles/<workload>_mfma_counters.md from rocprofv3 --pmc "
+                         "output directories (matrix-core counters) and a --kernel-trace --stats "
+                         "directory given last")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="decode workload: skip the prefill sub-record (T = 4096 on the same weights)")
+    ap.add_argument("--cpu-reps", type=int, default=3, help="CPU oracle repetitions (median reported)")
     ap.add_argument("--command", default="", help="profiling command recorded in the summary")
     return ap.parse_args()
 
@@ -130,12 +137,16 @@ def alg_work(inp, ids, k) -> dict:
         "ffn13_bytes": w13 + (T * d * 33 // 32 + A * I * 33 // 32 if inp.act_quant
                               else T * d * ab + A * I * ab),
         "ffn13_flops": A * 4 * d * I,
+        # W2: touched experts' W2 (+ scales), h of the real slots, and one fp32
+        # output row per slot handed to the combine
+        "ffn2_bytes": w2 + (A * I * 33 // 32 if inp.act_quant else A * I * ab) + A * d * 4,
+        "ffn2_flops": A * 2 * d * I,
     }
 
 
-def cpu_baseline(inp_T, k_sample: int, workload: str) -> dict:
+def cpu_baseline(inp_T, k_sample: int, workload: str, reps: int = 3) -> dict:
     """The oracle as it stands, on `k_sample` tokens of the batch, timed on
-    this host's cores."""
+    this host's cores: the median of `reps` forwards."""
     import numpy as np
     import threadpoolctl
 
@@ -155,14 +166,19 @@ def cpu_baseline(inp_T, k_sample: int, workload: str) -> dict:
         kw["w2"][e]
     info = threadpoolctl.threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info] or [1])
-    t0 = time.perf_counter()
-    oracle.moe_forward(**kw, block_m=16)
-    dt = time.perf_counter() - t0
+    times = []
+    for _ in range(max(reps, 1)):
+        t0 = time.perf_counter()
+        oracle.moe_forward(**kw, block_m=16)
+        times.append(time.perf_counter() - t0)
+    times.sort()
+    dt = times[len(times) // 2]
     return {"value": round(k_sample / dt, 3), "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{workload}: {k_sample} of the T={inp_T.T} batch's tokens through the "
-                      f"fp64 NumPy per-expert-loop oracle, one forward, {dt:.2f} s "
-                      f"({len(os.sched_getaffinity(0))} host cores visible, BLAS threads {threads})"}
+                      f"fp64 NumPy per-expert-loop oracle, median of {len(times)} forwards "
+                      f"({', '.join(f'{t:.2f}' for t in times)} s; "
+                      f"{len(os.sched_getaffinity(0))} host cores visible, BLAS threads {threads})"}
 
 
 COPY_CAL_BYTES = 1 << 30
@@ -192,10 +208,13 @@ def _short_kernel(name: str) -> str:
     return "".join(out).replace("moe::", "")
 
 
+EXPERT_KINDS = (("ffn13", "ffn13 (grouped W13 + SiLU*mul)"), ("ffn2", "ffn2 (grouped W2 + gate scale)"))
+
+
 def summarize_traffic(workload: str, dirs, command: str) -> str:
-    """HBM bytes per ffn13 launch: FETCH_SIZE and WRITE_SIZE (KiB per dispatch)
-    scaled by what the same counters read for a plain device copy of
-    COPY_CAL_BYTES bytes."""
+    """HBM bytes per ffn13 and per ffn2 launch: FETCH_SIZE and WRITE_SIZE
+    (KiB per dispatch) scaled by what the same counters read for a plain
+    device copy of COPY_CAL_BYTES bytes."""
     fetch, write, cfetch, cwrite = (_counter_rows(d) for d in dirs)
 
     def factor(rows, counter):
@@ -207,23 +226,12 @@ def summarize_traffic(workload: str, dirs, command: str) -> str:
 
     ff, fw = factor(cfetch, "FETCH_SIZE"), factor(cwrite, "WRITE_SIZE")
 
-    def launches(rows, counter):
+    def launches(rows, counter, kind):
         got = [(int(r["Dispatch_Id"]), r["Kernel_Name"], int(r["Grid_Size"]), float(r["Counter_Value"]))
-               for r in rows if r["Counter_Name"] == counter and "ffn13" in r["Kernel_Name"]]
+               for r in rows if r["Counter_Name"] == counter and kind + "_" in r["Kernel_Name"]]
         return sorted(got)
 
-    lf, lw = launches(fetch, "FETCH_SIZE"), launches(write, "WRITE_SIZE")
-    if len(lf) != len(lw) or not lf:
-        raise SystemExit(f"ffn13 launches differ between the runs: {len(lf)} vs {len(lw)}")
-    rows = []
-    for (_, kf, gf, vf), (_, kw, gw, vw) in zip(lf, lw):
-        if kf != kw or gf != gw:
-            raise SystemExit("the two runs launched different ffn13 kernels in order")
-        rows.append({"kernel": _short_kernel(kf), "grid_threads": gf,
-                     "fetch_bytes": int(vf * 1024 * ff), "write_bytes": int(vw * 1024 * fw)})
-    per_launch = sum(r["fetch_bytes"] + r["write_bytes"] for r in rows) / len(rows)
     out = {
-        "kernel": "ffn13 (grouped W13 + SiLU*mul)",
         "workload": workload,
         # expert-kernel sources (all but the routing-only files)
         "kernel_source_sha": kernel_source_sha(exclude=ROUTING_ONLY_SOURCES),
@@ -235,10 +243,20 @@ def summarize_traffic(workload: str, dirs, command: str) -> str:
             "note": "counter values are KiB per dispatch; each is scaled by the bytes a plain "
                     "device copy of copy_bytes moves per counted byte",
         },
-        "launches": rows,
-        "traffic_bytes_per_launch": int(per_launch),
     }
-    path = os.path.join(ROOT, "profiles", f"ffn13_{workload}_traffic.json")
+    for kind, label in EXPERT_KINDS:
+        lf, lw = launches(fetch, "FETCH_SIZE", kind), launches(write, "WRITE_SIZE", kind)
+        if len(lf) != len(lw) or not lf:
+            raise SystemExit(f"{kind} launches differ between the runs: {len(lf)} vs {len(lw)}")
+        rows = []
+        for (_, kf, gf, vf), (_, kw, gw, vw) in zip(lf, lw):
+            if kf != kw or gf != gw:
+                raise SystemExit(f"the two runs launched different {kind} kernels in order")
+            rows.append({"kernel": _short_kernel(kf), "grid_threads": gf,
+                         "fetch_bytes": int(vf * 1024 * ff), "write_bytes": int(vw * 1024 * fw)})
+        per_launch = sum(r["fetch_bytes"] + r["write_bytes"] for r in rows) / len(rows)
+        out[kind] = {"kernel": label, "launches": rows, "traffic_bytes_per_launch": int(per_launch)}
+    path = os.path.join(ROOT, "profiles", f"{workload}_expert_traffic.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
@@ -263,22 +281,106 @@ def summarize_stats(workload: str, paths, command: str) -> str:
         lines.append(f"| `{_short_kernel(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
                      f"{float(r['TotalDurationNs']) / 1e3:.0f} |")
-    f13 = [r for r in stats if "ffn13" in r["Name"]]
-    if f13:
-        calls = sum(int(r["Calls"]) for r in f13)
-        total = sum(float(r["TotalDurationNs"]) for r in f13)
-        lines += ["", f"ffn13 over all its instantiations: {calls} calls, average "
-                      f"{total / calls / 1e3:.1f} us per launch."]
+    lines.append("")
+    for kind, _ in EXPERT_KINDS:
+        ks = [r for r in stats if kind + "_" in r["Name"]]
+        if ks:
+            calls = sum(int(r["Calls"]) for r in ks)
+            total = sum(float(r["TotalDurationNs"]) for r in ks)
+            lines.append(f"{kind} over all its instantiations: {calls} calls, average "
+                         f"{total / calls / 1e3:.1f} us per launch.")
     if len(paths) > 1 and os.path.exists(paths[1]):
         with open(paths[1]) as fh:
             for line in fh:
                 if line.startswith("{") and '"roofline"' in line:
                     j = json.loads(line)
-                    lines.append(f"bench.py in the same run measured {j['roofline']['avg_launch_us']} us "
-                                 f"per ffn13 launch with HIP events inside its timed region.")
+                    r = j["roofline"]
+                    msg = (f"bench.py in the same run measured {r['avg_launch_us']} us per ffn13 "
+                           f"launch")
+                    if r.get("ffn2"):
+                        msg += f" and {r['ffn2']['avg_launch_us']} us per ffn2 launch"
+                    lines.append(msg + " with HIP events inside its timed region (those "
+                                 "launches run under the profiler too).")
     lines += ["Other kernels in the trace (torch RNG, casts, copies) are input generation, "
               "outside the timed region.", ""]
     path = os.path.join(ROOT, "profiles", f"{workload}_kernel_stats.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines))
+    return path
+
+
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F8",
+                 "SQ_INSTS_VALU_MFMA_MOPS_F6F4", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA",
+                 "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+N_CU, N_XCD = 256, 8
+
+
+def summarize_pmc(workload: str, paths, command: str) -> str:
+    """Matrix-core counters of the expert kernels, per dispatch: MFMA work
+    counted by the hardware (512 flops per MOPS unit) and MFMA busy cycles
+    against the cycles the GPU was active, with the expressions
+    rocprof-compute uses for gfx950 (GRBM_GUI_ACTIVE is summed over the 8
+    XCDs, so one XCD's active cycles are a eighth of it; each CU has 4 SIMDs
+    with one matrix core each).  The last path is a --kernel-trace --stats
+    directory of the same command, whose average durations turn counted
+    flops into a rate (counter runs serialise kernels, so their own
+    timestamps are not used)."""
+    import csv
+    import glob
+    *pmc_dirs, stats_dir = paths
+    rows = []
+    for d in pmc_dirs:
+        rows += _counter_rows(d)
+    files = glob.glob(os.path.join(stats_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {stats_dir}")
+    with open(files[0]) as fh:
+        stats = [r for r in csv.DictReader(fh) if "moe::" in r["Name"]]
+    peak = MFMA_PEAK_TFLOPS["mx_e4m3" if workload == "prefill_w8a8" else "bf16"]
+    lines = [f"# Matrix-core counters: {workload} workload (batches "
+             f"{', '.join(map(str, WORKLOAD_BATCHES[workload]))})", "",
+             "Commands (from the repository root, one MI355X), one counter pass each:", ""]
+    lines += [f"    {c}" for c in command.split(" ;; ")]
+    lines += ["", f"Kernel sources sha (bench.py kernel_source_sha): `{kernel_source_sha()}`", "",
+              "Per dispatch, averaged over the dispatches of each kind. flops = 512 x "
+              "(MOPS_BF16 + MOPS_F8 + MOPS_F6F4); util = 100 x MFMA_BUSY_CYCLES / "
+              f"(4 x {N_CU} CUs x GRBM_GUI_ACTIVE / {N_XCD}); rate = flops / the kernel's average "
+              f"duration in the stats run; frac = rate / {peak:.0f} TFLOP/s.", "",
+              "| kernel kind | dispatches | " + " | ".join(MFMA_COUNTERS) +
+              " | counted TFLOP | avg us (stats) | TFLOP/s | frac | MFMA busy % | GHz |",
+              "|---|---|" + "---|" * len(MFMA_COUNTERS) + "---|---|---|---|---|---|"]
+    for kind, _ in EXPERT_KINDS:
+        per = {}
+        clocks = []
+        for r in rows:
+            if kind + "_" not in r["Kernel_Name"] or r["Counter_Name"] not in MFMA_COUNTERS:
+                continue
+            per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            ns = float(r.get("End_Timestamp") or 0) - float(r.get("Start_Timestamp") or 0)
+            if r["Counter_Name"] == "GRBM_GUI_ACTIVE" and ns > 0:
+                clocks.append(float(r["Counter_Value"]) / N_XCD / ns)
+        if not per:
+            continue
+        n = max(len(v) for v in per.values())
+        mean = {c: (sum(per[c]) / len(per[c]) if c in per else None) for c in MFMA_COUNTERS}
+        mops = sum(mean[c] or 0.0 for c in MFMA_COUNTERS[:3])
+        flops = 512.0 * mops
+        ks = [r for r in stats if kind + "_" in r["Name"]]
+        us = (sum(float(r["TotalDurationNs"]) for r in ks) / sum(int(r["Calls"]) for r in ks) / 1e3
+              if ks else None)
+        rate = flops / (us * 1e-6) / 1e12 if us else None
+        util = (100.0 * mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (4 * N_CU * mean["GRBM_GUI_ACTIVE"] / N_XCD)
+                if mean.get("SQ_VALU_MFMA_BUSY_CYCLES") and mean.get("GRBM_GUI_ACTIVE") else None)
+        ghz = f"{sum(clocks) / len(clocks):.2f}" if clocks else "-"
+        cells = [f"{mean[c]:.4g}" if mean[c] is not None else "-" for c in MFMA_COUNTERS]
+        lines.append(f"| {kind} | {n} | " + " | ".join(cells) +
+                     f" | {flops / 1e12:.4f} | {us:.1f} | {rate:.1f} | {rate / peak:.3f} | "
+                     f"{util:.1f} | {ghz} |" if us and util is not None else
+                     f"| {kind} | {n} | " + " | ".join(cells) + f" | - | - | - | - | - | {ghz} |")
+    lines += ["", "GHz: one XCD's active cycles over the dispatch's duration in the counter run "
+              "(the clock the kernel ran at there). MFMA busy % counts against that clock, frac "
+              "against the published peak.", ""]
+    path = os.path.join(ROOT, "profiles", f"{workload}_mfma_counters.md")
     with open(path, "w") as f:
         f.write("\n".join(lines))
     return path
@@ -291,6 +393,9 @@ def main() -> int:
         return 0
     if args.summarize_stats:
         print(summarize_stats(args.workload, args.summarize_stats, args.command))
+        return 0
+    if args.summarize_pmc:
+        print(summarize_pmc(args.workload, args.summarize_pmc, args.command))
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the layer runs "
@@ -360,17 +465,23 @@ def main() -> int:
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done; timing {args.steps} steps")
 
-    # timed region: HIP events bracket only the dominant kernel (ffn13), on its stream
+    # timed region: the library's HIP events bracket the two expert kernels
+    # (ffn13 and ffn2) on the stream they run on; torch events on the same
+    # stream mark each step's boundaries (no synchronisation between steps)
     B.moe_timing_collect(reset=True)
-    B.moe_timing_enable(["ffn13"])
+    B.moe_timing_enable(["ffn13", "ffn2", "ffn_fused"])
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    marks[0].record()
+    for si in range(args.steps):
         step()
+        marks[si + 1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     B.moe_timing_enable(False)
     tim = B.moe_timing_collect(reset=True)
+    step_ms = [marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     tokens = sum(batches)
     value = tokens / (ms_per_step / 1e3)
@@ -379,20 +490,36 @@ def main() -> int:
 
     bytes_step = sum(w["bytes"] for w in work)
     flops_step = sum(w["flops"] for w in work)
-    f13_bytes_step = sum(w["ffn13_bytes"] for w in work)
-    f13_flops_step = sum(w["ffn13_flops"] for w in work)
-    f13_ms_step = ffn13_ms / args.steps
     mfma_bound = wl in ("prefill_bf16", "prefill_w8a8")
     compute = base.act_quant or base.w
-    if mfma_bound:
-        peak = MFMA_PEAK_TFLOPS[compute]
-        achieved = f13_flops_step / (f13_ms_step / 1e3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4)}
-    else:
-        achieved = f13_bytes_step / (f13_ms_step / 1e3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+
+    def kernel_roof(kind, ms_total, launches, kind_bytes, kind_flops):
+        """Achieved rate of one kernel kind over the timed steps."""
+        ms_step = ms_total / args.steps
+        if not launches or ms_step <= 0:
+            return None
+        if mfma_bound:
+            peak = MFMA_PEAK_TFLOPS[compute]
+            achieved = kind_flops / (ms_step / 1e3) / 1e12
+            r = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s"}
+        else:
+            peak = HBM_PEAK_GBS
+            achieved = kind_bytes / (ms_step / 1e3) / 1e9
+            r = {"bound": "hbm", "achieved": round(achieved, 1), "peak": peak, "unit": "GB/s"}
+        r["frac"] = round(achieved / peak, 4)
+        r["avg_launch_us"] = round(ms_total / launches * 1e3, 2)
+        r["launches"] = launches
+        return r
+
+    roof = kernel_roof("ffn13", ffn13_ms, ffn13_n, sum(w["ffn13_bytes"] for w in work),
+                       sum(w["ffn13_flops"] for w in work))
+    label = "ffn13 (grouped W13 + SiLU*mul)"
+    if roof is None:  # the persistent decode launch runs W13, W2 and the combine
+        roof = kernel_roof("ffn_fused", *tim.get("ffn_fused", (0.0, 0)),
+                           sum(w["ffn13_bytes"] + w["ffn2_bytes"] for w in work),
+                           sum(w["ffn13_flops"] + w["ffn2_flops"] for w in work))
+        label = "ffn_fused (W13 + SiLU*mul, W2 + gate, combine in one launch)"
+    achieved = roof["achieved"]
     # the chip's attainable rate for the same bound, measured here
     # (include/moe_bench.h): a streaming read in the weight-streaming pattern
     # over 1 GiB (past the 256 MB last-level cache), or the big tile's LDS-fed
@@ -410,12 +537,20 @@ def main() -> int:
         roof["frac_attainable"] = round(achieved / att, 4)
     except (RuntimeError, OSError) as e:
         log(f"attainable-rate probe unavailable: {e}")
+        att = None
         roof["attainable"] = roof["frac_attainable"] = None
-    roof["kernel"] = "ffn13 (grouped W13 + SiLU*mul)"
-    roof["avg_launch_us"] = round(ffn13_ms / max(ffn13_n, 1) * 1e3, 2)
-    roof["launches"] = ffn13_n
+    roof["kernel"] = label
     # the stored counters belong to the workload's own mode and schedule
-    roof["traffic"] = None if args.act_quant or args.schedule != "auto" else load_traffic(wl)
+    stored = None if args.act_quant or args.schedule != "auto" else load_traffic(wl)
+    roof["traffic"] = stored.get("ffn13") if stored else None
+    # the other expert kernel, timed in the same region
+    f2 = kernel_roof("ffn2", *tim.get("ffn2", (0.0, 0)), sum(w["ffn2_bytes"] for w in work),
+                     sum(w["ffn2_flops"] for w in work))
+    if f2 is not None:
+        f2["kernel"] = "ffn2 (grouped W2 + gate scale)"
+        f2["frac_attainable"] = round(f2["achieved"] / att, 4) if att else None
+        f2["traffic"] = stored.get("ffn2") if stored else None
+    roof["ffn2"] = f2
 
     # the same step as one recorded graph per forward (moe_graph_*): one
     # launch per forward, weights rotated through the same copies
@@ -496,12 +631,16 @@ def main() -> int:
                 "kernel_us": kern,
             })
 
+    prefill = None
+    if wl == "decode_bf16" and not args.no_prefill and not args.batches:
+        prefill = prefill_record(B, base, copies, dev, args, counter)
+
     cpu = None
     if not args.no_cpu_baseline and wl in CPU_SAMPLE:
         T_s, n_s = CPU_SAMPLE[wl]
         src = next((i for i in inputs if i.T == T_s), inputs[-1])
         log(f"timing the CPU oracle on {min(n_s, src.T)} tokens of T={src.T}")
-        cpu = cpu_baseline(src, min(n_s, src.T), wl)
+        cpu = cpu_baseline(src, min(n_s, src.T), wl, args.cpu_reps)
 
     line = {
         "metric": METRIC,
@@ -511,6 +650,7 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "step_ms_p10_p50_p90": [round(v / 1e3, 4) for v in _percentiles_us(step_ms)],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -534,11 +674,83 @@ def main() -> int:
         "graph_replay": {"ms_per_step": round(graph_ms_per_step, 4),
                          "tokens_per_s": round(tokens / (graph_ms_per_step / 1e3), 1)},
         "cpu_baseline": cpu,
+        "prefill": prefill,
         "per_batch": per_batch,
         "kernel_us_per_step": breakdown,
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+PREFILL_T = 4096
+
+
+def prefill_record(B, base, copies, dev, args, counter) -> dict:
+    """The prefill half of the metric on the decode layer's own weights: one
+    forward of T = 4096 tokens (x ~ N(0, 1), the prefill configuration; only
+    x differs from decode), timed like the main loop: K forwards after W
+    warm-up, the two expert kernels bracketed by the library's HIP events,
+    each forward by torch events, weights rotated through the same copies.
+    MFMA rates use the realised routing's flops (4 d I per slot for W13, 2 d I
+    for W2, plus the router's 2 d E per token for the layer)."""
+    import torch
+    from mixture_experts_moe_amd import synth
+    from dataclasses import replace
+    inp = replace(base, x=synth.make_x(PREFILL_T, base.d, base.act, 1.0, 0, dev))
+    out = torch.empty_like(inp.x)
+    desc = B.make_desc(inp.T, inp.d, inp.E, inp.I, B._act_code(inp.x), B._w_code(inp.w13))
+    ws = torch.empty(B.moe_workspace_bytes(desc, inp.top_k, True), dtype=torch.uint8, device=dev)
+    _, ids, _ = B.moe_route(inp.x, inp.w_gate, inp.top_k)
+    w = alg_work(inp, ids, inp.top_k)
+
+    def fw():
+        w13, w2 = copies[counter[0] % len(copies)]
+        counter[0] += 1
+        B.moe_forward(inp.x, inp.w_gate, w13, w2, inp.top_k, None, out, workspace=ws)
+
+    for _ in range(args.warmup):
+        fw()
+    torch.cuda.synchronize()
+    B.moe_timing_collect(reset=True)
+    B.moe_timing_enable(["ffn13", "ffn2"])
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    marks[0].record()
+    for si in range(args.steps):
+        fw()
+        marks[si + 1].record()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    B.moe_timing_enable(False)
+    tim = B.moe_timing_collect(reset=True)
+    fms = [marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
+    peak = MFMA_PEAK_TFLOPS["bf16"]
+    rec = {"T": PREFILL_T, "x_std": 1.0, "tokens_per_s": round(PREFILL_T / (ms / 1e3), 1),
+           "ms_per_forward": round(ms, 4), "forward_ms_p10_p50_p90":
+           [round(v / 1e3, 4) for v in _percentiles_us(fms)],
+           "touched_experts": w["touched_experts"], "peak": peak, "unit": "TFLOP/s",
+           "layer_TFLOPs": round(w["flops"] / (ms / 1e3) / 1e12, 1),
+           "layer_frac": round(w["flops"] / (ms / 1e3) / 1e12 / peak, 4)}
+    for kind in ("ffn13", "ffn2"):
+        k_ms, k_n = tim.get(kind, (0.0, 0))
+        if not k_n:
+            rec[kind] = None
+            continue
+        us = k_ms / k_n * 1e3
+        tf = w[kind + "_flops"] / (us * 1e-6) / 1e12
+        rec[kind] = {"bound": "mfma", "achieved": round(tf, 1), "frac": round(tf / peak, 4),
+                     "avg_launch_us": round(us, 1), "launches": k_n}
+    try:
+        att = B.bench_mfma_bf16(iters=4096, reps=4, device=dev)
+        rec["attainable"] = round(att, 1)
+        for kind in ("ffn13", "ffn2"):
+            if rec[kind]:
+                rec[kind]["frac_attainable"] = round(rec[kind]["achieved"] / att, 4)
+    except (RuntimeError, OSError) as e:
+        log(f"attainable-rate probe unavailable: {e}")
+        rec["attainable"] = None
+    log(f"prefill T={PREFILL_T}: {ms:.3f} ms/forward, ffn13 {rec['ffn13']}, ffn2 {rec['ffn2']}")
+    return rec
 
 
 def _percentiles_us(ms_list):
@@ -555,16 +767,17 @@ def _percentiles_us(ms_list):
 
 
 def load_traffic(workload: str):
-    """HBM bytes per ffn13 launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs,
-    if they were taken on the current expert-kernel sources (else null)."""
-    path = os.path.join(ROOT, "profiles", f"ffn13_{workload}_traffic.json")
+    """HBM bytes per ffn13 and per ffn2 launch ({"ffn13": B, "ffn2": B}) from
+    rocprofv3 FETCH_SIZE / WRITE_SIZE runs, if they were taken on the current
+    expert-kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_expert_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
     if t.get("kernel_source_sha") != kernel_source_sha(exclude=ROUTING_ONLY_SOURCES):
         return None
-    return t.get("traffic_bytes_per_launch")
+    return {kind: t[kind]["traffic_bytes_per_launch"] for kind, _ in EXPERT_KINDS if kind in t}
 
 
 if __name__ == "__main__":

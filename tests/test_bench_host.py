@@ -1,6 +1,7 @@
 """Host-side logic of bench.py that needs no GPU: the single-GPU refusal,
-and the HBM-traffic summary that fills the bench line's roofline.traffic
-(counter values in KiB per dispatch, scaled by a plain copy's reading)."""
+the HBM-traffic summary that fills the bench line's roofline.traffic
+(counter values in KiB per dispatch, scaled by a plain copy's reading), and
+the matrix-core counter summary."""
 
 import csv
 import json
@@ -39,6 +40,7 @@ def test_traffic_summary_scales_by_the_copy_calibration(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "kernel_source_sha", lambda exclude=(): "cafe")
     os.makedirs(tmp_path / "profiles")
     k13 = "void moe::ffn13_gemm_kernel<unsigned short, 128, 2, 1, 4, true>(int)"
+    k2 = "void moe::ffn2_gemm_kernel<unsigned short, 128, 2, 1, 4>(int)"
     cal = bench.COPY_CAL_BYTES
     # the copy of `cal` bytes reads cal/2 KiB-units on FETCH_SIZE (factor 2)
     # and cal on WRITE_SIZE (factor 1); other kernels are ignored
@@ -53,22 +55,30 @@ def test_traffic_summary_scales_by_the_copy_calibration(tmp_path, monkeypatch):
              Counter_Value=1000.0),
         dict(Dispatch_Id=7, Kernel_Name=k13, Grid_Size=256, Counter_Name="FETCH_SIZE",
              Counter_Value=3000.0),
+        dict(Dispatch_Id=4, Kernel_Name=k2, Grid_Size=128, Counter_Name="FETCH_SIZE",
+             Counter_Value=500.0),
         dict(Dispatch_Id=5, Kernel_Name="void moe::combine_kernel<float>(int)", Grid_Size=64,
              Counter_Name="FETCH_SIZE", Counter_Value=9e9)])
     w = _counters(tmp_path / "w", [
         dict(Dispatch_Id=3, Kernel_Name=k13, Grid_Size=256, Counter_Name="WRITE_SIZE",
              Counter_Value=10.0),
+        dict(Dispatch_Id=4, Kernel_Name=k2, Grid_Size=128, Counter_Name="WRITE_SIZE",
+             Counter_Value=64.0),
         dict(Dispatch_Id=7, Kernel_Name=k13, Grid_Size=256, Counter_Name="WRITE_SIZE",
              Counter_Value=30.0)])
-    path = bench.summarize_traffic("skew", [f, w, cf, cw], "cmd")
+    path = bench.summarize_traffic("skew", [f, w, cf, cw], "the command")
     t = json.load(open(path))
+    assert t["command"] == "the command"
     assert t["calibration"]["FETCH_SIZE_bytes_per_counted_byte"] == 2.0
     assert t["calibration"]["WRITE_SIZE_bytes_per_counted_byte"] == 1.0
-    assert [r["fetch_bytes"] for r in t["launches"]] == [2 * 1000 * 1024, 2 * 3000 * 1024]
-    assert [r["write_bytes"] for r in t["launches"]] == [10 * 1024, 30 * 1024]
-    assert t["traffic_bytes_per_launch"] == (2 * 4000 * 1024 + 40 * 1024) // 2
+    t13, t2 = t["ffn13"], t["ffn2"]
+    assert [r["fetch_bytes"] for r in t13["launches"]] == [2 * 1000 * 1024, 2 * 3000 * 1024]
+    assert [r["write_bytes"] for r in t13["launches"]] == [10 * 1024, 30 * 1024]
+    assert t13["traffic_bytes_per_launch"] == (2 * 4000 * 1024 + 40 * 1024) // 2
+    assert t2["traffic_bytes_per_launch"] == 2 * 500 * 1024 + 64 * 1024
     # read back only while the sources are the ones the counters were taken on
-    assert bench.load_traffic("skew") == t["traffic_bytes_per_launch"]
+    assert bench.load_traffic("skew") == {"ffn13": t13["traffic_bytes_per_launch"],
+                                          "ffn2": t2["traffic_bytes_per_launch"]}
     monkeypatch.setattr(bench, "kernel_source_sha", lambda exclude=(): "beef")
     assert bench.load_traffic("skew") is None
 
@@ -91,3 +101,37 @@ def test_traffic_summary_rejects_mismatched_runs(tmp_path, monkeypatch):
                                         Counter_Name="WRITE_SIZE", Counter_Value=1.0)])
     with pytest.raises(SystemExit):
         bench.summarize_traffic("skew", [f, w, cf, cw], "cmd")
+
+
+def test_matrix_core_summary(tmp_path, monkeypatch):
+    """Counted flops (512 per MOPS unit) over the stats run's average
+    duration, and MFMA busy cycles over 4 SIMDs x 256 CUs x one XCD's active
+    cycles (GRBM_GUI_ACTIVE summed over 8 XCDs)."""
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_sha", lambda exclude=(): "cafe")
+    os.makedirs(tmp_path / "profiles")
+    k13 = "void moe::ffn13_big_kernel<unsigned short>(int)"
+    vals = {"SQ_INSTS_VALU_MFMA_MOPS_BF16": 2e9, "SQ_INSTS_VALU_MFMA_MOPS_F8": 0.0,
+            "SQ_INSTS_VALU_MFMA_MOPS_F6F4": 0.0, "SQ_VALU_MFMA_BUSY_CYCLES": 4 * 256 * 1000.0 * 0.5,
+            "SQ_INSTS_MFMA": 1e6, "SQ_BUSY_CYCLES": 1.0, "GRBM_GUI_ACTIVE": 8 * 1000.0}
+    pm = _counters(tmp_path / "pm", [dict(Dispatch_Id=1, Kernel_Name=k13, Grid_Size=1,
+                                          Counter_Name=c, Counter_Value=v)
+                                     for c, v in vals.items()])
+    st = tmp_path / "st"
+    os.makedirs(st)
+    with open(st / "kt_kernel_stats.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Name", "Calls", "TotalDurationNs", "AverageNs",
+                                          "MinNs", "MaxNs"])
+        w.writeheader()
+        w.writerow(dict(Name=k13, Calls=2, TotalDurationNs=2 * 1024e3, AverageNs=1024e3,
+                        MinNs=1024e3, MaxNs=1024e3))
+    path = bench.summarize_pmc("prefill_bf16", [pm, str(st)], "cmd one ;; cmd two")
+    text = open(path).read()
+    assert "    cmd one" in text and "    cmd two" in text
+    row = next(l for l in text.splitlines() if l.startswith("| ffn13 |"))
+    cells = [c.strip() for c in row.strip("|").split("|")]
+    flops = 512 * 2e9
+    assert float(cells[-6]) == pytest.approx(flops / 1e12, rel=1e-3)
+    assert float(cells[-5]) == pytest.approx(1024.0)
+    assert float(cells[-4]) == pytest.approx(flops / 1024e-6 / 1e12, rel=1e-3)
+    assert float(cells[-2]) == pytest.approx(50.0)
