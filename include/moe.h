@@ -118,9 +118,12 @@ extern "C" {
  * whose workgroups take W13 tiles, then W2 tiles (each once the W13 tiles it
  * reads are done), from one ticket counter, and add up each token's slots as
  * soon as its last partial lands.  MOE_SCHED_AUTO (0) is the queue for 128-token
- * blocks and the three launches on the decode path, where the persistent
- * kernel is slower (every W13 tile has to publish its rows at device scope
- * before a W2 tile on another XCD may read them).  The two give
+ * blocks and, on the decode path, the three launches, except that for at
+ * most two row blocks of 16 (one token of a top-2 layer) W2 adds up each
+ * token's slots itself (two launches: the last W2 workgroup to finish a
+ * token's channel group sums its partials).  The persistent kernel is
+ * slower there (every W13 tile has to publish its rows at device scope
+ * before a W2 tile on another XCD may read them).  All of these give
  * bit-identical outputs; other paths ignore the field. */
 #define MOE_SCHED_AUTO 0
 #define MOE_SCHED_STATIC 1

@@ -107,7 +107,8 @@ struct Plan {
   size_t rpart;  // the split router's partial tiles (layer path, few tokens), or 0
   bool rsplit;
   bool fused;    // W13, W2 and combine as one persistent launch (layer path, decode)
-  size_t fcnt;   // its counters
+  bool w2c;      // W2 with the combine in its launch (layer path, decode)
+  size_t fcnt;   // counters of either, cleared by the routing launch
   int nfcnt;
 };
 
@@ -243,6 +244,7 @@ void make_plan(const moe_desc* d, int top_k, bool with_routing, Plan* p) {
   }
   p->qcnt = p->queue ? take(moe::gemm_queue_ints() * 4) : 0;
   p->fused = false;
+  p->w2c = false;
   p->fcnt = 0;
   p->nfcnt = 0;
   if (with_routing) {
@@ -267,6 +269,22 @@ void make_plan(const moe_desc* d, int top_k, bool with_routing, Plan* p) {
       p->nfcnt = moe::fused_counter_ints(a);
       p->fcnt = take(static_cast<size_t>(p->nfcnt) * 4);
       p->fused = true;
+    } else if (p->rsplit && p->A > 0 && d->schedule == MOE_SCHED_AUTO && !p->act_mx &&
+               p->act == MOE_DTYPE_BF16 &&
+               moe::dma_stream_use(p->wdt, p->act, p->B, p->d, p->I, blocks_est) &&
+               moe::ffn2_combine_pays(p->wdt, p->B, blocks_est) &&
+               p->d % moe::dma_w2_channels(p->wdt, p->B, blocks_est) == 0) {
+      FfnArgs a{};
+      a.T = p->T;
+      a.d = p->d;
+      a.E = p->E;
+      a.A = p->A;
+      a.B = p->B;
+      a.cap = p->cap;
+      a.w_dtype = p->wdt;
+      p->nfcnt = moe::ffn2_combine_ints(a);
+      p->fcnt = take(static_cast<size_t>(p->nfcnt) * 4);
+      p->w2c = true;
     }
   }
   p->total = p->T == 0 ? 0 : off;  // nothing runs for T = 0
@@ -373,6 +391,8 @@ hipError_t run_ffn(const FfnArgs& a, hipStream_t s) {
   if (a.act_mx) e = timed(MOE_KERNEL_QUANT_X, s, [&] { return moe::launch_quantize_x(a, s); });
   if (e == hipSuccess && a.queue_sched && !a.queue_zeroed) e = moe::launch_gemm_queue_reset(a, s);
   if (e == hipSuccess) e = timed(MOE_KERNEL_FFN13, s, [&] { return moe::launch_ffn13(a, s); });
+  if (e == hipSuccess && a.combine_cnt)  // W2 adds up each token's slots itself
+    return timed(MOE_KERNEL_FFN2, s, [&] { return moe::launch_ffn2_combine_dma(a, s); });
   if (e == hipSuccess) e = timed(MOE_KERNEL_FFN2, s, [&] { return moe::launch_ffn2(a, s); });
   if (e == hipSuccess) e = timed(MOE_KERNEL_COMBINE, s, [&] { return moe::launch_combine(a, s); });
   return e;
@@ -611,7 +631,7 @@ static int enqueue_forward(const Plan& p, const void* x, const float* w_gate, co
   int32_t* block_exp = reinterpret_cast<int32_t*>(ws + p.block_exp);
 
   int32_t* queue = p.queue ? reinterpret_cast<int32_t*>(ws + p.qcnt) : nullptr;
-  int32_t* fcnt = p.fused ? reinterpret_cast<int32_t*>(ws + p.fcnt) : nullptr;
+  int32_t* fcnt = p.fused || p.w2c ? reinterpret_cast<int32_t*>(ws + p.fcnt) : nullptr;
   bool zeroed = false;
   void* part = p.rsplit ? ws + p.rpart : nullptr;
   const hipError_t e = route_align(p, x, w_gate, logits, ids, gates, counts, sorted, block_exp,
@@ -619,7 +639,8 @@ static int enqueue_forward(const Plan& p, const void* x, const float* w_gate, co
   if (e != hipSuccess) return MOE_ERR_HIP;
   FfnArgs a = ffn_args(p, x, w13, w2, scales, gates, sorted, block_exp, num_padded, out, ws);
   a.queue_zeroed = zeroed;
-  a.fused_cnt = fcnt;
+  a.fused_cnt = p.fused ? fcnt : nullptr;
+  a.combine_cnt = p.w2c ? fcnt : nullptr;
   return to_status(run_ffn(a, s));
 }
 

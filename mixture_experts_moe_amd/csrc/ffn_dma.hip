@@ -339,7 +339,20 @@ __global__ __launch_bounds__(kDmaThreads) void ffn13_dma_kernel(
 // for the block's real slots f.  RN tiles per wave: every wave reads all h
 // rows of its block, so wider waves read less h per weight byte.
 
-template <typename WT, int NS, int P, int RN>
+// Device-scope store of four floats: agent-scope atomic stores, which the
+// gfx950 memory model issues with the device-coherence bit (sc1) so they
+// write through this XCD's L2; readers on other XCDs use agent-scope atomic
+// loads.
+__device__ __forceinline__ void store_device4(float* p, const float4& o) {
+  __hip_atomic_store(p + 0, o.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(p + 1, o.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(p + 2, o.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(p + 3, o.w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// kDevice: partials written with store_device4 (for a reader in the same
+// launch on another XCD) instead of plain stores.
+template <typename WT, int NS, int P, int RN, bool kDevice = false>
 __device__ __forceinline__ void dma2_tile(
     const bf16_t* __restrict__ h, const WT* __restrict__ w2, const float* __restrict__ s2,
     int scale_mode, const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
@@ -389,7 +402,10 @@ __device__ __forceinline__ void dma2_tile(
           o.y = acc[s][rt][1] * load_scale(s2, scale_mode, e, static_cast<size_t>(e) * d + nb + 1) * gate;
           o.z = acc[s][rt][2] * load_scale(s2, scale_mode, e, static_cast<size_t>(e) * d + nb + 2) * gate;
           o.w = acc[s][rt][3] * load_scale(s2, scale_mode, e, static_cast<size_t>(e) * d + nb + 3) * gate;
-          *reinterpret_cast<float4*>(yrow + nb) = o;
+          if constexpr (kDevice)
+            store_device4(yrow + nb, o);
+          else
+            *reinterpret_cast<float4*>(yrow + nb) = o;
         }
       }
     }
@@ -409,6 +425,131 @@ __global__ __launch_bounds__(kDmaThreads) void ffn2_dma_kernel(
   if (b * 16 * NS >= *num_padded) return;
   dma2_tile<WT, NS, P, RN>(h, w2, s2, scale_mode, topk_w, sorted_ids, block_expert, y_part, d,
                            I, A, ksplit, b, blockIdx.y * 16 * RN, blockIdx.z, ring);
+}
+
+// ------------------------------------------------------------ combine in the W2 launch
+// The combine's sum for one token and one group of 16 RN channels: every
+// slot of the token, each slot's K splits in order (the order of
+// combine_kernel, so the bits are the same), rounded to bf16 once.
+
+__device__ __forceinline__ void store_bf16x4(bf16_t* p, float4 v) {
+  const uint32_t lo = f32_to_bf16(v.x) | (static_cast<uint32_t>(f32_to_bf16(v.y)) << 16);
+  const uint32_t hi = f32_to_bf16(v.z) | (static_cast<uint32_t>(f32_to_bf16(v.w)) << 16);
+  *reinterpret_cast<uint2*>(p) = uint2{lo, hi};
+}
+
+// kDevice: the partials were written with store_device4 and are read with
+// agent-scope atomic loads; else the caller has made them visible (an
+// acquire fence after the writers' release) and plain loads read them.
+template <bool kDevice>
+__device__ __forceinline__ float4 load_partial4(const float* p) {
+  if constexpr (kDevice)
+    return float4{__hip_atomic_load(p + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                  __hip_atomic_load(p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                  __hip_atomic_load(p + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                  __hip_atomic_load(p + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)};
+  else
+    return *reinterpret_cast<const float4*>(p);
+}
+
+// After a W2 tile (row block `blk`, channel group dt of nd, 16 RN channels)
+// has written its partials: one arrival per real slot on the counter of the
+// slot's (token, channel group); the wave whose arrival is a counter's
+// k * splits-th adds up that token's partials and writes its 16 RN outputs.
+// The caller makes the tile's partials visible to other workgroups before
+// this counts its arrivals.
+template <int NS, int RN, bool kDevice>
+__device__ __forceinline__ void arrive_and_combine(const int32_t* blk, int32_t* arrive,
+                                                   const float* y_part, bf16_t* out, int A, int k,
+                                                   int splits, int d, int nd, int dt) {
+  const int lane = threadIdx.x & 63;
+  const int total = k * splits;
+  uint64_t last = 0;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    int mine = 0;
+    if (lane < 16) {
+      const int f = blk[16 * s + lane];
+      if (f < A) {
+        const int prev = __hip_atomic_fetch_add(arrive + (f / k) * nd + dt, 1, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+        mine = prev == total - 1;
+      }
+    }
+    last |= static_cast<uint64_t>(__ballot(mine)) << (16 * s);
+  }
+  if (last == 0) return;
+  if constexpr (kDevice)
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");  // loads stay after the counters
+  else
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the other tiles' partials
+  constexpr int kGroups = 4 * RN;  // float4 groups of the 16 RN channels
+  while (last) {
+    const int bit = __builtin_ctzll(last);
+    last &= last - 1;
+    const int tok = blk[16 * (bit / 16) + bit % 16] / k;
+    if (lane < kGroups) {
+      const int c = dt * 16 * RN + 4 * lane;
+      float4 o = {0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < k; ++j) {
+        const size_t f = static_cast<size_t>(tok) * k + j;
+        float4 sj = {0.f, 0.f, 0.f, 0.f};
+        // kBatch splits' loads in flight before their adds (each load is a
+        // round trip past the L2), added in split order
+        constexpr int kBatch = 8;
+        for (int z0 = 0; z0 < splits; z0 += kBatch) {
+          float4 q[kBatch];
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u)
+            if (z0 + u < splits)
+              q[u] = load_partial4<kDevice>(y_part + (static_cast<size_t>(z0 + u) * A + f) * d + c);
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u) {
+            if (z0 + u < splits) {
+              sj.x += q[u].x;
+              sj.y += q[u].y;
+              sj.z += q[u].z;
+              sj.w += q[u].w;
+            }
+          }
+        }
+        o.x += sj.x;
+        o.y += sj.y;
+        o.z += sj.z;
+        o.w += sj.w;
+      }
+      store_bf16x4(out + static_cast<size_t>(tok) * d + c, o);
+    }
+  }
+}
+
+// W2 + gate scale and the combine in one launch (grid as ffn2_dma_kernel).
+// Each tile writes its partials with device-scope stores, waits until they
+// are acknowledged (s_waitcnt vmcnt(0): on gfx950 a store's count drops once
+// it is visible at its scope), then counts its arrivals; the last tile for a
+// token's channel group reads the partials with device-scope loads.  So no
+// tile writes back or invalidates an L2 (the agent-scope fences would), and
+// the combine launch and its re-read of the partials are gone.  The counters
+// (arrive[T][d / (16 RN)]) start at zero: the routing launch clears them.
+template <typename WT, int NS, int P, int RN>
+__global__ __launch_bounds__(kDmaThreads) void ffn2_combine_dma_kernel(
+    const bf16_t* __restrict__ h, const WT* __restrict__ w2, const float* __restrict__ s2,
+    int scale_mode, const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
+    const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded,
+    float* __restrict__ y_part, int d, int I, int A, int ksplit, int k, int splits,
+    int32_t* __restrict__ arrive, bf16_t* __restrict__ out) {
+  using G = DmaGeom<WT, RN, NS>;
+  DMA_RING(ring, G::kStageBytes, P);
+  const int b = blockIdx.x;
+  if (b * 16 * NS >= *num_padded) return;
+  dma2_tile<WT, NS, P, RN, true>(h, w2, s2, scale_mode, topk_w, sorted_ids, block_expert, y_part,
+                                 d, I, A, ksplit, b, blockIdx.y * 16 * RN, blockIdx.z, ring);
+  // the compiler keeps the counters after the stores; the wait makes the
+  // stores complete first
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  arrive_and_combine<NS, RN, true>(sorted_ids + static_cast<size_t>(b) * 16 * NS, arrive, y_part,
+                                   out, A, k, splits, d, gridDim.y, blockIdx.y);
 }
 
 // ------------------------------------------------------------ fused W13 -> W2 -> combine
@@ -441,15 +582,6 @@ constexpr int kFusedDone = 64;
 
 static int fused_counter_words(int T, int cap, int B, int splits, int d, int rn) {
   return kFusedDone + (cap / B) * splits + T * (d / (16 * rn));
-}
-
-template <typename OT>
-__device__ __forceinline__ void fused_store4(OT* p, float4 v);
-template <>
-__device__ __forceinline__ void fused_store4<bf16_t>(bf16_t* p, float4 v) {
-  const uint32_t lo = f32_to_bf16(v.x) | (static_cast<uint32_t>(f32_to_bf16(v.y)) << 16);
-  const uint32_t hi = f32_to_bf16(v.z) | (static_cast<uint32_t>(f32_to_bf16(v.w)) << 16);
-  *reinterpret_cast<uint2*>(p) = uint2{lo, hi};
 }
 
 struct FusedParams {
@@ -529,54 +661,8 @@ __global__ __launch_bounds__(kDmaThreads) void ffn_fused_dma_kernel(FusedParams 
                                 p.block_expert, p.y_part, p.d, p.I, p.A, p.ksplit, b,
                                 dt * 16 * RN, z, ring);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // this tile's partials, device-wide
-      // one arrival per real slot; the last one for a token's channel group
-      // adds up that token's partials
-      const int32_t* blk = p.sorted_ids + static_cast<size_t>(b) * B;
-      const int total = p.k * p.splits;
-      uint64_t last = 0;
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        int mine = 0;
-        if (lane < 16) {
-          const int f = blk[16 * s + lane];
-          if (f < p.A) {
-            const int prev = __hip_atomic_fetch_add(arrive + (f / p.k) * nd + dt, 1,
-                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            mine = prev == total - 1;
-          }
-        }
-        last |= static_cast<uint64_t>(__ballot(mine)) << (16 * s);
-      }
-      if (last != 0) {
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the other tiles' partials
-        constexpr int kGroups = 4 * RN;  // float4 groups of the 16 RN channels
-        while (last) {
-          const int bit = __builtin_ctzll(last);
-          last &= last - 1;
-          const int tok = blk[16 * (bit / 16) + bit % 16] / p.k;
-          if (lane < kGroups) {
-            const int c = dt * 16 * RN + 4 * lane;
-            float4 o = {0.f, 0.f, 0.f, 0.f};
-            for (int j = 0; j < p.k; ++j) {
-              const size_t f = static_cast<size_t>(tok) * p.k + j;
-              float4 sj = {0.f, 0.f, 0.f, 0.f};
-              for (int zz = 0; zz < p.splits; ++zz) {
-                const float4 q = *reinterpret_cast<const float4*>(
-                    p.y_part + (static_cast<size_t>(zz) * p.A + f) * p.d + c);
-                sj.x += q.x;
-                sj.y += q.y;
-                sj.z += q.z;
-                sj.w += q.w;
-              }
-              o.x += sj.x;
-              o.y += sj.y;
-              o.z += sj.z;
-              o.w += sj.w;
-            }
-            fused_store4<bf16_t>(p.out + static_cast<size_t>(tok) * p.d + c, o);
-          }
-        }
-      }
+      arrive_and_combine<NS, RN, false>(p.sorted_ids + static_cast<size_t>(b) * B, arrive,
+                                        p.y_part, p.out, p.A, p.k, p.splits, p.d, nd, dt);
     }
   }
 }
@@ -651,6 +737,16 @@ bool dma_args_ok(const FfnArgs& a) {
          (a.w_dtype == kDtypeBF16 || a.w_dtype == kDtypeE4M3FN);
 }
 
+template <typename WT, int NS, int P, int RN = sizeof(WT) == 1 ? kDma2RNFp8 : kDma2RN>
+hipError_t ffn2_combine_dma_go(const FfnArgs& a, hipStream_t s) {
+  const dim3 grid(a.cap / a.B, a.d / (16 * RN), a.splits);
+  ffn2_combine_dma_kernel<WT, NS, P, RN><<<grid, kDmaThreads, 0, s>>>(
+      static_cast<const bf16_t*>(a.h), static_cast<const WT*>(a.w2), a.s2, a.scale_mode,
+      a.topk_w, a.sorted_ids, a.block_expert, a.num_padded, a.y_part, a.d, a.I, a.A, a.ksplit,
+      a.k, a.splits, a.combine_cnt, static_cast<bf16_t*>(a.out));
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_ffn13_dma(const FfnArgs& a, hipStream_t s) {
@@ -684,6 +780,31 @@ hipError_t launch_ffn2_dma(const FfnArgs& a, hipStream_t s) {
     case 32: return ffn2_dma_go<bf16_t, 2, MOE_DMA2_P2>(a, s);
   }
   return hipErrorInvalidValue;
+}
+
+// Each tile of the W2 + combine kernel waits for its partials to be
+// acknowledged before it counts them, and the counting and the last tile's
+// combine add latency to every tile: it pays only where the W2 grid is one
+// round of the chip and the combine launch is a large share of the layer,
+// a single token of a top-2 bf16 layer (d = 4096, I = 14336: 137.2 ->
+// 134.7 us per forward).  With more tiles it loses (T = 8: 453 against 451;
+// T = 64: 556 against 504; e4m3fn weights at T = 1: 94.6 against 90.6 us;
+// T = 64: 1.95 against 1.61 ms).
+bool ffn2_combine_pays(int w_dtype, int B, int64_t blocks_est) {
+  return w_dtype == kDtypeBF16 && dma_w2_rn(w_dtype, B, blocks_est) == kDma2WideRN;
+}
+
+int ffn2_combine_ints(const FfnArgs& a) {
+  return a.T * (a.d / dma_w2_channels(a.w_dtype, a.B, ffn_blocks_estimate(a.cap, a.B, a.E, a.A)));
+}
+
+hipError_t launch_ffn2_combine_dma(const FfnArgs& a, hipStream_t s) {
+  const int64_t blocks = ffn_blocks_estimate(a.cap, a.B, a.E, a.A);
+  if (!a.combine_cnt || !dma_args_ok(a) || !dma_stream_use(a) ||
+      !ffn2_combine_pays(a.w_dtype, a.B, blocks) || a.ksplit % dma_stream_kc(a.w_dtype) != 0 ||
+      a.d % dma_w2_channels(a.w_dtype, a.B, blocks) != 0)
+    return hipErrorInvalidValue;
+  return ffn2_combine_dma_go<bf16_t, 1, kDma2WideP, kDma2WideRN>(a, s);
 }
 
 // ------------------------------------------------------------ fused launcher

@@ -95,6 +95,10 @@ struct FfnArgs {
   // its counters (fused_counter_ints()), zeroed by the routing launch; null
   // when the expert kernels run as separate launches.
   int32_t* fused_cnt;
+  // W2 with the combine in its launch (LDS-streaming path): arrival counters
+  // (ffn2_combine_ints() int32), zeroed by the routing launch; null when the
+  // combine is a launch of its own.
+  int32_t* combine_cnt;
 };
 
 hipError_t launch_ffn13(const FfnArgs& a, hipStream_t s);
@@ -159,6 +163,12 @@ hipError_t launch_ffn13_dma(const FfnArgs& a, hipStream_t s);
 // output channels per W2 workgroup of that path for a block size and block estimate
 int dma_w2_channels(int w_dtype, int B, int64_t blocks_est);
 hipError_t launch_ffn2_dma(const FfnArgs& a, hipStream_t s);
+// W2 + gate scale with the combine folded in (same path, bf16 output):
+// needs a.combine_cnt with ffn2_combine_ints() zeroed counters.  The layer
+// uses it where ffn2_combine_pays() (measured faster than the two launches).
+bool ffn2_combine_pays(int w_dtype, int B, int64_t blocks_est);
+int ffn2_combine_ints(const FfnArgs& a);
+hipError_t launch_ffn2_combine_dma(const FfnArgs& a, hipStream_t s);
 
 // The fused decode kernel: bf16 activations and weights on the
 // LDS-streaming path (blocks of 16 or 32).  fused_counter_ints() is the

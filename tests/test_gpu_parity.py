@@ -610,10 +610,10 @@ FUSED_CASES = [
 @pytest.mark.parametrize("T,over", FUSED_CASES, ids=[f"T{c[0]}-{'full' if c[1] is None else 'small'}"
                                                      for c in FUSED_CASES])
 def test_fused_decode_equals_separate_launches(decode_inputs, T, over):
-    """The persistent W13 -> W2 -> combine launch (schedule queue) against
-    the three separate launches (schedules static and auto): bit-identical
-    outputs, one fused launch instead of three; and the oracle on the fused
-    output."""
+    """The decode path's three ways of running W13, W2 and the combine give
+    bit-identical outputs: three launches (schedule static), W13 then W2
+    with the combine folded in (auto), one persistent launch (queue); and
+    the oracle on the fused output."""
     note(f"fused decode T={T} {over}")
     if over is None:
         cfg = synth.WORKLOADS["decode_bf16"]
@@ -627,10 +627,55 @@ def test_fused_decode_equals_separate_launches(decode_inputs, T, over):
     dflt, n_a = _launches(lambda: run("auto"))
     torch.cuda.synchronize()
     assert n_f["ffn_fused"] == 1 and n_f["ffn13"] == n_f["ffn2"] == n_f["combine"] == 0, n_f
-    for n in (n_s, n_a):
-        assert n["ffn_fused"] == 0 and n["ffn13"] == n["ffn2"] == n["combine"] == 1, n
+    assert n_s["ffn_fused"] == 0 and n_s["ffn13"] == n_s["ffn2"] == n_s["combine"] == 1, n_s
+    # auto folds the combine into W2 for a single token (two row blocks)
+    folded = 1 if T == 1 else 0
+    assert n_a["ffn_fused"] == 0 and n_a["ffn13"] == n_a["ffn2"] == 1, n_a
+    assert n_a["combine"] == 1 - folded, n_a
     assert torch.equal(fused, sep) and torch.equal(dflt, sep)
     _full_case(inp, np.arange(T) if T <= 16 else None, out=fused)
+
+
+W2C_CASES = [(1, None), (1, dict(d=512, I=8192, E=8, k=2)), (2, dict(d=256, I=8192, E=4, k=1)),
+             (1, dict(d=1024, I=16384, E=2, k=2)), (1, dict(d=768, I=8192, E=16, k=2))]
+
+
+@pytest.mark.parametrize("T,over", W2C_CASES,
+                         ids=[f"T{c[0]}-{'full' if c[1] is None else c[1]['d']}" for c in W2C_CASES])
+def test_w2_with_combine(decode_inputs, T, over):
+    """At most two row blocks of 16 (a single token of a top-2 layer): W2
+    adds up each token's slots in its own launch (auto), bit-identical to W2
+    then the combine launch (static), and the oracle's result."""
+    note(f"w2+combine T={T} {over}")
+    if over is None:
+        cfg = synth.WORKLOADS["decode_bf16"]
+        inp = with_x(decode_inputs, synth.make_x(T, cfg["d"], "bf16", cfg["x_std"], 5, DEV))
+    else:
+        inp = synth.make_inputs("decode_bf16", T=T, device=DEV, x_std=1.0, **over)
+    run = lambda sched: B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k,
+                                      schedule=sched)
+    dflt, n_a = _launches(lambda: run("auto"))
+    sep, n_s = _launches(lambda: run("static"))
+    torch.cuda.synchronize()
+    assert n_a["combine"] == 0 and n_a["ffn2"] == 1, n_a
+    assert n_s["combine"] == 1 and n_s["ffn2"] == 1, n_s
+    assert torch.equal(dflt, sep)
+    _full_case(inp, np.arange(T), out=dflt)
+
+
+def test_w2_with_combine_back_to_back(decode_inputs):
+    """The default decode path on one shared workspace for batches of
+    different sizes in a row (W2 adds up the slots at T = 1): each call's
+    arrival counters start from zero."""
+    cfg = synth.WORKLOADS["decode_bf16"]
+    desc = B.make_desc(64, cfg["d"], cfg["E"], cfg["I"], B.MOE_DTYPE_BF16, B.MOE_DTYPE_BF16)
+    ws = torch.empty(B.moe_workspace_bytes(desc, cfg["k"], True), dtype=torch.uint8, device=DEV)
+    for T in (64, 1, 32, 8, 64, 1, 17):
+        inp = with_x(decode_inputs, synth.make_x(T, cfg["d"], "bf16", cfg["x_std"], 100 + T, DEV))
+        got = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, workspace=ws)
+        ref = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, schedule="static")
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), f"T={T}"
 
 
 def test_fused_decode_back_to_back_and_in_a_graph(decode_inputs):
