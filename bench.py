@@ -578,26 +578,35 @@ def main() -> int:
     breakdown = None
     per_batch = []
     if not args.no_breakdown:
-        # second pass, same number of forwards per batch: every kernel kind
-        # timed with HIP events, batch by batch, plus each whole forward
+        # second pass, batch by batch, K forwards each, one at a time
+        # (synchronised): the whole forward between two torch events; then K
+        # more with every kernel kind timed by the library's HIP events (the
+        # breakdown; those events are kept out of the forward times)
         breakdown = {}
         for bi, (i, w) in enumerate(zip(inputs, work)):
             ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            B.moe_timing_collect(reset=True)
-            B.moe_timing_enable(True)
-            fw = 0.0
-            fws = []
-            for _ in range(args.steps):
+
+            def one():
                 w13, w2 = copies[counter[0] % len(copies)]
                 counter[0] += 1
-                ev0.record()
                 B.moe_forward(i.x, i.w_gate, w13, w2, i.top_k, sc, outs[bi], block_m=args.block_m,
                               workspace=wss[bi], act_quant=i.act_quant,
                               schedule=args.schedule)
+
+            fw = 0.0
+            fws = []
+            for _ in range(args.steps):
+                ev0.record()
+                one()
                 ev1.record()
                 torch.cuda.synchronize()
                 fws.append(ev0.elapsed_time(ev1))
                 fw += fws[-1]
+            B.moe_timing_collect(reset=True)
+            B.moe_timing_enable(True)
+            for _ in range(args.steps):
+                one()
+                torch.cuda.synchronize()
             B.moe_timing_enable(False)
             t2 = B.moe_timing_collect(reset=True)
             # one forward at a time, as a single graph launch

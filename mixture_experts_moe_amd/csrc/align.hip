@@ -23,6 +23,17 @@
 // thread and 256 threads it took 32); small batches keep 256 threads, which
 // start sooner.
 // Workgroup 0 also writes counts, the padded total and the tail past it.
+//
+// That costs E passes over the slots.  For large E * A a counting
+// sort over slot tiles takes over (align_tiles_kernel): one workgroup per
+// tile of consecutive slots; each builds the histogram of all slots and of
+// the slots before its tile (a pass over the ids, which are 4 bytes a slot),
+// so that it knows every expert's group offset and where its tile's slots of
+// each expert start, then places its tile's slots 1024 at a time: a slot's
+// rank among its wave's lanes routed to the same expert (a shuffle loop),
+// plus the earlier waves' counts for that expert (LDS), plus the earlier
+// chunks' counts.  Each workgroup then writes the pads and block owners of
+// every gridDim.x-th expert.  The output is the same, slot for slot.
 
 #include "common.h"
 #include "kernels.h"
@@ -138,10 +149,142 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
   }
 }
 
+// ---------------------------------------------------------------- counting sort over slot tiles
+
+constexpr int kTileThreads = 1024;
+constexpr int kTileWaves = kTileThreads / kWave;
+// The per-expert kernel's cost grows with E * A, the counting sort's with A
+// (measured at E = 256: 13 against 27 us at 16384 slots, 105 against 71 us at
+// 262144; at E = 1024 and 16384 slots 39 against 57 us): the counting sort
+// runs above this many expert-slot pairs.
+#ifndef MOE_ALIGN_TILES_FROM
+#define MOE_ALIGN_TILES_FROM (24ll << 20)
+#endif
+constexpr int64_t kAlignTilesFrom = MOE_ALIGN_TILES_FROM;
+constexpr int kAlignTileSlots = 2048;                  // slots per tile (about)
+constexpr int kAlignMaxTiles = 64;
+
+// Exclusive prefix sum over the workgroup (v: one value per thread); *total
+// gets the sum.  `red` holds kTileWaves ints.
+__device__ __forceinline__ int tile_excl_scan(int v, int* red, int* total) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int incl = wave_incl_scan(v);
+  __syncthreads();
+  if (lane == kWave - 1) red[wave] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kTileWaves; ++w) {
+    before += w < wave ? red[w] : 0;
+    all += red[w];
+  }
+  *total = all;
+  return before + incl - v;
+}
+
+__global__ __launch_bounds__(kTileThreads) void align_tiles_kernel(
+    const int32_t* __restrict__ ids, int A, int E, int B, int cap, int tile,
+    int32_t* __restrict__ counts, int32_t* __restrict__ sorted_ids,
+    int32_t* __restrict__ block_expert, int32_t* __restrict__ num_padded,
+    int32_t* __restrict__ zero, int nzero) {
+  __shared__ int all[kMaxExperts];     // slots per expert
+  __shared__ int base[kMaxExperts];    // next position of the tile's slots of each expert
+  __shared__ int off[kMaxExperts];     // group offset of each expert
+  __shared__ int chunk[kMaxExperts];   // the current chunk's slots per expert
+  __shared__ int wc[kTileWaves][kMaxExperts];  // per chunk: wave's slots per expert, then their prefix
+  __shared__ int red[kTileWaves];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int t0 = blockIdx.x * tile;
+  const int t1 = min(A, t0 + tile);
+
+  if (blockIdx.x == 0)  // the next kernels' work-queue counters
+    for (int i = tid; i < nzero; i += kTileThreads) zero[i] = 0;
+  for (int i = tid; i < E; i += kTileThreads) all[i] = base[i] = 0;
+  __syncthreads();
+  // 1. histograms of every slot (all) and of the slots before the tile (base)
+  for (int f = tid; f < A; f += kTileThreads) {
+    const int id = ids[f];
+    if (static_cast<unsigned>(id) < static_cast<unsigned>(E)) {
+      atomicAdd(&all[id], 1);
+      if (f < t0) atomicAdd(&base[id], 1);
+    }
+  }
+  __syncthreads();
+  // 2. group offsets: exclusive scan of the block-rounded counts (E <= 1024:
+  // one expert per thread)
+  const int mine = tid < E ? (all[tid] + B - 1) / B * B : 0;
+  int total = 0;
+  const int o = tile_excl_scan(mine, red, &total);
+  if (tid < E) {
+    off[tid] = o;
+    base[tid] += o;
+    if (blockIdx.x == 0) counts[tid] = all[tid];
+  }
+  __syncthreads();
+  // 3. the tile's slots in order, one chunk of kTileThreads at a time
+  for (int c0 = t0; c0 < t1; c0 += kTileThreads) {
+    const int f = c0 + tid;
+    int id = f < t1 ? ids[f] : -1;
+    if (static_cast<unsigned>(id) >= static_cast<unsigned>(E)) id = -1;
+    // rank: lanes below this one routed to the same expert; n: all of the
+    // wave's lanes routed to it
+    int rank = 0, n = 0;
+    for (int j = 0; j < kWave; ++j) {
+      const int v = __shfl(id, j, kWave);
+      rank += (j < lane && v == id) ? 1 : 0;
+      n += v == id ? 1 : 0;
+    }
+    for (int i = tid; i < kTileWaves * E; i += kTileThreads) wc[i / E][i % E] = 0;
+    __syncthreads();
+    if (id >= 0 && rank == 0) wc[wave][id] = n;  // the wave's first slot of the expert
+    __syncthreads();
+    for (int e = tid; e < E; e += kTileThreads) {  // prefix over the waves, in place
+      int run = 0;
+#pragma unroll
+      for (int w = 0; w < kTileWaves; ++w) {
+        const int c = wc[w][e];
+        wc[w][e] = run;
+        run += c;
+      }
+      chunk[e] = run;
+    }
+    __syncthreads();
+    if (id >= 0) sorted_ids[base[id] + wc[wave][id] + rank] = f;
+    __syncthreads();
+    for (int e = tid; e < E; e += kTileThreads) base[e] += chunk[e];
+    __syncthreads();
+  }
+  // 4. pads and block owners of experts blockIdx.x, blockIdx.x + gridDim.x, ...
+  for (int e = blockIdx.x; e < E; e += gridDim.x) {
+    const int begin = off[e];
+    const int padded = (all[e] + B - 1) / B * B;
+    for (int r = all[e] + tid; r < padded; r += kTileThreads) sorted_ids[begin + r] = A;
+    for (int b = tid; b < padded / B; b += kTileThreads) block_expert[begin / B + b] = e;
+  }
+  if (blockIdx.x == 0) {
+    if (tid == 0) *num_padded = total;
+    for (int r = total + tid; r < cap; r += kTileThreads) sorted_ids[r] = A;
+    for (int b = total / B + tid; b < cap / B; b += kTileThreads) block_expert[b] = -1;
+  }
+}
+
 hipError_t launch_align(const int32_t* ids, int A, int E, int B, int cap, int32_t* counts,
                         int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded,
                         hipStream_t s, int32_t* zero, int nzero) {
   if (nzero > 0 && !zero) return hipErrorInvalidValue;
+  if (static_cast<int64_t>(A) * E > kAlignTilesFrom) {
+    // tiles of whole chunks; about kAlignTileSlots slots each, at most kAlignMaxTiles
+    const int want = (A + kAlignTileSlots - 1) / kAlignTileSlots;
+    const int tiles = want < kAlignMaxTiles ? want : kAlignMaxTiles;
+    const int per = (A + tiles - 1) / tiles;
+    const int tile = (per + kTileThreads - 1) / kTileThreads * kTileThreads;
+    align_tiles_kernel<<<(A + tile - 1) / tile, kTileThreads, 0, s>>>(
+        ids, A, E, B, cap, tile, counts, sorted_ids, block_expert, num_padded, zero, nzero);
+    return hipGetLastError();
+  }
   if (A > 2048)
     align_kernel<1024><<<E, 1024, 0, s>>>(ids, A, E, B, cap, counts, sorted_ids, block_expert,
                                           num_padded, zero, nzero);

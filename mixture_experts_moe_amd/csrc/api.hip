@@ -158,6 +158,15 @@ int default_block_m(const moe_desc* d, int top_k) {
 #define MOE_W2_MAX_SPLITS 8
 #endif
 
+// Big-tile W2 K split: double the splits while the grid has fewer
+// workgroups than this and there are fewer splits than the maximum.
+#ifndef MOE_BIG_W2_SPLIT_WGS
+#define MOE_BIG_W2_SPLIT_WGS 1024
+#endif
+#ifndef MOE_BIG_W2_MAX_SPLITS
+#define MOE_BIG_W2_MAX_SPLITS 4
+#endif
+
 int64_t capacity(int64_t A, int64_t E, int64_t B) {
   const int64_t n = A + (E < A ? E : A) * (B - 1);
   return (n + B - 1) / B * B;
@@ -190,7 +199,9 @@ void make_plan(const moe_desc* d, int top_k, bool with_routing, Plan* p) {
     const int64_t tiles = blocks_est * (p->d / 256);
     const int kc = p->act_mx ? moe::big8_w2_kchunk() : moe::big_w2_kchunk();
     int s = 1;
-    while (s < 4 && tiles * s < 1024 && p->I / (2 * s) >= 8 * kc) s *= 2;
+    while (s < MOE_BIG_W2_MAX_SPLITS && tiles * s < MOE_BIG_W2_SPLIT_WGS &&
+           p->I / (2 * s) >= 8 * kc)
+      s *= 2;
     const int per = (p->I + s - 1) / s;
     p->ksplit = (per + kc - 1) / kc * kc;
     p->splits = (p->I + p->ksplit - 1) / p->ksplit;

@@ -83,7 +83,12 @@ def _random_ids(T, E, k, seed, idle=()):
 
 @pytest.mark.parametrize("T,E,k,bm", [(1, 8, 2, 16), (64, 8, 2, 64), (33, 8, 2, 16),
                                       (300, 32, 4, 32), (2048, 256, 8, 64), (1000, 8, 2, 128),
-                                      (7, 300, 5, 16), (4096, 8, 2, 128)])
+                                      (7, 300, 5, 16), (4096, 8, 2, 128),
+                                      (2500, 64, 3, 32), (3000, 6, 1, 16), (2049, 1, 1, 128),
+                                      # counting sort over slot tiles (E * A > 24 Mi): ragged
+                                      # last tile and chunk, 13 to 64 tiles
+                                      (4096, 1024, 8, 16), (3001, 1024, 9, 16),
+                                      (1500, 1024, 20, 32), (4096, 256, 64, 64)])
 def test_align_is_exact(T, E, k, bm):
     note(f"align T={T} E={E} k={k} B={bm}")
     idle = (3, 5) if E > 5 + k else ()
