@@ -476,6 +476,8 @@ hipError_t launch_ffn13(const FfnArgs& a, hipStream_t s) {
   }
   if (a.act_mx) return launch_ffn13_big8(a, s);    // W8A8: block-scaled e4m3fn activations
   if (a.B == 256) return launch_ffn13_big(a, s);   // large-tile grouped GEMM
+  if (a.B == 128 && a.w_dtype == kDtypeE4M3FN && mid_gemm_fits(a.T, a.d, a.I))
+    return launch_ffn13_mid(a, s);                 // 128-token tile, both operands via LDS
   if (a.B == 128) return launch_ffn13_gemm(a, s);  // token-tiled grouped GEMM
   if (dma_stream_use(a)) return launch_ffn13_dma(a, s);  // weights through LDS
   if (a.w_dtype == kDtypeBF16) return ffn13_w<bf16_t>(a, s);
@@ -493,6 +495,8 @@ hipError_t launch_ffn2(const FfnArgs& a, hipStream_t s) {
   }
   if (a.act_mx) return launch_ffn2_big8(a, s);
   if (a.B == 256) return launch_ffn2_big(a, s);
+  if (a.B == 128 && a.w_dtype == kDtypeE4M3FN && mid_gemm_fits(a.T, a.d, a.I))
+    return launch_ffn2_mid(a, s);
   if (a.B == 128) return launch_ffn2_gemm(a, s);
   if (dma_stream_use(a)) return launch_ffn2_dma(a, s);
   if (a.w_dtype == kDtypeBF16) return ffn2_w<bf16_t>(a, s);

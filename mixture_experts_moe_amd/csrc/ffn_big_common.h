@@ -53,18 +53,20 @@ struct BigTile {
 // Same rasterisation as the 128-token GEMM: contiguous runs of the logical
 // order per XCD, super-rows of kBigGroupCols channel groups, row block
 // slowest inside a super-row.
+// kCols channel groups per super-row.
+template <int kCols = kBigGroupCols>
 __device__ __forceinline__ BigTile big_tile_of(int p, int gx, int gy) {
   const int total = gx * gy;
   const int per_xcd = (total + kBigXcds - 1) / kBigXcds;
   const int l = (p % kBigXcds) * per_xcd + p / kBigXcds;
   BigTile t{0, 0, l < total};
   if (!t.live) return t;
-  const int band = kBigGroupCols * gx;
+  const int band = kCols * gx;
   const int sr = l / band;
   const int rem = l - sr * band;
-  const int cols = min(kBigGroupCols, gy - sr * kBigGroupCols);
+  const int cols = min(kCols, gy - sr * kCols);
   t.b = rem / cols;
-  t.y = sr * kBigGroupCols + rem % cols;
+  t.y = sr * kCols + rem % cols;
   return t;
 }
 

@@ -124,6 +124,11 @@ int big8_w2_kchunk();  // a split of the W8A8 W2's K range is a multiple of this
 hipError_t launch_ffn13_big(const FfnArgs& a, hipStream_t s);
 hipError_t launch_ffn2_big(const FfnArgs& a, hipStream_t s);
 int big_w2_kchunk();  // a split of the big W2's K range is a multiple of this
+// 128-token tile with e4m3fn weights and bf16 activations (d % 256 == 0,
+// I % 128 == 0, 32-bit offsets); used for a.B == 128 where it fits.
+bool mid_gemm_fits(int64_t T, int d, int I);
+hipError_t launch_ffn13_mid(const FfnArgs& a, hipStream_t s);
+hipError_t launch_ffn2_mid(const FfnArgs& a, hipStream_t s);
 
 // Row blocks that hold at least one slot: the realised blocks are at most
 // the capacity's, and at most one partial block per used expert plus the

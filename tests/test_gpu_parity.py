@@ -153,6 +153,15 @@ SMALL = [
     ("fp8_lds", dict(workload="fp8", d=1536, I=1536, E=16, k=4), 12, 0),
     ("fp8_lds", dict(workload="fp8", d=512, I=512, E=64, k=4, scale_mode="tensor"), 16, 0),
     ("skew_small", dict(workload="skew", d=192, I=128), 300, 0),
+    # e4m3fn weights in blocks of 128 (d and I multiples of 256): the
+    # 128-token tile with both operands through LDS; blocks mostly padding,
+    # experts with two blocks, per-tensor scales, many W2 channel tiles, the
+    # shortest K (four stages)
+    ("fp8_mid", dict(workload="fp8", d=256, I=256, E=8, k=2), 300, 128),
+    ("fp8_mid", dict(workload="fp8", d=512, I=512, E=4, k=2, scale_mode="tensor"), 500, 0),
+    ("fp8_mid", dict(workload="fp8", d=768, I=256, E=16, k=4), 200, 128),
+    ("fp8_mid", dict(workload="fp8", d=256, I=1024, E=2, k=1), 129, 128),
+    ("fp8_mid", dict(workload="fp8", d=2048, I=512, E=32, k=8), 150, 128),
     # W8A8 (block-scaled e4m3fn x and h, blocks of 256): one token, a ragged
     # block, several blocks per expert, E = 1, per-tensor scales, more
     # channel tiles than one, and W2's K split in two (I = 4096, few tiles)
