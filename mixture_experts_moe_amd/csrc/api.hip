@@ -202,6 +202,9 @@ void make_plan(const moe_desc* d, int top_k, bool with_routing, Plan* p) {
     while (s < MOE_BIG_W2_MAX_SPLITS && tiles * s < MOE_BIG_W2_SPLIT_WGS &&
            p->I / (2 * s) >= 8 * kc)
       s *= 2;
+#ifdef MOE_BIG_W2_SPLITS
+    s = MOE_BIG_W2_SPLITS;
+#endif
     const int per = (p->I + s - 1) / s;
     p->ksplit = (per + kc - 1) / kc * kc;
     p->splits = (p->I + p->ksplit - 1) / p->ksplit;
