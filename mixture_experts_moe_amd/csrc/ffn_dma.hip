@@ -572,8 +572,10 @@ __global__ __launch_bounds__(kDmaThreads) void ffn2_combine_dma_kernel(
 // and K range have counted themselves done; every W13 ticket precedes every
 // W2 ticket and W13 tiles wait for nothing, so a waiting workgroup only ever
 // waits on work a running workgroup already holds (no deadlock, whatever
-// the grid size).  The wait is bounded (a flag records a timeout instead of
-// hanging).  The combine is fused: after a W2 tile writes its partials it
+// the grid size).  The wait is bounded: after MOE_FUSED_SPIN_LIMIT polls a
+// tile sets a flag in the counter words and writes NaN partials, so that a
+// timeout shows in the output instead of hanging or passing unnoticed.  The
+// combine is fused: after a W2 tile writes its partials it
 // counts one arrival per real slot on the slot's (token, channel group); the
 // tile that brings a counter to k * splits adds that token's partials, slots
 // then splits in the same fixed order as the combine kernel, and writes the
@@ -656,12 +658,14 @@ __global__ __launch_bounds__(kDmaThreads) void ffn_fused_dma_kernel(FusedParams 
       const int kb = z * p.ksplit;
       const int need = (min(p.I, kb + p.ksplit) - kb) / 16;
       // bounded wait for the W13 tiles of this block's K range
+      bool timed_out = false;  // wave-uniform: the count is broadcast from lane 0
       for (int spin = 0;; ++spin) {
         const int got = __builtin_amdgcn_readfirstlane(__hip_atomic_load(
             done13 + b * p.splits + z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
         if (got >= need) break;
         if (spin >= MOE_FUSED_SPIN_LIMIT) {
           __hip_atomic_store(p.cnt + kFusedTimeout, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          timed_out = true;
           break;
         }
         __builtin_amdgcn_s_sleep(2);
@@ -670,6 +674,21 @@ __global__ __launch_bounds__(kDmaThreads) void ffn_fused_dma_kernel(FusedParams 
       dma2_tile<WT, NS, P2, RN>(p.h, w2, p.s2, p.scale_mode, p.topk_w, p.sorted_ids,
                                 p.block_expert, p.y_part, p.d, p.I, p.A, p.ksplit, b,
                                 dt * 16 * RN, z, ring);
+      if (timed_out) {  // h may not be complete: make the tile's outputs NaN, not plausible
+        const int32_t* blk = p.sorted_ids + static_cast<size_t>(b) * B;
+        const float nan = __builtin_nanf("");
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const int f = blk[16 * s + (lane & 15)];
+          if (f < p.A) {
+#pragma unroll
+            for (int rt = 0; rt < RN; ++rt)
+              *reinterpret_cast<float4*>(p.y_part + (static_cast<size_t>(z) * p.A + f) * p.d +
+                                         dt * 16 * RN + 16 * rt + 4 * (lane >> 4)) =
+                  float4{nan, nan, nan, nan};
+          }
+        }
+      }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // this tile's partials, device-wide
       arrive_and_combine<NS, RN, false>(p.sorted_ids + static_cast<size_t>(b) * B, arrive,
                                         p.y_part, p.out, p.A, p.k, p.splits, p.d, nd, dt);

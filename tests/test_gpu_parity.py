@@ -278,6 +278,37 @@ def test_w8a8_forward_equals_stage_composition_and_is_deterministic():
     assert zero.shape == (0, inp.d)
 
 
+def test_fp8_mid_tile_forward_equals_stage_composition_and_graph():
+    """e4m3fn weights in blocks of 128 (the 128-token tile): moe_forward is
+    deterministic, equals routing + align + moe_expert_ffn bit for bit, and a
+    recorded graph replays it exactly."""
+    inp = synth.make_inputs("fp8", T=400, device=DEV, d=512, I=512, E=8, k=2)
+    sc = (inp.s13, inp.s2)
+    out1 = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, sc)
+    out2 = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, sc)
+    _, ids, w = B.moe_route(inp.x, inp.w_gate, inp.top_k)
+    counts, sorted_ids, block_expert, num_padded, bm = B.moe_align(
+        ids, inp.E, hidden=inp.d, intermediate=inp.I, weight_dtype=B.MOE_DTYPE_E4M3FN)
+    assert bm == 128
+    out3 = B.moe_expert_ffn(inp.x, inp.w13, inp.w2, inp.top_k, w, sorted_ids, block_expert,
+                            num_padded, sc)
+    out = torch.empty_like(inp.x)
+    g = B.MoeGraph(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, sc, out=out)
+    try:
+        for _ in range(3):
+            out.fill_(float("nan"))
+            g.launch()
+            torch.cuda.synchronize()
+            assert torch.equal(out, out1)
+    finally:
+        g.close()
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2)
+    assert torch.equal(out1, out3)
+    r = compare_layer(inp, out1, ids)
+    _report(r)
+
+
 def test_binding_rejects_bad_scales_before_any_launch():
     inp = synth.make_inputs("fp8", T=4, device=DEV, d=256, I=128, E=4, k=2)
     bad = [
