@@ -393,6 +393,109 @@ __global__ __launch_bounds__(64 * NW) void router_logits_bf16_kernel(
   }
 }
 
+// ---------------------------------------------------------------- many tokens, many experts
+// The 64-token x 16-expert tiles above read each token row once per 16
+// experts: at T = 2048, E = 256, d = 7168 that is 470 MB of x and 235 MB of
+// W_gate pulled from L2 and the last-level cache for 36 MB of data.  Here a
+// wave covers 64 tokens x 16 NE experts (NE expert tiles share each x
+// fragment), four waves split K as above and the tiles are added in wave
+// order, so every logit is computed with the same operations in the same
+// order as by router_logits_bf16_kernel<4, 4> (bit-identical); only the
+// reuse changes.
+
+template <int NE>
+__global__ __launch_bounds__(256) void router_logits_wide_kernel(
+    const bf16_t* __restrict__ x, const float* __restrict__ wg, float* __restrict__ logits, int T,
+    int E, int d) {
+  constexpr int NT = 4, NW = 4, U = 2;
+  __shared__ f32x4 red[NW][NT][NE][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  const int t0 = blockIdx.x * 16 * NT;
+  const int e0 = blockIdx.y * 16 * NE;
+  const float* wrow[NE];
+  bool e_ok[NE];
+#pragma unroll
+  for (int ne = 0; ne < NE; ++ne) {
+    const int e = e0 + 16 * ne + r16;
+    e_ok[ne] = e < E;
+    wrow[ne] = wg + static_cast<size_t>(e_ok[ne] ? e : 0) * d + 8 * g;
+  }
+  const bf16_t* xrow[NT];
+  bool t_ok[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int t = t0 + nt * 16 + r16;
+    t_ok[nt] = t < T;
+    xrow[nt] = x + static_cast<size_t>(t_ok[nt] ? t : 0) * d + 8 * g;
+  }
+  const int steps = d / 32;
+  const int s_begin = wave * steps / NW;
+  const int s_end = (wave + 1) * steps / NW;
+  f32x4 acc_h[NT][NE], acc_m[NT][NE], acc_l[NT][NE];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int ne = 0; ne < NE; ++ne)
+      acc_h[nt][ne] = acc_m[nt][ne] = acc_l[nt][ne] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int s0 = s_begin; s0 < s_end; s0 += U) {
+    float4 wa[U][NE], wb[U][NE];
+    uint4 xb[U][NT];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {  // issue every load of U steps first
+      const int k = (s0 + u) * 32;
+      const bool live = s0 + u < s_end;
+#pragma unroll
+      for (int ne = 0; ne < NE; ++ne) {
+        const bool on = live && e_ok[ne];
+        wa[u][ne] = on ? *reinterpret_cast<const float4*>(wrow[ne] + k) : float4{0.f, 0.f, 0.f, 0.f};
+        wb[u][ne] = on ? *reinterpret_cast<const float4*>(wrow[ne] + k + 4) : float4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        xb[u][nt] = (live && t_ok[nt]) ? *reinterpret_cast<const uint4*>(xrow[nt] + k) : uint4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int ne = 0; ne < NE; ++ne) {
+        const float w[8] = {wa[u][ne].x, wa[u][ne].y, wa[u][ne].z, wa[u][ne].w,
+                            wb[u][ne].x, wb[u][ne].y, wb[u][ne].z, wb[u][ne].w};
+        uint4 hi, mid, lo;
+        split3_bf16(w, hi, mid, lo);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const bf16x8 xf = as_frag(xb[u][nt]);
+          acc_h[nt][ne] = mfma16x16x32(as_frag(hi), xf, acc_h[nt][ne]);
+          acc_m[nt][ne] = mfma16x16x32(as_frag(mid), xf, acc_m[nt][ne]);
+          acc_l[nt][ne] = mfma16x16x32(as_frag(lo), xf, acc_l[nt][ne]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int ne = 0; ne < NE; ++ne) red[wave][nt][ne][lane] = acc_h[nt][ne] + (acc_m[nt][ne] + acc_l[nt][ne]);
+  __syncthreads();
+  // D layout: lane holds token column r16, expert rows 4g .. 4g+3 of a tile
+  for (int i = wave; i < NT * NE; i += NW) {
+    const int nt = i / NE, ne = i % NE;
+    f32x4 v = red[0][nt][ne][lane];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) v += red[w][nt][ne][lane];
+    const int t = t0 + nt * 16 + r16;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int ee = e0 + 16 * ne + 4 * g + q;
+      if (t < T && ee < E) logits[static_cast<size_t>(t) * E + ee] = v[q];
+    }
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 
 // Below this many (64-token x 16-expert) tiles the logits kernel runs
@@ -402,6 +505,15 @@ __global__ __launch_bounds__(64 * NW) void router_logits_bf16_kernel(
 #ifndef MOE_ROUTER_WIDE_WGS
 #define MOE_ROUTER_WIDE_WGS 512
 #endif
+// Expert tiles per wave of router_logits_wide_kernel, and the workgroups its
+// grid needs before it is used.
+#ifndef MOE_ROUTER_WIDE_NE
+#define MOE_ROUTER_WIDE_NE 2
+#endif
+#ifndef MOE_ROUTER_WIDE_NE_WGS
+#define MOE_ROUTER_WIDE_NE_WGS 256
+#endif
+constexpr int kRouterWideNE = MOE_ROUTER_WIDE_NE;
 
 hipError_t launch_router_logits(const void* x, int act_dtype, const float* wg, float* logits,
                                 int T, int E, int d, hipStream_t s) {
@@ -415,6 +527,13 @@ hipError_t launch_router_logits(const void* x, int act_dtype, const float* wg, f
     dim3 grid((T + 15) / 16, (E + 15) / 16);
     router_logits_bf16_kernel<1, 16, false><<<grid, 1024, 0, s>>>(
         static_cast<const bf16_t*>(x), wg, logits, nullptr, nullptr, T, E, d, 0, AlignOut{}, nullptr);
+  } else if (int64_t((T + 63) / 64) * ((E + 16 * kRouterWideNE - 1) / (16 * kRouterWideNE)) >=
+             MOE_ROUTER_WIDE_NE_WGS) {
+    // enough 64-token x (16 NE)-expert tiles to fill the GPU: each x
+    // fragment feeds NE expert tiles
+    dim3 grid((T + 63) / 64, (E + 16 * kRouterWideNE - 1) / (16 * kRouterWideNE));
+    router_logits_wide_kernel<kRouterWideNE><<<grid, 256, 0, s>>>(static_cast<const bf16_t*>(x), wg,
+                                                                  logits, T, E, d);
   } else {
     dim3 grid((T + 63) / 64, (E + 15) / 16);
     router_logits_bf16_kernel<4, 4, false><<<grid, 256, 0, s>>>(

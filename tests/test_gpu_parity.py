@@ -50,7 +50,8 @@ def test_topk_from_given_logits_is_exact(T, E, k):
     assert np.allclose(w.cpu().double().numpy(), ref_w, rtol=1e-6, atol=0)
 
 
-@pytest.mark.parametrize("wl,T", [("tiny_fp32", 16), ("decode_bf16", 64), ("fp8", 100), ("skew", 512)])
+@pytest.mark.parametrize("wl,T", [("tiny_fp32", 16), ("decode_bf16", 64), ("fp8", 100), ("skew", 512),
+                                  ("fp8", 2048)])
 def test_router_logits_and_selection(wl, T):
     note(f"route {wl} T={T}")
     cfg = synth.WORKLOADS[wl]
