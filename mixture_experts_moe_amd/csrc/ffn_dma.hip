@@ -740,8 +740,14 @@ constexpr int kDma2WideRN = 4;
 constexpr int kDma2WideP = 2;
 constexpr int64_t kDma2WideBlocks = 2;
 
+#ifndef MOE_DMA2_RN32
+#define MOE_DMA2_RN32 2
+#endif
+constexpr int kDma2RN32 = MOE_DMA2_RN32;  // channel tiles per W2 wave, blocks of 32
+
 static int dma_w2_rn(int w_dtype, int B, int64_t blocks_est) {
   if (w_dtype == kDtypeE4M3FN) return kDma2RNFp8;
+  if (B == 32) return kDma2RN32;
   return B == 16 && blocks_est <= kDma2WideBlocks ? kDma2WideRN : kDma2RN;
 }
 
@@ -817,7 +823,7 @@ hipError_t launch_ffn2_dma(const FfnArgs& a, hipStream_t s) {
       if (dma_w2_rn(a.w_dtype, a.B, ffn_blocks_estimate(a.cap, a.B, a.E, a.A)) == kDma2WideRN)
         return ffn2_dma_go<bf16_t, 1, kDma2WideP, kDma2WideRN>(a, s);
       return ffn2_dma_go<bf16_t, 1, MOE_DMA2_P1>(a, s);
-    case 32: return ffn2_dma_go<bf16_t, 2, MOE_DMA2_P2>(a, s);
+    case 32: return ffn2_dma_go<bf16_t, 2, MOE_DMA2_P2, kDma2RN32>(a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -831,7 +837,7 @@ hipError_t launch_ffn2_dma(const FfnArgs& a, hipStream_t s) {
 // T = 64: 556 against 504; e4m3fn weights at T = 1: 94.6 against 90.6 us;
 // T = 64: 1.95 against 1.61 ms).
 bool ffn2_combine_pays(int w_dtype, int B, int64_t blocks_est) {
-  return w_dtype == kDtypeBF16 && dma_w2_rn(w_dtype, B, blocks_est) == kDma2WideRN;
+  return w_dtype == kDtypeBF16 && B == 16 && dma_w2_rn(w_dtype, B, blocks_est) == kDma2WideRN;
 }
 
 int ffn2_combine_ints(const FfnArgs& a) {
@@ -840,7 +846,8 @@ int ffn2_combine_ints(const FfnArgs& a) {
 
 hipError_t launch_ffn2_combine_dma(const FfnArgs& a, hipStream_t s) {
   const int64_t blocks = ffn_blocks_estimate(a.cap, a.B, a.E, a.A);
-  if (!a.combine_cnt || !dma_args_ok(a) || !dma_stream_use(a) ||
+  // the one instantiation: blocks of 16 (one token subtile), four channel tiles
+  if (!a.combine_cnt || a.B != 16 || !dma_args_ok(a) || !dma_stream_use(a) ||
       !ffn2_combine_pays(a.w_dtype, a.B, blocks) || a.ksplit % dma_stream_kc(a.w_dtype) != 0 ||
       a.d % dma_w2_channels(a.w_dtype, a.B, blocks) != 0)
     return hipErrorInvalidValue;
@@ -928,7 +935,7 @@ hipError_t launch_ffn_fused(const FfnArgs& a, hipStream_t s) {
       if (dma_w2_rn(a.w_dtype, a.B, blocks) == kDma2WideRN)
         return ffn_fused_go<1, 2, kDma2WideP, kDma2WideRN>(a, s);
       return ffn_fused_go<1, MOE_DMA13_P1, MOE_DMA2_P1, kDma2RN>(a, s);
-    case 32: return ffn_fused_go<2, MOE_DMA13_P2, MOE_DMA2_P2, kDma2RN>(a, s);
+    case 32: return ffn_fused_go<2, MOE_DMA13_P2, MOE_DMA2_P2, kDma2RN32>(a, s);
   }
   return hipErrorInvalidValue;
 }
