@@ -1,0 +1,134 @@
+"""Host-side checks of the 128-token e4m3fn tile's LDS layout and stage
+ring (mixture_experts_moe_amd/csrc/ffn_gemm_mid.hip), replayed in Python:
+
+- every byte the direct-to-LDS loads write (weight load i of wave w: 16
+  rows x 64 bytes, lane l -> row l/4, physical slot l%4 holding logical slot
+  (l%4) ^ ((row >> 1) & 3); token load i: 8 rows x 128 bytes, lane l -> row
+  l/8, slot l%8 holding (l%8) ^ ((row >> 1) & 7)) is the byte the fragment
+  reads of the two 32-K steps expect (lane (r16, g): weight bytes
+  32j + 8g .. +7 of row r16 of a 16-row tile, token K 32j + 8g .. +7);
+- the four-buffer ring consumes every stage once, in order, from the buffer
+  it was issued into, never overwrites a stage before it is read, and waits
+  at each stage for exactly the loads of the stages issued before it.
+
+A mistake in either (a swizzle that ignores a load's row offset, a wait one
+stage short) gives in-bounds but wrong reads on the GPU, which only a
+parity test with the right shapes would catch.
+"""
+
+import pytest
+
+ROWS, TOKENS, WAVES = 256, 128, 8
+A_ROW, B_ROW = 64, 128           # bytes per row and stage: 64 e4m3fn, 64 bf16
+A_BYTES = ROWS * A_ROW           # 16 KB
+LOADS_A = A_BYTES // 1024 // WAVES
+LOADS_B = TOKENS * B_ROW // 1024 // WAVES
+
+
+def a_row(wave, i, lane):
+    return 32 * wave + 16 * i + lane // 4
+
+
+def a_slot(lane):
+    return (lane % 4) ^ (((lane // 4) >> 1) & 3)
+
+
+def b_row(wave, i, lane):
+    return 16 * wave + 8 * i + lane // 8
+
+
+def b_slot(i, lane):
+    return (lane % 8) ^ (((8 * i + lane // 8) >> 1) & 7)
+
+
+def _written():
+    """LDS byte -> (operand, row, k) as the loaders fill one stage."""
+    lds = {}
+    for w in range(WAVES):
+        for i in range(LOADS_A):
+            for lane in range(64):
+                base = (w * LOADS_A + i) * 1024 + lane * 16
+                row = a_row(w, i, lane)
+                assert base // A_ROW == row  # the load writes 16 whole rows
+                for byte in range(16):
+                    lds[base + byte] = ("A", row, 16 * a_slot(lane) + byte)
+        for i in range(LOADS_B):
+            for lane in range(64):
+                base = A_BYTES + (w * LOADS_B + i) * 1024 + lane * 16
+                row = b_row(w, i, lane)
+                assert (base - A_BYTES) // B_ROW == row
+                for byte in range(0, 16, 2):  # bf16: two bytes per k
+                    lds[base + byte] = ("B", row, (16 * b_slot(i, lane) + byte) // 2)
+    return lds
+
+
+def test_every_fragment_read_finds_its_operand():
+    lds = _written()
+    assert len(lds) == A_BYTES + TOKENS * B_ROW // 2
+    for lane in range(64):
+        r16, g = lane % 16, lane // 16
+        swa, swb = (r16 >> 1) & 3, (r16 >> 1) & 7
+        for j in range(2):
+            a_off = r16 * A_ROW + (((2 * j + (g >> 1)) ^ swa) << 4) + 8 * (g & 1)
+            b_off = A_BYTES + r16 * B_ROW + (((4 * j + g) ^ swb) << 4)
+            for tile in range(0, ROWS, 16):
+                for e in range(8):
+                    assert lds[a_off + tile * A_ROW + e] == ("A", tile + r16, 32 * j + 8 * g + e)
+            for tile in range(0, TOKENS, 16):
+                for e in range(8):
+                    assert lds[b_off + tile * B_ROW + 2 * e] == ("B", tile + r16, 32 * j + 8 * g + e)
+
+
+def test_a_swizzle_that_ignores_the_load_offset_is_caught():
+    """The planted mistake the first version made (token slots swizzled
+    with load 0's rows for every load) must fail the check above."""
+    def bad_slot(i, lane):
+        return (lane % 8) ^ (((lane // 8) >> 1) & 7)
+    mismatches = 0
+    for i in range(LOADS_B):
+        for lane in range(64):
+            mismatches += bad_slot(i, lane) != b_slot(i, lane)
+    assert mismatches > 0
+
+
+def _ring(nst):
+    """The ring of MidRing::run (four buffers): returns the consumed order,
+    asserting the waits and the buffer reuse."""
+    S = 4
+    issued, consumed, held = [], [], {}
+
+    def issue(buf, s):
+        assert s < nst and buf == s % S and buf not in held
+        held[buf] = s
+        issued.append(s)
+
+    def step(p, W, k_issue, s):
+        later = [x for x in issued if x > s]
+        assert s in issued and len(later) == W, (nst, s, W, later)
+        assert held.get(p) == s
+        if k_issue:
+            issue((p + 3) % S, s + 3)
+        consumed.append(s)
+        del held[p]
+
+    issue(0, 0), issue(1, 1), issue(2, 2)
+    s = 0
+    while s + 4 < nst:
+        for p in range(4):
+            step(p, 2, True, s + p)
+        s += 4
+    step(0, 2, True, s)
+    step(1, 2, False, s + 1)
+    step(2, 1, False, s + 2)
+    step(3, 0, False, s + 3)
+    return consumed
+
+
+@pytest.mark.parametrize("nst", [4, 8, 12, 16, 32, 56, 112, 224])
+def test_ring_consumes_every_stage_in_order(nst):
+    assert _ring(nst) == list(range(nst))
+
+
+def test_ring_needs_a_multiple_of_four_stages():
+    with pytest.raises(AssertionError):
+        _ring(6)
