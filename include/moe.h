@@ -106,12 +106,15 @@ extern "C" {
 /* How the expert products hand their tiles to workgroups (Hungarian page,
  * section "FP8 esetén ...": dynamic scheduling layouts for token groups of
  * varying size; section "A fused MoE ...": one batched GPU operation).
- * With 128-token blocks (block_m 128): MOE_SCHED_STATIC is one workgroup per
- * possible (row block, output-channel group) tile, in an XCD-aware raster,
- * those of row blocks past the realised ones exiting at once;
- * MOE_SCHED_QUEUE is as many workgroups as the GPU holds at once taking only
- * the realised tiles, from one work queue per XCD, helping drain the other
- * queues when their own is empty.  In moe_forward with bf16 weights and
+ * With 128-token blocks (block_m 128) on the token-tiled GEMM (bf16
+ * weights, and e4m3fn weights whose d or I is not a multiple of 256):
+ * MOE_SCHED_STATIC is one workgroup per possible (row block, output-channel
+ * group) tile, in an XCD-aware raster, those of row blocks past the
+ * realised ones exiting at once; MOE_SCHED_QUEUE is as many workgroups as
+ * the GPU holds at once taking only the realised tiles, from one work queue
+ * per XCD, helping drain the other queues when their own is empty.  (The
+ * 128-token tile that e4m3fn weights with d and I multiples of 256 take
+ * has the static raster only.)  In moe_forward with bf16 weights and
  * activations on the decode path (blocks of 16 or 32 tokens, d and I
  * multiples of 256, T <= 64): MOE_SCHED_STATIC runs W13, W2 and the combine
  * as three launches; MOE_SCHED_QUEUE runs them as one persistent launch
