@@ -106,28 +106,34 @@ extern "C" {
 /* How the expert products hand their tiles to workgroups (Hungarian page,
  * section "FP8 esetén ...": dynamic scheduling layouts for token groups of
  * varying size; section "A fused MoE ...": one batched GPU operation).
- * With 128-token blocks (block_m 128) on the token-tiled GEMM (bf16
- * weights, and e4m3fn weights whose d or I is not a multiple of 256):
- * MOE_SCHED_STATIC is one workgroup per possible (row block, output-channel
- * group) tile, in an XCD-aware raster, those of row blocks past the
- * realised ones exiting at once; MOE_SCHED_QUEUE is as many workgroups as
- * the GPU holds at once taking only the realised tiles, from one work queue
- * per XCD, helping drain the other queues when their own is empty.  (The
- * 128-token tile that e4m3fn weights with d and I multiples of 256 take
- * has the static raster only.)  In moe_forward with bf16 weights and
+ * With 128-token blocks (block_m 128), MOE_SCHED_STATIC and
+ * MOE_SCHED_QUEUE select the token-tiled GEMM: MOE_SCHED_STATIC is one
+ * workgroup per possible (row block, output-channel group) tile, in an
+ * XCD-aware raster, those of row blocks past the realised ones exiting at
+ * once; MOE_SCHED_QUEUE is as many workgroups as the GPU holds at once
+ * taking only the realised tiles, from one work queue per XCD, helping drain
+ * the other queues when their own is empty.  MOE_SCHED_AUTO takes the
+ * register-token tile there instead (static raster; bf16 activations, bf16
+ * weights with d and I multiples of 64 and at least 256, or e4m3fn weights
+ * with d and I multiples of 128 and at least 384; I a multiple of 32), else
+ * the 128-token tile with both operands through LDS (e4m3fn, d and I
+ * multiples of 256; static raster), else the GEMM's queue.  In moe_forward
+ * with bf16 weights and
  * activations on the decode path (blocks of 16 or 32 tokens, d and I
  * multiples of 256, T <= 64): MOE_SCHED_STATIC runs W13, W2 and the combine
  * as three launches; MOE_SCHED_QUEUE runs them as one persistent launch
  * whose workgroups take W13 tiles, then W2 tiles (each once the W13 tiles it
  * reads are done), from one ticket counter, and add up each token's slots as
- * soon as its last partial lands.  MOE_SCHED_AUTO (0) is the queue for 128-token
- * blocks and, on the decode path, the three launches, except that for at
+ * soon as its last partial lands.  MOE_SCHED_AUTO (0) is, on the decode
+ * path, the three launches, except that for at
  * most two row blocks of 16 (one token of a top-2 layer) W2 adds up each
  * token's slots itself (two launches: the last W2 workgroup to finish a
  * token's channel group sums its partials).  The persistent kernel is
  * slower there (every W13 tile has to publish its rows at device scope
- * before a W2 tile on another XCD may read them).  All of these give
- * bit-identical outputs; other paths ignore the field. */
+ * before a W2 tile on another XCD may read them).  The static and queue
+ * schedules give bit-identical outputs, and on the decode path so does the
+ * automatic one; with 128-token blocks its tiles sum over K in another
+ * order (equal within rounding).  Other paths ignore the field. */
 #define MOE_SCHED_AUTO 0
 #define MOE_SCHED_STATIC 1
 #define MOE_SCHED_QUEUE 2

@@ -101,6 +101,7 @@ struct Plan {
   int act, wdt;
   bool act_mx;  // W8A8 mode
   bool queue;   // tile-queue schedule of the 128-token GEMM
+  bool wide;    // blocks of 128 on the register-token tile (automatic schedule)
   // workspace offsets (bytes); xq, sx, sh only in the W8A8 mode, qcnt only
   // with the queue schedule
   size_t logits, ids, gates, counts, num_padded, sorted, block_exp, h, y, xq, sx, sh, qcnt, total;
@@ -167,6 +168,19 @@ int default_block_m(const moe_desc* d, int top_k) {
 #define MOE_BIG_W2_MAX_SPLITS 4
 #endif
 
+// Register-token tile W2 K split: double the splits while the grid has
+// fewer workgroups than this, there are fewer splits than the maximum, and
+// each range keeps at least the minimum number of K stages.
+#ifndef MOE_WIDE_W2_SPLIT_WGS
+#define MOE_WIDE_W2_SPLIT_WGS 1024
+#endif
+#ifndef MOE_WIDE_W2_MAX_SPLITS
+#define MOE_WIDE_W2_MAX_SPLITS 4
+#endif
+#ifndef MOE_WIDE_W2_MIN_STAGES
+#define MOE_WIDE_W2_MIN_STAGES 8
+#endif
+
 int64_t capacity(int64_t A, int64_t E, int64_t B) {
   const int64_t n = A + (E < A ? E : A) * (B - 1);
   return (n + B - 1) / B * B;
@@ -184,8 +198,12 @@ void make_plan(const moe_desc* d, int top_k, bool with_routing, Plan* p) {
   p->act = d->act_dtype;
   p->wdt = d->weight_dtype;
   p->act_mx = d->act_quant == MOE_ACT_MX_E4M3;
+  // blocks of 128: the register-token tile where it fits, unless the caller
+  // asked for one of the 128-token GEMM's schedules
+  p->wide = d->schedule == MOE_SCHED_AUTO &&
+            moe::wide_use(p->wdt, p->act, p->act_mx, p->B, p->T, p->d, p->I);
   p->queue = d->schedule != MOE_SCHED_STATIC && p->B == 128 && p->wdt != MOE_DTYPE_F32 &&
-             !p->act_mx;
+             !p->act_mx && !p->wide;
 
   // Split W2's K range when there are too few workgroups to keep enough
   // HBM requests in flight (small batches); the combine adds the splits in a
@@ -209,7 +227,21 @@ void make_plan(const moe_desc* d, int top_k, bool with_routing, Plan* p) {
     p->ksplit = (per + kc - 1) / kc * kc;
     p->splits = (p->I + p->ksplit - 1) / p->ksplit;
   }
-  if (p->wdt != MOE_DTYPE_F32 && p->A > 0 && p->B <= 64) {  // the 128-token GEMM does not split
+  if (p->A > 0 && p->wide) {
+    // the register-token tile's W2 has ceil(d/256) channel tiles per block:
+    // split K until the grid fills about four rounds of the CUs, each range
+    // keeping at least MOE_WIDE_W2_MIN_STAGES stages
+    const int64_t blocks_est = moe::ffn_blocks_estimate(p->cap, p->B, p->E, p->A);
+    const int64_t tiles = blocks_est * ((p->d + 255) / 256);
+    const int kc = moe::wide_kchunk(p->wdt);
+    int s = 1;
+    while (s < MOE_WIDE_W2_MAX_SPLITS && tiles * s < MOE_WIDE_W2_SPLIT_WGS &&
+           p->I / (2 * s) >= MOE_WIDE_W2_MIN_STAGES * kc)
+      s *= 2;
+    const int per = (p->I + s - 1) / s;
+    p->ksplit = (per + kc - 1) / kc * kc;
+    p->splits = (p->I + p->ksplit - 1) / p->ksplit;
+  } else if (p->wdt != MOE_DTYPE_F32 && p->A > 0 && p->B <= 64) {  // the 128-token GEMM does not split
     const int64_t blocks_est = moe::ffn_blocks_estimate(p->cap, p->B, p->E, p->A);
     const bool lds = moe::dma_stream_use(p->wdt, p->act, p->B, p->d, p->I, blocks_est);
     const int kc = moe::ffn2_kchunk(p->d, p->I, p->B, p->wdt, p->act, blocks_est);
@@ -395,6 +427,7 @@ FfnArgs ffn_args(const Plan& p, const void* x, const void* w13, const void* w2,
   a.sh = p.act_mx ? reinterpret_cast<uint8_t*>(ws + p.sh) : nullptr;
   a.queue_sched = p.queue;
   a.queue = p.queue ? reinterpret_cast<int32_t*>(ws + p.qcnt) : nullptr;
+  a.wide = p.wide;
   return a;
 }
 

@@ -476,6 +476,7 @@ hipError_t launch_ffn13(const FfnArgs& a, hipStream_t s) {
   }
   if (a.act_mx) return launch_ffn13_big8(a, s);    // W8A8: block-scaled e4m3fn activations
   if (a.B == 256) return launch_ffn13_big(a, s);   // large-tile grouped GEMM
+  if (wide_use(a)) return launch_ffn13_wide(a, s);  // 128-token tile, tokens in registers
   if (a.B == 128 && a.w_dtype == kDtypeE4M3FN && mid_gemm_fits(a.T, a.d, a.I))
     return launch_ffn13_mid(a, s);                 // 128-token tile, both operands via LDS
   if (a.B == 128) return launch_ffn13_gemm(a, s);  // token-tiled grouped GEMM
@@ -495,6 +496,7 @@ hipError_t launch_ffn2(const FfnArgs& a, hipStream_t s) {
   }
   if (a.act_mx) return launch_ffn2_big8(a, s);
   if (a.B == 256) return launch_ffn2_big(a, s);
+  if (wide_use(a)) return launch_ffn2_wide(a, s);
   if (a.B == 128 && a.w_dtype == kDtypeE4M3FN && mid_gemm_fits(a.T, a.d, a.I))
     return launch_ffn2_mid(a, s);
   if (a.B == 128) return launch_ffn2_gemm(a, s);

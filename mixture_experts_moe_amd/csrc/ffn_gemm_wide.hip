@@ -1,0 +1,635 @@
+// Grouped GEMM for blocks of 128 tokens, bf16 or e4m3fn weights, with the
+// token operand held in registers: the expert kernels of experts holding a
+// few dozen to a hundred-odd tokens at large T, where every weight byte
+// must be read once from HBM at close to the streaming rate.
+//
+// Sources: the Hungarian news page "Az AWS új MoE-optimalizációkkal
+// gyorsítja a SageMaker AI-t", section "FP8 esetén a Triton backend
+// bizonyult gyorsabbnak" (FP8 scaling fused with the matrix product over
+// token groups of varying size, each weight read once from HBM), and section
+// "A fused MoE a számítási folyamat több lépését egyesíti" (the experts'
+// computation as one batched operation).
+//
+// A workgroup computes 256 weight rows x the block's 128 tokens: eight
+// waves of 128 rows x 32 tokens (wave w: rows 128 (w % 2), tokens 32 (w / 2);
+// the four waves of a block's first 64 tokens sit on four SIMDs).  Only the
+// weights go through LDS: direct-to-LDS 16-byte buffer loads, eight rows x
+// 128 contiguous bytes per instruction (128 bytes of every row per stage: 64
+// bf16 or 128 e4m3fn values of K), through a ring of D buffers of 32 KB.
+// Each wave loads its own 32 token rows of the stage's K straight into MFMA
+// fragment registers (a ring of D register sets), in the same load stream:
+// loads complete in issue order, so one wait per stage covers both operands.
+// Keeping the tokens out of LDS is what lets two or three 32 KB weight stages
+// be in flight per CU; staging 128 bf16 token rows there as well would leave
+// room for only one.  The weight loads carry the nontemporal hint when the
+// block is its expert's only one (its weights are read once); an expert with
+// several blocks reads them plainly, so that its other blocks' workgroups,
+// which run at about the same time, find them in L2.
+//
+// Weight LDS rows are 128 bytes in eight 16-byte slots, XOR-swizzled by
+// (row >> 1) & 7 so that the 16 rows one 16-lane group reads at the same k
+// spread over the banks.  e4m3fn fragments are read 8 bytes at a time and
+// widened to bf16 in registers (exact); the product runs on
+// v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  Rows past the weight
+// matrix (a channel tile overhanging I, or d for W2) and token rows of
+// padding slots are loaded from an offset past the end of their buffer
+// resource, which reads zeros without touching memory; their outputs are
+// never stored.  A wave whose 32 token rows hold no real slot only loads
+// weights and meets the barriers.
+//
+// W13: the tile's rows are 128 gate rows then the matching 128 up rows (128
+// channels of h), each wave holding gate and up of the same 64 channels; the
+// epilogue applies the e4m3fn scales and writes h = SiLU(gate) * up.  W2: 256
+// output channels; the epilogue scales by the channel scale and the slot's
+// gate and writes the slot's fp32 row.  The grid is rasterised per XCD like
+// the other tiles.
+
+#include "ffn_big_common.h"
+
+namespace moe {
+
+constexpr int kWidTokens = 128;  // block size B of this path
+constexpr int kWidRows = 256;    // weight rows per tile
+constexpr int kWidWaves = 8;
+constexpr int kWidThreads = 64 * kWidWaves;
+constexpr int kWidRowBytes = 128;                          // weight bytes per row and stage
+constexpr int kWidStageBytes = kWidRows * kWidRowBytes;    // 32 KB
+constexpr int kWidLoadsA = kWidStageBytes / 1024 / kWidWaves;  // 1 KB weight loads per wave
+static_assert(kWidLoadsA == 4, "four weight loads per wave and stage");
+
+// Wave layout and ring depth.  bf16 weights: each wave takes all 256 rows
+// for 16 tokens (RG = 1 row group), so every token row is loaded once per
+// workgroup.  e4m3fn weights: two row groups of 128 rows, 32 tokens per
+// wave (RG = 2): each weight fragment is widened to bf16 by half as many
+// waves, which there costs more than loading each token row twice.  The
+// token fragments of a stage take kNB * kSteps registers of 16 bytes per
+// lane, and the ring depth is what the 256 registers of a wave allow: three
+// stages for e4m3fn (eight fragments a stage), four for bf16 (two).
+template <typename WT>
+struct WidGeom {
+  static constexpr int kK = kWidRowBytes / static_cast<int>(sizeof(WT));  // K per stage
+  static constexpr int kSteps = kK / 32;                    // MFMA k-steps per stage
+  static constexpr int kRG = sizeof(WT) == 1 ? 2 : 1;       // row groups
+  static constexpr int kTA = 16 / kRG;                      // 16-row weight tiles per wave
+  static constexpr int kNB = kRG;                           // 16-token tiles per wave
+  static constexpr int kWaveTok = 16 * kNB;                 // tokens per wave
+  static constexpr int kLoadsT = kNB * kSteps;              // token loads per wave and stage
+  static constexpr int kD = kLoadsT <= 4 ? 4 : 3;           // ring depth
+  static_assert(kD * kWidStageBytes <= 160 * 1024, "the ring fits in LDS");
+};
+
+template <typename WT>
+using WidAcc = f32x4[WidGeom<WT>::kTA][WidGeom<WT>::kNB];
+
+#ifndef MOE_WID13_GROUP_COLS
+#define MOE_WID13_GROUP_COLS 2
+#endif
+#ifndef MOE_WID2_GROUP_COLS
+#define MOE_WID2_GROUP_COLS 4
+#endif
+
+__device__ __forceinline__ int wid_swz(int row) { return (row >> 1) & 7; }
+
+// Weight load i of wave w fills tile rows 8q .. 8q+7 (q = 4w + i): lane l
+// writes row 8q + l/8, physical slot l%8, which holds logical slot
+// (l%8) ^ swz(row).
+__device__ __forceinline__ int wid_a_row(int wave, int i, int lane) {
+  return 8 * (kWidLoadsA * wave + i) + lane / 8;
+}
+__device__ __forceinline__ int wid_a_slot(int row, int lane) { return (lane % 8) ^ wid_swz(row); }
+
+// One 1 KB direct-to-LDS weight load (16 bytes per lane from byte `off` of
+// `r` into `lds` + 16 * lane), nontemporal or plain; one 16-byte token
+// fragment into registers.  (Plain functions: the builtins are only visible
+// to the device pass, and the templates below call these.)
+__device__ __forceinline__ void wid_load_w_nt(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off,
+                                           0, 0, 2);
+}
+__device__ __forceinline__ void wid_load_w(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off,
+                                           0, 0, 0);
+}
+__device__ __forceinline__ uint4 wid_load_t(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return uint4{v[0], v[1], v[2], v[3]};
+}
+
+// Per-lane sources (byte offsets at K = 0 of the tile's range; an offset at
+// or past the resource's size reads zeros).  Token tile u, k-step j of stage
+// s: lane (r16, g) loads k = 32j + 8g .. +7 of its token row, the MFMA B
+// fragment layout.
+struct WidLoader {
+  __amdgpu_buffer_rsrc_t ra;  // the expert's weight matrix
+  __amdgpu_buffer_rsrc_t rb;  // token rows (x, or the block's h rows)
+  uint32_t a[kWidLoadsA];
+  uint32_t b[2];              // this lane's token row of tile u, k = 8g
+};
+
+template <typename WT>
+using WidTok = uint4[WidGeom<WT>::kNB][WidGeom<WT>::kSteps];
+
+// Stage s: weights into `stage`, this wave's token fragments into `tok`
+// (when kLive).
+template <typename WT, bool kNT, bool kLive>
+__device__ __forceinline__ void wid_issue(const WidLoader& ld, uint8_t* stage, WidTok<WT>& tok,
+                                          int s, int wave) {
+  using G = WidGeom<WT>;
+#pragma unroll
+  for (int i = 0; i < kWidLoadsA; ++i) {
+    uint8_t* dst = stage + (wave * kWidLoadsA + i) * 1024;
+    const uint32_t off = ld.a[i] + static_cast<uint32_t>(s) * kWidRowBytes;
+    if constexpr (kNT)
+      wid_load_w_nt(ld.ra, dst, off);
+    else
+      wid_load_w(ld.ra, dst, off);
+  }
+  if constexpr (kLive) {
+#pragma unroll
+    for (int u = 0; u < G::kNB; ++u)
+#pragma unroll
+      for (int j = 0; j < G::kSteps; ++j)
+        tok[u][j] = wid_load_t(ld.rb, ld.b[u] + static_cast<uint32_t>(s) * (2 * G::kK) + 64 * j);
+  }
+}
+
+// Part j (of kSteps) of stage s's loads: weight loads j * 4 / kSteps ..
+// (j + 1) * 4 / kSteps - 1 and the token fragments of k-step j.  A live wave
+// issues the next stage's loads a part at a time between the k-steps of the
+// current one, so that they reach the texture units spread over the stage
+// rather than as one burst at the barrier (a wave that issues them all at
+// once stalls behind them before its first MFMA).
+template <typename WT, bool kNT>
+__device__ __forceinline__ void wid_issue_part(const WidLoader& ld, uint8_t* stage,
+                                               WidTok<WT>& tok, int s, int wave, int j) {
+  using G = WidGeom<WT>;
+  constexpr int kPer = kWidLoadsA / G::kSteps;
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int i = j * kPer + q;
+    uint8_t* dst = stage + (wave * kWidLoadsA + i) * 1024;
+    const uint32_t off = ld.a[i] + static_cast<uint32_t>(s) * kWidRowBytes;
+    if constexpr (kNT)
+      wid_load_w_nt(ld.ra, dst, off);
+    else
+      wid_load_w(ld.ra, dst, off);
+  }
+#pragma unroll
+  for (int u = 0; u < G::kNB; ++u)
+    tok[u][j] = wid_load_t(ld.rb, ld.b[u] + static_cast<uint32_t>(s) * (2 * G::kK) + 64 * j);
+}
+
+// A lane's byte offset inside a weight stage for k-step j: row r16,
+// e4m3fn: logical slot 2j + g/2, half g&1; bf16: slot 4j + g.  Tiles start
+// at multiples of 16 rows, so the swizzle depends on r16 only.
+template <typename WT>
+__device__ __forceinline__ uint32_t wid_a_off(int j) {
+  const int lane = threadIdx.x & 63;
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  if constexpr (sizeof(WT) == 1)
+    return r16 * kWidRowBytes + (((2 * j + (g >> 1)) ^ wid_swz(r16)) << 4) + 8 * (g & 1);
+  else
+    return r16 * kWidRowBytes + (((4 * j + g) ^ wid_swz(r16)) << 4);
+}
+
+// k-step j of a stage: acc[t][u] += W(rows of tile t) . X(tokens of tile
+// u)^T.  Weight tile t: rows arow0 + 16t (t < kTA/2) and arow1 + 16(t -
+// kTA/2).
+template <typename WT>
+__device__ __forceinline__ void wid_kstep(const uint8_t* cur, const WidTok<WT>& tok, int j,
+                                          int arow0, int arow1, WidAcc<WT>& acc) {
+  using G = WidGeom<WT>;
+  // opaque copy: the k-step forms its base, a tile's offset is an immediate
+  uint32_t la = wid_a_off<WT>(j);
+  asm volatile("" : "+v"(la));
+#pragma unroll
+  for (int t = 0; t < G::kTA; ++t) {
+    const int row = t < G::kTA / 2 ? arow0 + 16 * t : arow1 + 16 * (t - G::kTA / 2);
+    bf16x8 a;
+    if constexpr (sizeof(WT) == 1) {
+      const uint2 q = *reinterpret_cast<const uint2*>(cur + la + row * kWidRowBytes);
+      a = as_frag(e4m3x8_to_frag_bits(q.x, q.y));
+    } else {
+      a = as_frag(*reinterpret_cast<const uint4*>(cur + la + row * kWidRowBytes));
+    }
+#pragma unroll
+    for (int u = 0; u < G::kNB; ++u) acc[t][u] = mfma16x16x32(a, as_frag(tok[u][j]), acc[t][u]);
+  }
+}
+
+#define WID_RING3(name)                                                      \
+  __shared__ __attribute__((aligned(1024))) uint8_t name##0[kWidStageBytes]; \
+  __shared__ __attribute__((aligned(1024))) uint8_t name##1[kWidStageBytes]; \
+  __shared__ __attribute__((aligned(1024))) uint8_t name##2[kWidStageBytes]; \
+  uint8_t* const name[4] = {name##0, name##1, name##2, name##2}
+#define WID_RING4(name)                                                      \
+  __shared__ __attribute__((aligned(1024))) uint8_t name##0[kWidStageBytes]; \
+  __shared__ __attribute__((aligned(1024))) uint8_t name##1[kWidStageBytes]; \
+  __shared__ __attribute__((aligned(1024))) uint8_t name##2[kWidStageBytes]; \
+  __shared__ __attribute__((aligned(1024))) uint8_t name##3[kWidStageBytes]; \
+  uint8_t* const name[4] = {name##0, name##1, name##2, name##3}
+
+// The ring of depth D: stage s in LDS buffer and register set s % D; stages
+// 0 .. D-2 are issued up front.  At stage s a wave waits until its loads of
+// s have landed (only its loads of the D-2 stages after s may stay
+// outstanding, kL per stage), meets the other waves (after which all of
+// stage s's weights are in LDS and nobody reads buffer (s - 1) % D any
+// more), issues stage s + D - 1 into that buffer and register set while
+// there is one, and runs stage s's MFMAs.  The loop goes D stages at a time;
+// the last D-1 .. 2D-2 stages run as a fixed sequence chosen by the stage
+// count mod D once, before the loop, so every wait count, buffer and
+// register index is a compile-time constant (the LDS buffers are separate
+// arrays, so the compiler sees that reads of one stage do not depend on the
+// loads into another).  kLive: the wave's 32 token rows hold a real slot
+// (else it only loads weights and meets the barriers); kNT: weight loads
+// with the nontemporal hint.
+template <typename WT, bool kNT, bool kLive>
+struct WidRing {
+  using G = WidGeom<WT>;
+  static constexpr int D = G::kD;
+  static constexpr int kL = kWidLoadsA + (kLive ? G::kLoadsT : 0);
+  static_assert(kL * (D - 2) <= 63, "wait counts fit the 6-bit vmcnt field");
+  const WidLoader& ld;
+  uint8_t* const (&buf)[4];
+  int wave, arow0, arow1;
+
+  // stage s in buffer / register set p with W later stages issued; issues
+  // stage s + D - 1 into set (p + D - 1) % D when kIssue
+  template <int p, int W, bool kIssue>
+  __device__ __forceinline__ void step(int s, WidTok<WT> (&tok)[G::kD], WidAcc<WT>& acc) const {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kL * W));
+    big_barrier();
+    constexpr int n = (p + D - 1) % D;
+    if constexpr (kLive) {
+      // the next stage's loads a part at a time, each before one k-step
+#pragma unroll
+      for (int j = 0; j < G::kSteps; ++j) {
+        if constexpr (kIssue) wid_issue_part<WT, kNT>(ld, buf[n], tok[n], s + D - 1, wave, j);
+        wid_kstep<WT>(buf[p], tok[p], j, arow0, arow1, acc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else if constexpr (kIssue) {
+      wid_issue<WT, kNT, false>(ld, buf[n], tok[n], s + D - 1, wave);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // the last N stages from s (s a multiple of D): stage s + i waits with
+  // min(D - 2, N - 1 - i) later stages issued and issues while
+  // i < N - (D - 1)
+  template <int I, int N>
+  __device__ __forceinline__ void tail(int s, WidTok<WT> (&tok)[G::kD], WidAcc<WT>& acc) const {
+    if constexpr (I < N) {
+      constexpr int W = (N - 1 - I) < (D - 2) ? (N - 1 - I) : (D - 2);
+      step<I % D, W, (I < N - (D - 1))>(s + I, tok, acc);
+      tail<I + 1, N>(s, tok, acc);
+    }
+  }
+
+  // R = nst % D; nst >= D
+  template <int R>
+  __device__ __forceinline__ void run_r(int nst, WidAcc<WT>& acc) const {
+    WidTok<WT> tok[G::kD];
+#pragma unroll
+    for (int i = 0; i < D - 1; ++i) wid_issue<WT, kNT, kLive>(ld, buf[i], tok[i], i, wave);
+    int s = 0;
+    for (; s + 2 * D - 1 <= nst; s += D) {  // D stages that each issue the one D-1 ahead
+      step<0, D - 2, true>(s, tok, acc);
+      step<1, D - 2, true>(s + 1, tok, acc);
+      step<2, D - 2, true>(s + 2, tok, acc);
+      if constexpr (D == 4) step<3, D - 2, true>(s + 3, tok, acc);
+    }
+    tail<0, (R == D - 1 ? D - 1 : R + D)>(s, tok, acc);
+  }
+
+  __device__ __forceinline__ void run(int nst, WidAcc<WT>& acc) const {
+    const int r = nst % D;
+    if (r == 0) run_r<0>(nst, acc);
+    else if (r == 1) run_r<1>(nst, acc);
+    else if (r == 2) run_r<2>(nst, acc);
+    else if constexpr (D == 4) run_r<3>(nst, acc);
+  }
+};
+
+template <typename WT>
+__device__ __forceinline__ void wid_run(const WidLoader& ld, uint8_t* const (&buf)[4], int nst,
+                                        int wave, int arow0, int arow1, bool nt, bool live,
+                                        WidAcc<WT>& acc) {
+  if (nt) {
+    if (live)
+      WidRing<WT, true, true>{ld, buf, wave, arow0, arow1}.run(nst, acc);
+    else
+      WidRing<WT, true, false>{ld, buf, wave, arow0, arow1}.run(nst, acc);
+  } else {
+    if (live)
+      WidRing<WT, false, true>{ld, buf, wave, arow0, arow1}.run(nst, acc);
+    else
+      WidRing<WT, false, false>{ld, buf, wave, arow0, arow1}.run(nst, acc);
+  }
+}
+
+// The block is its expert's only one (the neighbours, if any, belong to
+// other experts): its weights are read once.
+__device__ __forceinline__ bool wid_single_block(const int32_t* block_expert, int b, int nblocks,
+                                                 int e) {
+  const bool before = b > 0 && block_expert[b - 1] == e;
+  const bool after = b + 1 < nblocks && block_expert[b + 1] == e;
+  return !before && !after;
+}
+
+// ------------------------------------------------------------ W13 + SiLU*mul
+// Tile (b, y): channels n0 = 128y .. +127 (rows: 128 gate, then 128 up;
+// channels at or past I read zeros and are not stored) x the 128 tokens of
+// row block b.  Wave w holds gate and up of channels n0 + 64 (w % 2) .. +63
+// for tokens 32 (w / 2) .. +31.
+
+template <typename WT>
+__device__ __forceinline__ void wide13_tile(WidLoader& ld, uint8_t* const (&buf)[4],
+                                            const int32_t* blk, const float* s13, int scale_mode,
+                                            bf16_t* h, int b, int e, int n0, int d, int I, int k,
+                                            int A, uint32_t xbytes, bool nt) {
+  using G = WidGeom<WT>;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  const int wm = wave % G::kRG, wn = wave / G::kRG;
+#pragma unroll
+  for (int u = 0; u < G::kNB; ++u) {
+    const int f = blk[G::kWaveTok * wn + 16 * u + r16];
+    ld.b[u] = f < A ? 2 * (static_cast<uint32_t>(f / k) * d + 8 * g) : xbytes;
+  }
+  WidAcc<WT> acc;
+#pragma unroll
+  for (int t = 0; t < G::kTA; ++t)
+#pragma unroll
+    for (int u = 0; u < G::kNB; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const bool live = __builtin_amdgcn_readfirstlane(blk[G::kWaveTok * wn]) < A;
+  const int arow0 = (128 / G::kRG) * wm;
+  wid_run<WT>(ld, buf, d / G::kK, wave, arow0, 128 + arow0, nt, live, acc);
+  if (!live) return;
+
+  // lane: token column r16 of tile u, channels n0 + arow0 + 16t + 4g .. +3
+  // (gate in tile t, up in tile t + kTA/2)
+  const size_t two_i = 2 * static_cast<size_t>(I);
+#pragma unroll
+  for (int t = 0; t < G::kTA / 2; ++t) {
+    const int c = n0 + arow0 + 16 * t + 4 * g;
+    if (c >= I) continue;
+    float sg[4], su[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      if constexpr (sizeof(WT) == 1) {
+        sg[v] = load_scale(s13, scale_mode, e, static_cast<size_t>(e) * two_i + c + v);
+        su[v] = load_scale(s13, scale_mode, e, static_cast<size_t>(e) * two_i + I + c + v);
+      } else {
+        sg[v] = su[v] = 1.0f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < G::kNB; ++u) {
+      const size_t row = static_cast<size_t>(b) * kWidTokens + G::kWaveTok * wn + 16 * u + r16;
+      uint32_t packed[2];
+#pragma unroll
+      for (int v = 0; v < 4; v += 2) {
+        const float h0 = silu(acc[t][u][v] * sg[v]) * (acc[t + G::kTA / 2][u][v] * su[v]);
+        const float h1 =
+            silu(acc[t][u][v + 1] * sg[v + 1]) * (acc[t + G::kTA / 2][u][v + 1] * su[v + 1]);
+        packed[v / 2] = static_cast<uint32_t>(f32_to_bf16(h0)) |
+                        (static_cast<uint32_t>(f32_to_bf16(h1)) << 16);
+      }
+      *reinterpret_cast<uint2*>(h + row * I + c) = uint2{packed[0], packed[1]};
+    }
+  }
+}
+
+template <typename WT>
+__global__ __launch_bounds__(kWidThreads) void ffn13_wide_kernel(
+    const bf16_t* __restrict__ x, const WT* __restrict__ w13, const float* __restrict__ s13,
+    int scale_mode, const int32_t* __restrict__ sorted_ids,
+    const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded,
+    bf16_t* __restrict__ h, int d, int I, int k, int A, int T, int gx, int gy) {
+  using G = WidGeom<WT>;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const BigTile tl = big_tile_of<MOE_WID13_GROUP_COLS>(blockIdx.x, gx, gy);
+  if (!tl.live) return;  // uniform
+  const int b = tl.b;
+  const int npad = *num_padded;
+  if (b * kWidTokens >= npad) return;
+  const int32_t* blk = sorted_ids + static_cast<size_t>(b) * kWidTokens;
+  if (blk[0] >= A) return;  // real slots come first: this block holds none
+  const int e = block_expert[b];
+  const int n0 = tl.y * 128;
+  const size_t two_i = 2 * static_cast<size_t>(I);
+  const uint32_t wbytes = static_cast<uint32_t>(two_i * d * sizeof(WT));
+  const uint32_t xbytes = static_cast<uint32_t>(static_cast<size_t>(T) * d * 2);
+  const uint32_t row_bytes = static_cast<uint32_t>(d) * sizeof(WT);
+
+  WidLoader ld;
+  ld.ra = big_rsrc(w13 + static_cast<size_t>(e) * two_i * d, wbytes);
+  ld.rb = big_rsrc(x, xbytes);
+#pragma unroll
+  for (int i = 0; i < kWidLoadsA; ++i) {
+    const int r = wid_a_row(wave, i, lane);  // tile rows 0..127 gate, 128..255 up
+    const int c = n0 + (r & 127);
+    const uint32_t wrow = r < 128 ? c : I + c;
+    ld.a[i] = c < I ? wrow * row_bytes + 16 * wid_a_slot(r, lane) : wbytes;
+  }
+  const bool nt = wid_single_block(block_expert, b, npad / kWidTokens, e);
+  if constexpr (G::kD == 3) {
+    WID_RING3(buf);
+    wide13_tile<WT>(ld, buf, blk, s13, scale_mode, h, b, e, n0, d, I, k, A, xbytes, nt);
+  } else {
+    WID_RING4(buf);
+    wide13_tile<WT>(ld, buf, blk, s13, scale_mode, h, b, e, n0, d, I, k, A, xbytes, nt);
+  }
+}
+
+// ------------------------------------------------------------ W2 + gate scale
+// Tile (b, y, z): output channels n0 = 256y .. +255 (those at or past d read
+// zeros and are not stored) x the block's 128 h rows, over K range z.  Wave
+// w holds channels n0 + 128 (w % 2) .. +127 for tokens 32 (w / 2) .. +31.
+
+template <typename WT>
+__device__ __forceinline__ void wide2_tile(WidLoader& ld, uint8_t* const (&buf)[4],
+                                           const int32_t* blk, const float* s2, int scale_mode,
+                                           const float* topk_w, float* y, int e, int n0, int d,
+                                           int I, int A, int k_begin, int nst, uint32_t hbytes,
+                                           bool nt) {
+  using G = WidGeom<WT>;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  const int wm = wave % G::kRG, wn = wave / G::kRG;
+  // h rows of the block; rows of padding slots read zeros
+#pragma unroll
+  for (int u = 0; u < G::kNB; ++u) {
+    const int r = G::kWaveTok * wn + 16 * u + r16;
+    ld.b[u] = blk[r] < A ? 2 * (static_cast<uint32_t>(r) * I + k_begin + 8 * g) : hbytes;
+  }
+  WidAcc<WT> acc;
+#pragma unroll
+  for (int t = 0; t < G::kTA; ++t)
+#pragma unroll
+    for (int u = 0; u < G::kNB; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // weight rows arow0 .. +16 kTA - 1: consecutive 16-row tiles
+  const bool live = __builtin_amdgcn_readfirstlane(blk[G::kWaveTok * wn]) < A;
+  const int arow0 = (256 / G::kRG) * wm;
+  wid_run<WT>(ld, buf, nst, wave, arow0, arow0 + 8 * G::kTA, nt, live, acc);
+  if (!live) return;
+
+  // lane: token column r16 of tile u, channels n0 + arow0 + 16t + 4g .. +3
+#pragma unroll
+  for (int u = 0; u < G::kNB; ++u) {
+    const int f = blk[G::kWaveTok * wn + 16 * u + r16];
+    if (f < A) {
+      const float gate = topk_w[f];
+      float* yrow = y + static_cast<size_t>(f) * d;
+#pragma unroll
+      for (int t = 0; t < G::kTA; ++t) {
+        const int c = n0 + arow0 + 16 * t + 4 * g;
+        if (c >= d) continue;
+        float sc[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+        if constexpr (sizeof(WT) == 1) {
+          const size_t base = static_cast<size_t>(e) * d + c;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) sc[v] = load_scale(s2, scale_mode, e, base + v);
+        }
+        *reinterpret_cast<float4*>(yrow + c) =
+            float4{acc[t][u][0] * sc[0] * gate, acc[t][u][1] * sc[1] * gate,
+                   acc[t][u][2] * sc[2] * gate, acc[t][u][3] * sc[3] * gate};
+      }
+    }
+  }
+}
+
+template <typename WT>
+__global__ __launch_bounds__(kWidThreads) void ffn2_wide_kernel(
+    const bf16_t* __restrict__ h, const WT* __restrict__ w2, const float* __restrict__ s2,
+    int scale_mode, const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
+    const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded,
+    float* __restrict__ y_part, int d, int I, int A, int ksplit, int gx, int gy) {
+  using G = WidGeom<WT>;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const BigTile tl = big_tile_of<MOE_WID2_GROUP_COLS>(blockIdx.x, gx, gy);
+  if (!tl.live) return;
+  const int b = tl.b;
+  const int npad = *num_padded;
+  if (b * kWidTokens >= npad) return;
+  const int32_t* blk = sorted_ids + static_cast<size_t>(b) * kWidTokens;
+  if (blk[0] >= A) return;
+  const int e = block_expert[b];
+  const int n0 = tl.y * kWidRows;
+  const int k_begin = blockIdx.z * ksplit;
+  const int nst = (min(I, k_begin + ksplit) - k_begin) / G::kK;
+  float* y = y_part + static_cast<size_t>(blockIdx.z) * A * d;
+  const uint32_t wbytes = static_cast<uint32_t>(static_cast<size_t>(d) * I * sizeof(WT));
+  const uint32_t hbytes = static_cast<uint32_t>(static_cast<size_t>(kWidTokens) * I * 2);
+
+  WidLoader ld;
+  ld.ra = big_rsrc(w2 + static_cast<size_t>(e) * d * I, wbytes);
+  ld.rb = big_rsrc(h + static_cast<size_t>(b) * kWidTokens * I, hbytes);
+#pragma unroll
+  for (int i = 0; i < kWidLoadsA; ++i) {
+    const int r = wid_a_row(wave, i, lane);
+    const int n = n0 + r;
+    ld.a[i] = n < d ? (static_cast<uint32_t>(n) * I + k_begin) * static_cast<uint32_t>(sizeof(WT)) +
+                          16 * wid_a_slot(r, lane)
+                    : wbytes;
+  }
+  const bool nt = wid_single_block(block_expert, b, npad / kWidTokens, e);
+  if constexpr (G::kD == 3) {
+    WID_RING3(buf);
+    wide2_tile<WT>(ld, buf, blk, s2, scale_mode, topk_w, y, e, n0, d, I, A, k_begin, nst,
+                   hbytes, nt);
+  } else {
+    WID_RING4(buf);
+    wide2_tile<WT>(ld, buf, blk, s2, scale_mode, topk_w, y, e, n0, d, I, A, k_begin, nst,
+                   hbytes, nt);
+  }
+}
+
+// ------------------------------------------------------------ launchers
+
+int wide_kchunk(int w_dtype) {
+  return w_dtype == kDtypeE4M3FN ? WidGeom<fp8_t>::kK : WidGeom<bf16_t>::kK;
+}
+static int wide_depth(int w_dtype) {
+  return w_dtype == kDtypeE4M3FN ? WidGeom<fp8_t>::kD : WidGeom<bf16_t>::kD;
+}
+
+// K stages of 128 bytes of weight row (d and I multiples of the stage's K:
+// 64 for bf16, 128 for e4m3fn; I also of 32), at least the ring depth of
+// stages per K range, and 32-bit byte offsets into an expert's W13
+// (2I x d), x (T x d bf16) and a block's h rows.
+bool wide_gemm_fits(int64_t T, int d, int I, int w_dtype) {
+#ifdef MOE_NO_WIDE_GEMM
+  return false;
+#else
+  if (w_dtype != kDtypeBF16 && w_dtype != kDtypeE4M3FN) return false;
+  const int kk = wide_kchunk(w_dtype), depth = wide_depth(w_dtype);
+  const int64_t ws = w_dtype == kDtypeE4M3FN ? 1 : 2;
+  const int64_t lim = int64_t(1) << 31;
+  return d % kk == 0 && I % kk == 0 && I % 32 == 0 && d / kk >= depth && I / kk >= depth &&
+         2 * int64_t(I) * d * ws < lim && T * d * 2 < lim && int64_t(kWidTokens) * I * 2 < lim;
+#endif
+}
+
+static bool wide_args_ok(const FfnArgs& a) {
+  return a.B == kWidTokens && a.act_dtype == kDtypeBF16 && !a.act_mx &&
+         wide_gemm_fits(a.T, a.d, a.I, a.w_dtype);
+}
+
+static int wide_grid(int gx, int gy) {
+  const int total = gx * gy;
+  return (total + kBigXcds - 1) / kBigXcds * kBigXcds;
+}
+
+template <typename WT>
+static void wide13_go(const FfnArgs& a, hipStream_t s) {
+  const int gx = a.cap / kWidTokens, gy = (a.I + 127) / 128;
+  ffn13_wide_kernel<WT><<<wide_grid(gx, gy), kWidThreads, 0, s>>>(
+      static_cast<const bf16_t*>(a.x), static_cast<const WT*>(a.w13), a.s13, a.scale_mode,
+      a.sorted_ids, a.block_expert, a.num_padded, static_cast<bf16_t*>(a.h), a.d, a.I, a.k, a.A,
+      a.T, gx, gy);
+}
+
+template <typename WT>
+static void wide2_go(const FfnArgs& a, hipStream_t s) {
+  const int gx = a.cap / kWidTokens, gy = (a.d + kWidRows - 1) / kWidRows;
+  ffn2_wide_kernel<WT><<<dim3(wide_grid(gx, gy), 1, a.splits), kWidThreads, 0, s>>>(
+      static_cast<const bf16_t*>(a.h), static_cast<const WT*>(a.w2), a.s2, a.scale_mode,
+      a.topk_w, a.sorted_ids, a.block_expert, a.num_padded, a.y_part, a.d, a.I, a.A, a.ksplit,
+      gx, gy);
+}
+
+hipError_t launch_ffn13_wide(const FfnArgs& a, hipStream_t s) {
+  if (!wide_args_ok(a)) return hipErrorInvalidValue;
+  if (a.w_dtype == kDtypeE4M3FN)
+    wide13_go<fp8_t>(a, s);
+  else
+    wide13_go<bf16_t>(a, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_ffn2_wide(const FfnArgs& a, hipStream_t s) {
+  // every K range a whole number of stages, at least the ring depth
+  const int kk = wide_kchunk(a.w_dtype), depth = wide_depth(a.w_dtype);
+  if (!wide_args_ok(a) || a.splits < 1 || a.ksplit < depth * kk || a.ksplit % kk != 0 ||
+      static_cast<int64_t>(a.splits - 1) * a.ksplit >= a.I ||
+      a.I - static_cast<int64_t>(a.splits - 1) * a.ksplit < depth * kk)
+    return hipErrorInvalidValue;
+  if (a.w_dtype == kDtypeE4M3FN)
+    wide2_go<fp8_t>(a, s);
+  else
+    wide2_go<bf16_t>(a, s);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -99,6 +99,9 @@ struct FfnArgs {
   // (ffn2_combine_ints() int32), zeroed by the routing launch; null when the
   // combine is a launch of its own.
   int32_t* combine_cnt;
+  // Blocks of 128 on the register-token tile (the plan's choice under the
+  // automatic schedule) rather than the 128-token GEMM.
+  bool wide;
 };
 
 hipError_t launch_ffn13(const FfnArgs& a, hipStream_t s);
@@ -129,6 +132,21 @@ int big_w2_kchunk();  // a split of the big W2's K range is a multiple of this
 bool mid_gemm_fits(int64_t T, int d, int I);
 hipError_t launch_ffn13_mid(const FfnArgs& a, hipStream_t s);
 hipError_t launch_ffn2_mid(const FfnArgs& a, hipStream_t s);
+// 128-token tile with the token operand in registers, bf16 or e4m3fn
+// weights with bf16 activations (K stages of 128 weight bytes: d and I
+// multiples of 64 for bf16, 128 for e4m3fn, at least three or four stages;
+// I a multiple of 32; 32-bit offsets).  A split of W2's K range is a
+// multiple of wide_kchunk() elements and holds at least four of them.
+bool wide_gemm_fits(int64_t T, int d, int I, int w_dtype);
+int wide_kchunk(int w_dtype);
+hipError_t launch_ffn13_wide(const FfnArgs& a, hipStream_t s);
+hipError_t launch_ffn2_wide(const FfnArgs& a, hipStream_t s);
+inline bool wide_use(int w_dtype, int act_dtype, bool act_mx, int B, int64_t T, int d, int I) {
+  return B == 128 && act_dtype == kDtypeBF16 && !act_mx && wide_gemm_fits(T, d, I, w_dtype);
+}
+inline bool wide_use(const FfnArgs& a) {
+  return a.wide && wide_use(a.w_dtype, a.act_dtype, a.act_mx, a.B, a.T, a.d, a.I);
+}
 
 // Row blocks that hold at least one slot: the realised blocks are at most
 // the capacity's, and at most one partial block per used expert plus the

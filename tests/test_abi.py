@@ -110,13 +110,18 @@ def test_schedule_field_validation(lib):
 
 def test_queue_schedule_workspace(lib):
     """The queue's counters take workspace only where the 128-token GEMM runs
-    with that schedule."""
+    with that schedule: not under the automatic schedule where blocks of 128
+    take the register-token tile (bf16 weights, d = 256 is four of its K
+    stages), but there where they do not (e4m3fn, two stages, below its
+    three)."""
     def nbytes(bm, schedule, w=B.MOE_DTYPE_BF16):
         return B.moe_workspace_bytes(
             B.make_desc(512, 256, 8, 256, B.MOE_DTYPE_BF16, w, bm, None, schedule), 2, True)
     for w in (B.MOE_DTYPE_BF16, E4):
-        assert nbytes(128, "auto", w) == nbytes(128, "queue", w) > nbytes(128, "static", w)
+        assert nbytes(128, "queue", w) > nbytes(128, "static", w)
         assert nbytes(128, "queue", w) - nbytes(128, "static", w) <= 4096
+    assert nbytes(128, "auto", B.MOE_DTYPE_BF16) == nbytes(128, "static", B.MOE_DTYPE_BF16)
+    assert nbytes(128, "auto", E4) == nbytes(128, "queue", E4)
     assert nbytes(64, "queue") == nbytes(64, "static")
     assert nbytes(256, "queue") == nbytes(256, "static")
 

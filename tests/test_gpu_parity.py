@@ -163,6 +163,16 @@ SMALL = [
     ("fp8_mid", dict(workload="fp8", d=768, I=256, E=16, k=4), 200, 128),
     ("fp8_mid", dict(workload="fp8", d=256, I=1024, E=2, k=1), 129, 128),
     ("fp8_mid", dict(workload="fp8", d=2048, I=512, E=32, k=8), 150, 128),
+    # blocks of 128 on the register-token tile (bf16 ring of four, e4m3fn of
+    # three): tails of every length, channel tiles overhanging I and d,
+    # experts with one block (nontemporal weights) and with two, waves
+    # without tokens, per-tensor scales, W2's K split in two
+    ("bf16_wide", dict(workload="decode_bf16", d=320, I=448, E=8, k=2, x_std=1.0), 600, 128),
+    ("bf16_wide", dict(workload="decode_bf16", d=256, I=2304, E=4, k=1, x_std=1.0), 200, 128),
+    ("bf16_wide", dict(workload="decode_bf16", d=384, I=384, E=16, k=4, x_std=1.0), 100, 128),
+    ("fp8_wide", dict(workload="fp8", d=384, I=384, E=8, k=2), 300, 128),
+    ("fp8_wide", dict(workload="fp8", d=512, I=640, E=4, k=2, scale_mode="tensor"), 300, 128),
+    ("fp8_wide", dict(workload="fp8", d=1024, I=4096, E=2, k=1), 150, 128),
     # W8A8 (block-scaled e4m3fn x and h, blocks of 256): one token, a ragged
     # block, several blocks per expert, E = 1, per-tensor scales, more
     # channel tiles than one, and W2's K split in two (I = 4096, few tiles)
@@ -279,22 +289,31 @@ def test_w8a8_forward_equals_stage_composition_and_is_deterministic():
     assert zero.shape == (0, inp.d)
 
 
-def test_fp8_mid_tile_forward_equals_stage_composition_and_graph():
-    """e4m3fn weights in blocks of 128 (the 128-token tile): moe_forward is
+@pytest.mark.parametrize("wl,bm,over", [
+    ("fp8", 128, dict(d=256, I=512, E=8, k=2)),
+    ("fp8", 128, dict(d=512, I=512, E=8, k=2)),
+    ("decode_bf16", 128, dict(d=320, I=2304, E=4, k=2, x_std=1.0)),
+], ids=["fp8-lds-tile", "fp8-register-tile", "bf16-register-tile-split"])
+def test_tile_forward_equals_stage_composition_and_graph(wl, bm, over):
+    """Blocks of 128 on the 128-token tile with both operands through LDS
+    (e4m3fn, d = 256: too few K stages for the other) and on the
+    register-token tile (the bf16 case splits W2's K): moe_forward is
     deterministic, equals routing + align + moe_expert_ffn bit for bit, and a
     recorded graph replays it exactly."""
-    inp = synth.make_inputs("fp8", T=400, device=DEV, d=512, I=512, E=8, k=2)
-    sc = (inp.s13, inp.s2)
-    out1 = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, sc)
-    out2 = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, sc)
+    note(f"stage composition {wl} B={bm}")
+    inp = synth.make_inputs(wl, T=400, device=DEV, **over)
+    sc = (inp.s13, inp.s2) if inp.w == "e4m3fn" else None
+    wdt = B.MOE_DTYPE_E4M3FN if inp.w == "e4m3fn" else B.MOE_DTYPE_BF16
+    out1 = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, sc, block_m=bm)
+    out2 = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, sc, block_m=bm)
     _, ids, w = B.moe_route(inp.x, inp.w_gate, inp.top_k)
-    counts, sorted_ids, block_expert, num_padded, bm = B.moe_align(
-        ids, inp.E, hidden=inp.d, intermediate=inp.I, weight_dtype=B.MOE_DTYPE_E4M3FN)
-    assert bm == 128
+    counts, sorted_ids, block_expert, num_padded, got_bm = B.moe_align(
+        ids, inp.E, block_m=bm, hidden=inp.d, intermediate=inp.I, weight_dtype=wdt)
+    assert got_bm == bm
     out3 = B.moe_expert_ffn(inp.x, inp.w13, inp.w2, inp.top_k, w, sorted_ids, block_expert,
-                            num_padded, sc)
+                            num_padded, sc, block_m=bm)
     out = torch.empty_like(inp.x)
-    g = B.MoeGraph(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, sc, out=out)
+    g = B.MoeGraph(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, sc, out=out, block_m=bm)
     try:
         for _ in range(3):
             out.fill_(float("nan"))
@@ -770,7 +789,8 @@ SCHED_CASES = [
 @pytest.mark.parametrize("name,over,T", SCHED_CASES, ids=[f"{c[0]}-T{c[2]}" for c in SCHED_CASES])
 def test_schedules_give_identical_bits(name, over, T):
     """The queue and the static raster run the same tile arithmetic, so the
-    layer's output is bit-identical; the queue's is also the oracle's."""
+    layer's output is bit-identical; the queue's is also the oracle's, and so
+    is the automatic schedule's (the register-token tile where it fits)."""
     note(f"schedules {name} T={T}")
     over = dict(over)
     wl = over.pop("workload")
@@ -781,8 +801,8 @@ def test_schedules_give_identical_bits(name, over, T):
     _, ids, _ = B.moe_route(inp.x, inp.w_gate, inp.top_k)
     torch.cuda.synchronize()
     assert torch.equal(outs["static"], outs["queue"])
-    assert torch.equal(outs["auto"], outs["queue"])
     compare_layer(inp, outs["queue"], ids)
+    compare_layer(inp, outs["auto"], ids)
 
 
 def test_queue_counters_restart_every_call():
@@ -792,7 +812,8 @@ def test_queue_counters_restart_every_call():
     small = synth.make_inputs("decode_bf16", T=200, device=DEV, d=512, I=512, E=8, x_std=1.0,
                               seed=5)
     ws_bytes = B.moe_workspace_bytes(
-        B.make_desc(1500, 512, 8, 512, B.MOE_DTYPE_BF16, B.MOE_DTYPE_BF16, 128), 2, True)
+        B.make_desc(1500, 512, 8, 512, B.MOE_DTYPE_BF16, B.MOE_DTYPE_BF16, 128, None, "queue"), 2,
+        True)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
     for inp in (big, small, big, small):
         ref = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, block_m=128,
@@ -816,7 +837,8 @@ sys.path.insert(0, sys.argv[1])
 from mixture_experts_moe_amd import binding as B, synth
 inp = synth.make_inputs("decode_bf16", T=300, device="cuda:0", d=512, I=256, x_std=1.0)
 out = torch.empty_like(inp.x)
-g = B.MoeGraph(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, out=out, block_m=128)
+g = B.MoeGraph(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, out=out, block_m=128,
+               schedule="queue")
 g.launch()
 ref = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, block_m=128,
                     schedule="static")

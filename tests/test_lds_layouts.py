@@ -132,3 +132,87 @@ def test_ring_consumes_every_stage_in_order(nst):
 def test_ring_needs_a_multiple_of_four_stages():
     with pytest.raises(AssertionError):
         _ring(6)
+
+
+# ---------------------------------------------------------------- the 128-token register-token tile
+# (mixture_experts_moe_amd/csrc/ffn_gemm_wide.hip): weights only through
+# LDS, 256 rows x 128 bytes per stage in eight-row loads; the token
+# fragments of a stage in one of D register sets; a ring of depth D (3 for
+# e4m3fn, 4 for bf16).
+
+
+def test_wide_weight_fragments_find_their_rows():
+    """Weight load q covers rows 8q .. 8q+7, lane l -> row 8q + l/8, physical
+    slot (l%8) holding logical slot (l%8) ^ ((row >> 1) & 7); the fragment
+    reads of each k-step find k = 32j + 8g .. +7 of row r16 of every tile."""
+    for wsize in (1, 2):
+        lds = {}
+        for q in range(32):
+            for lane in range(64):
+                row = 8 * q + lane // 8
+                slot = (lane % 8) ^ ((row >> 1) & 7)
+                for byte in range(16):
+                    lds[q * 1024 + lane * 16 + byte] = (row, (16 * slot + byte) // wsize)
+        for lane in range(64):
+            r16, g = lane % 16, lane // 16
+            sw = (r16 >> 1) & 7
+            for j in range(128 // wsize // 32):
+                if wsize == 1:
+                    off = r16 * 128 + (((2 * j + (g >> 1)) ^ sw) << 4) + 8 * (g & 1)
+                    elems = [off + e for e in range(8)]
+                else:
+                    off = r16 * 128 + (((4 * j + g) ^ sw) << 4)
+                    elems = [off + 2 * e for e in range(8)]
+                for tile in range(0, 256, 16):
+                    for e in range(8):
+                        assert lds[elems[e] + tile * 128] == (tile + r16, 32 * j + 8 * g + e)
+
+
+def _wide_ring(nst, D):
+    """WidRing::run: stages 0 .. D-2 issued up front; the loop runs D issuing
+    stages at a time while s + 2D - 1 <= nst; the tail of N stages (N = D-1
+    when nst % D == D-1, else nst % D + D) waits with min(D-2, N-1-i) later
+    stages issued and issues while i < N - (D-1)."""
+    issued, consumed, held = [], [], {}
+
+    def issue(buf, s):
+        assert s < nst and buf == s % D and buf not in held
+        held[buf] = s
+        issued.append(s)
+
+    def step(p, W, k_issue, s):
+        later = [x for x in issued if x > s]
+        assert s in issued and len(later) == W, (nst, D, s, W, later)
+        assert held.get(p) == s
+        del held[p]
+        if k_issue:
+            issue((p + D - 1) % D, s + D - 1)
+        consumed.append(s)
+
+    for i in range(D - 1):
+        issue(i, i)
+    s = 0
+    while s + 2 * D - 1 <= nst:
+        for p in range(D):
+            step(p, D - 2, True, s + p)
+        s += D
+    R = nst % D
+    N = D - 1 if R == D - 1 else R + D
+    assert s + N == nst
+    for i in range(N):
+        step(i % D, min(D - 2, N - 1 - i), i < N - (D - 1), s + i)
+    return consumed
+
+
+@pytest.mark.parametrize("D", [3, 4])
+@pytest.mark.parametrize("nst", list(range(4, 40)) + [45, 56, 112, 224])
+def test_wide_ring_consumes_every_stage_in_order(D, nst):
+    assert _wide_ring(nst, D) == list(range(nst))
+
+
+def test_wide_ring_shortest_k():
+    # the launcher asks for at least D stages; D - 1 would do, D - 2 would not
+    assert _wide_ring(3, 3) == [0, 1, 2]
+    assert _wide_ring(3, 4) == [0, 1, 2]
+    with pytest.raises(AssertionError):
+        _wide_ring(2, 4)
