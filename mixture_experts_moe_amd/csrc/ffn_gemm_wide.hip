@@ -10,9 +10,9 @@
 // "A fused MoE a számítási folyamat több lépését egyesíti" (the experts'
 // computation as one batched operation).
 //
-// A workgroup computes 256 weight rows x the block's 128 tokens: eight
-// waves of 128 rows x 32 tokens (wave w: rows 128 (w % 2), tokens 32 (w / 2);
-// the four waves of a block's first 64 tokens sit on four SIMDs).  Only the
+// A workgroup computes 256 weight rows x the block's 128 tokens with eight
+// waves (for bf16 weights each wave takes all 256 rows for 16 tokens, for
+// e4m3fn 128 rows for 32 tokens; see WidGeom).  Only the
 // weights go through LDS: direct-to-LDS 16-byte buffer loads, eight rows x
 // 128 contiguous bytes per instruction (128 bytes of every row per stage: 64
 // bf16 or 128 e4m3fn values of K), through a ring of D buffers of 32 KB.
@@ -49,13 +49,15 @@
 namespace moe {
 
 constexpr int kWidTokens = 128;  // block size B of this path
-constexpr int kWidRows = 256;    // weight rows per tile
-constexpr int kWidWaves = 8;
-constexpr int kWidThreads = 64 * kWidWaves;
-constexpr int kWidRowBytes = 128;                          // weight bytes per row and stage
-constexpr int kWidStageBytes = kWidRows * kWidRowBytes;    // 32 KB
-constexpr int kWidLoadsA = kWidStageBytes / 1024 / kWidWaves;  // 1 KB weight loads per wave
-static_assert(kWidLoadsA == 4, "four weight loads per wave and stage");
+constexpr int kWidRowBytes = 128;  // weight bytes per row and stage
+constexpr int kWidLoadsA = 4;      // 1 KB weight loads per wave and stage (32 rows)
+
+// Waves per workgroup for e4m3fn weights: 8 (256 rows, two row groups), or
+// 4 (128 rows, one row group, two workgroups per CU; measured slower at fp8
+// T = 2048: W13 1.96 against 1.77 ms).
+#ifndef MOE_WID8_WAVES
+#define MOE_WID8_WAVES 8
+#endif
 
 // Wave layout and ring depth.  bf16 weights: each wave takes all 256 rows
 // for 16 tokens (RG = 1 row group), so every token row is loaded once per
@@ -69,13 +71,18 @@ template <typename WT>
 struct WidGeom {
   static constexpr int kK = kWidRowBytes / static_cast<int>(sizeof(WT));  // K per stage
   static constexpr int kSteps = kK / 32;                    // MFMA k-steps per stage
-  static constexpr int kRG = sizeof(WT) == 1 ? 2 : 1;       // row groups
-  static constexpr int kTA = 16 / kRG;                      // 16-row weight tiles per wave
-  static constexpr int kNB = kRG;                           // 16-token tiles per wave
+  static constexpr int kWaves = sizeof(WT) == 1 ? MOE_WID8_WAVES : 8;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kRows = 32 * kWaves;                 // weight rows per tile
+  static constexpr int kStageBytes = kRows * kWidRowBytes;
+  static constexpr int kRG = kWaves == 8 && sizeof(WT) == 1 ? 2 : 1;  // row groups
+  static constexpr int kTA = kRows / 16 / kRG;              // 16-row weight tiles per wave
+  static constexpr int kNB = 8 * kRG / kWaves;              // 16-token tiles per wave
   static constexpr int kWaveTok = 16 * kNB;                 // tokens per wave
   static constexpr int kLoadsT = kNB * kSteps;              // token loads per wave and stage
   static constexpr int kD = kLoadsT <= 4 ? 4 : 3;           // ring depth
-  static_assert(kD * kWidStageBytes <= 160 * 1024, "the ring fits in LDS");
+  static_assert(kNB * 16 * kWaves / kRG == kWidTokens, "the waves cover the block");
+  static_assert(kD * kStageBytes <= 160 * 1024, "the ring fits in LDS");
 };
 
 template <typename WT>
@@ -218,16 +225,16 @@ __device__ __forceinline__ void wid_kstep(const uint8_t* cur, const WidTok<WT>& 
   }
 }
 
-#define WID_RING3(name)                                                      \
-  __shared__ __attribute__((aligned(1024))) uint8_t name##0[kWidStageBytes]; \
-  __shared__ __attribute__((aligned(1024))) uint8_t name##1[kWidStageBytes]; \
-  __shared__ __attribute__((aligned(1024))) uint8_t name##2[kWidStageBytes]; \
+#define WID_RING3(name, bytes)                                      \
+  __shared__ __attribute__((aligned(1024))) uint8_t name##0[bytes]; \
+  __shared__ __attribute__((aligned(1024))) uint8_t name##1[bytes]; \
+  __shared__ __attribute__((aligned(1024))) uint8_t name##2[bytes]; \
   uint8_t* const name[4] = {name##0, name##1, name##2, name##2}
-#define WID_RING4(name)                                                      \
-  __shared__ __attribute__((aligned(1024))) uint8_t name##0[kWidStageBytes]; \
-  __shared__ __attribute__((aligned(1024))) uint8_t name##1[kWidStageBytes]; \
-  __shared__ __attribute__((aligned(1024))) uint8_t name##2[kWidStageBytes]; \
-  __shared__ __attribute__((aligned(1024))) uint8_t name##3[kWidStageBytes]; \
+#define WID_RING4(name, bytes)                                      \
+  __shared__ __attribute__((aligned(1024))) uint8_t name##0[bytes]; \
+  __shared__ __attribute__((aligned(1024))) uint8_t name##1[bytes]; \
+  __shared__ __attribute__((aligned(1024))) uint8_t name##2[bytes]; \
+  __shared__ __attribute__((aligned(1024))) uint8_t name##3[bytes]; \
   uint8_t* const name[4] = {name##0, name##1, name##2, name##3}
 
 // The ring of depth D: stage s in LDS buffer and register set s % D; stages
@@ -367,8 +374,8 @@ __device__ __forceinline__ void wide13_tile(WidLoader& ld, uint8_t* const (&buf)
     for (int u = 0; u < G::kNB; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const bool live = __builtin_amdgcn_readfirstlane(blk[G::kWaveTok * wn]) < A;
-  const int arow0 = (128 / G::kRG) * wm;
-  wid_run<WT>(ld, buf, d / G::kK, wave, arow0, 128 + arow0, nt, live, acc);
+  const int arow0 = (G::kRows / 2 / G::kRG) * wm;
+  wid_run<WT>(ld, buf, d / G::kK, wave, arow0, G::kRows / 2 + arow0, nt, live, acc);
   if (!live) return;
 
   // lane: token column r16 of tile u, channels n0 + arow0 + 16t + 4g .. +3
@@ -406,7 +413,7 @@ __device__ __forceinline__ void wide13_tile(WidLoader& ld, uint8_t* const (&buf)
 }
 
 template <typename WT>
-__global__ __launch_bounds__(kWidThreads) void ffn13_wide_kernel(
+__global__ __launch_bounds__(WidGeom<WT>::kThreads) void ffn13_wide_kernel(
     const bf16_t* __restrict__ x, const WT* __restrict__ w13, const float* __restrict__ s13,
     int scale_mode, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded,
@@ -422,7 +429,8 @@ __global__ __launch_bounds__(kWidThreads) void ffn13_wide_kernel(
   const int32_t* blk = sorted_ids + static_cast<size_t>(b) * kWidTokens;
   if (blk[0] >= A) return;  // real slots come first: this block holds none
   const int e = block_expert[b];
-  const int n0 = tl.y * 128;
+  constexpr int kHalf = G::kRows / 2;  // channels per tile
+  const int n0 = tl.y * kHalf;
   const size_t two_i = 2 * static_cast<size_t>(I);
   const uint32_t wbytes = static_cast<uint32_t>(two_i * d * sizeof(WT));
   const uint32_t xbytes = static_cast<uint32_t>(static_cast<size_t>(T) * d * 2);
@@ -433,17 +441,17 @@ __global__ __launch_bounds__(kWidThreads) void ffn13_wide_kernel(
   ld.rb = big_rsrc(x, xbytes);
 #pragma unroll
   for (int i = 0; i < kWidLoadsA; ++i) {
-    const int r = wid_a_row(wave, i, lane);  // tile rows 0..127 gate, 128..255 up
-    const int c = n0 + (r & 127);
-    const uint32_t wrow = r < 128 ? c : I + c;
+    const int r = wid_a_row(wave, i, lane);  // tile rows: kHalf gate, then kHalf up
+    const int c = n0 + r % kHalf;
+    const uint32_t wrow = r < kHalf ? c : I + c;
     ld.a[i] = c < I ? wrow * row_bytes + 16 * wid_a_slot(r, lane) : wbytes;
   }
   const bool nt = wid_single_block(block_expert, b, npad / kWidTokens, e);
   if constexpr (G::kD == 3) {
-    WID_RING3(buf);
+    WID_RING3(buf, G::kStageBytes);
     wide13_tile<WT>(ld, buf, blk, s13, scale_mode, h, b, e, n0, d, I, k, A, xbytes, nt);
   } else {
-    WID_RING4(buf);
+    WID_RING4(buf, G::kStageBytes);
     wide13_tile<WT>(ld, buf, blk, s13, scale_mode, h, b, e, n0, d, I, k, A, xbytes, nt);
   }
 }
@@ -479,7 +487,7 @@ __device__ __forceinline__ void wide2_tile(WidLoader& ld, uint8_t* const (&buf)[
 
   // weight rows arow0 .. +16 kTA - 1: consecutive 16-row tiles
   const bool live = __builtin_amdgcn_readfirstlane(blk[G::kWaveTok * wn]) < A;
-  const int arow0 = (256 / G::kRG) * wm;
+  const int arow0 = (G::kRows / G::kRG) * wm;
   wid_run<WT>(ld, buf, nst, wave, arow0, arow0 + 8 * G::kTA, nt, live, acc);
   if (!live) return;
 
@@ -509,7 +517,7 @@ __device__ __forceinline__ void wide2_tile(WidLoader& ld, uint8_t* const (&buf)[
 }
 
 template <typename WT>
-__global__ __launch_bounds__(kWidThreads) void ffn2_wide_kernel(
+__global__ __launch_bounds__(WidGeom<WT>::kThreads) void ffn2_wide_kernel(
     const bf16_t* __restrict__ h, const WT* __restrict__ w2, const float* __restrict__ s2,
     int scale_mode, const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded,
@@ -525,7 +533,7 @@ __global__ __launch_bounds__(kWidThreads) void ffn2_wide_kernel(
   const int32_t* blk = sorted_ids + static_cast<size_t>(b) * kWidTokens;
   if (blk[0] >= A) return;
   const int e = block_expert[b];
-  const int n0 = tl.y * kWidRows;
+  const int n0 = tl.y * G::kRows;
   const int k_begin = blockIdx.z * ksplit;
   const int nst = (min(I, k_begin + ksplit) - k_begin) / G::kK;
   float* y = y_part + static_cast<size_t>(blockIdx.z) * A * d;
@@ -545,11 +553,11 @@ __global__ __launch_bounds__(kWidThreads) void ffn2_wide_kernel(
   }
   const bool nt = wid_single_block(block_expert, b, npad / kWidTokens, e);
   if constexpr (G::kD == 3) {
-    WID_RING3(buf);
+    WID_RING3(buf, G::kStageBytes);
     wide2_tile<WT>(ld, buf, blk, s2, scale_mode, topk_w, y, e, n0, d, I, A, k_begin, nst,
                    hbytes, nt);
   } else {
-    WID_RING4(buf);
+    WID_RING4(buf, G::kStageBytes);
     wide2_tile<WT>(ld, buf, blk, s2, scale_mode, topk_w, y, e, n0, d, I, A, k_begin, nst,
                    hbytes, nt);
   }
@@ -593,8 +601,9 @@ static int wide_grid(int gx, int gy) {
 
 template <typename WT>
 static void wide13_go(const FfnArgs& a, hipStream_t s) {
-  const int gx = a.cap / kWidTokens, gy = (a.I + 127) / 128;
-  ffn13_wide_kernel<WT><<<wide_grid(gx, gy), kWidThreads, 0, s>>>(
+  constexpr int kHalf = WidGeom<WT>::kRows / 2;
+  const int gx = a.cap / kWidTokens, gy = (a.I + kHalf - 1) / kHalf;
+  ffn13_wide_kernel<WT><<<wide_grid(gx, gy), WidGeom<WT>::kThreads, 0, s>>>(
       static_cast<const bf16_t*>(a.x), static_cast<const WT*>(a.w13), a.s13, a.scale_mode,
       a.sorted_ids, a.block_expert, a.num_padded, static_cast<bf16_t*>(a.h), a.d, a.I, a.k, a.A,
       a.T, gx, gy);
@@ -602,8 +611,9 @@ static void wide13_go(const FfnArgs& a, hipStream_t s) {
 
 template <typename WT>
 static void wide2_go(const FfnArgs& a, hipStream_t s) {
-  const int gx = a.cap / kWidTokens, gy = (a.d + kWidRows - 1) / kWidRows;
-  ffn2_wide_kernel<WT><<<dim3(wide_grid(gx, gy), 1, a.splits), kWidThreads, 0, s>>>(
+  constexpr int kRows = WidGeom<WT>::kRows;
+  const int gx = a.cap / kWidTokens, gy = (a.d + kRows - 1) / kRows;
+  ffn2_wide_kernel<WT><<<dim3(wide_grid(gx, gy), 1, a.splits), WidGeom<WT>::kThreads, 0, s>>>(
       static_cast<const bf16_t*>(a.h), static_cast<const WT*>(a.w2), a.s2, a.scale_mode,
       a.topk_w, a.sorted_ids, a.block_expert, a.num_padded, a.y_part, a.d, a.I, a.A, a.ksplit,
       gx, gy);
