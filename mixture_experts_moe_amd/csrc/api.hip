@@ -114,11 +114,14 @@ struct Plan {
 };
 
 // Block size of the regrouped layout.  Up to 64 tokens the weight-streaming
-// kernels run with B >= T: every expert's tokens fit one block (an expert
-// holds at most one slot per token), so each expert's weights are streamed
-// exactly once.  Larger batches use 128-token blocks and the token-tiled
-// grouped GEMM, and when experts average 256 tokens or more (bf16 weights,
-// fitting shapes) 256-token blocks and the large-tile GEMM.
+// kernels mostly run with B >= T: every expert's tokens fit one block (an
+// expert holds at most one slot per token), so each expert's weights are
+// streamed exactly once; where experts average few slots (at most 8 with
+// bf16 weights, 4 with e4m3fn) blocks of 16, an expert holding more taking
+// further blocks.  Larger batches use 128-token blocks (the register-token
+// tile, else the token-tiled grouped GEMM), and when experts average 256
+// tokens or more (bf16 weights, fitting shapes) 256-token blocks and the
+// large-tile GEMM.
 int default_block_m(const moe_desc* d, int top_k) {
   if (d->act_quant == MOE_ACT_MX_E4M3) return 256;  // the W8A8 tile
   if (d->weight_dtype == MOE_DTYPE_F32) return 16;
@@ -130,6 +133,13 @@ int default_block_m(const moe_desc* d, int top_k) {
   // the LDS-streaming kernel (an expert holding more takes further blocks)
   if (T <= 64 && d->weight_dtype == MOE_DTYPE_E4M3FN && bf16_act &&
       T * top_k <= 4 * d->num_experts && moe::dma_stream_fits(hid, inter, MOE_DTYPE_E4M3FN))
+    return 16;
+  // bf16 weights with experts averaging at most 8 slots (the decode shape
+  // at T = 32: 287 -> 279 us for W13 against blocks of 32, whose second
+  // token subtile is mostly padding); at 16 slots (T = 64) an expert's
+  // second block of 16 re-reads its weights and blocks of 32 win
+  if (T <= 64 && d->weight_dtype == MOE_DTYPE_BF16 && bf16_act &&
+      T * top_k <= 8 * d->num_experts && moe::dma_stream_fits(hid, inter, MOE_DTYPE_BF16))
     return 16;
   if (T <= 32) return 32;
   if (T <= 64) {

@@ -35,6 +35,9 @@
 namespace moe {
 
 constexpr int kDmaRowBytes = 512;  // bytes of one row per stage
+#ifndef MOE_DMA_TOKEN_MASK
+#define MOE_DMA_TOKEN_MASK 1
+#endif
 constexpr int kDmaThreads = 64;
 constexpr int kDmaAux = 2;         // cache policy of the loads: nontemporal
 
@@ -68,7 +71,15 @@ constexpr int dma_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) |
 //   wlane[t]: weight tile t's row `hi` (= lane / 32) at k = 0 (bytes); the
 //             stage row r of tile t is loaded by instruction 8t + (r & 15) / 2;
 //   arow[s]:  the token row of this lane's MFMA column in subtile s, k = 0
-//             (pad slots point at a valid row; their columns are dropped).
+//             (pad slots point at a valid row; their columns are dropped);
+//   tlive[s]: this lane's row of subtile s holds a real slot.  Only those
+//             lanes load token fragments (the others keep stale registers,
+//             which feed only the dropped columns): with one or a few tokens
+//             in a block the token loads then cost the texture units a few
+//             lanes instead of 64 per instruction.  A loaded subtile's first
+//             row is always real (real slots come first), so no token load
+//             instruction runs with every lane off and each still counts in
+//             the stage's vmcnt.
 // The token operand uses the k layout of the weight type (ActChunk): for
 // e4m3fn one 16-byte LDS read holds k = 64j + 16g .. +16 of a row, the first
 // eight feeding MFMA 2j and the last eight MFMA 2j+1.
@@ -77,6 +88,7 @@ struct DmaOperands {
   static constexpr int kF = DmaGeom<WT, NROW, NS>::kFrags;
   const uint8_t* wlane[NROW];
   const bf16_t* arow[NS];
+  bool tlive[NS];
   size_t wld;  // weight row length (bytes)
   int l31, hi, r16, g;
 
@@ -99,9 +111,11 @@ struct DmaOperands {
   __device__ __forceinline__ void issue_a(uint4 (&a)[NS][kF], int k0) const {
 #pragma unroll
     for (int s = 0; s < NSL; ++s)
+      if (!MOE_DMA_TOKEN_MASK || tlive[s]) {
 #pragma unroll
-      for (int i = 0; i < kF; ++i)
-        a[s][i] = *reinterpret_cast<const uint4*>(arow[s] + k0 + ActChunk<WT, 64>::off(i, g));
+        for (int i = 0; i < kF; ++i)
+          a[s][i] = *reinterpret_cast<const uint4*>(arow[s] + k0 + ActChunk<WT, 64>::off(i, g));
+      }
   }
 
   // acc[s][t] += W_tile(t) . A_subtile(s) over the stage's K.
@@ -290,6 +304,7 @@ __device__ __forceinline__ void dma13_tile(
   for (int s = 0; s < NS; ++s) {
     const int f = blk[16 * s + op.r16];  // pad slots read token 0
     op.arow[s] = x + static_cast<size_t>(f < A ? f / k : 0) * d;
+    op.tlive[s] = f < A;
   }
 
   f32x4 acc[NS][2 * RC];
@@ -388,6 +403,7 @@ __device__ __forceinline__ void dma2_tile(
     const int slot = 16 * s + op.r16;
     const size_t row = static_cast<size_t>(b) * B + (blk[slot] < A ? slot : 0);
     op.arow[s] = h + row * I;
+    op.tlive[s] = blk[slot] < A;
   }
 
   f32x4 acc[NS][RN];

@@ -149,7 +149,10 @@ def test_capacity_formula(lib, T, E, k, bm):
 def test_default_block_covers_a_decode_batch(lib):
     for T, want in [(1, 16), (8, 16), (16, 16), (17, 32), (32, 32), (64, 64), (65, 128)]:
         assert B.moe_align_capacity(desc(T=T), 2)[0] == want
-    # 33..64 tokens with LDS-streaming bf16 shapes take blocks of 32
+    # LDS-streaming bf16 shapes: blocks of 16 while experts average at most
+    # 8 slots (T = 32 at top-2 of 8), then blocks of 32 up to 64 tokens
+    assert B.moe_align_capacity(desc(T=32, d=4096, I=14336), 2)[0] == 16
+    assert B.moe_align_capacity(desc(T=33, d=4096, I=14336), 2)[0] == 32
     assert B.moe_align_capacity(desc(T=64, d=4096, I=14336), 2)[0] == 32
     assert B.moe_align_capacity(desc(T=64, d=4096, I=14336, w=B.MOE_DTYPE_E4M3FN), 2)[0] == 64
     # experts averaging >= 256 tokens with fitting bf16 shapes use the 256 GEMM
