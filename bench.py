@@ -82,6 +82,9 @@ def parse():
                     help="no GPU: write profiles/<workload>_mfma_counters.md from rocprofv3 --pmc "
                          "output directories (matrix-core counters) and a --kernel-trace --stats "
                          "directory given last")
+    ap.add_argument("--summarize-mempath", nargs="+", metavar="DIR",
+                    help="no GPU: write profiles/<workload>_memory_path_counters.md from rocprofv3 "
+                         "--pmc output directories (texture unit, L1 and L2 counters)")
     ap.add_argument("--no-prefill", action="store_true",
                     help="decode workload: skip the prefill sub-record (T = 4096 on the same weights)")
     ap.add_argument("--cpu-reps", type=int, default=3, help="CPU oracle repetitions (median reported)")
@@ -386,6 +389,61 @@ def summarize_pmc(workload: str, paths, command: str) -> str:
     return path
 
 
+MEMPATH_COUNTERS = ["TA_TA_BUSY_sum", "TD_TD_BUSY_sum", "TD_TC_STALL_sum",
+                    "TCP_PENDING_STALL_CYCLES_sum", "TCC_HIT_sum", "TCC_MISS_sum", "GRBM_GUI_ACTIVE"]
+
+
+def summarize_mempath(workload: str, dirs, command: str) -> str:
+    """Vector-memory path counters of the expert kernels, per dispatch
+    averaged per kernel kind: the texture address (TA) and data (TD) units'
+    busy cycles, the data unit's cycles stalled on the cache (TD_TC_STALL),
+    the L1's cycles at its pending-request limit (TCP_PENDING_STALL_CYCLES),
+    each summed over the CUs and divided by the CUs and by one XCD's active
+    cycles (GRBM_GUI_ACTIVE is summed over the XCDs), and the L2 hit rate.
+    `dirs`: output directories of rocprofv3 --pmc runs of one command."""
+    lines = [f"# Vector-memory path counters: {workload} workload", "",
+             "Commands (from the repository root, one MI355X), one counter pass each:", ""]
+    lines += [f"    {c}" for c in command.split(" ;; ")]
+    lines += ["", f"Kernel sources sha (bench.py kernel_source_sha): `{kernel_source_sha()}`", "",
+              f"Per dispatch, averaged over the dispatches of each kind. Unit fractions = "
+              f"counter / {N_CU} CUs / (GRBM_GUI_ACTIVE / {N_XCD}); L2 hit = TCC_HIT / "
+              "(TCC_HIT + TCC_MISS).", "",
+              "| kernel kind | dispatches | TA busy | TD busy | TD stalled on cache | "
+              "L1 at pending limit | L2 hit |",
+              "|---|---|---|---|---|---|---|"]
+    for kind, _ in EXPERT_KINDS:
+        # each pass has its own GRBM_GUI_ACTIVE: pair every counter with its pass's
+        per = {}
+        for d in dirs:
+            drows = [r for r in _counter_rows(d) if kind + "_" in r["Kernel_Name"]]
+            by_disp = {}
+            for r in drows:
+                by_disp.setdefault(r["Dispatch_Id"], {})[r["Counter_Name"]] = float(r["Counter_Value"])
+            for cs in by_disp.values():
+                g = cs.get("GRBM_GUI_ACTIVE")
+                for c, v in cs.items():
+                    if c in ("TCC_HIT_sum", "TCC_MISS_sum"):
+                        per.setdefault(c, []).append(v)
+                    elif c != "GRBM_GUI_ACTIVE" and g:
+                        per.setdefault(c, []).append(v / N_CU / (g / N_XCD))
+        if not per:
+            continue
+        n = max(len(v) for v in per.values())
+        mean = {c: sum(v) / len(v) for c, v in per.items()}
+
+        def cell(c):
+            return f"{mean[c]:.3f}" if c in mean else "-"
+        hit = (f"{mean['TCC_HIT_sum'] / (mean['TCC_HIT_sum'] + mean['TCC_MISS_sum']):.3f}"
+               if "TCC_HIT_sum" in mean and "TCC_MISS_sum" in mean else "-")
+        lines.append(f"| {kind} | {n} | {cell('TA_TA_BUSY_sum')} | {cell('TD_TD_BUSY_sum')} | "
+                     f"{cell('TD_TC_STALL_sum')} | {cell('TCP_PENDING_STALL_CYCLES_sum')} | {hit} |")
+    lines.append("")
+    path = os.path.join(ROOT, "profiles", f"{workload}_memory_path_counters.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines))
+    return path
+
+
 def main() -> int:
     args = parse()
     if args.summarize_traffic:
@@ -396,6 +454,9 @@ def main() -> int:
         return 0
     if args.summarize_pmc:
         print(summarize_pmc(args.workload, args.summarize_pmc, args.command))
+        return 0
+    if args.summarize_mempath:
+        print(summarize_mempath(args.workload, args.summarize_mempath, args.command))
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the layer runs "

@@ -135,3 +135,46 @@ def test_matrix_core_summary(tmp_path, monkeypatch):
     assert float(cells[-5]) == pytest.approx(1024.0)
     assert float(cells[-4]) == pytest.approx(flops / 1024e-6 / 1e12, rel=1e-3)
     assert float(cells[-2]) == pytest.approx(50.0)
+
+
+def test_memory_path_summary(tmp_path, monkeypatch):
+    """Unit busy fractions per CU and XCD-cycle (each counter paired with its
+    own pass's GRBM_GUI_ACTIVE) and the L2 hit rate, averaged per kind."""
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_sha", lambda exclude=(): "cafe")
+    os.makedirs(tmp_path / "profiles")
+    k13 = "void moe::ffn13_wide_kernel<unsigned char>(int)"
+    k2 = "void moe::ffn2_wide_kernel<unsigned char>(int)"
+    g = 8 * 1000.0  # one XCD active 1000 cycles
+    a = _counters(tmp_path / "a", [
+        dict(Dispatch_Id=1, Kernel_Name=k13, Grid_Size=1, Counter_Name="TA_TA_BUSY_sum",
+             Counter_Value=256 * 800.0),
+        dict(Dispatch_Id=1, Kernel_Name=k13, Grid_Size=1, Counter_Name="TD_TD_BUSY_sum",
+             Counter_Value=256 * 900.0),
+        dict(Dispatch_Id=1, Kernel_Name=k13, Grid_Size=1, Counter_Name="GRBM_GUI_ACTIVE",
+             Counter_Value=g),
+        dict(Dispatch_Id=2, Kernel_Name=k13, Grid_Size=1, Counter_Name="TA_TA_BUSY_sum",
+             Counter_Value=256 * 300.0),
+        dict(Dispatch_Id=2, Kernel_Name=k13, Grid_Size=1, Counter_Name="TD_TD_BUSY_sum",
+             Counter_Value=256 * 700.0),
+        dict(Dispatch_Id=2, Kernel_Name=k13, Grid_Size=1, Counter_Name="GRBM_GUI_ACTIVE",
+             Counter_Value=g / 2),
+        dict(Dispatch_Id=3, Kernel_Name=k2, Grid_Size=1, Counter_Name="TA_TA_BUSY_sum",
+             Counter_Value=256 * 500.0),
+        dict(Dispatch_Id=3, Kernel_Name=k2, Grid_Size=1, Counter_Name="GRBM_GUI_ACTIVE",
+             Counter_Value=g)])
+    b = _counters(tmp_path / "b", [
+        dict(Dispatch_Id=1, Kernel_Name=k13, Grid_Size=1, Counter_Name="TCC_HIT_sum",
+             Counter_Value=30.0),
+        dict(Dispatch_Id=1, Kernel_Name=k13, Grid_Size=1, Counter_Name="TCC_MISS_sum",
+             Counter_Value=70.0),
+        dict(Dispatch_Id=1, Kernel_Name=k13, Grid_Size=1, Counter_Name="GRBM_GUI_ACTIVE",
+             Counter_Value=g)])
+    path = bench.summarize_mempath("fp8", [a, b], "cmd one ;; cmd two")
+    text = open(path).read()
+    assert "    cmd one" in text and "    cmd two" in text and "`cafe`" in text
+    row13 = [c.strip() for c in next(l for l in text.splitlines() if l.startswith("| ffn13 |")).strip("|").split("|")]
+    # TA: (0.8 + 0.6) / 2; TD: (0.9 + 1.4) / 2; no stall counters; L2 30 / 100
+    assert row13[2:] == ["0.700", "1.150", "-", "-", "0.300"]
+    row2 = [c.strip() for c in next(l for l in text.splitlines() if l.startswith("| ffn2 |")).strip("|").split("|")]
+    assert row2[2] == "0.500" and row2[-1] == "-"
