@@ -251,8 +251,15 @@ void make_plan(const moe_desc* d, int top_k, bool with_routing, Plan* p) {
     while (s < MOE_WIDE_W2_MAX_SPLITS && tiles * s < MOE_WIDE_W2_SPLIT_WGS &&
            p->I / (2 * s) >= MOE_WIDE_W2_MIN_STAGES * kc)
       s *= 2;
-    const int per = (p->I + s - 1) / s;
-    p->ksplit = (per + kc - 1) / kc * kc;
+    // every range, the last included, keeps at least the minimum (the
+    // tile's ring needs a few stages)
+    int per = (p->I + s - 1) / s;
+    per = (per + kc - 1) / kc * kc;
+    while (s > 1 && p->I - (p->I + per - 1) / per * per + per < MOE_WIDE_W2_MIN_STAGES * kc) {
+      s /= 2;
+      per = ((p->I + s - 1) / s + kc - 1) / kc * kc;
+    }
+    p->ksplit = per;
     p->splits = (p->I + p->ksplit - 1) / p->ksplit;
   } else if (p->wdt != MOE_DTYPE_F32 && p->A > 0 && p->B <= 64) {  // the 128-token GEMM does not split
     const int64_t blocks_est = moe::ffn_blocks_estimate(p->cap, p->B, p->E, p->A);

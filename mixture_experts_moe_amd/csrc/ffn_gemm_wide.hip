@@ -88,12 +88,26 @@ struct WidGeom {
 template <typename WT>
 using WidAcc = f32x4[WidGeom<WT>::kTA][WidGeom<WT>::kNB];
 
-#ifndef MOE_WID13_GROUP_COLS
-#define MOE_WID13_GROUP_COLS 2
+// Channel groups per super-row of the XCD raster (big_tile_of), W13 and W2,
+// by weight type.  Measured: e4m3fn at T = 2048 W13 1.89 / 1.80 / 2.63 ms
+// with 1 / 2 / 4 groups; bf16 (skew) W13 224 -> 218 us and W2 151 -> 147 us
+// with 1 and 2 groups instead of 2 and 4.
+#ifndef MOE_WID13_GROUP_COLS_FP8
+#define MOE_WID13_GROUP_COLS_FP8 2
 #endif
-#ifndef MOE_WID2_GROUP_COLS
-#define MOE_WID2_GROUP_COLS 4
+#ifndef MOE_WID2_GROUP_COLS_FP8
+#define MOE_WID2_GROUP_COLS_FP8 4
 #endif
+#ifndef MOE_WID13_GROUP_COLS_BF16
+#define MOE_WID13_GROUP_COLS_BF16 1
+#endif
+#ifndef MOE_WID2_GROUP_COLS_BF16
+#define MOE_WID2_GROUP_COLS_BF16 2
+#endif
+template <typename WT>
+constexpr int wid13_cols() { return sizeof(WT) == 1 ? MOE_WID13_GROUP_COLS_FP8 : MOE_WID13_GROUP_COLS_BF16; }
+template <typename WT>
+constexpr int wid2_cols() { return sizeof(WT) == 1 ? MOE_WID2_GROUP_COLS_FP8 : MOE_WID2_GROUP_COLS_BF16; }
 
 __device__ __forceinline__ int wid_swz(int row) { return (row >> 1) & 7; }
 
@@ -421,7 +435,7 @@ __global__ __launch_bounds__(WidGeom<WT>::kThreads) void ffn13_wide_kernel(
   using G = WidGeom<WT>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const BigTile tl = big_tile_of<MOE_WID13_GROUP_COLS>(blockIdx.x, gx, gy);
+  const BigTile tl = big_tile_of<wid13_cols<WT>()>(blockIdx.x, gx, gy);
   if (!tl.live) return;  // uniform
   const int b = tl.b;
   const int npad = *num_padded;
@@ -525,7 +539,7 @@ __global__ __launch_bounds__(WidGeom<WT>::kThreads) void ffn2_wide_kernel(
   using G = WidGeom<WT>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const BigTile tl = big_tile_of<MOE_WID2_GROUP_COLS>(blockIdx.x, gx, gy);
+  const BigTile tl = big_tile_of<wid2_cols<WT>()>(blockIdx.x, gx, gy);
   if (!tl.live) return;
   const int b = tl.b;
   const int npad = *num_padded;
