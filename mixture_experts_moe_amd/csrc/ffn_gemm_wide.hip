@@ -359,6 +359,335 @@ __device__ __forceinline__ bool wid_single_block(const int32_t* block_expert, in
   return !before && !after;
 }
 
+// ------------------------------------------------------------ half-full blocks
+// A block whose real tokens all fit in its first 64 rows (e4m3fn weights;
+// at fp8 T = 2048 about half the blocks) takes its token rows through LDS
+// instead: each token row is loaded once per workgroup, as whole 256-byte
+// rows per stage (four rows per 1 KB direct-to-LDS load), where the
+// register path loads every token fragment twice (once per row group) as
+// 64-byte half lines.  A stage holds the 32 KB of weights and 64 token rows
+// (16 KB), three stages in flight-ring as above; eight waves of 64 weight
+// rows x 32 tokens (wave w: rows 64 (w % 4), tokens 32 (w / 4)).  Measured
+// on the tile alone (all blocks at most 64 tokens, fp8 shapes at T = 1024):
+// W13 1.25 against 1.40 ms on the register path.
+#ifndef MOE_WID_HALF
+#define MOE_WID_HALF 1
+#endif
+#ifndef MOE_WID_HALF_BF16
+#define MOE_WID_HALF_BF16 1
+#endif
+constexpr int kHalfTokens = 64;
+
+template <typename WT>
+struct HalfGeom {
+  using G = WidGeom<WT>;
+  static constexpr int kBRowBytes = 2 * G::kK;  // bf16 token row per stage
+  static constexpr int kBSlots = kBRowBytes / 16;
+  static constexpr int kBRowsPerLoad = 1024 / kBRowBytes;
+  static constexpr int kBBytes = kHalfTokens * kBRowBytes;
+  static constexpr int kLoadsB = kBBytes / 1024 / G::kWaves;  // token loads per wave and stage
+  static constexpr int kStageBytes = G::kStageBytes + kBBytes;
+  static constexpr int kTA = 4, kNB = 2;  // 16-row weight tiles, 16-token tiles per wave
+  static_assert(G::kWaves == 8 && G::kRows == 256, "eight waves over 256 weight rows");
+  static_assert(kLoadsB * kBRowsPerLoad == 8, "each wave loads eight token rows");
+  static_assert(G::kD * kStageBytes <= 160 * 1024, "the ring's stages fit in LDS");
+};
+
+typedef f32x4 HalfAcc[4][2];
+
+template <typename WT>
+__device__ __forceinline__ int half_bswz(int row) {
+  return HalfGeom<WT>::kBSlots == 16 ? (row & 15) : ((row >> 1) & 7);
+}
+// Token load i of wave w fills rows kBRowsPerLoad (kLoadsB w + i) + l / kBSlots
+// of the token region (wave w: rows 8w .. 8w+7), lane l at physical slot
+// l % kBSlots = logical slot (l % kBSlots) ^ bswz(row).
+template <typename WT>
+__device__ __forceinline__ int half_b_row(int wave, int i, int lane) {
+  using H = HalfGeom<WT>;
+  return H::kBRowsPerLoad * (H::kLoadsB * wave + i) + lane / H::kBSlots;
+}
+template <typename WT>
+__device__ __forceinline__ int half_b_slot(int row, int lane) {
+  return (lane % HalfGeom<WT>::kBSlots) ^ half_bswz<WT>(row);
+}
+
+struct HalfLoader {
+  __amdgpu_buffer_rsrc_t ra, rb;
+  uint32_t a[kWidLoadsA];
+  uint32_t b[2];  // this lane's token source of load i, k = 0
+};
+
+__device__ __forceinline__ void wid_load_t_lds(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off,
+                                           0, 0, 0);
+}
+
+// Part j of stage s's loads (one part per k-step): weight loads
+// j * 4 / kSteps .. (j + 1) * 4 / kSteps - 1, and token load j while
+// j < kLoadsB (when kB).
+template <typename WT, bool kNT, bool kB>
+__device__ __forceinline__ void half_issue_part(const HalfLoader& ld, uint8_t* stage, int s,
+                                                int wave, int j) {
+  using G = WidGeom<WT>;
+  using H = HalfGeom<WT>;
+  constexpr int kPer = kWidLoadsA / G::kSteps;
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int i = j * kPer + q;
+    uint8_t* dst = stage + (wave * kWidLoadsA + i) * 1024;
+    const uint32_t off = ld.a[i] + static_cast<uint32_t>(s) * kWidRowBytes;
+    if constexpr (kNT)
+      wid_load_w_nt(ld.ra, dst, off);
+    else
+      wid_load_w(ld.ra, dst, off);
+  }
+  if constexpr (kB) {
+    if (j < H::kLoadsB)
+      wid_load_t_lds(ld.rb, stage + G::kStageBytes + (wave * H::kLoadsB + j) * 1024,
+                     ld.b[j] + static_cast<uint32_t>(s) * H::kBRowBytes);
+  }
+}
+
+template <typename WT, bool kNT, bool kB>
+__device__ __forceinline__ void half_issue(const HalfLoader& ld, uint8_t* stage, int s, int wave) {
+#pragma unroll
+  for (int j = 0; j < WidGeom<WT>::kSteps; ++j) half_issue_part<WT, kNT, kB>(ld, stage, s, wave, j);
+}
+
+// k-step j: weight tiles t at rows arow0 + 16t (t < 2) and arow1 + 16(t - 2),
+// token tiles u at rows brow0 + 16u of the token region.
+template <typename WT>
+__device__ __forceinline__ void half_kstep(const uint8_t* cur, int j, int arow0, int arow1,
+                                           int brow0, HalfAcc& acc) {
+  using G = WidGeom<WT>;
+  using H = HalfGeom<WT>;
+  const int lane = threadIdx.x & 63;
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  uint32_t la = wid_a_off<WT>(j);
+  uint32_t lb = G::kStageBytes + r16 * H::kBRowBytes + (((4 * j + g) ^ half_bswz<WT>(r16)) << 4);
+  asm volatile("" : "+v"(la), "+v"(lb));
+  bf16x8 b[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    b[u] = as_frag(*reinterpret_cast<const uint4*>(cur + lb + (brow0 + 16 * u) * H::kBRowBytes));
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int row = t < 2 ? arow0 + 16 * t : arow1 + 16 * (t - 2);
+    bf16x8 a;
+    if constexpr (sizeof(WT) == 1) {
+      const uint2 q = *reinterpret_cast<const uint2*>(cur + la + row * kWidRowBytes);
+      a = as_frag(e4m3x8_to_frag_bits(q.x, q.y));
+    } else {
+      a = as_frag(*reinterpret_cast<const uint4*>(cur + la + row * kWidRowBytes));
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) acc[t][u] = mfma16x16x32(a, b[u], acc[t][u]);
+  }
+}
+
+// The ring of three stages (as WidRing at depth 3, both operands in LDS):
+// kB the wave loads token rows, kLive its 32 token rows hold a real slot.
+template <typename WT, bool kNT, bool kB, bool kLive>
+struct HalfRing {
+  using G = WidGeom<WT>;
+  static constexpr int kL = kWidLoadsA + (kB ? HalfGeom<WT>::kLoadsB : 0);
+  const HalfLoader& ld;
+  uint8_t* const (&buf)[4];
+  int wave, arow0, arow1, brow0;
+
+  template <int p, int W, bool kIssue>
+  __device__ __forceinline__ void step(int s, HalfAcc& acc) const {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kL * W));
+    big_barrier();
+    constexpr int n = (p + 2) % 3;
+    if constexpr (kLive) {
+#pragma unroll
+      for (int j = 0; j < G::kSteps; ++j) {
+        if constexpr (kIssue) half_issue_part<WT, kNT, kB>(ld, buf[n], s + 2, wave, j);
+        half_kstep<WT>(buf[p], j, arow0, arow1, brow0, acc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else if constexpr (kIssue) {
+      half_issue<WT, kNT, kB>(ld, buf[n], s + 2, wave);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  template <int R>  // R = nst % 3; nst >= 2
+  __device__ __forceinline__ void run_r(int nst, HalfAcc& acc) const {
+    half_issue<WT, kNT, kB>(ld, buf[0], 0, wave);
+    half_issue<WT, kNT, kB>(ld, buf[1], 1, wave);
+    int s = 0;
+    for (; s + 5 <= nst; s += 3) {
+      step<0, 1, true>(s, acc);
+      step<1, 1, true>(s + 1, acc);
+      step<2, 1, true>(s + 2, acc);
+    }
+    if constexpr (R == 2) {
+      step<0, 1, false>(s, acc);
+      step<1, 0, false>(s + 1, acc);
+    } else if constexpr (R == 0) {
+      step<0, 1, true>(s, acc);
+      step<1, 1, false>(s + 1, acc);
+      step<2, 0, false>(s + 2, acc);
+    } else {
+      step<0, 1, true>(s, acc);
+      step<1, 1, true>(s + 1, acc);
+      step<2, 1, false>(s + 2, acc);
+      step<0, 0, false>(s + 3, acc);
+    }
+  }
+
+  __device__ __forceinline__ void run(int nst, HalfAcc& acc) const {
+    const int r = nst % 3;
+    if (r == 0) run_r<0>(nst, acc);
+    else if (r == 1) run_r<1>(nst, acc);
+    else run_r<2>(nst, acc);
+  }
+};
+
+template <typename WT>
+__device__ __forceinline__ void half_run(const HalfLoader& ld, uint8_t* const (&buf)[4], int nst,
+                                         int wave, int arow0, int arow1, int brow0, bool nt,
+                                         bool b_live, bool live, HalfAcc& acc) {
+  // a live wave loads its eight token rows even when they are all padding
+  // (their loads read zeros past the buffer's end), so kLive implies kB
+  if (nt) {
+    if (live) HalfRing<WT, true, true, true>{ld, buf, wave, arow0, arow1, brow0}.run(nst, acc);
+    else if (b_live) HalfRing<WT, true, true, false>{ld, buf, wave, arow0, arow1, brow0}.run(nst, acc);
+    else HalfRing<WT, true, false, false>{ld, buf, wave, arow0, arow1, brow0}.run(nst, acc);
+  } else {
+    if (live) HalfRing<WT, false, true, true>{ld, buf, wave, arow0, arow1, brow0}.run(nst, acc);
+    else if (b_live) HalfRing<WT, false, true, false>{ld, buf, wave, arow0, arow1, brow0}.run(nst, acc);
+    else HalfRing<WT, false, false, false>{ld, buf, wave, arow0, arow1, brow0}.run(nst, acc);
+  }
+}
+
+// W13 of a half-full block: wave (wm, wn) = (w % 4, w / 4) holds gate and up
+// of channels n0 + 32 wm .. +31 for tokens 32 wn .. +31.
+template <typename WT>
+__device__ __forceinline__ void half13_tile(const WidLoader& wl, uint8_t* const (&buf)[4],
+                                            const int32_t* blk, const float* s13, int scale_mode,
+                                            bf16_t* h, int b, int e, int n0, int d, int I, int k,
+                                            int A, uint32_t xbytes, bool nt) {
+  using G = WidGeom<WT>;
+  using H = HalfGeom<WT>;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  HalfLoader ld;
+  ld.ra = wl.ra;
+  ld.rb = wl.rb;
+#pragma unroll
+  for (int i = 0; i < kWidLoadsA; ++i) ld.a[i] = wl.a[i];
+#pragma unroll
+  for (int i = 0; i < H::kLoadsB; ++i) {
+    const int r = half_b_row<WT>(wave, i, lane);
+    const int f = blk[r];
+    ld.b[i] = f < A ? 2 * static_cast<uint32_t>(f / k) * d + 16 * half_b_slot<WT>(r, lane) : xbytes;
+  }
+  const bool b_live = __builtin_amdgcn_readfirstlane(blk[8 * wave]) < A;
+  const int wm = wave & 3, wn = wave >> 2;
+  const bool live = __builtin_amdgcn_readfirstlane(blk[32 * wn]) < A;
+  HalfAcc acc;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  half_run<WT>(ld, buf, d / G::kK, wave, 32 * wm, 128 + 32 * wm, 32 * wn, nt, b_live, live, acc);
+  if (!live) return;
+
+  // lane: token column r16 of tile u, channels n0 + 32wm + 16t + 4g .. +3
+  // (gate in tile t, up in tile t + 2)
+  const size_t two_i = 2 * static_cast<size_t>(I);
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int c = n0 + 32 * wm + 16 * t + 4 * g;
+    if (c >= I) continue;
+    float sg[4], su[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      sg[v] = load_scale(s13, scale_mode, e, static_cast<size_t>(e) * two_i + c + v);
+      su[v] = load_scale(s13, scale_mode, e, static_cast<size_t>(e) * two_i + I + c + v);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const size_t row = static_cast<size_t>(b) * kWidTokens + 32 * wn + 16 * u + r16;
+      uint32_t packed[2];
+#pragma unroll
+      for (int v = 0; v < 4; v += 2) {
+        const float h0 = silu(acc[t][u][v] * sg[v]) * (acc[t + 2][u][v] * su[v]);
+        const float h1 = silu(acc[t][u][v + 1] * sg[v + 1]) * (acc[t + 2][u][v + 1] * su[v + 1]);
+        packed[v / 2] = static_cast<uint32_t>(f32_to_bf16(h0)) |
+                        (static_cast<uint32_t>(f32_to_bf16(h1)) << 16);
+      }
+      *reinterpret_cast<uint2*>(h + row * I + c) = uint2{packed[0], packed[1]};
+    }
+  }
+}
+
+// W2 of a half-full block: wave (wm, wn) = (w % 4, w / 4) holds output
+// channels n0 + 64 wm .. +63 for tokens 32 wn .. +31.
+template <typename WT>
+__device__ __forceinline__ void half2_tile(const WidLoader& wl, uint8_t* const (&buf)[4],
+                                           const int32_t* blk, const float* s2, int scale_mode,
+                                           const float* topk_w, float* y, int e, int n0, int d,
+                                           int I, int A, int k_begin, int nst, uint32_t hbytes,
+                                           bool nt) {
+  using H = HalfGeom<WT>;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  HalfLoader ld;
+  ld.ra = wl.ra;
+  ld.rb = wl.rb;
+#pragma unroll
+  for (int i = 0; i < kWidLoadsA; ++i) ld.a[i] = wl.a[i];
+  // h rows of the block; rows of padding slots read zeros
+#pragma unroll
+  for (int i = 0; i < H::kLoadsB; ++i) {
+    const int r = half_b_row<WT>(wave, i, lane);
+    ld.b[i] = blk[r] < A ? 2 * (static_cast<uint32_t>(r) * I + k_begin) + 16 * half_b_slot<WT>(r, lane)
+                         : hbytes;
+  }
+  const bool b_live = __builtin_amdgcn_readfirstlane(blk[8 * wave]) < A;
+  const int wm = wave & 3, wn = wave >> 2;
+  const bool live = __builtin_amdgcn_readfirstlane(blk[32 * wn]) < A;
+  HalfAcc acc;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  half_run<WT>(ld, buf, nst, wave, 64 * wm, 64 * wm + 32, 32 * wn, nt, b_live, live, acc);
+  if (!live) return;
+
+  // lane: token column r16 of tile u, channels n0 + 64wm + 16t + 4g .. +3
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int f = blk[32 * wn + 16 * u + r16];
+    if (f < A) {
+      const float gate = topk_w[f];
+      float* yrow = y + static_cast<size_t>(f) * d;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int c = n0 + 64 * wm + 16 * t + 4 * g;
+        if (c >= d) continue;
+        const size_t base = static_cast<size_t>(e) * d + c;
+        float sc[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sc[v] = load_scale(s2, scale_mode, e, base + v);
+        *reinterpret_cast<float4*>(yrow + c) =
+            float4{acc[t][u][0] * sc[0] * gate, acc[t][u][1] * sc[1] * gate,
+                   acc[t][u][2] * sc[2] * gate, acc[t][u][3] * sc[3] * gate};
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------ W13 + SiLU*mul
 // Tile (b, y): channels n0 = 128y .. +127 (rows: 128 gate, then 128 up;
 // channels at or past I read zeros and are not stored) x the 128 tokens of
@@ -462,10 +791,27 @@ __global__ __launch_bounds__(WidGeom<WT>::kThreads) void ffn13_wide_kernel(
   }
   const bool nt = wid_single_block(block_expert, b, npad / kWidTokens, e);
   if constexpr (G::kD == 3) {
-    WID_RING3(buf, G::kStageBytes);
+    constexpr int kBytes = HalfGeom<WT>::kStageBytes > G::kStageBytes ? HalfGeom<WT>::kStageBytes
+                                                                        : G::kStageBytes;
+    WID_RING3(buf, (sizeof(WT) == 1 && MOE_WID_HALF) ? kBytes : G::kStageBytes);
+    if constexpr (sizeof(WT) == 1 && MOE_WID_HALF) {
+      // real slots come first: no real slot past row 63 means a half-full block
+      if (__builtin_amdgcn_readfirstlane(blk[kHalfTokens]) >= A) {
+        half13_tile<WT>(ld, buf, blk, s13, scale_mode, h, b, e, n0, d, I, k, A, xbytes, nt);
+        return;
+      }
+    }
     wide13_tile<WT>(ld, buf, blk, s13, scale_mode, h, b, e, n0, d, I, k, A, xbytes, nt);
   } else {
-    WID_RING4(buf, G::kStageBytes);
+    constexpr int kBytes = HalfGeom<WT>::kStageBytes > G::kStageBytes ? HalfGeom<WT>::kStageBytes
+                                                                        : G::kStageBytes;
+    WID_RING4(buf, MOE_WID_HALF_BF16 ? kBytes : G::kStageBytes);
+    if constexpr (MOE_WID_HALF_BF16) {
+      if (__builtin_amdgcn_readfirstlane(blk[kHalfTokens]) >= A) {
+        half13_tile<WT>(ld, buf, blk, s13, scale_mode, h, b, e, n0, d, I, k, A, xbytes, nt);
+        return;
+      }
+    }
     wide13_tile<WT>(ld, buf, blk, s13, scale_mode, h, b, e, n0, d, I, k, A, xbytes, nt);
   }
 }
@@ -567,11 +913,29 @@ __global__ __launch_bounds__(WidGeom<WT>::kThreads) void ffn2_wide_kernel(
   }
   const bool nt = wid_single_block(block_expert, b, npad / kWidTokens, e);
   if constexpr (G::kD == 3) {
-    WID_RING3(buf, G::kStageBytes);
+    constexpr int kBytes = HalfGeom<WT>::kStageBytes > G::kStageBytes ? HalfGeom<WT>::kStageBytes
+                                                                        : G::kStageBytes;
+    WID_RING3(buf, (sizeof(WT) == 1 && MOE_WID_HALF) ? kBytes : G::kStageBytes);
+    if constexpr (sizeof(WT) == 1 && MOE_WID_HALF) {
+      if (__builtin_amdgcn_readfirstlane(blk[kHalfTokens]) >= A) {
+        half2_tile<WT>(ld, buf, blk, s2, scale_mode, topk_w, y, e, n0, d, I, A, k_begin, nst,
+                       hbytes, nt);
+        return;
+      }
+    }
     wide2_tile<WT>(ld, buf, blk, s2, scale_mode, topk_w, y, e, n0, d, I, A, k_begin, nst,
                    hbytes, nt);
   } else {
-    WID_RING4(buf, G::kStageBytes);
+    constexpr int kBytes = HalfGeom<WT>::kStageBytes > G::kStageBytes ? HalfGeom<WT>::kStageBytes
+                                                                        : G::kStageBytes;
+    WID_RING4(buf, MOE_WID_HALF_BF16 ? kBytes : G::kStageBytes);
+    if constexpr (MOE_WID_HALF_BF16) {
+      if (__builtin_amdgcn_readfirstlane(blk[kHalfTokens]) >= A) {
+        half2_tile<WT>(ld, buf, blk, s2, scale_mode, topk_w, y, e, n0, d, I, A, k_begin, nst,
+                       hbytes, nt);
+        return;
+      }
+    }
     wide2_tile<WT>(ld, buf, blk, s2, scale_mode, topk_w, y, e, n0, d, I, A, k_begin, nst,
                    hbytes, nt);
   }

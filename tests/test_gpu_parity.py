@@ -173,6 +173,10 @@ SMALL = [
     ("fp8_wide", dict(workload="fp8", d=384, I=384, E=8, k=2), 300, 128),
     ("fp8_wide", dict(workload="fp8", d=512, I=640, E=4, k=2, scale_mode="tensor"), 300, 128),
     ("fp8_wide", dict(workload="fp8", d=1024, I=4096, E=2, k=1), 150, 128),
+    # e4m3fn blocks of at most 64 tokens (tokens through LDS): 50 per expert,
+    # and 25 per expert (the second 32-token half of every wave idle)
+    ("fp8_wide", dict(workload="fp8", d=384, I=384, E=16, k=4), 200, 128),
+    ("fp8_wide", dict(workload="fp8", d=512, I=640, E=8, k=2, scale_mode="tensor"), 100, 128),
     # W8A8 (block-scaled e4m3fn x and h, blocks of 256): one token, a ragged
     # block, several blocks per expert, E = 1, per-tensor scales, more
     # channel tiles than one, and W2's K split in two (I = 4096, few tiles)

@@ -216,3 +216,33 @@ def test_wide_ring_shortest_k():
     assert _wide_ring(3, 4) == [0, 1, 2]
     with pytest.raises(AssertionError):
         _wide_ring(2, 4)
+
+
+def test_wide_half_block_token_rows_find_their_fragments():
+    """Half-full blocks of the register-token tile (e4m3fn weights): 64 token
+    rows of 256 bytes per stage after the 32 KB of weights, four rows per
+    1 KB load (wave w, load i: rows 4 (2w + i) + l / 16, physical slot l % 16
+    holding logical slot (l % 16) ^ (row & 15)); the k-step j fragment of
+    lane (r16, g) in token tile u reads k = 32j + 8g .. +7 of row 16u + r16."""
+    base_b = 256 * 128
+    lds = {}
+    rows_of_wave = {}
+    for w in range(8):
+        for i in range(2):
+            for lane in range(64):
+                row = 4 * (2 * w + i) + lane // 16
+                rows_of_wave.setdefault(w, set()).add(row)
+                slot = (lane % 16) ^ (row & 15)
+                base = base_b + (2 * w + i) * 1024 + lane * 16
+                assert (base - base_b) // 256 == row
+                for byte in range(0, 16, 2):
+                    lds[base + byte] = (row, (16 * slot + byte) // 2)
+    assert all(rows_of_wave[w] == set(range(8 * w, 8 * w + 8)) for w in range(8))
+    assert len(lds) == 64 * 128
+    for lane in range(64):
+        r16, g = lane % 16, lane // 16
+        for j in range(4):
+            off = base_b + r16 * 256 + (((4 * j + g) ^ r16) << 4)
+            for tile in range(0, 64, 16):
+                for e in range(8):
+                    assert lds[off + tile * 256 + 2 * e] == (tile + r16, 32 * j + 8 * g + e)
