@@ -58,8 +58,10 @@ template <int kCols = kBigGroupCols>
 __device__ __forceinline__ BigTile big_tile_of(int p, int gx, int gy) {
   const int total = gx * gy;
   const int per_xcd = (total + kBigXcds - 1) / kBigXcds;
+  // (a grid larger than 8 per_xcd, sized for more tiles than `total`:
+  // workgroups past per_xcd on their XCD have no tile)
   const int l = (p % kBigXcds) * per_xcd + p / kBigXcds;
-  BigTile t{0, 0, l < total};
+  BigTile t{0, 0, p / kBigXcds < per_xcd && l < total};
   if (!t.live) return t;
   const int band = kCols * gx;
   const int sr = l / band;
@@ -68,6 +70,18 @@ __device__ __forceinline__ BigTile big_tile_of(int p, int gx, int gy) {
   t.b = rem / cols;
   t.y = sr * kCols + rem % cols;
   return t;
+}
+
+// The raster over the realised row blocks only.  The grid is sized from the
+// capacity (gx blocks of bm slots), which also counts blocks that stay
+// empty; rasterising over gx would leave the XCDs whose share lies past the
+// realised blocks with less work.  Over the count read on the device every
+// XCD gets the same number of live tiles, and the workgroups left over
+// return.
+template <int kCols = kBigGroupCols>
+__device__ __forceinline__ BigTile big_tile_live(int p, int gx, int gy,
+                                                 const int32_t* num_padded, int bm) {
+  return big_tile_of<kCols>(p, min(gx, *num_padded / bm), gy);
 }
 
 // Each wave fills kBigGroups consecutive 1 KB groups (kBigRowsPerGroup rows

@@ -173,10 +173,9 @@ __global__ __launch_bounds__(kBigThreads) void ffn13_big_kernel(
   BIG_BUFFERS(buf);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const BigTile tl = big_tile_of(blockIdx.x, gx, gy);
+  const BigTile tl = big_tile_live(blockIdx.x, gx, gy, num_padded, kBigTokens);
   if (!tl.live) return;  // uniform
   const int b = tl.b;
-  if (b * kBigTokens >= *num_padded) return;
   const int32_t* blk = sorted_ids + static_cast<size_t>(b) * kBigTokens;
   if (blk[0] >= A) return;  // real slots come first: this block holds none
   const int e = block_expert[b];
@@ -246,10 +245,9 @@ __global__ __launch_bounds__(kBigThreads) void ffn2_big_kernel(
   BIG_BUFFERS(buf);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const BigTile tl = big_tile_of(blockIdx.x, gx, gy);
+  const BigTile tl = big_tile_live(blockIdx.x, gx, gy, num_padded, kBigTokens);
   if (!tl.live) return;
   const int b = tl.b;
-  if (b * kBigTokens >= *num_padded) return;
   const int32_t* blk = sorted_ids + static_cast<size_t>(b) * kBigTokens;
   if (blk[0] >= A) return;
   const int e = block_expert[b];

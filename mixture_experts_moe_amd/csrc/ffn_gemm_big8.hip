@@ -270,10 +270,9 @@ __global__ __launch_bounds__(kBigThreads) void ffn13_big8_kernel(
   BIG8_EXPS(exb);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const BigTile tl = big_tile_of(blockIdx.x, gx, gy);
+  const BigTile tl = big_tile_live(blockIdx.x, gx, gy, num_padded, kBigTokens);
   if (!tl.live) return;
   const int b = tl.b;
-  if (b * kBigTokens >= *num_padded) return;
   const int32_t* blk = sorted_ids + static_cast<size_t>(b) * kBigTokens;
   if (blk[0] >= A) return;
   const int e = block_expert[b];
@@ -377,10 +376,9 @@ __global__ __launch_bounds__(kBigThreads) void ffn2_big8_kernel(
   BIG8_EXPS(exb);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const BigTile tl = big_tile_of(blockIdx.x, gx, gy);
+  const BigTile tl = big_tile_live(blockIdx.x, gx, gy, num_padded, kBigTokens);
   if (!tl.live) return;
   const int b = tl.b;
-  if (b * kBigTokens >= *num_padded) return;
   const int32_t* blk = sorted_ids + static_cast<size_t>(b) * kBigTokens;
   if (blk[0] >= A) return;
   const int e = block_expert[b];

@@ -268,10 +268,9 @@ __global__ __launch_bounds__(kMidThreads) void ffn13_mid_kernel(
   MID_RING(buf);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const BigTile tl = big_tile_of<MOE_MID13_GROUP_COLS>(blockIdx.x, gx, gy);
+  const BigTile tl = big_tile_live<MOE_MID13_GROUP_COLS>(blockIdx.x, gx, gy, num_padded, kMidTokens);
   if (!tl.live) return;  // uniform
   const int b = tl.b;
-  if (b * kMidTokens >= *num_padded) return;
   const int32_t* blk = sorted_ids + static_cast<size_t>(b) * kMidTokens;
   if (blk[0] >= A) return;  // real slots come first: this block holds none
   const int e = block_expert[b];
@@ -344,10 +343,9 @@ __global__ __launch_bounds__(kMidThreads) void ffn2_mid_kernel(
   MID_RING(buf);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const BigTile tl = big_tile_of<MOE_MID2_GROUP_COLS>(blockIdx.x, gx, gy);
+  const BigTile tl = big_tile_live<MOE_MID2_GROUP_COLS>(blockIdx.x, gx, gy, num_padded, kMidTokens);
   if (!tl.live) return;
   const int b = tl.b;
-  if (b * kMidTokens >= *num_padded) return;
   const int32_t* blk = sorted_ids + static_cast<size_t>(b) * kMidTokens;
   if (blk[0] >= A) return;
   const int e = block_expert[b];

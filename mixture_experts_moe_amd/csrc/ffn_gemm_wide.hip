@@ -764,11 +764,10 @@ __global__ __launch_bounds__(WidGeom<WT>::kThreads) void ffn13_wide_kernel(
   using G = WidGeom<WT>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const BigTile tl = big_tile_of<wid13_cols<WT>()>(blockIdx.x, gx, gy);
+  const BigTile tl = big_tile_live<wid13_cols<WT>()>(blockIdx.x, gx, gy, num_padded, kWidTokens);
   if (!tl.live) return;  // uniform
   const int b = tl.b;
   const int npad = *num_padded;
-  if (b * kWidTokens >= npad) return;
   const int32_t* blk = sorted_ids + static_cast<size_t>(b) * kWidTokens;
   if (blk[0] >= A) return;  // real slots come first: this block holds none
   const int e = block_expert[b];
@@ -885,11 +884,10 @@ __global__ __launch_bounds__(WidGeom<WT>::kThreads) void ffn2_wide_kernel(
   using G = WidGeom<WT>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const BigTile tl = big_tile_of<wid2_cols<WT>()>(blockIdx.x, gx, gy);
+  const BigTile tl = big_tile_live<wid2_cols<WT>()>(blockIdx.x, gx, gy, num_padded, kWidTokens);
   if (!tl.live) return;
   const int b = tl.b;
   const int npad = *num_padded;
-  if (b * kWidTokens >= npad) return;
   const int32_t* blk = sorted_ids + static_cast<size_t>(b) * kWidTokens;
   if (blk[0] >= A) return;
   const int e = block_expert[b];

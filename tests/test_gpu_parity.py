@@ -333,6 +333,37 @@ def test_tile_forward_equals_stage_composition_and_graph(wl, bm, over):
     _report(r)
 
 
+@pytest.mark.parametrize("wl,over", [
+    ("decode_bf16", dict(d=2048, I=1024, E=32, k=8, x_std=1.0)),
+    ("fp8", dict(d=2048, I=1024, E=32, k=8)),
+], ids=["bf16", "fp8"])
+def test_register_tile_large_grid(wl, over):
+    """The register-token tile on a grid sized for 288 row blocks of which
+    fewer are realised (T = 4096, top-8 of 32 experts: full blocks,
+    every expert's ragged tail block, several blocks per expert): the
+    raster runs over the realised blocks only, so the workgroups left over
+    must do nothing.  Deterministic, equal to the stage composition, and
+    against the oracle on tokens that hold the first and the last real slot
+    of every row block."""
+    note(f"register-token tile, large grid {wl}")
+    inp = synth.make_inputs(wl, T=4096, device=DEV, **over)
+    sc = (inp.s13, inp.s2) if inp.w == "e4m3fn" else None
+    wdt = B.MOE_DTYPE_E4M3FN if inp.w == "e4m3fn" else B.MOE_DTYPE_BF16
+    out1 = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, sc, block_m=128)
+    out2 = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k, sc, block_m=128)
+    _, ids, w = B.moe_route(inp.x, inp.w_gate, inp.top_k)
+    counts, sorted_ids, block_expert, num_padded, got_bm = B.moe_align(
+        ids, inp.E, block_m=128, hidden=inp.d, intermediate=inp.I, weight_dtype=wdt)
+    out3 = B.moe_expert_ffn(inp.x, inp.w13, inp.w2, inp.top_k, w, sorted_ids, block_expert,
+                            num_padded, sc, block_m=128)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2)
+    assert torch.equal(out1, out3)
+    tokens = covering_tokens(ids.cpu().numpy(), inp.E, 128)
+    r = compare_layer(inp, out1, ids, tokens=tokens)
+    _report(r)
+
+
 def test_binding_rejects_bad_scales_before_any_launch():
     inp = synth.make_inputs("fp8", T=4, device=DEV, d=256, I=128, E=4, k=2)
     bad = [

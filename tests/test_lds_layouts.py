@@ -218,6 +218,43 @@ def test_wide_ring_shortest_k():
         _wide_ring(2, 4)
 
 
+def _big_tile_of(p, gx, gy, cols, xcds=8):
+    """big_tile_of (ffn_big_common.h): workgroup p -> (live, b, y)."""
+    total = gx * gy
+    per_xcd = -(-total // xcds)
+    l = (p % xcds) * per_xcd + p // xcds
+    if not (p // xcds < per_xcd and l < total):
+        return None
+    band = cols * gx
+    sr, rem = divmod(l, band)
+    c = min(cols, gy - sr * cols)
+    return rem // c, sr * cols + rem % c
+
+
+@pytest.mark.parametrize("gx_grid,gx_live,gy,cols", [
+    (384, 256, 16, 2), (384, 256, 28, 4), (384, 256, 4, 2), (384, 256, 7, 4),
+    (48, 36, 23, 1), (48, 36, 12, 2), (40, 40, 112, 4), (10, 0, 8, 2), (5, 3, 1, 4)])
+def test_raster_over_realised_blocks_covers_each_tile_once(gx_grid, gx_live, gy, cols):
+    """The grid is sized for the capacity's blocks (gx_grid, rounded up to
+    whole XCD rounds) while the raster runs over the realised ones: every
+    tile (b < gx_live, y) goes to exactly one workgroup, the same number of
+    tiles to each XCD but the last (which takes what is left, fewer than
+    eight less), and the workgroups left over have none."""
+    grid = -(-gx_grid * gy // 8) * 8
+    seen = {}
+    per = [0] * 8
+    for p in range(grid):
+        t = _big_tile_of(p, gx_live, gy, cols)
+        if t is None:
+            continue
+        assert t not in seen, (t, p, seen.get(t))
+        seen[t] = p
+        per[p % 8] += 1
+    assert set(seen) == {(b, y) for b in range(gx_live) for y in range(gy)}
+    assert max(per) - min(per) < 8
+    assert all(n == max(per) for n in per[:7]) or gx_live * gy < 8
+
+
 def test_wide_half_block_token_rows_find_their_fragments():
     """Half-full blocks of the register-token tile (e4m3fn weights): 64 token
     rows of 256 bytes per stage after the 32 KB of weights, four rows per
