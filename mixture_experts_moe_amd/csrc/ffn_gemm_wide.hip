@@ -1,7 +1,7 @@
-// Grouped GEMM for blocks of 128 tokens, bf16 or e4m3fn weights, with the
-// token operand held in registers: the expert kernels of experts holding a
-// few dozen to a hundred-odd tokens at large T, where every weight byte
-// must be read once from HBM at close to the streaming rate.
+// Grouped GEMM for blocks of 128 tokens, bf16 or e4m3fn weights: the
+// expert kernels of experts holding a few dozen to a hundred-odd tokens at
+// large T, where every weight byte must be read once from HBM at close to
+// the streaming rate.
 //
 // Sources: the Hungarian news page "Az AWS új MoE-optimalizációkkal
 // gyorsítja a SageMaker AI-t", section "FP8 esetén a Triton backend
@@ -11,20 +11,27 @@
 // computation as one batched operation).
 //
 // A workgroup computes 256 weight rows x the block's 128 tokens with eight
-// waves (for bf16 weights each wave takes all 256 rows for 16 tokens, for
-// e4m3fn 128 rows for 32 tokens; see WidGeom).  Only the
-// weights go through LDS: direct-to-LDS 16-byte buffer loads, eight rows x
-// 128 contiguous bytes per instruction (128 bytes of every row per stage: 64
-// bf16 or 128 e4m3fn values of K), through a ring of D buffers of 32 KB.
-// Each wave loads its own 32 token rows of the stage's K straight into MFMA
-// fragment registers (a ring of D register sets), in the same load stream:
-// loads complete in issue order, so one wait per stage covers both operands.
-// Keeping the tokens out of LDS is what lets two or three 32 KB weight stages
-// be in flight per CU; staging 128 bf16 token rows there as well would leave
-// room for only one.  The weight loads carry the nontemporal hint when the
-// block is its expert's only one (its weights are read once); an expert with
-// several blocks reads them plainly, so that its other blocks' workgroups,
-// which run at about the same time, find them in L2.
+// waves.  The weights go through LDS: direct-to-LDS 16-byte buffer loads,
+// eight rows x 128 contiguous bytes per instruction (128 bytes of every row
+// per stage: 64 bf16 or 128 e4m3fn values of K), through a ring of 32 KB
+// stages.  Where the token rows go depends on the weights and the block:
+//   - register path (bf16 weights; e4m3fn only with MOE_WID_FULL off): each
+//     wave loads its own token rows of the stage's K straight into MFMA
+//     fragment registers, in the same load stream (loads complete in issue
+//     order, so one wait per stage covers both operands);
+//   - half-full blocks (at most 64 real tokens): 64 token rows per stage
+//     through LDS beside the weights, each row loaded once per workgroup;
+//   - full blocks with e4m3fn weights: all 128 token rows through LDS in a
+//     ring of their own (see the full-block section).
+// The per-CU vector memory path (address and data units, the L1's pending
+// requests) is what these kernels run into before HBM does, so the token
+// bytes that path carries per weight byte are what the variants trade: the
+// register path loads each e4m3fn token fragment twice (once per row
+// group) as 64-byte half lines, the LDS paths once as whole rows.  The
+// weight loads carry the nontemporal hint when the block is its expert's
+// only one (its weights are read once); an expert with several blocks reads
+// them plainly, so that its other blocks' workgroups, which run at about
+// the same time, find them in L2.
 //
 // Weight LDS rows are 128 bytes in eight 16-byte slots, XOR-swizzled by
 // (row >> 1) & 7 so that the 16 rows one 16-lane group reads at the same k
@@ -88,12 +95,14 @@ struct WidGeom {
 template <typename WT>
 using WidAcc = f32x4[WidGeom<WT>::kTA][WidGeom<WT>::kNB];
 
-// Channel groups per super-row of the XCD raster (big_tile_of), W13 and W2,
-// by weight type.  Measured: e4m3fn at T = 2048 W13 1.89 / 1.80 / 2.63 ms
-// with 1 / 2 / 4 groups; bf16 (skew) W13 224 -> 218 us and W2 151 -> 147 us
-// with 1 and 2 groups instead of 2 and 4.
+// Channel groups per super-row of the XCD raster (big_tile_live), W13 and
+// W2, by weight type.  Measured at e4m3fn T = 2048 (raster over the
+// realised blocks, LDS token paths): W13 1.61 / 1.59 / 1.60 / 1.63 ms with
+// 2 / 4 / 8 / 16 groups, W2 0.99 / 0.96 / 0.97 / 0.97 ms with 2 / 4 / 8 /
+// 14; bf16 (skew) W13 224 -> 218 us and W2 151 -> 147 us with 1 and 2
+// groups instead of 2 and 4.
 #ifndef MOE_WID13_GROUP_COLS_FP8
-#define MOE_WID13_GROUP_COLS_FP8 2
+#define MOE_WID13_GROUP_COLS_FP8 4
 #endif
 #ifndef MOE_WID2_GROUP_COLS_FP8
 #define MOE_WID2_GROUP_COLS_FP8 4
@@ -427,8 +436,8 @@ __device__ __forceinline__ void wid_load_t_lds(__amdgpu_buffer_rsrc_t r, uint8_t
 // j * 4 / kSteps .. (j + 1) * 4 / kSteps - 1, and token load j while
 // j < kLoadsB (when kB).
 template <typename WT, bool kNT, bool kB>
-__device__ __forceinline__ void half_issue_part(const HalfLoader& ld, uint8_t* stage, int s,
-                                                int wave, int j) {
+__device__ __forceinline__ void half_issue_part(const HalfLoader& ld, uint8_t* stage,
+                                                uint8_t* tstage, int s, int wave, int j) {
   using G = WidGeom<WT>;
   using H = HalfGeom<WT>;
   constexpr int kPer = kWidLoadsA / G::kSteps;
@@ -444,34 +453,35 @@ __device__ __forceinline__ void half_issue_part(const HalfLoader& ld, uint8_t* s
   }
   if constexpr (kB) {
     if (j < H::kLoadsB)
-      wid_load_t_lds(ld.rb, stage + G::kStageBytes + (wave * H::kLoadsB + j) * 1024,
+      wid_load_t_lds(ld.rb, tstage + (wave * H::kLoadsB + j) * 1024,
                      ld.b[j] + static_cast<uint32_t>(s) * H::kBRowBytes);
   }
 }
 
 template <typename WT, bool kNT, bool kB>
-__device__ __forceinline__ void half_issue(const HalfLoader& ld, uint8_t* stage, int s, int wave) {
+__device__ __forceinline__ void half_issue(const HalfLoader& ld, uint8_t* stage, uint8_t* tstage,
+                                           int s, int wave) {
 #pragma unroll
-  for (int j = 0; j < WidGeom<WT>::kSteps; ++j) half_issue_part<WT, kNT, kB>(ld, stage, s, wave, j);
+  for (int j = 0; j < WidGeom<WT>::kSteps; ++j)
+    half_issue_part<WT, kNT, kB>(ld, stage, tstage, s, wave, j);
 }
 
 // k-step j: weight tiles t at rows arow0 + 16t (t < 2) and arow1 + 16(t - 2),
 // token tiles u at rows brow0 + 16u of the token region.
 template <typename WT>
-__device__ __forceinline__ void half_kstep(const uint8_t* cur, int j, int arow0, int arow1,
-                                           int brow0, HalfAcc& acc) {
-  using G = WidGeom<WT>;
+__device__ __forceinline__ void half_kstep(const uint8_t* cur, const uint8_t* tcur, int j,
+                                           int arow0, int arow1, int brow0, HalfAcc& acc) {
   using H = HalfGeom<WT>;
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15;
   const int g = lane >> 4;
   uint32_t la = wid_a_off<WT>(j);
-  uint32_t lb = G::kStageBytes + r16 * H::kBRowBytes + (((4 * j + g) ^ half_bswz<WT>(r16)) << 4);
+  uint32_t lb = r16 * H::kBRowBytes + (((4 * j + g) ^ half_bswz<WT>(r16)) << 4);
   asm volatile("" : "+v"(la), "+v"(lb));
   bf16x8 b[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u)
-    b[u] = as_frag(*reinterpret_cast<const uint4*>(cur + lb + (brow0 + 16 * u) * H::kBRowBytes));
+    b[u] = as_frag(*reinterpret_cast<const uint4*>(tcur + lb + (brow0 + 16 * u) * H::kBRowBytes));
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int row = t < 2 ? arow0 + 16 * t : arow1 + 16 * (t - 2);
@@ -494,7 +504,8 @@ struct HalfRing {
   using G = WidGeom<WT>;
   static constexpr int kL = kWidLoadsA + (kB ? HalfGeom<WT>::kLoadsB : 0);
   const HalfLoader& ld;
-  uint8_t* const (&buf)[4];
+  uint8_t* const (&buf)[4];  // weights of stage p
+  uint8_t* const (&tb)[4];   // token rows of stage p
   int wave, arow0, arow1, brow0;
 
   template <int p, int W, bool kIssue>
@@ -505,20 +516,20 @@ struct HalfRing {
     if constexpr (kLive) {
 #pragma unroll
       for (int j = 0; j < G::kSteps; ++j) {
-        if constexpr (kIssue) half_issue_part<WT, kNT, kB>(ld, buf[n], s + 2, wave, j);
-        half_kstep<WT>(buf[p], j, arow0, arow1, brow0, acc);
+        if constexpr (kIssue) half_issue_part<WT, kNT, kB>(ld, buf[n], tb[n], s + 2, wave, j);
+        half_kstep<WT>(buf[p], tb[p], j, arow0, arow1, brow0, acc);
         __builtin_amdgcn_sched_barrier(0);
       }
     } else if constexpr (kIssue) {
-      half_issue<WT, kNT, kB>(ld, buf[n], s + 2, wave);
+      half_issue<WT, kNT, kB>(ld, buf[n], tb[n], s + 2, wave);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
 
   template <int R>  // R = nst % 3; nst >= 2
   __device__ __forceinline__ void run_r(int nst, HalfAcc& acc) const {
-    half_issue<WT, kNT, kB>(ld, buf[0], 0, wave);
-    half_issue<WT, kNT, kB>(ld, buf[1], 1, wave);
+    half_issue<WT, kNT, kB>(ld, buf[0], tb[0], 0, wave);
+    half_issue<WT, kNT, kB>(ld, buf[1], tb[1], 1, wave);
     int s = 0;
     for (; s + 5 <= nst; s += 3) {
       step<0, 1, true>(s, acc);
@@ -549,19 +560,20 @@ struct HalfRing {
 };
 
 template <typename WT>
-__device__ __forceinline__ void half_run(const HalfLoader& ld, uint8_t* const (&buf)[4], int nst,
+__device__ __forceinline__ void half_run(const HalfLoader& ld, uint8_t* const (&buf)[4],
+                                         uint8_t* const (&tb)[4], int nst,
                                          int wave, int arow0, int arow1, int brow0, bool nt,
                                          bool b_live, bool live, HalfAcc& acc) {
   // a live wave loads its eight token rows even when they are all padding
   // (their loads read zeros past the buffer's end), so kLive implies kB
   if (nt) {
-    if (live) HalfRing<WT, true, true, true>{ld, buf, wave, arow0, arow1, brow0}.run(nst, acc);
-    else if (b_live) HalfRing<WT, true, true, false>{ld, buf, wave, arow0, arow1, brow0}.run(nst, acc);
-    else HalfRing<WT, true, false, false>{ld, buf, wave, arow0, arow1, brow0}.run(nst, acc);
+    if (live) HalfRing<WT, true, true, true>{ld, buf, tb, wave, arow0, arow1, brow0}.run(nst, acc);
+    else if (b_live) HalfRing<WT, true, true, false>{ld, buf, tb, wave, arow0, arow1, brow0}.run(nst, acc);
+    else HalfRing<WT, true, false, false>{ld, buf, tb, wave, arow0, arow1, brow0}.run(nst, acc);
   } else {
-    if (live) HalfRing<WT, false, true, true>{ld, buf, wave, arow0, arow1, brow0}.run(nst, acc);
-    else if (b_live) HalfRing<WT, false, true, false>{ld, buf, wave, arow0, arow1, brow0}.run(nst, acc);
-    else HalfRing<WT, false, false, false>{ld, buf, wave, arow0, arow1, brow0}.run(nst, acc);
+    if (live) HalfRing<WT, false, true, true>{ld, buf, tb, wave, arow0, arow1, brow0}.run(nst, acc);
+    else if (b_live) HalfRing<WT, false, true, false>{ld, buf, tb, wave, arow0, arow1, brow0}.run(nst, acc);
+    else HalfRing<WT, false, false, false>{ld, buf, tb, wave, arow0, arow1, brow0}.run(nst, acc);
   }
 }
 
@@ -569,6 +581,7 @@ __device__ __forceinline__ void half_run(const HalfLoader& ld, uint8_t* const (&
 // of channels n0 + 32 wm .. +31 for tokens 32 wn .. +31.
 template <typename WT>
 __device__ __forceinline__ void half13_tile(const WidLoader& wl, uint8_t* const (&buf)[4],
+                                            uint8_t* const (&tb)[4],
                                             const int32_t* blk, const float* s13, int scale_mode,
                                             bf16_t* h, int b, int e, int n0, int d, int I, int k,
                                             int A, uint32_t xbytes, bool nt) {
@@ -597,7 +610,7 @@ __device__ __forceinline__ void half13_tile(const WidLoader& wl, uint8_t* const 
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int u = 0; u < 2; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
-  half_run<WT>(ld, buf, d / G::kK, wave, 32 * wm, 128 + 32 * wm, 32 * wn, nt, b_live, live, acc);
+  half_run<WT>(ld, buf, tb, d / G::kK, wave, 32 * wm, 128 + 32 * wm, 32 * wn, nt, b_live, live, acc);
   if (!live) return;
 
   // lane: token column r16 of tile u, channels n0 + 32wm + 16t + 4g .. +3
@@ -633,6 +646,7 @@ __device__ __forceinline__ void half13_tile(const WidLoader& wl, uint8_t* const 
 // channels n0 + 64 wm .. +63 for tokens 32 wn .. +31.
 template <typename WT>
 __device__ __forceinline__ void half2_tile(const WidLoader& wl, uint8_t* const (&buf)[4],
+                                           uint8_t* const (&tb)[4],
                                            const int32_t* blk, const float* s2, int scale_mode,
                                            const float* topk_w, float* y, int e, int n0, int d,
                                            int I, int A, int k_begin, int nst, uint32_t hbytes,
@@ -662,7 +676,7 @@ __device__ __forceinline__ void half2_tile(const WidLoader& wl, uint8_t* const (
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int u = 0; u < 2; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
-  half_run<WT>(ld, buf, nst, wave, 64 * wm, 64 * wm + 32, 32 * wn, nt, b_live, live, acc);
+  half_run<WT>(ld, buf, tb, nst, wave, 64 * wm, 64 * wm + 32, 32 * wn, nt, b_live, live, acc);
   if (!live) return;
 
   // lane: token column r16 of tile u, channels n0 + 64wm + 16t + 4g .. +3
@@ -687,6 +701,314 @@ __device__ __forceinline__ void half2_tile(const WidLoader& wl, uint8_t* const (
     }
   }
 }
+
+// ------------------------------------------------------------ full blocks (e4m3fn)
+// A block with more than 64 real tokens (e4m3fn weights) also takes its
+// token rows through LDS: all 128 rows of a stage (256 bytes each, 32 KB),
+// loaded once per workgroup as whole rows, where the register path loads
+// each token fragment twice as 64-byte half lines.  Weights and tokens
+// together would take 64 KB a stage, so the two rings differ in depth: the
+// weights keep three stages in flight (32 KB each) and the tokens two (the
+// token rows are gathered rows of x or the block's h rows, which sit in the
+// caches more often than not, so one stage ahead suffices): 96 + 64 KB.  At
+// stage s a wave first issues the token rows of s + 1, then the weights of
+// s + 2 a part per k-step, so that the wait at stage s + 1 lets the weights
+// of s + 2 (the last four loads) stay in flight.  The token rows of a stage
+// lie in two 16 KB arrays (rows 0-63 and 64-127).  Eight waves of 32 weight
+// rows x all live token tiles (wave w: W13 gate rows 16w .. +15 and the
+// matching up rows, W2 output rows 32w .. +31), so every weight fragment is
+// widened once; a block of at most 96 tokens runs six token tiles, a
+// larger one eight.
+#ifndef MOE_WID_FULL
+#define MOE_WID_FULL 1
+#endif
+constexpr int kFullRowBytes = 256;  // bf16 token row per stage (128 K)
+constexpr int kFullLoadsB = 4;      // token loads per wave and stage, four rows each
+
+struct FullLoader {
+  __amdgpu_buffer_rsrc_t ra, rb;
+  uint32_t a[kWidLoadsA];   // weight sources, as WidLoader
+  uint32_t b[kFullLoadsB];  // token source of load i at K = 0
+};
+
+typedef f32x4 FullAcc[2][8];
+
+// Token load i of wave w fills block rows 16w + 4i + l / 16, lane l at
+// physical slot l % 16, which holds logical slot (l % 16) ^ (row & 15).
+__device__ __forceinline__ int full_b_row(int wave, int i, int lane) {
+  return 16 * wave + 4 * i + lane / 16;
+}
+__device__ __forceinline__ int full_b_slot(int row, int lane) { return (lane % 16) ^ (row & 15); }
+
+// Weight load j of stage s (one per k-step), plain or nontemporal.
+template <bool kNT>
+__device__ __forceinline__ void full_issue_w(const FullLoader& ld, uint8_t* wst, int s, int wave,
+                                             int j) {
+  uint8_t* dst = wst + (wave * kWidLoadsA + j) * 1024;
+  const uint32_t off = ld.a[j] + static_cast<uint32_t>(s) * kWidRowBytes;
+  if constexpr (kNT)
+    wid_load_w_nt(ld.ra, dst, off);
+  else
+    wid_load_w(ld.ra, dst, off);
+}
+
+// The wave's token rows of stage s (waves 0-3 rows 0-63 into xa, 4-7 rows
+// 64-127 into xb).
+__device__ __forceinline__ void full_issue_t(const FullLoader& ld, uint8_t* xa, uint8_t* xb, int s,
+                                             int wave) {
+  uint8_t* base = (wave < 4 ? xa : xb) + (wave & 3) * 16 * kFullRowBytes;
+#pragma unroll
+  for (int i = 0; i < kFullLoadsB; ++i)
+    wid_load_t_lds(ld.rb, base + i * 1024, ld.b[i] + static_cast<uint32_t>(s) * kFullRowBytes);
+}
+
+// k-step j: weight tiles at rows arow0 and arow1 of the stage, token tiles
+// u < NL at block rows 16u .. +15.
+template <int NL>
+__device__ __forceinline__ void full_kstep(const uint8_t* wcur, const uint8_t* xa,
+                                           const uint8_t* xb, int j, int arow0, int arow1,
+                                           FullAcc& acc) {
+  const int lane = threadIdx.x & 63;
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  uint32_t la = wid_a_off<fp8_t>(j);
+  uint32_t lb = r16 * kFullRowBytes + (((4 * j + g) ^ r16) << 4);
+  asm volatile("" : "+v"(la), "+v"(lb));
+  bf16x8 bf[NL];
+#pragma unroll
+  for (int u = 0; u < NL; ++u)
+    bf[u] = as_frag(*reinterpret_cast<const uint4*>((u < 4 ? xa : xb) + lb +
+                                                    16 * (u & 3) * kFullRowBytes));
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const uint2 q = *reinterpret_cast<const uint2*>(wcur + la + (t ? arow1 : arow0) * kWidRowBytes);
+    const bf16x8 a = as_frag(e4m3x8_to_frag_bits(q.x, q.y));
+#pragma unroll
+    for (int u = 0; u < NL; ++u) acc[t][u] = mfma16x16x32(a, bf[u], acc[t][u]);
+  }
+}
+
+// The two rings (weights depth 3, tokens depth 2) over `total` >= 2 stages;
+// the loop runs six stages at a time so that both buffer indices are
+// compile-time constants.
+template <bool kNT, int NL>
+struct FullRing {
+  const FullLoader& ld;
+  uint8_t* const (&wb)[4];
+  uint8_t* const (&xa)[2];
+  uint8_t* const (&xb)[2];
+  int wave, arow0, arow1, total;
+
+  template <int p>
+  __device__ __forceinline__ void step(int s, FullAcc& acc) const {
+    // stage s's loads are in; the weights of s + 1 (issued last) may not be
+    if (s + 1 < total)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kWidLoadsA));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    big_barrier();
+    if (s + 1 < total) full_issue_t(ld, xa[(p + 1) % 2], xb[(p + 1) % 2], s + 1, wave);
+    const bool iw = s + 2 < total;
+#pragma unroll
+    for (int j = 0; j < kWidLoadsA; ++j) {
+      if (iw) full_issue_w<kNT>(ld, wb[(p + 2) % 3], s + 2, wave, j);
+      full_kstep<NL>(wb[p % 3], xa[p % 2], xb[p % 2], j, arow0, arow1, acc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  __device__ __forceinline__ void run(FullAcc& acc) const {
+#pragma unroll
+    for (int j = 0; j < kWidLoadsA; ++j) full_issue_w<kNT>(ld, wb[0], 0, wave, j);
+    full_issue_t(ld, xa[0], xb[0], 0, wave);
+#pragma unroll
+    for (int j = 0; j < kWidLoadsA; ++j) full_issue_w<kNT>(ld, wb[1], 1, wave, j);
+    for (int s = 0; s < total; s += 6) {
+      step<0>(s, acc);
+      if (s + 1 < total) step<1>(s + 1, acc);
+      if (s + 2 < total) step<2>(s + 2, acc);
+      if (s + 3 < total) step<3>(s + 3, acc);
+      if (s + 4 < total) step<4>(s + 4, acc);
+      if (s + 5 < total) step<5>(s + 5, acc);
+    }
+  }
+};
+
+template <int NL>
+__device__ __forceinline__ void full_run_nl(const FullLoader& ld, uint8_t* const (&wb)[4],
+                                            uint8_t* const (&xa)[2], uint8_t* const (&xb)[2],
+                                            int total, int wave, int arow0, int arow1, bool nt,
+                                            FullAcc& acc) {
+  if (nt)
+    FullRing<true, NL>{ld, wb, xa, xb, wave, arow0, arow1, total}.run(acc);
+  else
+    FullRing<false, NL>{ld, wb, xa, xb, wave, arow0, arow1, total}.run(acc);
+}
+
+// The token tiles a full block runs: six when its real tokens fit in 96
+// rows, else eight.
+__device__ __forceinline__ bool full_six(const int32_t* blk, int A) {
+  return __builtin_amdgcn_readfirstlane(blk[96]) >= A;
+}
+
+// W13 of a full block: wave w holds gate and up of channels n0 + 16w + 4g
+// .. +3 (lane (r16, g)) for token column r16 of every token tile u.
+template <int NL>
+__device__ __forceinline__ void full13_store(const FullAcc& acc, const float* s13, int scale_mode,
+                                             bf16_t* h, int b, int e, int n0, int I) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  const int c = n0 + 16 * wave + 4 * g;
+  if (c >= I) return;
+  const size_t two_i = 2 * static_cast<size_t>(I);
+  float sg[4], su[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    sg[v] = load_scale(s13, scale_mode, e, static_cast<size_t>(e) * two_i + c + v);
+    su[v] = load_scale(s13, scale_mode, e, static_cast<size_t>(e) * two_i + I + c + v);
+  }
+#pragma unroll
+  for (int u = 0; u < NL; ++u) {
+    const size_t row = static_cast<size_t>(b) * kWidTokens + 16 * u + r16;
+    uint32_t packed[2];
+#pragma unroll
+    for (int v = 0; v < 4; v += 2) {
+      const float h0 = silu(acc[0][u][v] * sg[v]) * (acc[1][u][v] * su[v]);
+      const float h1 = silu(acc[0][u][v + 1] * sg[v + 1]) * (acc[1][u][v + 1] * su[v + 1]);
+      packed[v / 2] = static_cast<uint32_t>(f32_to_bf16(h0)) |
+                      (static_cast<uint32_t>(f32_to_bf16(h1)) << 16);
+    }
+    *reinterpret_cast<uint2*>(h + row * I + c) = uint2{packed[0], packed[1]};
+  }
+}
+
+template <int NL>
+__device__ __forceinline__ void full13_nl(const FullLoader& ld, uint8_t* const (&wb)[4],
+                                          uint8_t* const (&xa)[2], uint8_t* const (&xb)[2],
+                                          const float* s13, int scale_mode, bf16_t* h, int b,
+                                          int e, int n0, int d, int I, bool nt) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  FullAcc acc;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  full_run_nl<NL>(ld, wb, xa, xb, d / WidGeom<fp8_t>::kK, wave, 16 * wave, 128 + 16 * wave, nt,
+                  acc);
+  full13_store<NL>(acc, s13, scale_mode, h, b, e, n0, I);
+}
+
+__device__ __forceinline__ void full13_tile(const WidLoader& wl, uint8_t* const (&wb)[4],
+                                            uint8_t* const (&xa)[2], uint8_t* const (&xb)[2],
+                                            const int32_t* blk, const float* s13, int scale_mode,
+                                            bf16_t* h, int b, int e, int n0, int d, int I, int k,
+                                            int A, uint32_t xbytes, bool nt) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  FullLoader ld;
+  ld.ra = wl.ra;
+  ld.rb = wl.rb;
+#pragma unroll
+  for (int i = 0; i < kWidLoadsA; ++i) ld.a[i] = wl.a[i];
+#pragma unroll
+  for (int i = 0; i < kFullLoadsB; ++i) {
+    const int r = full_b_row(wave, i, lane);
+    const int f = blk[r];
+    ld.b[i] = f < A ? 2 * static_cast<uint32_t>(f / k) * d + 16 * full_b_slot(r, lane) : xbytes;
+  }
+  if (full_six(blk, A))
+    full13_nl<6>(ld, wb, xa, xb, s13, scale_mode, h, b, e, n0, d, I, nt);
+  else
+    full13_nl<8>(ld, wb, xa, xb, s13, scale_mode, h, b, e, n0, d, I, nt);
+}
+
+// W2 of a full block: wave w holds output channels n0 + 32w + 16t + 4g ..
+// +3 (weight tile t) for token column r16 of every token tile u.
+template <int NL>
+__device__ __forceinline__ void full2_nl(const FullLoader& ld, uint8_t* const (&wb)[4],
+                                         uint8_t* const (&xa)[2], uint8_t* const (&xb)[2],
+                                         const int32_t* blk, const float* s2, int scale_mode,
+                                         const float* topk_w, float* y, int e, int n0, int d,
+                                         int A, int nst, bool nt) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  FullAcc acc;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  full_run_nl<NL>(ld, wb, xa, xb, nst, wave, 32 * wave, 32 * wave + 16, nt, acc);
+#pragma unroll
+  for (int u = 0; u < NL; ++u) {
+    const int f = blk[16 * u + r16];
+    if (f < A) {
+      const float gate = topk_w[f];
+      float* yrow = y + static_cast<size_t>(f) * d;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int c = n0 + 32 * wave + 16 * t + 4 * g;
+        if (c >= d) continue;
+        const size_t base = static_cast<size_t>(e) * d + c;
+        float sc[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sc[v] = load_scale(s2, scale_mode, e, base + v);
+        *reinterpret_cast<float4*>(yrow + c) =
+            float4{acc[t][u][0] * sc[0] * gate, acc[t][u][1] * sc[1] * gate,
+                   acc[t][u][2] * sc[2] * gate, acc[t][u][3] * sc[3] * gate};
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void full2_tile(const WidLoader& wl, uint8_t* const (&wb)[4],
+                                           uint8_t* const (&xa)[2], uint8_t* const (&xb)[2],
+                                           const int32_t* blk, const float* s2, int scale_mode,
+                                           const float* topk_w, float* y, int e, int n0, int d,
+                                           int I, int A, int k_begin, int nst, uint32_t hbytes,
+                                           bool nt) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  FullLoader ld;
+  ld.ra = wl.ra;
+  ld.rb = wl.rb;
+#pragma unroll
+  for (int i = 0; i < kWidLoadsA; ++i) ld.a[i] = wl.a[i];
+  // h rows of the block; rows of padding slots read zeros
+#pragma unroll
+  for (int i = 0; i < kFullLoadsB; ++i) {
+    const int r = full_b_row(wave, i, lane);
+    ld.b[i] = blk[r] < A ? 2 * (static_cast<uint32_t>(r) * I + k_begin) + 16 * full_b_slot(r, lane)
+                         : hbytes;
+  }
+  if (full_six(blk, A))
+    full2_nl<6>(ld, wb, xa, xb, blk, s2, scale_mode, topk_w, y, e, n0, d, A, nst, nt);
+  else
+    full2_nl<8>(ld, wb, xa, xb, blk, s2, scale_mode, topk_w, y, e, n0, d, A, nst, nt);
+}
+
+// e4m3fn kernels' LDS: three 32 KB weight stages (`buf`, also the register
+// path's ring) and four 16 KB token arrays: the half-full path's three token
+// stages (`htb`), or the full path's two stages of two halves (`fxa`,
+// `fxb`).  160 KB.
+#define WID_FP8_LDS()                                                                    \
+  __shared__ __attribute__((aligned(1024))) uint8_t wst0[WidGeom<fp8_t>::kStageBytes];  \
+  __shared__ __attribute__((aligned(1024))) uint8_t wst1[WidGeom<fp8_t>::kStageBytes];  \
+  __shared__ __attribute__((aligned(1024))) uint8_t wst2[WidGeom<fp8_t>::kStageBytes];  \
+  __shared__ __attribute__((aligned(1024))) uint8_t xta0[64 * kFullRowBytes];           \
+  __shared__ __attribute__((aligned(1024))) uint8_t xtb0[64 * kFullRowBytes];           \
+  __shared__ __attribute__((aligned(1024))) uint8_t xta1[64 * kFullRowBytes];           \
+  __shared__ __attribute__((aligned(1024))) uint8_t xtb1[64 * kFullRowBytes];           \
+  uint8_t* const buf[4] = {wst0, wst1, wst2, wst2};                                      \
+  uint8_t* const htb[4] = {xta0, xta1, xtb0, xtb0};                                      \
+  uint8_t* const fxa[2] = {xta0, xta1};                                                  \
+  uint8_t* const fxb[2] = {xtb0, xtb1}
+static_assert(HalfGeom<fp8_t>::kBBytes == 64 * kFullRowBytes, "a half-full token stage is 64 rows");
+static_assert(3 * WidGeom<fp8_t>::kStageBytes + 4 * 64 * kFullRowBytes <= 160 * 1024,
+              "the e4m3fn LDS fits");
 
 // ------------------------------------------------------------ W13 + SiLU*mul
 // Tile (b, y): channels n0 = 128y .. +127 (rows: 128 gate, then 128 up;
@@ -789,17 +1111,20 @@ __global__ __launch_bounds__(WidGeom<WT>::kThreads) void ffn13_wide_kernel(
     ld.a[i] = c < I ? wrow * row_bytes + 16 * wid_a_slot(r, lane) : wbytes;
   }
   const bool nt = wid_single_block(block_expert, b, npad / kWidTokens, e);
-  if constexpr (G::kD == 3) {
-    constexpr int kBytes = HalfGeom<WT>::kStageBytes > G::kStageBytes ? HalfGeom<WT>::kStageBytes
-                                                                        : G::kStageBytes;
-    WID_RING3(buf, (sizeof(WT) == 1 && MOE_WID_HALF) ? kBytes : G::kStageBytes);
-    if constexpr (sizeof(WT) == 1 && MOE_WID_HALF) {
-      // real slots come first: no real slot past row 63 means a half-full block
-      if (__builtin_amdgcn_readfirstlane(blk[kHalfTokens]) >= A) {
-        half13_tile<WT>(ld, buf, blk, s13, scale_mode, h, b, e, n0, d, I, k, A, xbytes, nt);
-        return;
-      }
+  if constexpr (sizeof(WT) == 1 && G::kWaves == 8) {
+    WID_FP8_LDS();
+    // real slots come first: no real slot past row 63 means a half-full block
+    if (MOE_WID_HALF && __builtin_amdgcn_readfirstlane(blk[kHalfTokens]) >= A) {
+      half13_tile<WT>(ld, buf, htb, blk, s13, scale_mode, h, b, e, n0, d, I, k, A, xbytes, nt);
+      return;
     }
+    if (MOE_WID_FULL) {
+      full13_tile(ld, buf, fxa, fxb, blk, s13, scale_mode, h, b, e, n0, d, I, k, A, xbytes, nt);
+      return;
+    }
+    wide13_tile<WT>(ld, buf, blk, s13, scale_mode, h, b, e, n0, d, I, k, A, xbytes, nt);
+  } else if constexpr (G::kD == 3) {
+    WID_RING3(buf, G::kStageBytes);
     wide13_tile<WT>(ld, buf, blk, s13, scale_mode, h, b, e, n0, d, I, k, A, xbytes, nt);
   } else {
     constexpr int kBytes = HalfGeom<WT>::kStageBytes > G::kStageBytes ? HalfGeom<WT>::kStageBytes
@@ -807,7 +1132,9 @@ __global__ __launch_bounds__(WidGeom<WT>::kThreads) void ffn13_wide_kernel(
     WID_RING4(buf, MOE_WID_HALF_BF16 ? kBytes : G::kStageBytes);
     if constexpr (MOE_WID_HALF_BF16) {
       if (__builtin_amdgcn_readfirstlane(blk[kHalfTokens]) >= A) {
-        half13_tile<WT>(ld, buf, blk, s13, scale_mode, h, b, e, n0, d, I, k, A, xbytes, nt);
+        uint8_t* const tb[4] = {buf[0] + G::kStageBytes, buf[1] + G::kStageBytes,
+                                buf[2] + G::kStageBytes, buf[3] + G::kStageBytes};
+        half13_tile<WT>(ld, buf, tb, blk, s13, scale_mode, h, b, e, n0, d, I, k, A, xbytes, nt);
         return;
       }
     }
@@ -910,17 +1237,22 @@ __global__ __launch_bounds__(WidGeom<WT>::kThreads) void ffn2_wide_kernel(
                     : wbytes;
   }
   const bool nt = wid_single_block(block_expert, b, npad / kWidTokens, e);
-  if constexpr (G::kD == 3) {
-    constexpr int kBytes = HalfGeom<WT>::kStageBytes > G::kStageBytes ? HalfGeom<WT>::kStageBytes
-                                                                        : G::kStageBytes;
-    WID_RING3(buf, (sizeof(WT) == 1 && MOE_WID_HALF) ? kBytes : G::kStageBytes);
-    if constexpr (sizeof(WT) == 1 && MOE_WID_HALF) {
-      if (__builtin_amdgcn_readfirstlane(blk[kHalfTokens]) >= A) {
-        half2_tile<WT>(ld, buf, blk, s2, scale_mode, topk_w, y, e, n0, d, I, A, k_begin, nst,
-                       hbytes, nt);
-        return;
-      }
+  if constexpr (sizeof(WT) == 1 && G::kWaves == 8) {
+    WID_FP8_LDS();
+    if (MOE_WID_HALF && __builtin_amdgcn_readfirstlane(blk[kHalfTokens]) >= A) {
+      half2_tile<WT>(ld, buf, htb, blk, s2, scale_mode, topk_w, y, e, n0, d, I, A, k_begin, nst,
+                     hbytes, nt);
+      return;
     }
+    if (MOE_WID_FULL) {
+      full2_tile(ld, buf, fxa, fxb, blk, s2, scale_mode, topk_w, y, e, n0, d, I, A, k_begin, nst,
+                 hbytes, nt);
+      return;
+    }
+    wide2_tile<WT>(ld, buf, blk, s2, scale_mode, topk_w, y, e, n0, d, I, A, k_begin, nst,
+                   hbytes, nt);
+  } else if constexpr (G::kD == 3) {
+    WID_RING3(buf, G::kStageBytes);
     wide2_tile<WT>(ld, buf, blk, s2, scale_mode, topk_w, y, e, n0, d, I, A, k_begin, nst,
                    hbytes, nt);
   } else {
@@ -929,7 +1261,9 @@ __global__ __launch_bounds__(WidGeom<WT>::kThreads) void ffn2_wide_kernel(
     WID_RING4(buf, MOE_WID_HALF_BF16 ? kBytes : G::kStageBytes);
     if constexpr (MOE_WID_HALF_BF16) {
       if (__builtin_amdgcn_readfirstlane(blk[kHalfTokens]) >= A) {
-        half2_tile<WT>(ld, buf, blk, s2, scale_mode, topk_w, y, e, n0, d, I, A, k_begin, nst,
+        uint8_t* const tb[4] = {buf[0] + G::kStageBytes, buf[1] + G::kStageBytes,
+                                buf[2] + G::kStageBytes, buf[3] + G::kStageBytes};
+        half2_tile<WT>(ld, buf, tb, blk, s2, scale_mode, topk_w, y, e, n0, d, I, A, k_begin, nst,
                        hbytes, nt);
         return;
       }

@@ -283,3 +283,81 @@ def test_wide_half_block_token_rows_find_their_fragments():
             for tile in range(0, 64, 16):
                 for e in range(8):
                     assert lds[off + tile * 256 + 2 * e] == (tile + r16, 32 * j + 8 * g + e)
+
+
+def test_wide_full_block_token_rows_find_their_fragments():
+    """Full blocks of the register-token tile (e4m3fn weights, more than 64
+    tokens): 128 token rows of 256 bytes per stage in two 16 KB arrays (rows
+    0-63 and 64-127); wave w, load i fills rows 16w + 4i + l / 16 at
+    physical slot l % 16 holding logical slot (l % 16) ^ (row & 15); the
+    k-step j fragment of lane (r16, g) in token tile u reads k = 32j + 8g ..
+    +7 of row 16u + r16."""
+    lds = {}
+    for w in range(8):
+        region = "a" if w < 4 else "b"
+        for i in range(4):
+            base = (w & 3) * 16 * 256 + i * 1024
+            for lane in range(64):
+                row = 16 * w + 4 * i + lane // 16
+                slot = (lane % 16) ^ (row & 15)
+                off = base + lane * 16
+                assert off // 256 == row % 64 and off + 16 <= 16384
+                for byte in range(0, 16, 2):
+                    assert (region, off + byte) not in lds
+                    lds[(region, off + byte)] = (row, (16 * slot + byte) // 2)
+    assert len(lds) == 128 * 128
+    for lane in range(64):
+        r16, g = lane % 16, lane // 16
+        for j in range(4):
+            lb = r16 * 256 + (((4 * j + g) ^ r16) << 4)
+            for u in range(8):
+                region = "a" if u < 4 else "b"
+                for e in range(8):
+                    got = lds[(region, lb + 16 * (u & 3) * 256 + 2 * e)]
+                    assert got == (16 * u + r16, 32 * j + 8 * g + e)
+
+
+def _full_rings(total):
+    """FullRing::run: weights W(0), tokens T(0), weights W(1) up front; stage s
+    waits until only the weights of s + 1 (when issued) may be in flight,
+    then issues T(s + 1) into token buffer (s + 1) % 2 and W(s + 2) into
+    weight buffer (s + 2) % 3.  Checks that each stage's operands have
+    landed, in the buffers it reads, and that no buffer is reloaded before
+    the stage that read it is over."""
+    issued = []  # (kind, stage, buffer) in issue order
+    wbuf, xbuf = {}, {}
+
+    def issue(kind, st):
+        nb = 3 if kind == "W" else 2
+        held = wbuf if kind == "W" else xbuf
+        b = st % nb
+        assert b not in held, (kind, st, held)  # the stage that used it is over
+        held[b] = st
+        issued.append((kind, st))
+
+    issue("W", 0)
+    issue("T", 0)
+    issue("W", 1)
+    done = []
+    for s in range(total):
+        allowed = 1 if s + 1 < total else 0   # loads (of four) still in flight
+        landed = issued[:len(issued) - allowed]
+        assert ("W", s) in landed and ("T", s) in landed
+        if allowed:
+            assert issued[-1] == ("W", s + 1)
+        # the barrier: stage s - 1 is over everywhere
+        for held, nb in ((wbuf, 3), (xbuf, 2)):
+            for b in [b for b, st in held.items() if st == s - 1]:
+                del held[b]
+        if s + 1 < total:
+            issue("T", s + 1)
+        if s + 2 < total:
+            issue("W", s + 2)
+        assert wbuf.get(s % 3) == s and xbuf.get(s % 2) == s
+        done.append(s)
+    return done
+
+
+@pytest.mark.parametrize("total", list(range(3, 20)) + [56, 112])
+def test_wide_full_block_rings(total):
+    assert _full_rings(total) == list(range(total))
