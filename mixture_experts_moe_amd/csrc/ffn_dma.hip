@@ -107,14 +107,28 @@ struct DmaOperands {
       __builtin_amdgcn_global_load_lds(src + 16 * (l31 ^ j), lds + 1024 * i, 16, 0, kDmaAux);
     }
   }
-  template <int NSL>
+  // kDevA: the token rows were written in this launch by workgroups that
+  // may sit on other XCDs (the fused kernel's h): each 16-byte fragment is
+  // read as two 8-byte agent-scope atomic loads, which bypass this XCD's L2
+  // copy, so two load instructions per fragment (kTokenLoadsPer).
+  template <int NSL, bool kDevA = false>
   __device__ __forceinline__ void issue_a(uint4 (&a)[NS][kF], int k0) const {
 #pragma unroll
     for (int s = 0; s < NSL; ++s)
       if (!MOE_DMA_TOKEN_MASK || tlive[s]) {
 #pragma unroll
-        for (int i = 0; i < kF; ++i)
-          a[s][i] = *reinterpret_cast<const uint4*>(arow[s] + k0 + ActChunk<WT, 64>::off(i, g));
+        for (int i = 0; i < kF; ++i) {
+          const bf16_t* src = arow[s] + k0 + ActChunk<WT, 64>::off(i, g);
+          if constexpr (kDevA) {
+            const uint64_t* q = reinterpret_cast<const uint64_t*>(src);
+            const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            a[s][i] = uint4{static_cast<uint32_t>(lo), static_cast<uint32_t>(lo >> 32),
+                            static_cast<uint32_t>(hi), static_cast<uint32_t>(hi >> 32)};
+          } else {
+            a[s][i] = *reinterpret_cast<const uint4*>(src);
+          }
+        }
       }
   }
 
@@ -167,10 +181,13 @@ struct DmaOperands {
 // MFMAs.  Every wait count is a compile-time immediate: the steady loop goes
 // P chunks at a time, and the last P-1 chunks (which issue nothing) run from
 // a switch on the buffer they start in.  NSL: live token subtiles.
-template <typename WT, int NROW, int NS, int P, int NSL>
+template <typename WT, int NROW, int NS, int P, int NSL, bool kDevA = false>
 struct DmaRing {
   using Op = DmaOperands<WT, NROW, NS>;
-  static constexpr int kL = DmaGeom<WT, NROW, NSL>::kLoads;
+  // vector-memory instructions per stage: the weight loads, then one token
+  // load per fragment (two with device-scope token loads)
+  static constexpr int kL =
+      DmaGeom<WT, NROW, NSL>::kLoadsW + DmaGeom<WT, NROW, NSL>::kLoadsA * (kDevA ? 2 : 1);
   static constexpr int kKC = dma_kc<WT>();
   static constexpr int kF = Op::kF;
   const Op& op;
@@ -180,7 +197,7 @@ struct DmaRing {
   __device__ __forceinline__ void issue(uint8_t* stage, uint4 (&a)[NS][kF], int c) const {
     const int k = k_begin + c * kKC;
     op.issue_w(stage, static_cast<size_t>(k) * sizeof(WT));
-    op.template issue_a<NSL>(a, k);
+    op.template issue_a<NSL, kDevA>(a, k);
   }
 
   // chunk c in buffer p, issuing chunk c+P-1
@@ -245,14 +262,14 @@ struct DmaRing {
   }
 };
 
-template <typename WT, int NROW, int NS, int P>
+template <typename WT, int NROW, int NS, int P, bool kDevA = false>
 __device__ __forceinline__ void dma_dot(int nsub, const DmaOperands<WT, NROW, NS>& op,
                                         uint8_t* const (&ring)[4], int k_begin, int nch,
                                         f32x4 (&acc)[NS][NROW]) {
   if (nsub == 1 || NS == 1) {
-    DmaRing<WT, NROW, NS, P, 1>{op, ring, k_begin, nch}.run(acc);
+    DmaRing<WT, NROW, NS, P, 1, kDevA>{op, ring, k_begin, nch}.run(acc);
   } else {
-    DmaRing<WT, NROW, NS, P, NS>{op, ring, k_begin, nch}.run(acc);
+    DmaRing<WT, NROW, NS, P, NS, kDevA>{op, ring, k_begin, nch}.run(acc);
   }
 }
 
@@ -279,7 +296,9 @@ __device__ __forceinline__ void dma_lanes(DmaOperands<WT, NROW, NS>& op, size_t 
 // h[row, n] = SiLU(s_g gate) * (s_u up) for the live subtiles (pad rows
 // included: their columns never reach an output).
 
-template <typename WT, int NS, int P, int RC = 1>
+// kDevH: h is written with agent-scope atomic stores (write-through past
+// this XCD's L2) for readers in the same launch on other XCDs.
+template <typename WT, int NS, int P, int RC = 1, bool kDevH = false>
 __device__ __forceinline__ void dma13_tile(
     const bf16_t* __restrict__ x, const WT* __restrict__ w13, const float* __restrict__ s13,
     int scale_mode, const int32_t* __restrict__ sorted_ids,
@@ -337,7 +356,12 @@ __device__ __forceinline__ void dma13_tile(
           packed[v / 2] = static_cast<uint32_t>(f32_to_bf16(h0)) |
                           (static_cast<uint32_t>(f32_to_bf16(h1)) << 16);
         }
-        *reinterpret_cast<uint2*>(h + row * I + nb) = uint2{packed[0], packed[1]};
+        if constexpr (kDevH)
+          __hip_atomic_store(reinterpret_cast<uint64_t*>(h + row * I + nb),
+                             static_cast<uint64_t>(packed[0]) | (static_cast<uint64_t>(packed[1]) << 32),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+          *reinterpret_cast<uint2*>(h + row * I + nb) = uint2{packed[0], packed[1]};
       }
     }
   }
@@ -377,7 +401,8 @@ __device__ __forceinline__ void store_device4(float* p, const float4& o) {
 
 // kDevice: partials written with store_device4 (for a reader in the same
 // launch on another XCD) instead of plain stores.
-template <typename WT, int NS, int P, int RN, bool kDevice = false>
+// kDevH: h rows written in this launch (device-scope token loads).
+template <typename WT, int NS, int P, int RN, bool kDevice = false, bool kDevH = false>
 __device__ __forceinline__ void dma2_tile(
     const bf16_t* __restrict__ h, const WT* __restrict__ w2, const float* __restrict__ s2,
     int scale_mode, const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
@@ -411,7 +436,7 @@ __device__ __forceinline__ void dma2_tile(
   for (int s = 0; s < NS; ++s)
 #pragma unroll
     for (int rt = 0; rt < RN; ++rt) acc[s][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (nch > 0) dma_dot<WT, RN, NS, P>(nsub, op, ring, k_begin, nch, acc);
+  if (nch > 0) dma_dot<WT, RN, NS, P, kDevH>(nsub, op, ring, k_begin, nch, acc);
 
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
@@ -596,9 +621,13 @@ __global__ __launch_bounds__(kDmaThreads) void ffn2_combine_dma_kernel(
 // tile that brings a counter to k * splits adds that token's partials, slots
 // then splits in the same fixed order as the combine kernel, and writes the
 // output, so the result is bit-identical to the three separate launches.
-// Cross-workgroup data (h, the partials) is published with an agent-scope
-// release fence before the counter update and read after an acquire fence
-// (the GPU's L2s are per XCD).  Counters are zeroed by the routing launch.
+// Cross-workgroup data (h, the partials) goes out with agent-scope atomic
+// stores, which write through this XCD's L2 (the GPU's L2s are per XCD),
+// and is read with agent-scope atomic loads, which do not take another
+// XCD's stale copy; a writer waits for its stores to complete before it
+// counts, a reader reads after the count.  So no tile writes back or
+// invalidates an L2, which an agent-scope fence would (once per tile).
+// Counters are zeroed by the routing launch.
 
 // Counter words: ticket, timeout flag, done13[blocks][splits], arrive[T][d / (16 RN)].
 constexpr int kFusedTicket = 0;
@@ -660,9 +689,12 @@ __global__ __launch_bounds__(kDmaThreads) void ffn_fused_dma_kernel(FusedParams 
     if (t < n13) {
       const int y = t / nblk;
       const int b = t - y * nblk;
-      dma13_tile<WT, NS, P13>(p.x, w13, p.s13, p.scale_mode, p.sorted_ids, p.block_expert, p.h,
-                              p.d, p.I, p.k, p.A, b, 16 * y, ring);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // h of this tile, device-wide
+      dma13_tile<WT, NS, P13, 1, true>(p.x, w13, p.s13, p.scale_mode, p.sorted_ids,
+                                       p.block_expert, p.h, p.d, p.I, p.k, p.A, b, 16 * y, ring);
+      // h went out with device-scope stores: once they have completed, the
+      // count may publish them (no L2 write-back needed)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __hip_atomic_fetch_add(done13 + b * p.splits + (16 * y) / p.ksplit, lane == 0 ? 1 : 0,
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
@@ -686,10 +718,12 @@ __global__ __launch_bounds__(kDmaThreads) void ffn_fused_dma_kernel(FusedParams 
         }
         __builtin_amdgcn_s_sleep(2);
       }
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the W13 tiles' h
-      dma2_tile<WT, NS, P2, RN>(p.h, w2, p.s2, p.scale_mode, p.topk_w, p.sorted_ids,
-                                p.block_expert, p.y_part, p.d, p.I, p.A, p.ksplit, b,
-                                dt * 16 * RN, z, ring);
+      // h is read with device-scope loads, the partials written with
+      // device-scope stores: no L2 invalidation or write-back
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");  // loads stay after the count
+      dma2_tile<WT, NS, P2, RN, true, true>(p.h, w2, p.s2, p.scale_mode, p.topk_w, p.sorted_ids,
+                                            p.block_expert, p.y_part, p.d, p.I, p.A, p.ksplit, b,
+                                            dt * 16 * RN, z, ring);
       if (timed_out) {  // h may not be complete: make the tile's outputs NaN, not plausible
         const int32_t* blk = p.sorted_ids + static_cast<size_t>(b) * B;
         const float nan = __builtin_nanf("");
@@ -699,15 +733,17 @@ __global__ __launch_bounds__(kDmaThreads) void ffn_fused_dma_kernel(FusedParams 
           if (f < p.A) {
 #pragma unroll
             for (int rt = 0; rt < RN; ++rt)
-              *reinterpret_cast<float4*>(p.y_part + (static_cast<size_t>(z) * p.A + f) * p.d +
-                                         dt * 16 * RN + 16 * rt + 4 * (lane >> 4)) =
-                  float4{nan, nan, nan, nan};
+              store_device4(p.y_part + (static_cast<size_t>(z) * p.A + f) * p.d + dt * 16 * RN +
+                                16 * rt + 4 * (lane >> 4),
+                            float4{nan, nan, nan, nan});
           }
         }
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // this tile's partials, device-wide
-      arrive_and_combine<NS, RN, false>(p.sorted_ids + static_cast<size_t>(b) * B, arrive,
-                                        p.y_part, p.out, p.A, p.k, p.splits, p.d, nd, dt);
+      // this tile's partials have completed before it counts them
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      arrive_and_combine<NS, RN, true>(p.sorted_ids + static_cast<size_t>(b) * B, arrive,
+                                       p.y_part, p.out, p.A, p.k, p.splits, p.d, nd, dt);
     }
   }
 }
@@ -872,19 +908,25 @@ hipError_t launch_ffn2_combine_dma(const FfnArgs& a, hipStream_t s) {
 
 // ------------------------------------------------------------ fused launcher
 
+// W2 channel tiles per wave in the fused kernel: two.  Its ring is sized
+// for the larger of the two phases' stages, so four W2 tiles (the W2
+// launch's choice for a single token) would double the W13 phase's LDS per
+// workgroup and leave two workgroups per CU instead of five: measured at
+// one token (d = 4096, I = 14336), the W13 phase then streamed at about
+// half the W13 launch's rate.
+constexpr int kFusedRN = 2;
+
 bool fused_decode_fits(int w_dtype, int act_dtype, int B, int d, int I, int64_t blocks_est) {
 #ifdef MOE_NO_FUSED_DECODE
   return false;
 #else
   return w_dtype == kDtypeBF16 && act_dtype == kDtypeBF16 &&
-         dma_stream_use(w_dtype, act_dtype, B, d, I, blocks_est) &&
-         d % (16 * dma_w2_rn(w_dtype, B, blocks_est)) == 0;
+         dma_stream_use(w_dtype, act_dtype, B, d, I, blocks_est) && d % (16 * kFusedRN) == 0;
 #endif
 }
 
 int fused_counter_ints(const FfnArgs& a) {
-  const int64_t blocks = ffn_blocks_estimate(a.cap, a.B, a.E, a.A);
-  return fused_counter_words(a.T, a.cap, a.B, a.splits, a.d, dma_w2_rn(a.w_dtype, a.B, blocks));
+  return fused_counter_words(a.T, a.cap, a.B, a.splits, a.d, kFusedRN);
 }
 
 namespace {
@@ -946,12 +988,14 @@ hipError_t launch_ffn_fused(const FfnArgs& a, hipStream_t s) {
   if (!a.fused_cnt || !fused_decode_fits(a.w_dtype, a.act_dtype, a.B, a.d, a.I, blocks) ||
       a.ksplit % 16 != 0 || a.ksplit % dma_stream_kc(a.w_dtype) != 0)
     return hipErrorInvalidValue;
+  static_assert(kDma2RN == kFusedRN && kDma2RN32 == kFusedRN,
+                "the fused kernel's W2 tiles match the W2 launch's for blocks of 16 and 32");
   switch (a.B) {
     case 16:
-      if (dma_w2_rn(a.w_dtype, a.B, blocks) == kDma2WideRN)
-        return ffn_fused_go<1, 2, kDma2WideP, kDma2WideRN>(a, s);
-      return ffn_fused_go<1, MOE_DMA13_P1, MOE_DMA2_P1, kDma2RN>(a, s);
-    case 32: return ffn_fused_go<2, MOE_DMA13_P2, MOE_DMA2_P2, kDma2RN32>(a, s);
+      // at most two row blocks (one token): the W13 launch's two-stage ring
+      if (blocks <= kDma2WideBlocks) return ffn_fused_go<1, 2, kDma2WideP, kFusedRN>(a, s);
+      return ffn_fused_go<1, MOE_DMA13_P1, MOE_DMA2_P1, kFusedRN>(a, s);
+    case 32: return ffn_fused_go<2, MOE_DMA13_P2, MOE_DMA2_P2, kFusedRN>(a, s);
   }
   return hipErrorInvalidValue;
 }
