@@ -783,13 +783,22 @@ __global__ __launch_bounds__(kDmaThreads) void ffn_fused_dma_kernel(FusedParams 
 constexpr int kDma2RN = MOE_DMA2_RN;
 constexpr int kDma2RNFp8 = MOE_DMA_FP8_RN2;
 
-// Four channel tiles per bf16 W2 wave when blocks of 16 give at most two row
-// blocks (a single token of a top-2 layer): the grid is small there, and
-// wider waves read the block's h rows half as often (measured at d = 4096,
-// I = 14336: 50 -> 44 us with a two-stage ring); with more blocks two tiles
-// per wave are faster (T = 8: 160 against 172 us).
-constexpr int kDma2WideRN = 4;
-constexpr int kDma2WideP = 2;
+// The bf16 W2 when blocks of 16 give at most two row blocks (a single token
+// of a top-2 layer; these are the blocks W2 with the combine runs on): two
+// channel tiles per wave with a two-stage ring, 32 KB of LDS per workgroup,
+// so that five workgroups fit on a CU and the 1024 tiles of four K splits
+// are all resident at once.  Measured at d = 4096, I = 14336 (W2 with the
+// combine): 40.9 us, against 42.5 with four channel tiles and a two-stage
+// ring (two workgroups per CU), 50.4 with two tiles and a three-stage ring
+// (three per CU, 1.3 rounds), and 50 before the combine was folded in.
+#ifndef MOE_DMA2_WIDE_RN
+#define MOE_DMA2_WIDE_RN 2
+#endif
+#ifndef MOE_DMA2_WIDE_P
+#define MOE_DMA2_WIDE_P 2
+#endif
+constexpr int kDma2WideRN = MOE_DMA2_WIDE_RN;
+constexpr int kDma2WideP = MOE_DMA2_WIDE_P;
 constexpr int64_t kDma2WideBlocks = 2;
 
 #ifndef MOE_DMA2_RN32
@@ -872,7 +881,7 @@ hipError_t launch_ffn2_dma(const FfnArgs& a, hipStream_t s) {
     return a.B == 16 ? ffn2_dma_go<fp8_t, 1, MOE_DMA_FP8_P2>(a, s) : hipErrorInvalidValue;
   switch (a.B) {
     case 16:
-      if (dma_w2_rn(a.w_dtype, a.B, ffn_blocks_estimate(a.cap, a.B, a.E, a.A)) == kDma2WideRN)
+      if (ffn_blocks_estimate(a.cap, a.B, a.E, a.A) <= kDma2WideBlocks)
         return ffn2_dma_go<bf16_t, 1, kDma2WideP, kDma2WideRN>(a, s);
       return ffn2_dma_go<bf16_t, 1, MOE_DMA2_P1>(a, s);
     case 32: return ffn2_dma_go<bf16_t, 2, MOE_DMA2_P2, kDma2RN32>(a, s);
@@ -889,7 +898,7 @@ hipError_t launch_ffn2_dma(const FfnArgs& a, hipStream_t s) {
 // T = 64: 556 against 504; e4m3fn weights at T = 1: 94.6 against 90.6 us;
 // T = 64: 1.95 against 1.61 ms).
 bool ffn2_combine_pays(int w_dtype, int B, int64_t blocks_est) {
-  return w_dtype == kDtypeBF16 && B == 16 && dma_w2_rn(w_dtype, B, blocks_est) == kDma2WideRN;
+  return w_dtype == kDtypeBF16 && B == 16 && blocks_est <= kDma2WideBlocks;
 }
 
 int ffn2_combine_ints(const FfnArgs& a) {
