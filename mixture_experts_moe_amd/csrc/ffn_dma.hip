@@ -907,7 +907,8 @@ int ffn2_combine_ints(const FfnArgs& a) {
 
 hipError_t launch_ffn2_combine_dma(const FfnArgs& a, hipStream_t s) {
   const int64_t blocks = ffn_blocks_estimate(a.cap, a.B, a.E, a.A);
-  // the one instantiation: blocks of 16 (one token subtile), four channel tiles
+  // the one instantiation: blocks of 16 (one token subtile), the single-token
+  // geometry (kDma2WideRN channel tiles, a kDma2WideP-stage ring)
   if (!a.combine_cnt || a.B != 16 || !dma_args_ok(a) || !dma_stream_use(a) ||
       !ffn2_combine_pays(a.w_dtype, a.B, blocks) || a.ksplit % dma_stream_kc(a.w_dtype) != 0 ||
       a.d % dma_w2_channels(a.w_dtype, a.B, blocks) != 0)
