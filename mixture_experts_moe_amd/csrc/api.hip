@@ -105,8 +105,10 @@ struct Plan {
   // workspace offsets (bytes); xq, sx, sh only in the W8A8 mode, qcnt only
   // with the queue schedule
   size_t logits, ids, gates, counts, num_padded, sorted, block_exp, h, y, xq, sx, sh, qcnt, total;
-  size_t rpart;  // the split router's partial tiles (layer path, few tokens), or 0
+  size_t rpart;  // the split router's partial tiles (layer path, few tokens), or the
+                 // LDS-staged router's quarter logits (many tokens and experts), or 0
   bool rsplit;
+  bool rlds;
   bool fused;    // W13, W2 and combine as one persistent launch (layer path, decode)
   bool w2c;      // W2 with the combine in its launch (layer path, decode)
   size_t fcnt;   // counters of either, cleared by the routing launch
@@ -295,6 +297,7 @@ void make_plan(const moe_desc* d, int top_k, bool with_routing, Plan* p) {
     p->block_exp = take(cap / p->B * 4);
   } else {
     p->rsplit = false;
+    p->rlds = false;
     p->rpart = 0;
     p->logits = p->ids = p->gates = p->counts = p->num_padded = p->sorted = p->block_exp = 0;
   }
@@ -316,7 +319,10 @@ void make_plan(const moe_desc* d, int top_k, bool with_routing, Plan* p) {
   if (with_routing) {
     p->rsplit = moe::router_fused(p->act, p->T, p->E) ||
                 moe::router_split_logits(p->act, p->T, p->E);
-    p->rpart = p->rsplit ? take(moe::router_split_bytes(p->T, p->E)) : 0;
+    p->rlds = !p->rsplit && moe::router_lds_logits(p->act, p->T, p->E, p->d);
+    p->rpart = p->rsplit ? take(moe::router_split_bytes(p->T, p->E))
+               : p->rlds ? take(moe::router_lds_bytes(p->T, p->E))
+                         : 0;
     // the fused decode kernel: its counters are cleared by the split
     // router's first launch, so it runs where that launch does
     const int64_t blocks_est = moe::ffn_blocks_estimate(p->cap, p->B, p->E, p->A);
@@ -524,10 +530,11 @@ static hipError_t route(const void* x, int act, const float* w_gate, float* logi
                   : moe::launch_router_fused(x, w_gate, logits, ids, gates, T, E, d, k, s);
     });
   hipError_t e = timed(MOE_KERNEL_ROUTE_LOGITS, s, [&] {
-    return part && moe::router_split_logits(act, T, E)
-               ? moe::launch_router_split_logits(x, w_gate, logits, T, E, d, part, s, zero,
-                                                 nzero)
-               : moe::launch_router_logits(x, act, w_gate, logits, T, E, d, s);
+    if (part && moe::router_split_logits(act, T, E))
+      return moe::launch_router_split_logits(x, w_gate, logits, T, E, d, part, s, zero, nzero);
+    if (part && moe::router_lds_logits(act, T, E, d))
+      return moe::launch_router_logits_lds(x, w_gate, logits, T, E, d, part, s);
+    return moe::launch_router_logits(x, act, w_gate, logits, T, E, d, s);
   });
   if (e == hipSuccess)
     e = timed(MOE_KERNEL_ROUTE_TOPK, s,
@@ -700,7 +707,7 @@ static int enqueue_forward(const Plan& p, const void* x, const float* w_gate, co
   int32_t* queue = p.queue ? reinterpret_cast<int32_t*>(ws + p.qcnt) : nullptr;
   int32_t* fcnt = p.fused || p.w2c ? reinterpret_cast<int32_t*>(ws + p.fcnt) : nullptr;
   bool zeroed = false;
-  void* part = p.rsplit ? ws + p.rpart : nullptr;
+  void* part = p.rsplit || p.rlds ? ws + p.rpart : nullptr;
   const hipError_t e = route_align(p, x, w_gate, logits, ids, gates, counts, sorted, block_exp,
                                    num_padded, part, queue, &zeroed, s, fcnt);
   if (e != hipSuccess) return MOE_ERR_HIP;

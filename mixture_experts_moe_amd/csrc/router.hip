@@ -496,6 +496,170 @@ __global__ __launch_bounds__(256) void router_logits_wide_kernel(
   }
 }
 
+// ---------------------------------------------------------------- many tokens, many experts, through LDS
+// The wide tiles above load their operands straight into fragment
+// registers: each load instruction covers 16 rows x 64 bytes (half of each
+// row's 128-byte line), and a 64-token x 32-expert tile re-reads its x rows
+// once per 32 experts and its W_gate rows once per 64 tokens.  At T = 2048,
+// E = 256, d = 7168 that is about 470 MB through L2 and the last-level cache
+// for 36 MB of data, and the per-CU load path, not the arithmetic, sets the
+// time.  Here a workgroup of eight waves computes 128 tokens x 64 experts
+// over one quarter of K: each 64-wide K stage of the 128 x rows (128 bytes
+// each) and 64 W_gate rows (256 bytes each) moves into LDS once, with
+// consecutive lanes on consecutive 16 bytes (whole lines), two stages ahead
+// in registers, and wave w multiplies tokens 64 (w / 4) .. +63 by experts
+// 16 (w % 4) .. +15 out of LDS.  Per 16-token x 16-expert tile the MFMA
+// sequence is the wide kernel's, over the same K quarter (the quarters are
+// its four waves' ranges), and the quarters' partial tiles are added in the
+// same order by router_quarter_sum_kernel: the logits are bit-identical to
+// router_logits_wide_kernel's.
+//
+// LDS rows: x rows of 128 bytes in eight 16-byte slots, slot s of row r at
+// s ^ ((r >> 1) & 7); W_gate rows of 256 bytes in sixteen slots, slot s of
+// row r at s ^ (r & 15).  So the 16 rows one 16-lane group reads at one k
+// fall in 16 different 16-byte bank groups.
+constexpr int kRlTok = 128;  // tokens per workgroup tile
+constexpr int kRlExp = 64;   // experts per workgroup tile
+constexpr int kRlK = 64;     // K per stage
+constexpr int kRlQuarters = 4;
+constexpr int kRlWaves = 8;  // wave w: experts 16 (w % 4) .., tokens 64 (w / 4) ..
+constexpr int kRlThreads = 64 * kRlWaves;
+constexpr int kRlXBytes = kRlTok * kRlK * 2;  // 16 KB
+constexpr int kRlWBytes = kRlExp * kRlK * 4;  // 16 KB
+// two 16-byte slots of each operand per thread and stage
+static_assert(2 * 16 * kRlThreads == kRlXBytes && 2 * 16 * kRlThreads == kRlWBytes,
+              "every slot has one thread");
+
+// A stage's share of one thread, in registers: x slots 0 and 1, W_gate
+// slots 0 and 1 (plain members, so that they stay in registers).
+struct RlRegs {
+  uint4 x0, x1, w0, w1;
+};
+
+__global__ __launch_bounds__(kRlThreads) void router_logits_lds_kernel(
+    const bf16_t* __restrict__ x, const float* __restrict__ wg, float* __restrict__ part, int T,
+    int E, int d) {
+  __shared__ __attribute__((aligned(16))) uint8_t sx[2][kRlXBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sw[2][kRlWBytes];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  const int t0 = blockIdx.x * kRlTok;
+  const int e0 = blockIdx.y * kRlExp;
+  const int z = blockIdx.z;
+  const int steps = d / 32;
+  const int k_begin = (z * steps / kRlQuarters) * 32;
+  const int nst = ((z + 1) * steps / kRlQuarters - z * steps / kRlQuarters) / 2;  // 64-wide stages
+
+  // this thread's slots: x slot u = tid + kRlThreads i (row u >> 3, slot
+  // u & 7), W_gate slot u (row u >> 4, slot u & 15), i = 0, 1.  Rows past T
+  // or E read row 0: every load is issued (so the compiler's wait counts
+  // stay exact and the later stages' loads stay in flight), and those rows
+  // feed only output rows and columns that are never stored.
+  const bf16_t* xs[2];
+  const float* ws[2];
+  uint32_t xo[2], wo[2];  // LDS byte offsets
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int u = tid + kRlThreads * i;
+    const int xr = u >> 3, xsl = u & 7;
+    const int t = t0 + xr;
+    xs[i] = x + static_cast<size_t>(t < T ? t : 0) * d + k_begin + 8 * xsl;
+    xo[i] = xr * 128 + ((xsl ^ ((xr >> 1) & 7)) << 4);
+    const int wr = u >> 4, wsl = u & 15;
+    const int e = e0 + wr;
+    ws[i] = wg + static_cast<size_t>(e < E ? e : 0) * d + k_begin + 4 * wsl;
+    wo[i] = wr * 256 + ((wsl ^ (wr & 15)) << 4);
+  }
+  auto load = [&](int st) {
+    const int o = st * kRlK;
+    return RlRegs{*reinterpret_cast<const uint4*>(xs[0] + o), *reinterpret_cast<const uint4*>(xs[1] + o),
+                  *reinterpret_cast<const uint4*>(ws[0] + o), *reinterpret_cast<const uint4*>(ws[1] + o)};
+  };
+  auto store = [&](const RlRegs r, int b) {
+    *reinterpret_cast<uint4*>(sx[b] + xo[0]) = r.x0;
+    *reinterpret_cast<uint4*>(sx[b] + xo[1]) = r.x1;
+    *reinterpret_cast<uint4*>(sw[b] + wo[0]) = r.w0;
+    *reinterpret_cast<uint4*>(sw[b] + wo[1]) = r.w1;
+  };
+
+  const int er = 16 * (wave & 3) + r16;  // this lane's W_gate row in the tile
+  const int tr0 = 64 * (wave >> 2);      // the wave's first token row
+  f32x4 acc_h[4], acc_m[4], acc_l[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) acc_h[u] = acc_m[u] = acc_l[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int b) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {  // the stage's two 32-wide steps, in K order
+      const int sl = 8 * h + 2 * g;  // W_gate slots of k = 32 h + 8 g .. +8
+      const float4 wa = *reinterpret_cast<const float4*>(sw[b] + er * 256 + ((sl ^ r16) << 4));
+      const float4 wb =
+          *reinterpret_cast<const float4*>(sw[b] + er * 256 + (((sl + 1) ^ r16) << 4));
+      const float w[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+      uint4 hi, mid, lo;
+      split3_bf16(w, hi, mid, lo);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int tr = tr0 + 16 * u + r16;
+        const bf16x8 xf = as_frag(*reinterpret_cast<const uint4*>(
+            sx[b] + tr * 128 + (((4 * h + g) ^ ((tr >> 1) & 7)) << 4)));
+        acc_h[u] = mfma16x16x32(as_frag(hi), xf, acc_h[u]);
+        acc_m[u] = mfma16x16x32(as_frag(mid), xf, acc_m[u]);
+        acc_l[u] = mfma16x16x32(as_frag(lo), xf, acc_l[u]);
+      }
+    }
+  };
+
+  // stages s + 1 and s + 2 are in flight in registers while stage s is
+  // multiplied out of LDS buffer s % 2.  Every load is issued (past the
+  // last stage it repeats the last one, unused), so that the two register
+  // sets stay in registers and the compiler's wait counts leave the later
+  // set in flight.
+  RlRegs ra = load(0);
+  RlRegs rb = load(min(1, nst - 1));
+  store(ra, 0);
+  __syncthreads();
+  for (int s = 0; s < nst; s += 2) {
+    // stage s in buffer 0 (registers rb: stage s + 1)
+    ra = load(min(s + 2, nst - 1));
+    compute(0);
+    if (s + 1 < nst) store(rb, 1);
+    __syncthreads();
+    if (s + 1 >= nst) break;
+    // stage s + 1 in buffer 1 (registers ra: stage s + 2)
+    rb = load(min(s + 3, nst - 1));
+    compute(1);
+    if (s + 2 < nst) store(ra, 0);
+    __syncthreads();
+  }
+  // D layout: lane holds token column r16, expert rows 4g .. 4g+3
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const f32x4 v = acc_h[u] + (acc_m[u] + acc_l[u]);
+    const int t = t0 + tr0 + 16 * u + r16;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = e0 + 16 * (wave & 3) + 4 * g + q;
+      if (t < T && e < E) part[(static_cast<size_t>(z) * T + t) * E + e] = v[q];
+    }
+  }
+}
+
+// logits = the four quarters' partial logits added in quarter order.
+__global__ __launch_bounds__(256) void router_quarter_sum_kernel(const float* __restrict__ part,
+                                                                 float* __restrict__ logits,
+                                                                 int64_t n) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    float v = part[i];
+#pragma unroll
+    for (int q = 1; q < kRlQuarters; ++q) v += part[q * n + i];
+    logits[i] = v;
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 
 // Below this many (64-token x 16-expert) tiles the logits kernel runs
@@ -512,6 +676,11 @@ __global__ __launch_bounds__(256) void router_logits_wide_kernel(
 #endif
 // (128: at E = 256 the 16-token tiles re-read W_gate's 7.3 MB once per 16
 // tokens, 93 us at T = 1024 and 139 at T = 1536 on them.)
+// Logits of the wide-tile shapes through LDS when the layer has scratch
+// for the quarters (0: the wide tiles).
+#ifndef MOE_ROUTER_LDS
+#define MOE_ROUTER_LDS 1
+#endif
 #ifndef MOE_ROUTER_WIDE_NE_WGS
 #define MOE_ROUTER_WIDE_NE_WGS 128
 #endif
@@ -542,6 +711,39 @@ hipError_t launch_router_logits(const void* x, int act_dtype, const float* wg, f
     router_logits_bf16_kernel<4, 4, false><<<grid, 256, 0, s>>>(
         static_cast<const bf16_t*>(x), wg, logits, nullptr, nullptr, T, E, d, 0, AlignOut{}, nullptr);
   }
+  return hipGetLastError();
+}
+
+// The logits through LDS (router_logits_lds_kernel) where the wide tiles
+// would run and K splits into quarters of whole 64-wide stages: the same
+// bits as launch_router_logits, in two launches, with `part` of
+// router_lds_bytes(T, E) scratch.
+static bool router_wide(int T, int E) {
+  return T > 64 &&
+         int64_t((T + 63) / 64) * ((E + 16 * kRouterWideNE - 1) / (16 * kRouterWideNE)) >=
+             MOE_ROUTER_WIDE_NE_WGS;
+}
+
+bool router_lds_logits(int act_dtype, int T, int E, int d) {
+  static_assert(kRouterWideNE == 2, "the LDS tile reproduces the wide kernel's two expert tiles");
+  return MOE_ROUTER_LDS && act_dtype == kDtypeBF16 && router_wide(T, E) && d % 256 == 0;
+}
+
+size_t router_lds_bytes(int T, int E) {
+  return static_cast<size_t>(kRlQuarters) * T * E * sizeof(float);
+}
+
+hipError_t launch_router_logits_lds(const void* x, const float* wg, float* logits, int T, int E,
+                                    int d, void* part, hipStream_t s) {
+  if (!router_lds_logits(kDtypeBF16, T, E, d) || !part) return hipErrorInvalidValue;
+  float* pt = static_cast<float*>(part);
+  const dim3 grid((T + kRlTok - 1) / kRlTok, (E + kRlExp - 1) / kRlExp, kRlQuarters);
+  router_logits_lds_kernel<<<grid, kRlThreads, 0, s>>>(static_cast<const bf16_t*>(x), wg, pt, T,
+                                                       E, d);
+  const int64_t n = static_cast<int64_t>(T) * E;
+  const int64_t want = (n + 255) / 256;
+  router_quarter_sum_kernel<<<static_cast<int>(want < 4096 ? want : 4096), 256, 0, s>>>(pt, logits,
+                                                                                        n);
   return hipGetLastError();
 }
 

@@ -684,6 +684,25 @@ def test_layer_split_router_equals_single_workgroup_router(T, E, k, d):
     assert torch.equal(out, ref)
 
 
+@pytest.mark.parametrize("T,E,k,d", [(1024, 256, 8, 512), (2048, 256, 8, 2048),
+                                     (200, 1000, 4, 256), (4096, 64, 6, 256)])
+def test_layer_lds_router_equals_wide_router(T, E, k, d):
+    """With many tokens and experts the layer computes the logits through
+    the LDS-staged tile (K in quarters, then a sum); the stage entry points
+    use the wide register tiles.  Bit-equal layer outputs mean bit-equal
+    logits, ids and gates; T and E that are not multiples of the tile
+    (200 tokens, 1000 experts) cover the masked rows."""
+    note(f"lds router T={T} E={E} k={k} d={d}")
+    inp = synth.make_inputs("decode_bf16", T=T, device=DEV, d=d, I=128, E=E, k=k, x_std=1.0)
+    out = B.moe_forward(inp.x, inp.w_gate, inp.w13, inp.w2, inp.top_k)
+    got = B.moe_route_align(inp.x, inp.w_gate, inp.top_k, intermediate=inp.I)
+    logits, ids, w, counts, sorted_ids, block_expert, num_padded, bm = got
+    ref = B.moe_expert_ffn(inp.x, inp.w13, inp.w2, inp.top_k, w, sorted_ids, block_expert,
+                           num_padded)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+
+
 # ---------------------------------------------------------------- fused decode kernel
 
 def _launches(fn):
