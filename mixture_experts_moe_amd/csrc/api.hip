@@ -529,12 +529,15 @@ static hipError_t route(const void* x, int act, const float* w_gate, float* logi
                                                    part, s, zero, nzero)
                   : moe::launch_router_fused(x, w_gate, logits, ids, gates, T, E, d, k, s);
     });
+  if (part && moe::router_lds_logits(act, T, E, d))  // logits, then selection with the sum
+    return timed(MOE_KERNEL_ROUTE_LOGITS, s, [&] {
+      return moe::launch_router_lds_topk(x, w_gate, logits, ids, gates, T, E, d, k, part, s);
+    });
   hipError_t e = timed(MOE_KERNEL_ROUTE_LOGITS, s, [&] {
-    if (part && moe::router_split_logits(act, T, E))
-      return moe::launch_router_split_logits(x, w_gate, logits, T, E, d, part, s, zero, nzero);
-    if (part && moe::router_lds_logits(act, T, E, d))
-      return moe::launch_router_logits_lds(x, w_gate, logits, T, E, d, part, s);
-    return moe::launch_router_logits(x, act, w_gate, logits, T, E, d, s);
+    return part && moe::router_split_logits(act, T, E)
+               ? moe::launch_router_split_logits(x, w_gate, logits, T, E, d, part, s, zero,
+                                                 nzero)
+               : moe::launch_router_logits(x, act, w_gate, logits, T, E, d, s);
   });
   if (e == hipSuccess)
     e = timed(MOE_KERNEL_ROUTE_TOPK, s,

@@ -55,12 +55,13 @@ hipError_t launch_router_split_logits(const void* x, const float* wg, float* log
                                       int nzero = 0);
 // bf16 activations where the wide 64-token tiles would run (many tokens and
 // experts), d % 256 == 0: the same logits, bit for bit, through an
-// LDS-staged 128-token x 64-expert tile per K quarter and a sum of the
-// quarters; `part` is router_lds_bytes(T, E) of scratch.
+// LDS-staged 128-token x 64-expert tile per K quarter, then one launch that
+// adds the quarters and selects (the same ids and gates as
+// launch_router_topk); `part` is router_lds_bytes(T, E) of scratch.
 bool router_lds_logits(int act_dtype, int T, int E, int d);
 size_t router_lds_bytes(int T, int E);
-hipError_t launch_router_logits_lds(const void* x, const float* wg, float* logits, int T, int E,
-                                    int d, void* part, hipStream_t s);
+hipError_t launch_router_lds_topk(const void* x, const float* wg, float* logits, int32_t* ids,
+                                  float* w, int T, int E, int d, int k, void* part, hipStream_t s);
 // `zero`: nzero int32 that the launch also sets to 0 (the expert kernels'
 // work-queue counters when the layer runs align right before them).
 hipError_t launch_align(const int32_t* ids, int A, int E, int B, int cap, int32_t* counts,

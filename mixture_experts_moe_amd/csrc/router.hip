@@ -511,7 +511,7 @@ __global__ __launch_bounds__(256) void router_logits_wide_kernel(
 // 16 (w % 4) .. +15 out of LDS.  Per 16-token x 16-expert tile the MFMA
 // sequence is the wide kernel's, over the same K quarter (the quarters are
 // its four waves' ranges), and the quarters' partial tiles are added in the
-// same order by router_quarter_sum_kernel: the logits are bit-identical to
+// same order by router_quarter_topk_kernel: the logits are bit-identical to
 // router_logits_wide_kernel's.
 //
 // LDS rows: x rows of 128 bytes in eight 16-byte slots, slot s of row r at
@@ -647,17 +647,31 @@ __global__ __launch_bounds__(kRlThreads) void router_logits_lds_kernel(
   }
 }
 
-// logits = the four quarters' partial logits added in quarter order.
-__global__ __launch_bounds__(256) void router_quarter_sum_kernel(const float* __restrict__ part,
-                                                                 float* __restrict__ logits,
-                                                                 int64_t n) {
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
-       i += static_cast<int64_t>(gridDim.x) * 256) {
+// The quarter sum and the top-k in one launch: one wave per token adds its
+// E logits' quarters (the order above), writes them, keeps them in LDS and
+// selects from there (topk_wave, as router_topk_kernel does).
+__global__ __launch_bounds__(256) void router_quarter_topk_kernel(const float* __restrict__ part,
+                                                                  float* __restrict__ logits,
+                                                                  int32_t* __restrict__ topk_ids,
+                                                                  float* __restrict__ topk_w,
+                                                                  int T, int E, int k) {
+  __shared__ float row[4][kMaxExpertsPerLane * 64];
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;  // whole wave
+  const int64_t n = static_cast<int64_t>(T) * E;
+  for (int e = lane; e < E; e += 64) {
+    const int64_t i = static_cast<int64_t>(t) * E + e;
     float v = part[i];
 #pragma unroll
     for (int q = 1; q < kRlQuarters; ++q) v += part[q * n + i];
     logits[i] = v;
+    row[wave][e] = v;
   }
+  // the wave's own LDS row: its writes are visible to its later reads
+  topk_wave(row[wave], E, k, topk_ids + static_cast<size_t>(t) * k,
+            topk_w + static_cast<size_t>(t) * k);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -715,8 +729,9 @@ hipError_t launch_router_logits(const void* x, int act_dtype, const float* wg, f
 }
 
 // The logits through LDS (router_logits_lds_kernel) where the wide tiles
-// would run and K splits into quarters of whole 64-wide stages: the same
-// bits as launch_router_logits, in two launches, with `part` of
+// would run and K splits into quarters of whole 64-wide stages, then the
+// quarters' sum and the selection: the same bits as launch_router_logits
+// and launch_router_topk, in two launches, with `part` of
 // router_lds_bytes(T, E) scratch.
 static bool router_wide(int T, int E) {
   return T > 64 &&
@@ -733,17 +748,15 @@ size_t router_lds_bytes(int T, int E) {
   return static_cast<size_t>(kRlQuarters) * T * E * sizeof(float);
 }
 
-hipError_t launch_router_logits_lds(const void* x, const float* wg, float* logits, int T, int E,
-                                    int d, void* part, hipStream_t s) {
-  if (!router_lds_logits(kDtypeBF16, T, E, d) || !part) return hipErrorInvalidValue;
+hipError_t launch_router_lds_topk(const void* x, const float* wg, float* logits, int32_t* ids,
+                                  float* w, int T, int E, int d, int k, void* part, hipStream_t s) {
+  if (!router_lds_logits(kDtypeBF16, T, E, d) || !part || E > kMaxExpertsPerLane * 64)
+    return hipErrorInvalidValue;
   float* pt = static_cast<float*>(part);
   const dim3 grid((T + kRlTok - 1) / kRlTok, (E + kRlExp - 1) / kRlExp, kRlQuarters);
   router_logits_lds_kernel<<<grid, kRlThreads, 0, s>>>(static_cast<const bf16_t*>(x), wg, pt, T,
                                                        E, d);
-  const int64_t n = static_cast<int64_t>(T) * E;
-  const int64_t want = (n + 255) / 256;
-  router_quarter_sum_kernel<<<static_cast<int>(want < 4096 ? want : 4096), 256, 0, s>>>(pt, logits,
-                                                                                        n);
+  router_quarter_topk_kernel<<<(T + 3) / 4, 256, 0, s>>>(pt, logits, ids, w, T, E, k);
   return hipGetLastError();
 }
 

@@ -688,8 +688,9 @@ def test_layer_split_router_equals_single_workgroup_router(T, E, k, d):
                                      (200, 1000, 4, 256), (4096, 64, 6, 256)])
 def test_layer_lds_router_equals_wide_router(T, E, k, d):
     """With many tokens and experts the layer computes the logits through
-    the LDS-staged tile (K in quarters, then a sum); the stage entry points
-    use the wide register tiles.  Bit-equal layer outputs mean bit-equal
+    the LDS-staged tile (K in quarters, then one launch that adds them and
+    selects); the stage entry points use the wide register tiles and the
+    top-k kernel.  Bit-equal layer outputs mean bit-equal
     logits, ids and gates; T and E that are not multiples of the tile
     (200 tokens, 1000 experts) cover the masked rows."""
     note(f"lds router T={T} E={E} k={k} d={d}")
