@@ -41,6 +41,7 @@
 namespace moe {
 
 constexpr int kAlignSlots = 4;  // consecutive slots per thread in the compaction
+constexpr int kRegPasses = 4;   // passes whose slots stay in registers between the steps
 
 // Inclusive prefix sum over the wave's lanes (lane order).
 __device__ __forceinline__ int wave_incl_scan(int v) {
@@ -84,10 +85,48 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
   if (e == 0)  // the next kernels' work-queue counters (none: nzero = 0)
     for (int i = tid; i < nzero; i += kAlignThreads) zero[i] = 0;
   for (int i = tid; i < E; i += kAlignThreads) cnt[i] = 0;
+  // this thread's slots of pass p: f0 .. f0 + 3, f0 = p * kPassSlots + 4 tid
+  // (thread order is slot order inside a pass); with at most kRegPasses
+  // passes they are read once, here, and kept in registers for step 3
+  constexpr int kPassSlots = kAlignThreads * kAlignSlots;
+  const int passes = (A + kPassSlots - 1) / kPassSlots;
+  const bool in_regs = passes <= kRegPasses;
+  auto read4 = [&](int f0, int (&id)[kAlignSlots]) {
+    if (f0 + kAlignSlots <= A) {
+      const int4 v = *reinterpret_cast<const int4*>(ids + f0);  // f0 % 4 == 0, ids 16-byte aligned
+      id[0] = v.x;
+      id[1] = v.y;
+      id[2] = v.z;
+      id[3] = v.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < kAlignSlots; ++j) id[j] = f0 + j < A ? ids[f0 + j] : -1;
+    }
+  };
+  int held[kRegPasses][kAlignSlots];
+  if (in_regs) {
+#pragma unroll
+    for (int p = 0; p < kRegPasses; ++p) {
+      if (p < passes) {
+        read4(p * kPassSlots + kAlignSlots * tid, held[p]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < kAlignSlots; ++j) held[p][j] = -1;
+      }
+    }
+  }
   __syncthreads();
-  for (int f = tid; f < A; f += kAlignThreads) {
-    const int id = ids[f];
-    if (static_cast<unsigned>(id) < static_cast<unsigned>(E)) atomicAdd(&cnt[id], 1);
+  if (in_regs) {
+#pragma unroll
+    for (int p = 0; p < kRegPasses; ++p)
+#pragma unroll
+      for (int j = 0; j < kAlignSlots; ++j)
+        if (static_cast<unsigned>(held[p][j]) < static_cast<unsigned>(E)) atomicAdd(&cnt[held[p][j]], 1);
+  } else {
+    for (int f = tid; f < A; f += kAlignThreads) {
+      const int id = ids[f];
+      if (static_cast<unsigned>(id) < static_cast<unsigned>(E)) atomicAdd(&cnt[id], 1);
+    }
   }
   __syncthreads();
 
@@ -105,19 +144,7 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
   // 3. ordered compaction of this expert's slots: thread tid of a pass owns
   // slots f0 .. f0 + 3, f0 = base + 4 tid, so thread order is slot order
   int running = 0;
-  for (int base = 0; base < A; base += kAlignThreads * kAlignSlots) {
-    const int f0 = base + kAlignSlots * tid;
-    int id[kAlignSlots];
-    if (f0 + kAlignSlots <= A) {
-      const int4 v = *reinterpret_cast<const int4*>(ids + f0);  // f0 % 4 == 0, ids 16-byte aligned
-      id[0] = v.x;
-      id[1] = v.y;
-      id[2] = v.z;
-      id[3] = v.w;
-    } else {
-#pragma unroll
-      for (int j = 0; j < kAlignSlots; ++j) id[j] = f0 + j < A ? ids[f0 + j] : -1;
-    }
+  auto compact = [&](const int (&id)[kAlignSlots], int f0) {
     int hits = 0;
 #pragma unroll
     for (int j = 0; j < kAlignSlots; ++j) hits += id[j] == e;
@@ -136,6 +163,17 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     for (int j = 0; j < kAlignSlots; ++j)
       if (id[j] == e) sorted_ids[pos++] = f0 + j;
     running += chunk;
+  };
+  if (in_regs) {
+#pragma unroll
+    for (int p = 0; p < kRegPasses; ++p)
+      if (p < passes) compact(held[p], p * kPassSlots + kAlignSlots * tid);
+  } else {
+    for (int base = 0; base < A; base += kPassSlots) {
+      int id[kAlignSlots];
+      read4(base + kAlignSlots * tid, id);
+      compact(id, base + kAlignSlots * tid);
+    }
   }
   // 4. pads and block owners of this expert
   for (int r = mine + tid; r < padded; r += kAlignThreads) sorted_ids[off + r] = A;
