@@ -403,11 +403,13 @@ __global__ __launch_bounds__(64 * NW) void router_logits_bf16_kernel(
 // order as by router_logits_bf16_kernel<4, 4> (bit-identical); only the
 // reuse changes.
 
+constexpr int kRouterWideWaves = 4;  // waves splitting K in the wide tiles
+
 template <int NE>
-__global__ __launch_bounds__(256) void router_logits_wide_kernel(
+__global__ __launch_bounds__(64 * kRouterWideWaves) void router_logits_wide_kernel(
     const bf16_t* __restrict__ x, const float* __restrict__ wg, float* __restrict__ logits, int T,
     int E, int d) {
-  constexpr int NT = 4, NW = 4, U = 2;
+  constexpr int NT = 4, NW = kRouterWideWaves, U = 2;
   __shared__ f32x4 red[NW][NT][NE][64];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -521,7 +523,7 @@ __global__ __launch_bounds__(256) void router_logits_wide_kernel(
 constexpr int kRlTok = 128;  // tokens per workgroup tile
 constexpr int kRlExp = 64;   // experts per workgroup tile
 constexpr int kRlK = 64;     // K per stage
-constexpr int kRlQuarters = 4;
+constexpr int kRlQuarters = kRouterWideWaves;  // the wide tiles' K ranges
 constexpr int kRlWaves = 8;  // wave w: experts 16 (w % 4) .., tokens 64 (w / 4) ..
 constexpr int kRlThreads = 64 * kRlWaves;
 constexpr int kRlXBytes = kRlTok * kRlK * 2;  // 16 KB
@@ -700,19 +702,23 @@ __global__ __launch_bounds__(256) void router_quarter_topk_kernel(const float* _
 #endif
 constexpr int kRouterWideNE = MOE_ROUTER_WIDE_NE;
 
+// enough 64-token x (16 NE)-expert tiles to fill half the GPU or more
+static bool router_wide(int T, int E) {
+  return T > 64 &&
+         int64_t((T + 63) / 64) * ((E + 16 * kRouterWideNE - 1) / (16 * kRouterWideNE)) >=
+             MOE_ROUTER_WIDE_NE_WGS;
+}
+
 hipError_t launch_router_logits(const void* x, int act_dtype, const float* wg, float* logits,
                                 int T, int E, int d, hipStream_t s) {
   if (act_dtype == kDtypeF32) {
     dim3 grid((T + 15) / 16, (E + 63) / 64);
     router_logits_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(x), wg, logits,
                                                      T, E, d);
-  } else if (T > 64 &&
-             int64_t((T + 63) / 64) * ((E + 16 * kRouterWideNE - 1) / (16 * kRouterWideNE)) >=
-                 MOE_ROUTER_WIDE_NE_WGS) {
-    // enough 64-token x (16 NE)-expert tiles to fill half the GPU or more:
+  } else if (router_wide(T, E)) {
     // each x fragment feeds NE expert tiles
     dim3 grid((T + 63) / 64, (E + 16 * kRouterWideNE - 1) / (16 * kRouterWideNE));
-    router_logits_wide_kernel<kRouterWideNE><<<grid, 256, 0, s>>>(static_cast<const bf16_t*>(x), wg,
+    router_logits_wide_kernel<kRouterWideNE><<<grid, 64 * kRouterWideWaves, 0, s>>>(static_cast<const bf16_t*>(x), wg,
                                                                   logits, T, E, d);
   } else if (T <= 64 || int64_t((T + 63) / 64) * ((E + 15) / 16) < MOE_ROUTER_WIDE_WGS) {
     // few tokens, or too few 64-token tiles to fill the GPU: 16-token tiles
@@ -733,12 +739,6 @@ hipError_t launch_router_logits(const void* x, int act_dtype, const float* wg, f
 // quarters' sum and the selection: the same bits as launch_router_logits
 // and launch_router_topk, in two launches, with `part` of
 // router_lds_bytes(T, E) scratch.
-static bool router_wide(int T, int E) {
-  return T > 64 &&
-         int64_t((T + 63) / 64) * ((E + 16 * kRouterWideNE - 1) / (16 * kRouterWideNE)) >=
-             MOE_ROUTER_WIDE_NE_WGS;
-}
-
 bool router_lds_logits(int act_dtype, int T, int E, int d) {
   static_assert(kRouterWideNE == 2, "the LDS tile reproduces the wide kernel's two expert tiles");
   return MOE_ROUTER_LDS && act_dtype == kDtypeBF16 && router_wide(T, E) && d % 256 == 0;
