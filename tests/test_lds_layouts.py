@@ -14,6 +14,10 @@ ring (mixture_experts_moe_amd/csrc/ffn_gemm_mid.hip), replayed in Python:
 A mistake in either (a swizzle that ignores a load's row offset, a wait one
 stage short) gives in-bounds but wrong reads on the GPU, which only a
 parity test with the right shapes would catch.
+
+Further sections replay the register-token tile's layouts and rings
+(ffn_gemm_wide.hip), the XCD raster over the realised row blocks, and the
+LDS-staged router's stage layout and K quarters (router.hip).
 """
 
 import pytest
@@ -361,3 +365,87 @@ def _full_rings(total):
 @pytest.mark.parametrize("total", list(range(3, 20)) + [56, 112])
 def test_wide_full_block_rings(total):
     assert _full_rings(total) == list(range(total))
+
+
+# ---------------------------------------------------------------- router logits through LDS
+# (mixture_experts_moe_amd/csrc/router.hip, router_logits_lds_kernel): one
+# stage is 128 x rows x 64 bf16 (128 bytes, eight 16-byte slots, slot s of
+# row r at s ^ ((r >> 1) & 7)) and 64 W_gate rows x 64 fp32 (256 bytes,
+# sixteen slots, slot s of row r at s ^ (r & 15)); thread t of 512 stores x
+# slot u = t + 512 i (row u >> 3, slot u & 7) and W_gate slot u (row u >> 4,
+# slot u & 15) for i = 0, 1, from global element k = 8 (u & 7) of its x row
+# and k = 4 (u & 15) of its W_gate row.
+
+RL_THREADS = 512
+
+
+def _router_lds_written():
+    xs, ws = {}, {}
+    for t in range(RL_THREADS):
+        for i in range(2):
+            u = t + RL_THREADS * i
+            xr, xsl = u >> 3, u & 7
+            off = xr * 128 + ((xsl ^ ((xr >> 1) & 7)) << 4)
+            for b in range(0, 16, 2):
+                assert off + b not in xs
+                xs[off + b] = (xr, 8 * xsl + b // 2)  # (token row, k)
+            wr, wsl = u >> 4, u & 15
+            off = wr * 256 + ((wsl ^ (wr & 15)) << 4)
+            for b in range(0, 16, 4):
+                assert off + b not in ws
+                ws[off + b] = (wr, 4 * wsl + b // 4)  # (expert row, k)
+    return xs, ws
+
+
+def test_router_lds_fragments_find_their_operands():
+    """Every fragment the eight waves read (lane (r16, g) of wave w, step h:
+    W_gate row 16 (w % 4) + r16, k = 32 h + 8 g .. +8 in two 16-byte slots;
+    x row 64 (w / 4) + 16 u + r16, k = 32 h + 8 g .. +8) holds exactly those
+    values, both buffers are filled whole, and the 16 rows one 16-lane group
+    reads at one k fall in 16 different 16-byte bank groups."""
+    xs, ws = _router_lds_written()
+    assert len(xs) == 128 * 64 and len(ws) == 64 * 64
+    for w in range(8):
+        for lane in range(64):
+            r16, g = lane & 15, lane >> 4
+            er = 16 * (w & 3) + r16
+            for h in range(2):
+                sl = 8 * h + 2 * g
+                for half, slot in enumerate((sl, sl + 1)):
+                    off = er * 256 + ((slot ^ r16) << 4)
+                    for q in range(4):
+                        assert ws[off + 4 * q] == (er, 32 * h + 8 * g + 4 * half + q)
+                for u in range(4):
+                    tr = 64 * (w >> 2) + 16 * u + r16
+                    off = tr * 128 + (((4 * h + g) ^ ((tr >> 1) & 7)) << 4)
+                    for q in range(8):
+                        assert xs[off + 2 * q] == (tr, 32 * h + 8 * g + q)
+    # bank groups of one 16-lane group's reads (16-byte groups mod 256 bytes)
+    for w in range(8):
+        for g in range(4):
+            for h in range(2):
+                wb = {((16 * (w & 3) + r) * 256 + (((8 * h + 2 * g) ^ r) << 4)) % 256 // 16
+                      for r in range(16)}
+                assert len(wb) == 16
+                for u in range(4):
+                    xb = set()
+                    for r in range(16):
+                        tr = 64 * (w >> 2) + 16 * u + r
+                        xb.add((tr * 128 + (((4 * h + g) ^ ((tr >> 1) & 7)) << 4)) % 256 // 16)
+                    assert len(xb) == 16
+
+
+def test_router_lds_quarters_are_the_wide_waves_ranges():
+    """The LDS tile's K quarter z covers the 32-wide steps [z S/4, (z+1) S/4)
+    of the wide tiles' wave z, in whole 64-wide stages, for every d the
+    layer sends it (d % 256 == 0)."""
+    for d in range(256, 16385, 256):
+        steps = d // 32
+        covered = []
+        for z in range(4):
+            k_begin = (z * steps // 4) * 32
+            nst = ((z + 1) * steps // 4 - z * steps // 4) // 2
+            assert ((z + 1) * steps // 4 - z * steps // 4) % 2 == 0
+            covered += list(range(k_begin // 32, k_begin // 32 + 2 * nst))
+            assert covered[-1] + 1 == (z + 1) * steps // 4
+        assert covered == list(range(steps))
