@@ -192,8 +192,12 @@ int default_block_m(const moe_desc* d, int top_k) {
 #ifndef MOE_WIDE_W2_MAX_SPLITS
 #define MOE_WIDE_W2_MAX_SPLITS 4
 #endif
+// (32, not 8: at the skew shape, I = 2880, two ranges of 22 stages cost
+// more in ring fill and in the combine's second set of partials than they
+// gained in grid fill, W2 + combine 138 -> 129 us; the decode shapes at
+// T = 128..1024, I = 14336, keep their splits.)
 #ifndef MOE_WIDE_W2_MIN_STAGES
-#define MOE_WIDE_W2_MIN_STAGES 8
+#define MOE_WIDE_W2_MIN_STAGES 32
 #endif
 
 int64_t capacity(int64_t A, int64_t E, int64_t B) {

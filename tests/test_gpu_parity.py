@@ -166,7 +166,10 @@ SMALL = [
     # blocks of 128 on the register-token tile (bf16 ring of four, e4m3fn of
     # three): tails of every length, channel tiles overhanging I and d,
     # experts with one block (nontemporal weights) and with two, waves
-    # without tokens, per-tensor scales, W2's K split in two
+    # without tokens, per-tensor scales, W2's K split in two (I of 64
+    # stages: two ranges of the 32-stage minimum)
+    ("bf16_wide", dict(workload="decode_bf16", d=256, I=4096, E=4, k=1, x_std=1.0), 200, 128),
+    ("fp8_wide", dict(workload="fp8", d=256, I=8192, E=2, k=1), 150, 128),
     ("bf16_wide", dict(workload="decode_bf16", d=320, I=448, E=8, k=2, x_std=1.0), 600, 128),
     ("bf16_wide", dict(workload="decode_bf16", d=256, I=2304, E=4, k=1, x_std=1.0), 200, 128),
     ("bf16_wide", dict(workload="decode_bf16", d=384, I=384, E=16, k=4, x_std=1.0), 100, 128),
