@@ -129,8 +129,8 @@ extern "C" {
  * most two row blocks of 16 (one token of a top-2 layer) W2 adds up each
  * token's slots itself (two launches: the last W2 workgroup to finish a
  * token's channel group sums its partials).  The persistent kernel is
- * slower there (every W13 tile has to publish its rows at device scope
- * before a W2 tile on another XCD may read them).  The static and queue
+ * slower there (its W2 tiles wait for the W13 tiles they read, and read
+ * those h rows at device scope, past their own XCD's L2).  The static and queue
  * schedules give bit-identical outputs, and on the decode path so does the
  * automatic one; with 128-token blocks its tiles sum over K in another
  * order (equal within rounding).  Other paths ignore the field. */
