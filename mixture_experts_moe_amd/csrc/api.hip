@@ -533,6 +533,10 @@ static hipError_t route(const void* x, int act, const float* w_gate, float* logi
                                                    part, s, zero, nzero)
                   : moe::launch_router_fused(x, w_gate, logits, ids, gates, T, E, d, k, s);
     });
+  if (moe::router_selects(act, T, E))  // at most 16 experts: the logits kernel selects too
+    return timed(MOE_KERNEL_ROUTE_LOGITS, s, [&] {
+      return moe::launch_router_fused(x, w_gate, logits, ids, gates, T, E, d, k, s);
+    });
   if (part && moe::router_lds_logits(act, T, E, d))  // logits, then selection with the sum
     return timed(MOE_KERNEL_ROUTE_LOGITS, s, [&] {
       return moe::launch_router_lds_topk(x, w_gate, logits, ids, gates, T, E, d, k, part, s);

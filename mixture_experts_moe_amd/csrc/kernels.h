@@ -25,6 +25,10 @@ hipError_t launch_router_topk(const float* logits, int32_t* ids, float* w, int T
 bool router_fused(int act_dtype, int T, int E);
 hipError_t launch_router_fused(const void* x, const float* wg, float* logits, int32_t* ids,
                                float* w, int T, int E, int d, int k, hipStream_t s);
+// bf16 activations, E <= 16, any T whose logits launch_router_logits runs
+// on the 16-token tiles: launch_router_fused's kernel gives the same logits
+// and also selects (one launch instead of two).
+bool router_selects(int act_dtype, int T, int E);
 // bf16 activations, 1 <= T <= 16, E <= 16: logits, selection and the
 // regrouping (same outputs as launch_align) in one single-workgroup kernel.
 bool route_align_fused(int act_dtype, int T, int E);

@@ -709,6 +709,13 @@ static bool router_wide(int T, int E) {
              MOE_ROUTER_WIDE_NE_WGS;
 }
 
+// few tokens, or too few 64-token tiles to fill the GPU: 16-token tiles
+// with K split 16 ways (router_logits_bf16_kernel<1, 16>)
+static bool router_tile16(int T, int E) {
+  return !router_wide(T, E) &&
+         (T <= 64 || int64_t((T + 63) / 64) * ((E + 15) / 16) < MOE_ROUTER_WIDE_WGS);
+}
+
 hipError_t launch_router_logits(const void* x, int act_dtype, const float* wg, float* logits,
                                 int T, int E, int d, hipStream_t s) {
   if (act_dtype == kDtypeF32) {
@@ -720,9 +727,7 @@ hipError_t launch_router_logits(const void* x, int act_dtype, const float* wg, f
     dim3 grid((T + 63) / 64, (E + 16 * kRouterWideNE - 1) / (16 * kRouterWideNE));
     router_logits_wide_kernel<kRouterWideNE><<<grid, 64 * kRouterWideWaves, 0, s>>>(static_cast<const bf16_t*>(x), wg,
                                                                   logits, T, E, d);
-  } else if (T <= 64 || int64_t((T + 63) / 64) * ((E + 15) / 16) < MOE_ROUTER_WIDE_WGS) {
-    // few tokens, or too few 64-token tiles to fill the GPU: 16-token tiles
-    // with K split 16 ways
+  } else if (router_tile16(T, E)) {
     dim3 grid((T + 15) / 16, (E + 15) / 16);
     router_logits_bf16_kernel<1, 16, false><<<grid, 1024, 0, s>>>(
         static_cast<const bf16_t*>(x), wg, logits, nullptr, nullptr, T, E, d, 0, AlignOut{}, nullptr);
@@ -762,6 +767,10 @@ hipError_t launch_router_lds_topk(const void* x, const float* wg, float* logits,
 
 bool router_fused(int act_dtype, int T, int E) {
   return act_dtype == kDtypeBF16 && T <= 64 && E <= 16;
+}
+
+bool router_selects(int act_dtype, int T, int E) {
+  return act_dtype == kDtypeBF16 && E <= 16 && router_tile16(T, E);
 }
 
 hipError_t launch_router_fused(const void* x, const float* wg, float* logits, int32_t* ids,
