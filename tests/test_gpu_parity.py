@@ -51,7 +51,10 @@ def test_topk_from_given_logits_is_exact(T, E, k):
 
 
 @pytest.mark.parametrize("wl,T", [("tiny_fp32", 16), ("decode_bf16", 64), ("fp8", 100), ("skew", 512),
-                                  ("fp8", 2048)])
+                                  ("fp8", 2048),
+                                  # at most 16 experts past 64 tokens: the 16-token
+                                  # tiles select in the same launch
+                                  ("decode_bf16", 300), ("prefill_bf16", 4096)])
 def test_router_logits_and_selection(wl, T):
     note(f"route {wl} T={T}")
     cfg = synth.WORKLOADS[wl]
