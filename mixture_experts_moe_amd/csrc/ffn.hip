@@ -323,6 +323,10 @@ __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, float4 v) {
   *reinterpret_cast<uint2*>(p) = uint2{lo, hi};
 }
 
+#ifndef MOE_COMBINE_NT
+#define MOE_COMBINE_NT 1
+#endif
+
 template <typename OT>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_part,
                                                       OT* __restrict__ out, int T, int d, int k,
@@ -338,8 +342,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       const size_t f = static_cast<size_t>(t) * k + j;
       float4 sj = {0.f, 0.f, 0.f, 0.f};
       for (int z = 0; z < splits; ++z) {
+#if MOE_COMBINE_NT
+        const f32x4 pv = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(y_part + (static_cast<size_t>(z) * A + f) * d + c));
+        const float4 p{pv[0], pv[1], pv[2], pv[3]};
+#else
         const float4 p =
             *reinterpret_cast<const float4*>(y_part + (static_cast<size_t>(z) * A + f) * d + c);
+#endif
         sj.x += p.x;
         sj.y += p.y;
         sj.z += p.z;

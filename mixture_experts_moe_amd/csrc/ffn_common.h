@@ -114,4 +114,17 @@ struct WeightStream {
   }
 };
 
+// One slot's four fp32 output channels into the W2 partials (y_part), which
+// the combine reads once.  MOE_Y_NT: with the nontemporal hint.
+#ifndef MOE_Y_NT
+#define MOE_Y_NT 0
+#endif
+__device__ __forceinline__ void store_partial4(float* p, float a, float b, float c, float d) {
+#if MOE_Y_NT
+  __builtin_nontemporal_store(f32x4{a, b, c, d}, reinterpret_cast<f32x4*>(p));
+#else
+  *reinterpret_cast<float4*>(p) = float4{a, b, c, d};
+#endif
+}
+
 }  // namespace moe

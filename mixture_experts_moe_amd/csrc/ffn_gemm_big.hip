@@ -295,9 +295,8 @@ __global__ __launch_bounds__(kBigThreads) void ffn2_big_kernel(
       float* yrow = y + static_cast<size_t>(f) * d + n0 + 128 * wm + 4 * g;
 #pragma unroll
       for (int t = 0; t < kBigTA; ++t)
-        *reinterpret_cast<float4*>(yrow + 16 * t) =
-            float4{acc[t][u][0] * gate, acc[t][u][1] * gate, acc[t][u][2] * gate,
-                   acc[t][u][3] * gate};
+        store_partial4(yrow + 16 * t, acc[t][u][0] * gate, acc[t][u][1] * gate,
+                       acc[t][u][2] * gate, acc[t][u][3] * gate);
     }
   }
 }

@@ -435,11 +435,10 @@ __global__ __launch_bounds__(kBigThreads) void ffn2_big8_kernel(
       for (int t = 0; t < kBigTA; ++t) {
         const int nb = n0 + 128 * wm + 16 * t + 4 * g;
         const size_t base = static_cast<size_t>(e) * d + nb;
-        *reinterpret_cast<float4*>(yrow + nb) =
-            float4{acc[t][u][0] * load_scale(s2, scale_mode, e, base) * gate,
-                   acc[t][u][1] * load_scale(s2, scale_mode, e, base + 1) * gate,
-                   acc[t][u][2] * load_scale(s2, scale_mode, e, base + 2) * gate,
-                   acc[t][u][3] * load_scale(s2, scale_mode, e, base + 3) * gate};
+        store_partial4(yrow + nb, acc[t][u][0] * load_scale(s2, scale_mode, e, base) * gate,
+                       acc[t][u][1] * load_scale(s2, scale_mode, e, base + 1) * gate,
+                       acc[t][u][2] * load_scale(s2, scale_mode, e, base + 2) * gate,
+                       acc[t][u][3] * load_scale(s2, scale_mode, e, base + 3) * gate);
       }
     }
   }

@@ -694,9 +694,8 @@ __device__ __forceinline__ void half2_tile(const WidLoader& wl, uint8_t* const (
         float sc[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) sc[v] = load_scale(s2, scale_mode, e, base + v);
-        *reinterpret_cast<float4*>(yrow + c) =
-            float4{acc[t][u][0] * sc[0] * gate, acc[t][u][1] * sc[1] * gate,
-                   acc[t][u][2] * sc[2] * gate, acc[t][u][3] * sc[3] * gate};
+        store_partial4(yrow + c, acc[t][u][0] * sc[0] * gate, acc[t][u][1] * sc[1] * gate,
+                       acc[t][u][2] * sc[2] * gate, acc[t][u][3] * sc[3] * gate);
       }
     }
   }
@@ -956,9 +955,8 @@ __device__ __forceinline__ void full2_nl(const FullLoader& ld, uint8_t* const (&
         float sc[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) sc[v] = load_scale(s2, scale_mode, e, base + v);
-        *reinterpret_cast<float4*>(yrow + c) =
-            float4{acc[t][u][0] * sc[0] * gate, acc[t][u][1] * sc[1] * gate,
-                   acc[t][u][2] * sc[2] * gate, acc[t][u][3] * sc[3] * gate};
+        store_partial4(yrow + c, acc[t][u][0] * sc[0] * gate, acc[t][u][1] * sc[1] * gate,
+                       acc[t][u][2] * sc[2] * gate, acc[t][u][3] * sc[3] * gate);
       }
     }
   }
@@ -1194,9 +1192,8 @@ __device__ __forceinline__ void wide2_tile(WidLoader& ld, uint8_t* const (&buf)[
 #pragma unroll
           for (int v = 0; v < 4; ++v) sc[v] = load_scale(s2, scale_mode, e, base + v);
         }
-        *reinterpret_cast<float4*>(yrow + c) =
-            float4{acc[t][u][0] * sc[0] * gate, acc[t][u][1] * sc[1] * gate,
-                   acc[t][u][2] * sc[2] * gate, acc[t][u][3] * sc[3] * gate};
+        store_partial4(yrow + c, acc[t][u][0] * sc[0] * gate, acc[t][u][1] * sc[1] * gate,
+                       acc[t][u][2] * sc[2] * gate, acc[t][u][3] * sc[3] * gate);
       }
     }
   }
